@@ -1,0 +1,479 @@
+/*
+ * oracle.c -- plain, slow, direct-loop CPU implementation of the convolutional
+ * block backward pass, in double precision.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path (the HIP library and
+ * its Python binding) may include, link or call this file; it exists so the
+ * tests, the smoke check and the CPU-baseline leg of the benchmark can compare
+ * the GPU results against an independent reading of the pages.  It shares no
+ * source, header, table or helper with the HIP code.
+ *
+ * Every loop below is the textbook definition of the quantity, written out in
+ * the order the pages state it; there is no blocking, tiling or reordering.
+ * Parallel loops (OpenMP) split only over independent output elements, so the
+ * summation order of every output value is fixed and the result does not depend
+ * on the thread count.
+ *
+ * Pages cited (title, address), tagged [P1]..[P5] below:
+ *  [P1] "YOLOv3 backpropagation: full-flow source analysis"
+ *       (suzhouguqin.com/content/1291550.html)
+ *  [P2] "Caffe source study ch.4 (5): the LeNet backward pass"
+ *       (csdndocs.com/article/9344743)
+ *  [P3] "AlexeyAB DarkNet analysis (4): network forward/backward and the layer struct"
+ *       (m.dandelioncloud.cn/article/details/1675816420510003202)
+ *  [P4] "caffe source study -- one article is enough"
+ *       (geek-share.com/detail/2722348220.html)
+ *  [P5] "Understanding BatchNorm" (javaforall.cn/143067.html)
+ *
+ * Layouts: activations NCHW contiguous (the delta/output layout of the layer
+ * struct in [P3], Blob::offset in [P4]); conv weights OIHW ([P3] layer struct,
+ * "weights"); inner-product weights out x in ([P2] layer 8).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <string.h>
+
+#define ORC_ACT_LINEAR 0
+#define ORC_ACT_LEAKY 1
+#define ORC_ACT_LOGISTIC 2
+#define ORC_ACT_RELU 3
+
+int orc_version(void) { return 1; }
+
+/* ------------------------------------------------------------------ */
+/* activations                                                         */
+/* ------------------------------------------------------------------ */
+
+/* Forward activations used to build saved tensors: [P1] section 7 defines
+ * linear x, logistic 1/(1+e^-x), relu x*(x>0), leaky (x>0)?x:0.1x; the leaky
+ * slope is a parameter here (0.1 in all pages' uses). */
+static double act_fwd(int act, double slope, double u) {
+  switch (act) {
+    case ORC_ACT_LINEAR: return u;
+    case ORC_ACT_LEAKY: return (u > 0) ? u : slope * u;
+    case ORC_ACT_LOGISTIC: return 1.0 / (1.0 + exp(-u));
+    case ORC_ACT_RELU: return (u > 0) ? u : 0.0;
+  }
+  return NAN;
+}
+
+/* Activation derivative evaluated on the OUTPUT y, as Darknet's gradient
+ * functions do ([P1] section 7: leaky_gradient (x>0)?1:.1, logistic_gradient
+ * (1-x)*x, linear_gradient 1, relu_gradient (x>0)). */
+static double act_grad(int act, double slope, double y) {
+  switch (act) {
+    case ORC_ACT_LINEAR: return 1.0;
+    case ORC_ACT_LEAKY: return (y > 0) ? 1.0 : slope;
+    case ORC_ACT_LOGISTIC: return (1.0 - y) * y;
+    case ORC_ACT_RELU: return (y > 0) ? 1.0 : 0.0;
+  }
+  return NAN;
+}
+
+void orc_act_forward(int act, double slope, const double* u, double* y, long count) {
+#pragma omp parallel for schedule(static)
+  for (long i = 0; i < count; ++i) y[i] = act_fwd(act, slope, u[i]);
+}
+
+/* gradient_array ([P1] section 3.1 and section 7): g = delta * act'(y). */
+void orc_act_backward(int act, double slope, const double* y, const double* delta, double* g,
+                      long count) {
+#pragma omp parallel for schedule(static)
+  for (long i = 0; i < count; ++i) g[i] = delta[i] * act_grad(act, slope, y[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* batch normalisation                                                 */
+/* ------------------------------------------------------------------ */
+
+/* Training-mode forward, per channel over (batch, spatial): mean, BIASED
+ * variance E[(z-mean)^2] (the one Caffe normalises with, [P5] Forward_cpu),
+ * xhat = (z-mean)/sqrt(var+eps) with eps inside the root, u = gamma*xhat+beta
+ * (scale_bias / add_bias of [P1] section 4). */
+void orc_bn_forward(int n, int c, long hw, double eps, const double* z, const double* gamma,
+                    const double* beta, double* mean, double* var, double* xhat, double* u) {
+  const double m = (double)n * (double)hw;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int ch = 0; ch < c; ++ch) {
+    double s = 0.0;
+    for (int b = 0; b < n; ++b)
+      for (long i = 0; i < hw; ++i) s += z[((long)b * c + ch) * hw + i];
+    const double mu = s / m;
+    double v = 0.0;
+    for (int b = 0; b < n; ++b)
+      for (long i = 0; i < hw; ++i) {
+        const double d = z[((long)b * c + ch) * hw + i] - mu;
+        v += d * d;
+      }
+    v /= m;
+    mean[ch] = mu;
+    var[ch] = v;
+    const double inv = 1.0 / sqrt(v + eps);
+    for (int b = 0; b < n; ++b)
+      for (long i = 0; i < hw; ++i) {
+        const long idx = ((long)b * c + ch) * hw + i;
+        xhat[idx] = (z[idx] - mu) * inv;
+        u[idx] = gamma[ch] * xhat[idx] + beta[ch];
+      }
+  }
+}
+
+/* Training-mode BN backward from g = dL/du.
+ * Steps in the order of backward_batchnorm_layer ([P1] section 4):
+ *   backward_bias:       dbeta_c  += sum g
+ *   backward_scale_cpu:  dgamma_c += sum g * xhat
+ *   scale_bias:          g' = gamma_c * g
+ * then the input gradient in the closed form of Caffe's BatchNormLayer
+ * Backward_cpu ([P5]), which takes exactly xhat and sqrt(var+eps):
+ *   dz = (g' - mean(g') - mean(g' * xhat) * xhat) / sqrt(var + eps)
+ * means over (batch, spatial).  [P5] states this equals the three-step
+ * mean_delta / variance_delta / normalize_delta route of [P1] section 4; the
+ * tests check that equality independently. */
+void orc_bn_backward(int n, int c, long hw, double eps, const double* g, const double* xhat,
+                     const double* var, const double* gamma, double* dz, double* dgamma,
+                     double* dbeta) {
+  const double m = (double)n * (double)hw;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int ch = 0; ch < c; ++ch) {
+    double sg = 0.0, sgx = 0.0;
+    for (int b = 0; b < n; ++b)
+      for (long i = 0; i < hw; ++i) {
+        const long idx = ((long)b * c + ch) * hw + i;
+        sg += g[idx];
+        sgx += g[idx] * xhat[idx];
+      }
+    dbeta[ch] += sg;
+    dgamma[ch] += sgx;
+    const double gm = gamma[ch];
+    const double mean_g = gm * sg / m;      /* mean(g')        */
+    const double mean_gx = gm * sgx / m;    /* mean(g' * xhat) */
+    const double sd = sqrt(var[ch] + eps);
+    for (int b = 0; b < n; ++b)
+      for (long i = 0; i < hw; ++i) {
+        const long idx = ((long)b * c + ch) * hw + i;
+        dz[idx] = (gm * g[idx] - mean_g - mean_gx * xhat[idx]) / sd;
+      }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* convolution                                                         */
+/* ------------------------------------------------------------------ */
+
+/* Output size of a padded strided window, im2col_cpu of [P1] section 3.2:
+ * (size + 2*pad - ksize)/stride + 1. */
+int orc_conv_out_dim(int size, int k, int s, int p) { return (size + 2 * p - k) / s + 1; }
+
+/* Input value at (row, col) of plane `plane`, zero outside the image (the
+ * padding reading of im2col_get_pixel, whose body the pages do not show). */
+static double pix(const double* plane, int h, int w, int row, int col) {
+  if (row < 0 || col < 0 || row >= h || col >= w) return 0.0;
+  return plane[(long)row * w + col];
+}
+
+/* Forward convolution (cross-correlation, as im2col + gemm computes it):
+ * z[n,o,ho,wo] = sum_{i,kh,kw} W[o,i,kh,kw] * x[n,i,ho*s+kh-p,wo*s+kw-p] (+b[o]). */
+void orc_conv_forward(int n, int c, int h, int w, int oc, int k, int s, int p, const double* x,
+                      const double* wt, const double* bias, double* z) {
+  const int oh = orc_conv_out_dim(h, k, s, p), ow = orc_conv_out_dim(w, k, s, p);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < n; ++b)
+    for (int o = 0; o < oc; ++o)
+      for (int y = 0; y < oh; ++y)
+        for (int xo = 0; xo < ow; ++xo) {
+          double acc = bias ? bias[o] : 0.0;
+          for (int i = 0; i < c; ++i) {
+            const double* plane = x + ((long)b * c + i) * h * w;
+            for (int kh = 0; kh < k; ++kh)
+              for (int kw = 0; kw < k; ++kw)
+                acc += wt[(((long)o * c + i) * k + kh) * k + kw] *
+                       pix(plane, h, w, y * s + kh - p, xo * s + kw - p);
+          }
+          z[(((long)b * oc + o) * oh + y) * ow + xo] = acc;
+        }
+}
+
+/* Weight gradient, the gemm(0,1,...,beta=1) of backward_convolutional_layer
+ * ([P1] section 3.1) summed over images (section 1.2: per-image gradients are
+ * accumulated, not averaged):
+ *   dW[o,i,kh,kw] += sum_{n,ho,wo} dz[n,o,ho,wo] * x[n,i,ho*s+kh-p,wo*s+kw-p]. */
+void orc_conv_backward_weights(int n, int c, int h, int w, int oc, int k, int s, int p,
+                               const double* x, const double* dz, double* dw) {
+  const int oh = orc_conv_out_dim(h, k, s, p), ow = orc_conv_out_dim(w, k, s, p);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int o = 0; o < oc; ++o)
+    for (int i = 0; i < c; ++i)
+      for (int kh = 0; kh < k; ++kh)
+        for (int kw = 0; kw < k; ++kw) {
+          double acc = 0.0;
+          for (int b = 0; b < n; ++b) {
+            const double* plane = x + ((long)b * c + i) * h * w;
+            const double* d = dz + ((long)b * oc + o) * oh * ow;
+            for (int y = 0; y < oh; ++y)
+              for (int xo = 0; xo < ow; ++xo)
+                acc += d[(long)y * ow + xo] * pix(plane, h, w, y * s + kh - p, xo * s + kw - p);
+          }
+          dw[(((long)o * c + i) * k + kh) * k + kw] += acc;
+        }
+}
+
+/* One weight-gradient element (same sum as above, not accumulated). */
+double orc_conv_dw_at(int n, int c, int h, int w, int oc, int k, int s, int p, const double* x,
+                      const double* dz, int o, int i, int kh, int kw) {
+  const int oh = orc_conv_out_dim(h, k, s, p), ow = orc_conv_out_dim(w, k, s, p);
+  double acc = 0.0;
+  for (int b = 0; b < n; ++b) {
+    const double* plane = x + ((long)b * c + i) * h * w;
+    const double* d = dz + ((long)b * oc + o) * oh * ow;
+    for (int y = 0; y < oh; ++y)
+      for (int xo = 0; xo < ow; ++xo)
+        acc += d[(long)y * ow + xo] * pix(plane, h, w, y * s + kh - p, xo * s + kw - p);
+  }
+  return acc;
+}
+
+/* Bias gradient, backward_bias ([P1] section 3.1 / section 4; Caffe
+ * backward_cpu_bias in [P2] layer 4): db[o] += sum_{n,ho,wo} dz[n,o,ho,wo]. */
+void orc_conv_backward_bias(int n, int oc, long ohw, const double* dz, double* db) {
+#pragma omp parallel for schedule(static)
+  for (int o = 0; o < oc; ++o) {
+    double acc = 0.0;
+    for (int b = 0; b < n; ++b)
+      for (long i = 0; i < ohw; ++i) acc += dz[((long)b * oc + o) * ohw + i];
+    db[o] += acc;
+  }
+}
+
+/* Input gradient: the gemm(1,0,...) W^T x delta of backward_convolutional_layer
+ * followed by col2im_cpu, which ADDS every column value back at the pixel
+ * im2col read it from ([P1] section 3.2).  Written as that scatter, without the
+ * column buffer: for every (o, ho, wo, kh, kw),
+ *   dx[n,i,ho*s+kh-p,wo*s+kw-p] += W[o,i,kh,kw] * dz[n,o,ho,wo]  (in-image taps only).
+ * Each (n,i) plane is owned by one thread; within it the contributions are
+ * added in (o, ho, wo, kh, kw) order. */
+void orc_conv_backward_data(int n, int c, int h, int w, int oc, int k, int s, int p,
+                            const double* wt, const double* dz, double* dx) {
+  const int oh = orc_conv_out_dim(h, k, s, p), ow = orc_conv_out_dim(w, k, s, p);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < n; ++b)
+    for (int i = 0; i < c; ++i) {
+      double* plane = dx + ((long)b * c + i) * h * w;
+      for (int o = 0; o < oc; ++o) {
+        const double* d = dz + ((long)b * oc + o) * oh * ow;
+        for (int y = 0; y < oh; ++y)
+          for (int xo = 0; xo < ow; ++xo) {
+            const double dv = d[(long)y * ow + xo];
+            for (int kh = 0; kh < k; ++kh)
+              for (int kw = 0; kw < k; ++kw) {
+                const int row = y * s + kh - p, col = xo * s + kw - p;
+                if (row < 0 || col < 0 || row >= h || col >= w) continue;
+                plane[(long)row * w + col] += wt[(((long)o * c + i) * k + kh) * k + kw] * dv;
+              }
+          }
+      }
+    }
+}
+
+/* One input-gradient element: the same sum, collected at a single pixel
+ * (all (o, ho, wo, kh, kw) whose tap lands on (row, col)), not accumulated. */
+double orc_conv_dx_at(int n, int c, int h, int w, int oc, int k, int s, int p, const double* wt,
+                      const double* dz, int b, int i, int row, int col) {
+  const int oh = orc_conv_out_dim(h, k, s, p), ow = orc_conv_out_dim(w, k, s, p);
+  (void)n;
+  double acc = 0.0;
+  for (int o = 0; o < oc; ++o) {
+    const double* d = dz + ((long)b * oc + o) * oh * ow;
+    for (int kh = 0; kh < k; ++kh)
+      for (int kw = 0; kw < k; ++kw) {
+        const int ty = row + p - kh, tx = col + p - kw;
+        if (ty < 0 || tx < 0 || ty % s || tx % s) continue;
+        const int y = ty / s, xo = tx / s;
+        if (y >= oh || xo >= ow) continue;
+        acc += wt[(((long)o * c + i) * k + kh) * k + kw] * d[(long)y * ow + xo];
+      }
+  }
+  return acc;
+}
+
+/* ------------------------------------------------------------------ */
+/* max pooling                                                         */
+/* ------------------------------------------------------------------ */
+
+/* Forward max pool (square window k, stride s, no padding); idx holds the
+ * per-plane flat index h*W+w of the winner, the mask Caffe's backward reads
+ * ([P2] layer 5).  Ties: first maximum in row-major window order. */
+void orc_maxpool_forward(int n, int c, int h, int w, int k, int s, const double* x, double* y,
+                         int* idx) {
+  const int oh = (h - k) / s + 1, ow = (w - k) / s + 1;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < n; ++b)
+    for (int ch = 0; ch < c; ++ch) {
+      const double* plane = x + ((long)b * c + ch) * h * w;
+      for (int py = 0; py < oh; ++py)
+        for (int px = 0; px < ow; ++px) {
+          int best = -1;
+          double bv = 0.0;
+          for (int ky = 0; ky < k; ++ky)
+            for (int kx = 0; kx < k; ++kx) {
+              const int r = py * s + ky, q = px * s + kx;
+              const double v = plane[(long)r * w + q];
+              if (best < 0 || v > bv) { best = r * w + q; bv = v; }
+            }
+          const long o = (((long)b * c + ch) * oh + py) * ow + px;
+          y[o] = bv;
+          idx[o] = best;
+        }
+    }
+}
+
+/* Max-pool backward ([P2] layer 5): clear bottom_diff, then for every pooled
+ * output add its top_diff at the bottom position its mask names. */
+void orc_maxpool_backward(int n, int c, int ih, int iw, int oh, int ow, const int* idx,
+                          const double* delta, double* dx) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < n; ++b)
+    for (int ch = 0; ch < c; ++ch) {
+      double* plane = dx + ((long)b * c + ch) * ih * iw;
+      const long base = ((long)b * c + ch) * oh * ow;
+      for (long i = 0; i < (long)ih * iw; ++i) plane[i] = 0.0;
+      for (long j = 0; j < (long)oh * ow; ++j) plane[idx[base + j]] += delta[base + j];
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* inner product and softmax loss                                      */
+/* ------------------------------------------------------------------ */
+
+/* y[b,o] = sum_i x[b,i] * W[o,i] + bias[o]  (InnerProduct, [P2] layer 8). */
+void orc_fc_forward(int batch, int in, int out, const double* x, const double* wt,
+                    const double* bias, double* y) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int b = 0; b < batch; ++b)
+    for (int o = 0; o < out; ++o) {
+      double acc = bias ? bias[o] : 0.0;
+      for (int i = 0; i < in; ++i) acc += x[(long)b * in + i] * wt[(long)o * in + i];
+      y[(long)b * out + o] = acc;
+    }
+}
+
+/* InnerProduct Backward ([P2] layer 8):
+ *   dW (out x in)  += delta^T (out x batch) * X (batch x in)     (gemm T,N, beta 1)
+ *   db (out)       += delta^T * ones                              (gemv, beta 1)
+ *   dX (batch x in) = delta (batch x out) * W (out x in)          (gemm N,N, beta 0)
+ * dx may be NULL (bottom not propagated); dx_accumulate adds instead of
+ * overwriting. */
+void orc_fc_backward(int batch, int in, int out, const double* x, const double* wt,
+                     const double* delta, double* dw, double* db, double* dx, int dx_accumulate) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int o = 0; o < out; ++o)
+    for (int i = 0; i < in; ++i) {
+      double acc = 0.0;
+      for (int b = 0; b < batch; ++b) acc += delta[(long)b * out + o] * x[(long)b * in + i];
+      dw[(long)o * in + i] += acc;
+    }
+  if (db)
+    for (int o = 0; o < out; ++o) {
+      double acc = 0.0;
+      for (int b = 0; b < batch; ++b) acc += delta[(long)b * out + o];
+      db[o] += acc;
+    }
+  if (dx) {
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int b = 0; b < batch; ++b)
+      for (int i = 0; i < in; ++i) {
+        double acc = 0.0;
+        for (int o = 0; o < out; ++o) acc += delta[(long)b * out + o] * wt[(long)o * in + i];
+        dx[(long)b * in + i] = (dx_accumulate ? dx[(long)b * in + i] : 0.0) + acc;
+      }
+  }
+}
+
+/* Softmax over the class axis (Caffe SoftmaxLayer Forward, [P4]: subtract the
+ * row max, exponentiate, divide by the row sum). */
+void orc_softmax_forward(int batch, int classes, const double* logits, double* prob) {
+  for (int b = 0; b < batch; ++b) {
+    const double* r = logits + (long)b * classes;
+    double mx = r[0];
+    for (int j = 1; j < classes; ++j) mx = r[j] > mx ? r[j] : mx;
+    double sum = 0.0;
+    for (int j = 0; j < classes; ++j) sum += exp(r[j] - mx);
+    for (int j = 0; j < classes; ++j) prob[(long)b * classes + j] = exp(r[j] - mx) / sum;
+  }
+}
+
+/* Mean cross-entropy of the softmax, the loss SoftmaxWithLoss reports. */
+double orc_softmax_loss(int batch, int classes, const double* prob, const int* labels) {
+  double l = 0.0;
+  for (int b = 0; b < batch; ++b) l -= log(prob[(long)b * classes + labels[b]]);
+  return l / batch;
+}
+
+/* SoftmaxWithLoss Backward ([P2] layer 9): copy prob into the bottom diff,
+ * subtract 1 at each sample's label, scale by loss_weight / count (count =
+ * number of labelled samples = batch here, one label per sample). */
+void orc_softmax_loss_backward(int batch, int classes, const double* prob, const int* labels,
+                               double loss_weight, double* dlogits) {
+  for (long i = 0; i < (long)batch * classes; ++i) dlogits[i] = prob[i];
+  for (int b = 0; b < batch; ++b) dlogits[(long)b * classes + labels[b]] -= 1.0;
+  const double scale = loss_weight / batch;
+  for (long i = 0; i < (long)batch * classes; ++i) dlogits[i] *= scale;
+}
+
+/* ------------------------------------------------------------------ */
+/* shortcut, route, upsample                                           */
+/* ------------------------------------------------------------------ */
+
+/* backward_shortcut_layer for equal shapes ([P1] section 5): the delta goes
+ * to the previous layer with weight alpha (axpy) and to the shortcut source
+ * with weight beta (shortcut_cpu with s1 = 1, s2 = beta). */
+void orc_shortcut_backward(long count, double alpha, double beta, const double* delta,
+                           double* d_main, double* d_from) {
+#pragma omp parallel for schedule(static)
+  for (long i = 0; i < count; ++i) {
+    d_main[i] += alpha * delta[i];
+    d_from[i] = 1.0 * d_from[i] + beta * delta[i];
+  }
+}
+
+/* backward_route_layer ([P1] section 6): for input t and image j, add the
+ * slice [offset_t + j*outputs, +in_sizes[t]) of the route delta into that
+ * input's delta at j*in_sizes[t]; offsets advance by in_sizes[t]. */
+void orc_route_backward(int batch, int n_in, const long* in_sizes, const double* delta,
+                        double** d_in) {
+  long outputs = 0;
+  for (int t = 0; t < n_in; ++t) outputs += in_sizes[t];
+  long offset = 0;
+  for (int t = 0; t < n_in; ++t) {
+    for (int j = 0; j < batch; ++j)
+      for (long e = 0; e < in_sizes[t]; ++e)
+        d_in[t][(long)j * in_sizes[t] + e] += delta[offset + (long)j * outputs + e];
+    offset += in_sizes[t];
+  }
+}
+
+/* Nearest-neighbour upsample by `scale` (the pages do not show it; its
+ * plain definition): y[n,c,h,w] = x[n,c,h/scale,w/scale]. */
+void orc_upsample_forward(int n, int c, int h, int w, int scale, const double* x, double* y) {
+  const int H = h * scale, W = w * scale;
+  for (long pl = 0; pl < (long)n * c; ++pl)
+    for (int r = 0; r < H; ++r)
+      for (int q = 0; q < W; ++q)
+        y[(pl * H + r) * W + q] = x[(pl * h + r / scale) * w + q / scale];
+}
+
+/* Its adjoint: each small pixel collects the scale x scale block of the big
+ * delta, dx[n,c,h,w] += sum_{a,b<scale} delta[n,c,h*scale+a,w*scale+b]. */
+void orc_upsample_backward(int n, int c, int h, int w, int scale, const double* delta,
+                           double* dx) {
+  const int H = h * scale, W = w * scale;
+#pragma omp parallel for schedule(static)
+  for (long pl = 0; pl < (long)n * c; ++pl)
+    for (int r = 0; r < h; ++r)
+      for (int q = 0; q < w; ++q) {
+        double acc = 0.0;
+        for (int a = 0; a < scale; ++a)
+          for (int b = 0; b < scale; ++b)
+            acc += delta[(pl * H + r * scale + a) * W + q * scale + b];
+        dx[(pl * h + r) * w + q] += acc;
+      }
+}
