@@ -1,0 +1,282 @@
+"""Thin ctypes binding of libcbb.so (C ABI in include/cbb.h).
+
+Argument marshalling only: every function here checks that tensors are CUDA
+(HIP) float32/int32 contiguous tensors, passes their device pointers and the
+current HIP stream to the ``cbb_*`` entry point of the same name, and raises
+``CbbError`` on a non-zero status.  No arithmetic of the backward pass runs in
+Python; there is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcbb.so")
+
+ACT = {"linear": 0, "leaky": 1, "logistic": 2, "relu": 3}
+STATUS = {0: "CBB_OK", -1: "CBB_EINVAL", -2: "CBB_ESHAPE", -3: "CBB_EUNSUPPORTED",
+          -4: "CBB_EWORKSPACE", -5: "CBB_EHIP"}
+WORKSPACE_ALIGN = 256
+
+
+class CbbError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({text})")
+        self.status = status
+
+
+class ConvDesc(ctypes.Structure):
+    """cbb_conv_desc."""
+    _fields_ = [("batch", ctypes.c_int32), ("in_c", ctypes.c_int32), ("in_h", ctypes.c_int32),
+                ("in_w", ctypes.c_int32), ("out_c", ctypes.c_int32), ("ksize", ctypes.c_int32),
+                ("stride", ctypes.c_int32), ("pad", ctypes.c_int32),
+                ("batch_normalize", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("slope", ctypes.c_float), ("bn_eps", ctypes.c_float)]
+
+    @property
+    def out_h(self) -> int:
+        return (self.in_h + 2 * self.pad - self.ksize) // self.stride + 1
+
+    @property
+    def out_w(self) -> int:
+        return (self.in_w + 2 * self.pad - self.ksize) // self.stride + 1
+
+
+def conv_desc(batch, in_c, in_h, in_w, out_c, ksize, stride, pad, batch_normalize, act,
+              slope=0.1, bn_eps=1e-5) -> ConvDesc:
+    a = ACT[act] if isinstance(act, str) else int(act)
+    return ConvDesc(batch, in_c, in_h, in_w, out_c, ksize, stride, pad, int(batch_normalize), a,
+                    slope, bn_eps)
+
+
+_P = ctypes.c_void_p
+_i32, _i64, _f, _sz = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "cbb_abi_version": ([], _i32),
+    "cbb_status_string": ([_i32], ctypes.c_char_p),
+    "cbb_last_error": ([], ctypes.c_char_p),
+    "cbb_conv_block_workspace_size": ([ctypes.POINTER(ConvDesc), ctypes.POINTER(_sz)], _i32),
+    "cbb_conv_block_backward": ([ctypes.POINTER(ConvDesc)] + [_P] * 12 + [_i32, _P, _sz, _P], _i32),
+    "cbb_conv_act_bn_backward": ([ctypes.POINTER(ConvDesc)] + [_P] * 8 + [_P, _sz, _P], _i32),
+    "cbb_conv_backward_weights": ([ctypes.POINTER(ConvDesc), _P, _P, _P, _P, _sz, _P], _i32),
+    "cbb_conv_backward_data": ([ctypes.POINTER(ConvDesc), _P, _P, _P, _i32, _P], _i32),
+    "cbb_act_backward": ([_i32, _f, _P, _P, _P, _i64, _P], _i32),
+    "cbb_bn_backward_workspace_size": ([_i32, _i32, _i64, ctypes.POINTER(_sz)], _i32),
+    "cbb_bn_backward": ([_i32, _i32, _i64, _f] + [_P] * 7 + [_P, _sz, _P], _i32),
+    "cbb_fc_backward": ([_i32, _i32, _i32] + [_P] * 6 + [_i32, _P], _i32),
+    "cbb_softmax_loss_backward": ([_i32, _i32, _P, _P, _f, _P, _P, _P], _i32),
+    "cbb_fc_softmax_backward": ([_i32, _i32, _i32, _P, _P, _f] + [_P] * 7 + [_P], _i32),
+    "cbb_shortcut_backward": ([_i64, _f, _f, _P, _P, _P, _P], _i32),
+    "cbb_route_backward": ([_i32, _i32, ctypes.POINTER(_i64), _P, ctypes.POINTER(_P), _P], _i32),
+    "cbb_upsample_backward": ([_i32] * 5 + [_P, _P, _P], _i32),
+    "cbb_maxpool_backward": ([_i32] * 6 + [_P, _P, _P, _P], _i32),
+}
+EXPORTS = tuple(_SIGS)
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libcbb.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m cnn_backward_pass_amd.build` (hipcc, gfx950)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        text = (lib().cbb_status_string(rc) or b"").decode()
+        raise CbbError(fn, rc, text)
+
+
+def _ptr(t: torch.Tensor | None, dtype=torch.float32, name: str = "tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must live on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def abi_version() -> int:
+    return lib().cbb_abi_version()
+
+
+def status_string(status: int) -> str:
+    return (lib().cbb_status_string(status) or b"").decode()
+
+
+def last_error() -> str:
+    return (lib().cbb_last_error() or b"").decode()
+
+
+def workspace(nbytes: int, device="cuda") -> torch.Tensor | None:
+    """A device byte buffer usable as a cbb workspace (torch allocations are 256-byte aligned)."""
+    if nbytes == 0:
+        return None
+    buf = torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+    assert buf.data_ptr() % WORKSPACE_ALIGN == 0
+    return buf
+
+
+def _ws(buf: torch.Tensor | None):
+    if buf is None:
+        return None, 0
+    return _ptr(buf, torch.uint8, "workspace"), buf.numel()
+
+
+# ----------------------------------------------------------------------------- entry points
+def conv_block_workspace_size(desc: ConvDesc) -> int:
+    n = ctypes.c_size_t(0)
+    _check("cbb_conv_block_workspace_size",
+           lib().cbb_conv_block_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def conv_block_backward(desc: ConvDesc, x, w, y, x_norm, var, gamma, delta, dz, dw, db, dgamma,
+                        dx, dx_accumulate: bool = False, workspace=None, stream=None) -> None:
+    wsp, wsb = _ws(workspace)
+    _check("cbb_conv_block_backward", lib().cbb_conv_block_backward(
+        ctypes.byref(desc), _ptr(x, name="x"), _ptr(w, name="w"), _ptr(y, name="y"),
+        _ptr(x_norm, name="x_norm"), _ptr(var, name="var"), _ptr(gamma, name="gamma"),
+        _ptr(delta, name="delta"), _ptr(dz, name="dz"), _ptr(dw, name="dw"),
+        _ptr(db, name="db"), _ptr(dgamma, name="dgamma"), _ptr(dx, name="dx"),
+        int(dx_accumulate), wsp, wsb, _stream(stream)))
+
+
+def conv_act_bn_backward(desc: ConvDesc, y, x_norm, var, gamma, delta, dz, db, dgamma,
+                         workspace=None, stream=None) -> None:
+    wsp, wsb = _ws(workspace)
+    _check("cbb_conv_act_bn_backward", lib().cbb_conv_act_bn_backward(
+        ctypes.byref(desc), _ptr(y, name="y"), _ptr(x_norm, name="x_norm"), _ptr(var, name="var"),
+        _ptr(gamma, name="gamma"), _ptr(delta, name="delta"), _ptr(dz, name="dz"),
+        _ptr(db, name="db"), _ptr(dgamma, name="dgamma"), wsp, wsb, _stream(stream)))
+
+
+def conv_backward_weights(desc: ConvDesc, x, dz, dw, workspace=None, stream=None) -> None:
+    wsp, wsb = _ws(workspace)
+    _check("cbb_conv_backward_weights", lib().cbb_conv_backward_weights(
+        ctypes.byref(desc), _ptr(x, name="x"), _ptr(dz, name="dz"), _ptr(dw, name="dw"), wsp, wsb,
+        _stream(stream)))
+
+
+def conv_backward_data(desc: ConvDesc, w, dz, dx, dx_accumulate: bool = False,
+                       stream=None) -> None:
+    _check("cbb_conv_backward_data", lib().cbb_conv_backward_data(
+        ctypes.byref(desc), _ptr(w, name="w"), _ptr(dz, name="dz"), _ptr(dx, name="dx"),
+        int(dx_accumulate), _stream(stream)))
+
+
+def act_backward(act, slope: float, y, delta, g, stream=None) -> None:
+    a = ACT[act] if isinstance(act, str) else int(act)
+    if not (y.numel() == delta.numel() == g.numel()):
+        raise ValueError("act_backward: y, delta, g must have the same number of elements")
+    _check("cbb_act_backward", lib().cbb_act_backward(
+        a, slope, _ptr(y, name="y"), _ptr(delta, name="delta"), _ptr(g, name="g"), delta.numel(),
+        _stream(stream)))
+
+
+def bn_backward_workspace_size(n: int, c: int, hw: int) -> int:
+    b = ctypes.c_size_t(0)
+    _check("cbb_bn_backward_workspace_size",
+           lib().cbb_bn_backward_workspace_size(n, c, hw, ctypes.byref(b)))
+    return b.value
+
+
+def bn_backward(g, x_norm, var, gamma, dz, dgamma, dbeta, eps: float = 1e-5, workspace=None,
+                stream=None) -> None:
+    n, c = g.shape[0], g.shape[1]
+    hw = g.numel() // (n * c)
+    wsp, wsb = _ws(workspace)
+    _check("cbb_bn_backward", lib().cbb_bn_backward(
+        n, c, hw, eps, _ptr(g, name="g"), _ptr(x_norm, name="x_norm"), _ptr(var, name="var"),
+        _ptr(gamma, name="gamma"), _ptr(dz, name="dz"), _ptr(dgamma, name="dgamma"),
+        _ptr(dbeta, name="dbeta"), wsp, wsb, _stream(stream)))
+
+
+def fc_backward(x, w, delta, dw, db, dx, dx_accumulate: bool = False, stream=None) -> None:
+    batch, in_dim = x.shape
+    out_dim = w.shape[0]
+    _check("cbb_fc_backward", lib().cbb_fc_backward(
+        batch, in_dim, out_dim, _ptr(x, name="x"), _ptr(w, name="w"), _ptr(delta, name="delta"),
+        _ptr(dw, name="dw"), _ptr(db, name="db"), _ptr(dx, name="dx"), int(dx_accumulate),
+        _stream(stream)))
+
+
+def softmax_loss_backward(prob, labels, dlogits, loss_weight: float = 1.0, bad_labels=None,
+                          stream=None) -> None:
+    batch, classes = prob.shape
+    _check("cbb_softmax_loss_backward", lib().cbb_softmax_loss_backward(
+        batch, classes, _ptr(prob, name="prob"), _ptr(labels, torch.int32, "labels"), loss_weight,
+        _ptr(dlogits, name="dlogits"), _ptr(bad_labels, torch.int32, "bad_labels"),
+        _stream(stream)))
+
+
+def fc_softmax_backward(prob, labels, x, w, dlogits, dw, db, dx, loss_weight: float = 1.0,
+                        bad_labels=None, stream=None) -> None:
+    batch, classes = prob.shape
+    in_dim = x.shape[1]
+    _check("cbb_fc_softmax_backward", lib().cbb_fc_softmax_backward(
+        batch, in_dim, classes, _ptr(prob, name="prob"), _ptr(labels, torch.int32, "labels"),
+        loss_weight, _ptr(x, name="x"), _ptr(w, name="w"), _ptr(dlogits, name="dlogits"),
+        _ptr(dw, name="dw"), _ptr(db, name="db"), _ptr(dx, name="dx"),
+        _ptr(bad_labels, torch.int32, "bad_labels"), _stream(stream)))
+
+
+def shortcut_backward(delta, d_main, d_from, alpha: float = 1.0, beta: float = 1.0,
+                      stream=None) -> None:
+    if not (delta.numel() == d_main.numel() == d_from.numel()):
+        raise ValueError("shortcut_backward: equal shapes only")
+    _check("cbb_shortcut_backward", lib().cbb_shortcut_backward(
+        delta.numel(), alpha, beta, _ptr(delta, name="delta"), _ptr(d_main, name="d_main"),
+        _ptr(d_from, name="d_from"), _stream(stream)))
+
+
+def route_backward(delta, d_ins: Sequence[torch.Tensor], stream=None) -> None:
+    batch = delta.shape[0]
+    sizes = (ctypes.c_int64 * len(d_ins))(*[t.numel() // batch for t in d_ins])
+    ptrs = (ctypes.c_void_p * len(d_ins))(*[_ptr(t, name="d_in").value for t in d_ins])
+    _check("cbb_route_backward", lib().cbb_route_backward(
+        batch, len(d_ins), sizes, _ptr(delta, name="delta"), ptrs, _stream(stream)))
+
+
+def upsample_backward(delta, dx, scale: int = 2, stream=None) -> None:
+    n, c, h, w = dx.shape
+    if tuple(delta.shape) != (n, c, h * scale, w * scale):
+        raise ValueError("upsample_backward: delta must be dx's shape times scale")
+    _check("cbb_upsample_backward", lib().cbb_upsample_backward(
+        n, c, h, w, scale, _ptr(delta, name="delta"), _ptr(dx, name="dx"), _stream(stream)))
+
+
+def maxpool_backward(idx, delta, dx, ksize: int = 2, stride: int = 2, stream=None) -> None:
+    n, c, ih, iw = dx.shape
+    oh, ow = (ih - ksize) // stride + 1, (iw - ksize) // stride + 1
+    if tuple(delta.shape) != (n, c, oh, ow) or tuple(idx.shape) != (n, c, oh, ow):
+        raise ValueError("maxpool_backward: delta/idx shape does not match the pooled shape")
+    _check("cbb_maxpool_backward", lib().cbb_maxpool_backward(
+        n, c, ih, iw, ksize, stride, _ptr(idx, torch.int32, "idx"), _ptr(delta, name="delta"),
+        _ptr(dx, name="dx"), _stream(stream)))

@@ -1,0 +1,276 @@
+// cbb_api.hip -- the extern "C" entry points of libcbb.so: argument checks on
+// the host (before any HIP call), workspace carving, and kernel enqueue on the
+// caller's stream.  See include/cbb.h for the contract of every call.
+#include <cstdio>
+#include <cstring>
+
+#include "cbb_internal.h"
+
+namespace cbb {
+
+static thread_local char g_err[512] = "";
+
+void set_hip_error(hipError_t e, const char* where) {
+  snprintf(g_err, sizeof g_err, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+int check_launch(const char* where) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_hip_error(e, where);
+    return CBB_EHIP;
+  }
+  return CBB_OK;
+}
+
+}  // namespace cbb
+
+using namespace cbb;
+
+namespace {
+
+constexpr int64_t kMaxIndex = (int64_t)1 << 31;  // per-tensor element counts must index in int32
+constexpr size_t kAlign = 256;
+
+inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+struct ConvPlan {
+  int64_t oh, ow;
+  size_t part_bytes, dw_bytes, total;
+};
+
+int check_desc(const cbb_conv_desc* d, ConvPlan* plan) {
+  if (!d) return CBB_EINVAL;
+  if (d->batch < 1 || d->in_c < 1 || d->in_h < 1 || d->in_w < 1 || d->out_c < 1 ||
+      d->ksize < 1 || d->stride < 1 || d->pad < 0)
+    return CBB_EINVAL;
+  if (d->act < CBB_ACT_LINEAR || d->act > CBB_ACT_RELU) return CBB_EINVAL;
+  if (d->batch_normalize != 0 && d->batch_normalize != 1) return CBB_EINVAL;
+  if (d->batch_normalize && !(d->bn_eps > 0.f)) return CBB_EINVAL;
+  if (d->ksize > 7 || d->stride > 4 || d->pad >= d->ksize) return CBB_EUNSUPPORTED;
+  const int64_t oh = ((int64_t)d->in_h + 2 * d->pad - d->ksize) / d->stride + 1;
+  const int64_t ow = ((int64_t)d->in_w + 2 * d->pad - d->ksize) / d->stride + 1;
+  if ((int64_t)d->in_h + 2 * d->pad < d->ksize || (int64_t)d->in_w + 2 * d->pad < d->ksize ||
+      oh < 1 || ow < 1)
+    return CBB_ESHAPE;
+  const int64_t nx = (int64_t)d->batch * d->in_c * d->in_h * d->in_w;
+  const int64_t ny = (int64_t)d->batch * d->out_c * oh * ow;
+  const int64_t nw = (int64_t)d->out_c * d->in_c * d->ksize * d->ksize;
+  if (nx >= kMaxIndex || ny >= kMaxIndex || nw >= kMaxIndex) return CBB_EUNSUPPORTED;
+  if (plan) {
+    plan->oh = oh;
+    plan->ow = ow;
+    const ConvGeom g = make_geom(*d);
+    plan->part_bytes = align_up(actbn_workspace(d->batch, d->out_c, oh * ow), kAlign);
+    plan->dw_bytes = align_up(conv_dw_workspace(g), kAlign);
+    plan->total = plan->part_bytes + plan->dw_bytes;
+  }
+  return CBB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cbb_abi_version(void) { return CBB_ABI_VERSION; }
+
+const char* cbb_last_error(void) { return g_err; }
+
+const char* cbb_status_string(int status) {
+  switch (status) {
+    case CBB_OK: return "ok";
+    case CBB_EINVAL: return "invalid argument (NULL pointer, non-positive size or bad enum)";
+    case CBB_ESHAPE: return "inconsistent or empty shape";
+    case CBB_EUNSUPPORTED: return "unsupported configuration";
+    case CBB_EWORKSPACE: return "workspace missing or too small";
+    case CBB_EHIP: return g_err[0] ? g_err : "HIP error";
+  }
+  return "unknown status";
+}
+
+int cbb_conv_block_workspace_size(const cbb_conv_desc* desc, size_t* bytes) {
+  if (!bytes) return CBB_EINVAL;
+  ConvPlan p;
+  const int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  *bytes = p.total;
+  return CBB_OK;
+}
+
+int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const float* w,
+                            const float* y, const float* x_norm, const float* var,
+                            const float* gamma, const float* delta, float* dz, float* dw,
+                            float* db, float* dgamma, float* dx, int dx_accumulate,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  ConvPlan p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  const int bn = desc->batch_normalize, act = desc->act;
+  if (!x || !w || !delta || !dw || !db) return CBB_EINVAL;
+  if (act != CBB_ACT_LINEAR && !y) return CBB_EINVAL;
+  if (bn && (!x_norm || !var || !gamma || !dgamma)) return CBB_EINVAL;
+  if (!bn && (x_norm || var || gamma || dgamma)) return CBB_EINVAL;
+  const bool passthrough = act == CBB_ACT_LINEAR && !bn;  // dz is delta itself
+  if (!passthrough && !dz) return CBB_EINVAL;
+  if (dx_accumulate != 0 && dx_accumulate != 1) return CBB_EINVAL;
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return CBB_EWORKSPACE;
+  if (workspace && ((uintptr_t)workspace % kAlign)) return CBB_EWORKSPACE;
+
+  hipStream_t st = S(stream);
+  char* ws = static_cast<char*>(workspace);
+  const float* dz_eff = passthrough ? delta : dz;
+  rc = launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
+                    var, gamma, desc->bn_eps, bn, passthrough ? nullptr : dz, dgamma, db, ws, st);
+  if (rc) return rc;
+  const ConvGeom g = make_geom(*desc);
+  rc = launch_conv_dw(g, x, dz_eff, dw, reinterpret_cast<float*>(ws + p.part_bytes), st);
+  if (rc) return rc;
+  if (dx) rc = launch_conv_dx(g, w, dz_eff, dx, dx_accumulate, st);
+  return rc;
+}
+
+int cbb_conv_act_bn_backward(const cbb_conv_desc* desc, const float* y, const float* x_norm,
+                             const float* var, const float* gamma, const float* delta, float* dz,
+                             float* db, float* dgamma, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  ConvPlan p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  const int bn = desc->batch_normalize, act = desc->act;
+  if (!delta || !db) return CBB_EINVAL;
+  if (act != CBB_ACT_LINEAR && !y) return CBB_EINVAL;
+  if (bn && (!x_norm || !var || !gamma || !dgamma)) return CBB_EINVAL;
+  if (!bn && (x_norm || var || gamma || dgamma)) return CBB_EINVAL;
+  const bool passthrough = act == CBB_ACT_LINEAR && !bn;
+  if (!passthrough && !dz) return CBB_EINVAL;
+  if (!workspace || workspace_bytes < p.total || ((uintptr_t)workspace % kAlign))
+    return CBB_EWORKSPACE;
+  return launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
+                      var, gamma, desc->bn_eps, bn, passthrough ? nullptr : dz, dgamma, db,
+                      workspace, S(stream));
+}
+
+int cbb_conv_backward_weights(const cbb_conv_desc* desc, const float* x, const float* dz,
+                              float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  ConvPlan p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  if (!x || !dz || !dw) return CBB_EINVAL;
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return CBB_EWORKSPACE;
+  if (workspace && ((uintptr_t)workspace % kAlign)) return CBB_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  return launch_conv_dw(make_geom(*desc), x, dz, dw,
+                        reinterpret_cast<float*>(ws ? ws + p.part_bytes : nullptr), S(stream));
+}
+
+int cbb_conv_backward_data(const cbb_conv_desc* desc, const float* w, const float* dz, float* dx,
+                           int dx_accumulate, void* stream) {
+  int rc = check_desc(desc, nullptr);
+  if (rc) return rc;
+  if (!w || !dz || !dx) return CBB_EINVAL;
+  if (dx_accumulate != 0 && dx_accumulate != 1) return CBB_EINVAL;
+  return launch_conv_dx(make_geom(*desc), w, dz, dx, dx_accumulate, S(stream));
+}
+
+int cbb_act_backward(int act, float slope, const float* y, const float* delta, float* g,
+                     int64_t count, void* stream) {
+  if (act < CBB_ACT_LINEAR || act > CBB_ACT_RELU) return CBB_EINVAL;
+  if (count < 0 || !y || !delta || !g) return CBB_EINVAL;
+  if (count == 0) return CBB_OK;
+  return launch_act_backward(act, slope, y, delta, g, count, S(stream));
+}
+
+int cbb_bn_backward_workspace_size(int n, int c, int64_t hw, size_t* bytes) {
+  if (!bytes || n < 1 || c < 1 || hw < 1) return CBB_EINVAL;
+  if ((int64_t)n * c * hw >= kMaxIndex) return CBB_EUNSUPPORTED;
+  *bytes = align_up(actbn_workspace(n, c, hw), kAlign);
+  return CBB_OK;
+}
+
+int cbb_bn_backward(int n, int c, int64_t hw, float eps, const float* g, const float* x_norm,
+                    const float* var, const float* gamma, float* dz, float* dgamma, float* dbeta,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  int rc = cbb_bn_backward_workspace_size(n, c, hw, &need);
+  if (rc) return rc;
+  if (!(eps > 0.f) || !g || !x_norm || !var || !gamma || !dz || !dgamma || !dbeta)
+    return CBB_EINVAL;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign))
+    return CBB_EWORKSPACE;
+  return launch_actbn(n, c, hw, g, nullptr, x_norm, CBB_ACT_LINEAR, 0.f, var, gamma, eps, 1, dz,
+                      dgamma, dbeta, workspace, S(stream));
+}
+
+int cbb_fc_backward(int batch, int in_dim, int out_dim, const float* x, const float* w,
+                    const float* delta, float* dw, float* db, float* dx, int dx_accumulate,
+                    void* stream) {
+  if (batch < 1 || in_dim < 1 || out_dim < 1 || !x || !w || !delta || !dw) return CBB_EINVAL;
+  if (dx_accumulate != 0 && dx_accumulate != 1) return CBB_EINVAL;
+  if ((int64_t)batch * in_dim >= kMaxIndex || (int64_t)out_dim * in_dim >= kMaxIndex ||
+      (int64_t)batch * out_dim >= kMaxIndex)
+    return CBB_EUNSUPPORTED;
+  return launch_fc(batch, in_dim, out_dim, x, w, delta, dw, db, dx, dx_accumulate, S(stream));
+}
+
+int cbb_softmax_loss_backward(int batch, int classes, const float* prob, const int32_t* labels,
+                              float loss_weight, float* dlogits, int32_t* bad_labels,
+                              void* stream) {
+  if (batch < 1 || classes < 1 || !prob || !labels || !dlogits) return CBB_EINVAL;
+  if ((int64_t)batch * classes >= kMaxIndex) return CBB_EUNSUPPORTED;
+  return launch_softmax_loss(batch, classes, prob, labels, loss_weight, dlogits, bad_labels,
+                             S(stream));
+}
+
+int cbb_fc_softmax_backward(int batch, int in_dim, int classes, const float* prob,
+                            const int32_t* labels, float loss_weight, const float* x,
+                            const float* w, float* dlogits, float* dw, float* db, float* dx,
+                            int32_t* bad_labels, void* stream) {
+  if (batch < 1 || in_dim < 1 || classes < 1 || !prob || !labels || !x || !w || !dlogits || !dw)
+    return CBB_EINVAL;
+  if ((int64_t)batch * in_dim >= kMaxIndex || (int64_t)classes * in_dim >= kMaxIndex ||
+      (int64_t)batch * classes >= kMaxIndex)
+    return CBB_EUNSUPPORTED;
+  int rc = launch_softmax_loss(batch, classes, prob, labels, loss_weight, dlogits, bad_labels,
+                               S(stream));
+  if (rc) return rc;
+  return launch_fc(batch, in_dim, classes, x, w, dlogits, dw, db, dx, 0, S(stream));
+}
+
+int cbb_shortcut_backward(int64_t count, float alpha, float beta, const float* delta,
+                          float* d_main, float* d_from, void* stream) {
+  if (count < 0 || !delta || !d_main || !d_from) return CBB_EINVAL;
+  if (d_main == d_from || d_main == delta || d_from == delta) return CBB_EINVAL;
+  if (count == 0) return CBB_OK;
+  return launch_shortcut(count, alpha, beta, delta, d_main, d_from, S(stream));
+}
+
+int cbb_route_backward(int batch, int n_in, const int64_t* in_sizes, const float* delta,
+                       float* const* d_in, void* stream) {
+  if (batch < 1 || n_in < 1 || n_in > 8 || !in_sizes || !delta || !d_in) return CBB_EINVAL;
+  int64_t outputs = 0;
+  for (int t = 0; t < n_in; ++t) {
+    if (in_sizes[t] < 1 || !d_in[t]) return CBB_EINVAL;
+    outputs += in_sizes[t];
+  }
+  if (outputs * batch >= kMaxIndex) return CBB_EUNSUPPORTED;
+  return launch_route(batch, n_in, in_sizes, delta, d_in, S(stream));
+}
+
+int cbb_upsample_backward(int n, int c, int h, int w, int scale, const float* delta, float* dx,
+                          void* stream) {
+  if (n < 1 || c < 1 || h < 1 || w < 1 || scale < 1 || !delta || !dx) return CBB_EINVAL;
+  if (scale > 8) return CBB_EUNSUPPORTED;
+  if ((int64_t)n * c * h * w * scale * scale >= kMaxIndex) return CBB_EUNSUPPORTED;
+  return launch_upsample(n, c, h, w, scale, delta, dx, S(stream));
+}
+
+int cbb_maxpool_backward(int n, int c, int ih, int iw, int ksize, int stride,
+                         const int32_t* idx, const float* delta, float* dx, void* stream) {
+  if (n < 1 || c < 1 || ih < 1 || iw < 1 || ksize < 1 || stride < 1 || !idx || !delta || !dx)
+    return CBB_EINVAL;
+  if (ksize > ih || ksize > iw) return CBB_ESHAPE;
+  if ((int64_t)n * c * ih * iw >= kMaxIndex) return CBB_EUNSUPPORTED;
+  return launch_maxpool(n, c, ih, iw, ksize, stride, idx, delta, dx, S(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,289 @@
+// layers.hip -- the non-convolution steps of the backward pass: shortcut,
+// route, upsample, max-pool, softmax-with-loss and inner product.
+//
+// "YOLOv3 backpropagation: full-flow source analysis" (suzhouguqin.com):
+//   section 5 backward_shortcut_layer (axpy + shortcut_cpu, s1 = 1, s2 = beta),
+//   section 6 backward_route_layer (per input, per image axpy of a slice).
+// "Caffe source study ch.4 (5): the LeNet backward pass" (csdndocs.com):
+//   layer 9 SoftmaxWithLoss (prob - onehot, times loss_weight / count),
+//   layer 8 InnerProduct (dW += delta^T X, db += delta^T 1, dX = delta W),
+//   layer 5 Pooling MAX (bottom_diff = 0; bottom_diff[mask] += top_diff).
+#include "cbb_internal.h"
+
+namespace cbb {
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+static unsigned grid_for(int64_t work) {
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(work, kThreads), 16384));
+}
+
+// --------------------------------------------------------------- shortcut
+__global__ __launch_bounds__(kThreads) void shortcut_kernel(int64_t count, float alpha, float beta,
+                                                            const float* __restrict__ delta,
+                                                            float* __restrict__ d_main,
+                                                            float* __restrict__ d_from, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  int64_t tail = 0;
+  if (vec) {
+    const int64_t n4 = count >> 2;
+    for (int64_t i = i0; i < n4; i += stride) {
+      const float4 d = reinterpret_cast<const float4*>(delta)[i];
+      float4 m = reinterpret_cast<float4*>(d_main)[i];
+      float4 f = reinterpret_cast<float4*>(d_from)[i];
+      m.x += alpha * d.x; m.y += alpha * d.y; m.z += alpha * d.z; m.w += alpha * d.w;
+      f.x += beta * d.x;  f.y += beta * d.y;  f.z += beta * d.z;  f.w += beta * d.w;
+      reinterpret_cast<float4*>(d_main)[i] = m;
+      reinterpret_cast<float4*>(d_from)[i] = f;
+    }
+    tail = 4 * n4;
+  }
+  for (int64_t i = tail + i0; i < count; i += stride) {
+    d_main[i] += alpha * delta[i];
+    d_from[i] += beta * delta[i];
+  }
+}
+
+int launch_shortcut(int64_t count, float alpha, float beta, const float* delta, float* d_main,
+                    float* d_from, hipStream_t st) {
+  const int vec = aligned16(delta) && aligned16(d_main) && aligned16(d_from);
+  shortcut_kernel<<<grid_for(vec ? ceil_div(count, 4) : count), kThreads, 0, st>>>(
+      count, alpha, beta, delta, d_main, d_from, vec);
+  return check_launch("shortcut_kernel");
+}
+
+// --------------------------------------------------------------- route
+// d_in[j*size + e] += delta[offset + j*outputs + e], for all images j, e < size.
+__global__ __launch_bounds__(kThreads) void route_kernel(int batch, int64_t size, int64_t outputs,
+                                                         int64_t offset,
+                                                         const float* __restrict__ delta,
+                                                         float* __restrict__ d_in, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (vec) {
+    const int64_t s4 = size >> 2, total = (int64_t)batch * s4;
+    for (int64_t i = i0; i < total; i += stride) {
+      const int64_t j = i / s4, e4 = i - j * s4;
+      const float4 d =
+          *reinterpret_cast<const float4*>(delta + offset + j * outputs + 4 * e4);
+      float4* p = reinterpret_cast<float4*>(d_in + j * size) + e4;
+      float4 v = *p;
+      v.x += d.x; v.y += d.y; v.z += d.z; v.w += d.w;
+      *p = v;
+    }
+  } else {
+    const int64_t total = (int64_t)batch * size;
+    for (int64_t i = i0; i < total; i += stride) {
+      const int64_t j = i / size, e = i - j * size;
+      d_in[j * size + e] += delta[offset + j * outputs + e];
+    }
+  }
+}
+
+int launch_route(int batch, int n_in, const int64_t* sizes, const float* delta,
+                 float* const* d_in, hipStream_t st) {
+  int64_t outputs = 0;
+  for (int t = 0; t < n_in; ++t) outputs += sizes[t];
+  int64_t offset = 0;
+  for (int t = 0; t < n_in; ++t) {
+    const int vec = sizes[t] % 4 == 0 && outputs % 4 == 0 && offset % 4 == 0 &&
+                    aligned16(delta) && aligned16(d_in[t]);
+    const int64_t work = (int64_t)batch * (vec ? sizes[t] / 4 : sizes[t]);
+    route_kernel<<<grid_for(work), kThreads, 0, st>>>(batch, sizes[t], outputs, offset, delta,
+                                                      d_in[t], vec);
+    const int rc = check_launch("route_kernel");
+    if (rc) return rc;
+    offset += sizes[t];
+  }
+  return CBB_OK;
+}
+
+// --------------------------------------------------------------- upsample
+// dx[p, r, q] += sum_{a,b < scale} delta[p, r*scale + a, q*scale + b]; one thread per small pixel.
+__global__ __launch_bounds__(kThreads) void upsample_bwd_kernel(int64_t planes, int h, int w,
+                                                                int scale,
+                                                                const float* __restrict__ delta,
+                                                                float* __restrict__ dx) {
+  const int64_t total = planes * h * w;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const int W = w * scale;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
+    const int64_t pl = i / ((int64_t)h * w);
+    const int rq = (int)(i - pl * h * w);
+    const int r = rq / w, q = rq - r * w;
+    const float* src = delta + (pl * h * scale + (int64_t)r * scale) * W + (int64_t)q * scale;
+    float acc = 0.f;
+    for (int a = 0; a < scale; ++a)
+      for (int b = 0; b < scale; ++b) acc += src[(int64_t)a * W + b];
+    dx[i] += acc;
+  }
+}
+
+int launch_upsample(int n, int c, int h, int w, int scale, const float* delta, float* dx,
+                    hipStream_t st) {
+  const int64_t planes = (int64_t)n * c;
+  upsample_bwd_kernel<<<grid_for(planes * h * w), kThreads, 0, st>>>(planes, h, w, scale, delta,
+                                                                     dx);
+  return check_launch("upsample_bwd_kernel");
+}
+
+// --------------------------------------------------------------- max pool
+// Gather form: every bottom pixel sums, in (ph, pw) order, the deltas of the
+// windows that contain it and whose mask names it.  Writes every dx element
+// once (no separate clearing pass, no atomics).
+__global__ __launch_bounds__(kThreads) void maxpool_bwd_kernel(int64_t planes, int ih, int iw,
+                                                               int oh, int ow, int k, int s,
+                                                               const int* __restrict__ idx,
+                                                               const float* __restrict__ delta,
+                                                               float* __restrict__ dx) {
+  const int64_t total = planes * ih * iw;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
+    const int64_t pl = i / ((int64_t)ih * iw);
+    const int pix = (int)(i - pl * ih * iw);
+    const int h = pix / iw, w = pix - h * iw;
+    // windows ph with ph*s <= h <= ph*s + k - 1
+    const int ph0 = h >= k ? (h - k) / s + 1 : 0, ph1 = min(h / s, oh - 1);
+    const int pw0 = w >= k ? (w - k) / s + 1 : 0, pw1 = min(w / s, ow - 1);
+    const int64_t base = pl * oh * ow;
+    float acc = 0.f;
+    for (int ph = ph0; ph <= ph1; ++ph)
+      for (int pw = pw0; pw <= pw1; ++pw) {
+        const int64_t o = base + (int64_t)ph * ow + pw;
+        if (idx[o] == pix) acc += delta[o];
+      }
+    dx[i] = acc;
+  }
+}
+
+int launch_maxpool(int n, int c, int ih, int iw, int k, int s, const int32_t* idx,
+                   const float* delta, float* dx, hipStream_t st) {
+  const int oh = (ih - k) / s + 1, ow = (iw - k) / s + 1;
+  const int64_t planes = (int64_t)n * c;
+  maxpool_bwd_kernel<<<grid_for(planes * ih * iw), kThreads, 0, st>>>(planes, ih, iw, oh, ow, k,
+                                                                      s, idx, delta, dx);
+  return check_launch("maxpool_bwd_kernel");
+}
+
+// --------------------------------------------------------------- softmax loss
+__global__ __launch_bounds__(kThreads) void softmax_loss_bwd_kernel(
+    int batch, int classes, const float* __restrict__ prob, const int32_t* __restrict__ labels,
+    float scale, float* __restrict__ dlogits, int32_t* __restrict__ bad) {
+  const int64_t total = (int64_t)batch * classes;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
+    const int b = (int)(i / classes), j = (int)(i - (int64_t)b * classes);
+    const int lab = labels[b];
+    const bool valid = lab >= 0 && lab < classes;
+    float p = prob[i];
+    if (valid && j == lab) p -= 1.f;
+    dlogits[i] = p * scale;
+    if (!valid && j == 0 && bad) atomicAdd(bad, 1);
+  }
+}
+
+int launch_softmax_loss(int batch, int classes, const float* prob, const int32_t* labels,
+                        float loss_weight, float* dlogits, int32_t* bad, hipStream_t st) {
+  softmax_loss_bwd_kernel<<<grid_for((int64_t)batch * classes), kThreads, 0, st>>>(
+      batch, classes, prob, labels, loss_weight / (float)batch, dlogits, bad);
+  return check_launch("softmax_loss_bwd_kernel");
+}
+
+// --------------------------------------------------------------- inner product
+// C[m][n] (+)= sum_k A(m,k) B(k,n), A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn],
+// C[m*ldc + n].  64x64 tiles on the 32x32x2 fp32 matrix cores, K in steps of 32.
+struct GemmArgs {
+  int M, N, K;
+  const float* A;
+  int64_t sam, sak;
+  const float* B;
+  int64_t sbk, sbn;
+  float* C;
+  int64_t ldc;
+  int accumulate;
+};
+
+__global__ __launch_bounds__(kThreads) void strided_gemm_kernel(GemmArgs a, int tiles_n) {
+  using TS = TileShape<2, 2, 1>;
+  __shared__ float lds[TS::LDS_FLOATS];
+  float* As = lds;
+  float* Bs = lds + TS::BK * TS::LDA;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % TS::WM, wn = wave / TS::WM, wk = 0;
+  const int m0 = (blockIdx.x / tiles_n) * TS::BM, n0 = (blockIdx.x % tiles_n) * TS::BN;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int k0 = 0; k0 < a.K; k0 += TS::BK) {
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < TS::A_PER_T; ++r) {
+      const int e = tid + kThreads * r;
+      const int k = e % TS::BK, m = e / TS::BK;
+      const int gm = m0 + m, gk = k0 + k;
+      As[k * TS::LDA + m] = (gm < a.M && gk < a.K) ? a.A[gm * a.sam + gk * a.sak] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < TS::B_PER_T; ++r) {
+      const int e = tid + kThreads * r;
+      const int n = e % TS::BN, k = e / TS::BN;
+      const int gn = n0 + n, gk = k0 + k;
+      Bs[k * TS::LDB + n] = (gn < a.N && gk < a.K) ? a.B[gk * a.sbk + gn * a.sbn] : 0.f;
+    }
+    __syncthreads();
+    mfma_tile<TS>(As, Bs, acc, wm, wn, wk, lane);
+  }
+  const int n = n0 + wn * 32 + acc_col(lane);
+  if (n >= a.N) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + wm * 32 + acc_row(r, lane);
+    if (m < a.M) {
+      float* c = a.C + (int64_t)m * a.ldc + n;
+      *c = a.accumulate ? *c + acc[r] : acc[r];
+    }
+  }
+}
+
+static int launch_gemm(const GemmArgs& a, hipStream_t st) {
+  const int tiles_n = (int)ceil_div(a.N, 64);
+  const int tiles = (int)ceil_div(a.M, 64) * tiles_n;
+  strided_gemm_kernel<<<tiles, kThreads, 0, st>>>(a, tiles_n);
+  return check_launch("strided_gemm_kernel");
+}
+
+// db[o] += sum over the batch of delta[b][o], batch rows in order.
+__global__ __launch_bounds__(kThreads) void fc_bias_kernel(int batch, int out,
+                                                           const float* __restrict__ delta,
+                                                           float* __restrict__ db) {
+  const int o = blockIdx.x * kThreads + threadIdx.x;
+  if (o >= out) return;
+  float s = 0.f;
+  for (int b = 0; b < batch; ++b) s += delta[(int64_t)b * out + o];
+  db[o] += s;
+}
+
+int launch_fc(int batch, int in_dim, int out_dim, const float* x, const float* w,
+              const float* delta, float* dw, float* db, float* dx, int dx_accumulate,
+              hipStream_t st) {
+  // dW (out x in) += delta^T (out x batch) . X (batch x in)
+  GemmArgs gw{out_dim, in_dim, batch, delta, 1, out_dim, x, in_dim, 1, dw, in_dim, 1};
+  int rc = launch_gemm(gw, st);
+  if (rc) return rc;
+  if (db) {
+    fc_bias_kernel<<<(unsigned)ceil_div(out_dim, kThreads), kThreads, 0, st>>>(batch, out_dim,
+                                                                               delta, db);
+    rc = check_launch("fc_bias_kernel");
+    if (rc) return rc;
+  }
+  if (dx) {
+    // dX (batch x in) (+)= delta (batch x out) . W (out x in)
+    GemmArgs gx{batch, in_dim, out_dim, delta, out_dim, 1, w, in_dim, 1, dx, in_dim,
+                dx_accumulate};
+    rc = launch_gemm(gx, st);
+  }
+  return rc;
+}
+
+}  // namespace cbb

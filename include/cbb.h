@@ -1,0 +1,230 @@
+/*
+ * cbb.h -- C ABI of libcbb.so, the backward pass of a Darknet/Caffe-style
+ * convolutional block on an AMD Instinct MI355X (gfx950).
+ *
+ * Pages cited (title, address):
+ *  [P1] "YOLOv3 backpropagation: full-flow source analysis"
+ *       (suzhouguqin.com/content/1291550.html)
+ *  [P2] "Caffe source study ch.4 (5): the LeNet backward pass"
+ *       (csdndocs.com/article/9344743)
+ *  [P3] "AlexeyAB DarkNet analysis (4): network forward/backward and the layer struct"
+ *       (m.dandelioncloud.cn/article/details/1675816420510003202)
+ *  [P4] "caffe source study -- one article is enough"
+ *       (geek-share.com/detail/2722348220.html)
+ *  [P5] "Understanding BatchNorm" (javaforall.cn/143067.html)
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller; fp32 unless
+ *    noted; activations NCHW-contiguous (the delta/output layout of the layer
+ *    struct in [P3]); conv weights OIHW; inner-product weights out x in.
+ *  - Nothing here allocates device memory or synchronises the host.  Every
+ *    call validates its arguments on the host (before touching the GPU),
+ *    enqueues its kernels on `stream` (a hipStream_t passed as void*; NULL is
+ *    the default stream) and returns.  Scratch memory comes from a
+ *    caller-provided `workspace` whose size the matching *_workspace_size
+ *    call reports.
+ *  - Parameter gradients (dw, db, dgamma, dbeta) ACCUMULATE (+=), as the
+ *    beta = 1 gemm/gemv calls of [P1] section 3.1 and [P2] layers 4 and 8
+ *    do, so a caller sums several batches by calling again; zero them first
+ *    for a single batch.
+ *  - Input gradients are skipped when their pointer is NULL (the NULL
+ *    net.delta of the first layer, [P3] backward_network); otherwise they are
+ *    overwritten, or added onto when `*_accumulate` is 1 (an input feeding
+ *    several consumers receives the sum of their gradients).
+ *  - Results are deterministic: no floating-point atomics; repeated calls on
+ *    the same inputs give bitwise identical outputs.
+ *  - Errors are returned as a negative cbb_status and nothing is enqueued;
+ *    the pages abort instead (assert / CHECK).
+ */
+#ifndef CBB_H
+#define CBB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CBB_ABI_VERSION 1
+
+typedef enum cbb_status {
+  CBB_OK = 0,
+  CBB_EINVAL = -1,        /* NULL required pointer, non-positive size, bad enum value */
+  CBB_ESHAPE = -2,        /* geometry yields an empty or inconsistent output          */
+  CBB_EUNSUPPORTED = -3,  /* valid but not implemented (e.g. ksize > 7, scale > 8)     */
+  CBB_EWORKSPACE = -4,    /* workspace NULL or smaller than the reported size         */
+  CBB_EHIP = -5           /* a HIP launch failed; cbb_last_error() has its text       */
+} cbb_status;
+
+/* Activation whose gradient is taken, read from the activation OUTPUT y as
+ * Darknet's *_gradient functions do ([P1] section 7):
+ *   LINEAR 1;  LEAKY (y > 0) ? 1 : slope;  LOGISTIC (1 - y) y;  RELU (y > 0). */
+typedef enum cbb_act {
+  CBB_ACT_LINEAR = 0,
+  CBB_ACT_LEAKY = 1,
+  CBB_ACT_LOGISTIC = 2,
+  CBB_ACT_RELU = 3
+} cbb_act;
+
+/* Geometry of one convolutional block: Darknet layer fields batch, c, h, w
+ * (input), n (out_c), size, stride, pad, batch_normalize, activation
+ * ([P3] layer struct).  groups = dilation = 1.  Output size
+ * out = (in + 2 pad - ksize) / stride + 1 (im2col_cpu, [P1] section 3.2). */
+typedef struct cbb_conv_desc {
+  int32_t batch, in_c, in_h, in_w;
+  int32_t out_c, ksize, stride, pad;
+  int32_t batch_normalize; /* 1: BN follows the conv and its shift absorbs the conv bias */
+  int32_t act;             /* cbb_act                                                  */
+  float slope;             /* leaky slope (0.1 in every page's network)                 */
+  float bn_eps;            /* added to the variance inside the square root (1e-5)       */
+} cbb_conv_desc;
+
+int cbb_abi_version(void);
+/* Static text for a status code, or the last HIP error text for CBB_EHIP. */
+const char* cbb_status_string(int status);
+const char* cbb_last_error(void);
+
+/* ----------------------------------------------------------------------------
+ * Conv block backward: backward_convolutional_layer of [P1] section 3.1 with
+ * backward_batchnorm_layer of [P1] section 4:
+ *   g      = delta * act'(y)                                 (gradient_array)
+ *   BN:    dbeta += sum g;  dgamma += sum g * x_norm;        (backward_bias/_scale)
+ *          dz = gamma/sqrt(var+eps) * (g - mean(g) - x_norm * mean(g * x_norm))
+ *          (the closed form of Caffe's BatchNormLayer Backward_cpu, [P5], after
+ *           Darknet's scale_bias by gamma; means over batch and space)
+ *   no BN: db += sum g;  dz = g
+ *   dw[o,i,kh,kw] += sum_{n,ho,wo} dz[n,o,ho,wo] * x[n,i,ho*s+kh-p,wo*s+kw-p]
+ *   dx[n,i,h,w]   (+)= sum over (o,kh,kw) with h = ho*s+kh-p, w = wo*s+kw-p of
+ *                      W[o,i,kh,kw] * dz[n,o,ho,wo]    (W^T x delta, then col2im)
+ * Padding taps read zero.
+ *
+ * Arguments (shapes with N = batch, C = in_c, O = out_c, OH x OW the output):
+ *   x       [N,C,H,W]     block input (net.input)
+ *   w       [O,C,k,k]     weights
+ *   y       [N,O,OH,OW]   activation output (l.output); NULL allowed iff act = LINEAR
+ *   x_norm  [N,O,OH,OW]   normalised conv output (l.x_norm)   } required iff
+ *   var     [O]           biased batch variance (l.variance)  } batch_normalize,
+ *   gamma   [O]           BN scale (l.scales)                 } NULL otherwise
+ *   delta   [N,O,OH,OW]   dL/dy (l.delta on entry), read only
+ *   dz      [N,O,OH,OW]   receives dL/dz (l.delta on exit); may equal delta
+ *                         (in place); may be NULL iff act = LINEAR and no BN
+ *                         (then dz is delta itself)
+ *   dw      [O,C,k,k]     += weight gradient (l.weight_updates)
+ *   db      [O]           += bias gradient (l.bias_updates; with BN this is dbeta)
+ *   dgamma  [O]           += scale gradient (l.scale_updates); BN only, else NULL
+ *   dx      [N,C,H,W]     input gradient (net.delta); NULL skips it
+ *   dx_accumulate         1: dx += ...; 0: dx = ...
+ *   workspace             device scratch of at least cbb_conv_block_workspace_size
+ *                         bytes, 256-byte aligned; contents on entry ignored.
+ * Supported: 1 <= ksize <= 7, 1 <= stride <= 4, 0 <= pad < ksize, all sizes
+ * whose element counts fit in int32 per tensor index and int64 overall.
+ * ------------------------------------------------------------------------- */
+int cbb_conv_block_workspace_size(const cbb_conv_desc* desc, size_t* bytes);
+int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const float* w,
+                            const float* y, const float* x_norm, const float* var,
+                            const float* gamma, const float* delta, float* dz, float* dw,
+                            float* db, float* dgamma, float* dx, int dx_accumulate,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* The three stages of cbb_conv_block_backward as separate calls (Caffe splits
+ * the same work into backward_cpu_bias / weight_cpu_gemm / backward_cpu_gemm,
+ * [P4] BaseConvolutionLayer).  Enqueued one after another on one stream with
+ * the same workspace they do exactly what cbb_conv_block_backward does.
+ * Each takes the workspace sized by cbb_conv_block_workspace_size.
+ *
+ * Stage 1, activation gradient + BN backward (or the bias sum):
+ *   arguments as in cbb_conv_block_backward; writes dz (unless act = LINEAR
+ *   without BN, where dz may be NULL and nothing is written), adds to db and
+ *   (BN) dgamma. */
+int cbb_conv_act_bn_backward(const cbb_conv_desc* desc, const float* y, const float* x_norm,
+                             const float* var, const float* gamma, const float* delta, float* dz,
+                             float* db, float* dgamma, void* workspace, size_t workspace_bytes,
+                             void* stream);
+/* Stage 2, weight gradient: dw [O,C,k,k] += dz (x) im2col(x)^T, from
+ * dz [N,O,OH,OW] and x [N,C,H,W]. */
+int cbb_conv_backward_weights(const cbb_conv_desc* desc, const float* x, const float* dz,
+                              float* dw, void* workspace, size_t workspace_bytes, void* stream);
+/* Stage 3, input gradient: dx [N,C,H,W] (+)= col2im(W^T dz); uses no workspace.
+ * dx must not overlap w or dz. */
+int cbb_conv_backward_data(const cbb_conv_desc* desc, const float* w, const float* dz, float* dx,
+                           int dx_accumulate, void* stream);
+
+/* Activation gradient alone (gradient_array, [P1] sections 3.1 and 7):
+ * g[i] = delta[i] * act'(y[i]) for i < count.  g may equal delta. */
+int cbb_act_backward(int act, float slope, const float* y, const float* delta, float* g,
+                     int64_t count, void* stream);
+
+/* Batch-norm backward alone (training statistics), from g = dL/du where
+ * u = gamma * x_norm + beta; tensors [n, c, hw]:
+ *   dbeta += sum g;  dgamma += sum g * x_norm;
+ *   dz = gamma/sqrt(var+eps) * (g - mean(g) - x_norm * mean(g * x_norm)).
+ * ([P1] section 4 backward_batchnorm_layer; [P5] Backward_cpu.)  dz may equal g. */
+int cbb_bn_backward_workspace_size(int n, int c, int64_t hw, size_t* bytes);
+int cbb_bn_backward(int n, int c, int64_t hw, float eps, const float* g, const float* x_norm,
+                    const float* var, const float* gamma, float* dz, float* dgamma, float* dbeta,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Inner-product backward ([P2] layer 8), batch M, in K, out N:
+ *   dw [N,K] += delta^T [N,M] x [M,K];  db [N] += sum over the batch of delta;
+ *   dx [M,K] (+)= delta [M,N] x w [N,K]   (NULL skips; dx_accumulate as above).
+ * db may be NULL (no bias term). */
+int cbb_fc_backward(int batch, int in_dim, int out_dim, const float* x, const float* w,
+                    const float* delta, float* dw, float* db, float* dx, int dx_accumulate,
+                    void* stream);
+
+/* Softmax-with-loss gradient ([P2] layer 9): dlogits = prob, minus 1 at each
+ * sample's label, times loss_weight / batch (one label per sample, so the
+ * normalised count and the outer count are both `batch`).  prob, dlogits
+ * [batch, classes]; labels int32 [batch].  A label outside [0, classes)
+ * leaves its row without the -1 and adds 1 to *bad_labels (device int32,
+ * may be NULL); the caller reads it when it wants to know. */
+int cbb_softmax_loss_backward(int batch, int classes, const float* prob, const int32_t* labels,
+                              float loss_weight, float* dlogits, int32_t* bad_labels,
+                              void* stream);
+
+/* The loss gradient above followed by the backward of the inner product that
+ * produced the logits ([P2] layers 9 and 8 together): dlogits as above, then
+ * dw [classes, in_dim] += dlogits^T x, db [classes] += sum dlogits,
+ * dx [batch, in_dim] = dlogits x w (NULL skips). */
+int cbb_fc_softmax_backward(int batch, int in_dim, int classes, const float* prob,
+                            const int32_t* labels, float loss_weight, const float* x,
+                            const float* w, float* dlogits, float* dw, float* db, float* dx,
+                            int32_t* bad_labels, void* stream);
+
+/* Shortcut backward for equal shapes ([P1] section 5): d_main += alpha*delta
+ * (axpy into the previous layer's delta); d_from += beta*delta (shortcut_cpu
+ * with s1 = 1, s2 = beta, into the source layer's delta).  d_main and d_from
+ * must not overlap each other or delta. */
+int cbb_shortcut_backward(int64_t count, float alpha, float beta, const float* delta,
+                          float* d_main, float* d_from, void* stream);
+
+/* Route backward ([P1] section 6): the route delta holds, per image, the
+ * inputs' outputs one after another (in_sizes[t] floats each, t < n_in <= 8);
+ * for every input t and image j, d_in[t][j*in_sizes[t] + e] += the matching
+ * route-delta element.  `in_sizes` and `d_in` are HOST arrays (d_in of device
+ * pointers). */
+int cbb_route_backward(int batch, int n_in, const int64_t* in_sizes, const float* delta,
+                       float* const* d_in, void* stream);
+
+/* Nearest-neighbour upsample backward (adjoint of y[h,w] = x[h/scale, w/scale];
+ * the pages name the layer but do not show it):
+ *   dx[n,c,h,w] += sum_{a,b < scale} delta[n,c,h*scale+a,w*scale+b];
+ * dx [n,c,h,w], delta [n,c,h*scale,w*scale]. */
+int cbb_upsample_backward(int n, int c, int h, int w, int scale, const float* delta, float* dx,
+                          void* stream);
+
+/* Max-pool backward ([P2] layer 5): dx = 0, then every pooled output adds
+ * its delta at the bottom pixel its mask names.  Window ksize x ksize,
+ * stride `stride`, no padding: oh = (ih - ksize)/stride + 1.  idx int32
+ * [n,c,oh,ow] holds the per-plane flat index h*iw + w of the winner, which
+ * must lie inside that output's window (as a max-pool forward produces);
+ * dx [n,c,ih,iw] is overwritten. */
+int cbb_maxpool_backward(int n, int c, int ih, int iw, int ksize, int stride,
+                         const int32_t* idx, const float* delta, float* dx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CBB_H */

@@ -54,6 +54,7 @@ _i, _l, _d = ctypes.c_int, ctypes.c_long, ctypes.c_double
 
 _SIGS = {
     "orc_version": ([], _i),
+    "orc_num_threads": ([], _i),
     "orc_act_forward": ([_i, _d, _D, _D, _l], None),
     "orc_act_backward": ([_i, _d, _D, _D, _D, _l], None),
     "orc_bn_forward": ([_i, _i, _l, _d, _D, _D, _D, _D, _D, _D, _D], None),
@@ -106,6 +107,11 @@ def _p(a: np.ndarray | None):
 def _pi(a: np.ndarray):
     assert a.dtype == np.int32 and a.flags.c_contiguous
     return a.ctypes.data_as(_I)
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use (omp_get_max_threads)."""
+    return lib().orc_num_threads()
 
 
 def conv_out_dim(size: int, k: int, s: int, p: int) -> int:

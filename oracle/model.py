@@ -47,7 +47,8 @@ def conv_block_forward(layer, x, w, bias=None, gamma=None, beta=None, eps=EPS, s
     return out
 
 
-def conv_block_backward(layer, saved, delta, want_dx=True, dx_init=None, eps=EPS, slope=SLOPE):
+def conv_block_backward(layer, saved, delta, want_dx=True, dx_init=None, eps=EPS, slope=SLOPE,
+                        w=None):
     """Backward of one conv block from delta = dL/dy.
 
     Returns g, dz, dw, db (= dbeta when BN follows), dgamma (BN only) and dx
@@ -66,7 +67,8 @@ def conv_block_backward(layer, saved, delta, want_dx=True, dx_init=None, eps=EPS
     x = saved["x_in"]
     res["dw"] = conv_backward_weights(x, dz, layer.k, layer.stride, layer.pad)
     if want_dx:
-        res["dx"] = conv_backward_data(saved["w"], dz, x.shape[2:], layer.stride, layer.pad,
+        res["dx"] = conv_backward_data(saved["w"] if w is None else w, dz, x.shape[2:],
+                                       layer.stride, layer.pad,
                                        dx=dx_init)
     return res
 
@@ -160,10 +162,10 @@ def workload_backward(wl, inp, saved, delta=None) -> dict:
         n = d_pool2.shape[0]
         d_pool2 = d_pool2.reshape(n, c2.out_c, c2.out_h // 2, c2.out_w // 2)
         d_c2 = maxpool_backward(saved["pool_idx"][1], d_pool2, (c2.out_h, c2.out_w))
-        r2 = conv_block_backward(c2, L[1], d_c2, want_dx=True)
+        r2 = conv_block_backward(c2, L[1], d_c2, want_dx=True, w=inp["w"][1])
         put(1, r2)
         d_c1 = maxpool_backward(saved["pool_idx"][0], r2["dx"], (c1.out_h, c1.out_w))
-        r1 = conv_block_backward(c1, L[0], d_c1, want_dx=False)
+        r1 = conv_block_backward(c1, L[0], d_c1, want_dx=False, w=inp["w"][0])
         put(0, r1)
         out.update(dlogits=dlogits, fc_dw=[dw1, dw2], fc_db=[db1, db2], d_relu=d_relu,
                    g_relu=g_relu, d_pool2=d_pool2, d_c2=d_c2, d_c1=d_c1)
@@ -174,16 +176,17 @@ def workload_backward(wl, inp, saved, delta=None) -> dict:
         # shortcut backward: the delta reaches the last conv's output (alpha) and the
         # shortcut source, i.e. the block input (beta); both buffers start at zero.
         d_y2, d_x = shortcut_backward(delta, np.zeros_like(delta), np.zeros_like(delta), 1.0, 1.0)
-        r2 = conv_block_backward(convs[1], L[1], d_y2, want_dx=True)
+        r2 = conv_block_backward(convs[1], L[1], d_y2, want_dx=True, w=inp["w"][1])
         put(1, r2)
-        r1 = conv_block_backward(convs[0], L[0], r2["dx"], want_dx=True, dx_init=d_x)
+        r1 = conv_block_backward(convs[0], L[0], r2["dx"], want_dx=True, dx_init=d_x,
+                                 w=inp["w"][0])
         put(0, r1)
         out["dx"] = r1["dx"]
         return out
 
     d = delta
     for li in range(len(convs) - 1, -1, -1):
-        r = conv_block_backward(convs[li], L[li], d, want_dx=True)
+        r = conv_block_backward(convs[li], L[li], d, want_dx=True, w=inp["w"][li])
         put(li, r)
         d = r["dx"]
     if name == "yolov3_head":

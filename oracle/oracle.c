@@ -40,6 +40,13 @@
 
 int orc_version(void) { return 1; }
 
+#ifdef _OPENMP
+#include <omp.h>
+int orc_num_threads(void) { return omp_get_max_threads(); }
+#else
+int orc_num_threads(void) { return 1; }
+#endif
+
 /* ------------------------------------------------------------------ */
 /* activations                                                         */
 /* ------------------------------------------------------------------ */

@@ -1,0 +1,140 @@
+"""The C ABI on a host without a GPU: the library loads, exports every symbol
+include/cbb.h declares, and rejects bad arguments with status codes before any
+HIP call.  No call here passes arguments that would reach a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from cnn_backward_pass_amd import cbb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cbb.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(cbb.LIB_PATH),
+                                reason="libcbb.so not built (run __graft_entry__.build())")
+
+BOGUS = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(cbb_\w+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    names = declared_functions()
+    assert len(names) >= 14
+    lib = cbb.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(cbb.EXPORTS)
+
+
+def test_version_and_status_strings():
+    assert cbb.abi_version() == 1
+    for code in (0, -1, -2, -3, -4):
+        assert cbb.status_string(code)
+    assert cbb.status_string(123) == "unknown status"
+
+
+def _desc(**kw):
+    base = dict(batch=2, in_c=3, in_h=8, in_w=8, out_c=4, ksize=3, stride=1, pad=1,
+                batch_normalize=1, act="leaky")
+    base.update(kw)
+    return cbb.conv_desc(**base)
+
+
+def ws_size(desc):
+    n = ctypes.c_size_t(0)
+    rc = cbb.lib().cbb_conv_block_workspace_size(ctypes.byref(desc), ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), -1), (dict(in_c=0), -1), (dict(out_c=-2), -1), (dict(ksize=0), -1),
+    (dict(stride=0), -1), (dict(pad=-1), -1), (dict(act=7), -1), (dict(batch_normalize=2), -1),
+    (dict(ksize=9, pad=4), -3), (dict(stride=5), -3), (dict(ksize=3, pad=3), -3),
+    (dict(in_h=1, in_w=1, ksize=5, pad=1), -2),
+    (dict(batch=4096, in_c=512, in_h=1024, in_w=1024), -3),
+])
+def test_conv_desc_validation(kw, code):
+    assert ws_size(_desc(**kw))[0] == code
+
+
+def test_workspace_size_query_is_host_only():
+    rc, n = ws_size(_desc())
+    assert rc == 0 and n > 0 and n % 256 == 0
+    # larger problems never need less scratch
+    rc2, n2 = ws_size(_desc(batch=16, in_h=64, in_w=64))
+    assert rc2 == 0 and n2 >= n
+
+
+def _call_conv(desc, **ptrs):
+    names = ["x", "w", "y", "x_norm", "var", "gamma", "delta", "dz", "dw", "db", "dgamma", "dx"]
+    args = [ptrs.get(k, BOGUS) for k in names]
+    ws = ptrs.get("ws", BOGUS)
+    wsb = ptrs.get("wsb", 1 << 30)
+    return cbb.lib().cbb_conv_block_backward(ctypes.byref(desc), *args, ptrs.get("acc", 0), ws,
+                                             wsb, None)
+
+
+@pytest.mark.parametrize("missing", ["x", "w", "delta", "dw", "db", "y", "x_norm", "var", "gamma",
+                                     "dgamma", "dz"])
+def test_conv_null_required_pointer(missing):
+    assert _call_conv(_desc(), **{missing: None}) == -1
+
+
+def test_conv_pointer_rules_without_bn():
+    d = _desc(batch_normalize=0)
+    # BN tensors must be NULL when there is no BN
+    assert _call_conv(d, dgamma=BOGUS, x_norm=None, var=None, gamma=None) == -1
+    # linear without BN: y may be NULL but the other pointer rules still hold
+    dl = _desc(batch_normalize=0, act="linear")
+    assert _call_conv(dl, y=None, x_norm=None, var=None, gamma=None, dgamma=None, dz=None,
+                      x=None) == -1
+
+
+def test_conv_workspace_and_flags():
+    d = _desc()
+    _, need = ws_size(d)
+    assert _call_conv(d, wsb=need - 1) == -4
+    assert _call_conv(d, ws=None) == -4
+    assert _call_conv(d, ws=ctypes.c_void_p(0x1004)) == -4     # not 256-byte aligned
+    assert _call_conv(d, acc=2) == -1
+
+
+def test_other_entry_points_validate():
+    L = cbb.lib()
+    sz = ctypes.c_size_t(0)
+    assert L.cbb_act_backward(9, 0.1, BOGUS, BOGUS, BOGUS, 10, None) == -1
+    assert L.cbb_act_backward(1, 0.1, None, BOGUS, BOGUS, 10, None) == -1
+    assert L.cbb_act_backward(1, 0.1, BOGUS, BOGUS, BOGUS, -1, None) == -1
+    assert L.cbb_act_backward(1, 0.1, BOGUS, BOGUS, BOGUS, 0, None) == 0      # empty: no launch
+    assert L.cbb_bn_backward_workspace_size(0, 4, 16, ctypes.byref(sz)) == -1
+    assert L.cbb_bn_backward_workspace_size(2, 4, 16, ctypes.byref(sz)) == 0 and sz.value > 0
+    assert L.cbb_bn_backward(2, 4, 16, 1e-5, *[BOGUS] * 7, BOGUS, 0, None) == -4
+    assert L.cbb_bn_backward(2, 4, 16, 0.0, *[BOGUS] * 7, BOGUS, 1 << 20, None) == -1
+    assert L.cbb_fc_backward(0, 8, 8, *[BOGUS] * 6, 0, None) == -1
+    assert L.cbb_fc_backward(4, 8, 8, None, *[BOGUS] * 5, 0, None) == -1
+    assert L.cbb_softmax_loss_backward(4, 0, BOGUS, BOGUS, 1.0, BOGUS, None, None) == -1
+    assert L.cbb_fc_softmax_backward(4, 8, 10, BOGUS, None, 1.0, *[BOGUS] * 6, None, None) == -1
+    assert L.cbb_shortcut_backward(16, 1.0, 1.0, BOGUS, BOGUS, BOGUS, None) == -1  # aliasing
+    assert L.cbb_shortcut_backward(0, 1.0, 1.0, BOGUS, ctypes.c_void_p(0x2000),
+                                   ctypes.c_void_p(0x3000), None) == 0
+    sizes = (ctypes.c_int64 * 2)(10, 0)
+    ptrs = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert L.cbb_route_backward(2, 2, sizes, BOGUS, ptrs, None) == -1
+    assert L.cbb_route_backward(2, 9, sizes, BOGUS, ptrs, None) == -1
+    assert L.cbb_upsample_backward(2, 3, 4, 4, 9, BOGUS, BOGUS, None) == -3
+    assert L.cbb_upsample_backward(2, 3, 0, 4, 2, BOGUS, BOGUS, None) == -1
+    assert L.cbb_maxpool_backward(2, 3, 4, 4, 5, 2, BOGUS, BOGUS, BOGUS, None) == -2
+    assert L.cbb_maxpool_backward(2, 3, 4, 4, 2, 0, BOGUS, BOGUS, BOGUS, None) == -1
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(4)
+    with pytest.raises(ValueError):
+        cbb.act_backward("leaky", 0.1, t, t, t)
