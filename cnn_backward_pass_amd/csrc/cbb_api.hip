@@ -62,7 +62,8 @@ int check_desc(const cbb_conv_desc* d, ConvPlan* plan) {
     plan->ow = ow;
     const ConvGeom g = make_geom(*d);
     plan->part_bytes = align_up(actbn_workspace(d->batch, d->out_c, oh * ow), kAlign);
-    plan->dw_bytes = align_up(conv_dw_workspace(g), kAlign);
+    // dW and dX run one after the other on the stream and share the second region
+    plan->dw_bytes = align_up(std::max(conv_dw_workspace(g), conv_dx_workspace(g)), kAlign);
     plan->total = plan->part_bytes + plan->dw_bytes;
   }
   return CBB_OK;
@@ -125,7 +126,9 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
   const ConvGeom g = make_geom(*desc);
   rc = launch_conv_dw(g, x, dz_eff, dw, reinterpret_cast<float*>(ws + p.part_bytes), st);
   if (rc) return rc;
-  if (dx) rc = launch_conv_dx(g, w, dz_eff, dx, dx_accumulate, st);
+  if (dx)
+    rc = launch_conv_dx(g, w, dz_eff, dx, dx_accumulate,
+                        reinterpret_cast<float*>(ws + p.part_bytes), st);
   return rc;
 }
 
@@ -164,12 +167,18 @@ int cbb_conv_backward_weights(const cbb_conv_desc* desc, const float* x, const f
 }
 
 int cbb_conv_backward_data(const cbb_conv_desc* desc, const float* w, const float* dz, float* dx,
-                           int dx_accumulate, void* stream) {
-  int rc = check_desc(desc, nullptr);
+                           int dx_accumulate, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  ConvPlan p;
+  int rc = check_desc(desc, &p);
   if (rc) return rc;
   if (!w || !dz || !dx) return CBB_EINVAL;
   if (dx_accumulate != 0 && dx_accumulate != 1) return CBB_EINVAL;
-  return launch_conv_dx(make_geom(*desc), w, dz, dx, dx_accumulate, S(stream));
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return CBB_EWORKSPACE;
+  if (workspace && ((uintptr_t)workspace % kAlign)) return CBB_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  return launch_conv_dx(make_geom(*desc), w, dz, dx, dx_accumulate,
+                        reinterpret_cast<float*>(ws ? ws + p.part_bytes : nullptr), S(stream));
 }
 
 int cbb_act_backward(int act, float slope, const float* y, const float* delta, float* g,

@@ -57,65 +57,153 @@ __device__ __forceinline__ float block_sum_256(float v, float* scratch) {
 //
 // A work-group of 4 waves computes a BM x BN block of C = A x B over a range of
 // the reduction index.  Waves are arranged WM x WN x WK (WM*WN*WK = 4): each
-// wave owns a 32 x 32 output block (one 32x32x2 accumulator) and, when WK > 1,
-// a quarter/half of every K tile, with the WK partial blocks summed through
-// LDS at the end.  K tiles are BK = 32*WK deep and staged in LDS as
+// wave owns RM x RN blocks of 32 x 32 (one 32x32x2 accumulator each, so a wave
+// tile is 32RM x 32RN) and, when WK > 1, a share of every K tile, with the WK
+// partial blocks summed through LDS at the end.  K tiles are BK = 32*WK*KSUB
+// deep and staged in LDS, double-buffered, as
 //   As[BK][BM + 1]  (A transposed: K-major, padded against bank conflicts)
 //   Bs[BK][BN + 1]
-// The loaders (supplied by each kernel) fill registers for tile t+1 while the
+// The loaders (supplied by each kernel) fill registers for tile t+2 while the
 // matrix cores work on tile t.
 // ---------------------------------------------------------------------------
-template <int WM_, int WN_, int WK_>
+template <int WM_, int WN_, int WK_, int KSUB_ = 1, int RM_ = 1, int RN_ = 1>
 struct TileShape {
-  static constexpr int WM = WM_, WN = WN_, WK = WK_;
+  static constexpr int WM = WM_, WN = WN_, WK = WK_, KSUB = KSUB_, RM = RM_, RN = RN_;
   static_assert(WM * WN * WK == 4, "4 waves per work-group");
-  static constexpr int BM = 32 * WM, BN = 32 * WN, BK = 32 * WK;
+  // each wave consumes KSUB slabs of 32 K rows per tile
+  static constexpr int BM = 32 * WM * RM, BN = 32 * WN * RN, BK = 32 * WK * KSUB;
   static constexpr int LDA = BM + 1, LDB = BN + 1;
   static constexpr int A_PER_T = BM * BK / kThreads;  // A elements each thread stages
   static constexpr int B_PER_T = BN * BK / kThreads;
-  static constexpr int LDS_FLOATS = BK * LDA + BK * LDB;
-  static constexpr int RED_FLOATS = (WK - 1) * WM * WN * 64 * 16;
+  static constexpr int BUF_FLOATS = BK * LDA + BK * LDB;  // one stage (A and B tiles)
+  static constexpr int LDS_FLOATS = 2 * BUF_FLOATS;        // double-buffered
+  static constexpr int NACC = RM * RN;
+  static constexpr int RED_FLOATS = (WK - 1) * WM * WN * NACC * 64 * 16;
   static_assert(RED_FLOATS <= LDS_FLOATS, "WK reduction reuses the staging area");
 };
 
-// One K tile of MFMA work for the calling wave: 16 steps of K = 2.
+template <class TS>
+struct Acc {
+  f32x16 v[TS::RM][TS::RN];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < TS::RM; ++i)
+#pragma unroll
+      for (int j = 0; j < TS::RN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[i][j][r] = 0.f;
+  }
+};
+
+// Row offset (within the block tile) of accumulator (i, j)'s 32x32 block for wave (wm, wn).
+template <class TS>
+__device__ __forceinline__ int acc_m0(int wm, int i) { return (wm * TS::RM + i) * 32; }
+template <class TS>
+__device__ __forceinline__ int acc_n0(int wn, int j) { return (wn * TS::RN + j) * 32; }
+
+// One K tile of MFMA work for the calling wave: 16*KSUB steps of K = 2 over the
+// wave's K rows [wk*32*KSUB, (wk+1)*32*KSUB).  All operand fragments are read
+// from LDS first and the matrix-core chain is issued afterwards, so the LDS
+// latency is paid once per 32 K rows instead of once per step.
 template <class TS>
 __device__ __forceinline__ void mfma_tile(const float* __restrict__ As, const float* __restrict__ Bs,
-                                          f32x16& acc, int wm, int wn, int wk, int lane) {
+                                          Acc<TS>& acc, int wm, int wn, int wk, int lane) {
   const int col = lane & 31, khalf = lane >> 5;
-  const float* a = As + (wk * 32 + khalf) * TS::LDA + wm * 32 + col;
-  const float* b = Bs + (wk * 32 + khalf) * TS::LDB + wn * 32 + col;
 #pragma unroll
-  for (int kk = 0; kk < 16; ++kk) {
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2 * kk * TS::LDA], b[2 * kk * TS::LDB], acc, 0, 0,
-                                              0);
+  for (int ks = 0; ks < TS::KSUB; ++ks) {
+    const int krow = (wk * TS::KSUB + ks) * 32 + khalf;
+    float fa[TS::RM][16], fb[TS::RN][16];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+#pragma unroll
+      for (int i = 0; i < TS::RM; ++i)
+        fa[i][kk] = As[(krow + 2 * kk) * TS::LDA + acc_m0<TS>(wm, i) + col];
+#pragma unroll
+      for (int j = 0; j < TS::RN; ++j)
+        fb[j][kk] = Bs[(krow + 2 * kk) * TS::LDB + acc_n0<TS>(wn, j) + col];
+    }
+    // keep the scheduler from sinking the reads back between the matrix-core steps
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+#pragma unroll
+      for (int i = 0; i < TS::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TS::RN; ++j)
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[i][kk], fb[j][kk], acc.v[i][j], 0,
+                                                             0, 0);
+  }
+}
+
+// Double-buffered main loop over K tiles [kbeg, kend) in steps of BK.
+//   load(k0)   : global -> registers for the tile starting at k0 (may be any k0 < kend)
+//   store(buf) : registers -> LDS stage `buf` (A at buf, B at buf + BK*LDA)
+// Per tile t: the matrix cores consume stage t%2 while stage (t+1)%2 receives
+// tile t+1 and the loads of tile t+2 are in flight; one barrier per tile.
+template <class TS, class Load, class Store>
+__device__ __forceinline__ void gemm_mainloop(float* lds, int64_t kbeg, int64_t kend, Load&& load,
+                                              Store&& store, Acc<TS>& acc, int wm, int wn, int wk,
+                                              int lane) {
+  if (kbeg >= kend) return;
+  load(kbeg);
+  store(lds);
+  if (kbeg + TS::BK < kend) load(kbeg + TS::BK);
+  __syncthreads();
+  int cur = 0;
+  for (int64_t k0 = kbeg;; k0 += TS::BK) {
+    const float* A = lds + cur * TS::BUF_FLOATS;
+    mfma_tile<TS>(A, A + TS::BK * TS::LDA, acc, wm, wn, wk, lane);
+    if (k0 + TS::BK >= kend) break;
+    store(lds + (cur ^ 1) * TS::BUF_FLOATS);
+    if (k0 + 2 * TS::BK < kend) load(k0 + 2 * TS::BK);
+    __syncthreads();
+    cur ^= 1;
   }
 }
 
 // Sum the WK partial accumulators of a work-group into the wk == 0 waves.
-// Uses `red` (LDS, at least (WK-1) * WM*WN * 64 * 16 floats; the tile staging
-// area is large enough) after a barrier.  All threads must call it.
+// Uses `red` (LDS; the staging area is large enough) after a barrier.  All
+// threads must call it.
 template <class TS>
-__device__ __forceinline__ void reduce_wk(f32x16& acc, float* red, int wm, int wn, int wk,
+__device__ __forceinline__ void reduce_wk(Acc<TS>& acc, float* red, int wm, int wn, int wk,
                                           int lane) {
   if constexpr (TS::WK > 1) {
     __syncthreads();
-    const int slot = (wm + TS::WM * wn);
+    const int slot = (wm + TS::WM * wn) * TS::NACC;
     if (wk > 0) {
-      float* dst = red + ((wk - 1) * TS::WM * TS::WN + slot) * 64 * 16 + lane;
+      float* dst = red + ((wk - 1) * TS::WM * TS::WN * TS::NACC + slot) * 64 * 16 + lane;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[r * 64] = acc[r];
+      for (int i = 0; i < TS::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TS::RN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dst[((i * TS::RN + j) * 16 + r) * 64] = acc.v[i][j][r];
     }
     __syncthreads();
     if (wk == 0) {
 #pragma unroll
       for (int q = 1; q < TS::WK; ++q) {
-        const float* src = red + ((q - 1) * TS::WM * TS::WN + slot) * 64 * 16 + lane;
+        const float* src = red + ((q - 1) * TS::WM * TS::WN * TS::NACC + slot) * 64 * 16 + lane;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] += src[r * 64];
+        for (int i = 0; i < TS::RM; ++i)
+#pragma unroll
+          for (int j = 0; j < TS::RN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc.v[i][j][r] += src[((i * TS::RN + j) * 16 + r) * 64];
       }
     }
   }
+}
+
+// Work-groups are dispatched round-robin over the 8 XCDs, each with its own L2.
+// Remap the dispatch index so that XCD x runs one contiguous range of logical
+// work-group ids: logical neighbours (tiles that read the same operands) then
+// share an L2 instead of being spread over eight.  A bijection on [0, n).
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_remap(int phys, int n) {
+  const int per = n / kXcds, rem = n % kXcds;
+  const int xcd = phys % kXcds, k = phys / kXcds;
+  return xcd * per + min(xcd, rem) + k;
 }
 
 // Row / column of accumulator register r of lane `lane` inside a wave's 32x32 block.
@@ -127,8 +215,9 @@ ConvGeom make_geom(const cbb_conv_desc& d);
 size_t conv_dw_workspace(const ConvGeom& g);
 int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
                    hipStream_t st);
+size_t conv_dx_workspace(const ConvGeom& g);
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
-                   hipStream_t st);
+                   float* ws, hipStream_t st);
 size_t actbn_workspace(int N, int C, int64_t HW);
 int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, const float* xn,
                  int act, float slope, const float* var, const float* gamma, float eps, int bn,

@@ -23,14 +23,16 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
                                                            const float* __restrict__ dz,
                                                            float* __restrict__ out,
                                                            int64_t k_chunk, int tiles_n,
-                                                           int direct) {
+                                                           int nsplits, int direct) {
   __shared__ float lds[TS::LDS_FLOATS];
-  float* As = lds;
-  float* Bs = lds + TS::BK * TS::LDA;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
-  const int m0 = (blockIdx.x / tiles_n) * TS::BM, n0 = (blockIdx.x % tiles_n) * TS::BN;
-  const int64_t kbeg = (int64_t)blockIdx.y * k_chunk;
+  // id = split * tiles + tile: the tiles of one split (same dz rows) are dispatched together
+  const int tiles = gridDim.x / nsplits;
+  const int lid = blockIdx.x;
+  const int split = lid / tiles, tile = lid - split * tiles;
+  const int m0 = (tile / tiles_n) * TS::BM, n0 = (tile % tiles_n) * TS::BN;
+  const int64_t kbeg = (int64_t)split * k_chunk;
   const int64_t kend = min(g.Q, kbeg + k_chunk);
 
   constexpr int RSTEP = kThreads / TS::BK;
@@ -68,11 +70,15 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
       hb = ho * g.S - g.P;
       wb = wo * g.S - g.P;
     }
+    // Out-of-range elements load from a clamped (valid) address and are then
+    // replaced by zero: no divergent branches around the loads.
     const float* db = dz + ((int64_t)b * g.OC) * g.OHW + rem;
 #pragma unroll
     for (int r = 0; r < TS::A_PER_T; ++r) {
       const int o = m0 + rbase + RSTEP * r;
-      ra[r] = (qv && o < g.OC) ? db[(int64_t)o * g.OHW] : 0.f;
+      const bool ok = qv && o < g.OC;
+      const float v = db[(int64_t)(ok ? o : 0) * g.OHW];
+      ra[r] = ok ? v : 0.f;
     }
     // x index of (n, i, hb + kh, wb + kw) = image base + boff + hb*W + wb
     const float* xb = x + (int64_t)b * g.C * g.HW;
@@ -81,53 +87,70 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
     for (int r = 0; r < TS::B_PER_T; ++r) {
       const int h = hb + bkh[r], w = wb + bkw[r];
       const bool ok = qv && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
-      rb[r] = ok ? xb[boff[r] + pbase] : 0.f;
+      const float v = xb[ok ? boff[r] + pbase : 0];
+      rb[r] = ok ? v : 0.f;
     }
   };
-  auto store = [&]() {
+  auto store = [&](float* buf) {
+    float* As = buf;
+    float* Bs = buf + TS::BK * TS::LDA;
 #pragma unroll
     for (int r = 0; r < TS::A_PER_T; ++r) As[qi * TS::LDA + rbase + RSTEP * r] = ra[r];
 #pragma unroll
     for (int r = 0; r < TS::B_PER_T; ++r) Bs[qi * TS::LDB + rbase + RSTEP * r] = rb[r];
   };
 
-  f32x16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  if (kbeg < kend) load(kbeg);
-  for (int64_t k0 = kbeg; k0 < kend; k0 += TS::BK) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (k0 + TS::BK < kend) load(k0 + TS::BK);
-    mfma_tile<TS>(As, Bs, acc, wm, wn, wk, lane);
-  }
+  Acc<TS> acc;
+  acc.zero();
+  gemm_mainloop<TS>(lds, kbeg, kend, load, store, acc, wm, wn, wk, lane);
   reduce_wk<TS>(acc, lds, wm, wn, wk, lane);
   if (wk == 0) {
-    const int j = n0 + wn * 32 + acc_col(lane);
-    float* dst = direct ? out : out + (int64_t)blockIdx.y * g.OC * g.J;
+    float* dst = direct ? out : out + (int64_t)split * g.OC * g.J;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int o = m0 + wm * 32 + acc_row(r, lane);
-      if (o < g.OC && j < g.J) {
-        const int64_t e = (int64_t)o * g.J + j;
-        if (direct)
-          dst[e] += acc[r];
-        else
-          dst[e] = acc[r];
+    for (int ai = 0; ai < TS::RM; ++ai)
+#pragma unroll
+      for (int aj = 0; aj < TS::RN; ++aj) {
+        const int j = n0 + acc_n0<TS>(wn, aj) + acc_col(lane);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int o = m0 + acc_m0<TS>(wm, ai) + acc_row(r, lane);
+          if (o < g.OC && j < g.J) {
+            const int64_t e = (int64_t)o * g.J + j;
+            if (direct)
+              dst[e] += acc.v[ai][aj][r];
+            else
+              dst[e] = acc.v[ai][aj][r];
+          }
+        }
       }
-    }
   }
 }
 
-// dw[e] += sum over slices s (in order) of part[s][e].
-__global__ __launch_bounds__(kThreads) void dw_splitk_reduce(float* __restrict__ dw,
-                                                             const float* __restrict__ part,
-                                                             int splits, int64_t mn) {
+// Ordered sum of the dW split partials.  Level 1 (only when there are many
+// splits): work-group (e-block, g) sums splits [g*SG, (g+1)*SG) of 256
+// consecutive elements into part2[g][e].  Level 2: dw[e] += sum over g (or over
+// the splits directly) in index order.  Every output element is summed by one
+// thread in a fixed order, so the result does not depend on scheduling.
+constexpr int kReduceGroup = 32;
+
+__global__ __launch_bounds__(kThreads) void dw_reduce_l1(const float* __restrict__ part,
+                                                         float* __restrict__ part2, int splits,
+                                                         int64_t mn) {
+  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (e >= mn) return;
+  const int s0 = blockIdx.y * kReduceGroup, s1 = min(splits, s0 + kReduceGroup);
+  float acc = 0.f;
+  for (int sp = s0; sp < s1; ++sp) acc += part[(int64_t)sp * mn + e];
+  part2[(int64_t)blockIdx.y * mn + e] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void dw_reduce_l2(float* __restrict__ dw,
+                                                         const float* __restrict__ part, int n,
+                                                         int64_t mn) {
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (e >= mn) return;
   float s = 0.f;
-  for (int sp = 0; sp < splits; ++sp) s += part[(int64_t)sp * mn + e];
+  for (int k = 0; k < n; ++k) s += part[(int64_t)k * mn + e];
   dw[e] += s;
 }
 
@@ -137,36 +160,52 @@ __global__ __launch_bounds__(kThreads) void dw_splitk_reduce(float* __restrict__
 // receives the same set of taps kh = rh + s*th (rh = (ph + p) mod s), and the
 // output row it reads is ho = (h + p - kh)/s = hh + bh - th with h = ph + s*hh,
 // bh = (ph + p - rh)/s.  Each phase is a dense GEMM
-//   dx[i][pix] = sum_kk A[i][kk] * B[kk][pix],   kk = t*OC + o (tap-major),
+//   dx[i][pix] = sum_kk A[i][kk] * B[kk][pix],   kk = t*OCP + o (tap-major),
 //   A[i][kk] = W[o][i][kh][kw],  B[kk][pix] = dz[n][o][ho][wo] (0 off the map),
-// so no matrix-core work is spent on the stride's empty taps.
-// Grid: x = pixel tiles, y = channel tiles, z = phase.
+// so no matrix-core work is spent on the stride's empty taps.  OCP is C_out
+// rounded up to the K tile (rows o >= C_out are zero), so a K tile never
+// straddles two taps: the tap and the tile's first channel are uniform over
+// the work-group and the per-element index math is an add.
+// Grid: x = pixel tiles, y = channel tiles x K splits, z = phase.  With one
+// split the result goes to dx (overwrite or add); with several, each split
+// writes its partial at the pixel's dx position in ws[split] and
+// dx_splitk_reduce adds them up in order.
 // ---------------------------------------------------------------------------
 template <class TS>
 __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const float* __restrict__ wt,
                                                            const float* __restrict__ dz,
                                                            float* __restrict__ dx,
+                                                           float* __restrict__ ws, int ctiles,
+                                                           int ksplits, int pixtiles,
                                                            int accumulate) {
   static_assert(kThreads % TS::BN == 0 && kThreads % TS::BK == 0, "thread/tile mapping");
   __shared__ float lds[TS::LDS_FLOATS];
-  float* As = lds;
-  float* Bs = lds + TS::BK * TS::LDA;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
 
+  // id = ((phase * pixtiles + pixtile) * ksplits + split) * ctiles + ctile: the channel
+  // tiles of one pixel tile read the same dz and are dispatched together.
   const int S = g.S;
-  const int ph = blockIdx.z / S, pw = blockIdx.z % S;
+  int lid = blockIdx.x;
+  const int ctile = lid % ctiles;
+  lid /= ctiles;
+  const int split = lid % ksplits;
+  lid /= ksplits;
+  const int pixtile = lid % pixtiles, phase = lid / pixtiles;
+  const int ph = phase / S, pw = phase % S;
   const int HH = (g.H - ph + S - 1) / S, WW = (g.W - pw + S - 1) / S;
   const int npix = g.N * HH * WW;
-  const int n0 = blockIdx.x * TS::BN;
+  const int n0 = pixtile * TS::BN;
   if (n0 >= npix) return;  // this phase has fewer pixels than the grid covers
-  const int m0 = blockIdx.y * TS::BM;
+  const int m0 = ctile * TS::BM;
   const int rh = (ph + g.P) % S, rw = (pw + g.P) % S;
   const int nkh = rh < g.K ? (g.K - rh + S - 1) / S : 0;
   const int nkw = rw < g.K ? (g.K - rw + S - 1) / S : 0;
   const int bh = (ph + g.P - rh) / S, bw = (pw + g.P - rw) / S;
-  const int ntap = nkh * nkw;
-  const int KT = g.OC * ntap;
+  const int OCP = (g.OC + TS::BK - 1) / TS::BK * TS::BK;
+  const int KT = OCP * nkh * nkw;
+  const int kchunk = ((KT + ksplits - 1) / ksplits + TS::BK - 1) / TS::BK * TS::BK;
+  const int kbeg = split * kchunk, kend = min(KT, kbeg + kchunk);
 
   // B: this thread stages pixel column pcol for K rows krow0 + KSTEP*r.
   constexpr int KSTEP = kThreads / TS::BN;
@@ -186,75 +225,171 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
   // A: this thread stages K column acol for channel rows m0 + irow0 + ISTEP*r.
   constexpr int ISTEP = kThreads / TS::BK;
   const int acol = tid % TS::BK, irow0 = tid / TS::BK;
+  const int KK = g.K * g.K;
 
   float ra[TS::A_PER_T], rb[TS::B_PER_T];
+  // Out-of-range elements load from a clamped (valid) address and are then
+  // replaced by zero: no divergent branches around the loads.
   auto load = [&](int k0) {
+    const int t = k0 / OCP, o0 = k0 - t * OCP;  // uniform over the work-group
+    const int th = t / nkw, tw = t - th * nkw;
+    const int kh = rh + S * th, kw = rw + S * tw;
     {  // A = weights
-      const int kk = k0 + acol;
-      const int t = kk / g.OC, o = kk - t * g.OC;
-      const int th = nkw ? t / nkw : 0, tw = t - th * nkw;
-      const int kh = rh + S * th, kw = rw + S * tw;
-      const bool kv = kk < KT;
-      const float* wp = wt + ((int64_t)o * g.C * g.K + kh) * g.K + kw;
+      const int o = o0 + acol;
+      const bool ov = o < g.OC;
+      const float* wp = wt + ((int64_t)(ov ? o : 0) * g.C) * KK + kh * g.K + kw;
 #pragma unroll
       for (int r = 0; r < TS::A_PER_T; ++r) {
         const int i = m0 + irow0 + ISTEP * r;
-        ra[r] = (kv && i < g.C) ? wp[(int64_t)i * g.K * g.K] : 0.f;
+        const bool ok = ov && i < g.C;
+        const float v = wp[(int64_t)(ok ? i : 0) * KK];
+        ra[r] = ok ? v : 0.f;
       }
     }
     {  // B = deltas
-      int kk = k0 + krow0;
-      int t = kk / g.OC, o = kk - t * g.OC;
+      const int ho = hob - th, wo = wob - tw;
+      const bool ok = pv && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
+      const float* bp = dzb + (ok ? ho * g.OW + wo : 0);
 #pragma unroll
       for (int r = 0; r < TS::B_PER_T; ++r) {
-        const int th = nkw ? t / nkw : 0, tw = t - th * nkw;
-        const int ho = hob - th, wo = wob - tw;
-        const bool ok = pv && (k0 + krow0 + KSTEP * r) < KT && (unsigned)ho < (unsigned)g.OH &&
-                        (unsigned)wo < (unsigned)g.OW;
-        rb[r] = ok ? dzb[(int64_t)o * g.OHW + ho * g.OW + wo] : 0.f;
-        o += KSTEP;
-        while (o >= g.OC) {
-          o -= g.OC;
-          ++t;
-        }
+        const int o = o0 + krow0 + KSTEP * r;
+        const bool okr = ok && o < g.OC;
+        const float v = bp[(int64_t)(okr ? o : 0) * g.OHW];
+        rb[r] = okr ? v : 0.f;
       }
     }
   };
-  auto store = [&]() {
+  auto store = [&](float* buf) {
+    float* As = buf;
+    float* Bs = buf + TS::BK * TS::LDA;
 #pragma unroll
     for (int r = 0; r < TS::A_PER_T; ++r) As[acol * TS::LDA + irow0 + ISTEP * r] = ra[r];
 #pragma unroll
     for (int r = 0; r < TS::B_PER_T; ++r) Bs[(krow0 + KSTEP * r) * TS::LDB + pcol] = rb[r];
   };
 
-  f32x16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  if (KT > 0) load(0);
-  for (int k0 = 0; k0 < KT; k0 += TS::BK) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (k0 + TS::BK < KT) load(k0 + TS::BK);
-    mfma_tile<TS>(As, Bs, acc, wm, wn, wk, lane);
-  }
+  Acc<TS> acc;
+  acc.zero();
+  gemm_mainloop<TS>(lds, kbeg, kend, [&](int64_t k0) { load((int)k0); }, store, acc, wm, wn, wk,
+                    lane);
   reduce_wk<TS>(acc, lds, wm, wn, wk, lane);
   if (wk == 0) {
-    const int p = n0 + wn * 32 + acc_col(lane);
-    if (p < npix) {
+#pragma unroll
+    for (int aj = 0; aj < TS::RN; ++aj) {
+      const int p = n0 + acc_n0<TS>(wn, aj) + acc_col(lane);
+      if (p >= npix) continue;
       const int b = p / (HH * WW);
       const int r2 = p - b * HH * WW;
       const int hh = r2 / WW, ww = r2 - hh * WW;
       const int h = ph + S * hh, w = pw + S * ww;
-      float* dst = dx + ((int64_t)b * g.C) * g.HW + h * g.W + w;
+      const int64_t pix_off = ((int64_t)b * g.C) * g.HW + h * g.W + w;
+      float* dst = ksplits == 1 ? dx + pix_off : ws + (int64_t)split * g.N * g.C * g.HW + pix_off;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = m0 + wm * 32 + acc_row(r, lane);
-        if (i < g.C) {
-          float* d = dst + (int64_t)i * g.HW;
-          *d = accumulate ? *d + acc[r] : acc[r];
+      for (int ai = 0; ai < TS::RM; ++ai) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = m0 + acc_m0<TS>(wm, ai) + acc_row(r, lane);
+          if (i < g.C) {
+            float* d = dst + (int64_t)i * g.HW;
+            const float v = acc.v[ai][aj][r];
+            *d = (ksplits == 1 && accumulate) ? *d + v : v;
+          }
         }
       }
+    }
+  }
+}
+
+// dx[e] (+)= sum over splits s (in order) of ws[s][e].
+__global__ __launch_bounds__(kThreads) void dx_splitk_reduce(float* __restrict__ dx,
+                                                             const float* __restrict__ ws,
+                                                             int splits, int64_t n,
+                                                             int accumulate) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += stride) {
+    float s = 0.f;
+    for (int sp = 0; sp < splits; ++sp) s += ws[(int64_t)sp * n + e];
+    dx[e] = accumulate ? dx[e] + s : s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Input gradient for very few input channels (CI <= 4) at stride 1, e.g. the
+// image gradient of a network's first layer.  Such a layer is HBM-bound
+// (reads dz with C_out channels, writes only CI), and a matrix-core tile would
+// waste all but CI of its 32 rows, so it runs on the vector ALUs:
+//   dx[n][i][h][w] = sum_{o,kh,kw} W[o][i][kh][kw] * dz[n][o][h+p-kh][w+p-kw].
+// A work-group owns a 16 x 64 pixel tile of one image; dz for 8 output channels
+// at a time is staged in LDS with its (K-1) halo, and each thread accumulates 4
+// neighbouring pixels of one row for all CI channels.  Weights are read with
+// block-uniform addresses.
+// ---------------------------------------------------------------------------
+constexpr int kScTH = 16, kScTW = 64, kScOCB = 8;
+
+template <int CI, int K>
+__global__ __launch_bounds__(kThreads) void conv_dx_smallc_kernel(ConvGeom g,
+                                                                  const float* __restrict__ wt,
+                                                                  const float* __restrict__ dz,
+                                                                  float* __restrict__ dx,
+                                                                  int tiles_w, int tiles_h,
+                                                                  int accumulate) {
+  constexpr int LH = kScTH + K - 1, LW = kScTW + K - 1, LWP = LW + 1;
+  __shared__ float tile[kScOCB][LH][LWP];
+  const int tid = threadIdx.x;
+  const int tw_i = blockIdx.x % tiles_w;
+  const int th_i = (blockIdx.x / tiles_w) % tiles_h;
+  const int b = blockIdx.x / (tiles_w * tiles_h);
+  const int h0 = th_i * kScTH, w0 = tw_i * kScTW;
+  const int ho0 = h0 + g.P - (K - 1), wo0 = w0 + g.P - (K - 1);
+  const int r = tid / (kScTW / 4), c0 = (tid % (kScTW / 4)) * 4;
+
+  float acc[CI][4];
+#pragma unroll
+  for (int i = 0; i < CI; ++i)
+#pragma unroll
+    for (int px = 0; px < 4; ++px) acc[i][px] = 0.f;
+
+  const float* dzb = dz + (int64_t)b * g.OC * g.OHW;
+  for (int ob = 0; ob < g.OC; ob += kScOCB) {
+    __syncthreads();
+    for (int e = tid; e < kScOCB * LH * LW; e += kThreads) {
+      const int o = e / (LH * LW), rem = e - o * (LH * LW);
+      const int rr = rem / LW, cc = rem - rr * LW;
+      const int ho = ho0 + rr, wo = wo0 + cc;
+      float v = 0.f;
+      if (ob + o < g.OC && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW)
+        v = dzb[(int64_t)(ob + o) * g.OHW + ho * g.OW + wo];
+      tile[o][rr][cc] = v;
+    }
+    __syncthreads();
+    const int onum = min(kScOCB, g.OC - ob);
+    for (int o = 0; o < onum; ++o) {
+      const float* wo_ = wt + (int64_t)(ob + o) * CI * K * K;
+#pragma unroll
+      for (int kh = 0; kh < K; ++kh) {
+        float seg[4 + K - 1];
+#pragma unroll
+        for (int j = 0; j < 4 + K - 1; ++j) seg[j] = tile[o][r + K - 1 - kh][c0 + j];
+#pragma unroll
+        for (int kw = 0; kw < K; ++kw) {
+#pragma unroll
+          for (int i = 0; i < CI; ++i) {
+            const float wv = wo_[(i * K + kh) * K + kw];
+#pragma unroll
+            for (int px = 0; px < 4; ++px) acc[i][px] += wv * seg[px + K - 1 - kw];
+          }
+        }
+      }
+    }
+  }
+  const int h = h0 + r;
+  if (h >= g.H) return;
+#pragma unroll
+  for (int i = 0; i < CI; ++i) {
+    float* d = dx + ((int64_t)b * CI + i) * g.HW + (int64_t)h * g.W + w0 + c0;
+#pragma unroll
+    for (int px = 0; px < 4; ++px) {
+      if (w0 + c0 + px < g.W) d[px] = accumulate ? d[px] + acc[i][px] : acc[i][px];
     }
   }
 }
@@ -281,46 +416,63 @@ ConvGeom make_geom(const cbb_conv_desc& d) {
   return g;
 }
 
-enum DwShape { DW_64x64 = 0, DW_32x32 = 1, DW_32x64 = 2, DW_64x32 = 3 };
+// Weight-gradient tile shapes: BM x BN (x BK) and the TileShape that realises them.
+enum DwShape { DW_64x64 = 0, DW_32x32, DW_32x64, DW_64x32, DW_128x64, DW_64x128, DW_128x128, DW_NSHAPES };
+static const int kDwCand[DW_NSHAPES][3] = {{64, 64, 32},  {32, 32, 128}, {32, 64, 64}, {64, 32, 64},
+                                           {128, 64, 32}, {64, 128, 32}, {128, 128, 32}};
 
 struct DwPlan {
-  int shape, bm, bn, bk, tiles_m, tiles_n, splits;
+  int shape, bm, bn, bk, tiles_m, tiles_n, splits, groups;
   int64_t k_chunk;
 };
 
 static DwPlan plan_dw(const ConvGeom& g) {
-  static const int cand[4][3] = {{64, 64, 32}, {32, 32, 128}, {32, 64, 64}, {64, 32, 64}};
   DwPlan best{};
   double best_cost = 1e300;
-  for (int s = 0; s < 4; ++s) {
-    const int bm = cand[s][0], bn = cand[s][1];
+  for (int s = 0; s < DW_NSHAPES; ++s) {
+    const int bm = kDwCand[s][0], bn = kDwCand[s][1];
     const double tm = (double)ceil_div(g.OC, bm), tn = (double)ceil_div(g.J, bn);
-    // padded matrix-core work, lightly favouring larger tiles (less re-staging)
-    const double cost = tm * bm * tn * bn * (1.0 + 0.15 * (64.0 * 64.0) / (bm * bn));
+    // padded matrix-core work, weighted by how well the tile shape feeds the
+    // matrix cores (bigger wave tiles re-read LDS less per instruction)
+    // measured on MI355X: 64x64 is the sweet spot; larger tiles did not pay off
+    const double eff = (bm * bn > 64 * 64) ? 1.3 : (bm * bn == 64 * 64 ? 1.0 : 1.15);
+    const double cost = tm * bm * tn * bn * eff;
     if (cost < best_cost) {
       best_cost = cost;
       best.shape = s;
       best.bm = bm;
       best.bn = bn;
-      best.bk = cand[s][2];
+      best.bk = kDwCand[s][2];
     }
   }
   best.tiles_m = (int)ceil_div(g.OC, best.bm);
   best.tiles_n = (int)ceil_div(g.J, best.bn);
   const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
   const int64_t ktiles = ceil_div(g.Q, best.bk);
-  int64_t splits = ceil_div(1024, tiles);                  // aim at ~4 work-groups per CU
+  const int64_t target = 1024;  // work-groups
+  int64_t splits = ceil_div(target, tiles);
   splits = std::min<int64_t>(splits, std::max<int64_t>(1, ktiles / 4));  // >= 4 K tiles each
   splits = std::max<int64_t>(1, std::min<int64_t>(splits, 4096));
   int64_t chunk = ceil_div(ktiles, splits) * best.bk;
   best.splits = (int)ceil_div(g.Q, chunk);
   best.k_chunk = chunk;
+  best.groups = best.splits > kReduceGroup ? (int)ceil_div(best.splits, kReduceGroup) : 0;
   return best;
 }
 
 size_t conv_dw_workspace(const ConvGeom& g) {
   const DwPlan p = plan_dw(g);
-  return p.splits > 1 ? (size_t)p.splits * g.OC * g.J * sizeof(float) : 0;
+  if (p.splits == 1) return 0;
+  const size_t mn = (size_t)g.OC * g.J;
+  return ((size_t)p.splits + p.groups) * mn * sizeof(float);
+}
+
+template <class TS>
+static void launch_dw_tile(const ConvGeom& g, const DwPlan& p, const float* x, const float* dz,
+                           float* out, int direct, hipStream_t st) {
+  const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n * p.splits);
+  conv_dw_kernel<TS><<<blocks, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk, p.tiles_n, p.splits,
+                                                  direct);
 }
 
 int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
@@ -328,46 +480,121 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
   const DwPlan p = plan_dw(g);
   const int direct = p.splits == 1;
   float* out = direct ? dw : ws;
-  dim3 grid(p.tiles_m * p.tiles_n, p.splits);
   switch (p.shape) {
-    case DW_64x64:
-      conv_dw_kernel<TileShape<2, 2, 1>><<<grid, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk,
-                                                                     p.tiles_n, direct);
-      break;
-    case DW_32x32:
-      conv_dw_kernel<TileShape<1, 1, 4>><<<grid, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk,
-                                                                     p.tiles_n, direct);
-      break;
-    case DW_32x64:
-      conv_dw_kernel<TileShape<1, 2, 2>><<<grid, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk,
-                                                                     p.tiles_n, direct);
-      break;
-    default:
-      conv_dw_kernel<TileShape<2, 1, 2>><<<grid, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk,
-                                                                     p.tiles_n, direct);
-      break;
+    case DW_64x64: launch_dw_tile<TileShape<2, 2, 1>>(g, p, x, dz, out, direct, st); break;
+    case DW_32x32: launch_dw_tile<TileShape<1, 1, 4>>(g, p, x, dz, out, direct, st); break;
+    case DW_32x64: launch_dw_tile<TileShape<1, 2, 2>>(g, p, x, dz, out, direct, st); break;
+    case DW_64x32: launch_dw_tile<TileShape<2, 1, 2>>(g, p, x, dz, out, direct, st); break;
+    case DW_128x64: launch_dw_tile<TileShape<2, 2, 1, 1, 2, 1>>(g, p, x, dz, out, direct, st); break;
+    case DW_64x128: launch_dw_tile<TileShape<2, 2, 1, 1, 1, 2>>(g, p, x, dz, out, direct, st); break;
+    default: launch_dw_tile<TileShape<2, 2, 1, 1, 2, 2>>(g, p, x, dz, out, direct, st); break;
   }
   int rc = check_launch("conv_dw_kernel");
   if (rc != CBB_OK || direct) return rc;
   const int64_t mn = (int64_t)g.OC * g.J;
-  dw_splitk_reduce<<<(unsigned)ceil_div(mn, kThreads), kThreads, 0, st>>>(dw, ws, p.splits, mn);
-  return check_launch("dw_splitk_reduce");
+  const unsigned eblocks = (unsigned)ceil_div(mn, kThreads);
+  if (p.groups == 0) {
+    dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, ws, p.splits, mn);
+    return check_launch("dw_reduce_l2");
+  }
+  float* part2 = ws + (int64_t)p.splits * mn;
+  dw_reduce_l1<<<dim3(eblocks, p.groups), kThreads, 0, st>>>(ws, part2, p.splits, mn);
+  rc = check_launch("dw_reduce_l1");
+  if (rc) return rc;
+  dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, part2, p.groups, mn);
+  return check_launch("dw_reduce_l2");
+}
+
+// ----------------------------------------------------------------------------- dX planning
+enum DxKind { DX_SMALLC = 0, DX_32x128, DX_64x64 };
+
+struct DxPlan {
+  int kind, bm, bn, bk, ctiles, pixtiles, ksplits;
+};
+
+static bool smallc_ok(const ConvGeom& g) {
+  return g.C <= 4 && g.S == 1 && (g.K == 1 || g.K == 3 || g.K == 5 || g.K == 7);
+}
+
+static DxPlan plan_dx(const ConvGeom& g) {
+  DxPlan p{};
+  if (smallc_ok(g)) {
+    p.kind = DX_SMALLC;
+    p.ksplits = 1;
+    return p;
+  }
+  const int S = g.S;
+  const int64_t maxpix = (int64_t)g.N * ((g.H + S - 1) / S) * ((g.W + S - 1) / S);
+  p.bk = 32;
+  // Measured on MI355X: one 32x32 block per wave beats larger wave tiles here (the
+  // gathers, not the matrix cores, set the pace).
+  if (g.C <= 32) {
+    p.kind = DX_32x128; p.bm = 32; p.bn = 128;
+  } else {
+    p.kind = DX_64x64; p.bm = 64; p.bn = 64;
+  }
+  p.ctiles = (int)ceil_div(g.C, p.bm);
+  p.pixtiles = (int)ceil_div(maxpix, p.bn);
+  const int64_t blocks = (int64_t)p.ctiles * p.pixtiles * S * S;
+  // average K per phase, in tiles
+  const int64_t ocp = ceil_div(g.OC, p.bk) * p.bk;
+  const int64_t ktiles = std::max<int64_t>(1, ceil_div(ocp * g.K * g.K / (S * S), p.bk));
+  const int64_t target = 2048;   // work-groups in flight
+  int64_t ks = ceil_div(target, blocks);
+  ks = std::min<int64_t>(ks, std::max<int64_t>(1, ktiles / 4));  // >= 4 K tiles each
+  p.ksplits = (int)std::max<int64_t>(1, std::min<int64_t>(ks, 16));
+  return p;
+}
+
+size_t conv_dx_workspace(const ConvGeom& g) {
+  const DxPlan p = plan_dx(g);
+  if (p.ksplits <= 1) return 0;
+  return (size_t)p.ksplits * g.N * g.C * g.HW * sizeof(float);
+}
+
+template <int CI>
+static void launch_smallc(const ConvGeom& g, const float* wt, const float* dz, float* dx,
+                          int accumulate, hipStream_t st) {
+  const int tiles_w = (int)ceil_div(g.W, kScTW), tiles_h = (int)ceil_div(g.H, kScTH);
+  const unsigned blocks = (unsigned)(g.N * tiles_w * tiles_h);
+  switch (g.K) {
+    case 1: conv_dx_smallc_kernel<CI, 1><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, tiles_w, tiles_h, accumulate); break;
+    case 3: conv_dx_smallc_kernel<CI, 3><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, tiles_w, tiles_h, accumulate); break;
+    case 5: conv_dx_smallc_kernel<CI, 5><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, tiles_w, tiles_h, accumulate); break;
+    default: conv_dx_smallc_kernel<CI, 7><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, tiles_w, tiles_h, accumulate); break;
+  }
+}
+
+template <class TS>
+static void launch_dx_mfma(const ConvGeom& g, const DxPlan& p, const float* wt, const float* dz,
+                           float* dx, float* ws, int accumulate, hipStream_t st) {
+  const unsigned blocks = (unsigned)((int64_t)p.pixtiles * g.S * g.S * p.ksplits * p.ctiles);
+  conv_dx_kernel<TS><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, p.ctiles, p.ksplits,
+                                                  p.pixtiles, accumulate);
 }
 
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
-                   hipStream_t st) {
-  const int S = g.S;
-  const int maxpix = g.N * ((g.H + S - 1) / S) * ((g.W + S - 1) / S);
-  if (g.C <= 32) {
-    using TS = TileShape<1, 4, 1>;  // 32 channels x 128 pixels
-    dim3 grid((unsigned)ceil_div(maxpix, TS::BN), (unsigned)ceil_div(g.C, TS::BM), S * S);
-    conv_dx_kernel<TS><<<grid, kThreads, 0, st>>>(g, wt, dz, dx, accumulate);
-  } else {
-    using TS = TileShape<2, 2, 1>;  // 64 channels x 64 pixels
-    dim3 grid((unsigned)ceil_div(maxpix, TS::BN), (unsigned)ceil_div(g.C, TS::BM), S * S);
-    conv_dx_kernel<TS><<<grid, kThreads, 0, st>>>(g, wt, dz, dx, accumulate);
+                   float* ws, hipStream_t st) {
+  const DxPlan p = plan_dx(g);
+  if (p.kind == DX_SMALLC) {
+    switch (g.C) {
+      case 1: launch_smallc<1>(g, wt, dz, dx, accumulate, st); break;
+      case 2: launch_smallc<2>(g, wt, dz, dx, accumulate, st); break;
+      case 3: launch_smallc<3>(g, wt, dz, dx, accumulate, st); break;
+      default: launch_smallc<4>(g, wt, dz, dx, accumulate, st); break;
+    }
+    return check_launch("conv_dx_smallc_kernel");
   }
-  return check_launch("conv_dx_kernel");
+  if (p.kind == DX_32x128)
+    launch_dx_mfma<TileShape<1, 4, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
+  else
+    launch_dx_mfma<TileShape<2, 2, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
+  int rc = check_launch("conv_dx_kernel");
+  if (rc || p.ksplits == 1) return rc;
+  const int64_t n = (int64_t)g.N * g.C * g.HW;
+  const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
+  dx_splitk_reduce<<<blocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
+  return check_launch("dx_splitk_reduce");
 }
 
 }  // namespace cbb

@@ -206,15 +206,14 @@ struct GemmArgs {
 
 __global__ __launch_bounds__(kThreads) void strided_gemm_kernel(GemmArgs a, int tiles_n) {
   using TS = TileShape<2, 2, 1>;
-  __shared__ float lds[TS::LDS_FLOATS];
+  __shared__ float lds[TS::BUF_FLOATS];
   float* As = lds;
   float* Bs = lds + TS::BK * TS::LDA;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % TS::WM, wn = wave / TS::WM, wk = 0;
   const int m0 = (blockIdx.x / tiles_n) * TS::BM, n0 = (blockIdx.x % tiles_n) * TS::BN;
-  f32x16 acc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  Acc<TS> acc;
+  acc.zero();
   for (int k0 = 0; k0 < a.K; k0 += TS::BK) {
     __syncthreads();
 #pragma unroll
@@ -241,7 +240,7 @@ __global__ __launch_bounds__(kThreads) void strided_gemm_kernel(GemmArgs a, int 
     const int m = m0 + wm * 32 + acc_row(r, lane);
     if (m < a.M) {
       float* c = a.C + (int64_t)m * a.ldc + n;
-      *c = a.accumulate ? *c + acc[r] : acc[r];
+      *c = a.accumulate ? *c + acc.v[0][0][r] : acc.v[0][0][r];
     }
   }
 }

@@ -146,7 +146,8 @@ class Runner:
         mark(stage == "dW", False)
         if dx is not None:
             mark(stage == "dX", True)
-            cbb.conv_backward_data(e["desc"], e["w"], dz, dx, dx_accumulate, stream)
+            cbb.conv_backward_data(e["desc"], e["w"], dz, dx, dx_accumulate, self.workspace,
+                                   stream)
             mark(stage == "dX", False)
 
     def _dz_of(self, li: int, delta):

@@ -145,10 +145,11 @@ int cbb_conv_act_bn_backward(const cbb_conv_desc* desc, const float* y, const fl
  * dz [N,O,OH,OW] and x [N,C,H,W]. */
 int cbb_conv_backward_weights(const cbb_conv_desc* desc, const float* x, const float* dz,
                               float* dw, void* workspace, size_t workspace_bytes, void* stream);
-/* Stage 3, input gradient: dx [N,C,H,W] (+)= col2im(W^T dz); uses no workspace.
- * dx must not overlap w or dz. */
+/* Stage 3, input gradient: dx [N,C,H,W] (+)= col2im(W^T dz).  dx must not
+ * overlap w, dz or the workspace. */
 int cbb_conv_backward_data(const cbb_conv_desc* desc, const float* w, const float* dz, float* dx,
-                           int dx_accumulate, void* stream);
+                           int dx_accumulate, void* workspace, size_t workspace_bytes,
+                           void* stream);
 
 /* Activation gradient alone (gradient_array, [P1] sections 3.1 and 7):
  * g[i] = delta[i] * act'(y[i]) for i < count.  g may equal delta. */

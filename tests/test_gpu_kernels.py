@@ -35,6 +35,11 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (4, 129, 6, 6, 130, 3, 1, 1, True, "leaky"),
     (1, 3, 5, 5, 1, 5, 1, 0, False, "linear"),
     (2, 16, 21, 21, 8, 4, 2, 1, True, "leaky"),
+    (2, 64, 13, 13, 128, 3, 1, 1, True, "leaky"),    # dX: tap-aligned K, split over K
+    (2, 32, 20, 20, 256, 3, 2, 1, True, "leaky"),    # dX: stride-2 phases, tap-aligned, split
+    (4, 3, 128, 128, 8, 3, 1, 1, True, "leaky"),     # dW: many splits (two-level reduce)
+    (2, 2, 19, 70, 5, 7, 1, 3, False, "relu"),       # dX: 2-channel direct kernel, k = 7
+    (3, 4, 9, 9, 6, 1, 1, 0, True, "logistic"),      # dX: 4-channel direct kernel, k = 1
 ]
 
 
@@ -88,7 +93,8 @@ def test_conv_block_backward_parity(case):
             assert_close(k, got[k], ref[k] if k != "dgamma" else ref["dgamma"])
 
 
-@pytest.mark.parametrize("case", [CONV_CASES[1], CONV_CASES[3], CONV_CASES[6]])
+@pytest.mark.parametrize("case", [CONV_CASES[0], CONV_CASES[1], CONV_CASES[3], CONV_CASES[5],
+                                  CONV_CASES[6], CONV_CASES[12], CONV_CASES[13]])
 def test_conv_block_accumulate_inplace_and_no_dx(case):
     torch = require_gpu()
     announce(f"conv_block accumulate/in-place {case}")
