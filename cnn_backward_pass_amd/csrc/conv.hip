@@ -300,6 +300,240 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
   }
 }
 
+// ---------------------------------------------------------------------------
+// Input gradient of a 3x3, pad-1 convolution at stride 1 or 2 ("tile-direct").
+// The GEMM above fetches dz once per tap; here a work-group stages one dz tile
+// (with its halo) and the matching weights in LDS per chunk of 16 output
+// channels and runs all nine taps from LDS, so every dz element crosses the
+// memory system once per work-group instead of nine times.
+//
+// A fragment is 32 input pixels that take the same taps; lane l of the MFMA B
+// operand reads pixel l of a fragment at LDS address base(pixel) + tap offset,
+// the tap offset being a compile-time constant (stride 2) or a uniform value.
+//   S = 1: a work-group owns 128*F consecutive pixels (row-major) of one image
+//          of width <= 62; wave w owns fragments w*F .. w*F+F-1.
+//   S = 2: a work-group owns an 8*FR x 64 region; each wave owns, for each of
+//          the four phases (h mod 2, w mod 2), FR phase rows of 32 pixels, so
+//          the waves do equal work (the phases take 1, 2, 2 and 4 taps).
+// Each fragment accumulates RM blocks of 32 input channels.  No split over K:
+// a work-group sums all output channels in a fixed order.
+// ---------------------------------------------------------------------------
+template <int S, int F, int RM>
+struct Dx3Cfg {
+  // output channels per LDS chunk
+  static constexpr int OCB = (S == 1) ? 8 : 16, BMC = 32 * RM, BMCP = BMC + 1;
+  static constexpr int NFRAG = (S == 1) ? F : 4 * F;       // fragments per wave
+  // stride 2: region 8F rows x 64 cols -> dz tile (4F + 1) rows x 33 cols
+  static constexpr int ZC2 = 33, ZR2 = 4 * F + 1;
+  // LDS floats per channel plane (odd): stride 1 holds (rows spanned + 2) x (W + 2),
+  // checked on the host (dx3_s1_fits); stride 2 holds the fixed tile
+  static constexpr int ZPLANE = (S == 1) ? 513 : ZR2 * ZC2;
+  static constexpr int ZFLOATS = OCB * ZPLANE;
+  static constexpr int WFLOATS = 9 * OCB * BMC;
+  static constexpr int ZPT = (ZFLOATS + kThreads - 1) / kThreads;   // staging registers
+  static constexpr int WPT = (OCB * BMC * 9 + kThreads - 1) / kThreads;
+};
+
+// Stride-1 tile of 128*F pixels of a W-wide image spans at most floor((128F-1)/W) + 2
+// rows; with the 3x3 halo the dz tile is (that + 2) x (W + 2).
+static bool dx3_s1_fits(int W, int F, int zplane) {
+  if (W < 8 || W > 62) return false;
+  const int rows = (128 * F - 1) / W + 2;
+  return (rows + 2) * (W + 2) <= zplane;
+}
+
+template <int S, int F, int RM>
+__global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const float* __restrict__ wt,
+                                                            const float* __restrict__ dz,
+                                                            float* __restrict__ dx,
+                                                            float* __restrict__ ws,
+                                                            int accumulate, int tiles_per_img,
+                                                            int tiles_w, int ksplits) {
+  using C = Dx3Cfg<S, F, RM>;
+  __shared__ float Z[C::ZFLOATS];
+  __shared__ float Wl[C::WFLOATS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, khalf = lane >> 5;
+  const int ctiles = (g.C + C::BMC - 1) / C::BMC;
+  const int ctile = blockIdx.x % ctiles;
+  const int split = (blockIdx.x / ctiles) % ksplits;
+  const int t = blockIdx.x / (ctiles * ksplits);
+  const int b = t / tiles_per_img, tt = t - b * tiles_per_img;
+  const int i0 = ctile * C::BMC;
+
+  // ---- geometry of the dz tile and of this lane's pixels
+  int zr0, zc0, ZR, ZC;        // tile origin in dz, tile size
+  int pbase[C::NFRAG];         // LDS offset of the lane's pixel (tap (1,1) at stride 1)
+  int ph_[C::NFRAG], pw_[C::NFRAG], prow[C::NFRAG], pcol[C::NFRAG];
+  bool pval[C::NFRAG];
+  if constexpr (S == 1) {
+    const int p0 = tt * 128 * F;                       // first pixel of the tile
+    const int hmin = p0 / g.W;
+    zr0 = hmin - 1;
+    zc0 = -1;
+    ZC = g.W + 2;
+    const int plast = min(p0 + 128 * F, g.H * g.W) - 1;
+    ZR = plast / g.W - hmin + 3;
+#pragma unroll
+    for (int f = 0; f < C::NFRAG; ++f) {
+      const int p = p0 + (wave * F + f) * 32 + col;
+      const int h = p / g.W, w = p - h * g.W;
+      pval[f] = p < g.H * g.W;
+      prow[f] = h;
+      pcol[f] = w;
+      // dz[h+1-kh][w+1-kw] sits at Z row (h-hmin)+2-kh, col w+2-kw
+      pbase[f] = pval[f] ? (h - hmin) * ZC + w : 0;
+      ph_[f] = pw_[f] = 0;
+    }
+  } else {
+    const int th = tt / tiles_w, tw = tt - th * tiles_w;
+    const int h0 = th * 8 * F, w0 = tw * 64;
+    zr0 = h0 / 2;
+    zc0 = w0 / 2;
+    ZR = C::ZR2;
+    ZC = C::ZC2;
+#pragma unroll
+    for (int f = 0; f < C::NFRAG; ++f) {
+      const int phase = f % 4, fr = f / 4;             // fragment = (phase, phase row)
+      const int ph = phase >> 1, pw = phase & 1;
+      const int rr = wave * F + fr;                    // phase row within the region
+      const int h = h0 + 2 * rr + ph, w = w0 + pw + 2 * col;
+      pval[f] = h < g.H && w < g.W;
+      prow[f] = h;
+      pcol[f] = w;
+      ph_[f] = ph;
+      pw_[f] = pw;
+      // dz[(h+1-kh)/2][(w+1-kw)/2] sits at Z row rr + (ph+1-kh)/2, col col + (pw+1-kw)/2
+      pbase[f] = rr * C::ZC2 + col;
+    }
+  }
+
+  // ---- staging: registers <- global (next chunk), LDS <- registers.  The host
+  // guarantees C % BMC == 0 and OC % OCB == 0, so only the image border masks.
+  // A staged element's offset inside a chunk does not depend on the chunk:
+  // computed once (-1 = zero padding).
+  const float* dzb = dz + (int64_t)b * g.OC * g.OHW;
+  float rz[C::ZPT], rw[C::WPT];
+  const int zcount = C::OCB * ZR * ZC;
+  int zofs[C::ZPT];
+#pragma unroll
+  for (int r = 0; r < C::ZPT; ++r) {
+    const int e = tid + kThreads * r;
+    const int o = e / (ZR * ZC), rem = e - o * (ZR * ZC);
+    const int zr = rem / ZC, zc = rem - zr * ZC;
+    const int ho = zr0 + zr, wo = zc0 + zc;
+    const bool ok = e < zcount && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
+    zofs[r] = ok ? o * g.OHW + ho * g.OW + wo : -1;
+  }
+  auto load = [&](int o0) {
+    const float* zb = dzb + (int64_t)o0 * g.OHW;
+#pragma unroll
+    for (int r = 0; r < C::ZPT; ++r) {
+      const float v = zb[max(zofs[r], 0)];
+      rz[r] = zofs[r] >= 0 ? v : 0.f;
+    }
+    const float* wb = wt + ((int64_t)o0 * g.C + i0) * 9;
+#pragma unroll
+    for (int r = 0; r < C::WPT; ++r) {
+      const int e = tid + kThreads * r;                // (o, i, tap), tap fastest
+      const int o = e / (C::BMC * 9), rem = e - o * (C::BMC * 9);
+      const bool ok = e < C::OCB * C::BMC * 9;
+      const float v = wb[ok ? o * g.C * 9 + rem : 0];
+      rw[r] = ok ? v : 0.f;
+    }
+  };
+  // LDS keeps the staging order: Z planes of ZR*ZC floats, weights as [o][i][tap]
+  // (a lane reads weights 9 floats apart: no bank conflicts).
+  auto store = [&]() {
+#pragma unroll
+    for (int r = 0; r < C::ZPT; ++r) {
+      const int e = tid + kThreads * r;
+      if (e < zcount) Z[e] = rz[r];
+    }
+#pragma unroll
+    for (int r = 0; r < C::WPT; ++r) {
+      const int e = tid + kThreads * r;
+      if (e < C::OCB * C::BMC * 9) Wl[e] = rw[r];
+    }
+  };
+  const int zplane = ZR * ZC;
+
+  f32x16 acc[C::NFRAG][RM];
+#pragma unroll
+  for (int f = 0; f < C::NFRAG; ++f)
+#pragma unroll
+    for (int m = 0; m < RM; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[f][m][r] = 0.f;
+
+  // this split's output-channel chunks [c0, c1)
+  const int nch = (g.OC + C::OCB - 1) / C::OCB;
+  const int cps = (nch + ksplits - 1) / ksplits;
+  const int c0 = min(nch, split * cps), c1 = min(nch, c0 + cps);
+  if (c0 < c1) {
+    load(c0 * C::OCB);
+    store();
+  }
+  __syncthreads();
+  for (int c = c0; c < c1; ++c) {
+    if (c + 1 < c1) load((c + 1) * C::OCB);   // in flight during the matrix-core work
+#pragma unroll
+    for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw) {
+        const int tap = kh * 3 + kw;
+        __builtin_amdgcn_sched_barrier(0);  // one tap at a time: bounds the live ranges
+#pragma unroll
+        for (int kk = 0; kk < C::OCB / 2; ++kk) {
+          const int o = 2 * kk + khalf;
+          float a[RM];
+#pragma unroll
+          for (int m = 0; m < RM; ++m) a[m] = Wl[(o * C::BMC + m * 32 + col) * 9 + tap];
+#pragma unroll
+          for (int f = 0; f < C::NFRAG; ++f) {
+            int off;
+            if constexpr (S == 1) {
+              off = (2 - kh) * ZC + (2 - kw);
+            } else {
+              // taps of another phase contribute nothing to this fragment
+              if (((ph_[f] + 1 - kh) & 1) || ((pw_[f] + 1 - kw) & 1)) continue;
+              off = ((ph_[f] + 1 - kh) >> 1) * C::ZC2 + ((pw_[f] + 1 - kw) >> 1);
+            }
+            const float bv = Z[o * zplane + pbase[f] + off];
+#pragma unroll
+            for (int m = 0; m < RM; ++m)
+              acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], bv, acc[f][m], 0, 0, 0);
+          }
+        }
+      }
+    __syncthreads();
+    if (c + 1 < c1) {
+      store();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds pixel `col` of each fragment, channels acc_row(r)
+  // with several splits each writes its partial at the pixel's dx position in ws[split]
+  float* out = ksplits == 1 ? dx : ws + (int64_t)split * g.N * g.C * g.HW;
+  const bool add = ksplits == 1 && accumulate;
+#pragma unroll
+  for (int f = 0; f < C::NFRAG; ++f) {
+    if (!pval[f]) continue;
+    float* d = out + ((int64_t)b * g.C) * g.HW + prow[f] * g.W + pcol[f];
+#pragma unroll
+    for (int m = 0; m < RM; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + m * 32 + acc_row(r, lane);
+        if (i < g.C) {
+          float* q = d + (int64_t)i * g.HW;
+          *q = add ? *q + acc[f][m][r] : acc[f][m][r];
+        }
+      }
+  }
+}
+
 // dx[e] (+)= sum over splits s (in order) of ws[s][e].
 __global__ __launch_bounds__(kThreads) void dx_splitk_reduce(float* __restrict__ dx,
                                                              const float* __restrict__ ws,
@@ -506,7 +740,7 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
 }
 
 // ----------------------------------------------------------------------------- dX planning
-enum DxKind { DX_SMALLC = 0, DX_32x128, DX_64x64 };
+enum DxKind { DX_SMALLC = 0, DX_32x128, DX_64x64, DX_D3S1, DX_D3S2 };
 
 struct DxPlan {
   int kind, bm, bn, bk, ctiles, pixtiles, ksplits;
@@ -521,6 +755,31 @@ static DxPlan plan_dx(const ConvGeom& g) {
   if (smallc_ok(g)) {
     p.kind = DX_SMALLC;
     p.ksplits = 1;
+    return p;
+  }
+  // tile-direct 3x3: split the output channels when the grid cannot fill the GPU
+  // (~2 work-groups per CU are resident), keeping >= 4 chunks per split
+  auto direct_splits = [&](int64_t blocks, int nchunks) {
+    int64_t ks = ceil_div(512, blocks);
+    ks = std::min<int64_t>(ks, std::max<int64_t>(1, nchunks / 4));
+    return (int)std::max<int64_t>(1, std::min<int64_t>(ks, 16));
+  };
+  if (g.K == 3 && g.P == 1 && g.S == 1 && dx3_s1_fits(g.W, 2, Dx3Cfg<1, 2, 2>::ZPLANE) &&
+      g.C % Dx3Cfg<1, 2, 2>::BMC == 0 && g.OC % Dx3Cfg<1, 2, 2>::OCB == 0) {
+    using Cf = Dx3Cfg<1, 2, 2>;
+    p.kind = DX_D3S1;
+    p.pixtiles = (int)ceil_div((int64_t)g.H * g.W, 128 * 2);
+    p.ctiles = g.C / Cf::BMC;
+    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB);
+    return p;
+  }
+  if (g.K == 3 && g.P == 1 && g.S == 2 && g.C % Dx3Cfg<2, 1, 1>::BMC == 0 &&
+      g.OC % Dx3Cfg<2, 1, 1>::OCB == 0) {
+    using Cf = Dx3Cfg<2, 1, 1>;
+    p.kind = DX_D3S2;
+    p.pixtiles = (int)(ceil_div(g.H, 8) * ceil_div(g.W, 64));
+    p.ctiles = g.C / Cf::BMC;
+    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB);
     return p;
   }
   const int S = g.S;
@@ -576,6 +835,22 @@ static void launch_dx_mfma(const ConvGeom& g, const DxPlan& p, const float* wt, 
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
                    float* ws, hipStream_t st) {
   const DxPlan p = plan_dx(g);
+  if (p.kind == DX_D3S1 || p.kind == DX_D3S2) {
+    const unsigned blocks = (unsigned)((int64_t)g.N * p.pixtiles * p.ctiles * p.ksplits);
+    if (p.kind == DX_D3S1)
+      conv_dx3_direct<1, 2, 2><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, accumulate,
+                                                            p.pixtiles, 0, p.ksplits);
+    else
+      conv_dx3_direct<2, 1, 1><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, accumulate,
+                                                            p.pixtiles, (int)ceil_div(g.W, 64),
+                                                            p.ksplits);
+    int rc = check_launch("conv_dx3_direct");
+    if (rc || p.ksplits == 1) return rc;
+    const int64_t n = (int64_t)g.N * g.C * g.HW;
+    const unsigned rblocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
+    dx_splitk_reduce<<<rblocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
+    return check_launch("dx_splitk_reduce");
+  }
   if (p.kind == DX_SMALLC) {
     switch (g.C) {
       case 1: launch_smallc<1>(g, wt, dz, dx, accumulate, st); break;

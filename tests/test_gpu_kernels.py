@@ -40,6 +40,11 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (4, 3, 128, 128, 8, 3, 1, 1, True, "leaky"),     # dW: many splits (two-level reduce)
     (2, 2, 19, 70, 5, 7, 1, 3, False, "relu"),       # dX: 2-channel direct kernel, k = 7
     (3, 4, 9, 9, 6, 1, 1, 0, True, "logistic"),      # dX: 4-channel direct kernel, k = 1
+    (1, 64, 17, 23, 32, 3, 1, 1, True, "leaky"),     # dX: 3x3 tile-direct, ragged width
+    (2, 32, 19, 37, 16, 3, 2, 1, True, "leaky"),     # dX: 3x3 stride-2 tile-direct, odd sizes
+    (1, 64, 9, 62, 16, 3, 1, 1, False, "linear"),    # dX: tile-direct at the widest image
+    (3, 32, 7, 8, 48, 3, 1, 1, True, "relu"),        # dX: tile-direct at the narrowest image
+    (2, 64, 12, 130, 64, 3, 2, 1, True, "leaky"),    # dX: stride-2, width beyond one region
 ]
 
 
@@ -94,7 +99,8 @@ def test_conv_block_backward_parity(case):
 
 
 @pytest.mark.parametrize("case", [CONV_CASES[0], CONV_CASES[1], CONV_CASES[3], CONV_CASES[5],
-                                  CONV_CASES[6], CONV_CASES[12], CONV_CASES[13]])
+                                  CONV_CASES[6], CONV_CASES[12], CONV_CASES[13], CONV_CASES[17],
+                                  CONV_CASES[18]])
 def test_conv_block_accumulate_inplace_and_no_dx(case):
     torch = require_gpu()
     announce(f"conv_block accumulate/in-place {case}")
