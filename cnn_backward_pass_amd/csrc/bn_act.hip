@@ -31,64 +31,83 @@ __device__ __forceinline__ float act_grad(int act, float slope, float y) {
   }
 }
 
+// Work split of one channel: its N planes of HW floats are cut into `nseg`
+// segments.  Large planes (HW >= kPlaneSplit) are cut into `parts` equal ranges
+// per plane, one segment each; small planes are grouped `group` whole planes per
+// segment.  A segment is thus a list of contiguous ranges inside planes, which
+// a work-group streams with unrolled float4 accesses (no per-element index math).
+constexpr int kPlaneSplit = 16384;
+
 struct SegGeom {
   int N, C, HW;
   int64_t M;      // N*HW elements per channel
   int nseg;       // segments per channel
-  int64_t seg;    // elements per segment (multiple of 4 when VEC)
+  int parts;      // ranges per plane (large planes), else 1
+  int group;      // planes per segment (small planes), else 1
+  int chunk;      // elements per range (multiple of 4 when VEC), large planes
 };
 
-// Visit the elements of segment `sg` of channel `c`: f(offset) for scalar
-// offsets, in float4 groups when VEC (HW % 4 == 0, so a group never crosses a
-// plane).  Thread t takes groups t, t+256, ... of the segment.
+// Visit segment `sg` of channel `c`: f(offset, vec4) for every element (VEC:
+// every float4) of its ranges; thread t takes elements t, t+256, ... unrolled 4x.
 template <bool VEC, class F>
 __device__ __forceinline__ void for_segment(const SegGeom& s, int c, int sg, F&& f) {
-  const int64_t e0 = (int64_t)sg * s.seg;
-  const int64_t e1 = min(s.M, e0 + s.seg);
-  if constexpr (VEC) {
-    const int HW4 = s.HW >> 2;
-    int64_t g = (e0 >> 2) + threadIdx.x;
-    const int64_t gend = e1 >> 2;
-    if (g >= gend) return;
-    int n = (int)(g / HW4);
-    int i4 = (int)(g - (int64_t)n * HW4);
-    for (; g < gend; g += kThreads) {
-      f(((int64_t)n * s.C + c) * s.HW + 4 * i4);
-      i4 += kThreads;
-      while (i4 >= HW4) {
-        i4 -= HW4;
-        ++n;
-      }
-    }
+  int n0, n1, r0, r1;
+  if (s.parts > 1) {
+    n0 = sg / s.parts;
+    n1 = n0 + 1;
+    const int part = sg - n0 * s.parts;
+    r0 = part * s.chunk;
+    r1 = min(s.HW, r0 + s.chunk);
   } else {
-    int64_t e = e0 + threadIdx.x;
-    if (e >= e1) return;
-    int n = (int)(e / s.HW);
-    int i = (int)(e - (int64_t)n * s.HW);
-    for (; e < e1; e += kThreads) {
-      f(((int64_t)n * s.C + c) * s.HW + i);
-      i += kThreads;
-      while (i >= s.HW) {
-        i -= s.HW;
-        ++n;
+    n0 = sg * s.group;
+    n1 = min(s.N, n0 + s.group);
+    r0 = 0;
+    r1 = s.HW;
+  }
+  for (int n = n0; n < n1; ++n) {
+    const int64_t base = ((int64_t)n * s.C + c) * s.HW;
+    if constexpr (VEC) {
+      const int q0 = r0 >> 2, q1 = r1 >> 2;   // float4 range
+      int q = q0 + threadIdx.x;
+      for (; q + 3 * kThreads < q1; q += 4 * kThreads) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) f(base + 4 * (int64_t)(q + u * kThreads));
       }
+      for (; q < q1; q += kThreads) f(base + 4 * (int64_t)q);
+    } else {
+      int e = r0 + threadIdx.x;
+      for (; e + 3 * kThreads < r1; e += 4 * kThreads) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) f(base + e + u * kThreads);
+      }
+      for (; e < r1; e += kThreads) f(base + e);
     }
   }
 }
 
-template <bool VEC>
+typedef float nf4 __attribute__((ext_vector_type(4)));
+// streaming (non-temporal) 16-byte load: the data is touched once per pass
+__device__ __forceinline__ float4 ld4(const float* p) {
+  const nf4 v = __builtin_nontemporal_load(reinterpret_cast<const nf4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// ACT and HAS_X (BN) are compile-time so the streaming loop has no branches
+// around its loads.
+template <bool VEC, int ACT, bool HAS_X>
 __global__ __launch_bounds__(kThreads) void actbn_reduce(SegGeom s, const float* __restrict__ delta,
                                                          const float* __restrict__ y,
-                                                         const float* __restrict__ xn, int act,
+                                                         const float* __restrict__ xn,
                                                          float slope, float2* __restrict__ part) {
   const int c = blockIdx.x / s.nseg, sg = blockIdx.x % s.nseg;
   float sg_ = 0.f, sgx = 0.f;
-  const bool has_y = act != CBB_ACT_LINEAR, has_x = xn != nullptr;
+  constexpr int act = ACT;
+  constexpr bool has_y = ACT != CBB_ACT_LINEAR, has_x = HAS_X;
   if constexpr (VEC) {
     for_segment<true>(s, c, sg, [&](int64_t o) {
-      float4 d = *reinterpret_cast<const float4*>(delta + o);
+      float4 d = ld4(delta + o);
       if (has_y) {
-        const float4 yy = *reinterpret_cast<const float4*>(y + o);
+        const float4 yy = ld4(y + o);
         d.x *= act_grad(act, slope, yy.x);
         d.y *= act_grad(act, slope, yy.y);
         d.z *= act_grad(act, slope, yy.z);
@@ -96,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void actbn_reduce(SegGeom s, const float*
       }
       sg_ += (d.x + d.y) + (d.z + d.w);
       if (has_x) {
-        const float4 x = *reinterpret_cast<const float4*>(xn + o);
+        const float4 x = ld4(xn + o);
         sgx += (d.x * x.x + d.y * x.y) + (d.z * x.z + d.w * x.w);
       }
     });
@@ -131,13 +150,15 @@ __device__ __forceinline__ float2 fold_partials(const float2* __restrict__ part,
 // bn = 1: dz = a*g + b + cc*x_norm with a = gamma/sqrt(var+eps), b = -a*mean(g),
 //         cc = -a*mean(g*x_norm); dgamma[c] += sum g*x_norm, dbeta[c] += sum g.
 // bn = 0: dz = g (only launched when act != LINEAR), db[c] += sum g.
-template <bool VEC>
+template <bool VEC, int ACT, bool BN>
 __global__ __launch_bounds__(kThreads) void actbn_apply(
     SegGeom s, const float* delta, const float* __restrict__ y,
-    const float* __restrict__ xn, int act, float slope, const float2* __restrict__ part,
-    const float* __restrict__ var, const float* __restrict__ gamma, float eps, int bn,
+    const float* __restrict__ xn, float slope, const float2* __restrict__ part,
+    const float* __restrict__ var, const float* __restrict__ gamma, float eps,
     float* dz /* may alias delta */, float* __restrict__ dgamma, float* __restrict__ dbeta_or_db,
     int write_dz) {
+  constexpr int act = ACT;
+  constexpr bool bn = BN;
   const int c = blockIdx.x / s.nseg, sg = blockIdx.x % s.nseg;
   __shared__ float red[4];
   const float2 sums = fold_partials(part, c, s.nseg, red);
@@ -153,19 +174,19 @@ __global__ __launch_bounds__(kThreads) void actbn_apply(
     kb = -ka * (sums.x * inv_m);
     kc = -ka * (sums.y * inv_m);
   }
-  const bool has_y = act != CBB_ACT_LINEAR;
+  constexpr bool has_y = ACT != CBB_ACT_LINEAR;
   if constexpr (VEC) {
     for_segment<true>(s, c, sg, [&](int64_t o) {
-      float4 d = *reinterpret_cast<const float4*>(delta + o);
+      float4 d = ld4(delta + o);
       if (has_y) {
-        const float4 yy = *reinterpret_cast<const float4*>(y + o);
+        const float4 yy = ld4(y + o);
         d.x *= act_grad(act, slope, yy.x);
         d.y *= act_grad(act, slope, yy.y);
         d.z *= act_grad(act, slope, yy.z);
         d.w *= act_grad(act, slope, yy.w);
       }
       if (bn) {
-        const float4 x = *reinterpret_cast<const float4*>(xn + o);
+        const float4 x = ld4(xn + o);
         d.x = ka * d.x + kb + kc * x.x;
         d.y = ka * d.y + kb + kc * x.y;
         d.z = ka * d.z + kb + kc * x.z;
@@ -222,14 +243,21 @@ SegGeom plan_seg(int N, int C, int64_t HW) {
   s.C = C;
   s.HW = (int)HW;
   s.M = (int64_t)N * HW;
-  // ~2048 work-groups in total, each streaming at least 4096 elements.
-  int64_t nseg = ceil_div(2048, C);
-  nseg = std::min<int64_t>(nseg, std::max<int64_t>(1, s.M / 4096));
-  nseg = std::max<int64_t>(1, nseg);
-  int64_t seg = ceil_div(s.M, nseg);
-  seg = ceil_div(seg, 4) * 4;
-  s.seg = seg;
-  s.nseg = (int)ceil_div(s.M, seg);
+  // ~2048 work-groups in total, each streaming at least ~4096 elements
+  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(ceil_div(2048, C), s.M / 4096));
+  if (HW >= kPlaneSplit) {
+    int64_t parts = std::max<int64_t>(1, ceil_div(target, N));
+    int64_t chunk = ceil_div(ceil_div(HW, parts), 4) * 4;
+    s.parts = (int)ceil_div(HW, chunk);
+    s.chunk = (int)chunk;
+    s.group = 1;
+    s.nseg = N * s.parts;
+  } else {
+    s.parts = 1;
+    s.chunk = (int)HW;
+    s.group = (int)std::max<int64_t>(1, ceil_div(N, target));
+    s.nseg = (int)ceil_div(N, s.group);
+  }
   return s;
 }
 
@@ -242,6 +270,40 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // g/BN stage of a conv block, or a standalone BN backward (act = LINEAR).
 // Writes dz (when needed), adds to dgamma/dbeta (bn) or db (!bn).
+template <bool VEC, int ACT, bool BN>
+static void launch_actbn_t(const SegGeom& s, unsigned blocks, const float* delta, const float* y,
+                           const float* xn, float slope, const float* var, const float* gamma,
+                           float eps, float* dz, float* dgamma, float* dbeta_or_db, float2* part,
+                           int write_dz, hipStream_t st) {
+  actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, BN ? xn : nullptr, slope,
+                                                          part);
+  actbn_apply<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, slope, part, var, gamma,
+                                                         eps, dz, dgamma, dbeta_or_db, write_dz);
+}
+
+template <bool VEC>
+static void launch_actbn_v(const SegGeom& s, unsigned blocks, int act, int bn, const float* delta,
+                           const float* y, const float* xn, float slope, const float* var,
+                           const float* gamma, float eps, float* dz, float* dgamma,
+                           float* dbeta_or_db, float2* part, int write_dz, hipStream_t st) {
+#define CBB_ACTBN(A, B)                                                                   \
+  launch_actbn_t<VEC, A, B>(s, blocks, delta, y, xn, slope, var, gamma, eps, dz, dgamma, \
+                            dbeta_or_db, part, write_dz, st)
+  switch (act * 2 + (bn ? 1 : 0)) {
+    case CBB_ACT_LINEAR * 2: CBB_ACTBN(CBB_ACT_LINEAR, false); break;
+    case CBB_ACT_LINEAR * 2 + 1: CBB_ACTBN(CBB_ACT_LINEAR, true); break;
+    case CBB_ACT_LEAKY * 2: CBB_ACTBN(CBB_ACT_LEAKY, false); break;
+    case CBB_ACT_LEAKY * 2 + 1: CBB_ACTBN(CBB_ACT_LEAKY, true); break;
+    case CBB_ACT_LOGISTIC * 2: CBB_ACTBN(CBB_ACT_LOGISTIC, false); break;
+    case CBB_ACT_LOGISTIC * 2 + 1: CBB_ACTBN(CBB_ACT_LOGISTIC, true); break;
+    case CBB_ACT_RELU * 2: CBB_ACTBN(CBB_ACT_RELU, false); break;
+    default: CBB_ACTBN(CBB_ACT_RELU, true); break;
+  }
+#undef CBB_ACTBN
+}
+
+// g/BN stage of a conv block, or a standalone BN backward (act = LINEAR).
+// Writes dz (when needed), adds to dgamma/dbeta (bn) or db (!bn).
 int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, const float* xn,
                  int act, float slope, const float* var, const float* gamma, float eps, int bn,
                  float* dz, float* dgamma, float* dbeta_or_db, void* ws, hipStream_t st) {
@@ -250,21 +312,14 @@ int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, c
   const bool vec = (HW % 4 == 0) && aligned16(delta) && (!y || aligned16(y)) &&
                    (!xn || aligned16(xn)) && (!dz || aligned16(dz));
   const unsigned blocks = (unsigned)((int64_t)C * s.nseg);
-  const float* xn_r = bn ? xn : nullptr;
-  if (vec)
-    actbn_reduce<true><<<blocks, kThreads, 0, st>>>(s, delta, y, xn_r, act, slope, part);
-  else
-    actbn_reduce<false><<<blocks, kThreads, 0, st>>>(s, delta, y, xn_r, act, slope, part);
-  int rc = check_launch("actbn_reduce");
-  if (rc) return rc;
   const int write_dz = bn || act != CBB_ACT_LINEAR;
   if (vec)
-    actbn_apply<true><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, act, slope, part, var, gamma,
-                                                   eps, bn, dz, dgamma, dbeta_or_db, write_dz);
+    launch_actbn_v<true>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma,
+                         dbeta_or_db, part, write_dz, st);
   else
-    actbn_apply<false><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, act, slope, part, var, gamma,
-                                                    eps, bn, dz, dgamma, dbeta_or_db, write_dz);
-  return check_launch("actbn_apply");
+    launch_actbn_v<false>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma,
+                          dbeta_or_db, part, write_dz, st);
+  return check_launch("actbn_reduce/actbn_apply");
 }
 
 int launch_act_backward(int act, float slope, const float* y, const float* delta, float* g,

@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
     const float* zb = dzb + (int64_t)o0 * g.OHW;
 #pragma unroll
     for (int r = 0; r < C::ZPT; ++r) {
-      const float v = zb[max(zofs[r], 0)];
+      const float v = zb[(unsigned)max(zofs[r], 0)];
       rz[r] = zofs[r] >= 0 ? v : 0.f;
     }
     const float* wb = wt + ((int64_t)o0 * g.C + i0) * 9;
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
       const int e = tid + kThreads * r;                // (o, i, tap), tap fastest
       const int o = e / (C::BMC * 9), rem = e - o * (C::BMC * 9);
       const bool ok = e < C::OCB * C::BMC * 9;
-      const float v = wb[ok ? o * g.C * 9 + rem : 0];
+      const float v = wb[(unsigned)(ok ? o * g.C * 9 + rem : 0)];
       rw[r] = ok ? v : 0.f;
     }
   };
@@ -584,16 +584,40 @@ __global__ __launch_bounds__(kThreads) void conv_dx_smallc_kernel(ConvGeom g,
     for (int px = 0; px < 4; ++px) acc[i][px] = 0.f;
 
   const float* dzb = dz + (int64_t)b * g.OC * g.OHW;
+  // Staging: each wave copies whole tile rows, lane = column (and column + 64 for
+  // the halo), so the per-element index math is one add.
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wo_a = wo0 + lane;
+  const bool ca = (unsigned)wo_a < (unsigned)g.OW;
+  constexpr int ROWS = kScOCB * LH;                  // tile rows per chunk
+  constexpr int RB = 6;                              // rows in flight per wave
   for (int ob = 0; ob < g.OC; ob += kScOCB) {
     __syncthreads();
-    for (int e = tid; e < kScOCB * LH * LW; e += kThreads) {
-      const int o = e / (LH * LW), rem = e - o * (LH * LW);
-      const int rr = rem / LW, cc = rem - rr * LW;
+    for (int row0 = wave; row0 < ROWS; row0 += 4 * RB) {
+      float v[RB];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int row = row0 + 4 * u;
+        const int o = row / LH, rr = row - o * LH;
+        const int ho = ho0 + rr;
+        const bool ok = row < ROWS && ob + o < g.OC && (unsigned)ho < (unsigned)g.OH && ca;
+        const float t = dzb[ok ? (int64_t)(ob + o) * g.OHW + ho * g.OW + wo_a : 0];
+        v[u] = ok ? t : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        const int row = row0 + 4 * u;
+        if (row < ROWS) (&tile[0][0][0])[(row / LH) * LH * LWP + (row % LH) * LWP + lane] = v[u];
+      }
+    }
+    // the K-1 halo columns beyond the first 64
+    for (int e = tid; e < ROWS * (LW - 64); e += kThreads) {
+      const int row = e / (LW - 64), cc = 64 + e % (LW - 64);
+      const int o = row / LH, rr = row - o * LH;
       const int ho = ho0 + rr, wo = wo0 + cc;
-      float v = 0.f;
-      if (ob + o < g.OC && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW)
-        v = dzb[(int64_t)(ob + o) * g.OHW + ho * g.OW + wo];
-      tile[o][rr][cc] = v;
+      const bool ok = ob + o < g.OC && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
+      const float t = dzb[ok ? (int64_t)(ob + o) * g.OHW + ho * g.OW + wo : 0];
+      tile[o][rr][cc] = ok ? t : 0.f;
     }
     __syncthreads();
     const int onum = min(kScOCB, g.OC - ob);
