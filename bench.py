@@ -39,8 +39,51 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-batch", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle baseline (whole suite steps)")
+    ap.add_argument("--stage", default=None,
+                    help="profiling mode: run only WORKLOAD.LAYER.STAGE (e.g. yolov3_stem.1.dW) "
+                         "--reps times and print its event timings; no JSON line")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="profiling mode: run a plain device copy of this many bytes --reps times "
+                         "(calibrates the HBM byte counters); no JSON line")
+    ap.add_argument("--reps", type=int, default=5)
     return ap.parse_args()
+
+
+def profile_stage(spec, reps, torch):
+    """Run one stage of one conv layer on its own, ``reps`` times (for rocprofv3 counter
+    passes).  For dW / dX the layer's act+BN stage runs once first to fill dz."""
+    name, li, stage = spec.split(".")
+    li = int(li)
+    from cnn_backward_pass_amd import synth
+    from cnn_backward_pass_amd.workloads import Runner
+    r = Runner(name, synth.inputs(name), synth.saved_standins(name), "cuda:0")
+    r.reset()
+    if stage != "act_bn":
+        r.run_stage(li, "act_bn")
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        r.run_stage(li, stage)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    flops, nbytes = stage_work(r, li, stage)
+    print(f"[stage] {spec}: ms {' '.join(f'{m:.4f}' for m in ms)}; algorithmic "
+          f"{flops / 1e9:.3f} GFLOP, {nbytes / 1e6:.1f} MB", flush=True)
+
+
+def profile_copy(nbytes, reps, torch):
+    n = nbytes // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"[copy] {reps} copies of {n * 4} bytes", flush=True)
 
 
 def build_runners(device):
@@ -91,34 +134,35 @@ def time_stages(runners, torch, reps=3):
     return sorted(res, reverse=True)
 
 
-def cpu_baseline(sample_batch):
-    """The oracle (parity mode: double arithmetic on the fp32 inputs) on every workload at a
-    reduced batch; GFLOP/s = the sample's algorithmic FLOPs / wall time."""
+def cpu_baseline(min_seconds=10.0, max_reps=4):
+    """The oracle (double arithmetic on the fp32 inputs) on one full step of the suite at
+    full batch, repeated until ``min_seconds`` of CPU time have passed (at most
+    ``max_reps`` steps); GFLOP/s = the algorithmic FLOPs of the steps run / wall time."""
     import oracle
     import oracle.model as M
     from cnn_backward_pass_amd import synth
     oracle.build()
-    flops = 0.0
-    t_total = 0.0
+    cases = []
+    step_flops = 0.0
     for name in ORDER:
         wl = synth.WORKLOADS[name]
-        b = sample_batch if name != "lenet" else 8 * sample_batch
-        import dataclasses
-        wls = dataclasses.replace(wl, batch=b)
-        inp = synth.inputs(name, scale_batch=b)
-        saved = synth.saved_standins(name, scale_batch=b)
-        t0 = time.perf_counter()
-        M.workload_backward(wls, inp, saved, inp.get("delta"))
-        t_total += time.perf_counter() - t0
+        cases.append((wl, synth.inputs(name), synth.saved_standins(name)))
         for li, c in enumerate(wl.convs):
-            macs = b * c.out_c * c.out_h * c.out_w * c.in_c * c.k * c.k
-            flops += 2.0 * macs * (1 if (name == "lenet" and li == 0) else 2)
+            macs = wl.batch * c.out_c * c.out_h * c.out_w * c.in_c * c.k * c.k
+            step_flops += 2.0 * macs * (1 if (name == "lenet" and li == 0) else 2)
         if name == "lenet":
-            flops += sum(2.0 * 2 * b * i * o for i, o in synth.LENET_FC)
-    return {"value": flops / t_total / 1e9, "unit": "GFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"all five workloads at batch {sample_batch} (LeNet {8 * sample_batch}), "
-                      f"{flops / 1e9:.2f} GFLOP in {t_total:.1f} s, double precision",
+            step_flops += sum(2.0 * 2 * wl.batch * i * o for i, o in synth.LENET_FC)
+    t_total, reps = 0.0, 0
+    while reps < max_reps and (reps == 0 or t_total < min_seconds):
+        t0 = time.perf_counter()
+        for wl, inp, saved in cases:
+            M.workload_backward(wl, inp, saved, inp.get("delta"))
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": step_flops * reps / t_total / 1e9, "unit": "GFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{reps} full step(s) of the five-workload suite at full batch, "
+                      f"{step_flops * reps / 1e9:.1f} GFLOP in {t_total:.1f} s, double precision",
             "seconds": t_total, "host_cpus": os.cpu_count()}
 
 
@@ -136,6 +180,12 @@ def main():
     cbb.lib()
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.stage:
+        profile_stage(args.stage, args.reps, torch)
+        return
+    if args.copy_bytes:
+        profile_copy(args.copy_bytes, args.reps, torch)
+        return
     runners = build_runners(dev)
     step_flops = sum(r.flops() for r in runners.values())
     for r in runners.values():
@@ -146,9 +196,13 @@ def main():
             r.step()
     torch.cuda.synchronize()
 
-    # Find the dominant stage (largest in-place duration) before the timed region.
+    # Find the dominant kernel before the timed region: the longest dW or dX stage
+    # (each is one kernel plus, for split reductions, a short ordered-sum kernel);
+    # act+BN stages are two streaming kernels of comparable size and are reported
+    # separately (their longest kernel is shorter than the dominant conv kernel).
     stages = time_stages(runners, torch)
-    dom_ms, dom_name, dom_li, dom_stage = stages[0]
+    conv_stages = [st for st in stages if st[3] in ("dW", "dX")]
+    dom_ms, dom_name, dom_li, dom_stage = conv_stages[0]
     print(f"[bench] dominant stage {dom_name}.{dom_li}.{dom_stage} {dom_ms:.3f} ms",
           file=sys.stderr, flush=True)
 
@@ -200,7 +254,11 @@ def main():
         roof = {"bound": "mfma", "achieved": flops / (dom_avg_ms * 1e-3) / 1e12,
                 "peak": PEAK_MFMA_F32 / 1e12, "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    # HBM bytes per launch of this stage from the committed rocprofv3 counter summary,
+    # reported only while the kernel sources are the ones that were profiled.
+    from cnn_backward_pass_amd import profsum
+    rec = profsum.load_traffic(f"{dom_name}.{dom_li}.{dom_stage}")
+    roof["traffic"] = None if rec is None else rec["traffic_bytes"]
     roof["kernel"] = f"{dom_name}.{runners[dom_name].wl.convs[dom_li].name}.{dom_stage}"
     roof["avg_ms"] = dom_avg_ms
     roof["algorithmic_flops"] = flops
@@ -215,10 +273,14 @@ def main():
                                    "b8@52x52, yolov3_stem b16@416x416, yolov3_head b8@26x26",
                        "gflop_per_step": round(step_flops / 1e9, 3), "parallelism": "none"},
             "roofline": roof, "per_workload": per,
-            "top_stages_ms": [[f"{n}.{li}.{st}", round(ms, 4)] for ms, n, li, st in stages[:8]]}
+            "top_stages_ms": [[f"{n}.{li}.{st}", round(ms, 4)] for ms, n, li, st in stages[:8]],
+            "act_bn_stages": {f"{n}.{li}": {
+                "ms": round(ms, 4),
+                "algorithmic_GBps": round(stage_work(runners[n], li, st)[1] / (ms * 1e-3) / 1e9, 1)}
+                for ms, n, li, st in stages if st == "act_bn" and ms > 0.05}}
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(args.cpu_sample_batch)
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

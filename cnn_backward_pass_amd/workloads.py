@@ -90,8 +90,8 @@ class Runner:
             c1, c2 = wl.convs
             self.d_pool2 = torch.empty((n, c2.out_c, c2.out_h // 2, c2.out_w // 2), dtype=f32,
                                        device=device)
-            self.d_c2 = torch.empty((n, c2.out_c, c2.out_h, c2.out_w), dtype=f32, device=device)
-            self.d_c1 = torch.empty((n, c1.out_c, c1.out_h, c1.out_w), dtype=f32, device=device)
+            self.d_c2 = torch.zeros((n, c2.out_c, c2.out_h, c2.out_w), dtype=f32, device=device)
+            self.d_c1 = torch.zeros((n, c1.out_c, c1.out_h, c1.out_w), dtype=f32, device=device)
             self.bad_labels = torch.zeros(1, dtype=torch.int32, device=device)
         else:
             self.delta = d(inputs["delta"], f32)
@@ -149,6 +149,33 @@ class Runner:
             cbb.conv_backward_data(e["desc"], e["w"], dz, dx, dx_accumulate, self.workspace,
                                    stream)
             mark(stage == "dX", False)
+
+    def layer_delta(self, li: int):
+        """The gradient buffer a step feeds into conv layer li (its output's delta)."""
+        if self.name == "lenet":
+            return self.d_c2 if li == 1 else self.d_c1
+        if self.name == "darknet53_residual":
+            return self.d_main if li == 1 else self.d_in[1]
+        return self.delta if li == len(self.convs) - 1 else self.d_in[li + 1]
+
+    def run_stage(self, li: int, stage: str, stream=None) -> None:
+        """Enqueue one stage ("act_bn", "dW" or "dX") of conv layer li on its own, on the
+        buffers as they stand (for profiling; dX overwrites the layer's input gradient)."""
+        e = self.convs[li]
+        delta = self.layer_delta(li)
+        dz = delta if e["dz"] is None else e["dz"]
+        if stage == "act_bn":
+            cbb.conv_act_bn_backward(e["desc"], e["y"], e["xhat"], e["var"], e["gamma"], delta,
+                                     e["dz"], e["db"], e["dgamma"], self.workspace, stream)
+        elif stage == "dW":
+            cbb.conv_backward_weights(e["desc"], e["x"], dz, e["dw"], self.workspace, stream)
+        elif stage == "dX":
+            if self.name == "lenet" and li == 0:
+                raise ValueError("the first LeNet conv has no input gradient")
+            cbb.conv_backward_data(e["desc"], e["w"], dz, self.d_in[li], False, self.workspace,
+                                   stream)
+        else:
+            raise ValueError(f"unknown stage {stage!r}")
 
     def _dz_of(self, li: int, delta):
         e = self.convs[li]

@@ -1,0 +1,46 @@
+"""Host logic of the profile summaries: counter scaling and the source-digest gate."""
+import json
+import sqlite3
+import types
+
+from cnn_backward_pass_amd import profsum
+
+
+def _db(path, rows):
+    con = sqlite3.connect(path)
+    con.execute("create table counters_collection (dispatch_id int, kernel_name text, "
+                "counter_name text, value real)")
+    con.executemany("insert into counters_collection values (?,?,?,?)", rows)
+    con.commit()
+    con.close()
+
+
+def test_traffic_scaling_and_gate(tmp_path):
+    k = "void cbb::conv_dw_kernel<X>(int)"
+    fetch = tmp_path / "f.db"
+    write = tmp_path / "w.db"
+    cf = tmp_path / "cf.db"
+    cw = tmp_path / "cw.db"
+    # setup pass (act+BN) excluded; two XCD rows of one dispatch are summed
+    _db(fetch, [(1, "void cbb::actbn_reduce<1>(int)", "FETCH_SIZE", 999.0),
+                (2, k, "FETCH_SIZE", 100.0), (2, k, "FETCH_SIZE", 100.0),
+                (3, k, "FETCH_SIZE", 200.0), (4, "at::native::fill", "FETCH_SIZE", 5.0)])
+    _db(write, [(2, k, "WRITE_SIZE", 10.0), (3, k, "WRITE_SIZE", 10.0)])
+    _db(cf, [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 512.0)])
+    _db(cw, [(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1024.0)])
+    out = tmp_path / "x_hbm_traffic.md"
+    a = types.SimpleNamespace(stage="wl.1.dW", reps=2, fetch=str(fetch), write=str(write),
+                              copy_fetch=str(cf), copy_write=str(cw), copy_bytes=1 << 20,
+                              out=str(out), cmd=["cmd"])
+    profsum.write_traffic(a)
+    rec = profsum.load_traffic("wl.1.dW", str(tmp_path))
+    assert rec is not None
+    assert rec["fetch_bytes"] == 2.0 * 400 * 1024 / 2
+    assert rec["write_bytes"] == 20 * 1024 / 2
+    assert profsum.load_traffic("wl.0.dW", str(tmp_path)) is None
+    # a record taken from other kernel sources is not reported
+    text = out.read_text().replace(rec["sources"], "0" * 16)
+    out.write_text(text)
+    assert profsum.load_traffic("wl.1.dW", str(tmp_path)) is None
+    line = [l for l in text.splitlines() if l.startswith(profsum.TRAFFIC_TAG)][0]
+    assert json.loads(line[len(profsum.TRAFFIC_TAG):])["stage"] == "wl.1.dW"
