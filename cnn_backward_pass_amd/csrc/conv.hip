@@ -155,6 +155,169 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_l2(float* __restrict__ dw,
 }
 
 // ---------------------------------------------------------------------------
+// Weight gradient of a 3x3, pad-1 convolution at stride 1 or 2, row-streaming
+// tile-direct form (same sum as conv_dw_kernel, no im2col gather).
+//
+// A work-group owns a 64 (o) x 32 (i) block of dW for all nine taps and a run
+// of consecutive output rows of one image over a strip of TC output columns.
+// The three input rows under the current output row stay in an LDS ring
+// (input row h in slot h mod 3), so each input row is fetched once per run:
+// per output row only the S new input rows and the dz row are loaded, into
+// registers, while the matrix cores work on the previous row.  The reduction
+// index runs over output positions, two per 32x32x2 step: lane l of a step
+// takes column 2s + l/32 of the row, dz[o = l%32] as the A operand and
+// x[i = l%32] under tap (kh, kw) as the B operand; the tap shifts are constant
+// LDS offsets.  Six waves: (o half) x (tap row kh), each holding the three
+// accumulators of its taps (kw = 0, 1, 2) over the whole row.  Each
+// work-group writes its partial dW block for the ordered split reduction (or
+// adds into dW when it is the only split).
+// ---------------------------------------------------------------------------
+constexpr int kDw3Threads = 384;
+
+template <int S, int TC>
+struct Dw3RowCfg {
+  static constexpr int KS = TC / 2;            // 32x32x2 steps per output row
+  static constexpr int XC = S * (TC - 1) + 3;  // input columns under TC output columns
+  static constexpr int CS = XC | 1;            // channel pitch inside a ring slot (odd)
+  static constexpr int SLOT = 32 * CS;
+  static constexpr int OS = TC + 1;            // dz row pitch per output channel (odd)
+  static constexpr int Z0 = 3 * SLOT;          // dz row buffer after the three slots
+  static constexpr int LDS_FLOATS = Z0 + 64 * OS;
+  static constexpr int XNEW = S * 32 * XC;     // floats of the S input rows fetched per row
+  static constexpr int XPT = (XNEW + kDw3Threads - 1) / kDw3Threads;
+  static constexpr int ZNEW = 64 * TC;
+  static constexpr int ZPT = (ZNEW + kDw3Threads - 1) / kDw3Threads;
+  static_assert(TC % 2 == 0 && (S == 1 || S == 2), "even strip, stride 1 or 2");
+};
+
+template <int S, int TC>
+__global__ __launch_bounds__(kDw3Threads, 2) void conv_dw3_rows(
+    ConvGeom g, const float* __restrict__ x, const float* __restrict__ dz, float* __restrict__ out,
+    int strips, int rchunks, int rlen, int direct) {
+  using Cf = Dw3RowCfg<S, TC>;
+  constexpr int NT = kDw3Threads;
+  __shared__ float lds[Cf::LDS_FLOATS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int oh = wave & 1, kh = wave >> 1;
+  const int cblocks = g.C >> 5, nblk = (g.OC >> 6) * cblocks;
+  const int split = blockIdx.x / nblk, blk = blockIdx.x - split * nblk;
+  const int ob = blk / cblocks, cb = blk - ob * cblocks;
+  const int rc = split % rchunks, ns = split / rchunks;
+  const int strip = ns % strips, n = ns / strips;
+  const int r0 = rc * rlen, r1 = min(g.OH, r0 + rlen);  // non-empty by construction
+  const int oc0 = strip * TC;       // first output column of the strip
+  const int ic0 = oc0 * S - 1;      // input column held in LDS column 0
+  const float* xb = x + ((int64_t)n * g.C + cb * 32) * g.HW;
+  const float* zb = dz + ((int64_t)n * g.OC + ob * 64) * g.OHW;
+
+  // Ring rows fetched with output row q: h = S*q + 2 - S + rr, rr < S.  The
+  // loads go to registers as they are (positions off the image read a clamped
+  // valid address) and the zero padding is applied when they are written to
+  // LDS, so nothing consumes a loaded value before the next row: the loads
+  // stay in flight during the matrix-core work.
+  static_assert(Cf::XPT <= 32 && Cf::ZPT <= 32, "one mask bit per fetched element");
+  float px[Cf::XPT], pz[Cf::ZPT];
+  uint32_t xm = 0, zm = 0;
+  auto fetch = [&](int q) {
+    const int hb = S * q + 2 - S;
+    xm = 0;
+    zm = 0;
+#pragma unroll
+    for (int i = 0; i < Cf::XPT; ++i) {
+      const int e = tid + i * NT;
+      const int rr = e / (32 * Cf::XC), rem = e - rr * (32 * Cf::XC);
+      const int c = rem / Cf::XC, j = rem - c * Cf::XC;
+      const int h = hb + rr, w = ic0 + j;
+      const bool ok = e < Cf::XNEW && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+      px[i] = xb[ok ? c * g.HW + h * g.W + w : 0];
+      xm |= (uint32_t)ok << i;
+    }
+#pragma unroll
+    for (int i = 0; i < Cf::ZPT; ++i) {
+      const int e = tid + i * NT;
+      const int o = e / TC, j = e - o * TC;
+      const bool ok = e < Cf::ZNEW && oc0 + j < g.OW;
+      pz[i] = zb[ok ? o * g.OHW + q * g.OW + oc0 + j : 0];
+      zm |= (uint32_t)ok << i;
+    }
+  };
+  auto commit = [&](int q) {
+    const int hb = S * q + 2 - S;
+#pragma unroll
+    for (int i = 0; i < Cf::XPT; ++i) {
+      const int e = tid + i * NT;
+      const int rr = e / (32 * Cf::XC), rem = e - rr * (32 * Cf::XC);
+      const int c = rem / Cf::XC, j = rem - c * Cf::XC;
+      if (e < Cf::XNEW)
+        lds[((hb + rr + 3) % 3) * Cf::SLOT + c * Cf::CS + j] = ((xm >> i) & 1u) ? px[i] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < Cf::ZPT; ++i) {
+      const int e = tid + i * NT;
+      const int o = e / TC, j = e - o * TC;
+      if (e < Cf::ZNEW) lds[Cf::Z0 + o * Cf::OS + j] = ((zm >> i) & 1u) ? pz[i] : 0.f;
+    }
+  };
+
+  // The 3 - S ring rows of the first output row that no fetch covers.
+  for (int e = tid; e < (3 - S) * 32 * Cf::XC; e += NT) {
+    const int rr = e / (32 * Cf::XC), rem = e - rr * (32 * Cf::XC);
+    const int c = rem / Cf::XC, j = rem - c * Cf::XC;
+    const int h = S * r0 - 1 + rr, w = ic0 + j;
+    const bool ok = (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+    const float v = xb[ok ? c * g.HW + h * g.W + w : 0];
+    lds[((h + 3) % 3) * Cf::SLOT + c * Cf::CS + j] = ok ? v : 0.f;
+  }
+  fetch(r0);
+  commit(r0);
+  __syncthreads();
+  if (r0 + 1 < r1) fetch(r0 + 1);
+
+  f32x16 acc[3];
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+
+  const int abase = Cf::Z0 + (32 * oh + (lane & 31)) * Cf::OS + (lane >> 5);
+  const int bbase = (lane & 31) * Cf::CS + S * (lane >> 5);
+  for (int r = r0; r < r1; ++r) {
+    // input row S*r - 1 + kh sits in slot (S*r + kh + 2) mod 3
+    const int bs = ((S * r + kh + 2) % 3) * Cf::SLOT + bbase;
+#pragma unroll
+    for (int sp = 0; sp < Cf::KS; ++sp) {
+      const float a = lds[abase + 2 * sp];
+      float b[3];
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw) b[kw] = lds[bs + 2 * S * sp + kw];
+#pragma unroll
+      for (int kw = 0; kw < 3; ++kw)
+        acc[kw] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[kw], acc[kw], 0, 0, 0);
+    }
+    __syncthreads();
+    if (r + 1 < r1) {
+      commit(r + 1);
+      __syncthreads();
+      if (r + 2 < r1) fetch(r + 2);
+    }
+  }
+
+  float* dst = direct ? out : out + (int64_t)split * g.OC * g.J;
+  const int i = cb * 32 + (lane & 31);
+#pragma unroll
+  for (int kw = 0; kw < 3; ++kw)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int o = ob * 64 + 32 * oh + acc_row(r, lane);
+      const int64_t e = (int64_t)o * g.J + i * 9 + kh * 3 + kw;
+      if (direct)
+        dst[e] += acc[kw][r];
+      else
+        dst[e] = acc[kw][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Input gradient, gather form of col2im(W^T x delta).  For stride s the input
 // pixels split into s*s phases (h mod s, w mod s); inside a phase every pixel
 // receives the same set of taps kh = rh + s*th (rh = (ph + p) mod s), and the
@@ -682,10 +845,43 @@ static const int kDwCand[DW_NSHAPES][3] = {{64, 64, 32},  {32, 32, 128}, {32, 64
 struct DwPlan {
   int shape, bm, bn, bk, tiles_m, tiles_n, splits, groups;
   int64_t k_chunk;
+  int rows_tc;                // > 0: conv_dw3_rows with this strip width
+  int strips, rchunks, rlen;  // its strips, row runs per (image, strip), rows per run
 };
+
+// Row-streaming 3x3 dW: strip widths compiled in, and when to use it.
+static const int kDw3Tc[] = {64, 52, 32, 26};
+
+static bool plan_dw3_rows(const ConvGeom& g, DwPlan& p) {
+  if (!(g.K == 3 && g.P == 1 && (g.S == 1 || g.S == 2) && g.C % 32 == 0 && g.OC % 64 == 0))
+    return false;
+  int best_tc = 0;
+  int64_t best_pad = 0;
+  for (int tc : kDw3Tc) {
+    const int64_t padded = ceil_div(g.OW, tc) * tc;
+    if (best_tc == 0 || padded < best_pad) {  // first (widest) wins ties
+      best_tc = tc;
+      best_pad = padded;
+    }
+  }
+  if (best_pad * 8 > (int64_t)g.OW * 9) return false;  // > 1/8 of the columns wasted
+  p = DwPlan{};
+  p.rows_tc = best_tc;
+  p.strips = (int)ceil_div(g.OW, best_tc);
+  const int64_t nblk = (int64_t)(g.OC / 64) * (g.C / 32);
+  const int64_t base = (int64_t)g.N * p.strips * nblk;
+  // about 512 work-groups (two resident per CU), at least 4 rows per run
+  int64_t rch = std::max<int64_t>(1, std::min<int64_t>(ceil_div(512, base), g.OH / 4));
+  p.rlen = (int)ceil_div(g.OH, rch);
+  p.rchunks = (int)ceil_div(g.OH, p.rlen);
+  p.splits = g.N * p.strips * p.rchunks;
+  p.groups = p.splits > kReduceGroup ? (int)ceil_div(p.splits, kReduceGroup) : 0;
+  return true;
+}
 
 static DwPlan plan_dw(const ConvGeom& g) {
   DwPlan best{};
+  if (plan_dw3_rows(g, best)) return best;
   double best_cost = 1e300;
   for (int s = 0; s < DW_NSHAPES; ++s) {
     const int bm = kDwCand[s][0], bn = kDwCand[s][1];
@@ -733,11 +929,36 @@ static void launch_dw_tile(const ConvGeom& g, const DwPlan& p, const float* x, c
                                                   direct);
 }
 
+template <int S>
+static void launch_dw3_rows(const ConvGeom& g, const DwPlan& p, const float* x, const float* dz,
+                            float* out, int direct, hipStream_t st) {
+  const unsigned blocks = (unsigned)((int64_t)p.splits * (g.OC / 64) * (g.C / 32));
+#define CBB_DW3(TC)                                                                           \
+  case TC:                                                                                    \
+    conv_dw3_rows<S, TC><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips, p.rchunks,  \
+                                                      p.rlen, direct);                        \
+    break;
+  switch (p.rows_tc) {
+    CBB_DW3(64)
+    CBB_DW3(52)
+    CBB_DW3(32)
+    default:
+      CBB_DW3(26)
+  }
+#undef CBB_DW3
+}
+
 int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
                    hipStream_t st) {
   const DwPlan p = plan_dw(g);
   const int direct = p.splits == 1;
   float* out = direct ? dw : ws;
+  if (p.rows_tc > 0) {
+    if (g.S == 1)
+      launch_dw3_rows<1>(g, p, x, dz, out, direct, st);
+    else
+      launch_dw3_rows<2>(g, p, x, dz, out, direct, st);
+  } else
   switch (p.shape) {
     case DW_64x64: launch_dw_tile<TileShape<2, 2, 1>>(g, p, x, dz, out, direct, st); break;
     case DW_32x32: launch_dw_tile<TileShape<1, 1, 4>>(g, p, x, dz, out, direct, st); break;
@@ -747,7 +968,7 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
     case DW_64x128: launch_dw_tile<TileShape<2, 2, 1, 1, 1, 2>>(g, p, x, dz, out, direct, st); break;
     default: launch_dw_tile<TileShape<2, 2, 1, 1, 2, 2>>(g, p, x, dz, out, direct, st); break;
   }
-  int rc = check_launch("conv_dw_kernel");
+  int rc = check_launch(p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel");
   if (rc != CBB_OK || direct) return rc;
   const int64_t mn = (int64_t)g.OC * g.J;
   const unsigned eblocks = (unsigned)ceil_div(mn, kThreads);

@@ -45,6 +45,14 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (1, 64, 9, 62, 16, 3, 1, 1, False, "linear"),    # dX: tile-direct at the widest image
     (3, 32, 7, 8, 48, 3, 1, 1, True, "relu"),        # dX: tile-direct at the narrowest image
     (2, 64, 12, 130, 64, 3, 2, 1, True, "leaky"),    # dX: stride-2, width beyond one region
+    (2, 32, 20, 104, 64, 3, 2, 1, True, "leaky"),    # dW row-streaming: stride 2, split runs
+    (1, 32, 15, 121, 64, 3, 2, 1, True, "leaky"),    # dW row-streaming: odd sizes, ragged strip
+    (2, 64, 11, 52, 128, 3, 1, 1, True, "leaky"),    # dW row-streaming: stride 1, 2x2 (o, i) blocks
+    (3, 32, 9, 26, 64, 3, 1, 1, False, "linear"),    # dW row-streaming: 26-wide strip
+    (1, 96, 5, 62, 64, 3, 1, 1, True, "relu"),       # dW row-streaming: 64-wide strip, one split
+    (4, 32, 64, 52, 64, 3, 1, 1, True, "leaky"),     # dW row-streaming: many runs, two-level sum
+    (1, 32, 1, 30, 64, 3, 1, 1, True, "leaky"),      # dW row-streaming: a single output row
+    (2, 32, 2, 60, 64, 3, 2, 1, True, "leaky"),      # dW row-streaming: stride 2, one output row
 ]
 
 
@@ -100,7 +108,7 @@ def test_conv_block_backward_parity(case):
 
 @pytest.mark.parametrize("case", [CONV_CASES[0], CONV_CASES[1], CONV_CASES[3], CONV_CASES[5],
                                   CONV_CASES[6], CONV_CASES[12], CONV_CASES[13], CONV_CASES[17],
-                                  CONV_CASES[18]])
+                                  CONV_CASES[18], CONV_CASES[22], CONV_CASES[26]])
 def test_conv_block_accumulate_inplace_and_no_dx(case):
     torch = require_gpu()
     announce(f"conv_block accumulate/in-place {case}")
@@ -115,7 +123,8 @@ def test_conv_block_accumulate_inplace_and_no_dx(case):
 
 @pytest.mark.parametrize("case", [(2, 3, 32, 32, 16, 3, 1, 1), (1, 4, 41, 41, 6, 3, 2, 1),
                                   (2, 5, 9, 10, 3, 5, 2, 2), (3, 6, 8, 8, 70, 1, 1, 0),
-                                  (1, 33, 19, 23, 65, 3, 1, 1), (2, 3, 30, 30, 32, 3, 1, 1)])
+                                  (1, 33, 19, 23, 65, 3, 1, 1), (2, 3, 30, 30, 32, 3, 1, 1),
+                                  (1, 32, 9, 60, 64, 3, 2, 1), (2, 64, 8, 52, 128, 3, 1, 1)])
 def test_conv_coverage_bit_exact(case):
     """W = 1, delta = 1 (linear, no BN): dx counts covering windows times C_out; with x = 1,
     dW counts valid taps times N; db = N*OH*OW.  Integers below 2^24: exact in fp32."""
