@@ -58,7 +58,12 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
     }
   }
 
+  // Loads go to registers as they are; the zero padding is applied when they
+  // are stored to LDS, so no loaded value is consumed before the next tile and
+  // the loads stay in flight during the matrix-core work.
+  static_assert(TS::A_PER_T <= 32 && TS::B_PER_T <= 32, "one mask bit per staged element");
   float ra[TS::A_PER_T], rb[TS::B_PER_T];
+  uint32_t am = 0, bm = 0;
   auto load = [&](int64_t k0) {
     const int64_t q = k0 + qi;
     const bool qv = q < kend;
@@ -70,15 +75,17 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
       hb = ho * g.S - g.P;
       wb = wo * g.S - g.P;
     }
-    // Out-of-range elements load from a clamped (valid) address and are then
-    // replaced by zero: no divergent branches around the loads.
+    // Out-of-range elements load from a clamped (valid) address: no divergent
+    // branches around the loads.
     const float* db = dz + ((int64_t)b * g.OC) * g.OHW + rem;
+    am = 0;
+    bm = 0;
 #pragma unroll
     for (int r = 0; r < TS::A_PER_T; ++r) {
       const int o = m0 + rbase + RSTEP * r;
       const bool ok = qv && o < g.OC;
-      const float v = db[(int64_t)(ok ? o : 0) * g.OHW];
-      ra[r] = ok ? v : 0.f;
+      ra[r] = db[(int64_t)(ok ? o : 0) * g.OHW];
+      am |= (uint32_t)ok << r;
     }
     // x index of (n, i, hb + kh, wb + kw) = image base + boff + hb*W + wb
     const float* xb = x + (int64_t)b * g.C * g.HW;
@@ -87,17 +94,19 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
     for (int r = 0; r < TS::B_PER_T; ++r) {
       const int h = hb + bkh[r], w = wb + bkw[r];
       const bool ok = qv && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
-      const float v = xb[ok ? boff[r] + pbase : 0];
-      rb[r] = ok ? v : 0.f;
+      rb[r] = xb[ok ? boff[r] + pbase : 0];
+      bm |= (uint32_t)ok << r;
     }
   };
   auto store = [&](float* buf) {
     float* As = buf;
     float* Bs = buf + TS::BK * TS::LDA;
 #pragma unroll
-    for (int r = 0; r < TS::A_PER_T; ++r) As[qi * TS::LDA + rbase + RSTEP * r] = ra[r];
+    for (int r = 0; r < TS::A_PER_T; ++r)
+      As[qi * TS::LDA + rbase + RSTEP * r] = ((am >> r) & 1u) ? ra[r] : 0.f;
 #pragma unroll
-    for (int r = 0; r < TS::B_PER_T; ++r) Bs[qi * TS::LDB + rbase + RSTEP * r] = rb[r];
+    for (int r = 0; r < TS::B_PER_T; ++r)
+      Bs[qi * TS::LDB + rbase + RSTEP * r] = ((bm >> r) & 1u) ? rb[r] : 0.f;
   };
 
   Acc<TS> acc;
@@ -390,9 +399,12 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
   const int acol = tid % TS::BK, irow0 = tid / TS::BK;
   const int KK = g.K * g.K;
 
+  // Out-of-range elements load from a clamped (valid) address (no divergent
+  // branches around the loads); the zero padding is applied at the LDS store,
+  // so the loads stay in flight during the matrix-core work.
+  static_assert(TS::A_PER_T <= 32 && TS::B_PER_T <= 32, "one mask bit per staged element");
   float ra[TS::A_PER_T], rb[TS::B_PER_T];
-  // Out-of-range elements load from a clamped (valid) address and are then
-  // replaced by zero: no divergent branches around the loads.
+  uint32_t am = 0, bm = 0;
   auto load = [&](int k0) {
     const int t = k0 / OCP, o0 = k0 - t * OCP;  // uniform over the work-group
     const int th = t / nkw, tw = t - th * nkw;
@@ -401,24 +413,26 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
       const int o = o0 + acol;
       const bool ov = o < g.OC;
       const float* wp = wt + ((int64_t)(ov ? o : 0) * g.C) * KK + kh * g.K + kw;
+      am = 0;
 #pragma unroll
       for (int r = 0; r < TS::A_PER_T; ++r) {
         const int i = m0 + irow0 + ISTEP * r;
         const bool ok = ov && i < g.C;
-        const float v = wp[(int64_t)(ok ? i : 0) * KK];
-        ra[r] = ok ? v : 0.f;
+        ra[r] = wp[(int64_t)(ok ? i : 0) * KK];
+        am |= (uint32_t)ok << r;
       }
     }
     {  // B = deltas
       const int ho = hob - th, wo = wob - tw;
       const bool ok = pv && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
       const float* bp = dzb + (ok ? ho * g.OW + wo : 0);
+      bm = 0;
 #pragma unroll
       for (int r = 0; r < TS::B_PER_T; ++r) {
         const int o = o0 + krow0 + KSTEP * r;
         const bool okr = ok && o < g.OC;
-        const float v = bp[(int64_t)(okr ? o : 0) * g.OHW];
-        rb[r] = okr ? v : 0.f;
+        rb[r] = bp[(int64_t)(okr ? o : 0) * g.OHW];
+        bm |= (uint32_t)okr << r;
       }
     }
   };
@@ -426,9 +440,11 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
     float* As = buf;
     float* Bs = buf + TS::BK * TS::LDA;
 #pragma unroll
-    for (int r = 0; r < TS::A_PER_T; ++r) As[acol * TS::LDA + irow0 + ISTEP * r] = ra[r];
+    for (int r = 0; r < TS::A_PER_T; ++r)
+      As[acol * TS::LDA + irow0 + ISTEP * r] = ((am >> r) & 1u) ? ra[r] : 0.f;
 #pragma unroll
-    for (int r = 0; r < TS::B_PER_T; ++r) Bs[(krow0 + KSTEP * r) * TS::LDB + pcol] = rb[r];
+    for (int r = 0; r < TS::B_PER_T; ++r)
+      Bs[(krow0 + KSTEP * r) * TS::LDB + pcol] = ((bm >> r) & 1u) ? rb[r] : 0.f;
   };
 
   Acc<TS> acc;
@@ -588,21 +604,20 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
     const bool ok = e < zcount && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
     zofs[r] = ok ? o * g.OHW + ho * g.OW + wo : -1;
   }
+  // The loaded values are consumed only by the LDS store of the next chunk
+  // (the zero padding is applied there), so the loads stay in flight during
+  // the matrix-core work.
   auto load = [&](int o0) {
     const float* zb = dzb + (int64_t)o0 * g.OHW;
 #pragma unroll
-    for (int r = 0; r < C::ZPT; ++r) {
-      const float v = zb[(unsigned)max(zofs[r], 0)];
-      rz[r] = zofs[r] >= 0 ? v : 0.f;
-    }
+    for (int r = 0; r < C::ZPT; ++r) rz[r] = zb[(unsigned)max(zofs[r], 0)];
     const float* wb = wt + ((int64_t)o0 * g.C + i0) * 9;
 #pragma unroll
     for (int r = 0; r < C::WPT; ++r) {
       const int e = tid + kThreads * r;                // (o, i, tap), tap fastest
       const int o = e / (C::BMC * 9), rem = e - o * (C::BMC * 9);
       const bool ok = e < C::OCB * C::BMC * 9;
-      const float v = wb[(unsigned)(ok ? o * g.C * 9 + rem : 0)];
-      rw[r] = ok ? v : 0.f;
+      rw[r] = wb[(unsigned)(ok ? o * g.C * 9 + rem : 0)];
     }
   };
   // LDS keeps the staging order: Z planes of ZR*ZC floats, weights as [o][i][tap]
@@ -611,7 +626,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
 #pragma unroll
     for (int r = 0; r < C::ZPT; ++r) {
       const int e = tid + kThreads * r;
-      if (e < zcount) Z[e] = rz[r];
+      if (e < zcount) Z[e] = zofs[r] >= 0 ? rz[r] : 0.f;
     }
 #pragma unroll
     for (int r = 0; r < C::WPT; ++r) {
