@@ -107,6 +107,8 @@ def stage_work(runner, li, stage):
         # reads delta, y, x_hat and writes dz (BN); bias-only: reads delta (+ y)
         per = (16 if c.bn else (12 if c.act != "linear" else 4))
         return 0.0, float(per * out_elems)
+    if stage == "dWdX":  # both gradients from one read of dz: x, dz, W read; dW, dx written
+        return 4.0 * macs, 4.0 * (2 * in_elems + out_elems + 2 * w_elems)
     return 2.0 * macs, 4.0 * (in_elems + out_elems + w_elems)
 
 
@@ -115,9 +117,7 @@ def time_stages(runners, torch, reps=3):
     res = []
     for name, r in runners.items():
         for li in range(len(r.wl.convs)):
-            for stage in ("act_bn", "dW", "dX"):
-                if stage == "dX" and name == "lenet" and li == 0:
-                    continue
+            for stage in r.stages(li):
                 ms = []
                 for _ in range(reps):
                     ev = {}
@@ -196,12 +196,13 @@ def main():
             r.step()
     torch.cuda.synchronize()
 
-    # Find the dominant kernel before the timed region: the longest dW or dX stage
-    # (each is one kernel plus, for split reductions, a short ordered-sum kernel);
+    # Find the dominant kernel before the timed region: the longest dW, dX or fused
+    # dW+dX stage (each is one kernel plus, for split reductions, a short
+    # ordered-sum kernel);
     # act+BN stages are two streaming kernels of comparable size and are reported
     # separately (their longest kernel is shorter than the dominant conv kernel).
     stages = time_stages(runners, torch)
-    conv_stages = [st for st in stages if st[3] in ("dW", "dX")]
+    conv_stages = [st for st in stages if st[3] in ("dW", "dX", "dWdX")]
     dom_ms, dom_name, dom_li, dom_stage = conv_stages[0]
     print(f"[bench] dominant stage {dom_name}.{dom_li}.{dom_stage} {dom_ms:.3f} ms",
           file=sys.stderr, flush=True)

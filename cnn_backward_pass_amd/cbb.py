@@ -64,6 +64,9 @@ _SIGS = {
     "cbb_conv_act_bn_backward": ([ctypes.POINTER(ConvDesc)] + [_P] * 8 + [_P, _sz, _P], _i32),
     "cbb_conv_backward_weights": ([ctypes.POINTER(ConvDesc), _P, _P, _P, _P, _sz, _P], _i32),
     "cbb_conv_backward_data": ([ctypes.POINTER(ConvDesc), _P, _P, _P, _i32, _P, _sz, _P], _i32),
+    "cbb_conv_backward_weights_data": ([ctypes.POINTER(ConvDesc)] + [_P] * 5 + [_i32, _P, _sz, _P],
+                                       _i32),
+    "cbb_conv_fused_weights_data": ([ctypes.POINTER(ConvDesc)], _i32),
     "cbb_act_backward": ([_i32, _f, _P, _P, _P, _i64, _P], _i32),
     "cbb_bn_backward_workspace_size": ([_i32, _i32, _i64, ctypes.POINTER(_sz)], _i32),
     "cbb_bn_backward": ([_i32, _i32, _i64, _f] + [_P] * 7 + [_P, _sz, _P], _i32),
@@ -190,6 +193,21 @@ def conv_backward_data(desc: ConvDesc, w, dz, dx, dx_accumulate: bool = False, w
     _check("cbb_conv_backward_data", lib().cbb_conv_backward_data(
         ctypes.byref(desc), _ptr(w, name="w"), _ptr(dz, name="dz"), _ptr(dx, name="dx"),
         int(dx_accumulate), wsp, wsb, _stream(stream)))
+
+
+def conv_backward_weights_data(desc: ConvDesc, x, w, dz, dw, dx=None, dx_accumulate: bool = False,
+                               workspace=None, stream=None) -> None:
+    wsp, wsb = _ws(workspace)
+    _check("cbb_conv_backward_weights_data", lib().cbb_conv_backward_weights_data(
+        ctypes.byref(desc), _ptr(x, name="x"), _ptr(w, name="w"), _ptr(dz, name="dz"),
+        _ptr(dw, name="dw"), _ptr(dx, name="dx"), int(dx_accumulate), wsp, wsb, _stream(stream)))
+
+
+def conv_fused_weights_data(desc: ConvDesc) -> bool:
+    rc = lib().cbb_conv_fused_weights_data(ctypes.byref(desc))
+    if rc < 0:
+        _check("cbb_conv_fused_weights_data", rc)
+    return rc == 1
 
 
 def act_backward(act, slope: float, y, delta, g, stream=None) -> None:

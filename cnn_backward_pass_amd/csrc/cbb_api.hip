@@ -62,11 +62,25 @@ int check_desc(const cbb_conv_desc* d, ConvPlan* plan) {
     plan->ow = ow;
     const ConvGeom g = make_geom(*d);
     plan->part_bytes = align_up(actbn_workspace(d->batch, d->out_c, oh * ow), kAlign);
-    // dW and dX run one after the other on the stream and share the second region
-    plan->dw_bytes = align_up(std::max(conv_dw_workspace(g), conv_dx_workspace(g)), kAlign);
+    // dW and dX run one after the other on the stream (or as one fused kernel)
+    // and share the second region
+    plan->dw_bytes = align_up(
+        std::max({conv_dw_workspace(g), conv_dx_workspace(g), conv_fused_workspace(g)}), kAlign);
     plan->total = plan->part_bytes + plan->dw_bytes;
   }
   return CBB_OK;
+}
+
+// dW and (when dx is given) dX from dz: one fused kernel for the layers it
+// covers, else the two gradient kernels one after the other.
+int launch_weights_data(const ConvGeom& g, const float* x, const float* w, const float* dz,
+                        float* dw, float* dx, int dx_accumulate, float* ws, hipStream_t st) {
+  const bool aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)dz % 16 == 0);
+  if (dx && aligned && conv_fused_dwdx_ok(g))
+    return launch_conv_fused_dwdx(g, x, w, dz, dw, dx, dx_accumulate, ws, st);
+  int rc = launch_conv_dw(g, x, dz, dw, ws, st);
+  if (rc || !dx) return rc;
+  return launch_conv_dx(g, w, dz, dx, dx_accumulate, ws, st);
 }
 
 }  // namespace
@@ -123,13 +137,30 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
   rc = launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
                     var, gamma, desc->bn_eps, bn, passthrough ? nullptr : dz, dgamma, db, ws, st);
   if (rc) return rc;
-  const ConvGeom g = make_geom(*desc);
-  rc = launch_conv_dw(g, x, dz_eff, dw, reinterpret_cast<float*>(ws + p.part_bytes), st);
+  return launch_weights_data(make_geom(*desc), x, w, dz_eff, dw, dx, dx_accumulate,
+                             reinterpret_cast<float*>(ws + p.part_bytes), st);
+}
+
+int cbb_conv_fused_weights_data(const cbb_conv_desc* desc) {
+  const int rc = check_desc(desc, nullptr);
   if (rc) return rc;
-  if (dx)
-    rc = launch_conv_dx(g, w, dz_eff, dx, dx_accumulate,
-                        reinterpret_cast<float*>(ws + p.part_bytes), st);
-  return rc;
+  return conv_fused_dwdx_ok(make_geom(*desc)) ? 1 : 0;
+}
+
+int cbb_conv_backward_weights_data(const cbb_conv_desc* desc, const float* x, const float* w,
+                                   const float* dz, float* dw, float* dx, int dx_accumulate,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  ConvPlan p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  if (!x || !w || !dz || !dw) return CBB_EINVAL;
+  if (dx_accumulate != 0 && dx_accumulate != 1) return CBB_EINVAL;
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return CBB_EWORKSPACE;
+  if (workspace && ((uintptr_t)workspace % kAlign)) return CBB_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  return launch_weights_data(make_geom(*desc), x, w, dz, dw, dx, dx_accumulate,
+                             reinterpret_cast<float*>(ws ? ws + p.part_bytes : nullptr),
+                             S(stream));
 }
 
 int cbb_conv_act_bn_backward(const cbb_conv_desc* desc, const float* y, const float* x_norm,

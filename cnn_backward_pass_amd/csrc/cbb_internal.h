@@ -216,6 +216,10 @@ size_t conv_dw_workspace(const ConvGeom& g);
 int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
                    hipStream_t st);
 size_t conv_dx_workspace(const ConvGeom& g);
+bool conv_fused_dwdx_ok(const ConvGeom& g);
+size_t conv_fused_workspace(const ConvGeom& g);
+int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
+                           float* dw, float* dx, int accumulate, float* ws, hipStream_t st);
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
                    float* ws, hipStream_t st);
 size_t actbn_workspace(int N, int C, int64_t HW);

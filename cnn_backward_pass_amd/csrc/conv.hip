@@ -831,6 +831,228 @@ __global__ __launch_bounds__(kThreads) void conv_dx_smallc_kernel(ConvGeom g,
 }
 
 // ---------------------------------------------------------------------------
+// Weight and input gradients of a 3x3, pad-1, stride-1 convolution with at
+// most 3 input and at most 32 output channels (a network's first layer on an
+// RGB image) in one pass over dz.  Both gradients read the same dz and the
+// layer is HBM-bound, so fusing them halves its traffic.
+//
+// Persistent work-groups walk a contiguous run of 8 x 32 pixel tiles.  Per
+// tile, dz for all output channels and x for all input channels are staged in
+// LDS over the tile plus its halo, as 16-byte loads of 10 rows x 40 columns
+// (columns w0-4 .. w0+35; the image width is a multiple of 4, so every
+// 16-byte group is wholly inside or outside the image); the next tile's loads
+// are in registers while this one is computed.
+//   dW: matrix cores, M = o (32), N = (i, kh, kw) (9*CI <= 27 of 32 columns),
+//       K = the tile's 256 pixels, two per 32x32x2 step; each wave takes 64
+//       pixels and keeps its 32x32 accumulator across tiles.
+//   dX: vector ALUs.  Wave w sums output channels [8w, 8w+8) for all 256
+//       pixels, four neighbouring pixels per lane, with wave-uniform weight
+//       reads; the four waves' partial sums meet in LDS and are added in a
+//       fixed order.
+// At the end the waves' dW blocks are summed through LDS and each work-group
+// writes its partial for the ordered split reduction.
+// ---------------------------------------------------------------------------
+constexpr int kFuTH = 8, kFuTW = 32;
+constexpr int kFuRW = 40, kFuRH = kFuTH + 2;       // staged region: 10 x 40
+constexpr int kFuZP = kFuRH * kFuRW + 4;           // LDS pitch per channel (16-byte aligned)
+constexpr int kFuNV = kFuRH * (kFuRW / 4);         // 16-byte groups per channel
+constexpr int kFuZV = (32 * kFuNV + kThreads - 1) / kThreads;  // dz groups per thread
+constexpr int kFuXV = (3 * kFuNV + kThreads - 1) / kThreads;   // x groups per thread
+
+template <int CI>
+__global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
+    ConvGeom g, const float* __restrict__ x, const float* __restrict__ wt,
+    const float* __restrict__ dz, float* __restrict__ dwpart, float* __restrict__ dx,
+    int tiles_per_wg, int accumulate) {
+  static_assert(CI >= 1 && CI <= 3, "9*CI columns must fit one 32-wide block");
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  __shared__ __attribute__((aligned(16))) float Zs[32 * kFuZP];
+  __shared__ __attribute__((aligned(16))) float Xs[CI * kFuZP];
+  __shared__ float Pd[4 * CI * kFuTH * kFuTW];   // per-wave partial dx
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles_h = (g.H + kFuTH - 1) / kFuTH, tiles_w = (g.W + kFuTW - 1) / kFuTW;
+  const int ntiles = g.N * tiles_h * tiles_w;
+  const int t0 = blockIdx.x * tiles_per_wg, t1 = min(ntiles, t0 + tiles_per_wg);
+  const int zcount = g.OC * kFuNV, xcount = CI * kFuNV;
+
+  // output channels >= OC stay zero in LDS for the whole kernel
+  for (int e = tid; e < 32 * kFuZP; e += kThreads) Zs[e] = 0.f;
+
+  static_assert(kFuZV <= 32 && kFuXV <= 32, "one mask bit per staged group");
+  f4 pz[kFuZV], px[kFuXV];
+  uint32_t zmask = 0, xmask = 0;
+  auto tile_origin = [&](int t, int& n, int& h0, int& w0) {
+    const int tw = t % tiles_w, r = t / tiles_w;
+    const int th = r % tiles_h;
+    n = r / tiles_h;
+    h0 = th * kFuTH;
+    w0 = tw * kFuTW;
+  };
+  // Loads go to registers as they are (groups off the image read a clamped
+  // valid address); the zero padding is applied at the LDS store.  The index
+  // math is redone at every tile on purpose (the thread index goes through an
+  // empty asm): hoisted out of the tile loop it would keep too many offsets live.
+  auto fetch = [&](int t) {
+    int n, h0, w0;
+    tile_origin(t, n, h0, w0);
+    const float* zb = dz + (int64_t)n * g.OC * g.HW;
+    const float* xb = x + (int64_t)n * CI * g.HW;
+    int tt = tid;
+    asm volatile("" : "+v"(tt));
+    zmask = 0;
+    xmask = 0;
+#pragma unroll
+    for (int i = 0; i < kFuZV; ++i) {
+      const int e = tt + i * kThreads;
+      const int o = e / kFuNV, q = e - o * kFuNV;
+      const int rr = q / (kFuRW / 4), v = q - rr * (kFuRW / 4);
+      const int h = h0 - 1 + rr, w = w0 - 4 + 4 * v;
+      const bool ok = e < zcount && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+      pz[i] = *(const f4*)(zb + (ok ? o * g.HW + h * g.W + w : 0));
+      zmask |= (uint32_t)ok << i;
+    }
+#pragma unroll
+    for (int i = 0; i < kFuXV; ++i) {
+      const int e = tt + i * kThreads;
+      const int c = e / kFuNV, q = e - c * kFuNV;
+      const int rr = q / (kFuRW / 4), v = q - rr * (kFuRW / 4);
+      const int h = h0 - 1 + rr, w = w0 - 4 + 4 * v;
+      const bool ok = e < xcount && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+      px[i] = *(const f4*)(xb + (ok ? c * g.HW + h * g.W + w : 0));
+      xmask |= (uint32_t)ok << i;
+    }
+  };
+  auto commit = [&]() {
+    int tt = tid;
+    asm volatile("" : "+v"(tt));
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kFuZV; ++i) {
+      const int e = tt + i * kThreads;
+      const int o = e / kFuNV, q = e - o * kFuNV;
+      if (e < zcount) *(f4*)(Zs + o * kFuZP + 4 * q) = ((zmask >> i) & 1u) ? pz[i] : zero;
+    }
+#pragma unroll
+    for (int i = 0; i < kFuXV; ++i) {
+      const int e = tt + i * kThreads;
+      const int c = e / kFuNV, q = e - c * kFuNV;
+      if (e < xcount) *(f4*)(Xs + c * kFuZP + 4 * q) = ((xmask >> i) & 1u) ? px[i] : zero;
+    }
+  };
+
+  // dW operands: lane column j = (i, kh, kw); pixel (r, cc) of the tile has dz
+  // at region (r+1, cc+4) and x under tap (kh, kw) at region (r+kh, cc+kw+3).
+  const int j = lane & 31, kq = lane >> 5;
+  const bool jv = j < 9 * CI;
+  int boff;
+  {
+    const int i = j / 9, tap = j - 9 * i, kh = tap / 3, kw = tap - 3 * kh;
+    boff = jv ? i * kFuZP + kh * kFuRW + kw + 3 : 0;
+  }
+  const int aoff = (lane & 31) * kFuZP + kFuRW + 4;
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+
+  // dX: lane -> tile row pr, columns 4*pg .. 4*pg+3; wave -> output channels
+  const int pr = lane >> 3, pg = lane & 7;
+  const int o_lo = 8 * wave, o_hi = min(g.OC, 8 * wave + 8);
+
+  if (t0 < t1) fetch(t0);
+  __syncthreads();  // the zero fill is complete before any staging
+  for (int t = t0; t < t1; ++t) {
+    commit();
+    __syncthreads();
+    if (t + 1 < t1) fetch(t + 1);  // in flight during this tile's work
+
+    // dW: the wave's 64 pixels = tile rows 2*wave, 2*wave + 1; step s takes
+    // pixels 2s + kq of them
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      if (s % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // bounds the operand prefetch
+      const int pt = 64 * wave + 2 * s + kq;
+      const int po = (pt / kFuTW) * kFuRW + (pt % kFuTW);
+      const float a = Zs[aoff + po];
+      const float bx = Xs[boff + po];
+      const float b = jv ? bx : 0.f;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+
+    if (dx) {
+      // partial dx of this wave's channels: one running sum per (input channel,
+      // kernel row, pixel) -- 12*CI independent chains
+      float d[CI][3][4];
+#pragma unroll
+      for (int i = 0; i < CI; ++i)
+#pragma unroll
+        for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) d[i][kh][u] = 0.f;
+      // pixel (pr, 4pg+u) needs dz at region (pr+2-kh, 4pg+u+5-kw): rows pr..pr+2,
+      // columns 4pg+3 .. 4pg+8
+      const float* zp = Zs + pr * kFuRW + 4 * pg + 3;
+      for (int o = o_lo; o < o_hi; ++o) {
+        float z[3][6];
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+          for (int v = 0; v < 6; ++v) z[u][v] = zp[o * kFuZP + u * kFuRW + v];
+        const float* wo = wt + (int64_t)o * CI * 9;
+#pragma unroll
+        for (int i = 0; i < CI; ++i)
+#pragma unroll
+          for (int kh = 0; kh < 3; ++kh)
+#pragma unroll
+            for (int kw = 0; kw < 3; ++kw) {
+              const float wv = wo[i * 9 + kh * 3 + kw];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) d[i][kh][u] += wv * z[2 - kh][u + 2 - kw];
+            }
+      }
+#pragma unroll
+      for (int i = 0; i < CI; ++i)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          Pd[(wave * CI + i) * (kFuTH * kFuTW) + pr * kFuTW + 4 * pg + u] =
+              (d[i][0][u] + d[i][1][u]) + d[i][2][u];
+    }
+    __syncthreads();  // LDS tile reads and the partial dx are complete
+    if (dx) {
+      int n, h0, w0;
+      tile_origin(t, n, h0, w0);
+      const int r = tid / kFuTW, cc = tid - r * kFuTW;
+      const int h = h0 + r, w = w0 + cc;
+      if (h < g.H && w < g.W) {
+#pragma unroll
+        for (int i = 0; i < CI; ++i) {
+          const float v = (Pd[(0 * CI + i) * 256 + tid] + Pd[(1 * CI + i) * 256 + tid]) +
+                          (Pd[(2 * CI + i) * 256 + tid] + Pd[(3 * CI + i) * 256 + tid]);
+          float* q = dx + ((int64_t)n * CI + i) * g.HW + h * g.W + w;
+          *q = accumulate ? *q + v : v;
+        }
+      }
+    }
+  }
+
+  // Sum the four waves' dW blocks (fixed order) and write this work-group's partial.
+  __syncthreads();
+  float* red = Zs;  // 4 x 16 x 64 floats
+#pragma unroll
+  for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+  __syncthreads();
+  if (wave == 0) {
+    float* dst = dwpart + (int64_t)blockIdx.x * g.OC * g.J;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float v = (red[r * 64 + lane] + red[(16 + r) * 64 + lane]) +
+                      (red[(32 + r) * 64 + lane] + red[(48 + r) * 64 + lane]);
+      const int o = acc_row(r, lane);
+      if (o < g.OC && j < 9 * CI) dst[o * g.J + j] = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 ConvGeom make_geom(const cbb_conv_desc& d) {
@@ -929,6 +1151,57 @@ static DwPlan plan_dw(const ConvGeom& g) {
   return best;
 }
 
+// Fused small-channel dW + dX: which layers, and how the tiles are split.
+bool conv_fused_dwdx_ok(const ConvGeom& g) {
+  return g.C >= 1 && g.C <= 3 && g.K == 3 && g.P == 1 && g.S == 1 && g.OC <= 32 && g.W % 4 == 0;
+}
+
+struct FuPlan {
+  int tiles_per_wg, wgs, groups;
+};
+
+static FuPlan plan_fused(const ConvGeom& g) {
+  FuPlan p{};
+  const int64_t ntiles =
+      (int64_t)g.N * ceil_div(g.H, kFuTH) * ceil_div(g.W, kFuTW);
+  const int64_t target = 512;  // two resident work-groups per CU
+  p.tiles_per_wg = (int)std::max<int64_t>(1, ceil_div(ntiles, target));
+  p.wgs = (int)ceil_div(ntiles, p.tiles_per_wg);
+  p.groups = p.wgs > kReduceGroup ? (int)ceil_div(p.wgs, kReduceGroup) : 0;
+  return p;
+}
+
+size_t conv_fused_workspace(const ConvGeom& g) {
+  if (!conv_fused_dwdx_ok(g)) return 0;
+  const FuPlan p = plan_fused(g);
+  return ((size_t)p.wgs + p.groups) * g.OC * g.J * sizeof(float);
+}
+
+static int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
+                            hipStream_t st);
+
+int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
+                           float* dw, float* dx, int accumulate, float* ws, hipStream_t st) {
+  const FuPlan p = plan_fused(g);
+  switch (g.C) {
+    case 1:
+      conv_smallc_dwdx<1><<<p.wgs, kThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
+                                                      accumulate);
+      break;
+    case 2:
+      conv_smallc_dwdx<2><<<p.wgs, kThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
+                                                      accumulate);
+      break;
+    default:
+      conv_smallc_dwdx<3><<<p.wgs, kThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
+                                                      accumulate);
+      break;
+  }
+  const int rc = check_launch("conv_smallc_dwdx");
+  if (rc) return rc;
+  return launch_dw_reduce(g, dw, ws, p.wgs, p.groups, st);
+}
+
 size_t conv_dw_workspace(const ConvGeom& g) {
   const DwPlan p = plan_dw(g);
   if (p.splits == 1) return 0;
@@ -985,17 +1258,23 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
   }
   int rc = check_launch(p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel");
   if (rc != CBB_OK || direct) return rc;
+  return launch_dw_reduce(g, dw, ws, p.splits, p.groups, st);
+}
+
+// dw += ordered sum of the `splits` partials in ws (two levels when groups > 0).
+static int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
+                            hipStream_t st) {
   const int64_t mn = (int64_t)g.OC * g.J;
   const unsigned eblocks = (unsigned)ceil_div(mn, kThreads);
-  if (p.groups == 0) {
-    dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, ws, p.splits, mn);
+  if (groups == 0) {
+    dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, ws, splits, mn);
     return check_launch("dw_reduce_l2");
   }
-  float* part2 = ws + (int64_t)p.splits * mn;
-  dw_reduce_l1<<<dim3(eblocks, p.groups), kThreads, 0, st>>>(ws, part2, p.splits, mn);
-  rc = check_launch("dw_reduce_l1");
+  float* part2 = ws + (int64_t)splits * mn;
+  dw_reduce_l1<<<dim3(eblocks, groups), kThreads, 0, st>>>(ws, part2, splits, mn);
+  const int rc = check_launch("dw_reduce_l1");
   if (rc) return rc;
-  dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, part2, p.groups, mn);
+  dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, part2, groups, mn);
   return check_launch("dw_reduce_l2");
 }
 

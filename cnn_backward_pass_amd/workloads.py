@@ -65,6 +65,7 @@ class Runner:
                 ent["xhat"] = ent["var"] = ent["gamma"] = ent["dgamma"] = None
                 ent["dz"] = None if c.act == "linear" else torch.empty(oshape, dtype=f32,
                                                                        device=device)
+            ent["fused"] = cbb.conv_fused_weights_data(desc)
             ent["dw"] = torch.zeros_like(ent["w"])
             ent["db"] = torch.zeros(c.out_c, dtype=f32, device=device)
             ent["ws_bytes"] = cbb.conv_block_workspace_size(desc)
@@ -133,14 +134,21 @@ class Runner:
                                     e["gamma"], delta, e["dz"], e["dw"], e["db"], e["dgamma"], dx,
                                     dx_accumulate, self.workspace, stream)
             return
-        # The same three stages conv_block_backward runs, called one by one so that
-        # events can bracket one of them ("act_bn", "dW" or "dX").
+        # The same stages conv_block_backward runs, called one by one so that
+        # events can bracket one of them ("act_bn", "dW", "dX", or "dWdX" where
+        # the library computes both gradients in one fused kernel).
         _, stage, mark = probe
         dz = delta if e["dz"] is None else e["dz"]
         mark(stage == "act_bn", True)
         cbb.conv_act_bn_backward(e["desc"], e["y"], e["xhat"], e["var"], e["gamma"], delta,
                                  e["dz"], e["db"], e["dgamma"], self.workspace, stream)
         mark(stage == "act_bn", False)
+        if dx is not None and e["fused"]:
+            mark(stage == "dWdX", True)
+            cbb.conv_backward_weights_data(e["desc"], e["x"], e["w"], dz, e["dw"], dx,
+                                           dx_accumulate, self.workspace, stream)
+            mark(stage == "dWdX", False)
+            return
         mark(stage == "dW", True)
         cbb.conv_backward_weights(e["desc"], e["x"], dz, e["dw"], self.workspace, stream)
         mark(stage == "dW", False)
@@ -158,6 +166,13 @@ class Runner:
             return self.d_main if li == 1 else self.d_in[1]
         return self.delta if li == len(self.convs) - 1 else self.d_in[li + 1]
 
+    def stages(self, li: int) -> list[str]:
+        """The separately timed stages of conv layer li (see step's probe)."""
+        has_dx = not (self.name == "lenet" and li == 0)
+        if has_dx and self.convs[li]["fused"]:
+            return ["act_bn", "dWdX"]
+        return ["act_bn", "dW", "dX"] if has_dx else ["act_bn", "dW"]
+
     def run_stage(self, li: int, stage: str, stream=None) -> None:
         """Enqueue one stage ("act_bn", "dW" or "dX") of conv layer li on its own, on the
         buffers as they stand (for profiling; dX overwrites the layer's input gradient)."""
@@ -174,6 +189,9 @@ class Runner:
                 raise ValueError("the first LeNet conv has no input gradient")
             cbb.conv_backward_data(e["desc"], e["w"], dz, self.d_in[li], False, self.workspace,
                                    stream)
+        elif stage == "dWdX":
+            cbb.conv_backward_weights_data(e["desc"], e["x"], e["w"], dz, e["dw"], self.d_in[li],
+                                           False, self.workspace, stream)
         else:
             raise ValueError(f"unknown stage {stage!r}")
 

@@ -150,6 +150,22 @@ int cbb_conv_backward_weights(const cbb_conv_desc* desc, const float* x, const f
 int cbb_conv_backward_data(const cbb_conv_desc* desc, const float* w, const float* dz, float* dx,
                            int dx_accumulate, void* workspace, size_t workspace_bytes,
                            void* stream);
+/* Stages 2 and 3 together (the two GEMMs of [P1] section 3.1 that read the
+ * same delta): dw += weight gradient and, when dx is not NULL, dx (+)= input
+ * gradient, with the meanings and buffers of the two calls above.  For the
+ * layers cbb_conv_fused_weights_data reports, both come from one kernel that
+ * reads dz once; otherwise this is stage 2 followed by stage 3.  dx must not
+ * overlap x, w, dz, dw or the workspace. */
+int cbb_conv_backward_weights_data(const cbb_conv_desc* desc, const float* x, const float* w,
+                                   const float* dz, float* dw, float* dx, int dx_accumulate,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+/* 1 when cbb_conv_backward_weights_data (and cbb_conv_block_backward with dx)
+ * computes dW and dX in one fused kernel for this descriptor: 3x3 kernel, pad 1,
+ * stride 1, at most 3 input and at most 32 output channels, input width a
+ * multiple of 4 (a first layer on an RGB image), provided x and dz are 16-byte
+ * aligned at the call; 0 otherwise; a negative status for an invalid
+ * descriptor.  Informational: the results do not depend on it. */
+int cbb_conv_fused_weights_data(const cbb_conv_desc* desc);
 
 /* Activation gradient alone (gradient_array, [P1] sections 3.1 and 7):
  * g[i] = delta[i] * act'(y[i]) for i < count.  g may equal delta. */

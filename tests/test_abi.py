@@ -105,6 +105,27 @@ def test_conv_workspace_and_flags():
     assert _call_conv(d, acc=2) == -1
 
 
+def test_weights_data_entry_points_validate():
+    L = cbb.lib()
+    d = _desc()
+    _, need = ws_size(d)
+    call = lambda *a: L.cbb_conv_backward_weights_data(ctypes.byref(d), *a, None)
+    for i in range(4):  # x, w, dz, dw are required
+        args = [BOGUS] * 5
+        args[i] = None
+        assert call(*args, 0, BOGUS, need) == -1
+    assert call(*[BOGUS] * 5, 2, BOGUS, need) == -1            # dx_accumulate not 0/1
+    assert call(*[BOGUS] * 5, 0, BOGUS, need - 1) == -4        # workspace too small
+    assert call(*[BOGUS] * 5, 0, ctypes.c_void_p(0x1004), need) == -4
+    # which descriptors take the fused kernel (a host-side query)
+    fused = lambda **kw: L.cbb_conv_fused_weights_data(ctypes.byref(_desc(**kw)))
+    assert fused() == 1 and fused(out_c=32) == 1 and fused(in_c=1) == 1
+    assert fused(out_c=33) == 0 and fused(in_c=4) == 0 and fused(stride=2) == 0
+    assert fused(ksize=5, pad=2) == 0 and fused(pad=0) == 0 and fused(in_w=9) == 0
+    assert fused(batch=0) == -1
+    assert L.cbb_conv_fused_weights_data(None) == -1
+
+
 def test_other_entry_points_validate():
     L = cbb.lib()
     sz = ctypes.c_size_t(0)

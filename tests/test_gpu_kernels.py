@@ -150,6 +150,51 @@ def test_conv_coverage_bit_exact(case):
     assert_exact("db", db.cpu().double().numpy(), np.full(oc, n * oh * ow, np.float64))
 
 
+@pytest.mark.parametrize("case", [  # n, c, h, w, oc, k, s, p
+    (2, 3, 32, 32, 16, 3, 1, 1),    # fused: the single-block layer
+    (3, 3, 19, 44, 32, 3, 1, 1),    # fused: ragged tiles in both directions, 32 outputs
+    (1, 1, 9, 12, 7, 3, 1, 1),      # fused: one input channel, one partial tile
+    (2, 2, 40, 68, 20, 3, 1, 1),    # fused: two input channels
+    (1, 3, 1, 4, 5, 3, 1, 1),       # fused: one image row
+    (2, 3, 20, 20, 40, 3, 1, 1),    # not fused: more than 32 outputs
+    (1, 3, 9, 9, 8, 3, 1, 1),       # not fused: width not a multiple of 4
+    (2, 4, 12, 12, 8, 3, 1, 1),     # not fused: four inputs
+    (2, 32, 20, 104, 64, 3, 2, 1),  # not fused: row-streaming dW, tile-direct dX
+])
+def test_conv_backward_weights_data(case):
+    """dW and dX from one call (fused where the library reports it) against the oracle,
+    with and without dx, overwrite and accumulate."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    n, c, h, w, oc, k, s, p = case
+    announce(f"weights_data {case}")
+    r = np.random.default_rng(500 + c * 7 + oc)
+    oh, ow = O.conv_out_dim(h, k, s, p), O.conv_out_dim(w, k, s, p)
+    x = r.normal(size=(n, c, h, w)).astype(np.float32)
+    wt = (r.normal(size=(oc, c, k, k)) * 0.3).astype(np.float32)
+    dz = r.normal(size=(n, oc, oh, ow)).astype(np.float32)
+    dx0 = r.normal(size=x.shape).astype(np.float32)
+    desc = cbb.conv_desc(n, c, h, w, oc, k, s, p, False, "linear")
+    expect_fused = c <= 3 and k == 3 and p == 1 and s == 1 and oc <= 32 and w % 4 == 0
+    assert cbb.conv_fused_weights_data(desc) == expect_fused
+    ref_dw = O.conv_backward_weights(x, dz, k, s, p)
+    ref_dx = O.conv_backward_data(wt, dz, (h, w), s, p)
+    ws = cbb.workspace(cbb.conv_block_workspace_size(desc))
+    for accumulate in (False, True):
+        dw = _t(torch, np.full(wt.shape, 0.5, np.float32))
+        dx = _t(torch, dx0)
+        cbb.conv_backward_weights_data(desc, _t(torch, x), _t(torch, wt), _t(torch, dz), dw, dx,
+                                       accumulate, ws)
+        torch.cuda.synchronize()
+        assert_close("dw", dw.cpu().double().numpy() - 0.5, ref_dw)
+        assert_close("dx", dx.cpu().double().numpy(), ref_dx + (dx0 if accumulate else 0.0))
+    dw = _t(torch, np.zeros(wt.shape, np.float32))
+    cbb.conv_backward_weights_data(desc, _t(torch, x), _t(torch, wt), _t(torch, dz), dw, None,
+                                   False, ws)
+    torch.cuda.synchronize()
+    assert_close("dw (no dx)", dw.cpu().double().numpy(), ref_dw)
+
+
 def test_conv_one_hot_probes_bit_exact():
     torch = require_gpu()
     from cnn_backward_pass_amd import cbb
