@@ -274,7 +274,7 @@ def main():
                                    "b8@52x52, yolov3_stem b16@416x416, yolov3_head b8@26x26",
                        "gflop_per_step": round(step_flops / 1e9, 3), "parallelism": "none"},
             "roofline": roof, "per_workload": per,
-            "top_stages_ms": [[f"{n}.{li}.{st}", round(ms, 4)] for ms, n, li, st in stages[:8]],
+            "stages_ms": {f"{n}.{li}.{st}": round(ms, 4) for ms, n, li, st in stages},
             "act_bn_stages": {f"{n}.{li}": {
                 "ms": round(ms, 4),
                 "algorithmic_GBps": round(stage_work(runners[n], li, st)[1] / (ms * 1e-3) / 1e9, 1)}

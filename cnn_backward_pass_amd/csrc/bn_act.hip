@@ -63,6 +63,17 @@ __device__ __forceinline__ void for_segment(const SegGeom& s, int c, int sg, F&&
     n1 = min(s.N, n0 + s.group);
     r0 = 0;
     r1 = s.HW;
+    if (s.HW < 4 * kThreads) {
+      // small planes: spread the threads over the segment's planes (all lanes busy)
+      const int per = VEC ? s.HW >> 2 : s.HW;  // items per plane
+      const int64_t i1 = (int64_t)(n1 - n0) * per;
+      for (int64_t i = threadIdx.x; i < i1; i += kThreads) {
+        const int n = n0 + (int)(i / per), r = (int)(i % per);
+        const int64_t base = ((int64_t)n * s.C + c) * s.HW;
+        f(base + (VEC ? 4 * r : r));
+      }
+      return;
+    }
   }
   for (int n = n0; n < n1; ++n) {
     const int64_t base = ((int64_t)n * s.C + c) * s.HW;

@@ -206,33 +206,54 @@ struct GemmArgs {
 
 __global__ __launch_bounds__(kThreads) void strided_gemm_kernel(GemmArgs a, int tiles_n) {
   using TS = TileShape<2, 2, 1>;
-  __shared__ float lds[TS::BUF_FLOATS];
-  float* As = lds;
-  float* Bs = lds + TS::BK * TS::LDA;
+  __shared__ float lds[TS::LDS_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % TS::WM, wn = wave / TS::WM, wk = 0;
   const int m0 = (blockIdx.x / tiles_n) * TS::BM, n0 = (blockIdx.x % tiles_n) * TS::BN;
-  Acc<TS> acc;
-  acc.zero();
-  for (int k0 = 0; k0 < a.K; k0 += TS::BK) {
-    __syncthreads();
+  // Register-prefetched K tiles (two ahead, see gemm_mainloop); out-of-range
+  // elements read a clamped address and are zeroed at the LDS store, so the
+  // loads stay in flight during the matrix-core work.
+  float ra[TS::A_PER_T], rb[TS::B_PER_T];
+  uint32_t am = 0, bm = 0;
+  auto load = [&](int64_t k0) {
+    am = 0;
+    bm = 0;
 #pragma unroll
     for (int r = 0; r < TS::A_PER_T; ++r) {
       const int e = tid + kThreads * r;
       const int k = e % TS::BK, m = e / TS::BK;
-      const int gm = m0 + m, gk = k0 + k;
-      As[k * TS::LDA + m] = (gm < a.M && gk < a.K) ? a.A[gm * a.sam + gk * a.sak] : 0.f;
+      const int gm = m0 + m, gk = (int)k0 + k;
+      const bool ok = gm < a.M && gk < a.K;
+      ra[r] = a.A[ok ? (int64_t)gm * a.sam + (int64_t)gk * a.sak : 0];
+      am |= (uint32_t)ok << r;
     }
 #pragma unroll
     for (int r = 0; r < TS::B_PER_T; ++r) {
       const int e = tid + kThreads * r;
       const int n = e % TS::BN, k = e / TS::BN;
-      const int gn = n0 + n, gk = k0 + k;
-      Bs[k * TS::LDB + n] = (gn < a.N && gk < a.K) ? a.B[gk * a.sbk + gn * a.sbn] : 0.f;
+      const int gn = n0 + n, gk = (int)k0 + k;
+      const bool ok = gn < a.N && gk < a.K;
+      rb[r] = a.B[ok ? (int64_t)gk * a.sbk + (int64_t)gn * a.sbn : 0];
+      bm |= (uint32_t)ok << r;
     }
-    __syncthreads();
-    mfma_tile<TS>(As, Bs, acc, wm, wn, wk, lane);
-  }
+  };
+  auto store = [&](float* buf) {
+    float* As = buf;
+    float* Bs = buf + TS::BK * TS::LDA;
+#pragma unroll
+    for (int r = 0; r < TS::A_PER_T; ++r) {
+      const int e = tid + kThreads * r;
+      As[(e % TS::BK) * TS::LDA + e / TS::BK] = ((am >> r) & 1u) ? ra[r] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < TS::B_PER_T; ++r) {
+      const int e = tid + kThreads * r;
+      Bs[(e / TS::BN) * TS::LDB + e % TS::BN] = ((bm >> r) & 1u) ? rb[r] : 0.f;
+    }
+  };
+  Acc<TS> acc;
+  acc.zero();
+  gemm_mainloop<TS>(lds, 0, a.K, load, store, acc, wm, wn, wk, lane);
   const int n = n0 + wn * 32 + acc_col(lane);
   if (n >= a.N) return;
 #pragma unroll
