@@ -153,14 +153,23 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_l1(const float* __restrict
   part2[(int64_t)blockIdx.y * mn + e] = acc;
 }
 
+// Partials are either in dW's own [o][i][tap] order or, with kk > 0, tap-major
+// [tap][o][i] (kk taps, oc x c per tap), which the row-streaming kernel writes
+// so that its stores are contiguous; the sum is mapped back to dW's order here.
 __global__ __launch_bounds__(kThreads) void dw_reduce_l2(float* __restrict__ dw,
                                                          const float* __restrict__ part, int n,
-                                                         int64_t mn) {
+                                                         int64_t mn, int kk, int oc, int c) {
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (e >= mn) return;
   float s = 0.f;
   for (int k = 0; k < n; ++k) s += part[(int64_t)k * mn + e];
-  dw[e] += s;
+  int64_t d = e;
+  if (kk > 0) {
+    const int t = (int)(e / ((int64_t)oc * c)), r = (int)(e - (int64_t)t * oc * c);
+    const int o = r / c, i = r - o * c;
+    d = ((int64_t)o * c + i) * kk + t;
+  }
+  dw[d] += s;
 }
 
 // ---------------------------------------------------------------------------
@@ -311,18 +320,19 @@ __global__ __launch_bounds__(kDw3Threads, 2) void conv_dw3_rows(
     }
   }
 
-  float* dst = direct ? out : out + (int64_t)split * g.OC * g.J;
+  // the only split adds into dW ([o][i][tap]); partials are tap-major [tap][o][i]
+  // (contiguous stores), mapped back by the reduction
   const int i = cb * 32 + (lane & 31);
 #pragma unroll
   for (int kw = 0; kw < 3; ++kw)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int o = ob * 64 + 32 * oh + acc_row(r, lane);
-      const int64_t e = (int64_t)o * g.J + i * 9 + kh * 3 + kw;
+      const int t = kh * 3 + kw;
       if (direct)
-        dst[e] += acc[kw][r];
+        out[(int64_t)o * g.J + i * 9 + t] += acc[kw][r];
       else
-        dst[e] = acc[kw][r];
+        out[(int64_t)split * g.OC * g.J + ((int64_t)t * g.OC + o) * g.C + i] = acc[kw][r];
     }
 }
 
@@ -1178,7 +1188,7 @@ size_t conv_fused_workspace(const ConvGeom& g) {
 }
 
 static int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
-                            hipStream_t st);
+                            int tapmajor, hipStream_t st);
 
 int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
                            float* dw, float* dx, int accumulate, float* ws, hipStream_t st) {
@@ -1199,7 +1209,7 @@ int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, c
   }
   const int rc = check_launch("conv_smallc_dwdx");
   if (rc) return rc;
-  return launch_dw_reduce(g, dw, ws, p.wgs, p.groups, st);
+  return launch_dw_reduce(g, dw, ws, p.wgs, p.groups, 0, st);
 }
 
 size_t conv_dw_workspace(const ConvGeom& g) {
@@ -1258,23 +1268,24 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
   }
   int rc = check_launch(p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel");
   if (rc != CBB_OK || direct) return rc;
-  return launch_dw_reduce(g, dw, ws, p.splits, p.groups, st);
+  return launch_dw_reduce(g, dw, ws, p.splits, p.groups, p.rows_tc > 0, st);
 }
 
 // dw += ordered sum of the `splits` partials in ws (two levels when groups > 0).
 static int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
-                            hipStream_t st) {
+                            int tapmajor, hipStream_t st) {
   const int64_t mn = (int64_t)g.OC * g.J;
   const unsigned eblocks = (unsigned)ceil_div(mn, kThreads);
+  const int kk = tapmajor ? g.K * g.K : 0;
   if (groups == 0) {
-    dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, ws, splits, mn);
+    dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, ws, splits, mn, kk, g.OC, g.C);
     return check_launch("dw_reduce_l2");
   }
   float* part2 = ws + (int64_t)splits * mn;
   dw_reduce_l1<<<dim3(eblocks, groups), kThreads, 0, st>>>(ws, part2, splits, mn);
   const int rc = check_launch("dw_reduce_l1");
   if (rc) return rc;
-  dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, part2, groups, mn);
+  dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, part2, groups, mn, kk, g.OC, g.C);
   return check_launch("dw_reduce_l2");
 }
 
