@@ -7,8 +7,8 @@ One step = the full backward pass of all five workloads back to back (single
 its full batch: that covers every step of the path (activation, BN, conv
 dW/dX/db, shortcut, route, upsample, max-pool, inner product, softmax loss).
 Inputs are seeded synthetic tensors already resident in HBM when timing
-starts.  ``value`` = algorithmic conv + inner-product GFLOP (dW + dX) of one
-step / seconds per step.
+starts.  ``value`` = algorithmic conv + inner-product GFLOP (dW + dX) of one step /
+seconds per step.
 
 The JSON line also carries the roofline of the dominant kernel (the stage of
 one layer that takes the most time; it is timed in place inside the timed
@@ -48,6 +48,9 @@ def parse():
                     help="profiling mode: run a plain device copy of this many bytes --reps times "
                          "(calibrates the HBM byte counters); no JSON line")
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured as HIP graphs instead of eager "
+                         "steps (measured no faster on MI355X: the step is GPU-bound)")
     return ap.parse_args()
 
 
@@ -134,6 +137,33 @@ def time_stages(runners, torch, reps=3):
     return sorted(res, reverse=True)
 
 
+def capture_step(runners, torch, dom=None):
+    """One step of every workload captured as HIP graphs (hipGraph, through
+    torch.cuda.CUDAGraph): the step is ~60 small and large kernels, and replaying a
+    graph removes the launch gaps between them.  With dom = (workload, layer, stage)
+    the step is cut into three graphs -- before that stage, the stage, after it -- so
+    that events recorded between their replays time the stage in every step."""
+    graphs = [torch.cuda.CUDAGraph() for _ in range(3 if dom else 1)]
+    cur = [0]
+
+    def mark(target, before):
+        if target:
+            graphs[cur[0]].capture_end()
+            cur[0] += 1
+            graphs[cur[0]].capture_begin()
+
+    capture_stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(capture_stream):
+        graphs[0].capture_begin()
+        for name, r in runners.items():
+            r.step(probe=(dom[1], dom[2], mark) if dom and name == dom[0] else None)
+        graphs[-1].capture_end()
+    torch.cuda.synchronize()
+    assert cur[0] == len(graphs) - 1, "the dominant stage was not captured"
+    return graphs
+
+
 def cpu_baseline(min_seconds=10.0, max_reps=4):
     """The oracle (double arithmetic on the fp32 inputs) on one full step of the suite at
     full batch, repeated until ``min_seconds`` of CPU time have passed (at most
@@ -207,40 +237,53 @@ def main():
     print(f"[bench] dominant stage {dom_name}.{dom_li}.{dom_stage} {dom_ms:.3f} ms",
           file=sys.stderr, flush=True)
 
-    # Timed region: K steps; the dominant stage is bracketed by events in every step.
-    dom_events = []
+    # Timed region: K steps enqueued eagerly (or, with --graph, replayed from HIP
+    # graphs with the dominant stage as its own graph); the dominant stage is bracketed
+    # by events on its stream in every step.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
 
-    def mark(target, before):
-        if target:
-            e = torch.cuda.Event(enable_timing=True)
-            e.record()
-            if before:
-                dom_events.append([e, None])
-            else:
-                dom_events[-1][1] = e
+    def eager_step(k):
+        def mark(target, before):
+            if target:
+                ev[k][0 if before else 1].record()
+        for name, r in runners.items():
+            r.step(probe=(dom_li, dom_stage, mark) if name == dom_name else None)
 
+    if not (not args.graph):
+        g_pre, g_dom, g_post = capture_step(runners, torch, (dom_name, dom_li, dom_stage))
+        for _ in range(2):  # the first replays upload the graphs
+            g_pre.replay(); g_dom.replay(); g_post.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps):
-        for name, r in runners.items():
-            r.step(probe=(dom_li, dom_stage, mark) if name == dom_name else None)
+    for k in range(args.steps):
+        if (not args.graph):
+            eager_step(k)
+            continue
+        g_pre.replay()
+        ev[k][0].record()
+        g_dom.replay()
+        ev[k][1].record()
+        g_post.replay()
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(stop)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    dom_avg_ms = sum(a.elapsed_time(b) for a, b in dom_events) / len(dom_events)
+    dom_avg_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
 
-    # Per-workload breakdown (outside the timed region).
+    # Per-workload breakdown (outside the timed region), also from graph replays.
     per = {}
     for name, r in runners.items():
+        run = r.step if (not args.graph) else capture_step({name: r}, torch)[0].replay
+        run()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for _ in range(5):
-            r.step()
+            run()
         e.record()
         torch.cuda.synchronize()
         ms = s.elapsed_time(e) / 5
