@@ -250,7 +250,7 @@ def main():
         for name, r in runners.items():
             r.step(probe=(dom_li, dom_stage, mark) if name == dom_name else None)
 
-    if not (not args.graph):
+    if args.graph:
         g_pre, g_dom, g_post = capture_step(runners, torch, (dom_name, dom_li, dom_stage))
         for _ in range(2):  # the first replays upload the graphs
             g_pre.replay(); g_dom.replay(); g_post.replay()
@@ -260,7 +260,7 @@ def main():
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
     for k in range(args.steps):
-        if (not args.graph):
+        if not args.graph:
             eager_step(k)
             continue
         g_pre.replay()
@@ -278,7 +278,7 @@ def main():
     # Per-workload breakdown (outside the timed region), also from graph replays.
     per = {}
     for name, r in runners.items():
-        run = r.step if (not args.graph) else capture_step({name: r}, torch)[0].replay
+        run = r.step if not args.graph else capture_step({name: r}, torch)[0].replay
         run()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
