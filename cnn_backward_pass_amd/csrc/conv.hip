@@ -856,9 +856,10 @@ __global__ __launch_bounds__(kThreads) void conv_dx_smallc_kernel(ConvGeom g,
 //       K = the tile's 256 pixels, two per 32x32x2 step; each wave takes 64
 //       pixels and keeps its 32x32 accumulator across tiles.
 //   dX: vector ALUs.  Wave w sums output channels [8w, 8w+8) for all 256
-//       pixels, four neighbouring pixels per lane, with wave-uniform weight
-//       reads; the four waves' partial sums meet in LDS and are added in a
-//       fixed order.
+//       pixels, four pixels of one column per lane (neighbouring lanes take
+//       neighbouring columns, so the LDS reads are conflict-free), with
+//       wave-uniform weight reads; the four waves' partial sums meet in LDS
+//       and are added in a fixed order.
 // At the end the waves' dW blocks are summed through LDS and each work-group
 // writes its partial for the ordered split reduction.
 // ---------------------------------------------------------------------------
@@ -879,7 +880,11 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
   __shared__ __attribute__((aligned(16))) float Zs[32 * kFuZP];
   __shared__ __attribute__((aligned(16))) float Xs[CI * kFuZP];
   __shared__ float Pd[4 * CI * kFuTH * kFuTW];   // per-wave partial dx
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave-uniform by construction; readfirstlane lets the compiler know, so the
+  // weight reads below are scalar loads (a vector load would also wait, in order,
+  // for the next tile's prefetched loads)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_h = (g.H + kFuTH - 1) / kFuTH, tiles_w = (g.W + kFuTW - 1) / kFuTW;
   const int ntiles = g.N * tiles_h * tiles_w;
   const int t0 = blockIdx.x * tiles_per_wg, t1 = min(ntiles, t0 + tiles_per_wg);
@@ -964,8 +969,8 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  // dX: lane -> tile row pr, columns 4*pg .. 4*pg+3; wave -> output channels
-  const int pr = lane >> 3, pg = lane & 7;
+  // dX: lane -> tile column pc and row quad pq; wave -> output channels
+  const int pc = lane & 31, pq = lane >> 5;
   const int o_lo = 8 * wave, o_hi = min(g.OC, 8 * wave + 8);
 
   if (t0 < t1) fetch(t0);
@@ -989,42 +994,39 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
     }
 
     if (dx) {
-      // partial dx of this wave's channels: one running sum per (input channel,
-      // kernel row, pixel) -- 12*CI independent chains
-      float d[CI][3][4];
+      // partial dx of this wave's channels: lane -> tile column pc, rows 4*pq .. 4*pq+3
+      // (neighbouring lanes read neighbouring LDS words: no bank conflicts); pixel
+      // (r, pc) needs dz at region (r+2-kh, pc+5-kw): rows 4pq .. 4pq+5, columns
+      // pc+3 .. pc+5
+      float d[CI][4];
 #pragma unroll
       for (int i = 0; i < CI; ++i)
 #pragma unroll
-        for (int kh = 0; kh < 3; ++kh)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) d[i][kh][u] = 0.f;
-      // pixel (pr, 4pg+u) needs dz at region (pr+2-kh, 4pg+u+5-kw): rows pr..pr+2,
-      // columns 4pg+3 .. 4pg+8
-      const float* zp = Zs + pr * kFuRW + 4 * pg + 3;
+        for (int u = 0; u < 4; ++u) d[i][u] = 0.f;
+      const float* zp = Zs + 4 * pq * kFuRW + pc + 3;
       for (int o = o_lo; o < o_hi; ++o) {
-        float z[3][6];
+        float z[6][3];
 #pragma unroll
-        for (int u = 0; u < 3; ++u)
+        for (int u = 0; u < 6; ++u)
 #pragma unroll
-          for (int v = 0; v < 6; ++v) z[u][v] = zp[o * kFuZP + u * kFuRW + v];
+          for (int v = 0; v < 3; ++v) z[u][v] = zp[o * kFuZP + u * kFuRW + v];
         const float* wo = wt + (int64_t)o * CI * 9;
 #pragma unroll
-        for (int i = 0; i < CI; ++i)
+        for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
-          for (int kh = 0; kh < 3; ++kh)
+          for (int kw = 0; kw < 3; ++kw)
 #pragma unroll
-            for (int kw = 0; kw < 3; ++kw) {
+            for (int i = 0; i < CI; ++i) {
               const float wv = wo[i * 9 + kh * 3 + kw];
 #pragma unroll
-              for (int u = 0; u < 4; ++u) d[i][kh][u] += wv * z[2 - kh][u + 2 - kw];
+              for (int u = 0; u < 4; ++u) d[i][u] += wv * z[u + 2 - kh][2 - kw];
             }
       }
 #pragma unroll
       for (int i = 0; i < CI; ++i)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          Pd[(wave * CI + i) * (kFuTH * kFuTW) + pr * kFuTW + 4 * pg + u] =
-              (d[i][0][u] + d[i][1][u]) + d[i][2][u];
+          Pd[(wave * CI + i) * (kFuTH * kFuTW) + (4 * pq + u) * kFuTW + pc] = d[i][u];
     }
     __syncthreads();  // LDS tile reads and the partial dx are complete
     if (dx) {
