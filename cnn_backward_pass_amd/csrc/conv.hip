@@ -173,6 +173,183 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_l2(float* __restrict__ dw,
 }
 
 // ---------------------------------------------------------------------------
+// 1x1 stride-1 convolutions are plain batched GEMMs over the pixels q = (n, p):
+//   dW[o][i] = sum_q dz[n][o][p] * x[n][i][p]          (M = o, N = i, K = q)
+//   dx[n][i][p] = sum_o W[o][i] * dz[n][o][p]          (M = i, N = q, K = o)
+// Both operands are contiguous along the GEMM's K (dW) or N (dX) index, so the
+// tiles are staged with 16-byte loads (H*W and C_in are multiples of 4, so a
+// 4-pixel group never straddles two images).  Same tile core and ordered split
+// reduction as conv_dw_kernel.
+// ---------------------------------------------------------------------------
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+template <class TS>
+__global__ __launch_bounds__(kThreads) void conv1x1_dw_kernel(ConvGeom g, const float* __restrict__ x,
+                                                              const float* __restrict__ dz,
+                                                              float* __restrict__ out,
+                                                              int64_t k_chunk, int tiles_n,
+                                                              int nsplits, int direct) {
+  static_assert(TS::BK == 32 && TS::BM * 8 % kThreads == 0 && TS::BN * 8 % kThreads == 0, "");
+  __shared__ float lds[TS::LDS_FLOATS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
+  const int tiles = gridDim.x / nsplits;
+  const int split = blockIdx.x / tiles, tile = blockIdx.x - split * tiles;
+  const int m0 = (tile / tiles_n) * TS::BM, n0 = (tile % tiles_n) * TS::BN;
+  const int64_t kbeg = (int64_t)split * k_chunk;
+  const int64_t kend = min(g.Q, kbeg + k_chunk);
+  constexpr int AV = TS::BM * 8 / kThreads, BV = TS::BN * 8 / kThreads;  // float4 per thread
+  f4v ra[AV], rb[BV];
+  uint32_t am = 0, bm = 0;
+  auto load = [&](int64_t k0) {
+    am = 0;
+    bm = 0;
+#pragma unroll
+    for (int r = 0; r < AV; ++r) {
+      const int f = tid + kThreads * r, ml = f >> 3, q4 = f & 7;
+      const int64_t q = k0 + 4 * q4;
+      const int n = (int)(q / g.HW), pix = (int)(q - (int64_t)n * g.HW);
+      const int o = m0 + ml;
+      const bool ok = q < kend && o < g.OC;
+      ra[r] = *(const f4v*)(dz + (ok ? ((int64_t)n * g.OC + o) * g.HW + pix : 0));
+      am |= (uint32_t)ok << r;
+    }
+#pragma unroll
+    for (int r = 0; r < BV; ++r) {
+      const int f = tid + kThreads * r, nl = f >> 3, q4 = f & 7;
+      const int64_t q = k0 + 4 * q4;
+      const int n = (int)(q / g.HW), pix = (int)(q - (int64_t)n * g.HW);
+      const int i = n0 + nl;
+      const bool ok = q < kend && i < g.C;
+      rb[r] = *(const f4v*)(x + (ok ? ((int64_t)n * g.C + i) * g.HW + pix : 0));
+      bm |= (uint32_t)ok << r;
+    }
+  };
+  auto store = [&](float* buf) {
+    float* As = buf;
+    float* Bs = buf + TS::BK * TS::LDA;
+#pragma unroll
+    for (int r = 0; r < AV; ++r) {
+      const int f = tid + kThreads * r, ml = f >> 3, q4 = f & 7;
+      const bool ok = (am >> r) & 1u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[(4 * q4 + e) * TS::LDA + ml] = ok ? ra[r][e] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < BV; ++r) {
+      const int f = tid + kThreads * r, nl = f >> 3, q4 = f & 7;
+      const bool ok = (bm >> r) & 1u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Bs[(4 * q4 + e) * TS::LDB + nl] = ok ? rb[r][e] : 0.f;
+    }
+  };
+  Acc<TS> acc;
+  acc.zero();
+  gemm_mainloop<TS>(lds, kbeg, kend, load, store, acc, wm, wn, wk, lane);
+  reduce_wk<TS>(acc, lds, wm, wn, wk, lane);
+  if (wk != 0) return;
+  float* dst = direct ? out : out + (int64_t)split * g.OC * g.J;
+#pragma unroll
+  for (int ai = 0; ai < TS::RM; ++ai)
+#pragma unroll
+    for (int aj = 0; aj < TS::RN; ++aj) {
+      const int i = n0 + acc_n0<TS>(wn, aj) + acc_col(lane);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = m0 + acc_m0<TS>(wm, ai) + acc_row(r, lane);
+        if (o < g.OC && i < g.C) {
+          const int64_t e = (int64_t)o * g.J + i;
+          if (direct)
+            dst[e] += acc.v[ai][aj][r];
+          else
+            dst[e] = acc.v[ai][aj][r];
+        }
+      }
+    }
+}
+
+template <class TS>
+__global__ __launch_bounds__(kThreads) void conv1x1_dx_kernel(ConvGeom g, const float* __restrict__ wt,
+                                                              const float* __restrict__ dz,
+                                                              float* __restrict__ dx, int ctiles,
+                                                              int accumulate) {
+  static_assert(TS::BK == 32 && TS::BM * 8 % kThreads == 0 && TS::BN * 8 % kThreads == 0, "");
+  __shared__ float lds[TS::LDS_FLOATS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
+  const int ctile = blockIdx.x % ctiles, ptile = blockIdx.x / ctiles;
+  const int m0 = ctile * TS::BM;
+  const int64_t q0 = (int64_t)ptile * TS::BN;
+  constexpr int AV = TS::BM * 8 / kThreads, BV = TS::BN * 8 / kThreads;
+  constexpr int A4 = TS::BM / 4, B4 = TS::BN / 4;  // float4 per K row
+  f4v ra[AV], rb[BV];
+  uint32_t am = 0, bm = 0;
+  auto load = [&](int64_t k0) {
+    am = 0;
+    bm = 0;
+#pragma unroll
+    for (int r = 0; r < AV; ++r) {  // A[i][o] = W[o][i]: 16-byte groups along i
+      const int f = tid + kThreads * r, kl = f / A4, c4 = f % A4;
+      const int o = (int)k0 + kl, i = m0 + 4 * c4;
+      const bool ok = o < g.OC && i < g.C;
+      ra[r] = *(const f4v*)(wt + (ok ? (int64_t)o * g.C + i : 0));
+      am |= (uint32_t)ok << r;
+    }
+#pragma unroll
+    for (int r = 0; r < BV; ++r) {  // B[o][q] = dz[n][o][p]: 16-byte groups along q
+      const int f = tid + kThreads * r, kl = f / B4, q4 = f % B4;
+      const int o = (int)k0 + kl;
+      const int64_t q = q0 + 4 * q4;
+      const int n = (int)(q / g.HW), pix = (int)(q - (int64_t)n * g.HW);
+      const bool ok = o < g.OC && q < g.Q;
+      rb[r] = *(const f4v*)(dz + (ok ? ((int64_t)n * g.OC + o) * g.HW + pix : 0));
+      bm |= (uint32_t)ok << r;
+    }
+  };
+  auto store = [&](float* buf) {
+    float* As = buf;
+    float* Bs = buf + TS::BK * TS::LDA;
+#pragma unroll
+    for (int r = 0; r < AV; ++r) {
+      const int f = tid + kThreads * r, kl = f / A4, c4 = f % A4;
+      const bool ok = (am >> r) & 1u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) As[kl * TS::LDA + 4 * c4 + e] = ok ? ra[r][e] : 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < BV; ++r) {
+      const int f = tid + kThreads * r, kl = f / B4, q4 = f % B4;
+      const bool ok = (bm >> r) & 1u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Bs[kl * TS::LDB + 4 * q4 + e] = ok ? rb[r][e] : 0.f;
+    }
+  };
+  Acc<TS> acc;
+  acc.zero();
+  gemm_mainloop<TS>(lds, 0, g.OC, load, store, acc, wm, wn, wk, lane);
+  reduce_wk<TS>(acc, lds, wm, wn, wk, lane);
+  if (wk != 0) return;
+#pragma unroll
+  for (int aj = 0; aj < TS::RN; ++aj) {
+    const int64_t q = q0 + acc_n0<TS>(wn, aj) + acc_col(lane);
+    if (q >= g.Q) continue;
+    const int n = (int)(q / g.HW), pix = (int)(q - (int64_t)n * g.HW);
+    float* base = dx + (int64_t)n * g.C * g.HW + pix;
+#pragma unroll
+    for (int ai = 0; ai < TS::RM; ++ai)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = m0 + acc_m0<TS>(wm, ai) + acc_row(r, lane);
+        if (i < g.C) {
+          float* d = base + (int64_t)i * g.HW;
+          const float v = acc.v[ai][aj][r];
+          *d = accumulate ? *d + v : v;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Weight gradient of a 3x3, pad-1 convolution at stride 1 or 2, row-streaming
 // tile-direct form (same sum as conv_dw_kernel, no im2col gather).
 //
@@ -971,7 +1148,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
 
   // dX: lane -> tile column pc and row quad pq; wave -> output channels
   const int pc = lane & 31, pq = lane >> 5;
-  const int o_lo = 8 * wave, o_hi = min(g.OC, 8 * wave + 8);
+  const int o_lo = 8 * wave;
 
   if (t0 < t1) fetch(t0);
   __syncthreads();  // the zero fill is complete before any staging
@@ -1004,13 +1181,18 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
 #pragma unroll
         for (int u = 0; u < 4; ++u) d[i][u] = 0.f;
       const float* zp = Zs + 4 * pq * kFuRW + pc + 3;
-      for (int o = o_lo; o < o_hi; ++o) {
+      // all eight channels of the wave unrolled (straight-line code lets the loads of
+      // one channel overlap the arithmetic of the previous); channels >= OC read zero
+      // rows of Zs, with their weight reads clamped to a valid channel
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int o = o_lo + k;
         float z[6][3];
 #pragma unroll
         for (int u = 0; u < 6; ++u)
 #pragma unroll
           for (int v = 0; v < 3; ++v) z[u][v] = zp[o * kFuZP + u * kFuRW + v];
-        const float* wo = wt + (int64_t)o * CI * 9;
+        const float* wo = wt + (int64_t)min(o, g.OC - 1) * CI * 9;
 #pragma unroll
         for (int kh = 0; kh < 3; ++kh)
 #pragma unroll
@@ -1094,6 +1276,7 @@ static const int kDwCand[DW_NSHAPES][3] = {{64, 64, 32},  {32, 32, 128}, {32, 64
 struct DwPlan {
   int shape, bm, bn, bk, tiles_m, tiles_n, splits, groups;
   int64_t k_chunk;
+  int conv1x1;                // 1: conv1x1_dw_kernel
   int rows_tc;                // > 0: conv_dw3_rows with this strip width
   int strips, rchunks, rlen;  // its strips, row runs per (image, strip), rows per run
 };
@@ -1128,9 +1311,31 @@ static bool plan_dw3_rows(const ConvGeom& g, DwPlan& p) {
   return true;
 }
 
+static bool conv1x1_ok(const ConvGeom& g) {
+  return g.K == 1 && g.S == 1 && g.P == 0 && g.HW % 4 == 0 && g.C % 4 == 0;
+}
+
 static DwPlan plan_dw(const ConvGeom& g) {
   DwPlan best{};
   if (plan_dw3_rows(g, best)) return best;
+  if (conv1x1_ok(g)) {  // 64x64 tiles of (o, i), 16-byte staging
+    best.conv1x1 = 1;
+    best.shape = DW_64x64;
+    best.bm = best.bn = 64;
+    best.bk = 32;
+    best.tiles_m = (int)ceil_div(g.OC, 64);
+    best.tiles_n = (int)ceil_div(g.J, 64);
+    const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
+    const int64_t ktiles = ceil_div(g.Q, 32);
+    int64_t splits = ceil_div(1024, tiles);
+    splits = std::min<int64_t>(splits, std::max<int64_t>(1, ktiles / 4));
+    splits = std::max<int64_t>(1, std::min<int64_t>(splits, 4096));
+    const int64_t chunk = ceil_div(ktiles, splits) * 32;
+    best.splits = (int)ceil_div(g.Q, chunk);
+    best.k_chunk = chunk;
+    best.groups = best.splits > kReduceGroup ? (int)ceil_div(best.splits, kReduceGroup) : 0;
+    return best;
+  }
   double best_cost = 1e300;
   for (int s = 0; s < DW_NSHAPES; ++s) {
     const int bm = kDwCand[s][0], bn = kDwCand[s][1];
@@ -1163,6 +1368,8 @@ static DwPlan plan_dw(const ConvGeom& g) {
   return best;
 }
 
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 // Fused small-channel dW + dX: which layers, and how the tiles are split.
 bool conv_fused_dwdx_ok(const ConvGeom& g) {
   return g.C >= 1 && g.C <= 3 && g.K == 3 && g.P == 1 && g.S == 1 && g.OC <= 32 && g.W % 4 == 0;
@@ -1176,7 +1383,7 @@ static FuPlan plan_fused(const ConvGeom& g) {
   FuPlan p{};
   const int64_t ntiles =
       (int64_t)g.N * ceil_div(g.H, kFuTH) * ceil_div(g.W, kFuTW);
-  const int64_t target = 512;  // two resident work-groups per CU
+  const int64_t target = 1024;  // two rounds of two resident work-groups per CU
   p.tiles_per_wg = (int)std::max<int64_t>(1, ceil_div(ntiles, target));
   p.wgs = (int)ceil_div(ntiles, p.tiles_per_wg);
   p.groups = p.wgs > kReduceGroup ? (int)ceil_div(p.wgs, kReduceGroup) : 0;
@@ -1253,7 +1460,18 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
   const DwPlan p = plan_dw(g);
   const int direct = p.splits == 1;
   float* out = direct ? dw : ws;
-  if (p.rows_tc > 0) {
+  if (p.conv1x1) {
+    // 16-byte staging needs 16-byte aligned tensors; otherwise the general kernel
+    // runs the same tiles and splits (same partial layout and workspace)
+    using TS = TileShape<2, 2, 1>;
+    const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n * p.splits);
+    if (aligned16(x) && aligned16(dz))
+      conv1x1_dw_kernel<TS><<<blocks, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk, p.tiles_n,
+                                                         p.splits, direct);
+    else
+      conv_dw_kernel<TS><<<blocks, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk, p.tiles_n,
+                                                      p.splits, direct);
+  } else if (p.rows_tc > 0) {
     if (g.S == 1)
       launch_dw3_rows<1>(g, p, x, dz, out, direct, st);
     else
@@ -1268,7 +1486,8 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
     case DW_64x128: launch_dw_tile<TileShape<2, 2, 1, 1, 1, 2>>(g, p, x, dz, out, direct, st); break;
     default: launch_dw_tile<TileShape<2, 2, 1, 1, 2, 2>>(g, p, x, dz, out, direct, st); break;
   }
-  int rc = check_launch(p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel");
+  int rc = check_launch(p.conv1x1 ? "conv1x1_dw_kernel"
+                                  : p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel");
   if (rc != CBB_OK || direct) return rc;
   return launch_dw_reduce(g, dw, ws, p.splits, p.groups, p.rows_tc > 0, st);
 }
@@ -1292,7 +1511,7 @@ static int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits,
 }
 
 // ----------------------------------------------------------------------------- dX planning
-enum DxKind { DX_SMALLC = 0, DX_32x128, DX_64x64, DX_D3S1, DX_D3S2 };
+enum DxKind { DX_SMALLC = 0, DX_32x128, DX_64x64, DX_D3S1, DX_D3S2, DX_1X1 };
 
 struct DxPlan {
   int kind, bm, bn, bk, ctiles, pixtiles, ksplits;
@@ -1307,6 +1526,13 @@ static DxPlan plan_dx(const ConvGeom& g) {
   if (smallc_ok(g)) {
     p.kind = DX_SMALLC;
     p.ksplits = 1;
+    return p;
+  }
+  if (conv1x1_ok(g)) {
+    p.kind = DX_1X1;
+    p.ksplits = 1;
+    p.ctiles = (int)ceil_div(g.C, 64);
+    p.pixtiles = (int)ceil_div(g.Q, 64);
     return p;
   }
   // tile-direct 3x3: split the output channels when the grid cannot fill the GPU
@@ -1402,6 +1628,16 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
     const unsigned rblocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
     dx_splitk_reduce<<<rblocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
     return check_launch("dx_splitk_reduce");
+  }
+  if (p.kind == DX_1X1) {
+    if (!(aligned16(wt) && aligned16(dz))) {  // same tiles, no split: the general kernel
+      launch_dx_mfma<TileShape<2, 2, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
+      return check_launch("conv_dx_kernel");
+    }
+    const unsigned blocks = (unsigned)((int64_t)p.ctiles * p.pixtiles);
+    conv1x1_dx_kernel<TileShape<2, 2, 1>><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, p.ctiles,
+                                                                        accumulate);
+    return check_launch("conv1x1_dx_kernel");
   }
   if (p.kind == DX_SMALLC) {
     switch (g.C) {

@@ -53,6 +53,8 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (4, 32, 64, 52, 64, 3, 1, 1, True, "leaky"),     # dW row-streaming: many runs, two-level sum
     (1, 32, 1, 30, 64, 3, 1, 1, True, "leaky"),      # dW row-streaming: a single output row
     (2, 32, 2, 60, 64, 3, 2, 1, True, "leaky"),      # dW row-streaming: stride 2, one output row
+    (2, 64, 12, 12, 96, 1, 1, 0, True, "leaky"),     # 1x1 GEMMs with 16-byte staging, ragged o
+    (3, 20, 6, 10, 70, 1, 1, 0, False, "linear"),    # 1x1 GEMMs: ragged i and o tiles
 ]
 
 
@@ -193,6 +195,36 @@ def test_conv_backward_weights_data(case):
                                    False, ws)
     torch.cuda.synchronize()
     assert_close("dw (no dx)", dw.cpu().double().numpy(), ref_dw)
+
+
+@pytest.mark.parametrize("case", [(2, 64, 12, 12, 96, 1, 1, 0), (1, 3, 9, 12, 8, 3, 1, 1)])
+def test_misaligned_tensors_take_the_general_kernels(case):
+    """Tensors that are not 16-byte aligned (a view one float into a buffer) go through
+    the general kernels (same tiles, same workspace) and give the same gradients."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    n, c, h, w, oc, k, s, p = case
+    announce(f"misaligned {case}")
+    r = np.random.default_rng(77)
+    oh, ow = O.conv_out_dim(h, k, s, p), O.conv_out_dim(w, k, s, p)
+    x = r.normal(size=(n, c, h, w)).astype(np.float32)
+    wt = (r.normal(size=(oc, c, k, k)) * 0.3).astype(np.float32)
+    dz = r.normal(size=(n, oc, oh, ow)).astype(np.float32)
+
+    def shifted(a):  # contiguous view starting 4 bytes after a 256-byte aligned allocation
+        buf = torch.empty(a.size + 1, dtype=torch.float32, device="cuda")
+        v = buf[1:].view(a.shape)
+        v.copy_(torch.from_numpy(a))
+        return v
+
+    desc = cbb.conv_desc(n, c, h, w, oc, k, s, p, False, "linear")
+    ws = cbb.workspace(cbb.conv_block_workspace_size(desc))
+    dw = _t(torch, np.zeros(wt.shape, np.float32))
+    dx = shifted(np.zeros(x.shape, np.float32))
+    cbb.conv_backward_weights_data(desc, shifted(x), shifted(wt), shifted(dz), dw, dx, False, ws)
+    torch.cuda.synchronize()
+    assert_close("dw", dw.cpu().double().numpy(), O.conv_backward_weights(x, dz, k, s, p))
+    assert_close("dx", dx.cpu().double().numpy(), O.conv_backward_data(wt, dz, (h, w), s, p))
 
 
 def test_conv_one_hot_probes_bit_exact():
