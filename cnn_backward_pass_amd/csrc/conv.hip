@@ -1023,40 +1023,42 @@ __global__ __launch_bounds__(kThreads) void conv_dx_smallc_kernel(ConvGeom g,
 // RGB image) in one pass over dz.  Both gradients read the same dz and the
 // layer is HBM-bound, so fusing them halves its traffic.
 //
-// Persistent work-groups walk a contiguous run of 8 x 32 pixel tiles.  Per
-// tile, dz for all output channels and x for all input channels are staged in
-// LDS over the tile plus its halo, as 16-byte loads of 10 rows x 40 columns
-// (columns w0-4 .. w0+35; the image width is a multiple of 4, so every
-// 16-byte group is wholly inside or outside the image); the next tile's loads
-// are in registers while this one is computed.
+// Persistent work-groups of 8 waves walk a contiguous run of 8 x 32 pixel
+// tiles.  Per tile, dz for all output channels and x for all input channels
+// are staged in LDS over the tile plus its halo, as 16-byte loads of 10 rows x
+// 40 columns (columns w0-4 .. w0+35; the image width is a multiple of 4, so
+// every 16-byte group is wholly inside or outside the image); the next tile's
+// loads are in registers while this one is computed.
 //   dW: matrix cores, M = o (32), N = (i, kh, kw) (9*CI <= 27 of 32 columns),
-//       K = the tile's 256 pixels, two per 32x32x2 step; each wave takes 64
-//       pixels and keeps its 32x32 accumulator across tiles.
-//   dX: vector ALUs.  Wave w sums output channels [8w, 8w+8) for all 256
-//       pixels, four pixels of one column per lane (neighbouring lanes take
-//       neighbouring columns, so the LDS reads are conflict-free), with
-//       wave-uniform weight reads; the four waves' partial sums meet in LDS
-//       and are added in a fixed order.
-// At the end the waves' dW blocks are summed through LDS and each work-group
-// writes its partial for the ordered split reduction.
+//       K = the tile's 256 pixels, two per 32x32x2 step; wave w takes tile row
+//       w and keeps its 32x32 accumulator across tiles.
+//   dX: vector ALUs.  Waves are (output-channel quarter) x (tile half): each
+//       sums 8 output channels for 128 pixels, two pixels of one column per
+//       lane (neighbouring lanes take neighbouring columns, so the LDS reads
+//       are conflict-free), with wave-uniform weight reads; the four quarters'
+//       partial sums meet in LDS and are added in a fixed order.
+// At the end the waves' dW blocks are summed through LDS in a fixed order and
+// each work-group writes its partial for the ordered split reduction.
 // ---------------------------------------------------------------------------
+constexpr int kFuThreads = 512;
 constexpr int kFuTH = 8, kFuTW = 32;
 constexpr int kFuRW = 40, kFuRH = kFuTH + 2;       // staged region: 10 x 40
 constexpr int kFuZP = kFuRH * kFuRW + 4;           // LDS pitch per channel (16-byte aligned)
 constexpr int kFuNV = kFuRH * (kFuRW / 4);         // 16-byte groups per channel
-constexpr int kFuZV = (32 * kFuNV + kThreads - 1) / kThreads;  // dz groups per thread
-constexpr int kFuXV = (3 * kFuNV + kThreads - 1) / kThreads;   // x groups per thread
+constexpr int kFuZV = (32 * kFuNV + kFuThreads - 1) / kFuThreads;  // dz groups per thread
+constexpr int kFuXV = (3 * kFuNV + kFuThreads - 1) / kFuThreads;   // x groups per thread
 
 template <int CI>
-__global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
+__global__ __launch_bounds__(kFuThreads, 2) void conv_smallc_dwdx(
     ConvGeom g, const float* __restrict__ x, const float* __restrict__ wt,
     const float* __restrict__ dz, float* __restrict__ dwpart, float* __restrict__ dx,
     int tiles_per_wg, int accumulate) {
   static_assert(CI >= 1 && CI <= 3, "9*CI columns must fit one 32-wide block");
+  constexpr int NT = kFuThreads;
   typedef float f4 __attribute__((ext_vector_type(4)));
   __shared__ __attribute__((aligned(16))) float Zs[32 * kFuZP];
   __shared__ __attribute__((aligned(16))) float Xs[CI * kFuZP];
-  __shared__ float Pd[4 * CI * kFuTH * kFuTW];   // per-wave partial dx
+  __shared__ float Pd[4 * CI * kFuTH * kFuTW];   // per-quarter partial dx
   const int tid = threadIdx.x, lane = tid & 63;
   // wave-uniform by construction; readfirstlane lets the compiler know, so the
   // weight reads below are scalar loads (a vector load would also wait, in order,
@@ -1068,7 +1070,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
   const int zcount = g.OC * kFuNV, xcount = CI * kFuNV;
 
   // output channels >= OC stay zero in LDS for the whole kernel
-  for (int e = tid; e < 32 * kFuZP; e += kThreads) Zs[e] = 0.f;
+  for (int e = tid; e < 32 * kFuZP; e += NT) Zs[e] = 0.f;
 
   static_assert(kFuZV <= 32 && kFuXV <= 32, "one mask bit per staged group");
   f4 pz[kFuZV], px[kFuXV];
@@ -1095,7 +1097,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
     xmask = 0;
 #pragma unroll
     for (int i = 0; i < kFuZV; ++i) {
-      const int e = tt + i * kThreads;
+      const int e = tt + i * NT;
       const int o = e / kFuNV, q = e - o * kFuNV;
       const int rr = q / (kFuRW / 4), v = q - rr * (kFuRW / 4);
       const int h = h0 - 1 + rr, w = w0 - 4 + 4 * v;
@@ -1105,7 +1107,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
     }
 #pragma unroll
     for (int i = 0; i < kFuXV; ++i) {
-      const int e = tt + i * kThreads;
+      const int e = tt + i * NT;
       const int c = e / kFuNV, q = e - c * kFuNV;
       const int rr = q / (kFuRW / 4), v = q - rr * (kFuRW / 4);
       const int h = h0 - 1 + rr, w = w0 - 4 + 4 * v;
@@ -1120,13 +1122,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < kFuZV; ++i) {
-      const int e = tt + i * kThreads;
+      const int e = tt + i * NT;
       const int o = e / kFuNV, q = e - o * kFuNV;
       if (e < zcount) *(f4*)(Zs + o * kFuZP + 4 * q) = ((zmask >> i) & 1u) ? pz[i] : zero;
     }
 #pragma unroll
     for (int i = 0; i < kFuXV; ++i) {
-      const int e = tt + i * kThreads;
+      const int e = tt + i * NT;
       const int c = e / kFuNV, q = e - c * kFuNV;
       if (e < xcount) *(f4*)(Xs + c * kFuZP + 4 * q) = ((xmask >> i) & 1u) ? px[i] : zero;
     }
@@ -1146,9 +1148,11 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-  // dX: lane -> tile column pc and row quad pq; wave -> output channels
-  const int pc = lane & 31, pq = lane >> 5;
-  const int o_lo = 8 * wave;
+  // dX: wave -> output channels [8*oq, 8*oq+8) and tile rows [4*half, 4*half+4);
+  // lane -> column pc, rows 4*half + 2*pp + {0, 1}
+  const int oq = wave & 3, half = wave >> 2;
+  const int pc = lane & 31, pp = lane >> 5;
+  const int prow = 4 * half + 2 * pp;  // first of the lane's two tile rows
 
   if (t0 < t1) fetch(t0);
   __syncthreads();  // the zero fill is complete before any staging
@@ -1157,13 +1161,11 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
     __syncthreads();
     if (t + 1 < t1) fetch(t + 1);  // in flight during this tile's work
 
-    // dW: the wave's 64 pixels = tile rows 2*wave, 2*wave + 1; step s takes
-    // pixels 2s + kq of them
+    // dW: wave w takes tile row w (32 pixels); step s takes pixels 2s + kq
 #pragma unroll
-    for (int s = 0; s < 32; ++s) {
+    for (int s = 0; s < 16; ++s) {
       if (s % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // bounds the operand prefetch
-      const int pt = 64 * wave + 2 * s + kq;
-      const int po = (pt / kFuTW) * kFuRW + (pt % kFuTW);
+      const int po = wave * kFuRW + 2 * s + kq;
       const float a = Zs[aoff + po];
       const float bx = Xs[boff + po];
       const float b = jv ? bx : 0.f;
@@ -1171,25 +1173,23 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
     }
 
     if (dx) {
-      // partial dx of this wave's channels: lane -> tile column pc, rows 4*pq .. 4*pq+3
-      // (neighbouring lanes read neighbouring LDS words: no bank conflicts); pixel
-      // (r, pc) needs dz at region (r+2-kh, pc+5-kw): rows 4pq .. 4pq+5, columns
-      // pc+3 .. pc+5
-      float d[CI][4];
+      // pixel (r, pc) needs dz at region (r+2-kh, pc+5-kw): rows prow .. prow+3,
+      // columns pc+3 .. pc+5.  All eight channels unrolled; channels >= OC read
+      // zero rows of Zs, with their weight reads clamped to a valid channel.
+      float d[CI][2][3];  // (input channel, pixel, kernel row): independent chains
 #pragma unroll
       for (int i = 0; i < CI; ++i)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) d[i][u] = 0.f;
-      const float* zp = Zs + 4 * pq * kFuRW + pc + 3;
-      // all eight channels of the wave unrolled (straight-line code lets the loads of
-      // one channel overlap the arithmetic of the previous); channels >= OC read zero
-      // rows of Zs, with their weight reads clamped to a valid channel
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int kh = 0; kh < 3; ++kh) d[i][u][kh] = 0.f;
+      const float* zp = Zs + prow * kFuRW + pc + 3;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const int o = o_lo + k;
-        float z[6][3];
+        const int o = 8 * oq + k;
+        float z[4][3];
 #pragma unroll
-        for (int u = 0; u < 6; ++u)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int v = 0; v < 3; ++v) z[u][v] = zp[o * kFuZP + u * kFuRW + v];
         const float* wo = wt + (int64_t)min(o, g.OC - 1) * CI * 9;
@@ -1201,17 +1201,18 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
             for (int i = 0; i < CI; ++i) {
               const float wv = wo[i * 9 + kh * 3 + kw];
 #pragma unroll
-              for (int u = 0; u < 4; ++u) d[i][u] += wv * z[u + 2 - kh][2 - kw];
+              for (int u = 0; u < 2; ++u) d[i][u][kh] += wv * z[u + 2 - kh][2 - kw];
             }
       }
 #pragma unroll
       for (int i = 0; i < CI; ++i)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          Pd[(wave * CI + i) * (kFuTH * kFuTW) + (4 * pq + u) * kFuTW + pc] = d[i][u];
+        for (int u = 0; u < 2; ++u)
+          Pd[(oq * CI + i) * (kFuTH * kFuTW) + (prow + u) * kFuTW + pc] =
+              (d[i][u][0] + d[i][u][1]) + d[i][u][2];
     }
     __syncthreads();  // LDS tile reads and the partial dx are complete
-    if (dx) {
+    if (dx && tid < kFuTH * kFuTW) {
       int n, h0, w0;
       tile_origin(t, n, h0, w0);
       const int r = tid / kFuTW, cc = tid - r * kFuTW;
@@ -1228,9 +1229,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
     }
   }
 
-  // Sum the four waves' dW blocks (fixed order) and write this work-group's partial.
+  // Sum the eight waves' dW blocks (fixed order) and write this work-group's partial.
   __syncthreads();
-  float* red = Zs;  // 4 x 16 x 64 floats
+  float* red = Zs;  // 8 x 16 x 64 floats
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
   __syncthreads();
@@ -1238,8 +1239,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_dwdx(
     float* dst = dwpart + (int64_t)blockIdx.x * g.OC * g.J;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float v = (red[r * 64 + lane] + red[(16 + r) * 64 + lane]) +
-                      (red[(32 + r) * 64 + lane] + red[(48 + r) * 64 + lane]);
+      float v = 0.f;
+#pragma unroll
+      for (int w8 = 0; w8 < 8; ++w8) v += red[(w8 * 16 + r) * 64 + lane];
       const int o = acc_row(r, lane);
       if (o < g.OC && j < 9 * CI) dst[o * g.J + j] = v;
     }
@@ -1404,15 +1406,15 @@ int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, c
   const FuPlan p = plan_fused(g);
   switch (g.C) {
     case 1:
-      conv_smallc_dwdx<1><<<p.wgs, kThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
+      conv_smallc_dwdx<1><<<p.wgs, kFuThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
                                                       accumulate);
       break;
     case 2:
-      conv_smallc_dwdx<2><<<p.wgs, kThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
+      conv_smallc_dwdx<2><<<p.wgs, kFuThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
                                                       accumulate);
       break;
     default:
-      conv_smallc_dwdx<3><<<p.wgs, kThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
+      conv_smallc_dwdx<3><<<p.wgs, kFuThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
                                                       accumulate);
       break;
   }
