@@ -1537,10 +1537,12 @@ static DxPlan plan_dx(const ConvGeom& g) {
     p.pixtiles = (int)ceil_div(g.Q, 64);
     return p;
   }
-  // tile-direct 3x3: split the output channels when the grid cannot fill the GPU
-  // (~2 work-groups per CU are resident), keeping >= 4 chunks per split
+  // tile-direct 3x3: split the output channels when the grid cannot fill the GPU,
+  // keeping >= 4 chunks per split.  Measured on MI355X: a small grid (the 26x26
+  // head, 96 blocks) is best at ~1000 work-groups, a mid-size one (the 52x52
+  // residual unit, 176 blocks) at ~350, where more splits cost more partial traffic
   auto direct_splits = [&](int64_t blocks, int nchunks) {
-    int64_t ks = ceil_div(512, blocks);
+    int64_t ks = ceil_div(blocks < 128 ? 1024 : 256, blocks);
     ks = std::min<int64_t>(ks, std::max<int64_t>(1, nchunks / 4));
     return (int)std::max<int64_t>(1, std::min<int64_t>(ks, 16));
   };
