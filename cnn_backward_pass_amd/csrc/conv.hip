@@ -1329,7 +1329,7 @@ static DwPlan plan_dw(const ConvGeom& g) {
     best.tiles_n = (int)ceil_div(g.J, 64);
     const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
     const int64_t ktiles = ceil_div(g.Q, 32);
-    int64_t splits = ceil_div(1024, tiles);
+    int64_t splits = ceil_div(512, tiles);  // measured best for the 1x1 layers
     splits = std::min<int64_t>(splits, std::max<int64_t>(1, ktiles / 4));
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, 4096));
     const int64_t chunk = ceil_div(ktiles, splits) * 32;
@@ -1385,7 +1385,7 @@ static FuPlan plan_fused(const ConvGeom& g) {
   FuPlan p{};
   const int64_t ntiles =
       (int64_t)g.N * ceil_div(g.H, kFuTH) * ceil_div(g.W, kFuTW);
-  const int64_t target = 1024;  // two rounds of two resident work-groups per CU
+  const int64_t target = 512;  // two resident work-groups per CU (measured best)
   p.tiles_per_wg = (int)std::max<int64_t>(1, ceil_div(ntiles, target));
   p.wgs = (int)ceil_div(ntiles, p.tiles_per_wg);
   p.groups = p.wgs > kReduceGroup ? (int)ceil_div(p.wgs, kReduceGroup) : 0;
