@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void conv1x1_dx_kernel(ConvGeom g, const 
 // tile-direct form (same sum as conv_dw_kernel, no im2col gather).
 //
 // A work-group owns a 64 (o) x 32 (i) block of dW for all nine taps and a run
-// of consecutive output rows of one image over a strip of TC output columns.
+// of consecutive output rows over a strip of TC output columns of one image.
 // The three input rows under the current output row stay in an LDS ring
 // (input row h in slot h mod 3), so each input row is fetched once per run:
 // per output row only the S new input rows and the dz row are loaded, into
@@ -362,22 +362,27 @@ __global__ __launch_bounds__(kThreads) void conv1x1_dx_kernel(ConvGeom g, const 
 // index runs over output positions, two per 32x32x2 step: lane l of a step
 // takes column 2s + l/32 of the row, dz[o = l%32] as the A operand and
 // x[i = l%32] under tap (kh, kw) as the B operand; the tap shifts are constant
-// LDS offsets.  Six waves: (o half) x (tap row kh), each holding the three
-// accumulators of its taps (kw = 0, 1, 2) over the whole row.  Each
-// work-group writes its partial dW block for the ordered split reduction (or
-// adds into dW when it is the only split).
+// LDS offsets.  Twelve waves -- (o half) x (tap row kh) x (half of the row's
+// steps) -- each hold the three accumulators of their taps; twelve waves put
+// the same number of waves on each of the CU's four SIMDs (a six-wave group
+// measured 15-20% slower).  The two step halves are summed through LDS at the
+// end; each work-group writes its partial dW block (tap-major, contiguous
+// stores) for the ordered split reduction, or adds into dW when it is the
+// only split.
 // ---------------------------------------------------------------------------
-constexpr int kDw3Threads = 384;
+constexpr int kDw3Threads = 768;
 
 template <int S, int TC>
 struct Dw3RowCfg {
   static constexpr int KS = TC / 2;            // 32x32x2 steps per output row
+  static constexpr int KH = (KS + 1) / 2;      // steps per half
   static constexpr int XC = S * (TC - 1) + 3;  // input columns under TC output columns
   static constexpr int CS = XC | 1;            // channel pitch inside a ring slot (odd)
   static constexpr int SLOT = 32 * CS;
   static constexpr int OS = TC + 1;            // dz row pitch per output channel (odd)
   static constexpr int Z0 = 3 * SLOT;          // dz row buffer after the three slots
-  static constexpr int LDS_FLOATS = Z0 + 64 * OS;
+  static constexpr int RED = 6 * 3 * 16 * 64;  // step-half exchange: 6 waves x 3 accumulators
+  static constexpr int LDS_FLOATS = (Z0 + 64 * OS) > RED ? (Z0 + 64 * OS) : RED;
   static constexpr int XNEW = S * 32 * XC;     // floats of the S input rows fetched per row
   static constexpr int XPT = (XNEW + kDw3Threads - 1) / kDw3Threads;
   static constexpr int ZNEW = 64 * TC;
@@ -386,14 +391,14 @@ struct Dw3RowCfg {
 };
 
 template <int S, int TC>
-__global__ __launch_bounds__(kDw3Threads, 2) void conv_dw3_rows(
+__global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
     ConvGeom g, const float* __restrict__ x, const float* __restrict__ dz, float* __restrict__ out,
     int strips, int rchunks, int rlen, int direct) {
   using Cf = Dw3RowCfg<S, TC>;
   constexpr int NT = kDw3Threads;
   __shared__ float lds[Cf::LDS_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int oh = wave & 1, kh = wave >> 1;
+  const int oh = wave & 1, kh = (wave >> 1) % 3, kq = wave / 6;
   const int cblocks = g.C >> 5, nblk = (g.OC >> 6) * cblocks;
   const int split = blockIdx.x / nblk, blk = blockIdx.x - split * nblk;
   const int ob = blk / cblocks, cb = blk - ob * cblocks;
@@ -474,20 +479,23 @@ __global__ __launch_bounds__(kDw3Threads, 2) void conv_dw3_rows(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 
-  const int abase = Cf::Z0 + (32 * oh + (lane & 31)) * Cf::OS + (lane >> 5);
-  const int bbase = (lane & 31) * Cf::CS + S * (lane >> 5);
+  // this wave's half of the row: steps [kq*KH, min(KS, kq*KH + KH))
+  const int abase = Cf::Z0 + (32 * oh + (lane & 31)) * Cf::OS + (lane >> 5) + 2 * Cf::KH * kq;
+  const int bbase = (lane & 31) * Cf::CS + S * (lane >> 5) + 2 * S * Cf::KH * kq;
   for (int r = r0; r < r1; ++r) {
     // input row S*r - 1 + kh sits in slot (S*r + kh + 2) mod 3
     const int bs = ((S * r + kh + 2) % 3) * Cf::SLOT + bbase;
 #pragma unroll
-    for (int sp = 0; sp < Cf::KS; ++sp) {
-      const float a = lds[abase + 2 * sp];
-      float b[3];
+    for (int sp = 0; sp < Cf::KH; ++sp) {
+      if (Cf::KS % 2 == 0 || kq == 0 || sp < Cf::KS / 2) {
+        const float a = lds[abase + 2 * sp];
+        float b[3];
 #pragma unroll
-      for (int kw = 0; kw < 3; ++kw) b[kw] = lds[bs + 2 * S * sp + kw];
+        for (int kw = 0; kw < 3; ++kw) b[kw] = lds[bs + 2 * S * sp + kw];
 #pragma unroll
-      for (int kw = 0; kw < 3; ++kw)
-        acc[kw] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[kw], acc[kw], 0, 0, 0);
+        for (int kw = 0; kw < 3; ++kw)
+          acc[kw] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[kw], acc[kw], 0, 0, 0);
+      }
     }
     __syncthreads();
     if (r + 1 < r1) {
@@ -496,6 +504,21 @@ __global__ __launch_bounds__(kDw3Threads, 2) void conv_dw3_rows(
       if (r + 2 < r1) fetch(r + 2);
     }
   }
+
+  // Sum the step halves: waves kq = 1 hand their accumulators over through LDS.
+  __syncthreads();
+  if (kq == 1) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lds[(((wave - 6) * 3 + t) * 16 + r) * 64 + lane] = acc[t][r];
+  }
+  __syncthreads();
+  if (kq == 1) return;
+#pragma unroll
+  for (int t = 0; t < 3; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] += lds[((wave * 3 + t) * 16 + r) * 64 + lane];
 
   // the only split adds into dW ([o][i][tap]); partials are tap-major [tap][o][i]
   // (contiguous stores), mapped back by the reduction
@@ -1284,7 +1307,7 @@ struct DwPlan {
 };
 
 // Row-streaming 3x3 dW: strip widths compiled in, and when to use it.
-static const int kDw3Tc[] = {64, 52, 32, 26};
+static const int kDw3Tc[] = {104, 64, 52, 32, 26};
 
 static bool plan_dw3_rows(const ConvGeom& g, DwPlan& p) {
   if (!(g.K == 3 && g.P == 1 && (g.S == 1 || g.S == 2) && g.C % 32 == 0 && g.OC % 64 == 0))
@@ -1304,8 +1327,8 @@ static bool plan_dw3_rows(const ConvGeom& g, DwPlan& p) {
   p.strips = (int)ceil_div(g.OW, best_tc);
   const int64_t nblk = (int64_t)(g.OC / 64) * (g.C / 32);
   const int64_t base = (int64_t)g.N * p.strips * nblk;
-  // about 512 work-groups (two resident per CU), at least 4 rows per run
-  int64_t rch = std::max<int64_t>(1, std::min<int64_t>(ceil_div(512, base), g.OH / 4));
+  // about 256 work-groups (one resident per CU), at least 4 rows per run
+  int64_t rch = std::max<int64_t>(1, std::min<int64_t>(ceil_div(256, base), g.OH / 4));
   p.rlen = (int)ceil_div(g.OH, rch);
   p.rchunks = (int)ceil_div(g.OH, p.rlen);
   p.splits = g.N * p.strips * p.rchunks;
@@ -1448,6 +1471,7 @@ static void launch_dw3_rows(const ConvGeom& g, const DwPlan& p, const float* x, 
                                                       p.rlen, direct);                        \
     break;
   switch (p.rows_tc) {
+    CBB_DW3(104)
     CBB_DW3(64)
     CBB_DW3(52)
     CBB_DW3(32)

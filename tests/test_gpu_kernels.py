@@ -53,6 +53,8 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (4, 32, 64, 52, 64, 3, 1, 1, True, "leaky"),     # dW row-streaming: many runs, two-level sum
     (1, 32, 1, 30, 64, 3, 1, 1, True, "leaky"),      # dW row-streaming: a single output row
     (2, 32, 2, 60, 64, 3, 2, 1, True, "leaky"),      # dW row-streaming: stride 2, one output row
+    (1, 32, 12, 416, 64, 3, 2, 1, True, "leaky"),    # dW row-streaming: 104-wide strips, stride 2
+    (1, 32, 5, 208, 64, 3, 1, 1, False, "linear"),   # dW row-streaming: 104-wide strips, stride 1
     (2, 64, 12, 12, 96, 1, 1, 0, True, "leaky"),     # 1x1 GEMMs with 16-byte staging, ragged o
     (3, 20, 6, 10, 70, 1, 1, 0, False, "linear"),    # 1x1 GEMMs: ragged i and o tiles
 ]
