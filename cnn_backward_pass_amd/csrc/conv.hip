@@ -1537,7 +1537,7 @@ static int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits,
 }
 
 // ----------------------------------------------------------------------------- dX planning
-enum DxKind { DX_SMALLC = 0, DX_32x128, DX_64x64, DX_D3S1, DX_D3S2, DX_1X1 };
+enum DxKind { DX_SMALLC = 0, DX_32x128, DX_64x64, DX_D3S1, DX_D3S2, DX_1X1, DX_D3S1_SMALL };
 
 struct DxPlan {
   int kind, bm, bn, bk, ctiles, pixtiles, ksplits;
@@ -1570,6 +1570,18 @@ static DxPlan plan_dx(const ConvGeom& g) {
     ks = std::min<int64_t>(ks, std::max<int64_t>(1, nchunks / 4));
     return (int)std::max<int64_t>(1, std::min<int64_t>(ks, 16));
   };
+  // stride 1: larger images (>= 1024 pixels per plane) measured faster with the
+  // small (128-pixel, 32-channel) tile, smaller ones with the 256-pixel, 64-channel tile
+  if (g.K == 3 && g.P == 1 && g.S == 1 && (int64_t)g.H * g.W >= 1024 &&
+      dx3_s1_fits(g.W, 1, Dx3Cfg<1, 1, 1>::ZPLANE) && g.C % Dx3Cfg<1, 1, 1>::BMC == 0 &&
+      g.OC % Dx3Cfg<1, 1, 1>::OCB == 0) {
+    using Cf = Dx3Cfg<1, 1, 1>;
+    p.kind = DX_D3S1_SMALL;
+    p.pixtiles = (int)ceil_div((int64_t)g.H * g.W, 128);
+    p.ctiles = g.C / Cf::BMC;
+    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB);
+    return p;
+  }
   if (g.K == 3 && g.P == 1 && g.S == 1 && dx3_s1_fits(g.W, 2, Dx3Cfg<1, 2, 2>::ZPLANE) &&
       g.C % Dx3Cfg<1, 2, 2>::BMC == 0 && g.OC % Dx3Cfg<1, 2, 2>::OCB == 0) {
     using Cf = Dx3Cfg<1, 2, 2>;
@@ -1641,10 +1653,13 @@ static void launch_dx_mfma(const ConvGeom& g, const DxPlan& p, const float* wt, 
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
                    float* ws, hipStream_t st) {
   const DxPlan p = plan_dx(g);
-  if (p.kind == DX_D3S1 || p.kind == DX_D3S2) {
+  if (p.kind == DX_D3S1 || p.kind == DX_D3S1_SMALL || p.kind == DX_D3S2) {
     const unsigned blocks = (unsigned)((int64_t)g.N * p.pixtiles * p.ctiles * p.ksplits);
     if (p.kind == DX_D3S1)
       conv_dx3_direct<1, 2, 2><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, accumulate,
+                                                            p.pixtiles, 0, p.ksplits);
+    else if (p.kind == DX_D3S1_SMALL)
+      conv_dx3_direct<1, 1, 1><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, accumulate,
                                                             p.pixtiles, 0, p.ksplits);
     else
       conv_dx3_direct<2, 1, 1><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, accumulate,

@@ -57,6 +57,7 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (1, 32, 5, 208, 64, 3, 1, 1, False, "linear"),   # dW row-streaming: 104-wide strips, stride 1
     (2, 64, 12, 12, 96, 1, 1, 0, True, "leaky"),     # 1x1 GEMMs with 16-byte staging, ragged o
     (3, 20, 6, 10, 70, 1, 1, 0, False, "linear"),    # 1x1 GEMMs: ragged i and o tiles
+    (2, 64, 40, 31, 24, 3, 1, 1, True, "leaky"),     # dX: 128-pixel tile-direct, ragged plane
 ]
 
 
