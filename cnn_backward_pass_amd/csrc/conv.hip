@@ -731,7 +731,17 @@ static bool dx3_s1_fits(int W, int F, int zplane) {
   return (rows + 2) * (W + 2) <= zplane;
 }
 
-template <int S, int F, int RM>
+// Source of the zero padding staged by the LDS-DMA loads (never written).
+__device__ float g_dx3_zero[4];
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(float* p) {
+  return (__attribute__((address_space(3))) void*)p;
+}
+
+// DMA = true stages each chunk with direct global-to-LDS loads into one of two
+// LDS buffers (the next chunk lands while the matrix cores work on this one;
+// needs 16-byte aligned weights); DMA = false stages through registers.
+template <int S, int F, int RM, bool DMA>
 __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const float* __restrict__ wt,
                                                             const float* __restrict__ dz,
                                                             float* __restrict__ dx,
@@ -739,9 +749,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
                                                             int accumulate, int tiles_per_img,
                                                             int tiles_w, int ksplits) {
   using C = Dx3Cfg<S, F, RM>;
-  __shared__ float Z[C::ZFLOATS];
-  __shared__ float Wl[C::WFLOATS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int ZBUF = (C::ZFLOATS + 63) / 64 * 64;   // whole 64-float DMA blocks
+  // two buffers as separate arrays, so that reads of one provably do not alias
+  // the copies in flight into the other
+  __shared__ float Z[ZBUF], Z1[DMA ? ZBUF : 1];
+  __shared__ float Wl[C::WFLOATS], Wl1[DMA ? C::WFLOATS : 1];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, khalf = lane >> 5;
   const int ctiles = (g.C + C::BMC - 1) / C::BMC;
   const int ctile = blockIdx.x % ctiles;
@@ -797,37 +811,68 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
     }
   }
 
-  // ---- staging: registers <- global (next chunk), LDS <- registers.  The host
-  // guarantees C % BMC == 0 and OC % OCB == 0, so only the image border masks.
-  // A staged element's offset inside a chunk does not depend on the chunk:
-  // computed once (-1 = zero padding).
+  // ---- staging of one chunk (OCB output channels): the dz tile and the weights
+  // [o][i][tap].  The host guarantees C % BMC == 0 and OC % OCB == 0, so only
+  // the image border masks.  A staged element's offset inside a chunk does not
+  // depend on the chunk: computed once (-1 = zero padding).  Element e of the
+  // tile is staged by thread e % 256 (wave-contiguous blocks of 64).
+  // Planes sit ZPLANE floats apart in LDS whatever the tile size (ZR*ZC <= ZPLANE),
+  // so channel and tap offsets of the operand reads are compile-time immediates;
+  // the rest of a plane is staged as zeros.
+  const int ZP = S == 1 ? ZR * ZC : C::ZPLANE;
   const float* dzb = dz + (int64_t)b * g.OC * g.OHW;
-  float rz[C::ZPT], rw[C::WPT];
-  const int zcount = C::OCB * ZR * ZC;
+  const int zcount = C::OCB * ZP;
   int zofs[C::ZPT];
 #pragma unroll
   for (int r = 0; r < C::ZPT; ++r) {
     const int e = tid + kThreads * r;
-    const int o = e / (ZR * ZC), rem = e - o * (ZR * ZC);
+    const int o = e / ZP, rem = e - o * ZP;
     const int zr = rem / ZC, zc = rem - zr * ZC;
     const int ho = zr0 + zr, wo = zc0 + zc;
-    const bool ok = e < zcount && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
+    const bool ok = e < zcount && zr < ZR && (unsigned)ho < (unsigned)g.OH &&
+                    (unsigned)wo < (unsigned)g.OW;
     zofs[r] = ok ? o * g.OHW + ho * g.OW + wo : -1;
   }
-  // The loaded values are consumed only by the LDS store of the next chunk
-  // (the zero padding is applied there), so the loads stay in flight during
+  float rz[DMA ? 1 : C::ZPT], rw[DMA ? 1 : C::WPT];
+  // DMA: each wave copies its 64-float blocks of the tile (padding read from the
+  // zero page) and its 256-float blocks of the weights straight into LDS buffer `buf`.
+  auto issue = [&](int o0, float* zl, float* wl) {
+    const float* zb = dzb + (int64_t)o0 * g.OHW;
+#pragma unroll
+    for (int r = 0; r < C::ZPT; ++r) {
+      const int q = wave + 4 * r;
+      int zo = zofs[r];
+      asm volatile("" : "+v"(zo));   // keeps the 64-bit addresses from being hoisted
+      if (64 * q < zcount)
+        __builtin_amdgcn_global_load_lds(zo >= 0 ? zb + zo : g_dx3_zero, lds_ptr(zl + 64 * q),
+                                         4, 0, 0);
+    }
+    const float* wb = wt + ((int64_t)o0 * g.C + i0) * 9;
+    constexpr int WQ = C::WFLOATS / 256;
+#pragma unroll
+    for (int r = 0; r < (WQ + 3) / 4; ++r) {
+      const int q = wave + 4 * r;
+      if (q < WQ) {
+        const int e = 4 * (64 * q + lane);
+        const int o = e / (C::BMC * 9), rem = e - o * (C::BMC * 9);
+        __builtin_amdgcn_global_load_lds(wb + o * g.C * 9 + rem, lds_ptr(wl + 256 * q), 16, 0, 0);
+      }
+    }
+  };
+  // registers: the loaded values are consumed only by the LDS store of the next
+  // chunk (the zero padding is applied there), so the loads stay in flight during
   // the matrix-core work.
   auto load = [&](int o0) {
     const float* zb = dzb + (int64_t)o0 * g.OHW;
 #pragma unroll
-    for (int r = 0; r < C::ZPT; ++r) rz[r] = zb[(unsigned)max(zofs[r], 0)];
+    for (int r = 0; r < C::ZPT; ++r) rz[DMA ? 0 : r] = zb[(unsigned)max(zofs[r], 0)];
     const float* wb = wt + ((int64_t)o0 * g.C + i0) * 9;
 #pragma unroll
     for (int r = 0; r < C::WPT; ++r) {
       const int e = tid + kThreads * r;                // (o, i, tap), tap fastest
       const int o = e / (C::BMC * 9), rem = e - o * (C::BMC * 9);
       const bool ok = e < C::OCB * C::BMC * 9;
-      rw[r] = wb[(unsigned)(ok ? o * g.C * 9 + rem : 0)];
+      rw[DMA ? 0 : r] = wb[(unsigned)(ok ? o * g.C * 9 + rem : 0)];
     }
   };
   // LDS keeps the staging order: Z planes of ZR*ZC floats, weights as [o][i][tap]
@@ -836,16 +881,14 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
 #pragma unroll
     for (int r = 0; r < C::ZPT; ++r) {
       const int e = tid + kThreads * r;
-      if (e < zcount) Z[e] = zofs[r] >= 0 ? rz[r] : 0.f;
+      if (e < zcount) Z[e] = zofs[r] >= 0 ? rz[DMA ? 0 : r] : 0.f;
     }
 #pragma unroll
     for (int r = 0; r < C::WPT; ++r) {
       const int e = tid + kThreads * r;
-      if (e < C::OCB * C::BMC * 9) Wl[e] = rw[r];
+      if (e < C::OCB * C::BMC * 9) Wl[e] = rw[DMA ? 0 : r];
     }
   };
-  const int zplane = ZR * ZC;
-
   f32x16 acc[C::NFRAG][RM];
 #pragma unroll
   for (int f = 0; f < C::NFRAG; ++f)
@@ -854,52 +897,98 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[f][m][r] = 0.f;
 
+  // All taps of one chunk from LDS buffer (zl, wl).  The operands of tap t + 1
+  // are read into the other register set while the matrix cores work on tap t.
+  // Stride 2: a tap feeds only the fragments of the phases it reaches.
+  auto tap_hits = [&](int f, int kh, int kw) {
+    return S == 1 || (((ph_[f] + 1 - kh) & 1) == 0 && ((pw_[f] + 1 - kw) & 1) == 0);
+  };
+  auto compute = [&](const float* zl, const float* wl) {
+    constexpr int KK = C::OCB / 2;
+    float av[2][KK][RM], bv[2][KK][C::NFRAG];
+    auto fetch = [&](int tap, int sl) {
+      const int kh = tap / 3, kw = tap - 3 * kh;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int o = 2 * kk + khalf;
+#pragma unroll
+        for (int m = 0; m < RM; ++m) av[sl][kk][m] = wl[(o * C::BMC + m * 32 + col) * 9 + tap];
+#pragma unroll
+        for (int f = 0; f < C::NFRAG; ++f) {
+          if (!tap_hits(f, kh, kw)) continue;
+          int off;
+          if constexpr (S == 1)
+            off = (2 - kh) * ZC + (2 - kw);
+          else
+            off = ((ph_[f] + 1 - kh) >> 1) * C::ZC2 + ((pw_[f] + 1 - kw) >> 1);
+          bv[sl][kk][f] = zl[o * ZP + pbase[f] + off];
+        }
+      }
+    };
+    // per tap: fragments hit, operand reads of the next tap, matrix instructions
+    constexpr int HITS = S == 1 ? C::NFRAG : C::NFRAG / 4;
+    constexpr int NRD = KK * (RM + HITS), NMF = KK * HITS * RM;
+    fetch(0, 0);
+#pragma unroll
+    for (int tap = 0; tap < 9; ++tap) {
+      const int kh = tap / 3, kw = tap - 3 * kh, sl = tap & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (tap < 8) fetch(tap + 1, sl ^ 1);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int f = 0; f < C::NFRAG; ++f) {
+          if (!tap_hits(f, kh, kw)) continue;
+#pragma unroll
+          for (int m = 0; m < RM; ++m)
+            acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[sl][kk][m], bv[sl][kk][f],
+                                                             acc[f][m], 0, 0, 0);
+        }
+      // issue all reads of the next tap first, then this tap's matrix work
+      if (tap < 8) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   // this split's output-channel chunks [c0, c1)
   const int nch = (g.OC + C::OCB - 1) / C::OCB;
   const int cps = (nch + ksplits - 1) / ksplits;
   const int c0 = min(nch, split * cps), c1 = min(nch, c0 + cps);
-  if (c0 < c1) {
-    load(c0 * C::OCB);
-    store();
-  }
-  __syncthreads();
-  for (int c = c0; c < c1; ++c) {
-    if (c + 1 < c1) load((c + 1) * C::OCB);   // in flight during the matrix-core work
-#pragma unroll
-    for (int kh = 0; kh < 3; ++kh)
-#pragma unroll
-      for (int kw = 0; kw < 3; ++kw) {
-        const int tap = kh * 3 + kw;
-        __builtin_amdgcn_sched_barrier(0);  // one tap at a time: bounds the live ranges
-#pragma unroll
-        for (int kk = 0; kk < C::OCB / 2; ++kk) {
-          const int o = 2 * kk + khalf;
-          float a[RM];
-#pragma unroll
-          for (int m = 0; m < RM; ++m) a[m] = Wl[(o * C::BMC + m * 32 + col) * 9 + tap];
-#pragma unroll
-          for (int f = 0; f < C::NFRAG; ++f) {
-            int off;
-            if constexpr (S == 1) {
-              off = (2 - kh) * ZC + (2 - kw);
-            } else {
-              // taps of another phase contribute nothing to this fragment
-              if (((ph_[f] + 1 - kh) & 1) || ((pw_[f] + 1 - kw) & 1)) continue;
-              off = ((ph_[f] + 1 - kh) >> 1) * C::ZC2 + ((pw_[f] + 1 - kw) >> 1);
-            }
-            const float bv = Z[o * zplane + pbase[f] + off];
-#pragma unroll
-            for (int m = 0; m < RM; ++m)
-              acc[f][m] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m], bv, acc[f][m], 0, 0, 0);
-          }
-        }
-      }
-    __syncthreads();
-    if (c + 1 < c1) {
-      store();
+  if constexpr (DMA) {
+    // chunks alternate between the buffers (Z, Wl) and (Z1, Wl1).  Before each
+    // chunk: this wave's copies of it have landed; after the barrier everyone's
+    // have, and every wave is done with the previous chunk, whose buffer is
+    // refilled next.
+    if (c0 < c1) issue(c0 * C::OCB, Z, Wl);
+    for (int c = c0; c < c1; c += 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      if (c + 1 < c1) issue((c + 1) * C::OCB, Z1, Wl1);
+      compute(Z, Wl);
+      if (c + 1 >= c1) break;
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (c + 2 < c1) issue((c + 2) * C::OCB, Z, Wl);
+      compute(Z1, Wl1);
+    }
+  } else {
+    if (c0 < c1) {
+      load(c0 * C::OCB);
+      store();
+    }
+    __syncthreads();
+    for (int c = c0; c < c1; ++c) {
+      if (c + 1 < c1) load((c + 1) * C::OCB);   // in flight during the matrix-core work
+      compute(Z, Wl);
+      __syncthreads();
+      if (c + 1 < c1) {
+        store();
+        __syncthreads();
+      }
     }
   }
+
 
   // ---- epilogue: lane holds pixel `col` of each fragment, channels acc_row(r)
   // with several splits each writes its partial at the pixel's dx position in ws[split]
@@ -1655,16 +1744,22 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
   const DxPlan p = plan_dx(g);
   if (p.kind == DX_D3S1 || p.kind == DX_D3S1_SMALL || p.kind == DX_D3S2) {
     const unsigned blocks = (unsigned)((int64_t)g.N * p.pixtiles * p.ctiles * p.ksplits);
-    if (p.kind == DX_D3S1)
-      conv_dx3_direct<1, 2, 2><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, accumulate,
-                                                            p.pixtiles, 0, p.ksplits);
-    else if (p.kind == DX_D3S1_SMALL)
-      conv_dx3_direct<1, 1, 1><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, accumulate,
-                                                            p.pixtiles, 0, p.ksplits);
-    else
-      conv_dx3_direct<2, 1, 1><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, accumulate,
-                                                            p.pixtiles, (int)ceil_div(g.W, 64),
-                                                            p.ksplits);
+    const int tiles_w = p.kind == DX_D3S2 ? (int)ceil_div(g.W, 64) : 0;
+#define CBB_DX3(S_, F_, RM_)                                                              \
+  if (aligned16(wt))                                                                      \
+    conv_dx3_direct<S_, F_, RM_, true><<<blocks, kThreads, 0, st>>>(                      \
+        g, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);                   \
+  else                                                                                    \
+    conv_dx3_direct<S_, F_, RM_, false><<<blocks, kThreads, 0, st>>>(                     \
+        g, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);
+    if (p.kind == DX_D3S1) {
+      CBB_DX3(1, 2, 2)
+    } else if (p.kind == DX_D3S1_SMALL) {
+      CBB_DX3(1, 1, 1)
+    } else {
+      CBB_DX3(2, 1, 1)
+    }
+#undef CBB_DX3
     int rc = check_launch("conv_dx3_direct");
     if (rc || p.ksplits == 1) return rc;
     const int64_t n = (int64_t)g.N * g.C * g.HW;

@@ -200,10 +200,13 @@ def test_conv_backward_weights_data(case):
     assert_close("dw (no dx)", dw.cpu().double().numpy(), ref_dw)
 
 
-@pytest.mark.parametrize("case", [(2, 64, 12, 12, 96, 1, 1, 0), (1, 3, 9, 12, 8, 3, 1, 1)])
+@pytest.mark.parametrize("case", [(2, 64, 12, 12, 96, 1, 1, 0), (1, 3, 9, 12, 8, 3, 1, 1),
+                                  (1, 64, 9, 20, 16, 3, 1, 1), (1, 32, 40, 30, 16, 3, 1, 1),
+                                  (2, 32, 12, 70, 32, 3, 2, 1)])
 def test_misaligned_tensors_take_the_general_kernels(case):
     """Tensors that are not 16-byte aligned (a view one float into a buffer) go through
-    the general kernels (same tiles, same workspace) and give the same gradients."""
+    the general kernels, or the 3x3 input-gradient kernels staged through registers
+    (same tiles, same workspace), and give the same gradients."""
     torch = require_gpu()
     from cnn_backward_pass_amd import cbb
     n, c, h, w, oc, k, s, p = case
@@ -294,6 +297,35 @@ def test_bn_backward_entry_point(shape):
         assert np.all(np.abs(s) <= 1e-5 * scale + 1e-30)
     else:  # the degenerate two-sample case: bounded by the size of the cancelling terms
         assert np.all(np.abs(s) <= 1e-5 * terms)
+
+
+@pytest.mark.parametrize("shape", [(16, 32, 104, 104), (2, 300, 16, 16), (1, 7, 1, 4)])
+def test_bn_backward_in_place_accumulating(shape):
+    """dz written over g, dgamma / dbeta added to non-zero values, workspace holding
+    garbage on entry: a large plane, many short channels, one tiny plane."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    announce(f"bn_backward in place {shape}")
+    r = np.random.default_rng(12)
+    n, c = shape[:2]
+    z = r.normal(size=shape) * 0.7 - 0.3
+    gamma = 1 + 0.2 * r.normal(size=c)
+    _, var, xhat, _ = O.bn_forward(z, gamma, np.zeros(c), 1e-5)
+    g = r.normal(size=shape).astype(np.float32)
+    xhat32, var32, gamma32 = (a.astype(np.float32) for a in (xhat, var, gamma))
+    dz_ref, dg_ref, dbeta_ref = O.bn_backward(g, xhat32, var32, gamma32, 1e-5)
+    hw = int(np.prod(shape[2:]))
+    ws = cbb.workspace(cbb.bn_backward_workspace_size(n, c, hw))
+    ws.fill_(0xAB)
+    dg = torch.full((c,), 0.5, device="cuda")
+    dbeta = torch.full((c,), -0.25, device="cuda")
+    gt = _t(torch, g)
+    cbb.bn_backward(gt, _t(torch, xhat32), _t(torch, var32), _t(torch, gamma32), gt, dg, dbeta,
+                    1e-5, ws)   # dz written over g
+    torch.cuda.synchronize()
+    assert_close("dz", gt.cpu().double().numpy(), dz_ref)
+    assert_close("dgamma", dg.cpu().double().numpy(), dg_ref + 0.5)
+    assert_close("dbeta", dbeta.cpu().double().numpy(), dbeta_ref - 0.25)
 
 
 @pytest.mark.parametrize("act", ["linear", "leaky", "logistic", "relu"])
