@@ -994,6 +994,56 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   // with several splits each writes its partial at the pixel's dx position in ws[split]
   float* out = ksplits == 1 ? dx : ws + (int64_t)split * g.N * g.C * g.HW;
   const bool add = ksplits == 1 && accumulate;
+  if constexpr (S == 2 && DMA) {
+    // Stride 2: a fragment's pixels are two columns apart, so the region is first
+    // put back in row order in LDS, 8 channels at a time ([8][8F][64] floats in
+    // the weight buffer), and written as whole 16-byte row pieces.
+    constexpr int RR = 8 * F, TP = 64, CH = 8;
+    static_assert(CH * RR * TP <= C::WFLOATS, "epilogue tile exceeds the weight buffer");
+    constexpr int NV = CH * RR * TP / 4 / kThreads;   // float4 per thread per pass
+    const int th = tt / tiles_w, tw = tt - th * tiles_w;
+    const int h0 = th * 8 * F, w0 = tw * 64;
+    const bool vec = (g.W % 4) == 0 && ((uintptr_t)out % 16) == 0;
+#pragma unroll
+    for (int m = 0; m < RM; ++m)
+#pragma unroll
+      for (int pass = 0; pass < 4; ++pass) {
+        __syncthreads();   // the buffer is free (matrix work or previous pass done)
+#pragma unroll
+        for (int f = 0; f < C::NFRAG; ++f) {
+          const int rr = 2 * (wave * F + f / 4) + ph_[f], cc = 2 * col + pw_[f];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            Wl[((4 * khalf + j) * RR + rr) * TP + cc] = acc[f][m][4 * pass + j];
+        }
+        __syncthreads();
+        const int ib = i0 + m * 32 + 8 * pass;   // channels ib .. ib+7 (acc_row of pass)
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          const int u = tid + kThreads * k;
+          const int il = u / (RR * TP / 4), rem = u - il * (RR * TP / 4);
+          const int rr = rem / (TP / 4), c4 = rem - rr * (TP / 4);
+          const int h = h0 + rr, w = w0 + 4 * c4;
+          if (h >= g.H || w >= g.W) continue;
+          const float4 v = *reinterpret_cast<const float4*>(&Wl[(il * RR + rr) * TP + 4 * c4]);
+          float* q = out + (((int64_t)b * g.C + ib + il) * g.H + h) * g.W + w;
+          if (vec && w + 3 < g.W) {
+            float4 o = v;
+            if (add) {
+              const float4 a = *reinterpret_cast<const float4*>(q);
+              o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
+            }
+            *reinterpret_cast<float4*>(q) = o;
+          } else {
+            const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (w + e < g.W) q[e] = add ? q[e] + vv[e] : vv[e];
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int f = 0; f < C::NFRAG; ++f) {
     if (!pval[f]) continue;
