@@ -1182,230 +1182,254 @@ __global__ __launch_bounds__(kThreads) void conv_dx_smallc_kernel(ConvGeom g,
 // ---------------------------------------------------------------------------
 // Weight and input gradients of a 3x3, pad-1, stride-1 convolution with at
 // most 3 input and at most 32 output channels (a network's first layer on an
-// RGB image) in one pass over dz.  Both gradients read the same dz and the
-// layer is HBM-bound, so fusing them halves its traffic.
+// RGB image) in one streaming pass over dz: both gradients read the same dz
+// and the layer is HBM-bound, so fusing them halves its traffic.  Every dz, x
+// and dx element crosses HBM once (plus two halo dz rows per run of rows).
 //
-// Persistent work-groups of 8 waves walk a contiguous run of 8 x 32 pixel
-// tiles.  Per tile, dz for all output channels and x for all input channels
-// are staged in LDS over the tile plus its halo, as 16-byte loads of 10 rows x
-// 40 columns (columns w0-4 .. w0+35; the image width is a multiple of 4, so
-// every 16-byte group is wholly inside or outside the image); the next tile's
-// loads are in registers while this one is computed.
+// A work-group owns (image, strip of SWo <= 120 output columns starting at w0,
+// run of rows r0 .. r1-1) and walks the dz rows h = r0-1 .. r1 inside the image.
+// LDS column k holds image column w0 - 4 + k (16-byte load groups; the image
+// width is a multiple of 4).  Per dz row:
 //   dW: matrix cores, M = o (32), N = (i, kh, kw) (9*CI <= 27 of 32 columns),
-//       K = the tile's 256 pixels, two per 32x32x2 step; wave w takes tile row
-//       w and keeps its 32x32 accumulator across tiles.
-//   dX: vector ALUs.  Waves are (output-channel quarter) x (tile half): each
-//       sums 8 output channels for 128 pixels, two pixels of one column per
-//       lane (neighbouring lanes take neighbouring columns, so the LDS reads
-//       are conflict-free), with wave-uniform weight reads; the four quarters'
-//       partial sums meet in LDS and are added in a fixed order.
-// At the end the waves' dW blocks are summed through LDS in a fixed order and
-// each work-group writes its partial for the ordered split reduction.
+//       K = the strip's pixels of row h, two per 32x32x2 step; wave w takes the
+//       32 pixels w0 - 1 + 32w ..; pixels outside the strip are masked.  Only the
+//       rows r0 .. r1-1 count, so each dz row is counted by exactly one run.
+//   dX: matrix cores form P[(i,kh,kw)][p] = sum_o W[o][i][kh][kw] dz[o][h][p] for
+//       the 128 pixels p = w0 - 1 .. w0 + 126 (M = (i,kh,kw), N = 32 pixels per
+//       wave, K = o).  dz[o][h][p] reaches dx[i][h+kh-1][p+kw-1], so after P
+//       goes through LDS, strip column c takes, in a fixed order,
+//       P[(i,kh,0)][c+1] + P[(i,kh,1)][c] + P[(i,kh,2)][c-1] into dx row
+//       h + kh - 1; each dx row stays in registers until its third dz row.
+// dz row h+1 and x row h+2 are loaded into registers during row h and stored
+// to LDS after its matrix work; x rows live in a ring of four (slot = row & 3).
 // ---------------------------------------------------------------------------
-constexpr int kFuThreads = 512;
-constexpr int kFuTH = 8, kFuTW = 32;
-constexpr int kFuRW = 40, kFuRH = kFuTH + 2;       // staged region: 10 x 40
-constexpr int kFuZP = kFuRH * kFuRW + 4;           // LDS pitch per channel (16-byte aligned)
-constexpr int kFuNV = kFuRH * (kFuRW / 4);         // 16-byte groups per channel
-constexpr int kFuZV = (32 * kFuNV + kFuThreads - 1) / kFuThreads;  // dz groups per thread
-constexpr int kFuXV = (3 * kFuNV + kFuThreads - 1) / kFuThreads;   // x groups per thread
+// odd row pitch: the dW operand reads one column across 32 channel rows
+constexpr int kFrThreads = 256, kFrPitch = 133, kFrMaxW = 120;
 
-template <int CI>
-__global__ __launch_bounds__(kFuThreads, 2) void conv_smallc_dwdx(
+template <int CI, bool ACC>
+__global__ __launch_bounds__(kFrThreads, 3) void conv_first_rows(
     ConvGeom g, const float* __restrict__ x, const float* __restrict__ wt,
     const float* __restrict__ dz, float* __restrict__ dwpart, float* __restrict__ dx,
-    int tiles_per_wg, int accumulate) {
+    int nstrips, int sw, int nruns, int rlen) {
   static_assert(CI >= 1 && CI <= 3, "9*CI columns must fit one 32-wide block");
-  constexpr int NT = kFuThreads;
   typedef float f4 __attribute__((ext_vector_type(4)));
-  __shared__ __attribute__((aligned(16))) float Zs[32 * kFuZP];
-  __shared__ __attribute__((aligned(16))) float Xs[CI * kFuZP];
-  __shared__ float Pd[4 * CI * kFuTH * kFuTW];   // per-quarter partial dx
+  constexpr int P = kFrPitch;
+  __shared__ float Zs[32 * P];
+  __shared__ float Xs[4 * CI * P];
+  __shared__ float Ps[32 * P];
+  __shared__ float Z0[64];   // zeros: masked operands read here (no branches around reads)
   const int tid = threadIdx.x, lane = tid & 63;
-  // wave-uniform by construction; readfirstlane lets the compiler know, so the
-  // weight reads below are scalar loads (a vector load would also wait, in order,
-  // for the next tile's prefetched loads)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tiles_h = (g.H + kFuTH - 1) / kFuTH, tiles_w = (g.W + kFuTW - 1) / kFuTW;
-  const int ntiles = g.N * tiles_h * tiles_w;
-  const int t0 = blockIdx.x * tiles_per_wg, t1 = min(ntiles, t0 + tiles_per_wg);
-  const int zcount = g.OC * kFuNV, xcount = CI * kFuNV;
+  const int run = blockIdx.x % nruns, strip = (blockIdx.x / nruns) % nstrips;
+  const int n = blockIdx.x / (nruns * nstrips);
+  const int w0 = strip * sw, r0 = run * rlen, r1 = min(g.H, r0 + rlen);
+  // dz rows hA .. hE are walked (row H, past the image, reads as zeros and
+  // completes dx row H-1); the count is rounded up to even, and the extra row
+  // changes nothing (its dx row is outside the run)
+  const int hA = max(r0 - 1, 0), hE = min(r1, g.H);
+  const float* zb = dz + (int64_t)n * g.OC * g.HW;
+  const float* xb = x + (int64_t)n * CI * g.HW;
 
-  // output channels >= OC stay zero in LDS for the whole kernel
-  for (int e = tid; e < 32 * kFuZP; e += NT) Zs[e] = 0.f;
+  // channels >= OC are never staged and stay zero
+  for (int e = tid; e < 32 * P; e += kFrThreads) Zs[e] = 0.f;
+  if (tid < 64) Z0[tid] = 0.f;
 
-  static_assert(kFuZV <= 32 && kFuXV <= 32, "one mask bit per staged group");
-  f4 pz[kFuZV], px[kFuXV];
-  uint32_t zmask = 0, xmask = 0;
-  auto tile_origin = [&](int t, int& n, int& h0, int& w0) {
-    const int tw = t % tiles_w, r = t / tiles_w;
-    const int th = r % tiles_h;
-    n = r / tiles_h;
-    h0 = th * kFuTH;
-    w0 = tw * kFuTW;
+  // ---- staging: thread slot k takes 16-byte group e = tid + 256k of a row
+  // (dz: channel e / 32, group e % 32; x: the same with CI channels).  Groups
+  // off the image are zero, applied at the LDS store.  Two register sets: the
+  // rows loaded at the end of row h are stored to LDS during row h + 2.
+  struct Stage {
+    f4 pz[4], px;
+    uint32_t zmask;
+    bool xok;
   };
-  // Loads go to registers as they are (groups off the image read a clamped
-  // valid address); the zero padding is applied at the LDS store.  The index
-  // math is redone at every tile on purpose (the thread index goes through an
-  // empty asm): hoisted out of the tile loop it would keep too many offsets live.
-  auto fetch = [&](int t) {
-    int n, h0, w0;
-    tile_origin(t, n, h0, w0);
-    const float* zb = dz + (int64_t)n * g.OC * g.HW;
-    const float* xb = x + (int64_t)n * CI * g.HW;
-    int tt = tid;
-    asm volatile("" : "+v"(tt));
-    zmask = 0;
-    xmask = 0;
+  auto load_dz = [&](Stage& q, int h) {
+    q.zmask = 0;
 #pragma unroll
-    for (int i = 0; i < kFuZV; ++i) {
-      const int e = tt + i * NT;
-      const int o = e / kFuNV, q = e - o * kFuNV;
-      const int rr = q / (kFuRW / 4), v = q - rr * (kFuRW / 4);
-      const int h = h0 - 1 + rr, w = w0 - 4 + 4 * v;
-      const bool ok = e < zcount && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
-      pz[i] = *(const f4*)(zb + (ok ? o * g.HW + h * g.W + w : 0));
-      zmask |= (uint32_t)ok << i;
-    }
-#pragma unroll
-    for (int i = 0; i < kFuXV; ++i) {
-      const int e = tt + i * NT;
-      const int c = e / kFuNV, q = e - c * kFuNV;
-      const int rr = q / (kFuRW / 4), v = q - rr * (kFuRW / 4);
-      const int h = h0 - 1 + rr, w = w0 - 4 + 4 * v;
-      const bool ok = e < xcount && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
-      px[i] = *(const f4*)(xb + (ok ? c * g.HW + h * g.W + w : 0));
-      xmask |= (uint32_t)ok << i;
+    for (int k = 0; k < 4; ++k) {
+      const int e = tid + kFrThreads * k, o = e >> 5, v = e & 31;
+      const int w = w0 - 4 + 4 * v;
+      const bool ok = o < g.OC && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+      q.pz[k] = *(const f4*)(zb + (ok ? (o * g.H + h) * g.W + w : 0));
+      q.zmask |= (uint32_t)ok << k;
     }
   };
-  auto commit = [&]() {
-    int tt = tid;
-    asm volatile("" : "+v"(tt));
+  auto store_dz = [&](const Stage& q) {
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kFuZV; ++i) {
-      const int e = tt + i * NT;
-      const int o = e / kFuNV, q = e - o * kFuNV;
-      if (e < zcount) *(f4*)(Zs + o * kFuZP + 4 * q) = ((zmask >> i) & 1u) ? pz[i] : zero;
+    for (int k = 0; k < 4; ++k) {
+      const int e = tid + kFrThreads * k, o = e >> 5, v = e & 31;
+      if (o < g.OC) {
+        const f4 val = ((q.zmask >> k) & 1u) ? q.pz[k] : zero;
+        float* d = Zs + o * P + 4 * v;
+        d[0] = val.x;
+        d[1] = val.y;
+        d[2] = val.z;
+        d[3] = val.w;
+      }
     }
-#pragma unroll
-    for (int i = 0; i < kFuXV; ++i) {
-      const int e = tt + i * NT;
-      const int c = e / kFuNV, q = e - c * kFuNV;
-      if (e < xcount) *(f4*)(Xs + c * kFuZP + 4 * q) = ((xmask >> i) & 1u) ? px[i] : zero;
+  };
+  auto load_x = [&](Stage& q, int h) {
+    const int c = tid >> 5, v = tid & 31, w = w0 - 4 + 4 * v;
+    q.xok = tid < CI * 32 && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+    q.px = *(const f4*)(xb + (q.xok ? (c * g.H + h) * g.W + w : 0));
+  };
+  auto store_x = [&](const Stage& q, int h) {
+    const int c = tid >> 5, v = tid & 31;
+    const f4 zero = {0.f, 0.f, 0.f, 0.f};
+    if (tid < CI * 32) {
+      const f4 val = q.xok ? q.px : zero;
+      float* d = Xs + ((h & 3) * CI + c) * P + 4 * v;
+      d[0] = val.x;
+      d[1] = val.y;
+      d[2] = val.z;
+      d[3] = val.w;
     }
   };
 
-  // dW operands: lane column j = (i, kh, kw); pixel (r, cc) of the tile has dz
-  // at region (r+1, cc+4) and x under tap (kh, kw) at region (r+kh, cc+kw+3).
-  const int j = lane & 31, kq = lane >> 5;
+  // ---- matrix-core operands.  Lane: kq = lane / 32, j = lane % 32.
+  const int kq = lane >> 5, j = lane & 31;
   const bool jv = j < 9 * CI;
-  int boff;
-  {
-    const int i = j / 9, tap = j - 9 * i, kh = tap / 3, kw = tap - 3 * kh;
-    boff = jv ? i * kFuZP + kh * kFuRW + kw + 3 : 0;
+  // P: A = W^T, constant: wa[k] = W[o = 2k + kq][j]
+  float wa[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int o = 2 * k + kq;
+    wa[k] = (jv && o < g.OC) ? wt[o * 9 * CI + j] : 0.f;
   }
-  const int aoff = (lane & 31) * kFuZP + kFuRW + 4;
-  f32x16 acc;
+  // dW: B column j = (i, kh, kw) reads x row h + kh - 1 at column p + kw - 1
+  int xi = 0, xkh = 0, xkw = 0;
+  if (jv) {
+    xi = j / 9;
+    const int tap = j - 9 * xi;
+    xkh = tap / 3;
+    xkw = tap - 3 * xkh;
+  }
+  f32x16 adw;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int r = 0; r < 16; ++r) adw[r] = 0.f;
+  // dx rows h-1 and h of strip column w0 + tid (threads tid < sw)
+  float dprev[CI], dcur[CI];
+#pragma unroll
+  for (int i = 0; i < CI; ++i) dprev[i] = dcur[i] = 0.f;
+  const int col = w0 + tid;
+  const bool cown = tid < sw && col < g.W;
+  const int pb = 3 + 32 * wave;   // LDS column of this wave's first pixel w0 - 1 + 32 * wave
 
-  // dX: wave -> output channels [8*oq, 8*oq+8) and tile rows [4*half, 4*half+4);
-  // lane -> column pc, rows 4*half + 2*pp + {0, 1}
-  const int oq = wave & 3, half = wave >> 2;
-  const int pc = lane & 31, pp = lane >> 5;
-  const int prow = 4 * half + 2 * pp;  // first of the lane's two tile rows
-
-  if (t0 < t1) fetch(t0);
-  __syncthreads();  // the zero fill is complete before any staging
-  for (int t = t0; t < t1; ++t) {
-    commit();
-    __syncthreads();
-    if (t + 1 < t1) fetch(t + 1);  // in flight during this tile's work
-
-    // dW: wave w takes tile row w (32 pixels); step s takes pixels 2s + kq
+  // One dz row.  `q` holds dz row h+1 and x row h+2 on entry; refilled with
+  // dz row h+3 and x row h+4 on exit.
+  auto row = [&](int h, Stage& q) {
+    // dW over this wave's 32 pixels of row h (rows of the run only)
+    if (h >= r0 && h < r1) {
+      // masked operands (pixels outside the strip, columns j >= 9*CI) read zeros:
+      // the address is selected, so every read is unconditional
+      const float* xr =
+          jv ? Xs + (((h + xkh - 1) & 3) * CI + xi) * P + pb + xkw - 1 + kq : Z0;
+      const float* zr = Zs + j * P + pb + kq;
+      float av[16], bv[16];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      if (s % 8 == 0) __builtin_amdgcn_sched_barrier(0);  // bounds the operand prefetch
-      const int po = wave * kFuRW + 2 * s + kq;
-      const float a = Zs[aoff + po];
-      const float bx = Xs[boff + po];
-      const float b = jv ? bx : 0.f;
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
-    }
-
-    if (dx) {
-      // pixel (r, pc) needs dz at region (r+2-kh, pc+5-kw): rows prow .. prow+3,
-      // columns pc+3 .. pc+5.  All eight channels unrolled; channels >= OC read
-      // zero rows of Zs, with their weight reads clamped to a valid channel.
-      float d[CI][2][3];  // (input channel, pixel, kernel row): independent chains
-#pragma unroll
-      for (int i = 0; i < CI; ++i)
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int kh = 0; kh < 3; ++kh) d[i][u][kh] = 0.f;
-      const float* zp = Zs + prow * kFuRW + pc + 3;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int o = 8 * oq + k;
-        float z[4][3];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int v = 0; v < 3; ++v) z[u][v] = zp[o * kFuZP + u * kFuRW + v];
-        const float* wo = wt + (int64_t)min(o, g.OC - 1) * CI * 9;
-#pragma unroll
-        for (int kh = 0; kh < 3; ++kh)
-#pragma unroll
-          for (int kw = 0; kw < 3; ++kw)
-#pragma unroll
-            for (int i = 0; i < CI; ++i) {
-              const float wv = wo[i * 9 + kh * 3 + kw];
-#pragma unroll
-              for (int u = 0; u < 2; ++u) d[i][u][kh] += wv * z[u + 2 - kh][2 - kw];
-            }
+      for (int s = 0; s < 16; ++s) {
+        const bool pin = (unsigned)(32 * wave + 2 * s + kq - 1) < (unsigned)sw;
+        av[s] = *(pin ? zr + 2 * s : Z0);
+        bv[s] = xr[2 * s];
       }
 #pragma unroll
+      for (int s = 0; s < 16; ++s)
+        adw = __builtin_amdgcn_mfma_f32_32x32x2f32(av[s], bv[s], adw, 0, 0, 0);
+      // all operand reads in flight before the matrix work starts
+      __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // P for this wave's 32 pixels
+    {
+      f32x16 ap;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ap[r] = 0.f;
+      const float* zc = Zs + kq * P + pb + j;
+      float zv[16];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) zv[k] = zc[2 * k * P];
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        ap = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[k], zv[k], ap, 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Ps[acc_row(r, lane) * P + pb + j] = ap[r];
+    }
+    __syncthreads();   // P complete; row h's reads of Zs and Xs are done
+
+    // staging is unconditional (rows past the image are zeros): straight-line
+    // code keeps the compiler's waits on these loads precise
+    store_dz(q);
+    store_x(q, h + 2);
+    if (cown) {
+      // dx row h-1 is complete after this row; rows h and h+1 take their share
+      float qv[CI][3];
+      const int k0 = tid + 4;   // LDS column of strip column col
+#pragma unroll
       for (int i = 0; i < CI; ++i)
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          Pd[(oq * CI + i) * (kFuTH * kFuTW) + (prow + u) * kFuTW + pc] =
-              (d[i][u][0] + d[i][u][1]) + d[i][u][2];
-    }
-    __syncthreads();  // LDS tile reads and the partial dx are complete
-    if (dx && tid < kFuTH * kFuTW) {
-      int n, h0, w0;
-      tile_origin(t, n, h0, w0);
-      const int r = tid / kFuTW, cc = tid - r * kFuTW;
-      const int h = h0 + r, w = w0 + cc;
-      if (h < g.H && w < g.W) {
-#pragma unroll
-        for (int i = 0; i < CI; ++i) {
-          const float v = (Pd[(0 * CI + i) * 256 + tid] + Pd[(1 * CI + i) * 256 + tid]) +
-                          (Pd[(2 * CI + i) * 256 + tid] + Pd[(3 * CI + i) * 256 + tid]);
-          float* q = dx + ((int64_t)n * CI + i) * g.HW + h * g.W + w;
-          *q = accumulate ? *q + v : v;
+        for (int kh = 0; kh < 3; ++kh) {
+          const float* pr = Ps + (i * 9 + kh * 3) * P + k0;
+          qv[i][kh] = (pr[1] + pr[P]) + pr[2 * P - 1];
         }
+      const int hp = h - 1;
+#pragma unroll
+      for (int i = 0; i < CI; ++i) {
+        const float vprev = dprev[i] + qv[i][0];
+        if (hp >= r0 && hp < r1) {
+          float* d = dx + ((int64_t)(n * CI + i) * g.H + hp) * g.W + col;
+          *d = ACC ? *d + vprev : vprev;
+        }
+        dprev[i] = dcur[i] + qv[i][1];
+        dcur[i] = qv[i][2];
       }
     }
+    load_dz(q, h + 3);
+    load_x(q, h + 4);
+    __syncthreads();   // row h+1 staged; P reads done
+  };
+
+  // ---- prologue: x rows hA-1 .. hA+1 and dz row hA staged; rows hA+1 and hA+2
+  // (x: hA+2 and hA+3) in the two register sets
+  Stage s0, s1;
+  for (int h = hA - 1; h <= hA + 1; ++h) {
+    load_x(s0, h);
+    store_x(s0, h);
+  }
+  load_dz(s0, hA);
+  __syncthreads();   // the zero fill is done before the staged rows land
+  store_dz(s0);
+  load_dz(s0, hA + 1);
+  load_x(s0, hA + 2);
+  load_dz(s1, hA + 2);
+  load_x(s1, hA + 3);
+  __syncthreads();
+
+  for (int h = hA; h <= hE; h += 2) {
+    row(h, s0);
+    row(h + 1, s1);
   }
 
-  // Sum the eight waves' dW blocks (fixed order) and write this work-group's partial.
+  // Sum the four waves' dW blocks (fixed order) and write this work-group's partial.
   __syncthreads();
-  float* red = Zs;  // 8 x 16 x 64 floats
+  float* red = Zs;  // 4 x 16 x 64 floats
 #pragma unroll
-  for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = acc[r];
+  for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = adw[r];
   __syncthreads();
   if (wave == 0) {
     float* dst = dwpart + (int64_t)blockIdx.x * g.OC * g.J;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float v = 0.f;
-#pragma unroll
-      for (int w8 = 0; w8 < 8; ++w8) v += red[(w8 * 16 + r) * 64 + lane];
+      const float v = (red[r * 64 + lane] + red[(16 + r) * 64 + lane]) +
+                      (red[(32 + r) * 64 + lane] + red[(48 + r) * 64 + lane]);
       const int o = acc_row(r, lane);
-      if (o < g.OC && j < 9 * CI) dst[o * g.J + j] = v;
+      if (o < g.OC && jv) dst[o * g.J + j] = v;
     }
   }
 }
@@ -1540,16 +1564,23 @@ bool conv_fused_dwdx_ok(const ConvGeom& g) {
 }
 
 struct FuPlan {
-  int tiles_per_wg, wgs, groups;
+  int nstrips, sw, nruns, rlen, wgs, groups;
 };
 
 static FuPlan plan_fused(const ConvGeom& g) {
   FuPlan p{};
-  const int64_t ntiles =
-      (int64_t)g.N * ceil_div(g.H, kFuTH) * ceil_div(g.W, kFuTW);
-  const int64_t target = 512;  // two resident work-groups per CU (measured best)
-  p.tiles_per_wg = (int)std::max<int64_t>(1, ceil_div(ntiles, target));
-  p.wgs = (int)ceil_div(ntiles, p.tiles_per_wg);
+  // strips of at most kFrMaxW columns, a multiple of 4, as even as possible
+  const int ns0 = (int)ceil_div(g.W, kFrMaxW);
+  p.sw = (int)(ceil_div(ceil_div(g.W, ns0), 4) * 4);
+  p.nstrips = (int)ceil_div(g.W, p.sw);
+  // runs of rows: about three work-groups per CU, at least 4 rows each (each
+  // run also walks the dz rows just above and below it)
+  const int64_t target = 768;
+  const int64_t runs = std::max<int64_t>(
+      1, std::min<int64_t>(ceil_div(g.H, 4), ceil_div(target, (int64_t)g.N * p.nstrips)));
+  p.rlen = (int)ceil_div(g.H, runs);
+  p.nruns = (int)ceil_div(g.H, p.rlen);
+  p.wgs = g.N * p.nstrips * p.nruns;
   p.groups = p.wgs > kReduceGroup ? (int)ceil_div(p.wgs, kReduceGroup) : 0;
   return p;
 }
@@ -1566,21 +1597,20 @@ static int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits,
 int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
                            float* dw, float* dx, int accumulate, float* ws, hipStream_t st) {
   const FuPlan p = plan_fused(g);
+#define CBB_FR(CI_)                                                                      \
+  if (accumulate)                                                                          \
+    conv_first_rows<CI_, true><<<p.wgs, kFrThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.nstrips, \
+                                                             p.sw, p.nruns, p.rlen);       \
+  else                                                                                     \
+    conv_first_rows<CI_, false><<<p.wgs, kFrThreads, 0, st>>>(g, x, wt, dz, ws, dx,          \
+                                                              p.nstrips, p.sw, p.nruns, p.rlen)
   switch (g.C) {
-    case 1:
-      conv_smallc_dwdx<1><<<p.wgs, kFuThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
-                                                      accumulate);
-      break;
-    case 2:
-      conv_smallc_dwdx<2><<<p.wgs, kFuThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
-                                                      accumulate);
-      break;
-    default:
-      conv_smallc_dwdx<3><<<p.wgs, kFuThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.tiles_per_wg,
-                                                      accumulate);
-      break;
+    case 1: CBB_FR(1); break;
+    case 2: CBB_FR(2); break;
+    default: CBB_FR(3); break;
   }
-  const int rc = check_launch("conv_smallc_dwdx");
+#undef CBB_FR
+  const int rc = check_launch("conv_first_rows");
   if (rc) return rc;
   return launch_dw_reduce(g, dw, ws, p.wgs, p.groups, 0, st);
 }

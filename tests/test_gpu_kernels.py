@@ -161,6 +161,8 @@ def test_conv_coverage_bit_exact(case):
     (1, 1, 9, 12, 7, 3, 1, 1),      # fused: one input channel, one partial tile
     (2, 2, 40, 68, 20, 3, 1, 1),    # fused: two input channels
     (1, 3, 1, 4, 5, 3, 1, 1),       # fused: one image row
+    (1, 3, 37, 244, 32, 3, 1, 1),   # fused: three column strips, runs of one row
+    (8, 3, 100, 256, 32, 3, 1, 1),  # fused: ragged last strip, runs of four rows
     (2, 3, 20, 20, 40, 3, 1, 1),    # not fused: more than 32 outputs
     (1, 3, 9, 9, 8, 3, 1, 1),       # not fused: width not a multiple of 4
     (2, 4, 12, 12, 8, 3, 1, 1),     # not fused: four inputs
