@@ -741,7 +741,10 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(float
 // DMA = true stages each chunk with direct global-to-LDS loads into one of two
 // LDS buffers (the next chunk lands while the matrix cores work on this one;
 // needs 16-byte aligned weights); DMA = false stages through registers.
-template <int S, int F, int RM, bool DMA>
+// Z4 (stride 1, DMA, width a multiple of 4, 16-byte aligned dz): the dz tile
+// rows span columns -4 .. W+3 and are copied in 16-byte pieces (a quarter of the
+// copy instructions).
+template <int S, int F, int RM, bool DMA, bool Z4>
 __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const float* __restrict__ wt,
                                                             const float* __restrict__ dz,
                                                             float* __restrict__ dx,
@@ -749,7 +752,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
                                                             int accumulate, int tiles_per_img,
                                                             int tiles_w, int ksplits) {
   using C = Dx3Cfg<S, F, RM>;
-  constexpr int ZBUF = (C::ZFLOATS + 63) / 64 * 64;   // whole 64-float DMA blocks
+  static_assert(!Z4 || (S == 1 && DMA), "16-byte tile copies: stride 1, direct copies");
+  // whole copy blocks: 64 floats (4-byte copies) or 256 floats (16-byte copies)
+  constexpr int ZBUF = Z4 ? (C::ZFLOATS + 255) / 256 * 256 : (C::ZFLOATS + 63) / 64 * 64;
   // two buffers as separate arrays, so that reads of one provably do not alias
   // the copies in flight into the other
   __shared__ float Z[ZBUF], Z1[DMA ? ZBUF : 1];
@@ -773,8 +778,8 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
     const int p0 = tt * 128 * F;                       // first pixel of the tile
     const int hmin = p0 / g.W;
     zr0 = hmin - 1;
-    zc0 = -1;
-    ZC = g.W + 2;
+    zc0 = Z4 ? -4 : -1;
+    ZC = Z4 ? g.W + 8 : g.W + 2;
     const int plast = min(p0 + 128 * F, g.H * g.W) - 1;
     ZR = plast / g.W - hmin + 3;
 #pragma unroll
@@ -784,8 +789,8 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
       pval[f] = p < g.H * g.W;
       prow[f] = h;
       pcol[f] = w;
-      // dz[h+1-kh][w+1-kw] sits at Z row (h-hmin)+2-kh, col w+2-kw
-      pbase[f] = pval[f] ? (h - hmin) * ZC + w : 0;
+      // dz[h+1-kh][w+1-kw] sits at Z row (h-hmin)+2-kh, col w+2-kw (+3 with Z4)
+      pbase[f] = pval[f] ? (h - hmin) * ZC + w + (Z4 ? 3 : 0) : 0;
       ph_[f] = pw_[f] = 0;
     }
   } else {
@@ -814,18 +819,18 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   // ---- staging of one chunk (OCB output channels): the dz tile and the weights
   // [o][i][tap].  The host guarantees C % BMC == 0 and OC % OCB == 0, so only
   // the image border masks.  A staged element's offset inside a chunk does not
-  // depend on the chunk: computed once (-1 = zero padding).  Element e of the
-  // tile is staged by thread e % 256 (wave-contiguous blocks of 64).
-  // Planes sit ZPLANE floats apart in LDS whatever the tile size (ZR*ZC <= ZPLANE),
-  // so channel and tap offsets of the operand reads are compile-time immediates;
-  // the rest of a plane is staged as zeros.
-  const int ZP = S == 1 ? ZR * ZC : C::ZPLANE;
+  // depend on the chunk: computed once (-1 = zero padding).  Unit e of the tile
+  // (one float, or a 16-byte piece with Z4) is staged by thread e % 256
+  // (wave-contiguous blocks of 64 units).  Planes are ZR*ZC floats apart (dense).
+  const int ZP = ZR * ZC;
   const float* dzb = dz + (int64_t)b * g.OC * g.OHW;
   const int zcount = C::OCB * ZP;
-  int zofs[C::ZPT];
+  constexpr int ZU = Z4 ? 4 : 1;   // floats per staged unit
+  constexpr int ZQ = Z4 ? (C::ZFLOATS / 4 + kThreads - 1) / kThreads : C::ZPT;
+  int zofs[ZQ];
 #pragma unroll
-  for (int r = 0; r < C::ZPT; ++r) {
-    const int e = tid + kThreads * r;
+  for (int r = 0; r < ZQ; ++r) {
+    const int e = (tid + kThreads * r) * ZU;
     const int o = e / ZP, rem = e - o * ZP;
     const int zr = rem / ZC, zc = rem - zr * ZC;
     const int ho = zr0 + zr, wo = zc0 + zc;
@@ -839,13 +844,17 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   auto issue = [&](int o0, float* zl, float* wl) {
     const float* zb = dzb + (int64_t)o0 * g.OHW;
 #pragma unroll
-    for (int r = 0; r < C::ZPT; ++r) {
+    for (int r = 0; r < ZQ; ++r) {
       const int q = wave + 4 * r;
       int zo = zofs[r];
       asm volatile("" : "+v"(zo));   // keeps the 64-bit addresses from being hoisted
-      if (64 * q < zcount)
-        __builtin_amdgcn_global_load_lds(zo >= 0 ? zb + zo : g_dx3_zero, lds_ptr(zl + 64 * q),
-                                         4, 0, 0);
+      if (64 * ZU * q < zcount) {
+        const float* src = zo >= 0 ? zb + zo : g_dx3_zero;
+        if constexpr (Z4)
+          __builtin_amdgcn_global_load_lds(src, lds_ptr(zl + 256 * q), 16, 0, 0);
+        else
+          __builtin_amdgcn_global_load_lds(src, lds_ptr(zl + 64 * q), 4, 0, 0);
+      }
     }
     const float* wb = wt + ((int64_t)o0 * g.C + i0) * 9;
     constexpr int WQ = C::WFLOATS / 256;
@@ -865,7 +874,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   auto load = [&](int o0) {
     const float* zb = dzb + (int64_t)o0 * g.OHW;
 #pragma unroll
-    for (int r = 0; r < C::ZPT; ++r) rz[DMA ? 0 : r] = zb[(unsigned)max(zofs[r], 0)];
+    for (int r = 0; r < ZQ; ++r) rz[DMA ? 0 : r] = zb[(unsigned)max(zofs[r], 0)];
     const float* wb = wt + ((int64_t)o0 * g.C + i0) * 9;
 #pragma unroll
     for (int r = 0; r < C::WPT; ++r) {
@@ -879,7 +888,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   // (a lane reads weights 9 floats apart: no bank conflicts).
   auto store = [&]() {
 #pragma unroll
-    for (int r = 0; r < C::ZPT; ++r) {
+    for (int r = 0; r < ZQ; ++r) {
       const int e = tid + kThreads * r;
       if (e < zcount) Z[e] = zofs[r] >= 0 ? rz[DMA ? 0 : r] : 0.f;
     }
@@ -1825,19 +1834,31 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
   if (p.kind == DX_D3S1 || p.kind == DX_D3S1_SMALL || p.kind == DX_D3S2) {
     const unsigned blocks = (unsigned)((int64_t)g.N * p.pixtiles * p.ctiles * p.ksplits);
     const int tiles_w = p.kind == DX_D3S2 ? (int)ceil_div(g.W, 64) : 0;
-#define CBB_DX3(S_, F_, RM_)                                                              \
+    // 16-byte tile copies: the tile rows (W + 8 floats) must still fit the plane
+    const int f1 = p.kind == DX_D3S1 ? 2 : 1;
+    const bool z4 = g.S == 1 && aligned16(wt) && aligned16(dz) && g.W % 4 == 0 &&
+                    ((128 * f1 - 1) / g.W + 4) * (g.W + 8) <= Dx3Cfg<1, 1, 1>::ZPLANE;
+#define CBB_DX3(S_, F_, RM_, Z4_)                                                         \
   if (aligned16(wt))                                                                      \
-    conv_dx3_direct<S_, F_, RM_, true><<<blocks, kThreads, 0, st>>>(                      \
+    conv_dx3_direct<S_, F_, RM_, true, Z4_><<<blocks, kThreads, 0, st>>>(                 \
         g, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);                   \
   else                                                                                    \
-    conv_dx3_direct<S_, F_, RM_, false><<<blocks, kThreads, 0, st>>>(                     \
+    conv_dx3_direct<S_, F_, RM_, false, false><<<blocks, kThreads, 0, st>>>(              \
         g, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);
     if (p.kind == DX_D3S1) {
-      CBB_DX3(1, 2, 2)
+      if (z4) {
+        CBB_DX3(1, 2, 2, true)
+      } else {
+        CBB_DX3(1, 2, 2, false)
+      }
     } else if (p.kind == DX_D3S1_SMALL) {
-      CBB_DX3(1, 1, 1)
+      if (z4) {
+        CBB_DX3(1, 1, 1, true)
+      } else {
+        CBB_DX3(1, 1, 1, false)
+      }
     } else {
-      CBB_DX3(2, 1, 1)
+      CBB_DX3(2, 1, 1, false)
     }
 #undef CBB_DX3
     int rc = check_launch("conv_dx3_direct");

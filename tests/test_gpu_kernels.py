@@ -58,6 +58,10 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (2, 64, 12, 12, 96, 1, 1, 0, True, "leaky"),     # 1x1 GEMMs with 16-byte staging, ragged o
     (3, 20, 6, 10, 70, 1, 1, 0, False, "linear"),    # 1x1 GEMMs: ragged i and o tiles
     (2, 64, 40, 31, 24, 3, 1, 1, True, "leaky"),     # dX: 128-pixel tile-direct, ragged plane
+    (2, 3, 24, 40, 32, 3, 1, 1, True, "logistic"),   # first layer, logistic
+    (1, 2, 17, 36, 12, 3, 1, 1, False, "relu"),      # first layer, bias only
+    (2, 1, 20, 16, 5, 3, 1, 1, True, "linear"),      # first layer, BN, no activation
+    (1, 3, 13, 132, 30, 3, 1, 1, False, "leaky"),    # first layer, two column strips
 ]
 
 
@@ -124,6 +128,17 @@ def test_conv_block_accumulate_inplace_and_no_dx(case):
         assert_close("dz in place", got["dz"], ref["dz"])
     ref, got = run_conv(torch, case, seed=8, want_dx=False)
     assert_close("dw (no dx)", got["dw"], ref["dw"])
+
+
+@pytest.mark.parametrize("case", [CONV_CASES[0], CONV_CASES[-4], CONV_CASES[-1]])
+def test_first_layer_accumulate(case):
+    """First layers (one streaming kernel for dW and dX) with dx accumulation and dz
+    in its own buffer."""
+    torch = require_gpu()
+    announce(f"first layer, accumulate {case}")
+    ref, got = run_conv(torch, case, seed=9, dx_accumulate=True)
+    for k in ("dw", "db", "dz", "dx"):
+        assert_close(k, got[k], ref[k])
 
 
 @pytest.mark.parametrize("case", [(2, 3, 32, 32, 16, 3, 1, 1), (1, 4, 41, 41, 6, 3, 2, 1),
