@@ -741,9 +741,9 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(float
 // DMA = true stages each chunk with direct global-to-LDS loads into one of two
 // LDS buffers (the next chunk lands while the matrix cores work on this one;
 // needs 16-byte aligned weights); DMA = false stages through registers.
-// Z4 (stride 1, DMA, width a multiple of 4, 16-byte aligned dz): the dz tile
-// rows span columns -4 .. W+3 and are copied in 16-byte pieces (a quarter of the
-// copy instructions).
+// Z4 (DMA, dz width a multiple of 4, 16-byte aligned dz): the dz tile is copied
+// in 16-byte pieces (a quarter of the copy instructions); its rows span columns
+// -4 .. W+3 at stride 1 and 36 columns at stride 2.
 template <int S, int F, int RM, bool DMA, bool Z4>
 __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const float* __restrict__ wt,
                                                             const float* __restrict__ dz,
@@ -752,9 +752,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
                                                             int accumulate, int tiles_per_img,
                                                             int tiles_w, int ksplits) {
   using C = Dx3Cfg<S, F, RM>;
-  static_assert(!Z4 || (S == 1 && DMA), "16-byte tile copies: stride 1, direct copies");
+  static_assert(!Z4 || DMA, "16-byte tile copies are direct copies");
+  // stride 2 with 16-byte copies: tile columns zc0 .. zc0+35 (nine pieces)
+  constexpr int ZC2 = (S == 2 && Z4) ? 36 : C::ZC2;
+  constexpr int ZFL = S == 2 ? C::OCB * C::ZR2 * ZC2 : C::ZFLOATS;   // tile floats, at most
   // whole copy blocks: 64 floats (4-byte copies) or 256 floats (16-byte copies)
-  constexpr int ZBUF = Z4 ? (C::ZFLOATS + 255) / 256 * 256 : (C::ZFLOATS + 63) / 64 * 64;
+  constexpr int ZBUF = Z4 ? (ZFL + 255) / 256 * 256 : (ZFL + 63) / 64 * 64;
   // two buffers as separate arrays, so that reads of one provably do not alias
   // the copies in flight into the other
   __shared__ float Z[ZBUF], Z1[DMA ? ZBUF : 1];
@@ -797,9 +800,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
     const int th = tt / tiles_w, tw = tt - th * tiles_w;
     const int h0 = th * 8 * F, w0 = tw * 64;
     zr0 = h0 / 2;
-    zc0 = w0 / 2;
+    zc0 = w0 / 2;   // a multiple of 32
     ZR = C::ZR2;
-    ZC = C::ZC2;
+    ZC = ZC2;
 #pragma unroll
     for (int f = 0; f < C::NFRAG; ++f) {
       const int phase = f % 4, fr = f / 4;             // fragment = (phase, phase row)
@@ -812,7 +815,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
       ph_[f] = ph;
       pw_[f] = pw;
       // dz[(h+1-kh)/2][(w+1-kw)/2] sits at Z row rr + (ph+1-kh)/2, col col + (pw+1-kw)/2
-      pbase[f] = rr * C::ZC2 + col;
+      pbase[f] = rr * ZC2 + col;
     }
   }
 
@@ -826,7 +829,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   const float* dzb = dz + (int64_t)b * g.OC * g.OHW;
   const int zcount = C::OCB * ZP;
   constexpr int ZU = Z4 ? 4 : 1;   // floats per staged unit
-  constexpr int ZQ = Z4 ? (C::ZFLOATS / 4 + kThreads - 1) / kThreads : C::ZPT;
+  constexpr int ZQ = Z4 ? (ZFL / 4 + kThreads - 1) / kThreads : C::ZPT;
   int zofs[ZQ];
 #pragma unroll
   for (int r = 0; r < ZQ; ++r) {
@@ -929,7 +932,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
           if constexpr (S == 1)
             off = (2 - kh) * ZC + (2 - kw);
           else
-            off = ((ph_[f] + 1 - kh) >> 1) * C::ZC2 + ((pw_[f] + 1 - kw) >> 1);
+            off = ((ph_[f] + 1 - kh) >> 1) * ZC2 + ((pw_[f] + 1 - kw) >> 1);
           bv[sl][kk][f] = zl[o * ZP + pbase[f] + off];
         }
       }
@@ -1836,8 +1839,10 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
     const int tiles_w = p.kind == DX_D3S2 ? (int)ceil_div(g.W, 64) : 0;
     // 16-byte tile copies: the tile rows (W + 8 floats) must still fit the plane
     const int f1 = p.kind == DX_D3S1 ? 2 : 1;
-    const bool z4 = g.S == 1 && aligned16(wt) && aligned16(dz) && g.W % 4 == 0 &&
-                    ((128 * f1 - 1) / g.W + 4) * (g.W + 8) <= Dx3Cfg<1, 1, 1>::ZPLANE;
+    const bool z4 = aligned16(wt) && aligned16(dz) &&
+                    (g.S == 1 ? g.W % 4 == 0 &&
+                                    ((128 * f1 - 1) / g.W + 4) * (g.W + 8) <= Dx3Cfg<1, 1, 1>::ZPLANE
+                              : g.OW % 4 == 0);
 #define CBB_DX3(S_, F_, RM_, Z4_)                                                         \
   if (aligned16(wt))                                                                      \
     conv_dx3_direct<S_, F_, RM_, true, Z4_><<<blocks, kThreads, 0, st>>>(                 \
@@ -1858,7 +1863,11 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
         CBB_DX3(1, 1, 1, false)
       }
     } else {
-      CBB_DX3(2, 1, 1, false)
+      if (z4) {
+        CBB_DX3(2, 1, 1, true)
+      } else {
+        CBB_DX3(2, 1, 1, false)
+      }
     }
 #undef CBB_DX3
     int rc = check_launch("conv_dx3_direct");
