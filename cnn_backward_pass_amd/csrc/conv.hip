@@ -390,7 +390,10 @@ struct Dw3RowCfg {
   static_assert(TC % 2 == 0 && (S == 1 || S == 2), "even strip, stride 1 or 2");
 };
 
-template <int S, int TC>
+// V4: 16-byte loads (the host checks that W and OW are multiples of 4, TC too,
+// and that x and dz are 16-byte aligned); x pieces start three columns before
+// LDS column 0 and the extra columns are dropped at the LDS store.
+template <int S, int TC, bool V4>
 __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
     ConvGeom g, const float* __restrict__ x, const float* __restrict__ dz, float* __restrict__ out,
     int strips, int rchunks, int rlen, int direct) {
@@ -416,12 +419,39 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
   // LDS, so nothing consumes a loaded value before the next row: the loads
   // stay in flight during the matrix-core work.
   static_assert(Cf::XPT <= 32 && Cf::ZPT <= 32, "one mask bit per fetched element");
-  float px[Cf::XPT], pz[Cf::ZPT];
+  static_assert(!V4 || TC % 4 == 0, "16-byte loads need a strip width multiple of 4");
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  constexpr int XV = (Cf::XC + 6) / 4;   // 16-byte pieces per input row (columns -3 ..)
+  constexpr int XNEW4 = S * 32 * XV, XPT4 = (XNEW4 + NT - 1) / NT;
+  constexpr int ZV = TC / 4, ZNEW4 = 64 * ZV, ZPT4 = (ZNEW4 + NT - 1) / NT;
+  float px[V4 ? 1 : Cf::XPT], pz[V4 ? 1 : Cf::ZPT];
+  f4 px4[V4 ? XPT4 : 1], pz4[V4 ? ZPT4 : 1];
   uint32_t xm = 0, zm = 0;
   auto fetch = [&](int q) {
     const int hb = S * q + 2 - S;
     xm = 0;
     zm = 0;
+    if constexpr (V4) {
+#pragma unroll
+      for (int i = 0; i < XPT4; ++i) {
+        const int e = tid + i * NT;
+        const int rr = e / (32 * XV), rem = e - rr * (32 * XV);
+        const int c = rem / XV, v = rem - c * XV;
+        const int h = hb + rr, w = ic0 - 3 + 4 * v;
+        const bool ok = e < XNEW4 && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+        px4[i] = *(const f4*)(xb + (ok ? c * g.HW + h * g.W + w : 0));
+        xm |= (uint32_t)ok << i;
+      }
+#pragma unroll
+      for (int i = 0; i < ZPT4; ++i) {
+        const int e = tid + i * NT;
+        const int o = e / ZV, v = e - o * ZV;
+        const bool ok = e < ZNEW4 && oc0 + 4 * v < g.OW;
+        pz4[i] = *(const f4*)(zb + (ok ? o * g.OHW + q * g.OW + oc0 + 4 * v : 0));
+        zm |= (uint32_t)ok << i;
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < Cf::XPT; ++i) {
       const int e = tid + i * NT;
@@ -443,6 +473,33 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
   };
   auto commit = [&](int q) {
     const int hb = S * q + 2 - S;
+    if constexpr (V4) {
+#pragma unroll
+      for (int i = 0; i < XPT4; ++i) {
+        const int e = tid + i * NT;
+        const int rr = e / (32 * XV), rem = e - rr * (32 * XV);
+        const int c = rem / XV, v = rem - c * XV;
+        if (e < XNEW4) {
+          float* d = lds + ((hb + rr + 3) % 3) * Cf::SLOT + c * Cf::CS + 4 * v - 3;
+          const bool ok = (xm >> i) & 1u;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if ((unsigned)(4 * v - 3 + u) < (unsigned)Cf::XC) d[u] = ok ? px4[i][u] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < ZPT4; ++i) {
+        const int e = tid + i * NT;
+        const int o = e / ZV, v = e - o * ZV;
+        if (e < ZNEW4) {
+          float* d = lds + Cf::Z0 + o * Cf::OS + 4 * v;
+          const bool ok = (zm >> i) & 1u;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) d[u] = ok ? pz4[i][u] : 0.f;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < Cf::XPT; ++i) {
       const int e = tid + i * NT;
@@ -1646,10 +1703,17 @@ template <int S>
 static void launch_dw3_rows(const ConvGeom& g, const DwPlan& p, const float* x, const float* dz,
                             float* out, int direct, hipStream_t st) {
   const unsigned blocks = (unsigned)((int64_t)p.splits * (g.OC / 64) * (g.C / 32));
-#define CBB_DW3(TC)                                                                           \
-  case TC:                                                                                    \
-    conv_dw3_rows<S, TC><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips, p.rchunks,  \
-                                                      p.rlen, direct);                        \
+  // 16-byte loads: rows and strip origins on 16-byte boundaries
+  const bool v4 = aligned16(x) && aligned16(dz) && g.W % 4 == 0 && g.OW % 4 == 0 &&
+                  p.rows_tc % 4 == 0;
+#define CBB_DW3(TC)                                                                          \
+  case TC:                                                                                   \
+    if (v4)                                                                                  \
+      conv_dw3_rows<S, TC, true><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,    \
+                                                                 p.rchunks, p.rlen, direct); \
+    else                                                                                     \
+      conv_dw3_rows<S, TC, false><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,   \
+                                                                  p.rchunks, p.rlen, direct); \
     break;
   switch (p.rows_tc) {
     CBB_DW3(104)
@@ -1657,7 +1721,8 @@ static void launch_dw3_rows(const ConvGeom& g, const DwPlan& p, const float* x, 
     CBB_DW3(52)
     CBB_DW3(32)
     default:
-      CBB_DW3(26)
+      conv_dw3_rows<S, 26, false><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,
+                                                                  p.rchunks, p.rlen, direct);
   }
 #undef CBB_DW3
 }
