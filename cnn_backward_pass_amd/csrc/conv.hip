@@ -379,10 +379,13 @@ struct Dw3RowCfg {
   static constexpr int XC = S * (TC - 1) + 3;  // input columns under TC output columns
   static constexpr int CS = XC | 1;            // channel pitch inside a ring slot (odd)
   static constexpr int SLOT = 32 * CS;
+  static constexpr int NSLOT = 3 + S;          // ring: the three rows in use + the S arriving
   static constexpr int OS = TC + 1;            // dz row pitch per output channel (odd)
-  static constexpr int Z0 = 3 * SLOT;          // dz row buffer after the three slots
+  static constexpr int Z0 = NSLOT * SLOT;      // two dz row buffers after the slots
+  static constexpr int ZB = 64 * OS;
   static constexpr int RED = 6 * 3 * 16 * 64;  // step-half exchange: 6 waves x 3 accumulators
-  static constexpr int LDS_FLOATS = (Z0 + 64 * OS) > RED ? (Z0 + 64 * OS) : RED;
+  static constexpr int LDS_FLOATS = (Z0 + 2 * ZB) > RED ? (Z0 + 2 * ZB) : RED;
+  static constexpr bool FITS = LDS_FLOATS * 4 <= 160 * 1024;
   static constexpr int XNEW = S * 32 * XC;     // floats of the S input rows fetched per row
   static constexpr int XPT = (XNEW + kDw3Threads - 1) / kDw3Threads;
   static constexpr int ZNEW = 64 * TC;
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
         const int rr = e / (32 * XV), rem = e - rr * (32 * XV);
         const int c = rem / XV, v = rem - c * XV;
         if (e < XNEW4) {
-          float* d = lds + ((hb + rr + 3) % 3) * Cf::SLOT + c * Cf::CS + 4 * v - 3;
+          float* d = lds + ((hb + rr + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + 4 * v - 3;
           const bool ok = (xm >> i) & 1u;
 #pragma unroll
           for (int u = 0; u < 4; ++u)
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
         const int e = tid + i * NT;
         const int o = e / ZV, v = e - o * ZV;
         if (e < ZNEW4) {
-          float* d = lds + Cf::Z0 + o * Cf::OS + 4 * v;
+          float* d = lds + Cf::Z0 + (q & 1) * Cf::ZB + o * Cf::OS + 4 * v;
           const bool ok = (zm >> i) & 1u;
 #pragma unroll
           for (int u = 0; u < 4; ++u) d[u] = ok ? pz4[i][u] : 0.f;
@@ -506,13 +509,15 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
       const int rr = e / (32 * Cf::XC), rem = e - rr * (32 * Cf::XC);
       const int c = rem / Cf::XC, j = rem - c * Cf::XC;
       if (e < Cf::XNEW)
-        lds[((hb + rr + 3) % 3) * Cf::SLOT + c * Cf::CS + j] = ((xm >> i) & 1u) ? px[i] : 0.f;
+        lds[((hb + rr + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + j] =
+            ((xm >> i) & 1u) ? px[i] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < Cf::ZPT; ++i) {
       const int e = tid + i * NT;
       const int o = e / TC, j = e - o * TC;
-      if (e < Cf::ZNEW) lds[Cf::Z0 + o * Cf::OS + j] = ((zm >> i) & 1u) ? pz[i] : 0.f;
+      if (e < Cf::ZNEW)
+        lds[Cf::Z0 + (q & 1) * Cf::ZB + o * Cf::OS + j] = ((zm >> i) & 1u) ? pz[i] : 0.f;
     }
   };
 
@@ -523,7 +528,7 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
     const int h = S * r0 - 1 + rr, w = ic0 + j;
     const bool ok = (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
     const float v = xb[ok ? c * g.HW + h * g.W + w : 0];
-    lds[((h + 3) % 3) * Cf::SLOT + c * Cf::CS + j] = ok ? v : 0.f;
+    lds[((h + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + j] = ok ? v : 0.f;
   }
   fetch(r0);
   commit(r0);
@@ -537,11 +542,15 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 
   // this wave's half of the row: steps [kq*KH, min(KS, kq*KH + KH))
-  const int abase = Cf::Z0 + (32 * oh + (lane & 31)) * Cf::OS + (lane >> 5) + 2 * Cf::KH * kq;
+  const int abase0 = Cf::Z0 + (32 * oh + (lane & 31)) * Cf::OS + (lane >> 5) + 2 * Cf::KH * kq;
   const int bbase = (lane & 31) * Cf::CS + S * (lane >> 5) + 2 * S * Cf::KH * kq;
+  // One barrier per row: the rows and the dz buffer that arrive for row r+1 go
+  // to slots (buffer) that row r does not read, so the staging of r+1 overlaps
+  // other waves' matrix work on r.
   for (int r = r0; r < r1; ++r) {
-    // input row S*r - 1 + kh sits in slot (S*r + kh + 2) mod 3
-    const int bs = ((S * r + kh + 2) % 3) * Cf::SLOT + bbase;
+    // input row S*r - 1 + kh sits in slot (S*r - 1 + kh) mod NSLOT
+    const int bs = ((S * r + kh - 1 + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + bbase;
+    const int abase = abase0 + (r & 1) * Cf::ZB;
 #pragma unroll
     for (int sp = 0; sp < Cf::KH; ++sp) {
       if (Cf::KS % 2 == 0 || kq == 0 || sp < Cf::KS / 2) {
@@ -554,12 +563,11 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
           acc[kw] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[kw], acc[kw], 0, 0, 0);
       }
     }
-    __syncthreads();
     if (r + 1 < r1) {
       commit(r + 1);
-      __syncthreads();
       if (r + 2 < r1) fetch(r + 2);
     }
+    __syncthreads();
   }
 
   // Sum the step halves: waves kq = 1 hand their accumulators over through LDS.
@@ -1541,12 +1549,27 @@ struct DwPlan {
 // Row-streaming 3x3 dW: strip widths compiled in, and when to use it.
 static const int kDw3Tc[] = {104, 64, 52, 32, 26};
 
+static bool dw3_fits(int S, int tc) {
+  switch (tc) {
+#define CBB_FIT(T) \
+  case T: return S == 1 ? Dw3RowCfg<1, T>::FITS : Dw3RowCfg<2, T>::FITS;
+    CBB_FIT(104)
+    CBB_FIT(64)
+    CBB_FIT(52)
+    CBB_FIT(32)
+    CBB_FIT(26)
+#undef CBB_FIT
+  }
+  return false;
+}
+
 static bool plan_dw3_rows(const ConvGeom& g, DwPlan& p) {
   if (!(g.K == 3 && g.P == 1 && (g.S == 1 || g.S == 2) && g.C % 32 == 0 && g.OC % 64 == 0))
     return false;
   int best_tc = 0;
   int64_t best_pad = 0;
   for (int tc : kDw3Tc) {
+    if (!dw3_fits(g.S, tc)) continue;
     const int64_t padded = ceil_div(g.OW, tc) * tc;
     if (best_tc == 0 || padded < best_pad) {  // first (widest) wins ties
       best_tc = tc;
@@ -1708,12 +1731,14 @@ static void launch_dw3_rows(const ConvGeom& g, const DwPlan& p, const float* x, 
                   p.rows_tc % 4 == 0;
 #define CBB_DW3(TC)                                                                          \
   case TC:                                                                                   \
-    if (v4)                                                                                  \
-      conv_dw3_rows<S, TC, true><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,    \
-                                                                 p.rchunks, p.rlen, direct); \
-    else                                                                                     \
-      conv_dw3_rows<S, TC, false><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,   \
-                                                                  p.rchunks, p.rlen, direct); \
+    if constexpr (Dw3RowCfg<S, TC>::FITS) {                                                  \
+      if (v4)                                                                                \
+        conv_dw3_rows<S, TC, true><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,  \
+                                                                   p.rchunks, p.rlen, direct); \
+      else                                                                                   \
+        conv_dw3_rows<S, TC, false><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips, \
+                                                                    p.rchunks, p.rlen, direct); \
+    }                                                                                        \
     break;
   switch (p.rows_tc) {
     CBB_DW3(104)
