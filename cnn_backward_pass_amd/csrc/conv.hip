@@ -142,15 +142,27 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
 // thread in a fixed order, so the result does not depend on scheduling.
 constexpr int kReduceGroup = 32;
 
+// part[s0*mn + e] + ... + part[(s1-1)*mn + e] (s1 - s0 <= kReduceGroup), added in
+// index order; all the loads are issued before the first add.
+__device__ __forceinline__ float sum_in_order(const float* __restrict__ part, int s0, int s1,
+                                              int64_t mn, int64_t e) {
+  float v[kReduceGroup];
+#pragma unroll
+  for (int k = 0; k < kReduceGroup; ++k) v[k] = part[(int64_t)min(s0 + k, s1 - 1) * mn + e];
+  float acc = v[0];
+#pragma unroll
+  for (int k = 1; k < kReduceGroup; ++k)
+    if (s0 + k < s1) acc += v[k];
+  return acc;
+}
+
 __global__ __launch_bounds__(kThreads) void dw_reduce_l1(const float* __restrict__ part,
                                                          float* __restrict__ part2, int splits,
                                                          int64_t mn) {
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (e >= mn) return;
   const int s0 = blockIdx.y * kReduceGroup, s1 = min(splits, s0 + kReduceGroup);
-  float acc = 0.f;
-  for (int sp = s0; sp < s1; ++sp) acc += part[(int64_t)sp * mn + e];
-  part2[(int64_t)blockIdx.y * mn + e] = acc;
+  part2[(int64_t)blockIdx.y * mn + e] = sum_in_order(part, s0, s1, mn, e);
 }
 
 // Partials are either in dW's own [o][i][tap] order or, with kk > 0, tap-major
@@ -162,7 +174,8 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_l2(float* __restrict__ dw,
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (e >= mn) return;
   float s = 0.f;
-  for (int k = 0; k < n; ++k) s += part[(int64_t)k * mn + e];
+  for (int k0 = 0; k0 < n; k0 += kReduceGroup)
+    s += sum_in_order(part, k0, min(n, k0 + kReduceGroup), mn, e);
   int64_t d = e;
   if (kk > 0) {
     const int t = (int)(e / ((int64_t)oc * c)), r = (int)(e - (int64_t)t * oc * c);
@@ -1146,7 +1159,8 @@ __global__ __launch_bounds__(kThreads) void dx_splitk_reduce(float* __restrict__
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += stride) {
     float s = 0.f;
-    for (int sp = 0; sp < splits; ++sp) s += ws[(int64_t)sp * n + e];
+    for (int k0 = 0; k0 < splits; k0 += kReduceGroup)
+      s += sum_in_order(ws, k0, min(splits, k0 + kReduceGroup), n, e);
     dx[e] = accumulate ? dx[e] + s : s;
   }
 }
