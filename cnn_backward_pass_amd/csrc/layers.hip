@@ -204,11 +204,13 @@ struct GemmArgs {
   int accumulate;
 };
 
+// TS = TileShape<2, 2, 1> (64x64 tiles), or TileShape<1, 1, 4> (32x32 tiles,
+// the four waves splitting each K tile) for small outputs with a long K.
+template <class TS>
 __global__ __launch_bounds__(kThreads) void strided_gemm_kernel(GemmArgs a, int tiles_n) {
-  using TS = TileShape<2, 2, 1>;
   __shared__ float lds[TS::LDS_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % TS::WM, wn = wave / TS::WM, wk = 0;
+  const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
   const int m0 = (blockIdx.x / tiles_n) * TS::BM, n0 = (blockIdx.x % tiles_n) * TS::BN;
   // Register-prefetched K tiles (two ahead, see gemm_mainloop); out-of-range
   // elements read a clamped address and are zeroed at the LDS store, so the
@@ -254,22 +256,39 @@ __global__ __launch_bounds__(kThreads) void strided_gemm_kernel(GemmArgs a, int 
   Acc<TS> acc;
   acc.zero();
   gemm_mainloop<TS>(lds, 0, a.K, load, store, acc, wm, wn, wk, lane);
-  const int n = n0 + wn * 32 + acc_col(lane);
-  if (n >= a.N) return;
+  reduce_wk<TS>(acc, lds, wm, wn, wk, lane);
+  if (wk != 0) return;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = m0 + wm * 32 + acc_row(r, lane);
-    if (m < a.M) {
-      float* c = a.C + (int64_t)m * a.ldc + n;
-      *c = a.accumulate ? *c + acc.v[0][0][r] : acc.v[0][0][r];
+  for (int i = 0; i < TS::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < TS::RN; ++j) {
+      const int n = n0 + acc_n0<TS>(wn, j) + acc_col(lane);
+      if (n >= a.N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + acc_m0<TS>(wm, i) + acc_row(r, lane);
+        if (m < a.M) {
+          float* c = a.C + (int64_t)m * a.ldc + n;
+          *c = a.accumulate ? *c + acc.v[i][j][r] : acc.v[i][j][r];
+        }
+      }
     }
-  }
 }
 
 static int launch_gemm(const GemmArgs& a, hipStream_t st) {
-  const int tiles_n = (int)ceil_div(a.N, 64);
-  const int tiles = (int)ceil_div(a.M, 64) * tiles_n;
-  strided_gemm_kernel<<<tiles, kThreads, 0, st>>>(a, tiles_n);
+  const int64_t tiles64 = ceil_div(a.M, 64) * ceil_div(a.N, 64);
+  if (tiles64 < 64 && a.K >= 256) {
+    // few 64x64 tiles over a long K: 32x32 tiles, K split over the four waves
+    using TS = TileShape<1, 1, 4>;
+    const int tiles_n = (int)ceil_div(a.N, 32);
+    const int tiles = (int)ceil_div(a.M, 32) * tiles_n;
+    strided_gemm_kernel<TS><<<tiles, kThreads, 0, st>>>(a, tiles_n);
+  } else {
+    using TS = TileShape<2, 2, 1>;
+    const int tiles_n = (int)ceil_div(a.N, 64);
+    const int tiles = (int)ceil_div(a.M, 64) * tiles_n;
+    strided_gemm_kernel<TS><<<tiles, kThreads, 0, st>>>(a, tiles_n);
+  }
   return check_launch("strided_gemm_kernel");
 }
 

@@ -428,7 +428,8 @@ def test_fc_and_softmax_loss():
     from cnn_backward_pass_amd import cbb
     announce("fc / softmax loss")
     r = np.random.default_rng(4)
-    for (b, din, dout) in [(64, 800, 500), (64, 500, 10), (5, 37, 3), (1, 1, 1), (70, 65, 129)]:
+    for (b, din, dout) in [(64, 800, 500), (64, 500, 10), (5, 37, 3), (1, 1, 1), (70, 65, 129),
+                           (3, 300, 700)]:
         x = r.normal(size=(b, din)).astype(np.float32)
         w = r.normal(size=(dout, din)).astype(np.float32)
         d = r.normal(size=(b, dout)).astype(np.float32)
