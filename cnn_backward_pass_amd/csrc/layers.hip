@@ -298,8 +298,16 @@ __global__ __launch_bounds__(kThreads) void fc_bias_kernel(int batch, int out,
                                                            float* __restrict__ db) {
   const int o = blockIdx.x * kThreads + threadIdx.x;
   if (o >= out) return;
+  // batch rows in order, 16 loads in flight before each group's adds
   float s = 0.f;
-  for (int b = 0; b < batch; ++b) s += delta[(int64_t)b * out + o];
+  for (int b0 = 0; b0 < batch; b0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = delta[(int64_t)min(b0 + k, batch - 1) * out + o];
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (b0 + k < batch) s += v[k];
+  }
   db[o] += s;
 }
 
