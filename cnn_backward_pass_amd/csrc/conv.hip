@@ -1151,6 +1151,231 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   }
 }
 
+// Persistent form of the stride-2 tile-direct dX (16-byte tile copies, no split
+// over output channels, NCH chunks of 16 output channels per tile).  Each
+// work-group walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ... as one
+// sequence of chunk steps: the first chunk of the next tile is copied while the
+// last chunk of this one is computed, and a tile's output stores overlap the
+// next tile's work.  Output positions off the image store to a sink, so every
+// thread issues the same number of stores per tile and the waits for the next
+// chunk's copies can count past them (memory operations complete in order).
+__device__ float g_dx3_sink[4 * kThreads];
+
+template <int NCH>
+__global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
+                                                           const float* __restrict__ wt,
+                                                           const float* __restrict__ dz,
+                                                           float* __restrict__ dx, int accumulate,
+                                                           int ntiles, int tiles_per_img,
+                                                           int tiles_w) {
+  using C = Dx3Cfg<2, 1, 1>;
+  static_assert(NCH % 2 == 0, "chunks alternate between the two buffers within a tile");
+  constexpr int OCB = C::OCB, BMC = C::BMC, NFRAG = C::NFRAG;   // 16, 32, 4
+  constexpr int ZC2 = 36, ZR2 = C::ZR2, ZP = ZR2 * ZC2, ZFL = OCB * ZP;
+  constexpr int ZBUF = (ZFL + 255) / 256 * 256;
+  constexpr int ZQ = (ZFL / 4 + kThreads - 1) / kThreads;   // 16-byte pieces per thread
+  constexpr int WQ = C::WFLOATS / 256;                      // 16-byte weight copies per WG
+  constexpr int RR = 8, TP = 64, CH = 8, NV = CH * RR * TP / 4 / kThreads;
+  constexpr int NST = 4 * NV;                               // stores per thread per tile
+  __shared__ float Z[ZBUF], Z1[ZBUF];
+  __shared__ float Wl[C::WFLOATS], Wl1[C::WFLOATS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, khalf = lane >> 5;
+  const int ctiles = g.C / BMC;
+
+  // fragment f = output phase (ph, pw), phase row = wave: the same in every tile
+  int pbase[NFRAG], ph_[NFRAG], pw_[NFRAG];
+#pragma unroll
+  for (int f = 0; f < NFRAG; ++f) {
+    ph_[f] = (f >> 1) & 1;
+    pw_[f] = f & 1;
+    pbase[f] = wave * ZC2 + col;
+  }
+  struct Tile {
+    int b, i0, h0, w0;
+  };
+  auto tile_of = [&](int t) {
+    Tile r;
+    const int ct = t % ctiles, pt = t / ctiles;
+    r.b = pt / tiles_per_img;
+    const int tp = pt - r.b * tiles_per_img, th = tp / tiles_w;
+    r.h0 = th * 8;
+    r.w0 = (tp - th * tiles_w) * 64;
+    r.i0 = ct * BMC;
+    return r;
+  };
+  // source offsets of this thread's tile pieces for tile `nt` (-1: zero padding)
+  int zofs[ZQ];
+  auto set_zofs = [&](const Tile& nt) {
+    const int zr0 = nt.h0 / 2, zc0 = nt.w0 / 2;
+#pragma unroll
+    for (int r = 0; r < ZQ; ++r) {
+      const int e = (tid + kThreads * r) * 4;
+      const int o = e / ZP, rem = e - o * ZP;
+      const int zr = rem / ZC2, zc = rem - zr * ZC2;
+      const int ho = zr0 + zr, wo = zc0 + zc;
+      const bool ok = e < ZFL && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
+      zofs[r] = ok ? o * g.OHW + ho * g.OW + wo : -1;
+    }
+  };
+  auto issue = [&](const Tile& nt, int chunk, float* zl, float* wl) {
+    const float* zb = dz + ((int64_t)nt.b * g.OC + chunk * OCB) * g.OHW;
+#pragma unroll
+    for (int r = 0; r < ZQ; ++r) {
+      const int q = wave + 4 * r;
+      int zo = zofs[r];
+      asm volatile("" : "+v"(zo));   // keeps the 64-bit addresses from being hoisted
+      if (256 * q < ZFL)
+        __builtin_amdgcn_global_load_lds(zo >= 0 ? zb + zo : g_dx3_zero, lds_ptr(zl + 256 * q),
+                                         16, 0, 0);
+    }
+    const float* wb = wt + ((int64_t)chunk * OCB * g.C + nt.i0) * 9;
+#pragma unroll
+    for (int r = 0; r < (WQ + 3) / 4; ++r) {
+      const int q = wave + 4 * r;
+      if (q < WQ) {
+        const int e = 4 * (64 * q + lane);
+        const int o = e / (BMC * 9), rem = e - o * (BMC * 9);
+        __builtin_amdgcn_global_load_lds(wb + o * g.C * 9 + rem, lds_ptr(wl + 256 * q), 16, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[NFRAG];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int f = 0; f < NFRAG; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[f][r] = 0.f;
+  };
+  auto tap_hits = [&](int f, int kh, int kw) {
+    return ((ph_[f] + 1 - kh) & 1) == 0 && ((pw_[f] + 1 - kw) & 1) == 0;
+  };
+  // all taps of one chunk; tap t+1's operands are read while tap t's matrix work runs
+  auto compute = [&](const float* zl, const float* wl) {
+    constexpr int KK = OCB / 2;
+    float av[2][KK], bv[2][KK][NFRAG];
+    auto fetch = [&](int tap, int sl) {
+      const int kh = tap / 3, kw = tap - 3 * kh;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int o = 2 * kk + khalf;
+        av[sl][kk] = wl[(o * BMC + col) * 9 + tap];
+#pragma unroll
+        for (int f = 0; f < NFRAG; ++f) {
+          if (!tap_hits(f, kh, kw)) continue;
+          const int off = ((ph_[f] + 1 - kh) >> 1) * ZC2 + ((pw_[f] + 1 - kw) >> 1);
+          bv[sl][kk][f] = zl[o * ZP + pbase[f] + off];
+        }
+      }
+    };
+    constexpr int NRD = KK * 2, NMF = KK;   // one fragment per tap
+    fetch(0, 0);
+#pragma unroll
+    for (int tap = 0; tap < 9; ++tap) {
+      const int kh = tap / 3, kw = tap - 3 * kh, sl = tap & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (tap < 8) fetch(tap + 1, sl ^ 1);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int f = 0; f < NFRAG; ++f) {
+          if (!tap_hits(f, kh, kw)) continue;
+          acc[f] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[sl][kk], bv[sl][kk][f], acc[f], 0, 0, 0);
+        }
+      if (tap < 8) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The tile's 8 x 64 output region, 8 channels at a time, regrouped in row
+  // order in the free weight buffer `buf` and stored in 16-byte pieces; every
+  // thread issues NST stores (positions off the image go to the sink).
+  const bool vec = (g.W % 4) == 0 && ((uintptr_t)dx % 16) == 0;
+  auto epilogue = [&](const Tile& ct, float* buf) {
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      __syncthreads();   // the buffer is free (matrix work or previous pass done)
+#pragma unroll
+      for (int f = 0; f < NFRAG; ++f) {
+        const int rr = 2 * wave + ph_[f], cc = 2 * col + pw_[f];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) buf[((4 * khalf + j) * RR + rr) * TP + cc] = acc[f][4 * pass + j];
+      }
+      __syncthreads();
+      const int ib = ct.i0 + 8 * pass;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int u = tid + kThreads * k;
+        const int il = u / (RR * TP / 4), rem = u - il * (RR * TP / 4);
+        const int rr = rem / (TP / 4), c4 = rem - rr * (TP / 4);
+        const int h = ct.h0 + rr, w = ct.w0 + 4 * c4;
+        float4 v = *reinterpret_cast<const float4*>(&buf[(il * RR + rr) * TP + 4 * c4]);
+        float* q = dx + (((int64_t)ct.b * g.C + ib + il) * g.H + h) * g.W + w;
+        const bool whole = h < g.H && w + 3 < g.W && vec;
+        if (!whole && h < g.H && w < g.W) {
+          // ragged right edge or unaligned rows: element stores, then the sink
+          const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (w + e < g.W) q[e] = accumulate ? q[e] + vv[e] : vv[e];
+        }
+        float4* d = whole ? reinterpret_cast<float4*>(q) : reinterpret_cast<float4*>(g_dx3_sink) + tid;
+        if (accumulate && whole) {
+          const float4 a = *d;
+          v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
+        }
+        *d = v;
+      }
+    }
+  };
+
+  const int mytiles = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  if (mytiles <= 0) return;
+  Tile cur = tile_of(blockIdx.x);
+  set_zofs(cur);
+  issue(cur, 0, Z, Wl);
+  // the same count of younger stores as after a tile, so the first wait below
+  // looks like every later one
+  {
+    const float4 zero4 = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < NST; ++k) reinterpret_cast<float4*>(g_dx3_sink)[tid] = zero4;
+  }
+  for (int k = 0; k < mytiles; ++k) {
+    const int tn = blockIdx.x + (k + 1 < mytiles ? k + 1 : k) * gridDim.x;   // next (or this) tile
+    const Tile nxt = tile_of(tn);
+    zero_acc();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      float* zr = (c & 1) ? Z1 : Z;
+      float* wr = (c & 1) ? Wl1 : Wl;
+      float* zn = (c & 1) ? Z : Z1;
+      float* wn = (c & 1) ? Wl : Wl1;
+      // this wave's copies of chunk c have landed (only the previous tile's stores
+      // can be younger); after the barrier everyone's have, and the other buffer is free
+      static_assert(NST == 16, "the wait below counts 16 stores");
+      if (c == 0)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (c + 1 < NCH) {
+        issue(cur, c + 1, zn, wn);
+      } else {
+        set_zofs(nxt);
+        issue(nxt, 0, zn, wn);
+      }
+      compute(zr, wr);
+    }
+    // chunk NCH-1 used buffer 1 (NCH even): its weight buffer is free for the regroup
+    epilogue(cur, Wl1);
+    cur = nxt;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // nothing in flight at exit
+}
+
 // dx[e] (+)= sum over splits s (in order) of ws[s][e].
 __global__ __launch_bounds__(kThreads) void dx_splitk_reduce(float* __restrict__ dx,
                                                              const float* __restrict__ ws,
@@ -1954,6 +2179,17 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
   else                                                                                    \
     conv_dx3_direct<S_, F_, RM_, false, false><<<blocks, kThreads, 0, st>>>(              \
         g, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);
+    if (p.kind == DX_D3S2 && z4 && p.ksplits == 1 && (g.OC == 64 || g.OC == 128)) {
+      const int ntiles = (int)((int64_t)g.N * p.pixtiles * p.ctiles);
+      const unsigned grid = (unsigned)std::min(ntiles, 2 * 256);
+      if (g.OC == 64)
+        conv_dx3_s2p<4><<<grid, kThreads, 0, st>>>(g, wt, dz, dx, accumulate, ntiles, p.pixtiles,
+                                                   tiles_w);
+      else
+        conv_dx3_s2p<8><<<grid, kThreads, 0, st>>>(g, wt, dz, dx, accumulate, ntiles, p.pixtiles,
+                                                   tiles_w);
+      return check_launch("conv_dx3_s2p");
+    }
     if (p.kind == DX_D3S1) {
       if (z4) {
         CBB_DX3(1, 2, 2, true)

@@ -62,6 +62,8 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (1, 2, 17, 36, 12, 3, 1, 1, False, "relu"),      # first layer, bias only
     (2, 1, 20, 16, 5, 3, 1, 1, True, "linear"),      # first layer, BN, no activation
     (1, 3, 13, 132, 30, 3, 1, 1, False, "leaky"),    # first layer, two column strips
+    (6, 32, 200, 264, 64, 3, 2, 1, True, "leaky"),   # stride-2 dX: persistent, 1-2 tiles per WG
+    (2, 32, 36, 136, 128, 3, 2, 1, False, "relu"),   # stride-2 dX: persistent, 8 chunks per tile
 ]
 
 
@@ -117,7 +119,8 @@ def test_conv_block_backward_parity(case):
 
 @pytest.mark.parametrize("case", [CONV_CASES[0], CONV_CASES[1], CONV_CASES[3], CONV_CASES[5],
                                   CONV_CASES[6], CONV_CASES[12], CONV_CASES[13], CONV_CASES[17],
-                                  CONV_CASES[18], CONV_CASES[22], CONV_CASES[26]])
+                                  CONV_CASES[18], CONV_CASES[22], CONV_CASES[26],
+                                  CONV_CASES[-2]])
 def test_conv_block_accumulate_inplace_and_no_dx(case):
     torch = require_gpu()
     announce(f"conv_block accumulate/in-place {case}")
