@@ -30,7 +30,9 @@ _lock = threading.Lock()
 _lib = None
 
 ACT_LINEAR, ACT_LEAKY, ACT_LOGISTIC, ACT_RELU = 0, 1, 2, 3
-ACT_NAMES = {"linear": ACT_LINEAR, "leaky": ACT_LEAKY, "logistic": ACT_LOGISTIC, "relu": ACT_RELU}
+ACT_NAMES = {"linear": ACT_LINEAR, "leaky": ACT_LEAKY, "logistic": ACT_LOGISTIC, "relu": ACT_RELU,
+             "tanh": 4, "elu": 5, "selu": 6, "plse": 7, "lhtan": 8, "hardtan": 9, "stair": 10,
+             "ramp": 11, "relie": 12, "loggy": 13}
 
 
 def build(force: bool = False) -> str:

@@ -37,6 +37,16 @@
 #define ORC_ACT_LEAKY 1
 #define ORC_ACT_LOGISTIC 2
 #define ORC_ACT_RELU 3
+#define ORC_ACT_TANH 4
+#define ORC_ACT_ELU 5
+#define ORC_ACT_SELU 6
+#define ORC_ACT_PLSE 7
+#define ORC_ACT_LHTAN 8
+#define ORC_ACT_HARDTAN 9
+#define ORC_ACT_STAIR 10
+#define ORC_ACT_RAMP 11
+#define ORC_ACT_RELIE 12
+#define ORC_ACT_LOGGY 13
 
 int orc_version(void) { return 1; }
 
@@ -51,28 +61,71 @@ int orc_num_threads(void) { return 1; }
 /* activations                                                         */
 /* ------------------------------------------------------------------ */
 
-/* Forward activations used to build saved tensors: [P1] section 7 defines
- * linear x, logistic 1/(1+e^-x), relu x*(x>0), leaky (x>0)?x:0.1x; the leaky
- * slope is a parameter here (0.1 in all pages' uses). */
+/* Forward activations used to build saved tensors, as the *_activate functions
+ * of [P1] section 7 define them: linear x, logistic 1/(1+e^-x), relu x*(x>0),
+ * leaky (x>0)?x:0.1x (the slope is a parameter here, 0.1 in all pages' uses);
+ * tanh (e^2x-1)/(e^2x+1) (written as tanh(), the same function without the
+ * overflow of e^2x); elu x for x>=0, e^x-1 below; selu 1.0507 x for x>=0,
+ * 1.0507*1.6732 (e^x-1) below; plse .01(x+4) below -4, .01(x-4)+1 above 4,
+ * .125x+.5 between; lhtan .001x below 0, .001(x-1)+1 above 1, x between;
+ * hardtan x clamped to [-1, 1]; stair with n = floor(x): floor(x/2) for even n,
+ * (x-n)+floor(x/2) for odd n; ramp x*(x>0)+.1x; relie x for x>0, .01x otherwise;
+ * loggy 2/(1+e^-x)-1. */
 static double act_fwd(int act, double slope, double u) {
   switch (act) {
     case ORC_ACT_LINEAR: return u;
     case ORC_ACT_LEAKY: return (u > 0) ? u : slope * u;
     case ORC_ACT_LOGISTIC: return 1.0 / (1.0 + exp(-u));
     case ORC_ACT_RELU: return (u > 0) ? u : 0.0;
+    case ORC_ACT_TANH: return tanh(u);
+    case ORC_ACT_ELU: return (u >= 0) ? u : exp(u) - 1.0;
+    case ORC_ACT_SELU: return (u >= 0) ? 1.0507 * u : 1.0507 * 1.6732 * (exp(u) - 1.0);
+    case ORC_ACT_PLSE:
+      if (u < -4) return .01 * (u + 4);
+      if (u > 4) return .01 * (u - 4) + 1;
+      return .125 * u + .5;
+    case ORC_ACT_LHTAN:
+      if (u < 0) return .001 * u;
+      if (u > 1) return .001 * (u - 1) + 1;
+      return u;
+    case ORC_ACT_HARDTAN: return (u < -1) ? -1.0 : ((u > 1) ? 1.0 : u);
+    case ORC_ACT_STAIR: {
+      const double n = floor(u);
+      if (fmod(n, 2.0) == 0) return floor(u / 2.);
+      return (u - n) + floor(u / 2.);
+    }
+    case ORC_ACT_RAMP: return u * (u > 0) + .1 * u;
+    case ORC_ACT_RELIE: return (u > 0) ? u : .01 * u;
+    case ORC_ACT_LOGGY: return 2. / (1. + exp(-u)) - 1;
   }
   return NAN;
 }
 
-/* Activation derivative evaluated on the OUTPUT y, as Darknet's gradient
- * functions do ([P1] section 7: leaky_gradient (x>0)?1:.1, logistic_gradient
- * (1-x)*x, linear_gradient 1, relu_gradient (x>0)). */
+/* Activation derivative evaluated on the OUTPUT y, as Darknet's *_gradient
+ * functions do ([P1] section 7): linear 1; leaky (y>0)?1:slope; logistic
+ * (1-y)y; relu (y>0); tanh 1-y^2; elu (y>=0) + (y<0)(y+1); selu (y>=0)1.0507 +
+ * (y<0)(y + 1.0507*1.6732); plse (y<0 || y>1) ? .01 : .125; lhtan (0<y<1) ? 1 :
+ * .001; hardtan (-1<y<1) ? 1 : 0; stair floor(y)==y ? 0 : 1; ramp (y>0) + .1;
+ * relie (y>0) ? 1 : .01; loggy 2(1-s)s with s = (y+1)/2. */
 static double act_grad(int act, double slope, double y) {
   switch (act) {
     case ORC_ACT_LINEAR: return 1.0;
     case ORC_ACT_LEAKY: return (y > 0) ? 1.0 : slope;
     case ORC_ACT_LOGISTIC: return (1.0 - y) * y;
     case ORC_ACT_RELU: return (y > 0) ? 1.0 : 0.0;
+    case ORC_ACT_TANH: return 1.0 - y * y;
+    case ORC_ACT_ELU: return (y >= 0) + (y < 0) * (y + 1.0);
+    case ORC_ACT_SELU: return (y >= 0) * 1.0507 + (y < 0) * (y + 1.0507 * 1.6732);
+    case ORC_ACT_PLSE: return (y < 0 || y > 1) ? .01 : .125;
+    case ORC_ACT_LHTAN: return (y > 0 && y < 1) ? 1.0 : .001;
+    case ORC_ACT_HARDTAN: return (y > -1 && y < 1) ? 1.0 : 0.0;
+    case ORC_ACT_STAIR: return (floor(y) == y) ? 0.0 : 1.0;
+    case ORC_ACT_RAMP: return (y > 0) + .1;
+    case ORC_ACT_RELIE: return (y > 0) ? 1.0 : .01;
+    case ORC_ACT_LOGGY: {
+      const double s = (y + 1.) / 2.;
+      return 2 * (1 - s) * s;
+    }
   }
   return NAN;
 }

@@ -50,6 +50,67 @@ def test_activation_backward_matches_autograd(act, slope):
     np.testing.assert_allclose(O.act_backward(act, slope, y, d), tu.grad.numpy(), rtol=0, atol=1e-14)
 
 
+# The other ten activations of Darknet's activation list.  Each forward is pinned to an
+# independent definition (a torch routine or a mathematical identity), each gradient to the
+# central finite difference of the forward away from its breakpoints.
+A = O.ACT_NAMES
+_F = torch.nn.functional
+_FWD_PINS = {
+    "tanh": lambda t: torch.tanh(t),
+    "elu": lambda t: _F.elu(t, alpha=1.0),
+    "selu": lambda t: 1.0507 * _F.elu(t, alpha=1.6732),
+    "hardtan": lambda t: _F.hardtanh(t, -1.0, 1.0),
+    "relie": lambda t: _F.leaky_relu(t, 0.01),
+    "ramp": lambda t: torch.relu(t) + 0.1 * t,
+    "loggy": lambda t: torch.tanh(t / 2),                 # 2*sigmoid(x)-1 == tanh(x/2)
+    # piecewise-linear ones: a min/max composition of their three pieces
+    "plse": lambda t: torch.maximum(torch.minimum(0.125 * t + 0.5, 0.01 * (t - 4) + 1), 0.01 * (t + 4)),
+    "lhtan": lambda t: torch.minimum(torch.maximum(0.001 * t, t), 0.001 * (t - 1) + 1),
+    # flat at k on [2k, 2k+1), rising from k to k+1 on [2k+1, 2k+2)
+    "stair": lambda t: torch.floor(t / 2) + torch.relu(t - 2 * torch.floor(t / 2) - 1),
+}
+_BREAKS = {"plse": [-4, 4], "lhtan": [0, 1], "hardtan": [-1, 1], "relie": [0], "ramp": [0],
+           "elu": [0], "selu": [0], "stair": list(range(-8, 9))}
+
+
+@pytest.mark.parametrize("name", sorted(_FWD_PINS))
+def test_extra_activation_forward_pins(name):
+    u = np.linspace(-7.3, 7.3, 2921)
+    y = O.act_forward(A[name], 0.0, u)
+    ref = _FWD_PINS[name](torch.tensor(u)).numpy()
+    np.testing.assert_allclose(y, ref, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("name", sorted(_FWD_PINS))
+def test_extra_activation_gradient_is_derivative_of_forward(name):
+    u = np.random.default_rng(7).uniform(-7, 7, 4000)
+    for b in _BREAKS.get(name, []):
+        u = u[np.abs(u - b) > 1e-3]
+    h = 1e-6
+    fd = (O.act_forward(A[name], 0, u + h) - O.act_forward(A[name], 0, u - h)) / (2 * h)
+    y = O.act_forward(A[name], 0.0, u)
+    d = np.random.default_rng(8).standard_normal(u.shape)
+    g = O.act_backward(A[name], 0.0, y, d)
+    np.testing.assert_allclose(g, d * fd, rtol=1e-6, atol=1e-8)
+
+
+def test_extra_activation_gradients_at_page_breakpoints():
+    """Values the gradient functions take at and around their thresholds, read from the output."""
+    one = np.ones(5)
+    g = lambda n, y: O.act_backward(A[n], 0.0, np.array(y, dtype=np.float64), one[:len(y)])
+    np.testing.assert_array_equal(g("plse", [-0.5, 0.0, 0.5, 1.0, 1.5]), [.01, .125, .125, .125, .01])
+    np.testing.assert_array_equal(g("lhtan", [-0.5, 0.0, 0.5, 1.0, 1.5]), [.001, .001, 1, .001, .001])
+    np.testing.assert_array_equal(g("hardtan", [-1.0, -0.5, 0.5, 1.0]), [0, 1, 1, 0])
+    np.testing.assert_array_equal(g("stair", [-1.0, -0.5, 0.0, 2.0, 2.25]), [0, 1, 0, 0, 1])
+    np.testing.assert_array_equal(g("ramp", [-1.0, 0.0, 1.0]), [.1, .1, 1.1])
+    np.testing.assert_array_equal(g("relie", [-1.0, 0.0, 1.0]), [.01, .01, 1])
+    np.testing.assert_array_equal(g("elu", [-0.5, 0.0, 2.0]), [0.5, 1, 1])
+    np.testing.assert_allclose(g("selu", [-0.5, 0.0, 2.0]), [1.0507 * 1.6732 - 0.5, 1.0507, 1.0507],
+                               rtol=0, atol=1e-15)
+    np.testing.assert_allclose(g("loggy", [-1.0, 0.0, 1.0]), [0, 0.5, 0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(g("tanh", [-1.0, 0.0, 0.5]), [0, 1, 0.75], rtol=0, atol=1e-15)
+
+
 # ----------------------------------------------------------------------------- batch norm
 def _bn_case(seed, shape, gamma_scale=1.0):
     z = _rand(seed, *shape) * 2.0 + 0.3
