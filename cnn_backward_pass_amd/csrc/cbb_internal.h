@@ -206,11 +206,30 @@ __device__ __forceinline__ int xcd_remap(int phys, int n) {
   return xcd * per + min(xcd, rem) + k;
 }
 
+// LDS address of a shared-memory float, as the direct global-to-LDS copy builtin
+// takes it (the copy of a wave fills 64 consecutive 4- or 16-byte slots from there).
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(float* p) {
+  return (__attribute__((address_space(3))) void*)p;
+}
+
 // Row / column of accumulator register r of lane `lane` inside a wave's 32x32 block.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 __device__ __forceinline__ int acc_col(int lane) { return lane & 31; }
 
 // Kernel launchers (host), one per translation unit's kernels ------------------
+// Split-K partial sums are added in groups of this many, in a fixed order.
+constexpr int kReduceGroup = 32;
+// dw += the ordered sum of `splits` partial weight gradients in ws ([split][o][i][tap],
+// or tap-major [split][tap][o][i] when tapmajor); two levels when groups > 0.
+int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
+                     int tapmajor, hipStream_t st);
+// 1x1 stride-1 gradients with direct global-to-LDS staging (16-byte aligned operands).
+bool conv1x1_dma_ok(const ConvGeom& g, const void* a, const void* b);
+size_t conv1x1_dw_workspace(const ConvGeom& g);
+int launch_conv1x1_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
+                      hipStream_t st);
+int launch_conv1x1_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx,
+                      int accumulate, hipStream_t st);
 ConvGeom make_geom(const cbb_conv_desc& d);
 size_t conv_dw_workspace(const ConvGeom& g);
 int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,

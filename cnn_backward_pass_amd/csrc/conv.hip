@@ -140,7 +140,6 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
 // consecutive elements into part2[g][e].  Level 2: dw[e] += sum over g (or over
 // the splits directly) in index order.  Every output element is summed by one
 // thread in a fixed order, so the result does not depend on scheduling.
-constexpr int kReduceGroup = 32;
 
 // part[s0*mn + e] + ... + part[(s1-1)*mn + e] (s1 - s0 <= kReduceGroup), added in
 // index order; all the loads are issued before the first add.
@@ -183,183 +182,6 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_l2(float* __restrict__ dw,
     d = ((int64_t)o * c + i) * kk + t;
   }
   dw[d] += s;
-}
-
-// ---------------------------------------------------------------------------
-// 1x1 stride-1 convolutions are plain batched GEMMs over the pixels q = (n, p):
-//   dW[o][i] = sum_q dz[n][o][p] * x[n][i][p]          (M = o, N = i, K = q)
-//   dx[n][i][p] = sum_o W[o][i] * dz[n][o][p]          (M = i, N = q, K = o)
-// Both operands are contiguous along the GEMM's K (dW) or N (dX) index, so the
-// tiles are staged with 16-byte loads (H*W and C_in are multiples of 4, so a
-// 4-pixel group never straddles two images).  Same tile core and ordered split
-// reduction as conv_dw_kernel.
-// ---------------------------------------------------------------------------
-typedef float f4v __attribute__((ext_vector_type(4)));
-
-template <class TS>
-__global__ __launch_bounds__(kThreads) void conv1x1_dw_kernel(ConvGeom g, const float* __restrict__ x,
-                                                              const float* __restrict__ dz,
-                                                              float* __restrict__ out,
-                                                              int64_t k_chunk, int tiles_n,
-                                                              int nsplits, int direct) {
-  static_assert(TS::BK == 32 && TS::BM * 8 % kThreads == 0 && TS::BN * 8 % kThreads == 0, "");
-  __shared__ float lds[TS::LDS_FLOATS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
-  const int tiles = gridDim.x / nsplits;
-  const int split = blockIdx.x / tiles, tile = blockIdx.x - split * tiles;
-  const int m0 = (tile / tiles_n) * TS::BM, n0 = (tile % tiles_n) * TS::BN;
-  const int64_t kbeg = (int64_t)split * k_chunk;
-  const int64_t kend = min(g.Q, kbeg + k_chunk);
-  constexpr int AV = TS::BM * 8 / kThreads, BV = TS::BN * 8 / kThreads;  // float4 per thread
-  f4v ra[AV], rb[BV];
-  uint32_t am = 0, bm = 0;
-  auto load = [&](int64_t k0) {
-    am = 0;
-    bm = 0;
-#pragma unroll
-    for (int r = 0; r < AV; ++r) {
-      const int f = tid + kThreads * r, ml = f >> 3, q4 = f & 7;
-      const int64_t q = k0 + 4 * q4;
-      const int n = (int)(q / g.HW), pix = (int)(q - (int64_t)n * g.HW);
-      const int o = m0 + ml;
-      const bool ok = q < kend && o < g.OC;
-      ra[r] = *(const f4v*)(dz + (ok ? ((int64_t)n * g.OC + o) * g.HW + pix : 0));
-      am |= (uint32_t)ok << r;
-    }
-#pragma unroll
-    for (int r = 0; r < BV; ++r) {
-      const int f = tid + kThreads * r, nl = f >> 3, q4 = f & 7;
-      const int64_t q = k0 + 4 * q4;
-      const int n = (int)(q / g.HW), pix = (int)(q - (int64_t)n * g.HW);
-      const int i = n0 + nl;
-      const bool ok = q < kend && i < g.C;
-      rb[r] = *(const f4v*)(x + (ok ? ((int64_t)n * g.C + i) * g.HW + pix : 0));
-      bm |= (uint32_t)ok << r;
-    }
-  };
-  auto store = [&](float* buf) {
-    float* As = buf;
-    float* Bs = buf + TS::BK * TS::LDA;
-#pragma unroll
-    for (int r = 0; r < AV; ++r) {
-      const int f = tid + kThreads * r, ml = f >> 3, q4 = f & 7;
-      const bool ok = (am >> r) & 1u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) As[(4 * q4 + e) * TS::LDA + ml] = ok ? ra[r][e] : 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < BV; ++r) {
-      const int f = tid + kThreads * r, nl = f >> 3, q4 = f & 7;
-      const bool ok = (bm >> r) & 1u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Bs[(4 * q4 + e) * TS::LDB + nl] = ok ? rb[r][e] : 0.f;
-    }
-  };
-  Acc<TS> acc;
-  acc.zero();
-  gemm_mainloop<TS>(lds, kbeg, kend, load, store, acc, wm, wn, wk, lane);
-  reduce_wk<TS>(acc, lds, wm, wn, wk, lane);
-  if (wk != 0) return;
-  float* dst = direct ? out : out + (int64_t)split * g.OC * g.J;
-#pragma unroll
-  for (int ai = 0; ai < TS::RM; ++ai)
-#pragma unroll
-    for (int aj = 0; aj < TS::RN; ++aj) {
-      const int i = n0 + acc_n0<TS>(wn, aj) + acc_col(lane);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int o = m0 + acc_m0<TS>(wm, ai) + acc_row(r, lane);
-        if (o < g.OC && i < g.C) {
-          const int64_t e = (int64_t)o * g.J + i;
-          if (direct)
-            dst[e] += acc.v[ai][aj][r];
-          else
-            dst[e] = acc.v[ai][aj][r];
-        }
-      }
-    }
-}
-
-template <class TS>
-__global__ __launch_bounds__(kThreads) void conv1x1_dx_kernel(ConvGeom g, const float* __restrict__ wt,
-                                                              const float* __restrict__ dz,
-                                                              float* __restrict__ dx, int ctiles,
-                                                              int accumulate) {
-  static_assert(TS::BK == 32 && TS::BM * 8 % kThreads == 0 && TS::BN * 8 % kThreads == 0, "");
-  __shared__ float lds[TS::LDS_FLOATS];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
-  const int ctile = blockIdx.x % ctiles, ptile = blockIdx.x / ctiles;
-  const int m0 = ctile * TS::BM;
-  const int64_t q0 = (int64_t)ptile * TS::BN;
-  constexpr int AV = TS::BM * 8 / kThreads, BV = TS::BN * 8 / kThreads;
-  constexpr int A4 = TS::BM / 4, B4 = TS::BN / 4;  // float4 per K row
-  f4v ra[AV], rb[BV];
-  uint32_t am = 0, bm = 0;
-  auto load = [&](int64_t k0) {
-    am = 0;
-    bm = 0;
-#pragma unroll
-    for (int r = 0; r < AV; ++r) {  // A[i][o] = W[o][i]: 16-byte groups along i
-      const int f = tid + kThreads * r, kl = f / A4, c4 = f % A4;
-      const int o = (int)k0 + kl, i = m0 + 4 * c4;
-      const bool ok = o < g.OC && i < g.C;
-      ra[r] = *(const f4v*)(wt + (ok ? (int64_t)o * g.C + i : 0));
-      am |= (uint32_t)ok << r;
-    }
-#pragma unroll
-    for (int r = 0; r < BV; ++r) {  // B[o][q] = dz[n][o][p]: 16-byte groups along q
-      const int f = tid + kThreads * r, kl = f / B4, q4 = f % B4;
-      const int o = (int)k0 + kl;
-      const int64_t q = q0 + 4 * q4;
-      const int n = (int)(q / g.HW), pix = (int)(q - (int64_t)n * g.HW);
-      const bool ok = o < g.OC && q < g.Q;
-      rb[r] = *(const f4v*)(dz + (ok ? ((int64_t)n * g.OC + o) * g.HW + pix : 0));
-      bm |= (uint32_t)ok << r;
-    }
-  };
-  auto store = [&](float* buf) {
-    float* As = buf;
-    float* Bs = buf + TS::BK * TS::LDA;
-#pragma unroll
-    for (int r = 0; r < AV; ++r) {
-      const int f = tid + kThreads * r, kl = f / A4, c4 = f % A4;
-      const bool ok = (am >> r) & 1u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) As[kl * TS::LDA + 4 * c4 + e] = ok ? ra[r][e] : 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < BV; ++r) {
-      const int f = tid + kThreads * r, kl = f / B4, q4 = f % B4;
-      const bool ok = (bm >> r) & 1u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Bs[kl * TS::LDB + 4 * q4 + e] = ok ? rb[r][e] : 0.f;
-    }
-  };
-  Acc<TS> acc;
-  acc.zero();
-  gemm_mainloop<TS>(lds, 0, g.OC, load, store, acc, wm, wn, wk, lane);
-  reduce_wk<TS>(acc, lds, wm, wn, wk, lane);
-  if (wk != 0) return;
-#pragma unroll
-  for (int aj = 0; aj < TS::RN; ++aj) {
-    const int64_t q = q0 + acc_n0<TS>(wn, aj) + acc_col(lane);
-    if (q >= g.Q) continue;
-    const int n = (int)(q / g.HW), pix = (int)(q - (int64_t)n * g.HW);
-    float* base = dx + (int64_t)n * g.C * g.HW + pix;
-#pragma unroll
-    for (int ai = 0; ai < TS::RM; ++ai)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = m0 + acc_m0<TS>(wm, ai) + acc_row(r, lane);
-        if (i < g.C) {
-          float* d = base + (int64_t)i * g.HW;
-          const float v = acc.v[ai][aj][r];
-          *d = accumulate ? *d + v : v;
-        }
-      }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -812,9 +634,6 @@ static bool dx3_s1_fits(int W, int F, int zplane) {
 // Source of the zero padding staged by the LDS-DMA loads (never written).
 __device__ float g_dx3_zero[4];
 
-__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(float* p) {
-  return (__attribute__((address_space(3))) void*)p;
-}
 
 // DMA = true stages each chunk with direct global-to-LDS loads into one of two
 // LDS buffers (the next chunk lands while the matrix cores work on this one;
@@ -1837,7 +1656,9 @@ static bool conv1x1_ok(const ConvGeom& g) {
 static DwPlan plan_dw(const ConvGeom& g) {
   DwPlan best{};
   if (plan_dw3_rows(g, best)) return best;
-  if (conv1x1_ok(g)) {  // 64x64 tiles of (o, i), 16-byte staging
+  // 1x1: conv1x1_dw_dma when the tensors are 16-byte aligned (it has its own plan and
+  // workspace, conv1x1_dw_workspace); otherwise the general kernel on these 64x64 tiles
+  if (conv1x1_ok(g)) {
     best.conv1x1 = 1;
     best.shape = DW_64x64;
     best.bm = best.bn = 64;
@@ -1846,7 +1667,7 @@ static DwPlan plan_dw(const ConvGeom& g) {
     best.tiles_n = (int)ceil_div(g.J, 64);
     const int64_t tiles = (int64_t)best.tiles_m * best.tiles_n;
     const int64_t ktiles = ceil_div(g.Q, 32);
-    int64_t splits = ceil_div(512, tiles);  // measured best for the 1x1 layers
+    int64_t splits = ceil_div(512, tiles);
     splits = std::min<int64_t>(splits, std::max<int64_t>(1, ktiles / 4));
     splits = std::max<int64_t>(1, std::min<int64_t>(splits, 4096));
     const int64_t chunk = ceil_div(ktiles, splits) * 32;
@@ -1922,8 +1743,6 @@ size_t conv_fused_workspace(const ConvGeom& g) {
   return ((size_t)p.wgs + p.groups) * g.OC * g.J * sizeof(float);
 }
 
-static int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
-                            int tapmajor, hipStream_t st);
 
 int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
                            float* dw, float* dx, int accumulate, float* ws, hipStream_t st) {
@@ -1948,9 +1767,10 @@ int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, c
 
 size_t conv_dw_workspace(const ConvGeom& g) {
   const DwPlan p = plan_dw(g);
-  if (p.splits == 1) return 0;
+  const size_t c1 = p.conv1x1 ? conv1x1_dw_workspace(g) : 0;
+  if (p.splits == 1) return c1;
   const size_t mn = (size_t)g.OC * g.J;
-  return ((size_t)p.splits + p.groups) * mn * sizeof(float);
+  return std::max(c1, ((size_t)p.splits + p.groups) * mn * sizeof(float));
 }
 
 template <class TS>
@@ -1996,17 +1816,11 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
   const DwPlan p = plan_dw(g);
   const int direct = p.splits == 1;
   float* out = direct ? dw : ws;
+  if (p.conv1x1 && conv1x1_dma_ok(g, x, dz)) return launch_conv1x1_dw(g, x, dz, dw, ws, st);
   if (p.conv1x1) {
-    // 16-byte staging needs 16-byte aligned tensors; otherwise the general kernel
-    // runs the same tiles and splits (same partial layout and workspace)
-    using TS = TileShape<2, 2, 1>;
-    const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n * p.splits);
-    if (aligned16(x) && aligned16(dz))
-      conv1x1_dw_kernel<TS><<<blocks, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk, p.tiles_n,
-                                                         p.splits, direct);
-    else
-      conv_dw_kernel<TS><<<blocks, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk, p.tiles_n,
-                                                      p.splits, direct);
+    // the direct copies need 16-byte aligned tensors; otherwise the general kernel
+    // runs 64 x 64 tiles with the same split over K
+    launch_dw_tile<TileShape<2, 2, 1>>(g, p, x, dz, out, direct, st);
   } else if (p.rows_tc > 0) {
     if (g.S == 1)
       launch_dw3_rows<1>(g, p, x, dz, out, direct, st);
@@ -2022,15 +1836,14 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
     case DW_64x128: launch_dw_tile<TileShape<2, 2, 1, 1, 1, 2>>(g, p, x, dz, out, direct, st); break;
     default: launch_dw_tile<TileShape<2, 2, 1, 1, 2, 2>>(g, p, x, dz, out, direct, st); break;
   }
-  int rc = check_launch(p.conv1x1 ? "conv1x1_dw_kernel"
-                                  : p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel");
+  int rc = check_launch(p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel");
   if (rc != CBB_OK || direct) return rc;
   return launch_dw_reduce(g, dw, ws, p.splits, p.groups, p.rows_tc > 0, st);
 }
 
 // dw += ordered sum of the `splits` partials in ws (two levels when groups > 0).
-static int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
-                            int tapmajor, hipStream_t st) {
+int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
+                     int tapmajor, hipStream_t st) {
   const int64_t mn = (int64_t)g.OC * g.J;
   const unsigned eblocks = (unsigned)ceil_div(mn, kThreads);
   const int kk = tapmajor ? g.K * g.K : 0;
@@ -2218,14 +2031,10 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
     return check_launch("dx_splitk_reduce");
   }
   if (p.kind == DX_1X1) {
-    if (!(aligned16(wt) && aligned16(dz))) {  // same tiles, no split: the general kernel
-      launch_dx_mfma<TileShape<2, 2, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
-      return check_launch("conv_dx_kernel");
-    }
-    const unsigned blocks = (unsigned)((int64_t)p.ctiles * p.pixtiles);
-    conv1x1_dx_kernel<TileShape<2, 2, 1>><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, p.ctiles,
-                                                                        accumulate);
-    return check_launch("conv1x1_dx_kernel");
+    if (conv1x1_dma_ok(g, wt, dz)) return launch_conv1x1_dx(g, wt, dz, dx, accumulate, st);
+    // misaligned tensors: the general kernel on 64 x 64 tiles, no split
+    launch_dx_mfma<TileShape<2, 2, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
+    return check_launch("conv_dx_kernel");
   }
   if (p.kind == DX_SMALLC) {
     switch (g.C) {

@@ -57,6 +57,8 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (1, 32, 5, 208, 64, 3, 1, 1, False, "linear"),   # dW row-streaming: 104-wide strips, stride 1
     (2, 64, 12, 12, 96, 1, 1, 0, True, "leaky"),     # 1x1 GEMMs with 16-byte staging, ragged o
     (3, 20, 6, 10, 70, 1, 1, 0, False, "linear"),    # 1x1 GEMMs: ragged i and o tiles
+    (4, 32, 64, 64, 48, 1, 1, 0, True, "leaky"),     # 1x1 dW: 64 K splits, two-level sum
+    (2, 128, 26, 26, 255, 1, 1, 0, False, "linear"), # 1x1: 255 output channels (ragged K of dX)
     (2, 64, 40, 31, 24, 3, 1, 1, True, "leaky"),     # dX: 128-pixel tile-direct, ragged plane
     (2, 3, 24, 40, 32, 3, 1, 1, True, "logistic"),   # first layer, logistic
     (1, 2, 17, 36, 12, 3, 1, 1, False, "relu"),      # first layer, bias only
@@ -119,7 +121,8 @@ def test_conv_block_backward_parity(case):
 
 @pytest.mark.parametrize("case", [CONV_CASES[0], CONV_CASES[1], CONV_CASES[3], CONV_CASES[5],
                                   CONV_CASES[6], CONV_CASES[12], CONV_CASES[13], CONV_CASES[17],
-                                  CONV_CASES[18], CONV_CASES[22], CONV_CASES[26],
+                                  CONV_CASES[18], CONV_CASES[22], CONV_CASES[26], CONV_CASES[33],
+                                  CONV_CASES[35],
                                   CONV_CASES[-2]])
 def test_conv_block_accumulate_inplace_and_no_dx(case):
     torch = require_gpu()
