@@ -61,6 +61,8 @@ _SIGS = {
     "orc_act_backward": ([_i, _d, _D, _D, _D, _l], None),
     "orc_bn_forward": ([_i, _i, _l, _d, _D, _D, _D, _D, _D, _D, _D], None),
     "orc_bn_backward": ([_i, _i, _l, _d, _D, _D, _D, _D, _D, _D, _D], None),
+    "orc_bn_forward_fixed": ([_i, _i, _l, _d, _D, _D, _D, _D, _D, _D, _D], None),
+    "orc_bn_backward_fixed": ([_i, _i, _l, _d, _D, _D, _D, _D, _D, _D, _D], None),
     "orc_conv_out_dim": ([_i, _i, _i, _i], _i),
     "orc_conv_forward": ([_i] * 8 + [_D, _D, _D, _D], None),
     "orc_conv_backward_weights": ([_i] * 8 + [_D, _D, _D], None),
@@ -162,6 +164,32 @@ def bn_backward(g, xhat, var, gamma, eps: float, dgamma=None, dbeta=None):
     dz = np.empty_like(g)
     lib().orc_bn_backward(n, c, hw, eps, _p(g), _p(xhat), _p(var), _p(gamma), _p(dz), _p(dgamma),
                           _p(dbeta))
+    return dz, dgamma, dbeta
+
+
+def bn_forward_fixed(z, mean, var, gamma, beta, eps: float):
+    """BN with fixed (stored) statistics; returns xhat, u."""
+    z = _f64(z)
+    n, c = z.shape[0], z.shape[1]
+    hw = int(np.prod(z.shape[2:])) if z.ndim > 2 else 1
+    mean, var, gamma, beta = _f64(mean), _f64(var), _f64(gamma), _f64(beta)
+    xhat, u = np.empty_like(z), np.empty_like(z)
+    lib().orc_bn_forward_fixed(n, c, hw, eps, _p(z), _p(mean), _p(var), _p(gamma), _p(beta),
+                               _p(xhat), _p(u))
+    return xhat, u
+
+
+def bn_backward_fixed(g, xhat, var, gamma, eps: float, dgamma=None, dbeta=None):
+    """BN backward with fixed statistics; returns dz, dgamma (+=), dbeta (+=)."""
+    g, xhat = _f64(g), _f64(xhat)
+    n, c = g.shape[0], g.shape[1]
+    hw = int(np.prod(g.shape[2:])) if g.ndim > 2 else 1
+    var, gamma = _f64(var), _f64(gamma)
+    dgamma = np.zeros(c) if dgamma is None else _f64(dgamma).copy()
+    dbeta = np.zeros(c) if dbeta is None else _f64(dbeta).copy()
+    dz = np.empty_like(g)
+    lib().orc_bn_backward_fixed(n, c, hw, eps, _p(g), _p(xhat), _p(var), _p(gamma), _p(dz),
+                                _p(dgamma), _p(dbeta))
     return dz, dgamma, dbeta
 
 

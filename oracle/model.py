@@ -19,7 +19,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (ACT_NAMES, act_backward, act_forward, bn_backward, bn_forward, conv_backward_bias,
+from . import (ACT_NAMES, act_backward, act_forward, bn_backward, bn_backward_fixed, bn_forward,
+               bn_forward_fixed, conv_backward_bias,
                conv_backward_data, conv_backward_weights, conv_forward, fc_backward, fc_forward,
                maxpool_backward, maxpool_forward, route_backward, shortcut_backward,
                softmax_forward, softmax_loss_backward, upsample_backward, upsample_forward)
@@ -32,12 +33,18 @@ def _f64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
 
 
-def conv_block_forward(layer, x, w, bias=None, gamma=None, beta=None, eps=EPS, slope=SLOPE):
-    """Forward of one conv block; returns the tensors its backward reads (and more)."""
+def conv_block_forward(layer, x, w, bias=None, gamma=None, beta=None, eps=EPS, slope=SLOPE,
+                       mean=None, var=None):
+    """Forward of one conv block; returns the tensors its backward reads (and more).
+    layer.bn: 0 none, 1 (or True) batch statistics, 2 the fixed statistics mean, var."""
     act = ACT_NAMES[layer.act]
     z = conv_forward(x, w, layer.stride, layer.pad, bias=None if layer.bn else bias)
     out = {"x_in": _f64(x), "w": _f64(w), "z": z}
-    if layer.bn:
+    if layer.bn == 2:
+        xhat, u = bn_forward_fixed(z, mean, var, gamma, beta, eps)
+        out.update(mean=_f64(mean), var=_f64(var), xhat=xhat, gamma=_f64(gamma),
+                   beta=_f64(beta))
+    elif layer.bn:
         mean, var, xhat, u = bn_forward(z, gamma, beta, eps)
         out.update(mean=mean, var=var, xhat=xhat, gamma=_f64(gamma), beta=_f64(beta))
     else:
@@ -59,7 +66,8 @@ def conv_block_backward(layer, saved, delta, want_dx=True, dx_init=None, eps=EPS
     g = act_backward(act, slope, saved["y"], delta)
     res = {"g": g}
     if layer.bn:
-        dz, dgamma, dbeta = bn_backward(g, saved["xhat"], saved["var"], saved["gamma"], eps)
+        bwd = bn_backward_fixed if layer.bn == 2 else bn_backward
+        dz, dgamma, dbeta = bwd(g, saved["xhat"], saved["var"], saved["gamma"], eps)
         res.update(dz=dz, db=dbeta, dgamma=dgamma)
     else:
         dz = g

@@ -216,6 +216,50 @@ void orc_bn_backward(int n, int c, long hw, double eps, const double* g, const d
   }
 }
 
+/* Forward with fixed (stored) statistics: xhat = (z - mean)/sqrt(var + eps)
+ * with the given mean and variance, u = gamma*xhat + beta (normalize_cpu with
+ * the rolling mean and variance when not training, [P1] section 4; Caffe's
+ * use_global_stats, [P5] Forward_cpu). */
+void orc_bn_forward_fixed(int n, int c, long hw, double eps, const double* z, const double* mean,
+                          const double* var, const double* gamma, const double* beta,
+                          double* xhat, double* u) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int ch = 0; ch < c; ++ch) {
+    const double inv = 1.0 / sqrt(var[ch] + eps);
+    for (int b = 0; b < n; ++b)
+      for (long i = 0; i < hw; ++i) {
+        const long idx = ((long)b * c + ch) * hw + i;
+        xhat[idx] = (z[idx] - mean[ch]) * inv;
+        u[idx] = gamma[ch] * xhat[idx] + beta[ch];
+      }
+  }
+}
+
+/* Backward with fixed statistics from g = dL/du.  The mean and variance do not
+ * depend on z, so u is affine in z per channel.  backward_bias and
+ * backward_scale_cpu as in training ([P1] section 4), scale_bias by gamma, then
+ * Caffe's use_global_stats branch of Backward_cpu ([P5]), which divides the top
+ * gradient by sqrt(var + eps):
+ *   dbeta += sum g;  dgamma += sum g*xhat;  dz = gamma*g / sqrt(var + eps). */
+void orc_bn_backward_fixed(int n, int c, long hw, double eps, const double* g, const double* xhat,
+                           const double* var, const double* gamma, double* dz, double* dgamma,
+                           double* dbeta) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int ch = 0; ch < c; ++ch) {
+    double sg = 0.0, sgx = 0.0;
+    const double sd = sqrt(var[ch] + eps);
+    for (int b = 0; b < n; ++b)
+      for (long i = 0; i < hw; ++i) {
+        const long idx = ((long)b * c + ch) * hw + i;
+        sg += g[idx];
+        sgx += g[idx] * xhat[idx];
+        dz[idx] = gamma[ch] * g[idx] / sd;
+      }
+    dbeta[ch] += sg;
+    dgamma[ch] += sgx;
+  }
+}
+
 /* ------------------------------------------------------------------ */
 /* convolution                                                         */
 /* ------------------------------------------------------------------ */

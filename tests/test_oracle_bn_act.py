@@ -219,3 +219,64 @@ def test_bn_parameter_gradients_accumulate():
     _, dg2, db2 = O.bn_backward(g, xhat, var, gamma, EPS, dgamma=dg1, dbeta=db1)
     np.testing.assert_allclose(dg2, 2 * dg1, rtol=1e-15)
     np.testing.assert_allclose(db2, 2 * db1, rtol=1e-15)
+
+
+# ----------------------------------------------------------------------------- fixed statistics
+def _fixed_stats(seed, c):
+    r = np.random.default_rng(seed)
+    return r.normal(size=c), r.uniform(0.3, 3.0, size=c)
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 4, 4), (4, 5, 3, 7), (8, 3, 1, 1)])
+def test_bn_fixed_statistics_match_autograd(shape):
+    """Forward and backward with stored statistics against float64 autograd of torch's
+    batch_norm in evaluation mode (running mean and variance, no batch statistics)."""
+    z, gamma, beta = _bn_case(21, shape)
+    mean, var = _fixed_stats(22, shape[1])
+    xhat, u = O.bn_forward_fixed(z, mean, var, gamma, beta, EPS)
+    tz = torch.tensor(z, requires_grad=True)
+    tg = torch.tensor(gamma, requires_grad=True)
+    tb = torch.tensor(beta, requires_grad=True)
+    tu = torch.nn.functional.batch_norm(tz, torch.tensor(mean), torch.tensor(var), tg, tb,
+                                        training=False, eps=EPS)
+    np.testing.assert_allclose(u, tu.detach().numpy(), rtol=0, atol=1e-12)
+    g = _rand(23, *shape)
+    tu.backward(torch.tensor(g))
+    dz, dgamma, dbeta = O.bn_backward_fixed(g, xhat, var, gamma, EPS)
+    np.testing.assert_allclose(dz, tz.grad.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dgamma, tg.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dbeta, tb.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_bn_fixed_statistics_finite_differences_and_caffe_form():
+    """Central differences of the fixed-statistics forward; with gamma = 1 the input
+    gradient is Caffe's use_global_stats branch: the top gradient divided by
+    sqrt(var + eps) (a division, as the code on the BatchNorm page does)."""
+    shape = (2, 2, 3, 3)
+    z, gamma, beta = _bn_case(24, shape)
+    mean, var = _fixed_stats(25, shape[1])
+    g = _rand(26, *shape)
+
+    def loss(zz, gg, bb):
+        return float(np.sum(O.bn_forward_fixed(zz, mean, var, gg, bb, EPS)[1] * g))
+
+    xhat, _ = O.bn_forward_fixed(z, mean, var, gamma, beta, EPS)
+    dz, dgamma, dbeta = O.bn_backward_fixed(g, xhat, var, gamma, EPS)
+    h = 1e-6
+    for idx in np.ndindex(*shape):
+        zp, zm = z.copy(), z.copy()
+        zp[idx] += h
+        zm[idx] -= h
+        assert (loss(zp, gamma, beta) - loss(zm, gamma, beta)) / (2 * h) == \
+            pytest.approx(dz[idx], rel=1e-6, abs=1e-8)
+    for ch in range(shape[1]):
+        gp, gm = gamma.copy(), gamma.copy()
+        gp[ch] += h
+        gm[ch] -= h
+        assert (loss(z, gp, beta) - loss(z, gm, beta)) / (2 * h) == pytest.approx(dgamma[ch], rel=1e-6)
+        bp, bm = beta.copy(), beta.copy()
+        bp[ch] += h
+        bm[ch] -= h
+        assert (loss(z, gamma, bp) - loss(z, gamma, bm)) / (2 * h) == pytest.approx(dbeta[ch], rel=1e-6)
+    dz1, _, _ = O.bn_backward_fixed(g, xhat, var, np.ones(shape[1]), EPS)
+    np.testing.assert_allclose(dz1, g / np.sqrt(var + EPS)[None, :, None, None], rtol=1e-15)
