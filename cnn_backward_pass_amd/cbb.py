@@ -17,7 +17,9 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcbb.so")
 
-ACT = {"linear": 0, "leaky": 1, "logistic": 2, "relu": 3}
+ACT = {"linear": 0, "leaky": 1, "logistic": 2, "relu": 3, "tanh": 4, "elu": 5, "selu": 6, "plse": 7,
+       "lhtan": 8, "hardtan": 9, "stair": 10, "ramp": 11, "relie": 12, "loggy": 13}
+BN_NONE, BN_BATCH, BN_FIXED = 0, 1, 2
 STATUS = {0: "CBB_OK", -1: "CBB_EINVAL", -2: "CBB_ESHAPE", -3: "CBB_EUNSUPPORTED",
           -4: "CBB_EWORKSPACE", -5: "CBB_EHIP"}
 WORKSPACE_ALIGN = 256
@@ -70,6 +72,7 @@ _SIGS = {
     "cbb_act_backward": ([_i32, _f, _P, _P, _P, _i64, _P], _i32),
     "cbb_bn_backward_workspace_size": ([_i32, _i32, _i64, ctypes.POINTER(_sz)], _i32),
     "cbb_bn_backward": ([_i32, _i32, _i64, _f] + [_P] * 7 + [_P, _sz, _P], _i32),
+    "cbb_bn_backward_fixed": ([_i32, _i32, _i64, _f] + [_P] * 7 + [_P, _sz, _P], _i32),
     "cbb_fc_backward": ([_i32, _i32, _i32] + [_P] * 6 + [_i32, _P], _i32),
     "cbb_softmax_loss_backward": ([_i32, _i32, _P, _P, _f, _P, _P, _P], _i32),
     "cbb_fc_softmax_backward": ([_i32, _i32, _i32, _P, _P, _f] + [_P] * 7 + [_P], _i32),
@@ -232,6 +235,17 @@ def bn_backward(g, x_norm, var, gamma, dz, dgamma, dbeta, eps: float = 1e-5, wor
     hw = g.numel() // (n * c)
     wsp, wsb = _ws(workspace)
     _check("cbb_bn_backward", lib().cbb_bn_backward(
+        n, c, hw, eps, _ptr(g, name="g"), _ptr(x_norm, name="x_norm"), _ptr(var, name="var"),
+        _ptr(gamma, name="gamma"), _ptr(dz, name="dz"), _ptr(dgamma, name="dgamma"),
+        _ptr(dbeta, name="dbeta"), wsp, wsb, _stream(stream)))
+
+
+def bn_backward_fixed(g, x_norm, var, gamma, dz, dgamma, dbeta, eps: float = 1e-5, workspace=None,
+                stream=None) -> None:
+    n, c = g.shape[0], g.shape[1]
+    hw = g.numel() // (n * c)
+    wsp, wsb = _ws(workspace)
+    _check("cbb_bn_backward_fixed", lib().cbb_bn_backward_fixed(
         n, c, hw, eps, _ptr(g, name="g"), _ptr(x_norm, name="x_norm"), _ptr(var, name="var"),
         _ptr(gamma, name="gamma"), _ptr(dz, name="dz"), _ptr(dgamma, name="dgamma"),
         _ptr(dbeta, name="dbeta"), wsp, wsb, _stream(stream)))

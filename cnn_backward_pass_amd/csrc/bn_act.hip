@@ -5,7 +5,7 @@
 //   section 3.1 gradient_array: g = delta * act'(y), act' read from the output;
 //   section 4 backward_batchnorm_layer: dbeta += sum g (backward_bias),
 //   dgamma += sum g*x_norm (backward_scale_cpu), then the input gradient;
-//   section 7: leaky (y>0 ? 1 : .1), logistic (1-y)y, linear 1, relu (y>0).
+//   section 7: the *_gradient functions of the fourteen activations.
 // "Understanding BatchNorm" (javaforall.cn): Caffe's closed form
 //   dz = (g' - mean(g') - mean(g' x_norm) x_norm) / sqrt(var + eps), g' = gamma g.
 //
@@ -22,14 +22,35 @@
 
 namespace cbb {
 
+// Activation derivative read from the activation output y, as Darknet's
+// *_gradient functions compute it ("YOLOv3 backpropagation", section 7).
 __device__ __forceinline__ float act_grad(int act, float slope, float y) {
   switch (act) {
     case CBB_ACT_LEAKY: return y > 0.f ? 1.f : slope;
     case CBB_ACT_LOGISTIC: return (1.f - y) * y;
     case CBB_ACT_RELU: return y > 0.f ? 1.f : 0.f;
+    case CBB_ACT_TANH: return 1.f - y * y;
+    case CBB_ACT_ELU: return y >= 0.f ? 1.f : y + 1.f;
+    case CBB_ACT_SELU: return y >= 0.f ? 1.0507f : y + 1.0507f * 1.6732f;
+    case CBB_ACT_PLSE: return (y < 0.f || y > 1.f) ? .01f : .125f;
+    case CBB_ACT_LHTAN: return (y > 0.f && y < 1.f) ? 1.f : .001f;
+    case CBB_ACT_HARDTAN: return (y > -1.f && y < 1.f) ? 1.f : 0.f;
+    case CBB_ACT_STAIR: return floorf(y) == y ? 0.f : 1.f;
+    case CBB_ACT_RAMP: return (y > 0.f ? 1.f : 0.f) + .1f;
+    case CBB_ACT_RELIE: return y > 0.f ? 1.f : .01f;
+    case CBB_ACT_LOGGY: {
+      const float s = (y + 1.f) * .5f;
+      return 2.f * (1.f - s) * s;
+    }
     default: return 1.f;
   }
 }
+
+// The streaming kernels take the activation as a template argument for the four
+// the networks use (no branch in the loop); kActAny takes it from `act_rt`.
+constexpr int kActAny = -1;
+// BN modes: none (bias sum), batch statistics, fixed statistics.
+constexpr int kBnNone = 0, kBnBatch = 1, kBnFixed = 2;
 
 // Work split of one channel: its N planes of HW floats are cut into `nseg`
 // segments.  Large planes (HW >= kPlaneSplit) are cut into `parts` equal ranges
@@ -103,17 +124,21 @@ __device__ __forceinline__ float4 ld4(const float* p) {
   return make_float4(v.x, v.y, v.z, v.w);
 }
 
-// ACT and HAS_X (BN) are compile-time so the streaming loop has no branches
-// around its loads.
-template <bool VEC, int ACT, bool HAS_X>
-__global__ __launch_bounds__(kThreads) void actbn_reduce(SegGeom s, const float* __restrict__ delta,
-                                                         const float* __restrict__ y,
-                                                         const float* __restrict__ xn,
-                                                         float slope, float2* __restrict__ part) {
+// Pass 1: per-segment sums of g and g*x_norm.  ACT and BN are compile-time so the
+// streaming loop has no branches around its loads.  With fixed statistics dz does
+// not depend on the sums, so this pass also writes dz = gamma/sqrt(var+eps) * g
+// and is the only streaming pass.
+template <bool VEC, int ACT, int BN>
+__global__ __launch_bounds__(kThreads) void actbn_reduce(
+    SegGeom s, const float* delta, const float* __restrict__ y, const float* __restrict__ xn,
+    float slope, int act_rt, const float* __restrict__ var, const float* __restrict__ gamma,
+    float eps, float* dz /* fixed statistics only; may alias delta */,
+    float2* __restrict__ part) {
   const int c = blockIdx.x / s.nseg, sg = blockIdx.x % s.nseg;
   float sg_ = 0.f, sgx = 0.f;
-  constexpr int act = ACT;
-  constexpr bool has_y = ACT != CBB_ACT_LINEAR, has_x = HAS_X;
+  const int act = ACT == kActAny ? act_rt : ACT;
+  constexpr bool has_y = ACT != CBB_ACT_LINEAR, has_x = BN != kBnNone, fixed = BN == kBnFixed;
+  const float ka = fixed ? gamma[c] / sqrtf(var[c] + eps) : 0.f;
   if constexpr (VEC) {
     for_segment<true>(s, c, sg, [&](int64_t o) {
       float4 d = ld4(delta + o);
@@ -129,6 +154,8 @@ __global__ __launch_bounds__(kThreads) void actbn_reduce(SegGeom s, const float*
         const float4 x = ld4(xn + o);
         sgx += (d.x * x.x + d.y * x.y) + (d.z * x.z + d.w * x.w);
       }
+      if (fixed)
+        *reinterpret_cast<float4*>(dz + o) = make_float4(ka * d.x, ka * d.y, ka * d.z, ka * d.w);
     });
   } else {
     for_segment<false>(s, c, sg, [&](int64_t o) {
@@ -136,6 +163,7 @@ __global__ __launch_bounds__(kThreads) void actbn_reduce(SegGeom s, const float*
       if (has_y) d *= act_grad(act, slope, y[o]);
       sg_ += d;
       if (has_x) sgx += d * xn[o];
+      if (fixed) dz[o] = ka * d;
     });
   }
   __shared__ float red[4];
@@ -161,15 +189,16 @@ __device__ __forceinline__ float2 fold_partials(const float2* __restrict__ part,
 // bn = 1: dz = a*g + b + cc*x_norm with a = gamma/sqrt(var+eps), b = -a*mean(g),
 //         cc = -a*mean(g*x_norm); dgamma[c] += sum g*x_norm, dbeta[c] += sum g.
 // bn = 0: dz = g (only launched when act != LINEAR), db[c] += sum g.
-template <bool VEC, int ACT, bool BN>
+template <bool VEC, int ACT, int BN>
 __global__ __launch_bounds__(kThreads) void actbn_apply(
     SegGeom s, const float* delta, const float* __restrict__ y,
-    const float* __restrict__ xn, float slope, const float2* __restrict__ part,
+    const float* __restrict__ xn, float slope, int act_rt, const float2* __restrict__ part,
     const float* __restrict__ var, const float* __restrict__ gamma, float eps,
     float* dz /* may alias delta */, float* __restrict__ dgamma, float* __restrict__ dbeta_or_db,
     int write_dz) {
-  constexpr int act = ACT;
-  constexpr bool bn = BN;
+  static_assert(BN != kBnFixed, "fixed statistics write dz in pass 1");
+  const int act = ACT == kActAny ? act_rt : ACT;
+  constexpr bool bn = BN == kBnBatch;
   const int c = blockIdx.x / s.nseg, sg = blockIdx.x % s.nseg;
   __shared__ float red[4];
   const float2 sums = fold_partials(part, c, s.nseg, red);
@@ -212,6 +241,20 @@ __global__ __launch_bounds__(kThreads) void actbn_apply(
       if (bn) d = ka * d + kb + kc * xn[o];
       dz[o] = d;
     });
+  }
+}
+
+// Fixed statistics, pass 2: one work-group per channel adds the channel's sums,
+// folded in a fixed order, into dgamma / dbeta.
+__global__ __launch_bounds__(kThreads) void actbn_fold(const float2* __restrict__ part, int nseg,
+                                                       float* __restrict__ dgamma,
+                                                       float* __restrict__ dbeta) {
+  __shared__ float red[4];
+  const int c = blockIdx.x;
+  const float2 sums = fold_partials(part, c, nseg, red);
+  if (threadIdx.x == 0) {
+    dbeta[c] += sums.x;
+    dgamma[c] += sums.y;
   }
 }
 
@@ -281,16 +324,37 @@ size_t actbn_workspace(int N, int C, int64_t HW) {
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // g/BN stage of a conv block, or a standalone BN backward (act = LINEAR).
-// Writes dz (when needed), adds to dgamma/dbeta (bn) or db (!bn).
-template <bool VEC, int ACT, bool BN>
-static void launch_actbn_t(const SegGeom& s, unsigned blocks, const float* delta, const float* y,
-                           const float* xn, float slope, const float* var, const float* gamma,
-                           float eps, float* dz, float* dgamma, float* dbeta_or_db, float2* part,
-                           int write_dz, hipStream_t st) {
-  actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, BN ? xn : nullptr, slope,
-                                                          part);
-  actbn_apply<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, slope, part, var, gamma,
-                                                         eps, dz, dgamma, dbeta_or_db, write_dz);
+// Writes dz (when needed), adds to dgamma/dbeta (BN) or db (no BN).
+template <bool VEC, int ACT, int BN>
+static void launch_actbn_t(const SegGeom& s, unsigned blocks, int act, const float* delta,
+                           const float* y, const float* xn, float slope, const float* var,
+                           const float* gamma, float eps, float* dz, float* dgamma,
+                           float* dbeta_or_db, float2* part, int write_dz, hipStream_t st) {
+  actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(
+      s, delta, y, BN != kBnNone ? xn : nullptr, slope, act, var, gamma, eps, dz, part);
+  if constexpr (BN == kBnFixed)
+    actbn_fold<<<(unsigned)s.C, kThreads, 0, st>>>(part, s.nseg, dgamma, dbeta_or_db);
+  else
+    actbn_apply<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, slope, act, part, var,
+                                                           gamma, eps, dz, dgamma, dbeta_or_db,
+                                                           write_dz);
+}
+
+template <bool VEC, int ACT>
+static void launch_actbn_a(const SegGeom& s, unsigned blocks, int act, int bn, const float* delta,
+                           const float* y, const float* xn, float slope, const float* var,
+                           const float* gamma, float eps, float* dz, float* dgamma,
+                           float* dbeta_or_db, float2* part, int write_dz, hipStream_t st) {
+#define CBB_ACTBN(B)                                                                        \
+  launch_actbn_t<VEC, ACT, B>(s, blocks, act, delta, y, xn, slope, var, gamma, eps, dz, dgamma, \
+                              dbeta_or_db, part, write_dz, st)
+  if (bn == kBnFixed)
+    CBB_ACTBN(kBnFixed);
+  else if (bn == kBnBatch)
+    CBB_ACTBN(kBnBatch);
+  else
+    CBB_ACTBN(kBnNone);
+#undef CBB_ACTBN
 }
 
 template <bool VEC>
@@ -298,24 +362,21 @@ static void launch_actbn_v(const SegGeom& s, unsigned blocks, int act, int bn, c
                            const float* y, const float* xn, float slope, const float* var,
                            const float* gamma, float eps, float* dz, float* dgamma,
                            float* dbeta_or_db, float2* part, int write_dz, hipStream_t st) {
-#define CBB_ACTBN(A, B)                                                                   \
-  launch_actbn_t<VEC, A, B>(s, blocks, delta, y, xn, slope, var, gamma, eps, dz, dgamma, \
-                            dbeta_or_db, part, write_dz, st)
-  switch (act * 2 + (bn ? 1 : 0)) {
-    case CBB_ACT_LINEAR * 2: CBB_ACTBN(CBB_ACT_LINEAR, false); break;
-    case CBB_ACT_LINEAR * 2 + 1: CBB_ACTBN(CBB_ACT_LINEAR, true); break;
-    case CBB_ACT_LEAKY * 2: CBB_ACTBN(CBB_ACT_LEAKY, false); break;
-    case CBB_ACT_LEAKY * 2 + 1: CBB_ACTBN(CBB_ACT_LEAKY, true); break;
-    case CBB_ACT_LOGISTIC * 2: CBB_ACTBN(CBB_ACT_LOGISTIC, false); break;
-    case CBB_ACT_LOGISTIC * 2 + 1: CBB_ACTBN(CBB_ACT_LOGISTIC, true); break;
-    case CBB_ACT_RELU * 2: CBB_ACTBN(CBB_ACT_RELU, false); break;
-    default: CBB_ACTBN(CBB_ACT_RELU, true); break;
+#define CBB_ACTBN(A)                                                                          \
+  launch_actbn_a<VEC, A>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma, \
+                         dbeta_or_db, part, write_dz, st)
+  switch (act) {
+    case CBB_ACT_LINEAR: CBB_ACTBN(CBB_ACT_LINEAR); break;
+    case CBB_ACT_LEAKY: CBB_ACTBN(CBB_ACT_LEAKY); break;
+    case CBB_ACT_LOGISTIC: CBB_ACTBN(CBB_ACT_LOGISTIC); break;
+    case CBB_ACT_RELU: CBB_ACTBN(CBB_ACT_RELU); break;
+    default: CBB_ACTBN(kActAny); break;
   }
 #undef CBB_ACTBN
 }
 
 // g/BN stage of a conv block, or a standalone BN backward (act = LINEAR).
-// Writes dz (when needed), adds to dgamma/dbeta (bn) or db (!bn).
+// bn: 0 none (db += sum g), 1 batch statistics, 2 fixed statistics.
 int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, const float* xn,
                  int act, float slope, const float* var, const float* gamma, float eps, int bn,
                  float* dz, float* dgamma, float* dbeta_or_db, void* ws, hipStream_t st) {

@@ -44,8 +44,8 @@ int check_desc(const cbb_conv_desc* d, ConvPlan* plan) {
   if (d->batch < 1 || d->in_c < 1 || d->in_h < 1 || d->in_w < 1 || d->out_c < 1 ||
       d->ksize < 1 || d->stride < 1 || d->pad < 0)
     return CBB_EINVAL;
-  if (d->act < CBB_ACT_LINEAR || d->act > CBB_ACT_RELU) return CBB_EINVAL;
-  if (d->batch_normalize != 0 && d->batch_normalize != 1) return CBB_EINVAL;
+  if (d->act < CBB_ACT_LINEAR || d->act > CBB_ACT_LOGGY) return CBB_EINVAL;
+  if (d->batch_normalize < CBB_BN_NONE || d->batch_normalize > CBB_BN_FIXED) return CBB_EINVAL;
   if (d->batch_normalize && !(d->bn_eps > 0.f)) return CBB_EINVAL;
   if (d->ksize > 7 || d->stride > 4 || d->pad >= d->ksize) return CBB_EUNSUPPORTED;
   const int64_t oh = ((int64_t)d->in_h + 2 * d->pad - d->ksize) / d->stride + 1;
@@ -214,7 +214,7 @@ int cbb_conv_backward_data(const cbb_conv_desc* desc, const float* w, const floa
 
 int cbb_act_backward(int act, float slope, const float* y, const float* delta, float* g,
                      int64_t count, void* stream) {
-  if (act < CBB_ACT_LINEAR || act > CBB_ACT_RELU) return CBB_EINVAL;
+  if (act < CBB_ACT_LINEAR || act > CBB_ACT_LOGGY) return CBB_EINVAL;
   if (count < 0 || !y || !delta || !g) return CBB_EINVAL;
   if (count == 0) return CBB_OK;
   return launch_act_backward(act, slope, y, delta, g, count, S(stream));
@@ -227,9 +227,10 @@ int cbb_bn_backward_workspace_size(int n, int c, int64_t hw, size_t* bytes) {
   return CBB_OK;
 }
 
-int cbb_bn_backward(int n, int c, int64_t hw, float eps, const float* g, const float* x_norm,
-                    const float* var, const float* gamma, float* dz, float* dgamma, float* dbeta,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+static int bn_backward_mode(int mode, int n, int c, int64_t hw, float eps, const float* g,
+                            const float* x_norm, const float* var, const float* gamma, float* dz,
+                            float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   size_t need = 0;
   int rc = cbb_bn_backward_workspace_size(n, c, hw, &need);
   if (rc) return rc;
@@ -237,8 +238,23 @@ int cbb_bn_backward(int n, int c, int64_t hw, float eps, const float* g, const f
     return CBB_EINVAL;
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign))
     return CBB_EWORKSPACE;
-  return launch_actbn(n, c, hw, g, nullptr, x_norm, CBB_ACT_LINEAR, 0.f, var, gamma, eps, 1, dz,
+  return launch_actbn(n, c, hw, g, nullptr, x_norm, CBB_ACT_LINEAR, 0.f, var, gamma, eps, mode, dz,
                       dgamma, dbeta, workspace, S(stream));
+}
+
+int cbb_bn_backward(int n, int c, int64_t hw, float eps, const float* g, const float* x_norm,
+                    const float* var, const float* gamma, float* dz, float* dgamma, float* dbeta,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return bn_backward_mode(CBB_BN_BATCH, n, c, hw, eps, g, x_norm, var, gamma, dz, dgamma, dbeta,
+                          workspace, workspace_bytes, stream);
+}
+
+int cbb_bn_backward_fixed(int n, int c, int64_t hw, float eps, const float* g,
+                          const float* x_norm, const float* var, const float* gamma, float* dz,
+                          float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return bn_backward_mode(CBB_BN_FIXED, n, c, hw, eps, g, x_norm, var, gamma, dz, dgamma, dbeta,
+                          workspace, workspace_bytes, stream);
 }
 
 int cbb_fc_backward(int batch, int in_dim, int out_dim, const float* x, const float* w,

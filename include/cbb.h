@@ -59,13 +59,39 @@ typedef enum cbb_status {
 
 /* Activation whose gradient is taken, read from the activation OUTPUT y as
  * Darknet's *_gradient functions do ([P1] section 7):
- *   LINEAR 1;  LEAKY (y > 0) ? 1 : slope;  LOGISTIC (1 - y) y;  RELU (y > 0). */
+ *   LINEAR 1;  LEAKY (y > 0) ? 1 : slope;  LOGISTIC (1 - y) y;  RELU (y > 0);
+ *   TANH 1 - y^2;  ELU (y >= 0) ? 1 : y + 1;  SELU (y >= 0) ? 1.0507 : y + 1.0507 * 1.6732;
+ *   PLSE (y < 0 || y > 1) ? .01 : .125;  LHTAN (0 < y < 1) ? 1 : .001;
+ *   HARDTAN (-1 < y < 1) ? 1 : 0;  STAIR (floor(y) == y) ? 0 : 1;  RAMP (y > 0) + .1;
+ *   RELIE (y > 0) ? 1 : .01;  LOGGY 2 (1 - s) s with s = (y + 1) / 2.
+ * The networks on the pages use the first four; the slope applies to LEAKY only. */
 typedef enum cbb_act {
   CBB_ACT_LINEAR = 0,
   CBB_ACT_LEAKY = 1,
   CBB_ACT_LOGISTIC = 2,
-  CBB_ACT_RELU = 3
+  CBB_ACT_RELU = 3,
+  CBB_ACT_TANH = 4,
+  CBB_ACT_ELU = 5,
+  CBB_ACT_SELU = 6,
+  CBB_ACT_PLSE = 7,
+  CBB_ACT_LHTAN = 8,
+  CBB_ACT_HARDTAN = 9,
+  CBB_ACT_STAIR = 10,
+  CBB_ACT_RAMP = 11,
+  CBB_ACT_RELIE = 12,
+  CBB_ACT_LOGGY = 13
 } cbb_act;
+
+/* Batch-norm mode of a block (cbb_conv_desc.batch_normalize):
+ *   NONE  no BN; the conv has a bias, db += sum g.
+ *   BATCH statistics of the batch itself (training, [P1] section 4): var is the
+ *         biased batch variance and the statistics depend on the input.
+ *   FIXED stored statistics (Caffe's use_global_stats, [P5] Backward_cpu; Darknet's
+ *         rolling mean and variance when not training, [P1] section 4): the mean
+ *         and variance are constants, so BN is a per-channel affine map and
+ *         dz = gamma/sqrt(var + eps) * g; dgamma += sum g * x_norm; dbeta += sum g.
+ *         var is the stored variance and x_norm the forward's normalised value. */
+typedef enum cbb_bn_mode { CBB_BN_NONE = 0, CBB_BN_BATCH = 1, CBB_BN_FIXED = 2 } cbb_bn_mode;
 
 /* Geometry of one convolutional block: Darknet layer fields batch, c, h, w
  * (input), n (out_c), size, stride, pad, batch_normalize, activation
@@ -74,7 +100,7 @@ typedef enum cbb_act {
 typedef struct cbb_conv_desc {
   int32_t batch, in_c, in_h, in_w;
   int32_t out_c, ksize, stride, pad;
-  int32_t batch_normalize; /* 1: BN follows the conv and its shift absorbs the conv bias */
+  int32_t batch_normalize; /* cbb_bn_mode; with BN its shift absorbs the conv bias      */
   int32_t act;             /* cbb_act                                                  */
   float slope;             /* leaky slope (0.1 in every page's network)                 */
   float bn_eps;            /* added to the variance inside the square root (1e-5)       */
@@ -90,9 +116,10 @@ const char* cbb_last_error(void);
  * backward_batchnorm_layer of [P1] section 4:
  *   g      = delta * act'(y)                                 (gradient_array)
  *   BN:    dbeta += sum g;  dgamma += sum g * x_norm;        (backward_bias/_scale)
- *          dz = gamma/sqrt(var+eps) * (g - mean(g) - x_norm * mean(g * x_norm))
+ *          BATCH: dz = gamma/sqrt(var+eps) * (g - mean(g) - x_norm * mean(g * x_norm))
  *          (the closed form of Caffe's BatchNormLayer Backward_cpu, [P5], after
  *           Darknet's scale_bias by gamma; means over batch and space)
+ *          FIXED: dz = gamma/sqrt(var+eps) * g   (see cbb_bn_mode)
  *   no BN: db += sum g;  dz = g
  *   dw[o,i,kh,kw] += sum_{n,ho,wo} dz[n,o,ho,wo] * x[n,i,ho*s+kh-p,wo*s+kw-p]
  *   dx[n,i,h,w]   (+)= sum over (o,kh,kw) with h = ho*s+kh-p, w = wo*s+kw-p of
@@ -104,8 +131,9 @@ const char* cbb_last_error(void);
  *   w       [O,C,k,k]     weights
  *   y       [N,O,OH,OW]   activation output (l.output); NULL allowed iff act = LINEAR
  *   x_norm  [N,O,OH,OW]   normalised conv output (l.x_norm)   } required iff
- *   var     [O]           biased batch variance (l.variance)  } batch_normalize,
- *   gamma   [O]           BN scale (l.scales)                 } NULL otherwise
+ *   var     [O]           variance: biased batch variance     } batch_normalize,
+ *                         (l.variance) or the stored one      } NULL otherwise
+ *   gamma   [O]           BN scale (l.scales)                 }
  *   delta   [N,O,OH,OW]   dL/dy (l.delta on entry), read only
  *   dz      [N,O,OH,OW]   receives dL/dz (l.delta on exit); may equal delta
  *                         (in place); may be NULL iff act = LINEAR and no BN
@@ -181,6 +209,15 @@ int cbb_bn_backward_workspace_size(int n, int c, int64_t hw, size_t* bytes);
 int cbb_bn_backward(int n, int c, int64_t hw, float eps, const float* g, const float* x_norm,
                     const float* var, const float* gamma, float* dz, float* dgamma, float* dbeta,
                     void* workspace, size_t workspace_bytes, void* stream);
+/* The same with fixed (stored) statistics, see CBB_BN_FIXED:
+ *   dbeta += sum g;  dgamma += sum g * x_norm;  dz = gamma/sqrt(var+eps) * g.
+ * ([P5] Backward_cpu with use_global_stats, which divides the top gradient by
+ * sqrt(var + eps), after Darknet's scale_bias by gamma.)  Same workspace size as
+ * cbb_bn_backward; dz may equal g. */
+int cbb_bn_backward_fixed(int n, int c, int64_t hw, float eps, const float* g,
+                          const float* x_norm, const float* var, const float* gamma, float* dz,
+                          float* dgamma, float* dbeta, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Inner-product backward ([P2] layer 8), batch M, in K, out N:
  *   dw [N,K] += delta^T [N,M] x [M,K];  db [N] += sum over the batch of delta;

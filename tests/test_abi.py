@@ -54,7 +54,8 @@ def ws_size(desc):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), -1), (dict(in_c=0), -1), (dict(out_c=-2), -1), (dict(ksize=0), -1),
-    (dict(stride=0), -1), (dict(pad=-1), -1), (dict(act=7), -1), (dict(batch_normalize=2), -1),
+    (dict(stride=0), -1), (dict(pad=-1), -1), (dict(act=14), -1), (dict(act=-1), -1),
+    (dict(batch_normalize=3), -1), (dict(batch_normalize=-1), -1),
     (dict(ksize=9, pad=4), -3), (dict(stride=5), -3), (dict(ksize=3, pad=3), -3),
     (dict(in_h=1, in_w=1, ksize=5, pad=1), -2),
     (dict(batch=4096, in_c=512, in_h=1024, in_w=1024), -3),
@@ -129,7 +130,8 @@ def test_weights_data_entry_points_validate():
 def test_other_entry_points_validate():
     L = cbb.lib()
     sz = ctypes.c_size_t(0)
-    assert L.cbb_act_backward(9, 0.1, BOGUS, BOGUS, BOGUS, 10, None) == -1
+    assert L.cbb_act_backward(14, 0.1, BOGUS, BOGUS, BOGUS, 10, None) == -1
+    assert L.cbb_act_backward(-1, 0.1, BOGUS, BOGUS, BOGUS, 10, None) == -1
     assert L.cbb_act_backward(1, 0.1, None, BOGUS, BOGUS, 10, None) == -1
     assert L.cbb_act_backward(1, 0.1, BOGUS, BOGUS, BOGUS, -1, None) == -1
     assert L.cbb_act_backward(1, 0.1, BOGUS, BOGUS, BOGUS, 0, None) == 0      # empty: no launch
@@ -137,6 +139,9 @@ def test_other_entry_points_validate():
     assert L.cbb_bn_backward_workspace_size(2, 4, 16, ctypes.byref(sz)) == 0 and sz.value > 0
     assert L.cbb_bn_backward(2, 4, 16, 1e-5, *[BOGUS] * 7, BOGUS, 0, None) == -4
     assert L.cbb_bn_backward(2, 4, 16, 0.0, *[BOGUS] * 7, BOGUS, 1 << 20, None) == -1
+    assert L.cbb_bn_backward_fixed(2, 4, 16, 1e-5, *[BOGUS] * 7, BOGUS, 0, None) == -4
+    assert L.cbb_bn_backward_fixed(2, 4, 16, 0.0, *[BOGUS] * 7, BOGUS, 1 << 20, None) == -1
+    assert L.cbb_bn_backward_fixed(2, 4, 16, 1e-5, *[BOGUS] * 6, None, BOGUS, 1 << 20, None) == -1
     assert L.cbb_fc_backward(0, 8, 8, *[BOGUS] * 6, 0, None) == -1
     assert L.cbb_fc_backward(4, 8, 8, None, *[BOGUS] * 5, 0, None) == -1
     assert L.cbb_softmax_loss_backward(4, 0, BOGUS, BOGUS, 1.0, BOGUS, None, None) == -1

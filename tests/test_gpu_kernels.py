@@ -59,6 +59,11 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
     (3, 20, 6, 10, 70, 1, 1, 0, False, "linear"),    # 1x1 GEMMs: ragged i and o tiles
     (4, 32, 64, 64, 48, 1, 1, 0, True, "leaky"),     # 1x1 dW: 64 K splits, two-level sum
     (2, 128, 26, 26, 255, 1, 1, 0, False, "linear"), # 1x1: 255 output channels (ragged K of dX)
+    (2, 16, 12, 12, 32, 3, 1, 1, True, "tanh"),      # the other activations, batch BN
+    (2, 24, 10, 10, 40, 3, 1, 1, 2, "selu"),         # BN with fixed statistics
+    (3, 20, 9, 9, 24, 1, 1, 0, 2, "loggy"),          # fixed statistics, 1x1
+    (2, 8, 11, 13, 16, 3, 2, 1, False, "stair"),     # no BN, run-time activation switch
+    (2, 64, 12, 12, 64, 3, 1, 1, 2, "leaky"),        # fixed statistics, 3x3 tile-direct
     (2, 64, 40, 31, 24, 3, 1, 1, True, "leaky"),     # dX: 128-pixel tile-direct, ragged plane
     (2, 3, 24, 40, 32, 3, 1, 1, True, "logistic"),   # first layer, logistic
     (1, 2, 17, 36, 12, 3, 1, 1, False, "relu"),      # first layer, bias only
@@ -79,7 +84,10 @@ def run_conv(torch, case, seed, dx_accumulate=False, in_place=False, want_dx=Tru
     gamma = (1.0 + 0.3 * r.normal(size=oc)) if bn else None
     beta = r.normal(size=oc) if bn else None
     bias = None if bn else r.normal(size=oc)
-    saved = M.round_saved_to_f32(M.conv_block_forward(L, x, wt, bias=bias, gamma=gamma, beta=beta))
+    # fixed statistics (bn = 2): the stored mean and variance
+    mean, var = (r.normal(size=oc), r.uniform(0.5, 2.0, size=oc)) if bn == 2 else (None, None)
+    saved = M.round_saved_to_f32(M.conv_block_forward(L, x, wt, bias=bias, gamma=gamma, beta=beta,
+                                                      mean=mean, var=var))
     delta = r.normal(size=saved["y"].shape).astype(np.float32)
     dx0 = r.normal(size=x.shape).astype(np.float32)
     ref = M.conv_block_backward(L, saved, delta, want_dx=want_dx,
@@ -322,6 +330,35 @@ def test_bn_backward_entry_point(shape):
         assert np.all(np.abs(s) <= 1e-5 * terms)
 
 
+@pytest.mark.parametrize("shape", [(2, 16, 32, 32), (4, 64, 13, 13), (3, 5, 7, 9), (1, 3, 1, 1)])
+def test_bn_backward_fixed_entry_point(shape):
+    """Fixed statistics: dz = gamma g / sqrt(var + eps) in the streaming pass, dgamma /
+    dbeta from the per-segment sums, added onto non-zero values."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    announce(f"bn_backward_fixed {shape}")
+    r = np.random.default_rng(17)
+    n, c = shape[:2]
+    z = r.normal(size=shape)
+    gamma = (1 + 0.2 * r.normal(size=c)).astype(np.float32)
+    mean, var = r.normal(size=c), r.uniform(0.5, 2.0, size=c).astype(np.float32)
+    xhat, _ = O.bn_forward_fixed(z, mean, var, gamma, np.zeros(c), 1e-5)
+    g = r.normal(size=shape).astype(np.float32)
+    xhat32 = xhat.astype(np.float32)
+    dz_ref, dg_ref, dbeta_ref = O.bn_backward_fixed(g, xhat32, var, gamma, 1e-5)
+    hw = int(np.prod(shape[2:]))
+    ws = cbb.workspace(cbb.bn_backward_workspace_size(n, c, hw))
+    dz = torch.empty(shape, device="cuda")
+    dg = _t(torch, np.full(c, 0.5, np.float32))
+    dbeta = _t(torch, np.full(c, -0.25, np.float32))
+    cbb.bn_backward_fixed(_t(torch, g), _t(torch, xhat32), _t(torch, var), _t(torch, gamma), dz,
+                          dg, dbeta, 1e-5, ws)
+    torch.cuda.synchronize()
+    assert_close("dz", dz.cpu().double().numpy(), dz_ref)
+    assert_close("dgamma", dg.cpu().double().numpy() - 0.5, dg_ref)
+    assert_close("dbeta", dbeta.cpu().double().numpy() + 0.25, dbeta_ref)
+
+
 @pytest.mark.parametrize("shape", [(16, 32, 104, 104), (2, 300, 16, 16), (1, 7, 1, 4)])
 def test_bn_backward_in_place_accumulating(shape):
     """dz written over g, dgamma / dbeta added to non-zero values, workspace holding
@@ -351,24 +388,39 @@ def test_bn_backward_in_place_accumulating(shape):
     assert_close("dbeta", dbeta.cpu().double().numpy(), dbeta_ref - 0.25)
 
 
-@pytest.mark.parametrize("act", ["linear", "leaky", "logistic", "relu"])
+# activations whose derivative is a function of y (rounded differently in fp32), not a constant
+SMOOTH_ACTS = ("logistic", "tanh", "elu", "selu", "loggy")
+
+
+@pytest.mark.parametrize("act", ["linear", "leaky", "logistic", "relu", "tanh", "elu", "selu",
+                                 "plse", "lhtan", "hardtan", "stair", "ramp", "relie", "loggy"])
 @pytest.mark.parametrize("count", [1, 7, 4096, 1000003])
 def test_act_backward_exact(act, count):
-    """g = delta * act'(y): one fp32 multiply by 1, slope, y(1-y) -- matches the oracle rounded."""
+    """g = delta * act'(y): where act' is piecewise constant, one fp32 multiply by the
+    page's constant, equal to the oracle's product rounded to fp32; otherwise within 1e-6."""
     torch = require_gpu()
     from cnn_backward_pass_amd import cbb
     announce(f"act {act} {count}")
     r = np.random.default_rng(count)
-    y = r.normal(size=count).astype(np.float32)
+    y = (1.5 * r.normal(size=count)).astype(np.float32)
     if act == "logistic":
         y = r.uniform(0, 1, size=count).astype(np.float32)
+    elif act in ("tanh", "loggy"):
+        y = r.uniform(-1, 1, size=count).astype(np.float32)
+    elif act == "elu":
+        y = np.maximum(y, -0.999).astype(np.float32)
+    elif act == "stair":   # outputs on and off the integers
+        y = np.where(r.uniform(size=count) < 0.5, np.round(y), y).astype(np.float32)
     y[: min(count, 3)] = 0.0                       # the kink value goes to the slope branch
+    for v, at in ((1.0, 3), (-1.0, 4)):            # breakpoints of hardtan, lhtan, plse
+        if count > at:
+            y[at] = v
     d = r.normal(size=count).astype(np.float32)
     g = torch.empty(count, device="cuda")
     cbb.act_backward(act, 0.1, _t(torch, y), _t(torch, d), g)
     torch.cuda.synchronize()
     ref = O.act_backward(O.ACT_NAMES[act], np.float32(0.1), y, d)
-    if act == "logistic":
+    if act in SMOOTH_ACTS:
         assert_close("g", g.cpu().double().numpy(), ref, tol=1e-6)
     else:
         ref32 = (d.astype(np.float64) * O.act_backward(O.ACT_NAMES[act], np.float32(0.1), y,
