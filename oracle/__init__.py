@@ -78,6 +78,7 @@ _SIGS = {
     "orc_softmax_loss": ([_i, _i, _D, _I], _d),
     "orc_softmax_loss_backward": ([_i, _i, _D, _I, _d, _D], None),
     "orc_shortcut_backward": ([_l, _d, _d, _D, _D, _D], None),
+    "orc_shortcut_backward_resize": ([_i] * 7 + [_d, _d, _D, _D, _D], None),
     "orc_route_backward": ([_i, _i, _L, _D, ctypes.POINTER(_D)], None),
     "orc_upsample_forward": ([_i] * 5 + [_D, _D], None),
     "orc_upsample_backward": ([_i] * 5 + [_D, _D], None),
@@ -331,6 +332,19 @@ def shortcut_backward(delta, d_main, d_from, alpha: float = 1.0, beta: float = 1
     d_main, d_from = _f64(d_main).copy(), _f64(d_from).copy()
     assert d_main.shape == delta.shape == d_from.shape
     lib().orc_shortcut_backward(delta.size, alpha, beta, _p(delta), _p(d_main), _p(d_from))
+    return d_main, d_from
+
+
+def shortcut_backward_resize(delta, d_main, d_from, alpha: float = 1.0, beta: float = 1.0):
+    """Shortcut backward between shapes that differ (delta [b,c1,h1,w1], d_from [b,c2,h2,w2]);
+    d_main (same shape as delta, or None) += alpha*delta.  Returns (d_main, d_from) copies."""
+    delta = _f64(delta)
+    b, c1, h1, w1 = delta.shape
+    _, c2, h2, w2 = d_from.shape
+    d_from = _f64(d_from).copy()
+    d_main = None if d_main is None else _f64(d_main).copy()
+    lib().orc_shortcut_backward_resize(b, w1, h1, c1, w2, h2, c2, alpha, beta, _p(delta),
+                                       None if d_main is None else _p(d_main), _p(d_from))
     return d_main, d_from
 
 

@@ -539,6 +539,34 @@ void orc_shortcut_backward(long count, double alpha, double beta, const double* 
   }
 }
 
+/* backward_shortcut_layer when the two shapes differ ([P1] section 5): the delta
+ * (batch x c1 x h1 x w1, the shortcut's output) goes to the previous layer with
+ * weight alpha, and shortcut_cpu adds it into the source's delta (batch x c2 x
+ * h2 x w2) over the smaller of the two shapes: with stride = w1/w2 and sample =
+ * w2/w1 (each at least 1),
+ *   d_from[b, k, j*sample, i*sample] = 1 * d_from[...] + beta * delta[b, k, j*stride, i*stride]
+ * for k < min(c1, c2), j < min(h1, h2), i < min(w1, w2).  The page asserts
+ * stride == h1/h2 and sample == h2/h1 (same aspect); the caller checks it. */
+void orc_shortcut_backward_resize(int batch, int w1, int h1, int c1, int w2, int h2, int c2,
+                                  double alpha, double beta, const double* delta, double* d_main,
+                                  double* d_from) {
+  const long n1 = (long)batch * c1 * h1 * w1;
+  if (d_main)
+    for (long e = 0; e < n1; ++e) d_main[e] += alpha * delta[e];
+  int stride = w1 / w2, sample = w2 / w1;
+  if (stride < 1) stride = 1;
+  if (sample < 1) sample = 1;
+  const int minw = w1 < w2 ? w1 : w2, minh = h1 < h2 ? h1 : h2, minc = c1 < c2 ? c1 : c2;
+  for (int b = 0; b < batch; ++b)
+    for (int k = 0; k < minc; ++k)
+      for (int j = 0; j < minh; ++j)
+        for (int i = 0; i < minw; ++i) {
+          const long out = i * sample + (long)w2 * (j * sample + (long)h2 * (k + (long)c2 * b));
+          const long add = i * stride + (long)w1 * (j * stride + (long)h1 * (k + (long)c1 * b));
+          d_from[out] = 1.0 * d_from[out] + beta * delta[add];
+        }
+}
+
 /* backward_route_layer ([P1] section 6): for input t and image j, add the
  * slice [offset_t + j*outputs, +in_sizes[t]) of the route delta into that
  * input's delta at j*in_sizes[t]; offsets advance by in_sizes[t]. */

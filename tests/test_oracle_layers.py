@@ -166,3 +166,38 @@ def test_lenet_shapes_fixture():
     d = O.softmax_loss_backward(prob, labels)
     assert list(d.shape) == g["loss_bottom_diff"]
     assert d.shape[1] == g["loss_dim"] and d.shape[0] == g["loss_nthreads"]
+
+
+def _shortcut_forward_torch(prev, src, alpha, beta):
+    """The page's forward shortcut between different shapes, written as strided slices:
+    out = alpha * prev, then over the smaller shape out[.., j*sample, i*sample] +=
+    beta * src[.., j*stride, i*stride] with stride = w_src / w_out, sample = w_out / w_src."""
+    _, cd, hd, wd = prev.shape
+    _, cs, hs, ws = src.shape
+    stride, sample = max(1, ws // wd), max(1, wd // ws)
+    mc, mh, mw = min(cd, cs), min(hd, hs), min(wd, ws)
+    out = alpha * prev
+    out = out.clone()
+    out[:, :mc, 0:mh * sample:sample, 0:mw * sample:sample] += \
+        beta * src[:, :mc, 0:mh * stride:stride, 0:mw * stride:stride]
+    return out
+
+
+@pytest.mark.parametrize("dshape,sshape", [((2, 4, 8, 8), (2, 6, 4, 4)), ((2, 6, 4, 4), (2, 3, 8, 8)),
+                                           ((1, 3, 12, 6), (1, 3, 4, 2)), ((3, 5, 6, 6), (3, 5, 6, 6))])
+def test_shortcut_backward_resize_is_adjoint_of_forward(dshape, sshape):
+    """Backward between different shapes against float64 autograd of the forward shortcut."""
+    r = np.random.default_rng(31)
+    alpha, beta = 0.75, 1.5
+    prev = torch.tensor(r.normal(size=dshape), requires_grad=True)
+    src = torch.tensor(r.normal(size=sshape), requires_grad=True)
+    delta = r.normal(size=dshape)
+    _shortcut_forward_torch(prev, src, alpha, beta).backward(torch.tensor(delta))
+    m0, f0 = r.normal(size=dshape), r.normal(size=sshape)
+    dm, df = O.shortcut_backward_resize(delta, m0, f0, alpha, beta)
+    np.testing.assert_allclose(dm - m0, prev.grad.numpy(), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(df - f0, src.grad.numpy(), rtol=0, atol=1e-14)
+    if dshape == sshape:   # equal shapes: the plain shortcut
+        pm, pf = O.shortcut_backward(delta, m0, f0, alpha, beta)
+        np.testing.assert_array_equal(dm, pm)
+        np.testing.assert_array_equal(df, pf)
