@@ -76,6 +76,7 @@ _SIGS = {
     "orc_fc_backward": ([_i, _i, _i, _D, _D, _D, _D, _D, _D, _i], None),
     "orc_softmax_forward": ([_i, _i, _D, _D], None),
     "orc_softmax_loss": ([_i, _i, _D, _I], _d),
+    "orc_softmax_backward": ([_i, _i, _l, _D, _D, _D], None),
     "orc_softmax_loss_backward": ([_i, _i, _D, _I, _d, _D], None),
     "orc_shortcut_backward": ([_l, _d, _d, _D, _D, _D], None),
     "orc_shortcut_backward_resize": ([_i] * 7 + [_d, _d, _D, _D, _D], None),
@@ -308,6 +309,17 @@ def softmax_forward(logits) -> np.ndarray:
     prob = np.empty_like(logits)
     lib().orc_softmax_forward(b, c, _p(logits), _p(prob))
     return prob
+
+
+def softmax_backward(y, dy) -> np.ndarray:
+    """Softmax backward along axis 1 of y (outer = axis 0, inner = the axes after 1)."""
+    y, dy = _f64(y), _f64(dy)
+    outer, channels = y.shape[0], y.shape[1]
+    inner = int(np.prod(y.shape[2:])) if y.ndim > 2 else 1
+    dx = np.empty_like(y)
+    lib().orc_softmax_backward(outer, channels, inner, _p(np.ascontiguousarray(y)),
+                               _p(np.ascontiguousarray(dy)), _p(dx))
+    return dx
 
 
 def softmax_loss(prob, labels) -> float:

@@ -505,6 +505,26 @@ void orc_softmax_forward(int batch, int classes, const double* logits, double* p
   }
 }
 
+/* Softmax backward along the channel axis (Caffe's SoftmaxLayer Backward_cpu,
+ * [P4]): for each outer index i and inner position k, with the channel stride
+ * `inner`: copy top_diff, take the strided dot of top_diff and top_data over the
+ * channels, subtract it from every channel, then multiply by top_data:
+ *   dx[i,c,k] = (dy[i,c,k] - sum_c' dy[i,c',k] y[i,c',k]) * y[i,c,k]. */
+void orc_softmax_backward(int outer, int channels, long inner, const double* y, const double* dy,
+                          double* dx) {
+  const long dim = (long)channels * inner;
+#pragma omp parallel for schedule(static)
+  for (int i = 0; i < outer; ++i)
+    for (long k = 0; k < inner; ++k) {
+      double dot = 0.0;
+      for (int c = 0; c < channels; ++c) dot += dy[i * dim + c * inner + k] * y[i * dim + c * inner + k];
+      for (int c = 0; c < channels; ++c) {
+        const long e = i * dim + c * inner + k;
+        dx[e] = (dy[e] - dot) * y[e];
+      }
+    }
+}
+
 /* Mean cross-entropy of the softmax, the loss SoftmaxWithLoss reports. */
 double orc_softmax_loss(int batch, int classes, const double* prob, const int* labels) {
   double l = 0.0;

@@ -104,6 +104,28 @@ def test_maxpool_backward_overlapping_indices_add():
     assert dx[0, 0, 1, 1] == 7.0 and dx[0, 0, 0, 0] == 8.0 and dx.sum() == 15.0
 
 
+@pytest.mark.parametrize("shape", [(64, 10), (3, 5, 4, 6), (2, 7, 9)])
+def test_softmax_backward_matches_autograd(shape):
+    """Generic softmax backward over axis 1 against float64 autograd of torch.softmax."""
+    logits = torch.tensor(_rand(51, *shape), requires_grad=True)
+    y = torch.softmax(logits, dim=1)
+    dy = _rand(52, *shape)
+    y.backward(torch.tensor(dy))
+    dx = O.softmax_backward(y.detach().numpy(), dy)
+    np.testing.assert_allclose(dx, logits.grad.numpy(), rtol=0, atol=1e-15)
+
+
+def test_softmax_backward_composed_with_ce_is_softmax_loss_gradient():
+    """Fed dp = -onehot / (N p), the generic backward gives SoftmaxWithLoss's (p - onehot)/N."""
+    n, c = 64, 10
+    prob = O.softmax_forward(_rand(53, n, c))
+    labels = np.random.default_rng(54).integers(0, c, size=n).astype(np.int32)
+    dp = np.zeros((n, c))
+    dp[np.arange(n), labels] = -1.0 / (n * prob[np.arange(n), labels])
+    np.testing.assert_allclose(O.softmax_backward(prob, dp), O.softmax_loss_backward(prob, labels),
+                               rtol=0, atol=1e-16)
+
+
 # ----------------------------------------------------------------------------- shortcut / route / upsample
 def test_shortcut_backward():
     d = _rand(12, 2, 3, 4, 4)
