@@ -77,6 +77,8 @@ _SIGS = {
     "cbb_softmax_loss_backward": ([_i32, _i32, _P, _P, _f, _P, _P, _P], _i32),
     "cbb_fc_softmax_backward": ([_i32, _i32, _i32, _P, _P, _f] + [_P] * 7 + [_P], _i32),
     "cbb_shortcut_backward": ([_i64, _f, _f, _P, _P, _P, _P], _i32),
+    "cbb_softmax_backward": ([_i32, _i32, _i64, _P, _P, _P, _P], _i32),
+    "cbb_shortcut_backward_resize": ([_i32] * 7 + [_f, _f, _P, _P, _P, _P], _i32),
     "cbb_route_backward": ([_i32, _i32, ctypes.POINTER(_i64), _P, ctypes.POINTER(_P), _P], _i32),
     "cbb_upsample_backward": ([_i32] * 5 + [_P, _P, _P], _i32),
     "cbb_maxpool_backward": ([_i32] * 6 + [_P, _P, _P, _P], _i32),
@@ -280,6 +282,17 @@ def fc_softmax_backward(prob, labels, x, w, dlogits, dw, db, dx, loss_weight: fl
         _ptr(bad_labels, torch.int32, "bad_labels"), _stream(stream)))
 
 
+def softmax_backward(y, dy, dx, stream=None) -> None:
+    """Softmax backward along axis 1 of y ([outer, channels, ...])."""
+    outer, channels = y.shape[0], y.shape[1]
+    inner = y.numel() // (outer * channels)
+    if tuple(dy.shape) != tuple(y.shape) or tuple(dx.shape) != tuple(y.shape):
+        raise ValueError("y, dy and dx must have one shape")
+    _check("cbb_softmax_backward", lib().cbb_softmax_backward(
+        outer, channels, inner, _ptr(y, name="y"), _ptr(dy, name="dy"), _ptr(dx, name="dx"),
+        _stream(stream)))
+
+
 def shortcut_backward(delta, d_main, d_from, alpha: float = 1.0, beta: float = 1.0,
                       stream=None) -> None:
     if not (delta.numel() == d_main.numel() == d_from.numel()):
@@ -287,6 +300,21 @@ def shortcut_backward(delta, d_main, d_from, alpha: float = 1.0, beta: float = 1
     _check("cbb_shortcut_backward", lib().cbb_shortcut_backward(
         delta.numel(), alpha, beta, _ptr(delta, name="delta"), _ptr(d_main, name="d_main"),
         _ptr(d_from, name="d_from"), _stream(stream)))
+
+
+def shortcut_backward_resize(delta, d_main, d_from, alpha: float = 1.0, beta: float = 1.0,
+                             stream=None) -> None:
+    """delta [b, c1, h1, w1], d_from [b, c2, h2, w2], d_main like delta or None."""
+    b, c1, h1, w1 = delta.shape
+    b2, c2, h2, w2 = d_from.shape
+    if b2 != b:
+        raise ValueError("delta and d_from differ in batch")
+    if d_main is not None and tuple(d_main.shape) != tuple(delta.shape):
+        raise ValueError("d_main must have delta's shape")
+    _check("cbb_shortcut_backward_resize", lib().cbb_shortcut_backward_resize(
+        b, w1, h1, c1, w2, h2, c2, alpha, beta, _ptr(delta, name="delta"),
+        None if d_main is None else _ptr(d_main, name="d_main"), _ptr(d_from, name="d_from"),
+        _stream(stream)))
 
 
 def route_backward(delta, d_ins: Sequence[torch.Tensor], stream=None) -> None:

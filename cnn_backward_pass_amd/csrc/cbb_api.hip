@@ -292,6 +292,28 @@ int cbb_fc_softmax_backward(int batch, int in_dim, int classes, const float* pro
   return launch_fc(batch, in_dim, classes, x, w, dlogits, dw, db, dx, 0, S(stream));
 }
 
+int cbb_softmax_backward(int outer, int channels, int64_t inner, const float* y, const float* dy,
+                         float* dx, void* stream) {
+  if (outer < 1 || channels < 1 || inner < 1 || !y || !dy || !dx) return CBB_EINVAL;
+  if (dx == y) return CBB_EINVAL;
+  if ((int64_t)outer * channels * inner >= kMaxIndex) return CBB_EUNSUPPORTED;
+  return launch_softmax_backward(outer, channels, inner, y, dy, dx, S(stream));
+}
+
+int cbb_shortcut_backward_resize(int batch, int w1, int h1, int c1, int w2, int h2, int c2,
+                                 float alpha, float beta, const float* delta, float* d_main,
+                                 float* d_from, void* stream) {
+  if (batch < 1 || w1 < 1 || h1 < 1 || c1 < 1 || w2 < 1 || h2 < 1 || c2 < 1 || !delta || !d_from)
+    return CBB_EINVAL;
+  if (d_from == delta || d_main == delta || (d_main && d_main == d_from)) return CBB_EINVAL;
+  // the page's asserts: one integer ratio for both sides, the same aspect
+  if (w1 / w2 != h1 / h2 || w2 / w1 != h2 / h1) return CBB_ESHAPE;
+  if ((int64_t)batch * c1 * h1 * w1 >= kMaxIndex || (int64_t)batch * c2 * h2 * w2 >= kMaxIndex)
+    return CBB_EUNSUPPORTED;
+  return launch_shortcut_resize(batch, w1, h1, c1, w2, h2, c2, alpha, beta, delta, d_main, d_from,
+                                S(stream));
+}
+
 int cbb_shortcut_backward(int64_t count, float alpha, float beta, const float* delta,
                           float* d_main, float* d_from, void* stream) {
   if (count < 0 || !delta || !d_main || !d_from) return CBB_EINVAL;

@@ -249,6 +249,11 @@ int launch_act_backward(int act, float slope, const float* y, const float* delta
                         int64_t count, hipStream_t st);
 int launch_shortcut(int64_t count, float alpha, float beta, const float* delta, float* d_main,
                     float* d_from, hipStream_t st);
+int launch_shortcut_resize(int batch, int w1, int h1, int c1, int w2, int h2, int c2, float alpha,
+                           float beta, const float* delta, float* d_main, float* d_from,
+                           hipStream_t st);
+int launch_softmax_backward(int outer, int channels, int64_t inner, const float* y,
+                            const float* dy, float* dx, hipStream_t st);
 int launch_route(int batch, int n_in, const int64_t* sizes, const float* delta,
                  float* const* d_in, hipStream_t st);
 int launch_upsample(int n, int c, int h, int w, int scale, const float* delta, float* dx,

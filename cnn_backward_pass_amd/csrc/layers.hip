@@ -45,6 +45,101 @@ __global__ __launch_bounds__(kThreads) void shortcut_kernel(int64_t count, float
   }
 }
 
+// Shapes that differ: d_from[b, k, j*sample, i*sample] += beta * delta[b, k, j*stride,
+// i*stride] over the smaller shape (one thread per term; the targets are distinct),
+// and d_main += alpha * delta over the whole delta.
+__global__ __launch_bounds__(kThreads) void shortcut_resize_kernel(
+    int batch, int w1, int h1, int c1, int w2, int h2, int c2, int stride, int sample, int minw,
+    int minh, int minc, float beta, const float* __restrict__ delta, float* __restrict__ d_from) {
+  const int64_t total = (int64_t)batch * minc * minh * minw;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * kThreads) {
+    const int i = (int)(e % minw);
+    const int64_t r = e / minw;
+    const int j = (int)(r % minh);
+    const int64_t r2 = r / minh;
+    const int k = (int)(r2 % minc), b = (int)(r2 / minc);
+    const int64_t out = i * sample + (int64_t)w2 * (j * sample + (int64_t)h2 * (k + (int64_t)c2 * b));
+    const int64_t add = i * stride + (int64_t)w1 * (j * stride + (int64_t)h1 * (k + (int64_t)c1 * b));
+    d_from[out] += beta * delta[add];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void axpy_kernel(int64_t count, float alpha,
+                                                        const float* __restrict__ x,
+                                                        float* __restrict__ y) {
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < count;
+       e += (int64_t)gridDim.x * kThreads)
+    y[e] += alpha * x[e];
+}
+
+int launch_shortcut_resize(int batch, int w1, int h1, int c1, int w2, int h2, int c2, float alpha,
+                           float beta, const float* delta, float* d_main, float* d_from,
+                           hipStream_t st) {
+  const int stride = std::max(1, w1 / w2), sample = std::max(1, w2 / w1);
+  const int minw = std::min(w1, w2), minh = std::min(h1, h2), minc = std::min(c1, c2);
+  if (d_main) {
+    const int64_t n1 = (int64_t)batch * c1 * h1 * w1;
+    axpy_kernel<<<grid_for(n1), kThreads, 0, st>>>(n1, alpha, delta, d_main);
+    const int rc = check_launch("axpy_kernel");
+    if (rc) return rc;
+  }
+  shortcut_resize_kernel<<<grid_for((int64_t)batch * minc * minh * minw), kThreads, 0, st>>>(
+      batch, w1, h1, c1, w2, h2, c2, stride, sample, minw, minh, minc, beta, delta, d_from);
+  return check_launch("shortcut_resize_kernel");
+}
+
+// ------------------------------------------------------------- softmax
+// dx[i,c,k] = (dy[i,c,k] - sum_c' dy[i,c',k] y[i,c',k]) * y[i,c,k] (Caffe's
+// SoftmaxLayer Backward_cpu).  Contiguous rows (inner = 1): one wave per row,
+// the dot summed by a fixed butterfly; otherwise one thread per (i, k), walking
+// the channels (consecutive threads read consecutive k).  Every thread reads all
+// the dy it needs before writing, so dx may equal dy.
+__global__ __launch_bounds__(kThreads) void softmax_bwd_rows(int outer, int channels,
+                                                             const float* __restrict__ y,
+                                                             const float* dy, float* dx) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (row >= outer) return;
+  const float* yr = y + row * channels;
+  const float* dr = dy + row * channels;
+  float dot = 0.f;
+  for (int c = lane; c < channels; c += 64) dot += dr[c] * yr[c];
+  dot = wave_sum(dot);
+  float* xr = dx + row * channels;
+  for (int c = lane; c < channels; c += 64) xr[c] = (dr[c] - dot) * yr[c];
+}
+
+__global__ __launch_bounds__(kThreads) void softmax_bwd_strided(int outer, int channels,
+                                                                int64_t inner,
+                                                                const float* __restrict__ y,
+                                                                const float* dy, float* dx) {
+  const int64_t total = (int64_t)outer * inner;
+  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * kThreads) {
+    const int64_t i = t / inner, k = t - i * inner;
+    const int64_t base = i * channels * inner + k;
+    float dot = 0.f;
+    for (int c = 0; c < channels; ++c) dot += dy[base + c * inner] * y[base + c * inner];
+    for (int c = 0; c < channels; ++c) {
+      const int64_t e = base + c * inner;
+      dx[e] = (dy[e] - dot) * y[e];
+    }
+  }
+}
+
+int launch_softmax_backward(int outer, int channels, int64_t inner, const float* y,
+                            const float* dy, float* dx, hipStream_t st) {
+  if (inner == 1) {
+    softmax_bwd_rows<<<(unsigned)ceil_div(outer, kThreads / 64), kThreads, 0, st>>>(outer, channels,
+                                                                                 y, dy, dx);
+    return check_launch("softmax_bwd_rows");
+  }
+  softmax_bwd_strided<<<grid_for((int64_t)outer * inner), kThreads, 0, st>>>(outer, channels,
+                                                                             inner, y, dy, dx);
+  return check_launch("softmax_bwd_strided");
+}
+
 int launch_shortcut(int64_t count, float alpha, float beta, const float* delta, float* d_main,
                     float* d_from, hipStream_t st) {
   const int vec = aligned16(delta) && aligned16(d_main) && aligned16(d_from);

@@ -246,12 +246,33 @@ int cbb_fc_softmax_backward(int batch, int in_dim, int classes, const float* pro
                             const float* w, float* dlogits, float* dw, float* db, float* dx,
                             int32_t* bad_labels, void* stream);
 
+/* Softmax backward along the channel axis ([P4] SoftmaxLayer Backward_cpu):
+ * tensors [outer, channels, inner] (inner = 1 for [batch, classes] rows),
+ *   dx[i,c,k] = (dy[i,c,k] - sum_c' dy[i,c',k] * y[i,c',k]) * y[i,c,k]
+ * with y the softmax output.  dx may equal dy, not y.  (cbb_softmax_loss_backward
+ * is this composed with the cross-entropy gradient, in closed form.) */
+int cbb_softmax_backward(int outer, int channels, int64_t inner, const float* y, const float* dy,
+                         float* dx, void* stream);
+
 /* Shortcut backward for equal shapes ([P1] section 5): d_main += alpha*delta
  * (axpy into the previous layer's delta); d_from += beta*delta (shortcut_cpu
  * with s1 = 1, s2 = beta, into the source layer's delta).  d_main and d_from
  * must not overlap each other or delta. */
 int cbb_shortcut_backward(int64_t count, float alpha, float beta, const float* delta,
                           float* d_main, float* d_from, void* stream);
+
+/* Shortcut backward between layers of different shapes ([P1] section 5,
+ * shortcut_cpu): delta is [batch, c1, h1, w1] (the shortcut's output), d_from
+ * [batch, c2, h2, w2] (the source layer's delta).  With stride = w1/w2 and
+ * sample = w2/w1 (each raised to at least 1), over k < min(c1,c2),
+ * j < min(h1,h2), i < min(w1,w2):
+ *   d_from[b, k, j*sample, i*sample] += beta * delta[b, k, j*stride, i*stride]
+ * and, unless d_main is NULL, d_main [batch, c1, h1, w1] += alpha * delta.
+ * CBB_ESHAPE when w1/w2 != h1/h2 or w2/w1 != h2/h1 (the page's asserts).
+ * With equal shapes this is cbb_shortcut_backward. */
+int cbb_shortcut_backward_resize(int batch, int w1, int h1, int c1, int w2, int h2, int c2,
+                                 float alpha, float beta, const float* delta, float* d_main,
+                                 float* d_from, void* stream);
 
 /* Route backward ([P1] section 6): the route delta holds, per image, the
  * inputs' outputs one after another (in_sizes[t] floats each, t < n_in <= 8);

@@ -147,6 +147,18 @@ def test_other_entry_points_validate():
     assert L.cbb_softmax_loss_backward(4, 0, BOGUS, BOGUS, 1.0, BOGUS, None, None) == -1
     assert L.cbb_fc_softmax_backward(4, 8, 10, BOGUS, None, 1.0, *[BOGUS] * 6, None, None) == -1
     assert L.cbb_shortcut_backward(16, 1.0, 1.0, BOGUS, BOGUS, BOGUS, None) == -1  # aliasing
+    X = ctypes.c_void_p(0x3000)
+    assert L.cbb_softmax_backward(0, 10, 1, BOGUS, X, X, None) == -1
+    assert L.cbb_softmax_backward(4, 10, 1, BOGUS, X, BOGUS, None) == -1       # dx aliases y
+    assert L.cbb_softmax_backward(4, 10, 0, BOGUS, X, X, None) == -1
+    assert L.cbb_shortcut_backward_resize(2, 8, 8, 4, 4, 8, 4, 1.0, 1.0, BOGUS, X, BOGUS,
+                                          None) == -1                  # d_from aliases delta
+    assert L.cbb_shortcut_backward_resize(2, 8, 8, 4, 4, 6, 4, 1.0, 1.0, BOGUS, None, X,
+                                          None) == -2                  # aspect differs
+    assert L.cbb_shortcut_backward_resize(2, 4, 8, 4, 8, 8, 4, 1.0, 1.0, BOGUS, None, X,
+                                          None) == -2
+    assert L.cbb_shortcut_backward_resize(0, 8, 8, 4, 4, 4, 4, 1.0, 1.0, BOGUS, None, X,
+                                          None) == -1
     assert L.cbb_shortcut_backward(0, 1.0, 1.0, BOGUS, ctypes.c_void_p(0x2000),
                                    ctypes.c_void_p(0x3000), None) == 0
     sizes = (ctypes.c_int64 * 2)(10, 0)

@@ -428,6 +428,53 @@ def test_act_backward_exact(act, count):
         assert_exact("g", g.cpu().numpy(), ref32)
 
 
+@pytest.mark.parametrize("dshape,sshape,alpha,beta", [
+    ((2, 64, 52, 52), (2, 32, 26, 26), 1.0, 1.0),     # source smaller: every second row/col
+    ((2, 32, 26, 26), (2, 64, 52, 52), 0.5, 2.0),     # source larger: strided targets
+    ((3, 5, 9, 9), (3, 7, 9, 9), 1.0, 1.0),           # equal size, channels differ
+    ((1, 8, 12, 6), (1, 8, 4, 2), 1.0, 0.25),         # ratio 3, no d_main
+])
+def test_shortcut_backward_resize_exact(dshape, sshape, alpha, beta):
+    """Single adds of a power-of-two multiple into distinct targets: bit-exact."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    announce(f"shortcut resize {dshape} -> {sshape}")
+    r = np.random.default_rng(41)
+    delta = r.normal(size=dshape).astype(np.float32)
+    m0 = r.normal(size=dshape).astype(np.float32)
+    f0 = r.normal(size=sshape).astype(np.float32)
+    use_main = beta != 0.25
+    dm = _t(torch, m0) if use_main else None
+    df = _t(torch, f0)
+    cbb.shortcut_backward_resize(_t(torch, delta), dm, df, alpha, beta)
+    torch.cuda.synchronize()
+    rm, rf = O.shortcut_backward_resize(delta, m0 if use_main else None, f0, alpha, beta)
+    assert_exact("d_from", df.cpu().numpy(), rf.astype(np.float32))
+    if use_main:
+        assert_exact("d_main", dm.cpu().numpy(), rm.astype(np.float32))
+
+
+@pytest.mark.parametrize("shape", [(64, 10), (1000, 513), (3, 5, 4, 6), (16, 80, 13, 13)])
+def test_softmax_backward(shape):
+    """Generic softmax backward: rows (one wave each) and the strided form; in place too."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    announce(f"softmax backward {shape}")
+    r = np.random.default_rng(61)
+    logits = r.normal(size=shape)
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    y = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    dy = r.normal(size=shape).astype(np.float32)
+    ref = O.softmax_backward(y, dy)
+    dx = torch.empty(shape, device="cuda")
+    cbb.softmax_backward(_t(torch, y), _t(torch, dy), dx)
+    d_in = _t(torch, dy)
+    cbb.softmax_backward(_t(torch, y), d_in, d_in)
+    torch.cuda.synchronize()
+    assert_close("dx", dx.cpu().double().numpy(), ref)
+    assert_close("dx in place", d_in.cpu().double().numpy(), ref)
+
+
 def test_shortcut_route_upsample_maxpool_exact():
     torch = require_gpu()
     from cnn_backward_pass_amd import cbb
