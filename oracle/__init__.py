@@ -75,6 +75,10 @@ _SIGS = {
     "orc_fc_forward": ([_i, _i, _i, _D, _D, _D, _D], None),
     "orc_fc_backward": ([_i, _i, _i, _D, _D, _D, _D, _D, _D, _i], None),
     "orc_softmax_forward": ([_i, _i, _D, _D], None),
+    "orc_conv_out_dim_d": ([_i] * 5, _i),
+    "orc_conv_forward_gd": ([_i] * 10 + [_D, _D, _D, _D], None),
+    "orc_conv_backward_weights_gd": ([_i] * 10 + [_D, _D, _D], None),
+    "orc_conv_backward_data_gd": ([_i] * 10 + [_D, _D, _D], None),
     "orc_softmax_loss": ([_i, _i, _D, _I], _d),
     "orc_softmax_backward": ([_i, _i, _l, _D, _D, _D], None),
     "orc_softmax_loss_backward": ([_i, _i, _D, _I, _d, _D], None),
@@ -242,6 +246,51 @@ def conv_backward_data(w, dz, in_hw, stride: int, pad: int, dx=None) -> np.ndarr
     assert dz.shape == (n, oc, conv_out_dim(h, k, stride, pad), conv_out_dim(wd, k, stride, pad))
     dx = np.zeros((n, c, h, wd)) if dx is None else _f64(dx).copy()
     lib().orc_conv_backward_data(n, c, h, wd, oc, k, stride, pad, _p(w), _p(dz), _p(dx))
+    return dx
+
+
+def conv_out_dim_d(size: int, k: int, s: int, p: int, d: int) -> int:
+    return int(lib().orc_conv_out_dim_d(size, k, s, p, d))
+
+
+def conv_forward_gd(x, w, stride: int, pad: int, dilation: int, groups: int, bias=None):
+    """Grouped, dilated convolution; w is [oc, c/groups, k, k]."""
+    x, w = _f64(x), _f64(w)
+    n, c, h, wd = x.shape
+    oc, cg, k, _ = w.shape
+    assert cg * groups == c and oc % groups == 0
+    oh, ow = conv_out_dim_d(h, k, stride, pad, dilation), conv_out_dim_d(wd, k, stride, pad, dilation)
+    z = np.empty((n, oc, oh, ow))
+    b = None if bias is None else _f64(bias)
+    lib().orc_conv_forward_gd(n, c, h, wd, oc, k, stride, pad, dilation, groups, _p(x), _p(w), _p(b),
+                              _p(z))
+    return z
+
+
+def conv_backward_weights_gd(x, dz, k: int, stride: int, pad: int, dilation: int, groups: int,
+                             dw=None):
+    x, dz = _f64(x), _f64(dz)
+    n, c, h, wd = x.shape
+    oc = dz.shape[1]
+    assert dz.shape == (n, oc, conv_out_dim_d(h, k, stride, pad, dilation),
+                        conv_out_dim_d(wd, k, stride, pad, dilation))
+    dw = np.zeros((oc, c // groups, k, k)) if dw is None else _f64(dw).copy()
+    lib().orc_conv_backward_weights_gd(n, c, h, wd, oc, k, stride, pad, dilation, groups, _p(x),
+                                       _p(dz), _p(dw))
+    return dw
+
+
+def conv_backward_data_gd(w, dz, in_hw, stride: int, pad: int, dilation: int, groups: int, dx=None):
+    w, dz = _f64(w), _f64(dz)
+    oc, cg, k, _ = w.shape
+    n = dz.shape[0]
+    h, wd = in_hw
+    c = cg * groups
+    assert dz.shape == (n, oc, conv_out_dim_d(h, k, stride, pad, dilation),
+                        conv_out_dim_d(wd, k, stride, pad, dilation))
+    dx = np.zeros((n, c, h, wd)) if dx is None else _f64(dx).copy()
+    lib().orc_conv_backward_data_gd(n, c, h, wd, oc, k, stride, pad, dilation, groups, _p(w),
+                                    _p(dz), _p(dx))
     return dx
 
 

@@ -20,7 +20,8 @@ from __future__ import annotations
 import numpy as np
 
 from . import (ACT_NAMES, act_backward, act_forward, bn_backward, bn_backward_fixed, bn_forward,
-               bn_forward_fixed, conv_backward_bias,
+               bn_forward_fixed, conv_backward_bias, conv_backward_data_gd,
+               conv_backward_weights_gd, conv_forward_gd,
                conv_backward_data, conv_backward_weights, conv_forward, fc_backward, fc_forward,
                maxpool_backward, maxpool_forward, route_backward, shortcut_backward,
                softmax_forward, softmax_loss_backward, upsample_backward, upsample_forward)
@@ -38,7 +39,12 @@ def conv_block_forward(layer, x, w, bias=None, gamma=None, beta=None, eps=EPS, s
     """Forward of one conv block; returns the tensors its backward reads (and more).
     layer.bn: 0 none, 1 (or True) batch statistics, 2 the fixed statistics mean, var."""
     act = ACT_NAMES[layer.act]
-    z = conv_forward(x, w, layer.stride, layer.pad, bias=None if layer.bn else bias)
+    groups, dil = getattr(layer, "groups", 1), getattr(layer, "dilation", 1)
+    if groups != 1 or dil != 1:
+        z = conv_forward_gd(x, w, layer.stride, layer.pad, dil, groups,
+                            bias=None if layer.bn else bias)
+    else:
+        z = conv_forward(x, w, layer.stride, layer.pad, bias=None if layer.bn else bias)
     out = {"x_in": _f64(x), "w": _f64(w), "z": z}
     if layer.bn == 2:
         xhat, u = bn_forward_fixed(z, mean, var, gamma, beta, eps)
@@ -73,11 +79,17 @@ def conv_block_backward(layer, saved, delta, want_dx=True, dx_init=None, eps=EPS
         dz = g
         res.update(dz=dz, db=conv_backward_bias(dz))
     x = saved["x_in"]
+    groups, dil = getattr(layer, "groups", 1), getattr(layer, "dilation", 1)
+    wt = saved["w"] if w is None else w
+    if groups != 1 or dil != 1:
+        res["dw"] = conv_backward_weights_gd(x, dz, layer.k, layer.stride, layer.pad, dil, groups)
+        if want_dx:
+            res["dx"] = conv_backward_data_gd(wt, dz, x.shape[2:], layer.stride, layer.pad, dil,
+                                              groups, dx=dx_init)
+        return res
     res["dw"] = conv_backward_weights(x, dz, layer.k, layer.stride, layer.pad)
     if want_dx:
-        res["dx"] = conv_backward_data(saved["w"] if w is None else w, dz, x.shape[2:],
-                                       layer.stride, layer.pad,
-                                       dx=dx_init)
+        res["dx"] = conv_backward_data(wt, dz, x.shape[2:], layer.stride, layer.pad, dx=dx_init)
     return res
 
 

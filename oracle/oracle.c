@@ -445,6 +445,99 @@ void orc_maxpool_backward(int n, int c, int ih, int iw, int oh, int ow, const in
 }
 
 /* ------------------------------------------------------------------ */
+/* grouped and dilated convolution                                     */
+/* ------------------------------------------------------------------ */
+
+/* Output size with dilation d: the window spans d*(k-1)+1 input pixels. */
+int orc_conv_out_dim_d(int size, int k, int s, int p, int d) {
+  return (size + 2 * p - d * (k - 1) - 1) / s + 1;
+}
+
+/* Grouped, dilated convolution.  Group j ([P1] section 3.1,
+ * backward_convolutional_layer with l.groups) owns output channels
+ * [j*oc/g, (j+1)*oc/g), input channels [j*c/g, (j+1)*c/g) and weight block j
+ * ([oc][c/g][k][k]); tap (kh, kw) of output (ho, wo) reads input row
+ * ho*s + kh*d - p and column wo*s + kw*d - p (the layer's dilation field, [P3];
+ * zero outside the image).
+ *   z[n,o,ho,wo] = sum_{i in group, kh, kw} W[o,i-c0,kh,kw] * x[n,i,ho*s+kh*d-p,wo*s+kw*d-p] */
+void orc_conv_forward_gd(int n, int c, int h, int w, int oc, int k, int s, int p, int d, int groups,
+                         const double* x, const double* wt, const double* bias, double* z) {
+  const int oh = orc_conv_out_dim_d(h, k, s, p, d), ow = orc_conv_out_dim_d(w, k, s, p, d);
+  const int cg = c / groups, og = oc / groups;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < n; ++b)
+    for (int o = 0; o < oc; ++o) {
+      const int c0 = (o / og) * cg;
+      for (int y = 0; y < oh; ++y)
+        for (int xo = 0; xo < ow; ++xo) {
+          double acc = bias ? bias[o] : 0.0;
+          for (int i = 0; i < cg; ++i)
+            for (int kh = 0; kh < k; ++kh)
+              for (int kw = 0; kw < k; ++kw) {
+                const int row = y * s + kh * d - p, col = xo * s + kw * d - p;
+                if (row < 0 || col < 0 || row >= h || col >= w) continue;
+                acc += wt[(((long)o * cg + i) * k + kh) * k + kw] *
+                       x[(((long)b * c + c0 + i) * h + row) * w + col];
+              }
+          z[(((long)b * oc + o) * oh + y) * ow + xo] = acc;
+        }
+    }
+}
+
+/* dW[o,i,kh,kw] += sum_{n,ho,wo} dz[n,o,ho,wo] * x[n, c0+i, ho*s+kh*d-p, wo*s+kw*d-p]
+ * (the gemm(0,1,...) of group j with beta = 1, accumulated over the images). */
+void orc_conv_backward_weights_gd(int n, int c, int h, int w, int oc, int k, int s, int p, int d,
+                                  int groups, const double* x, const double* dz, double* dw) {
+  const int oh = orc_conv_out_dim_d(h, k, s, p, d), ow = orc_conv_out_dim_d(w, k, s, p, d);
+  const int cg = c / groups, og = oc / groups;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int o = 0; o < oc; ++o) {
+    const int c0 = (o / og) * cg;
+    for (int i = 0; i < cg; ++i)
+      for (int kh = 0; kh < k; ++kh)
+        for (int kw = 0; kw < k; ++kw) {
+          double acc = 0.0;
+          for (int b = 0; b < n; ++b)
+            for (int y = 0; y < oh; ++y)
+              for (int xo = 0; xo < ow; ++xo) {
+                const int row = y * s + kh * d - p, col = xo * s + kw * d - p;
+                if (row < 0 || col < 0 || row >= h || col >= w) continue;
+                acc += dz[(((long)b * oc + o) * oh + y) * ow + xo] *
+                       x[(((long)b * c + c0 + i) * h + row) * w + col];
+              }
+          dw[(((long)o * cg + i) * k + kh) * k + kw] += acc;
+        }
+  }
+}
+
+/* dX of input channel i (group j = i / (c/g)): the col2im scatter of W^T x dz
+ * over the group's output channels, dilated taps as in the forward. */
+void orc_conv_backward_data_gd(int n, int c, int h, int w, int oc, int k, int s, int p, int d,
+                               int groups, const double* wt, const double* dz, double* dx) {
+  const int oh = orc_conv_out_dim_d(h, k, s, p, d), ow = orc_conv_out_dim_d(w, k, s, p, d);
+  const int cg = c / groups, og = oc / groups;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (int b = 0; b < n; ++b)
+    for (int i = 0; i < c; ++i) {
+      const int j = i / cg, il = i - j * cg;
+      double* plane = dx + ((long)b * c + i) * h * w;
+      for (int o = j * og; o < (j + 1) * og; ++o) {
+        const double* dzp = dz + ((long)b * oc + o) * oh * ow;
+        for (int y = 0; y < oh; ++y)
+          for (int xo = 0; xo < ow; ++xo) {
+            const double dv = dzp[(long)y * ow + xo];
+            for (int kh = 0; kh < k; ++kh)
+              for (int kw = 0; kw < k; ++kw) {
+                const int row = y * s + kh * d - p, col = xo * s + kw * d - p;
+                if (row < 0 || col < 0 || row >= h || col >= w) continue;
+                plane[(long)row * w + col] += wt[(((long)o * cg + il) * k + kh) * k + kw] * dv;
+              }
+          }
+      }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* inner product and softmax loss                                      */
 /* ------------------------------------------------------------------ */
 

@@ -218,3 +218,50 @@ def test_output_dims():
     assert O.conv_out_dim(12, 5, 1, 0) == 8
     assert O.conv_out_dim(28, 5, 1, 0) == 24
     assert O.lib().orc_conv_out_dim(52, 3, 1, 1) == 52
+
+
+# ----------------------------------------------------------------------------- groups, dilation
+GD_SHAPES = [  # n, c, h, w, oc, k, s, p, d, groups
+    (2, 4, 9, 9, 6, 3, 1, 1, 1, 2),
+    (2, 6, 11, 10, 6, 3, 2, 2, 2, 3),
+    (1, 3, 12, 12, 4, 3, 1, 2, 2, 1),
+    (2, 8, 13, 9, 8, 5, 1, 4, 2, 8),     # depthwise
+    (1, 4, 10, 11, 2, 1, 1, 0, 1, 2),    # grouped 1x1
+    (2, 2, 15, 14, 4, 3, 3, 1, 3, 2),    # stride 3, dilation 3
+]
+
+
+@pytest.mark.parametrize("shape", GD_SHAPES)
+def test_grouped_dilated_conv_matches_float64_autograd(shape):
+    """Forward, dW and dX of the grouped / dilated convolution against float64 autograd of
+    torch's conv2d with the same groups and dilation."""
+    n, c, h, w, oc, k, s, p, d, g = shape
+    r = np.random.default_rng(71)
+    x = r.normal(size=(n, c, h, w))
+    wt = r.normal(size=(oc, c // g, k, k))
+    tx = torch.tensor(x, requires_grad=True)
+    tw = torch.tensor(wt, requires_grad=True)
+    tz = torch.nn.functional.conv2d(tx, tw, stride=s, padding=p, dilation=d, groups=g)
+    z = O.conv_forward_gd(x, wt, s, p, d, g)
+    assert z.shape == tuple(tz.shape)
+    np.testing.assert_allclose(z, tz.detach().numpy(), rtol=0, atol=1e-12)
+    dz = r.normal(size=z.shape)
+    tz.backward(torch.tensor(dz))
+    np.testing.assert_allclose(O.conv_backward_weights_gd(x, dz, k, s, p, d, g), tw.grad.numpy(),
+                               rtol=0, atol=1e-11)
+    np.testing.assert_allclose(O.conv_backward_data_gd(wt, dz, (h, w), s, p, d, g),
+                               tx.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_grouped_dilated_conv_reduces_to_plain_conv():
+    """groups = dilation = 1 gives the ungrouped functions' results exactly."""
+    n, c, h, w, oc, k, s, p = 2, 3, 9, 8, 5, 3, 2, 1
+    r = np.random.default_rng(72)
+    x, wt = r.normal(size=(n, c, h, w)), r.normal(size=(oc, c, k, k))
+    z = O.conv_forward(x, wt, s, p)
+    np.testing.assert_array_equal(O.conv_forward_gd(x, wt, s, p, 1, 1), z)
+    dz = r.normal(size=z.shape)
+    np.testing.assert_array_equal(O.conv_backward_weights_gd(x, dz, k, s, p, 1, 1),
+                                  O.conv_backward_weights(x, dz, k, s, p))
+    np.testing.assert_allclose(O.conv_backward_data_gd(wt, dz, (h, w), s, p, 1, 1),
+                               O.conv_backward_data(wt, dz, (h, w), s, p), rtol=0, atol=1e-13)
