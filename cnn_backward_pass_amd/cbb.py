@@ -37,22 +37,26 @@ class ConvDesc(ctypes.Structure):
                 ("in_w", ctypes.c_int32), ("out_c", ctypes.c_int32), ("ksize", ctypes.c_int32),
                 ("stride", ctypes.c_int32), ("pad", ctypes.c_int32),
                 ("batch_normalize", ctypes.c_int32), ("act", ctypes.c_int32),
-                ("slope", ctypes.c_float), ("bn_eps", ctypes.c_float)]
+                ("slope", ctypes.c_float), ("bn_eps", ctypes.c_float),
+                ("groups", ctypes.c_int32), ("dilation", ctypes.c_int32)]
+
+    def _span(self) -> int:
+        return max(1, self.dilation) * (self.ksize - 1) + 1
 
     @property
     def out_h(self) -> int:
-        return (self.in_h + 2 * self.pad - self.ksize) // self.stride + 1
+        return (self.in_h + 2 * self.pad - self._span()) // self.stride + 1
 
     @property
     def out_w(self) -> int:
-        return (self.in_w + 2 * self.pad - self.ksize) // self.stride + 1
+        return (self.in_w + 2 * self.pad - self._span()) // self.stride + 1
 
 
 def conv_desc(batch, in_c, in_h, in_w, out_c, ksize, stride, pad, batch_normalize, act,
-              slope=0.1, bn_eps=1e-5) -> ConvDesc:
+              slope=0.1, bn_eps=1e-5, groups=1, dilation=1) -> ConvDesc:
     a = ACT[act] if isinstance(act, str) else int(act)
     return ConvDesc(batch, in_c, in_h, in_w, out_c, ksize, stride, pad, int(batch_normalize), a,
-                    slope, bn_eps)
+                    slope, bn_eps, groups, dilation)
 
 
 _P = ctypes.c_void_p

@@ -47,15 +47,20 @@ int check_desc(const cbb_conv_desc* d, ConvPlan* plan) {
   if (d->act < CBB_ACT_LINEAR || d->act > CBB_ACT_LOGGY) return CBB_EINVAL;
   if (d->batch_normalize < CBB_BN_NONE || d->batch_normalize > CBB_BN_FIXED) return CBB_EINVAL;
   if (d->batch_normalize && !(d->bn_eps > 0.f)) return CBB_EINVAL;
-  if (d->ksize > 7 || d->stride > 4 || d->pad >= d->ksize) return CBB_EUNSUPPORTED;
-  const int64_t oh = ((int64_t)d->in_h + 2 * d->pad - d->ksize) / d->stride + 1;
-  const int64_t ow = ((int64_t)d->in_w + 2 * d->pad - d->ksize) / d->stride + 1;
-  if ((int64_t)d->in_h + 2 * d->pad < d->ksize || (int64_t)d->in_w + 2 * d->pad < d->ksize ||
-      oh < 1 || ow < 1)
+  if (d->groups < 0 || d->dilation < 0) return CBB_EINVAL;
+  const int groups = d->groups > 1 ? d->groups : 1, dil = d->dilation > 1 ? d->dilation : 1;
+  if (d->in_c % groups || d->out_c % groups) return CBB_EINVAL;
+  if (d->ksize > 7 || d->stride > 4 || dil > 16 || d->pad > dil * (d->ksize - 1))
+    return CBB_EUNSUPPORTED;
+  const int64_t span = (int64_t)dil * (d->ksize - 1) + 1;   // input pixels under one window
+  const int64_t oh = ((int64_t)d->in_h + 2 * d->pad - span) / d->stride + 1;
+  const int64_t ow = ((int64_t)d->in_w + 2 * d->pad - span) / d->stride + 1;
+  if ((int64_t)d->in_h + 2 * d->pad < span || (int64_t)d->in_w + 2 * d->pad < span || oh < 1 ||
+      ow < 1)
     return CBB_ESHAPE;
   const int64_t nx = (int64_t)d->batch * d->in_c * d->in_h * d->in_w;
   const int64_t ny = (int64_t)d->batch * d->out_c * oh * ow;
-  const int64_t nw = (int64_t)d->out_c * d->in_c * d->ksize * d->ksize;
+  const int64_t nw = (int64_t)d->out_c * (d->in_c / groups) * d->ksize * d->ksize;
   if (nx >= kMaxIndex || ny >= kMaxIndex || nw >= kMaxIndex) return CBB_EUNSUPPORTED;
   if (plan) {
     plan->oh = oh;

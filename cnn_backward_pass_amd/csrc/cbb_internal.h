@@ -20,11 +20,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;  // every kernel runs 4 waves of 64 lanes
 
-// Geometry of one convolution, derived from cbb_conv_desc.
+// Geometry of one convolution, derived from cbb_conv_desc.  With groups, the
+// general kernels run once per group on a geometry whose C and OC are the
+// group's channel counts while xs / zs keep the image strides of the whole
+// tensors; everywhere else xs = C*HW and zs = OC*OHW.
 struct ConvGeom {
   int N, C, H, W, OC, K, S, P, OH, OW;
   int HW, OHW, J;  // J = C*K*K, columns of the weight-gradient matrix
   int64_t Q;       // N*OH*OW, the reduction length of the weight gradient
+  int G, D;        // groups, dilation (tap k reads input row ho*S + k*D - P)
+  int64_t xs, zs;  // image strides (floats) of x / dx and of dz
 };
 
 // Host-side launch bookkeeping -------------------------------------------------

@@ -48,9 +48,9 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
     const int i = j / kk, rem = j - i * kk;
     const int kh = rem / g.K, kw = rem - kh * g.K;
     if (j < g.J) {
-      boff[r] = i * g.HW + kh * g.W + kw;
-      bkh[r] = kh;
-      bkw[r] = kw;
+      boff[r] = i * g.HW + (kh * g.W + kw) * g.D;
+      bkh[r] = kh * g.D;
+      bkw[r] = kw * g.D;
     } else {  // column beyond J: force the bounds test to fail
       boff[r] = 0;
       bkh[r] = -(1 << 28);
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
     }
     // Out-of-range elements load from a clamped (valid) address: no divergent
     // branches around the loads.
-    const float* db = dz + ((int64_t)b * g.OC) * g.OHW + rem;
+    const float* db = dz + (int64_t)b * g.zs + rem;
     am = 0;
     bm = 0;
 #pragma unroll
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
       am |= (uint32_t)ok << r;
     }
     // x index of (n, i, hb + kh, wb + kw) = image base + boff + hb*W + wb
-    const float* xb = x + (int64_t)b * g.C * g.HW;
+    const float* xb = x + (int64_t)b * g.xs;
     const int pbase = hb * g.W + wb;
 #pragma unroll
     for (int r = 0; r < TS::B_PER_T; ++r) {
@@ -480,10 +480,24 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
   const int n0 = pixtile * TS::BN;
   if (n0 >= npix) return;  // this phase has fewer pixels than the grid covers
   const int m0 = ctile * TS::BM;
-  const int rh = (ph + g.P) % S, rw = (pw + g.P) % S;
-  const int nkh = rh < g.K ? (g.K - rh + S - 1) / S : 0;
-  const int nkw = rw < g.K ? (g.K - rw + S - 1) / S : 0;
-  const int bh = (ph + g.P - rh) / S, bw = (pw + g.P - rw) / S;
+  // Taps that reach this phase: kh with (ph + P - kh*D) divisible by S, i.e.
+  // kh = rh, rh + SK, rh + 2 SK, ... with SK = S / gcd(D, S); along them the
+  // output row moves down by DS = D / gcd(D, S) (S and 1 when D = 1).
+  int gcd = S, dd = g.D;
+  while (dd) {
+    const int t = gcd % dd;
+    gcd = dd;
+    dd = t;
+  }
+  const int SK = S / gcd, DS = g.D / gcd;
+  int rh = g.K, rw = g.K;
+  for (int k = g.K - 1; k >= 0; --k) {
+    if ((ph + g.P - k * g.D) % S == 0) rh = k;
+    if ((pw + g.P - k * g.D) % S == 0) rw = k;
+  }
+  const int nkh = rh < g.K ? (g.K - rh + SK - 1) / SK : 0;
+  const int nkw = rw < g.K ? (g.K - rw + SK - 1) / SK : 0;
+  const int bh = (ph + g.P - rh * g.D) / S, bw = (pw + g.P - rw * g.D) / S;
   const int OCP = (g.OC + TS::BK - 1) / TS::BK * TS::BK;
   const int KT = OCP * nkh * nkw;
   const int kchunk = ((KT + ksplits - 1) / ksplits + TS::BK - 1) / TS::BK * TS::BK;
@@ -501,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
     phh = r / WW;
     pww = r - phh * WW;
   }
-  const float* dzb = dz + (int64_t)pb * g.OC * g.OHW;
+  const float* dzb = dz + (int64_t)pb * g.zs;
   const int hob = phh + bh, wob = pww + bw;
 
   // A: this thread stages K column acol for channel rows m0 + irow0 + ISTEP*r.
@@ -518,7 +532,7 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
   auto load = [&](int k0) {
     const int t = k0 / OCP, o0 = k0 - t * OCP;  // uniform over the work-group
     const int th = t / nkw, tw = t - th * nkw;
-    const int kh = rh + S * th, kw = rw + S * tw;
+    const int kh = rh + SK * th, kw = rw + SK * tw;
     {  // A = weights
       const int o = o0 + acol;
       const bool ov = o < g.OC;
@@ -533,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
       }
     }
     {  // B = deltas
-      const int ho = hob - th, wo = wob - tw;
+      const int ho = hob - th * DS, wo = wob - tw * DS;
       const bool ok = pv && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
       const float* bp = dzb + (ok ? ho * g.OW + wo : 0);
       bm = 0;
@@ -571,8 +585,8 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
       const int r2 = p - b * HH * WW;
       const int hh = r2 / WW, ww = r2 - hh * WW;
       const int h = ph + S * hh, w = pw + S * ww;
-      const int64_t pix_off = ((int64_t)b * g.C) * g.HW + h * g.W + w;
-      float* dst = ksplits == 1 ? dx + pix_off : ws + (int64_t)split * g.N * g.C * g.HW + pix_off;
+      const int64_t pix_off = (int64_t)b * g.xs + h * g.W + w;
+      float* dst = ksplits == 1 ? dx + pix_off : ws + (int64_t)split * g.N * g.xs + pix_off;
 #pragma unroll
       for (int ai = 0; ai < TS::RM; ++ai) {
 #pragma unroll
@@ -1582,13 +1596,35 @@ ConvGeom make_geom(const cbb_conv_desc& d) {
   g.K = d.ksize;
   g.S = d.stride;
   g.P = d.pad;
-  g.OH = (d.in_h + 2 * d.pad - d.ksize) / d.stride + 1;
-  g.OW = (d.in_w + 2 * d.pad - d.ksize) / d.stride + 1;
+  g.G = d.groups > 1 ? d.groups : 1;
+  g.D = d.dilation > 1 ? d.dilation : 1;
+  const int span = g.D * (d.ksize - 1) + 1;   // input pixels under one window
+  g.OH = (d.in_h + 2 * d.pad - span) / d.stride + 1;
+  g.OW = (d.in_w + 2 * d.pad - span) / d.stride + 1;
   g.HW = g.H * g.W;
   g.OHW = g.OH * g.OW;
-  g.J = g.C * g.K * g.K;
+  g.J = g.C / g.G * g.K * g.K;
   g.Q = (int64_t)g.N * g.OHW;
+  g.xs = (int64_t)g.C * g.HW;
+  g.zs = (int64_t)g.OC * g.OHW;
   return g;
+}
+
+// A plain convolution: no groups, no dilation, packed image strides.  Only these
+// take the specialised kernels; the others run the general ones per group.
+static bool dense(const ConvGeom& g) {
+  return g.G == 1 && g.D == 1 && g.xs == (int64_t)g.C * g.HW && g.zs == (int64_t)g.OC * g.OHW;
+}
+
+// The geometry of one group of a grouped convolution (channel counts of the
+// group, image strides of the whole tensors).
+static ConvGeom group_geom(const ConvGeom& g) {
+  ConvGeom s = g;
+  s.C = g.C / g.G;
+  s.OC = g.OC / g.G;
+  s.J = s.C * g.K * g.K;
+  s.G = 1;
+  return s;
 }
 
 // Weight-gradient tile shapes: BM x BN (x BK) and the TileShape that realises them.
@@ -1655,10 +1691,10 @@ static bool conv1x1_ok(const ConvGeom& g) {
 
 static DwPlan plan_dw(const ConvGeom& g) {
   DwPlan best{};
-  if (plan_dw3_rows(g, best)) return best;
+  if (dense(g) && plan_dw3_rows(g, best)) return best;
   // 1x1: conv1x1_dw_dma when the tensors are 16-byte aligned (it has its own plan and
   // workspace, conv1x1_dw_workspace); otherwise the general kernel on these 64x64 tiles
-  if (conv1x1_ok(g)) {
+  if (dense(g) && conv1x1_ok(g)) {
     best.conv1x1 = 1;
     best.shape = DW_64x64;
     best.bm = best.bn = 64;
@@ -1712,7 +1748,7 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // Fused small-channel dW + dX: which layers, and how the tiles are split.
 bool conv_fused_dwdx_ok(const ConvGeom& g) {
-  return g.C >= 1 && g.C <= 3 && g.K == 3 && g.P == 1 && g.S == 1 && g.OC <= 32 && g.W % 4 == 0;
+  return dense(g) && g.C >= 1 && g.C <= 3 && g.K == 3 && g.P == 1 && g.S == 1 && g.OC <= 32 && g.W % 4 == 0;
 }
 
 struct FuPlan {
@@ -1766,6 +1802,11 @@ int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, c
 }
 
 size_t conv_dw_workspace(const ConvGeom& g) {
+  if (!dense(g)) {   // one group at a time, the groups reusing one region
+    const ConvGeom s = group_geom(g);
+    const DwPlan p = plan_dw(s);
+    return p.splits == 1 ? 0 : ((size_t)p.splits + p.groups) * s.OC * s.J * sizeof(float);
+  }
   const DwPlan p = plan_dw(g);
   const size_t c1 = p.conv1x1 ? conv1x1_dw_workspace(g) : 0;
   if (p.splits == 1) return c1;
@@ -1811,8 +1852,9 @@ static void launch_dw3_rows(const ConvGeom& g, const DwPlan& p, const float* x, 
 #undef CBB_DW3
 }
 
-int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
-                   hipStream_t st) {
+// dW of one group (or of a plain convolution).
+static int launch_conv_dw_plain(const ConvGeom& g, const float* x, const float* dz, float* dw,
+                                float* ws, hipStream_t st) {
   const DwPlan p = plan_dw(g);
   const int direct = p.splits == 1;
   float* out = direct ? dw : ws;
@@ -1839,6 +1881,22 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
   int rc = check_launch(p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel");
   if (rc != CBB_OK || direct) return rc;
   return launch_dw_reduce(g, dw, ws, p.splits, p.groups, p.rows_tc > 0, st);
+}
+
+int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
+                   hipStream_t st) {
+  if (!dense(g)) {
+    // group j: input channels j*C/G.., output channels j*OC/G.., weight block j
+    const ConvGeom s = group_geom(g);
+    for (int j = 0; j < g.G; ++j) {
+      const int rc = launch_conv_dw_plain(s, x + (int64_t)j * s.C * g.HW,
+                                          dz + (int64_t)j * s.OC * g.OHW,
+                                          dw + (int64_t)j * s.OC * s.J, ws, st);
+      if (rc) return rc;
+    }
+    return CBB_OK;
+  }
+  return launch_conv_dw_plain(g, x, dz, dw, ws, st);
 }
 
 // dw += ordered sum of the `splits` partials in ws (two levels when groups > 0).
@@ -1872,12 +1930,13 @@ static bool smallc_ok(const ConvGeom& g) {
 
 static DxPlan plan_dx(const ConvGeom& g) {
   DxPlan p{};
-  if (smallc_ok(g)) {
+  const bool special = dense(g);   // the specialised kernels assume a plain convolution
+  if (special && smallc_ok(g)) {
     p.kind = DX_SMALLC;
     p.ksplits = 1;
     return p;
   }
-  if (conv1x1_ok(g)) {
+  if (special && conv1x1_ok(g)) {
     p.kind = DX_1X1;
     p.ksplits = 1;
     p.ctiles = (int)ceil_div(g.C, 64);
@@ -1895,7 +1954,7 @@ static DxPlan plan_dx(const ConvGeom& g) {
   };
   // stride 1: larger images (>= 1024 pixels per plane) measured faster with the
   // small (128-pixel, 32-channel) tile, smaller ones with the 256-pixel, 64-channel tile
-  if (g.K == 3 && g.P == 1 && g.S == 1 && (int64_t)g.H * g.W >= 1024 &&
+  if (special && g.K == 3 && g.P == 1 && g.S == 1 && (int64_t)g.H * g.W >= 1024 &&
       dx3_s1_fits(g.W, 1, Dx3Cfg<1, 1, 1>::ZPLANE) && g.C % Dx3Cfg<1, 1, 1>::BMC == 0 &&
       g.OC % Dx3Cfg<1, 1, 1>::OCB == 0) {
     using Cf = Dx3Cfg<1, 1, 1>;
@@ -1905,7 +1964,7 @@ static DxPlan plan_dx(const ConvGeom& g) {
     p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB);
     return p;
   }
-  if (g.K == 3 && g.P == 1 && g.S == 1 && dx3_s1_fits(g.W, 2, Dx3Cfg<1, 2, 2>::ZPLANE) &&
+  if (special && g.K == 3 && g.P == 1 && g.S == 1 && dx3_s1_fits(g.W, 2, Dx3Cfg<1, 2, 2>::ZPLANE) &&
       g.C % Dx3Cfg<1, 2, 2>::BMC == 0 && g.OC % Dx3Cfg<1, 2, 2>::OCB == 0) {
     using Cf = Dx3Cfg<1, 2, 2>;
     p.kind = DX_D3S1;
@@ -1914,7 +1973,7 @@ static DxPlan plan_dx(const ConvGeom& g) {
     p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB);
     return p;
   }
-  if (g.K == 3 && g.P == 1 && g.S == 2 && g.C % Dx3Cfg<2, 1, 1>::BMC == 0 &&
+  if (special && g.K == 3 && g.P == 1 && g.S == 2 && g.C % Dx3Cfg<2, 1, 1>::BMC == 0 &&
       g.OC % Dx3Cfg<2, 1, 1>::OCB == 0) {
     using Cf = Dx3Cfg<2, 1, 1>;
     p.kind = DX_D3S2;
@@ -1947,7 +2006,8 @@ static DxPlan plan_dx(const ConvGeom& g) {
 }
 
 size_t conv_dx_workspace(const ConvGeom& g) {
-  const DxPlan p = plan_dx(g);
+  // grouped: every group writes its channels of the same [split][n][c][hw] partials
+  const DxPlan p = plan_dx(dense(g) ? g : group_geom(g));
   if (p.ksplits <= 1) return 0;
   return (size_t)p.ksplits * g.N * g.C * g.HW * sizeof(float);
 }
@@ -1975,6 +2035,31 @@ static void launch_dx_mfma(const ConvGeom& g, const DxPlan& p, const float* wt, 
 
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
                    float* ws, hipStream_t st) {
+  if (!dense(g)) {
+    // grouped or dilated: the general kernel once per group (input channels
+    // j*C/G.., output channels j*OC/G.., weight block j), then one ordered sum of
+    // the split partials over all channels
+    const ConvGeom s = group_geom(g);
+    const DxPlan p = plan_dx(s);
+    const int64_t wblock = (int64_t)s.OC * s.C * g.K * g.K;
+    for (int j = 0; j < g.G; ++j) {
+      const float* wj = wt + j * wblock;
+      const float* dzj = dz + (int64_t)j * s.OC * g.OHW;
+      float* dxj = dx + (int64_t)j * s.C * g.HW;
+      float* wsj = ws ? ws + (int64_t)j * s.C * g.HW : nullptr;
+      if (p.kind == DX_32x128)
+        launch_dx_mfma<TileShape<1, 4, 1>>(s, p, wj, dzj, dxj, wsj, accumulate, st);
+      else
+        launch_dx_mfma<TileShape<2, 2, 1>>(s, p, wj, dzj, dxj, wsj, accumulate, st);
+      const int rc = check_launch("conv_dx_kernel");
+      if (rc) return rc;
+    }
+    if (p.ksplits == 1) return CBB_OK;
+    const int64_t n = (int64_t)g.N * g.C * g.HW;
+    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
+    dx_splitk_reduce<<<blocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
+    return check_launch("dx_splitk_reduce");
+  }
   const DxPlan p = plan_dx(g);
   if (p.kind == DX_D3S1 || p.kind == DX_D3S1_SMALL || p.kind == DX_D3S2) {
     const unsigned blocks = (unsigned)((int64_t)g.N * p.pixtiles * p.ctiles * p.ksplits);

@@ -94,9 +94,15 @@ typedef enum cbb_act {
 typedef enum cbb_bn_mode { CBB_BN_NONE = 0, CBB_BN_BATCH = 1, CBB_BN_FIXED = 2 } cbb_bn_mode;
 
 /* Geometry of one convolutional block: Darknet layer fields batch, c, h, w
- * (input), n (out_c), size, stride, pad, batch_normalize, activation
- * ([P3] layer struct).  groups = dilation = 1.  Output size
- * out = (in + 2 pad - ksize) / stride + 1 (im2col_cpu, [P1] section 3.2). */
+ * (input), n (out_c), size, stride, pad, batch_normalize, activation, groups,
+ * dilation ([P3] layer struct).  Output size
+ * out = (in + 2 pad - dilation (ksize - 1) - 1) / stride + 1, which is
+ * im2col_cpu's (in + 2 pad - ksize) / stride + 1 ([P1] section 3.2) at dilation 1.
+ * Groups ([P1] section 3.1, l.groups): group j owns output channels
+ * [j out_c/groups, (j+1) out_c/groups), input channels [j in_c/groups, ...) and
+ * weight block j; weights are [out_c][in_c/groups][ksize][ksize].  Dilation: tap
+ * (kh, kw) of output (ho, wo) reads input (ho stride + kh dilation - pad,
+ * wo stride + kw dilation - pad).  groups and dilation of 0 mean 1. */
 typedef struct cbb_conv_desc {
   int32_t batch, in_c, in_h, in_w;
   int32_t out_c, ksize, stride, pad;
@@ -104,6 +110,8 @@ typedef struct cbb_conv_desc {
   int32_t act;             /* cbb_act                                                  */
   float slope;             /* leaky slope (0.1 in every page's network)                 */
   float bn_eps;            /* added to the variance inside the square root (1e-5)       */
+  int32_t groups;          /* divides in_c and out_c                                    */
+  int32_t dilation;        /* 1..16                                                      */
 } cbb_conv_desc;
 
 int cbb_abi_version(void);
@@ -128,7 +136,7 @@ const char* cbb_last_error(void);
  *
  * Arguments (shapes with N = batch, C = in_c, O = out_c, OH x OW the output):
  *   x       [N,C,H,W]     block input (net.input)
- *   w       [O,C,k,k]     weights
+ *   w       [O,C/groups,k,k] weights
  *   y       [N,O,OH,OW]   activation output (l.output); NULL allowed iff act = LINEAR
  *   x_norm  [N,O,OH,OW]   normalised conv output (l.x_norm)   } required iff
  *   var     [O]           variance: biased batch variance     } batch_normalize,
@@ -138,15 +146,17 @@ const char* cbb_last_error(void);
  *   dz      [N,O,OH,OW]   receives dL/dz (l.delta on exit); may equal delta
  *                         (in place); may be NULL iff act = LINEAR and no BN
  *                         (then dz is delta itself)
- *   dw      [O,C,k,k]     += weight gradient (l.weight_updates)
+ *   dw      [O,C/groups,k,k] += weight gradient (l.weight_updates)
  *   db      [O]           += bias gradient (l.bias_updates; with BN this is dbeta)
  *   dgamma  [O]           += scale gradient (l.scale_updates); BN only, else NULL
  *   dx      [N,C,H,W]     input gradient (net.delta); NULL skips it
  *   dx_accumulate         1: dx += ...; 0: dx = ...
  *   workspace             device scratch of at least cbb_conv_block_workspace_size
  *                         bytes, 256-byte aligned; contents on entry ignored.
- * Supported: 1 <= ksize <= 7, 1 <= stride <= 4, 0 <= pad < ksize, all sizes
- * whose element counts fit in int32 per tensor index and int64 overall.
+ * Supported: 1 <= ksize <= 7, 1 <= stride <= 4, 0 <= pad <= dilation (ksize - 1),
+ * all sizes whose element counts fit in int32 per tensor index and int64 overall.
+ * Grouped or dilated layers run the general implicit-GEMM kernels, one launch
+ * per group; the specialised kernels cover groups = dilation = 1.
  * ------------------------------------------------------------------------- */
 int cbb_conv_block_workspace_size(const cbb_conv_desc* desc, size_t* bytes);
 int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const float* w,

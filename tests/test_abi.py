@@ -56,6 +56,9 @@ def ws_size(desc):
     (dict(batch=0), -1), (dict(in_c=0), -1), (dict(out_c=-2), -1), (dict(ksize=0), -1),
     (dict(stride=0), -1), (dict(pad=-1), -1), (dict(act=14), -1), (dict(act=-1), -1),
     (dict(batch_normalize=3), -1), (dict(batch_normalize=-1), -1),
+    (dict(groups=3), -1), (dict(groups=-1), -1), (dict(dilation=-2), -1),
+    (dict(dilation=17, pad=0), -3), (dict(ksize=3, pad=3, dilation=1), -3),
+    (dict(in_h=4, in_w=4, ksize=3, pad=0, dilation=3), -2),
     (dict(ksize=9, pad=4), -3), (dict(stride=5), -3), (dict(ksize=3, pad=3), -3),
     (dict(in_h=1, in_w=1, ksize=5, pad=1), -2),
     (dict(batch=4096, in_c=512, in_h=1024, in_w=1024), -3),

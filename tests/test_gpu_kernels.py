@@ -12,9 +12,9 @@ from gpu_common import announce, assert_close, assert_exact, require_gpu
 pytestmark = pytest.mark.gpu
 
 
-def _layer(c, oc, k, s, p, bn, act, h, w):
+def _layer(c, oc, k, s, p, bn, act, h, w, groups=1, dilation=1):
     return types.SimpleNamespace(in_c=c, out_c=oc, k=k, stride=s, pad=p, bn=bn, act=act,
-                                 in_h=h, in_w=w)
+                                 in_h=h, in_w=w, groups=groups, dilation=dilation)
 
 
 def _t(torch, a, dtype=None):
@@ -76,11 +76,12 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
 
 def run_conv(torch, case, seed, dx_accumulate=False, in_place=False, want_dx=True):
     from cnn_backward_pass_amd import cbb
-    n, c, h, w, oc, k, s, p, bn, act = case
-    L = _layer(c, oc, k, s, p, bn, act, h, w)
+    n, c, h, w, oc, k, s, p, bn, act = case[:10]
+    groups, dil = case[10:12] if len(case) > 10 else (1, 1)
+    L = _layer(c, oc, k, s, p, bn, act, h, w, groups, dil)
     r = np.random.default_rng(seed)
     x = r.normal(size=(n, c, h, w)).astype(np.float32)
-    wt = (r.normal(size=(oc, c, k, k)) * 0.2).astype(np.float32)
+    wt = (r.normal(size=(oc, c // groups, k, k)) * 0.2).astype(np.float32)
     gamma = (1.0 + 0.3 * r.normal(size=oc)) if bn else None
     beta = r.normal(size=oc) if bn else None
     bias = None if bn else r.normal(size=oc)
@@ -92,7 +93,7 @@ def run_conv(torch, case, seed, dx_accumulate=False, in_place=False, want_dx=Tru
     dx0 = r.normal(size=x.shape).astype(np.float32)
     ref = M.conv_block_backward(L, saved, delta, want_dx=want_dx,
                                 dx_init=dx0 if dx_accumulate else None)
-    desc = cbb.conv_desc(n, c, h, w, oc, k, s, p, bn, act)
+    desc = cbb.conv_desc(n, c, h, w, oc, k, s, p, bn, act, groups=groups, dilation=dil)
     T = lambda a: None if a is None else _t(torch, a)
     d_delta = T(delta)
     d_dz = d_delta if in_place else (torch.empty_like(d_delta) if (bn or act != "linear") else None)
@@ -125,6 +126,33 @@ def test_conv_block_backward_parity(case):
     for k in ("dw", "db", "dz", "dx", "dgamma"):
         if k in got:
             assert_close(k, got[k], ref[k] if k != "dgamma" else ref["dgamma"])
+
+
+GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
+    (2, 8, 13, 13, 12, 3, 1, 1, True, "leaky", 2, 1),       # grouped 3x3
+    (2, 16, 12, 12, 16, 3, 1, 2, True, "leaky", 16, 2),     # depthwise, dilated
+    (2, 6, 15, 14, 9, 3, 2, 2, False, "linear", 3, 2),      # stride 2, dilation 2, 3 groups
+    (1, 4, 17, 16, 8, 5, 1, 4, True, "relu", 1, 2),         # dilated 5x5
+    (2, 12, 10, 12, 24, 1, 1, 0, True, "leaky", 4, 1),      # grouped 1x1
+    (2, 64, 20, 20, 64, 3, 1, 1, True, "leaky", 2, 1),      # grouped, channels of the 3x3 kernels
+    (1, 6, 19, 19, 6, 3, 3, 3, False, "leaky", 2, 3),       # stride 3, dilation 3
+    (2, 64, 8, 8, 256, 3, 1, 1, True, "leaky", 2, 1),       # dX split over K across the groups
+]
+
+
+@pytest.mark.parametrize("case", GD_CASES)
+def test_grouped_dilated_conv_block(case):
+    """Grouped and dilated layers (general kernels, one launch per group) against the
+    oracle's grouped / dilated loops; overwrite, then accumulate in place."""
+    torch = require_gpu()
+    announce(f"grouped/dilated conv_block {case}")
+    ref, got = run_conv(torch, case, seed=300 + GD_CASES.index(case))
+    for k in ("dw", "db", "dz", "dx", "dgamma"):
+        if k in got:
+            assert_close(k, got[k], ref[k])
+    ref, got = run_conv(torch, case, seed=7, dx_accumulate=True, in_place=True)
+    for k in ("dw", "db", "dx"):
+        assert_close(k + " (accumulate)", got[k], ref[k])
 
 
 @pytest.mark.parametrize("case", [CONV_CASES[0], CONV_CASES[1], CONV_CASES[3], CONV_CASES[5],
