@@ -30,6 +30,9 @@ struct ConvGeom {
   int64_t Q;       // N*OH*OW, the reduction length of the weight gradient
   int G, D;        // groups, dilation (tap k reads input row ho*S + k*D - P)
   int64_t xs, zs;  // image strides (floats) of x / dx and of dz
+  // offsets (floats) from one group to the next: x / dx channels, dz channels, and
+  // weight / dW blocks; the general kernels take the group from blockIdx.y
+  int64_t gx, gz, gw;
 };
 
 // Host-side launch bookkeeping -------------------------------------------------

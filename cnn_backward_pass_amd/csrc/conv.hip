@@ -23,7 +23,12 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
                                                            const float* __restrict__ dz,
                                                            float* __restrict__ out,
                                                            int64_t k_chunk, int tiles_n,
-                                                           int nsplits, int direct) {
+                                                           int nsplits, int direct,
+                                                           int64_t out_gstride) {
+  // group blockIdx.y of a grouped convolution (g holds the group's channel counts)
+  x += blockIdx.y * g.gx;
+  dz += blockIdx.y * g.gz;
+  out += blockIdx.y * out_gstride;
   __shared__ float lds[TS::LDS_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
@@ -157,7 +162,9 @@ __device__ __forceinline__ float sum_in_order(const float* __restrict__ part, in
 
 __global__ __launch_bounds__(kThreads) void dw_reduce_l1(const float* __restrict__ part,
                                                          float* __restrict__ part2, int splits,
-                                                         int64_t mn) {
+                                                         int64_t mn, int64_t region) {
+  part += blockIdx.z * region;    // grouped convolution: one partial region per group
+  part2 += blockIdx.z * region;
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (e >= mn) return;
   const int s0 = blockIdx.y * kReduceGroup, s1 = min(splits, s0 + kReduceGroup);
@@ -169,7 +176,10 @@ __global__ __launch_bounds__(kThreads) void dw_reduce_l1(const float* __restrict
 // so that its stores are contiguous; the sum is mapped back to dW's order here.
 __global__ __launch_bounds__(kThreads) void dw_reduce_l2(float* __restrict__ dw,
                                                          const float* __restrict__ part, int n,
-                                                         int64_t mn, int kk, int oc, int c) {
+                                                         int64_t mn, int kk, int oc, int c,
+                                                         int64_t region) {
+  part += blockIdx.z * region;    // grouped convolution: group blockIdx.z's partials
+  dw += blockIdx.z * mn;          // and its dW block
   const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (e >= mn) return;
   float s = 0.f;
@@ -461,6 +471,11 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
                                                            int ksplits, int pixtiles,
                                                            int accumulate) {
   static_assert(kThreads % TS::BN == 0 && kThreads % TS::BK == 0, "thread/tile mapping");
+  // group blockIdx.y of a grouped convolution (g holds the group's channel counts)
+  wt += blockIdx.y * g.gw;
+  dz += blockIdx.y * g.gz;
+  dx += blockIdx.y * g.gx;
+  if (ws) ws += blockIdx.y * g.gx;
   __shared__ float lds[TS::LDS_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
@@ -1607,6 +1622,9 @@ ConvGeom make_geom(const cbb_conv_desc& d) {
   g.Q = (int64_t)g.N * g.OHW;
   g.xs = (int64_t)g.C * g.HW;
   g.zs = (int64_t)g.OC * g.OHW;
+  g.gx = (int64_t)(g.C / g.G) * g.HW;
+  g.gz = (int64_t)(g.OC / g.G) * g.OHW;
+  g.gw = (int64_t)(g.OC / g.G) * g.J;
   return g;
 }
 
@@ -1623,7 +1641,6 @@ static ConvGeom group_geom(const ConvGeom& g) {
   s.C = g.C / g.G;
   s.OC = g.OC / g.G;
   s.J = s.C * g.K * g.K;
-  s.G = 1;
   return s;
 }
 
@@ -1802,10 +1819,11 @@ int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, c
 }
 
 size_t conv_dw_workspace(const ConvGeom& g) {
-  if (!dense(g)) {   // one group at a time, the groups reusing one region
+  if (!dense(g)) {   // a partial region per group
     const ConvGeom s = group_geom(g);
     const DwPlan p = plan_dw(s);
-    return p.splits == 1 ? 0 : ((size_t)p.splits + p.groups) * s.OC * s.J * sizeof(float);
+    return p.splits == 1 ? 0
+                         : (size_t)g.G * ((size_t)p.splits + p.groups) * s.OC * s.J * sizeof(float);
   }
   const DwPlan p = plan_dw(g);
   const size_t c1 = p.conv1x1 ? conv1x1_dw_workspace(g) : 0;
@@ -1817,9 +1835,12 @@ size_t conv_dw_workspace(const ConvGeom& g) {
 template <class TS>
 static void launch_dw_tile(const ConvGeom& g, const DwPlan& p, const float* x, const float* dz,
                            float* out, int direct, hipStream_t st) {
-  const unsigned blocks = (unsigned)(p.tiles_m * p.tiles_n * p.splits);
-  conv_dw_kernel<TS><<<blocks, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk, p.tiles_n, p.splits,
-                                                  direct);
+  // grouped: one grid row per group; its output is its dW block, or its partial region
+  const int64_t mn = (int64_t)g.OC * g.J;
+  const int64_t ostride = direct ? mn : ((int64_t)p.splits + p.groups) * mn;
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n * p.splits), (unsigned)g.G);
+  conv_dw_kernel<TS><<<grid, kThreads, 0, st>>>(g, x, dz, out, p.k_chunk, p.tiles_n, p.splits,
+                                                direct, ostride);
 }
 
 template <int S>
@@ -1885,18 +1906,9 @@ static int launch_conv_dw_plain(const ConvGeom& g, const float* x, const float* 
 
 int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
                    hipStream_t st) {
-  if (!dense(g)) {
-    // group j: input channels j*C/G.., output channels j*OC/G.., weight block j
-    const ConvGeom s = group_geom(g);
-    for (int j = 0; j < g.G; ++j) {
-      const int rc = launch_conv_dw_plain(s, x + (int64_t)j * s.C * g.HW,
-                                          dz + (int64_t)j * s.OC * g.OHW,
-                                          dw + (int64_t)j * s.OC * s.J, ws, st);
-      if (rc) return rc;
-    }
-    return CBB_OK;
-  }
-  return launch_conv_dw_plain(g, x, dz, dw, ws, st);
+  // grouped or dilated: the general kernel on the group geometry, all groups in one
+  // launch (group j: input channels j*C/G.., output channels j*OC/G.., weight block j)
+  return launch_conv_dw_plain(dense(g) ? g : group_geom(g), x, dz, dw, ws, st);
 }
 
 // dw += ordered sum of the `splits` partials in ws (two levels when groups > 0).
@@ -1905,15 +1917,19 @@ int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int gr
   const int64_t mn = (int64_t)g.OC * g.J;
   const unsigned eblocks = (unsigned)ceil_div(mn, kThreads);
   const int kk = tapmajor ? g.K * g.K : 0;
+  // grouped convolution: grid z = group, each with its own partial region
+  const int64_t region = ((int64_t)splits + groups) * mn;
   if (groups == 0) {
-    dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, ws, splits, mn, kk, g.OC, g.C);
+    dw_reduce_l2<<<dim3(eblocks, 1, g.G), kThreads, 0, st>>>(dw, ws, splits, mn, kk, g.OC, g.C,
+                                                               region);
     return check_launch("dw_reduce_l2");
   }
   float* part2 = ws + (int64_t)splits * mn;
-  dw_reduce_l1<<<dim3(eblocks, groups), kThreads, 0, st>>>(ws, part2, splits, mn);
+  dw_reduce_l1<<<dim3(eblocks, groups, g.G), kThreads, 0, st>>>(ws, part2, splits, mn, region);
   const int rc = check_launch("dw_reduce_l1");
   if (rc) return rc;
-  dw_reduce_l2<<<eblocks, kThreads, 0, st>>>(dw, part2, groups, mn, kk, g.OC, g.C);
+  dw_reduce_l2<<<dim3(eblocks, 1, g.G), kThreads, 0, st>>>(dw, part2, groups, mn, kk, g.OC, g.C,
+                                                             region);
   return check_launch("dw_reduce_l2");
 }
 
@@ -2028,33 +2044,28 @@ static void launch_smallc(const ConvGeom& g, const float* wt, const float* dz, f
 template <class TS>
 static void launch_dx_mfma(const ConvGeom& g, const DxPlan& p, const float* wt, const float* dz,
                            float* dx, float* ws, int accumulate, hipStream_t st) {
-  const unsigned blocks = (unsigned)((int64_t)p.pixtiles * g.S * g.S * p.ksplits * p.ctiles);
-  conv_dx_kernel<TS><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, ws, p.ctiles, p.ksplits,
-                                                  p.pixtiles, accumulate);
+  const dim3 grid((unsigned)((int64_t)p.pixtiles * g.S * g.S * p.ksplits * p.ctiles),
+                  (unsigned)g.G);   // grouped: one grid row per group
+  conv_dx_kernel<TS><<<grid, kThreads, 0, st>>>(g, wt, dz, dx, ws, p.ctiles, p.ksplits,
+                                                p.pixtiles, accumulate);
 }
 
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
                    float* ws, hipStream_t st) {
   if (!dense(g)) {
-    // grouped or dilated: the general kernel once per group (input channels
-    // j*C/G.., output channels j*OC/G.., weight block j), then one ordered sum of
-    // the split partials over all channels
+    // grouped or dilated: the general kernel on the group geometry, all groups in
+    // one launch (group j: input channels j*C/G.., output channels j*OC/G.., weight
+    // block j), then one ordered sum of the split partials over all channels
     const ConvGeom s = group_geom(g);
     const DxPlan p = plan_dx(s);
-    const int64_t wblock = (int64_t)s.OC * s.C * g.K * g.K;
-    for (int j = 0; j < g.G; ++j) {
-      const float* wj = wt + j * wblock;
-      const float* dzj = dz + (int64_t)j * s.OC * g.OHW;
-      float* dxj = dx + (int64_t)j * s.C * g.HW;
-      float* wsj = ws ? ws + (int64_t)j * s.C * g.HW : nullptr;
-      if (p.kind == DX_32x128)
-        launch_dx_mfma<TileShape<1, 4, 1>>(s, p, wj, dzj, dxj, wsj, accumulate, st);
-      else
-        launch_dx_mfma<TileShape<2, 2, 1>>(s, p, wj, dzj, dxj, wsj, accumulate, st);
-      const int rc = check_launch("conv_dx_kernel");
-      if (rc) return rc;
-    }
-    if (p.ksplits == 1) return CBB_OK;
+    if (p.kind == DX_32x128)
+      launch_dx_mfma<TileShape<1, 4, 1>>(s, p, wt, dz, dx, p.ksplits > 1 ? ws : nullptr,
+                                         accumulate, st);
+    else
+      launch_dx_mfma<TileShape<2, 2, 1>>(s, p, wt, dz, dx, p.ksplits > 1 ? ws : nullptr,
+                                         accumulate, st);
+    const int rc = check_launch("conv_dx_kernel");
+    if (rc || p.ksplits == 1) return rc;
     const int64_t n = (int64_t)g.N * g.C * g.HW;
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
     dx_splitk_reduce<<<blocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
