@@ -164,6 +164,83 @@ def capture_step(runners, torch, dom=None):
     return graphs
 
 
+def _roof(ms, flops, nbytes):
+    """Roofline entry of one timed call: TFLOP/s against the fp32 matrix peak above the
+    ridge, GB/s against HBM below it."""
+    if flops / max(nbytes, 1.0) >= RIDGE:
+        a = flops / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 4), "bound": "mfma", "achieved": round(a, 2),
+                "unit": "TFLOP/s", "frac": round(a / (PEAK_MFMA_F32 / 1e12), 4)}
+    a = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "bound": "hbm", "achieved": round(a, 1), "unit": "GB/s",
+            "frac": round(a / (PEAK_HBM / 1e9), 4)}
+
+
+def time_variants(torch, reps=10):
+    """The entry points beyond the five workloads' path (the other activations, batch
+    norm with fixed statistics, the shortcut between different shapes, the generic
+    softmax backward, grouped and dilated convolutions), each timed on its own with
+    events at a size taken from the workloads' layers; algorithmic work touch-once."""
+    from cnn_backward_pass_amd import cbb
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    rn = lambda *s: torch.randn(*s, device=dev, generator=g)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    out = {}
+    # activation gradient (tanh) and act+BN with fixed statistics at the stem's first layer
+    shp = (16, 32, 416, 416)
+    cnt = 16 * 32 * 416 * 416
+    y, d = torch.tanh(rn(*shp)), rn(*shp)
+    gbuf = torch.empty_like(d)
+    ms = timed(lambda: cbb.act_backward("tanh", 0.1, y, d, gbuf))
+    out["act_backward.tanh.yolov3_stem_conv1"] = _roof(ms, 0.0, 12.0 * cnt)
+    desc = cbb.conv_desc(16, 3, 416, 416, 32, 3, 1, 1, cbb.BN_FIXED, "leaky")
+    xn, var, gam = rn(*shp), torch.rand(32, device=dev) + 0.5, torch.ones(32, device=dev)
+    db, dg = torch.zeros(32, device=dev), torch.zeros(32, device=dev)
+    ws = cbb.workspace(cbb.conv_block_workspace_size(desc), dev)
+    ms = timed(lambda: cbb.conv_act_bn_backward(desc, y, xn, var, gam, d, gbuf, db, dg, ws))
+    out["act_bn.fixed_statistics.yolov3_stem_conv1"] = _roof(ms, 0.0, 16.0 * cnt)
+    del y, d, gbuf, xn
+    # shortcut into a source of half the size and channels (residual-unit delta)
+    delta, dm, dfr = rn(8, 256, 52, 52), rn(8, 256, 52, 52), rn(8, 128, 26, 26)
+    ms = timed(lambda: cbb.shortcut_backward_resize(delta, dm, dfr, 1.0, 1.0))
+    out["shortcut_resize.256x52x52_to_128x26x26"] = _roof(
+        ms, 0.0, 12.0 * delta.numel() + 12.0 * dfr.numel())
+    # generic softmax backward over the head's 255 channels (strided along the channels)
+    ys = torch.softmax(rn(8, 255, 26, 26), dim=1)
+    dys, dxs = rn(8, 255, 26, 26), torch.empty(8, 255, 26, 26, device=dev)
+    ms = timed(lambda: cbb.softmax_backward(ys, dys, dxs))
+    out["softmax_backward.8x255x26x26"] = _roof(ms, 0.0, 12.0 * ys.numel())
+    # grouped and dilated 3x3 convolutions at the residual unit's size (dW then dX)
+    for name, c, oc, gr, dil, pad in (("depthwise_3x3", 256, 256, 256, 1, 1),
+                                      ("grouped2_3x3", 256, 256, 2, 1, 1),
+                                      ("dilated2_3x3", 128, 256, 1, 2, 2)):
+        dsc = cbb.conv_desc(8, c, 52, 52, oc, 3, 1, pad, 0, "linear", groups=gr, dilation=dil)
+        x, w = rn(8, c, 52, 52), rn(oc, c // gr, 3, 3)
+        dz, dw, dx = rn(8, oc, 52, 52), torch.zeros(oc, c // gr, 3, 3, device=dev), torch.empty(
+            8, c, 52, 52, device=dev)
+        wsc = cbb.workspace(cbb.conv_block_workspace_size(dsc), dev)
+        macs = 8.0 * oc * 52 * 52 * (c // gr) * 9
+        by = 4.0 * (x.numel() + dz.numel() + w.numel())
+        ms = timed(lambda: cbb.conv_backward_weights(dsc, x, dz, dw, wsc))
+        out[f"conv_dW.{name}.8x{c}x52x52"] = _roof(ms, 2.0 * macs, by)
+        ms = timed(lambda: cbb.conv_backward_data(dsc, w, dz, dx, False, wsc))
+        out[f"conv_dX.{name}.8x{c}x52x52"] = _roof(ms, 2.0 * macs, by)
+    return out
+
+
 def cpu_baseline(min_seconds=10.0, max_reps=4):
     """The oracle (double arithmetic on the fp32 inputs) on one full step of the suite at
     full batch, repeated until ``min_seconds`` of CPU time have passed (at most
@@ -322,6 +399,8 @@ def main():
                 "ms": round(ms, 4),
                 "algorithmic_GBps": round(stage_work(runners[n], li, st)[1] / (ms * 1e-3) / 1e9, 1)}
                 for ms, n, li, st in stages if st == "act_bn" and ms > 0.05}}
+    print("[bench] variants", file=sys.stderr, flush=True)
+    line["variants"] = time_variants(torch)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -231,6 +231,13 @@ constexpr int kReduceGroup = 32;
 // or tap-major [split][tap][o][i] when tapmajor); two levels when groups > 0.
 int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
                      int tapmajor, hipStream_t st);
+// Depthwise convolution (groups = in_c = out_c): streaming per-channel kernels.
+bool conv_depthwise(const ConvGeom& g);
+size_t conv_depthwise_workspace(const ConvGeom& g);
+int launch_depthwise_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
+                        hipStream_t st);
+int launch_depthwise_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx,
+                        int accumulate, hipStream_t st);
 // 1x1 stride-1 gradients with direct global-to-LDS staging (16-byte aligned operands).
 bool conv1x1_dma_ok(const ConvGeom& g, const void* a, const void* b);
 size_t conv1x1_dw_workspace(const ConvGeom& g);

@@ -1819,6 +1819,7 @@ int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, c
 }
 
 size_t conv_dw_workspace(const ConvGeom& g) {
+  if (conv_depthwise(g)) return conv_depthwise_workspace(g);
   if (!dense(g)) {   // a partial region per group
     const ConvGeom s = group_geom(g);
     const DwPlan p = plan_dw(s);
@@ -1906,6 +1907,7 @@ static int launch_conv_dw_plain(const ConvGeom& g, const float* x, const float* 
 
 int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
                    hipStream_t st) {
+  if (conv_depthwise(g)) return launch_depthwise_dw(g, x, dz, dw, ws, st);
   // grouped or dilated: the general kernel on the group geometry, all groups in one
   // launch (group j: input channels j*C/G.., output channels j*OC/G.., weight block j)
   return launch_conv_dw_plain(dense(g) ? g : group_geom(g), x, dz, dw, ws, st);
@@ -2022,6 +2024,7 @@ static DxPlan plan_dx(const ConvGeom& g) {
 }
 
 size_t conv_dx_workspace(const ConvGeom& g) {
+  if (conv_depthwise(g)) return 0;
   // grouped: every group writes its channels of the same [split][n][c][hw] partials
   const DxPlan p = plan_dx(dense(g) ? g : group_geom(g));
   if (p.ksplits <= 1) return 0;
@@ -2052,6 +2055,7 @@ static void launch_dx_mfma(const ConvGeom& g, const DxPlan& p, const float* wt, 
 
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
                    float* ws, hipStream_t st) {
+  if (conv_depthwise(g)) return launch_depthwise_dx(g, wt, dz, dx, accumulate, st);
   if (!dense(g)) {
     // grouped or dilated: the general kernel on the group geometry, all groups in
     // one launch (group j: input channels j*C/G.., output channels j*OC/G.., weight

@@ -1,0 +1,154 @@
+// depthwise.hip -- gradients of a depthwise convolution (groups = in_c = out_c):
+// every channel has its own k x k filter, so there is no contraction over
+// channels to put on the matrix cores.  dW is a per-channel streaming reduction
+// (like the batch-norm sums) and dX a per-plane stencil; both read x / dz from
+// HBM once, neighbouring taps hitting the caches.
+//
+// Pages: "YOLOv3 backpropagation: full-flow source analysis" (suzhouguqin.com),
+// section 3.1 (backward_convolutional_layer per group: with l.groups = l.c the
+// gemm of group j is the 1 x (k*k) filter of channel j).  Tap (kh, kw) of output
+// (ho, wo) reads input (ho*S + kh*D - P, wo*S + kw*D - P), zero outside.
+#include "cbb_internal.h"
+
+namespace cbb {
+
+bool conv_depthwise(const ConvGeom& g) { return g.G > 1 && g.G == g.C && g.G == g.OC; }
+
+// Output positions of a channel (N * OH * OW) are cut into nseg segments.
+struct DwiseSeg {
+  int nseg;
+  int64_t seglen;
+};
+
+static DwiseSeg dwise_plan(const ConvGeom& g) {
+  const int64_t m = (int64_t)g.N * g.OHW;
+  // ~1024 work-groups in total, each over at least ~2048 positions
+  const int64_t nseg = std::max<int64_t>(1, std::min<int64_t>(ceil_div(1024, g.C), m / 2048));
+  DwiseSeg s;
+  s.seglen = ceil_div(m, nseg);
+  s.nseg = (int)ceil_div(m, s.seglen);
+  return s;
+}
+
+// dW partial sums: work-group (c, segment) accumulates all K*K taps of channel c
+// over its output positions; part[(c*nseg + seg)*K*K + tap].
+template <int K>
+__global__ __launch_bounds__(kThreads) void dwise_dw_partial(ConvGeom g, const float* __restrict__ x,
+                                                             const float* __restrict__ dz,
+                                                             float* __restrict__ part, int nseg,
+                                                             int64_t seglen) {
+  const int c = blockIdx.x / nseg, sg = blockIdx.x % nseg;
+  const int64_t m = (int64_t)g.N * g.OHW;
+  const int64_t q0 = (int64_t)sg * seglen, q1 = min(m, q0 + seglen);
+  float acc[K * K];
+#pragma unroll
+  for (int t = 0; t < K * K; ++t) acc[t] = 0.f;
+  for (int64_t q = q0 + threadIdx.x; q < q1; q += kThreads) {
+    const int n = (int)(q / g.OHW), r = (int)(q - (int64_t)n * g.OHW);
+    const int ho = r / g.OW, wo = r - ho * g.OW;
+    const float d = dz[((int64_t)n * g.C + c) * g.OHW + r];
+    const float* xp = x + ((int64_t)n * g.C + c) * g.HW;
+    const int h0 = ho * g.S - g.P, w0 = wo * g.S - g.P;
+#pragma unroll
+    for (int kh = 0; kh < K; ++kh) {
+      const int h = h0 + kh * g.D;
+      const bool hv = (unsigned)h < (unsigned)g.H;
+#pragma unroll
+      for (int kw = 0; kw < K; ++kw) {
+        const int w = w0 + kw * g.D;
+        if (hv && (unsigned)w < (unsigned)g.W) acc[kh * K + kw] += d * xp[h * g.W + w];
+      }
+    }
+  }
+  __shared__ float red[4];
+#pragma unroll
+  for (int t = 0; t < K * K; ++t) {
+    const float v = block_sum_256(acc[t], red);
+    if (threadIdx.x == 0) part[((int64_t)c * nseg + sg) * (K * K) + t] = v;
+  }
+}
+
+// dW[c][tap] += the channel's segment sums, added in segment order.
+__global__ __launch_bounds__(64) void dwise_dw_fold(const float* __restrict__ part, int nseg,
+                                                    int kk, float* __restrict__ dw) {
+  const int c = blockIdx.x, t = threadIdx.x;
+  if (t >= kk) return;
+  float s = 0.f;
+  for (int sg = 0; sg < nseg; ++sg) s += part[((int64_t)c * nseg + sg) * kk + t];
+  dw[(int64_t)c * kk + t] += s;
+}
+
+// dX[n,c,h,w] (+)= sum over the taps that reach (h, w) of W[c][kh][kw] * dz[n,c,ho,wo],
+// ho = (h + P - kh*D) / S when that divides exactly and lands inside the output.
+template <int K>
+__global__ __launch_bounds__(kThreads) void dwise_dx(ConvGeom g, const float* __restrict__ wt,
+                                                     const float* __restrict__ dz,
+                                                     float* __restrict__ dx, int accumulate) {
+  const int64_t total = (int64_t)g.N * g.C * g.HW;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * kThreads) {
+    const int64_t plane = e / g.HW;   // n * C + c
+    const int r = (int)(e - plane * g.HW);
+    const int c = (int)(plane % g.C);
+    const int h = r / g.W, w = r - h * g.W;
+    const float* dzp = dz + plane * g.OHW;
+    const float* wp = wt + (int64_t)c * K * K;
+    float acc = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < K; ++kh) {
+      const int th = h + g.P - kh * g.D;
+      if (th < 0 || th % g.S) continue;
+      const int ho = th / g.S;
+      if (ho >= g.OH) continue;
+#pragma unroll
+      for (int kw = 0; kw < K; ++kw) {
+        const int tw = w + g.P - kw * g.D;
+        if (tw < 0 || tw % g.S) continue;
+        const int wo = tw / g.S;
+        if (wo >= g.OW) continue;
+        acc += wp[kh * K + kw] * dzp[ho * g.OW + wo];
+      }
+    }
+    dx[e] = accumulate ? dx[e] + acc : acc;
+  }
+}
+
+size_t conv_depthwise_workspace(const ConvGeom& g) {
+  const DwiseSeg s = dwise_plan(g);
+  return (size_t)g.C * s.nseg * g.K * g.K * sizeof(float);
+}
+
+int launch_depthwise_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
+                        hipStream_t st) {
+  const DwiseSeg s = dwise_plan(g);
+  const unsigned blocks = (unsigned)((int64_t)g.C * s.nseg);
+#define CBB_DWW(K_)                                                                        \
+  case K_:                                                                                 \
+    dwise_dw_partial<K_><<<blocks, kThreads, 0, st>>>(g, x, dz, ws, s.nseg, s.seglen);     \
+    break;
+  switch (g.K) {
+    CBB_DWW(1) CBB_DWW(2) CBB_DWW(3) CBB_DWW(4) CBB_DWW(5) CBB_DWW(6) CBB_DWW(7)
+  }
+#undef CBB_DWW
+  const int rc = check_launch("dwise_dw_partial");
+  if (rc) return rc;
+  dwise_dw_fold<<<(unsigned)g.C, 64, 0, st>>>(ws, s.nseg, g.K * g.K, dw);
+  return check_launch("dwise_dw_fold");
+}
+
+int launch_depthwise_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx,
+                        int accumulate, hipStream_t st) {
+  const int64_t total = (int64_t)g.N * g.C * g.HW;
+  const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(total, kThreads), 16384);
+#define CBB_DWX(K_)                                                                   \
+  case K_:                                                                            \
+    dwise_dx<K_><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, accumulate);             \
+    break;
+  switch (g.K) {
+    CBB_DWX(1) CBB_DWX(2) CBB_DWX(3) CBB_DWX(4) CBB_DWX(5) CBB_DWX(6) CBB_DWX(7)
+  }
+#undef CBB_DWX
+  return check_launch("dwise_dx");
+}
+
+}  // namespace cbb

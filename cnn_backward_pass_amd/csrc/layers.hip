@@ -92,9 +92,10 @@ int launch_shortcut_resize(int batch, int w1, int h1, int c1, int w2, int h2, in
 // ------------------------------------------------------------- softmax
 // dx[i,c,k] = (dy[i,c,k] - sum_c' dy[i,c',k] y[i,c',k]) * y[i,c,k] (Caffe's
 // SoftmaxLayer Backward_cpu).  Contiguous rows (inner = 1): one wave per row,
-// the dot summed by a fixed butterfly; otherwise one thread per (i, k), walking
-// the channels (consecutive threads read consecutive k).  Every thread reads all
-// the dy it needs before writing, so dx may equal dy.
+// the dot summed by a fixed butterfly; otherwise a work-group per 16 positions k
+// with the channels split over slices.  Every element's dy is read before any
+// thread writes dx (the dot is complete, behind a barrier, before the writes), so
+// dx may equal dy.
 __global__ __launch_bounds__(kThreads) void softmax_bwd_rows(int outer, int channels,
                                                              const float* __restrict__ y,
                                                              const float* dy, float* dx) {
@@ -110,21 +111,31 @@ __global__ __launch_bounds__(kThreads) void softmax_bwd_rows(int outer, int chan
   for (int c = lane; c < channels; c += 64) xr[c] = (dr[c] - dot) * yr[c];
 }
 
+// Strided layout (inner > 1): a work-group takes 16 consecutive positions k of one
+// outer index and splits the channels over 16 slices (thread = (slice, k)); the
+// 16 slice sums of each position are added in slice order through LDS.
+constexpr int kSmK = 16, kSmSlices = kThreads / kSmK;
 __global__ __launch_bounds__(kThreads) void softmax_bwd_strided(int outer, int channels,
-                                                                int64_t inner,
+                                                                int64_t inner, int64_t ktiles,
                                                                 const float* __restrict__ y,
                                                                 const float* dy, float* dx) {
-  const int64_t total = (int64_t)outer * inner;
-  for (int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * kThreads) {
-    const int64_t i = t / inner, k = t - i * inner;
-    const int64_t base = i * channels * inner + k;
-    float dot = 0.f;
-    for (int c = 0; c < channels; ++c) dot += dy[base + c * inner] * y[base + c * inner];
-    for (int c = 0; c < channels; ++c) {
-      const int64_t e = base + c * inner;
-      dx[e] = (dy[e] - dot) * y[e];
-    }
+  __shared__ float part[kSmSlices][kSmK];
+  const int kl = threadIdx.x % kSmK, sl = threadIdx.x / kSmK;
+  const int64_t i = blockIdx.x / ktiles, k = (blockIdx.x % ktiles) * kSmK + kl;
+  const bool kv = k < inner;
+  const int64_t base = i * channels * inner + k;
+  float dot = 0.f;
+  if (kv)
+    for (int c = sl; c < channels; c += kSmSlices) dot += dy[base + c * inner] * y[base + c * inner];
+  part[sl][kl] = dot;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int q = 0; q < kSmSlices; ++q) tot += part[q][kl];
+  if (!kv) return;
+  for (int c = sl; c < channels; c += kSmSlices) {
+    const int64_t e = base + c * inner;
+    dx[e] = (dy[e] - tot) * y[e];
   }
 }
 
@@ -135,8 +146,9 @@ int launch_softmax_backward(int outer, int channels, int64_t inner, const float*
                                                                                  y, dy, dx);
     return check_launch("softmax_bwd_rows");
   }
-  softmax_bwd_strided<<<grid_for((int64_t)outer * inner), kThreads, 0, st>>>(outer, channels,
-                                                                             inner, y, dy, dx);
+  const int64_t ktiles = ceil_div(inner, kSmK);
+  softmax_bwd_strided<<<(unsigned)(outer * ktiles), kThreads, 0, st>>>(outer, channels, inner,
+                                                                       ktiles, y, dy, dx);
   return check_launch("softmax_bwd_strided");
 }
 

@@ -137,6 +137,13 @@ GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (2, 64, 20, 20, 64, 3, 1, 1, True, "leaky", 2, 1),      # grouped, channels of the 3x3 kernels
     (1, 6, 19, 19, 6, 3, 3, 3, False, "leaky", 2, 3),       # stride 3, dilation 3
     (2, 64, 8, 8, 256, 3, 1, 1, True, "leaky", 2, 1),       # dX split over K across the groups
+    (2, 32, 13, 13, 32, 3, 2, 1, True, "leaky", 32, 1),     # depthwise, stride 2
+    (3, 24, 17, 15, 24, 5, 1, 2, False, "relu", 24, 1),     # depthwise 5x5
+    # depthwise 1x1, no BN: with BN its dW would be sum dz * x, a multiple of sum dz * x_norm
+    # (x_norm is affine in x per channel) -- zero up to an eps-sized residue
+    (2, 8, 9, 9, 8, 1, 1, 0, False, "leaky", 8, 1),
+    (8, 64, 52, 52, 64, 3, 1, 1, True, "leaky", 64, 1),     # depthwise, many segments per channel
+    (2, 16, 12, 12, 32, 3, 1, 1, True, "leaky", 16, 1),     # two filters per channel (general)
 ]
 
 
