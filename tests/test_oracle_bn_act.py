@@ -280,3 +280,16 @@ def test_bn_fixed_statistics_finite_differences_and_caffe_form():
         assert (loss(z, gamma, bp) - loss(z, gamma, bm)) / (2 * h) == pytest.approx(dbeta[ch], rel=1e-6)
     dz1, _, _ = O.bn_backward_fixed(g, xhat, var, np.ones(shape[1]), EPS)
     np.testing.assert_allclose(dz1, g / np.sqrt(var + EPS)[None, :, None, None], rtol=1e-15)
+
+
+@pytest.mark.parametrize("shape", [(4, 3, 5, 7), (16, 2, 9, 9)])
+def test_bn_forward_statistics_are_batch_mean_and_biased_variance(shape):
+    """The statistics the forward returns (and the GPU forward must reproduce): per channel
+    over (batch, space), the mean and the variance with divisor m (numpy's ddof = 0)."""
+    z, gamma, beta = _bn_case(41, shape)
+    z = z * 3.0 + 5.0   # an offset mean: the two-pass variance must not cancel
+    mean, var, xhat, _ = O.bn_forward(z, gamma, beta, EPS)
+    np.testing.assert_allclose(mean, z.mean(axis=(0, 2, 3)), rtol=1e-14)
+    np.testing.assert_allclose(var, z.var(axis=(0, 2, 3), ddof=0), rtol=1e-12)
+    np.testing.assert_allclose(xhat, (z - mean[None, :, None, None])
+                               / np.sqrt(var + EPS)[None, :, None, None], rtol=1e-12, atol=1e-13)
