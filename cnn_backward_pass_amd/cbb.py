@@ -73,6 +73,9 @@ _SIGS = {
     "cbb_conv_backward_weights_data": ([ctypes.POINTER(ConvDesc)] + [_P] * 5 + [_i32, _P, _sz, _P],
                                        _i32),
     "cbb_conv_fused_weights_data": ([ctypes.POINTER(ConvDesc)], _i32),
+    "cbb_conv_block_forward_workspace_size": ([ctypes.POINTER(ConvDesc), ctypes.POINTER(_sz)],
+                                              _i32),
+    "cbb_conv_block_forward": ([ctypes.POINTER(ConvDesc)] + [_P] * 9 + [_P, _sz, _P], _i32),
     "cbb_act_backward": ([_i32, _f, _P, _P, _P, _i64, _P], _i32),
     "cbb_bn_backward_workspace_size": ([_i32, _i32, _i64, ctypes.POINTER(_sz)], _i32),
     "cbb_bn_backward": ([_i32, _i32, _i64, _f] + [_P] * 7 + [_P, _sz, _P], _i32),
@@ -178,6 +181,23 @@ def conv_block_backward(desc: ConvDesc, x, w, y, x_norm, var, gamma, delta, dz, 
         _ptr(delta, name="delta"), _ptr(dz, name="dz"), _ptr(dw, name="dw"),
         _ptr(db, name="db"), _ptr(dgamma, name="dgamma"), _ptr(dx, name="dx"),
         int(dx_accumulate), wsp, wsb, _stream(stream)))
+
+
+def conv_block_forward_workspace_size(desc: ConvDesc) -> int:
+    b = ctypes.c_size_t(0)
+    _check("cbb_conv_block_forward_workspace_size",
+           lib().cbb_conv_block_forward_workspace_size(ctypes.byref(desc), ctypes.byref(b)))
+    return b.value
+
+
+def conv_block_forward(desc: ConvDesc, x, w, bias, gamma, beta, mean, var, x_norm, y,
+                       workspace=None, stream=None) -> None:
+    wsp, wsb = _ws(workspace)
+    _check("cbb_conv_block_forward", lib().cbb_conv_block_forward(
+        ctypes.byref(desc), _ptr(x, name="x"), _ptr(w, name="w"), _ptr(bias, name="bias"),
+        _ptr(gamma, name="gamma"), _ptr(beta, name="beta"), _ptr(mean, name="mean"),
+        _ptr(var, name="var"), _ptr(x_norm, name="x_norm"), _ptr(y, name="y"), wsp, wsb,
+        _stream(stream)))
 
 
 def conv_act_bn_backward(desc: ConvDesc, y, x_norm, var, gamma, delta, dz, db, dgamma,

@@ -289,6 +289,129 @@ __global__ __launch_bounds__(kThreads) void act_backward_scalar(int act, float s
 }
 
 // ---------------------------------------------------------------------------
+// Forward of the block after the convolution (the tensors the backward reads):
+// batch statistics of z per channel over (batch, space) -- the mean, then the
+// biased variance E[(z - mean)^2] ("Understanding BatchNorm", Forward_cpu; the
+// YOLOv3 page's mean_cpu / variance_cpu) -- x_norm = (z - mean)/sqrt(var + eps),
+// u = gamma x_norm + beta (scale_bias, add_bias), y = act(u) (section 7's
+// *_activate functions).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float act_fwd(int act, float slope, float u) {
+  switch (act) {
+    case CBB_ACT_LEAKY: return u > 0.f ? u : slope * u;
+    case CBB_ACT_LOGISTIC: return 1.f / (1.f + expf(-u));
+    case CBB_ACT_RELU: return u > 0.f ? u : 0.f;
+    case CBB_ACT_TANH: return tanhf(u);
+    case CBB_ACT_ELU: return u >= 0.f ? u : expm1f(u);
+    case CBB_ACT_SELU: return u >= 0.f ? 1.0507f * u : 1.0507f * 1.6732f * expm1f(u);
+    case CBB_ACT_PLSE:
+      if (u < -4.f) return .01f * (u + 4.f);
+      if (u > 4.f) return .01f * (u - 4.f) + 1.f;
+      return .125f * u + .5f;
+    case CBB_ACT_LHTAN:
+      if (u < 0.f) return .001f * u;
+      if (u > 1.f) return .001f * (u - 1.f) + 1.f;
+      return u;
+    case CBB_ACT_HARDTAN: return u < -1.f ? -1.f : (u > 1.f ? 1.f : u);
+    case CBB_ACT_STAIR: {
+      const float n = floorf(u);
+      return fmodf(n, 2.f) == 0.f ? floorf(u * .5f) : (u - n) + floorf(u * .5f);
+    }
+    case CBB_ACT_RAMP: return (u > 0.f ? u : 0.f) + .1f * u;
+    case CBB_ACT_RELIE: return u > 0.f ? u : .01f * u;
+    case CBB_ACT_LOGGY: return 2.f / (1.f + expf(-u)) - 1.f;
+    default: return u;
+  }
+}
+
+// Per-(channel, segment) sum of z (CENTER = false) or of (z - mean)^2 (CENTER = true).
+template <bool VEC, bool CENTER>
+__global__ __launch_bounds__(kThreads) void bnf_partial(SegGeom s, const float* __restrict__ z,
+                                                        const float* __restrict__ mean,
+                                                        float* __restrict__ part) {
+  const int c = blockIdx.x / s.nseg, sg = blockIdx.x % s.nseg;
+  const float mu = CENTER ? mean[c] : 0.f;
+  float acc = 0.f;
+  if constexpr (VEC) {
+    for_segment<true>(s, c, sg, [&](int64_t o) {
+      const float4 v = ld4(z + o);
+      if (CENTER) {
+        const float a = v.x - mu, b = v.y - mu, cc = v.z - mu, d = v.w - mu;
+        acc += (a * a + b * b) + (cc * cc + d * d);
+      } else {
+        acc += (v.x + v.y) + (v.z + v.w);
+      }
+    });
+  } else {
+    for_segment<false>(s, c, sg, [&](int64_t o) {
+      const float v = z[o] - mu;
+      acc += CENTER ? v * v : v;
+    });
+  }
+  __shared__ float red[4];
+  acc = block_sum_256(acc, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = acc;
+}
+
+// out[c] = (the channel's segment sums, folded in a fixed order) * inv_m.
+__global__ __launch_bounds__(kThreads) void bnf_fold(const float* __restrict__ part, int nseg,
+                                                     float inv_m, float* __restrict__ out) {
+  __shared__ float red[4];
+  const int c = blockIdx.x;
+  float a = 0.f;
+  for (int k = threadIdx.x; k < nseg; k += kThreads) a += part[(int64_t)c * nseg + k];
+  a = block_sum_256(a, red);
+  if (threadIdx.x == 0) out[c] = a * inv_m;
+}
+
+// BN: xn holds z on entry and x_norm on exit; y = act(gamma x_norm + beta).
+// No BN: y holds z (+ bias) on entry and act of it on exit (xn == y).
+template <bool VEC, bool BN>
+__global__ __launch_bounds__(kThreads) void bnf_apply(SegGeom s, float* xn, float* y,
+                                                      const float* __restrict__ mean,
+                                                      const float* __restrict__ var,
+                                                      const float* __restrict__ gamma,
+                                                      const float* __restrict__ beta, float eps,
+                                                      int act, float slope) {
+  const int c = blockIdx.x / s.nseg, sg = blockIdx.x % s.nseg;
+  float mu = 0.f, inv = 1.f, ga = 1.f, be = 0.f;
+  if (BN) {
+    mu = mean[c];
+    inv = 1.f / sqrtf(var[c] + eps);
+    ga = gamma[c];
+    be = beta[c];
+  }
+  auto one = [&](float v, float* xo) {
+    float u = v;
+    if (BN) {
+      const float xh = (v - mu) * inv;
+      *xo = xh;
+      u = ga * xh + be;
+    }
+    return act_fwd(act, slope, u);
+  };
+  if constexpr (VEC) {
+    for_segment<true>(s, c, sg, [&](int64_t o) {
+      const float4 v = *reinterpret_cast<const float4*>(xn + o);
+      float4 xh = v, r;
+      r.x = one(v.x, &xh.x);
+      r.y = one(v.y, &xh.y);
+      r.z = one(v.z, &xh.z);
+      r.w = one(v.w, &xh.w);
+      if (BN) *reinterpret_cast<float4*>(xn + o) = xh;
+      *reinterpret_cast<float4*>(y + o) = r;
+    });
+  } else {
+    for_segment<false>(s, c, sg, [&](int64_t o) {
+      float xh = 0.f;
+      const float r = one(xn[o], &xh);
+      if (BN) xn[o] = xh;
+      y[o] = r;
+    });
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 SegGeom plan_seg(int N, int C, int64_t HW) {
@@ -393,6 +516,46 @@ int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, c
     launch_actbn_v<false>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma,
                           dbeta_or_db, part, write_dz, st);
   return check_launch("actbn_reduce/actbn_apply");
+}
+
+// Forward after the convolution (see bnf_apply).  bn: 0 none (z + bias already in y),
+// 1 batch statistics (written to mean / var), 2 fixed statistics (read).
+int launch_bn_act_forward(int N, int C, int64_t HW, int bn, float eps, int act, float slope,
+                          const float* gamma, const float* beta, float* mean, float* var,
+                          float* xn, float* y, void* ws, hipStream_t st) {
+  const SegGeom s = plan_seg(N, C, HW);
+  const unsigned blocks = (unsigned)((int64_t)C * s.nseg);
+  const bool vec = (HW % 4 == 0) && aligned16(xn) && aligned16(y);
+  float* part = reinterpret_cast<float*>(ws);
+  if (bn == 1) {
+    const float inv_m = 1.f / (float)s.M;
+    if (vec)
+      bnf_partial<true, false><<<blocks, kThreads, 0, st>>>(s, xn, nullptr, part);
+    else
+      bnf_partial<false, false><<<blocks, kThreads, 0, st>>>(s, xn, nullptr, part);
+    bnf_fold<<<(unsigned)C, kThreads, 0, st>>>(part, s.nseg, inv_m, mean);
+    if (vec)
+      bnf_partial<true, true><<<blocks, kThreads, 0, st>>>(s, xn, mean, part);
+    else
+      bnf_partial<false, true><<<blocks, kThreads, 0, st>>>(s, xn, mean, part);
+    bnf_fold<<<(unsigned)C, kThreads, 0, st>>>(part, s.nseg, inv_m, var);
+  }
+  if (bn) {
+    if (vec)
+      bnf_apply<true, true><<<blocks, kThreads, 0, st>>>(s, xn, y, mean, var, gamma, beta, eps,
+                                                          act, slope);
+    else
+      bnf_apply<false, true><<<blocks, kThreads, 0, st>>>(s, xn, y, mean, var, gamma, beta, eps,
+                                                           act, slope);
+  } else if (act != CBB_ACT_LINEAR) {
+    if (vec)
+      bnf_apply<true, false><<<blocks, kThreads, 0, st>>>(s, y, y, nullptr, nullptr, nullptr,
+                                                           nullptr, eps, act, slope);
+    else
+      bnf_apply<false, false><<<blocks, kThreads, 0, st>>>(s, y, y, nullptr, nullptr, nullptr,
+                                                            nullptr, eps, act, slope);
+  }
+  return check_launch("bnf_partial/bnf_fold/bnf_apply");
 }
 
 int launch_act_backward(int act, float slope, const float* y, const float* delta, float* g,

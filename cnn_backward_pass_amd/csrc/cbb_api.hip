@@ -146,6 +146,38 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
                              reinterpret_cast<float*>(ws + p.part_bytes), st);
 }
 
+int cbb_conv_block_forward_workspace_size(const cbb_conv_desc* desc, size_t* bytes) {
+  if (!bytes) return CBB_EINVAL;
+  ConvPlan p;
+  const int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  *bytes = p.part_bytes;
+  return CBB_OK;
+}
+
+int cbb_conv_block_forward(const cbb_conv_desc* desc, const float* x, const float* w,
+                           const float* bias, const float* gamma, const float* beta, float* mean,
+                           float* var, float* x_norm, float* y, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  ConvPlan p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  const int bn = desc->batch_normalize;
+  if (!x || !w || !y || y == x) return CBB_EINVAL;
+  if (bn && (!gamma || !beta || !mean || !var || !x_norm || bias)) return CBB_EINVAL;
+  if (!bn && (gamma || beta || mean || var || x_norm)) return CBB_EINVAL;
+  if (x_norm && (x_norm == y || x_norm == x)) return CBB_EINVAL;
+  if (!workspace || workspace_bytes < p.part_bytes || ((uintptr_t)workspace % kAlign))
+    return CBB_EWORKSPACE;
+  hipStream_t st = S(stream);
+  // z goes where it is consumed: into x_norm (normalised in place) or, without BN, into y
+  rc = launch_conv_forward(make_geom(*desc), x, w, bn ? nullptr : bias, bn ? x_norm : y, st);
+  if (rc) return rc;
+  return launch_bn_act_forward(desc->batch, desc->out_c, p.oh * p.ow, bn, desc->bn_eps, desc->act,
+                               desc->slope, gamma, beta, mean, var, bn ? x_norm : y, y, workspace,
+                               st);
+}
+
 int cbb_conv_fused_weights_data(const cbb_conv_desc* desc) {
   const int rc = check_desc(desc, nullptr);
   if (rc) return rc;

@@ -1,0 +1,156 @@
+// conv_fwd.hip -- forward convolution as an implicit GEMM on the gfx950 fp32
+// matrix cores, the first half of the conv block's forward (the saved tensors the
+// backward reads come from it).
+//
+// Pages: "YOLOv3 backpropagation: full-flow source analysis" (suzhouguqin.com),
+// sections 3.1-3.2: per image, im2col(x) then gemm(W, col) -- here one launch over
+// the whole batch with the im2col index map applied while staging (no column
+// buffer):
+//   z[n][o][q] = sum_j W[o][j] * B[j][q],   j = (i, kh, kw),  q = (ho, wo),
+//   B[j][q] = x[n][i][ho*S + kh*D - P][wo*S + kw*D - P]   (0 off the image).
+// Groups: the group index is blockIdx.y (group g owns output channels g*OC/G..,
+// input channels g*C/G.. and weight block g); ConvGeom holds the group's channel
+// counts and the whole tensors' image strides.
+#include "cbb_internal.h"
+
+namespace cbb {
+
+// k / d for k < 2^32 / d with one multiply-high: m = ceil(2^32 / d), exact in that
+// range (the error of the rounded-up reciprocal stays below 1/d).
+struct FastDiv {
+  uint32_t m, d;
+};
+static FastDiv make_fastdiv(uint32_t d) {
+  return FastDiv{d == 1 ? 0u : (uint32_t)(((uint64_t)1 << 32) / d + (((uint64_t)1 << 32) % d != 0)), d};
+}
+__device__ __forceinline__ uint32_t fdiv(uint32_t k, FastDiv f) {
+  return f.d == 1 ? k : __umulhi(k, f.m);
+}
+
+template <class TS>
+__global__ __launch_bounds__(kThreads) void conv_fwd_kernel(ConvGeom g, const float* __restrict__ x,
+                                                            const float* __restrict__ wt,
+                                                            const float* __restrict__ bias,
+                                                            float* __restrict__ z, int tiles_m,
+                                                            FastDiv div_kk, FastDiv div_k) {
+  static_assert(kThreads % TS::BN == 0 && kThreads % TS::BK == 0, "thread/tile mapping");
+  // group blockIdx.y (g holds the group's channel counts)
+  x += blockIdx.y * g.gx;
+  wt += blockIdx.y * g.gw;
+  z += blockIdx.y * g.gz;
+  if (bias) bias += blockIdx.y * (int64_t)g.OC;
+  __shared__ float lds[TS::LDS_FLOATS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
+  // the output-channel tiles of one pixel tile (the same x gathers) run together
+  const int m0 = (int)(blockIdx.x % (unsigned)tiles_m) * TS::BM;
+  const int64_t n0 = (int64_t)(blockIdx.x / (unsigned)tiles_m) * TS::BN;
+  const int KK = g.K * g.K;
+
+  // B: this thread stages pixel column pcol for K rows krow0 + KSTEP*r
+  constexpr int KSTEP = kThreads / TS::BN;
+  const int pcol = tid % TS::BN, krow0 = tid / TS::BN;
+  const int64_t q = n0 + pcol;
+  const bool qv = q < g.Q;
+  int hb = 0, wb = 0;
+  const float* xb = x;
+  if (qv) {
+    const int b = (int)(q / g.OHW), r = (int)(q - (int64_t)b * g.OHW);
+    const int ho = r / g.OW, wo = r - ho * g.OW;
+    hb = ho * g.S - g.P;
+    wb = wo * g.S - g.P;
+    xb = x + (int64_t)b * g.xs;
+  }
+  // A: this thread stages K column acol for output-channel rows irow0 + ISTEP*r
+  constexpr int ISTEP = kThreads / TS::BK;
+  const int acol = tid % TS::BK, irow0 = tid / TS::BK;
+
+  // Loads go to registers as they are (out-of-range elements from a clamped valid
+  // address); the zero padding is applied at the LDS store, so the loads stay in
+  // flight during the matrix-core work.
+  static_assert(TS::A_PER_T <= 32 && TS::B_PER_T <= 32, "one mask bit per staged element");
+  float ra[TS::A_PER_T], rb[TS::B_PER_T];
+  uint32_t am = 0, bm = 0;
+  auto load = [&](int64_t k0l) {
+    const int k0 = (int)k0l;
+    {  // A = weights W[o][j]
+      const int j = k0 + acol;
+      const bool jv = j < g.J;
+      am = 0;
+#pragma unroll
+      for (int r = 0; r < TS::A_PER_T; ++r) {
+        const int o = m0 + irow0 + ISTEP * r;
+        const bool ok = jv && o < g.OC;
+        ra[r] = wt[ok ? (int64_t)o * g.J + j : 0];
+        am |= (uint32_t)ok << r;
+      }
+    }
+    bm = 0;
+#pragma unroll
+    for (int r = 0; r < TS::B_PER_T; ++r) {  // B = im2col(x)
+      const int j = k0 + krow0 + KSTEP * r;
+      const int i = (int)fdiv((uint32_t)j, div_kk);
+      const int rem = j - i * KK;
+      const int kh = (int)fdiv((uint32_t)rem, div_k), kw = rem - kh * g.K;
+      const int h = hb + kh * g.D, w = wb + kw * g.D;
+      const bool ok = qv && j < g.J && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+      rb[r] = xb[ok ? (int64_t)i * g.HW + h * g.W + w : 0];
+      bm |= (uint32_t)ok << r;
+    }
+  };
+  auto store = [&](float* buf) {
+    float* As = buf;
+    float* Bs = buf + TS::BK * TS::LDA;
+#pragma unroll
+    for (int r = 0; r < TS::A_PER_T; ++r)
+      As[acol * TS::LDA + irow0 + ISTEP * r] = ((am >> r) & 1u) ? ra[r] : 0.f;
+#pragma unroll
+    for (int r = 0; r < TS::B_PER_T; ++r)
+      Bs[(krow0 + KSTEP * r) * TS::LDB + pcol] = ((bm >> r) & 1u) ? rb[r] : 0.f;
+  };
+
+  Acc<TS> acc;
+  acc.zero();
+  gemm_mainloop<TS>(lds, 0, g.J, load, store, acc, wm, wn, wk, lane);
+  reduce_wk<TS>(acc, lds, wm, wn, wk, lane);
+  if (wk != 0) return;
+#pragma unroll
+  for (int aj = 0; aj < TS::RN; ++aj) {
+    const int64_t qq = n0 + acc_n0<TS>(wn, aj) + acc_col(lane);
+    if (qq >= g.Q) continue;
+    const int b = (int)(qq / g.OHW), p = (int)(qq - (int64_t)b * g.OHW);
+    float* zb = z + (int64_t)b * g.zs + p;
+#pragma unroll
+    for (int ai = 0; ai < TS::RM; ++ai)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = m0 + acc_m0<TS>(wm, ai) + acc_row(r, lane);
+        if (o < g.OC) zb[(int64_t)o * g.OHW] = acc.v[ai][aj][r] + (bias ? bias[o] : 0.f);
+      }
+  }
+}
+
+// z = conv(x, W) (+ bias).  g is the whole layer's geometry; a grouped layer runs
+// all groups in one launch on the group geometry.
+int launch_conv_forward(const ConvGeom& g, const float* x, const float* wt, const float* bias,
+                        float* z, hipStream_t st) {
+  ConvGeom s = g;
+  s.C = g.C / g.G;
+  s.OC = g.OC / g.G;
+  s.J = s.C * g.K * g.K;
+  const FastDiv dkk = make_fastdiv((uint32_t)(g.K * g.K)), dk = make_fastdiv((uint32_t)g.K);
+  if (s.OC <= 32) {
+    using TS = TileShape<1, 4, 1>;   // 32 output channels x 128 pixels
+    const int tm = (int)ceil_div(s.OC, TS::BM);
+    const dim3 grid((unsigned)(tm * ceil_div(g.Q, TS::BN)), (unsigned)g.G);
+    conv_fwd_kernel<TS><<<grid, kThreads, 0, st>>>(s, x, wt, bias, z, tm, dkk, dk);
+  } else {
+    using TS = TileShape<2, 2, 1>;   // 64 x 64
+    const int tm = (int)ceil_div(s.OC, TS::BM);
+    const dim3 grid((unsigned)(tm * ceil_div(g.Q, TS::BN)), (unsigned)g.G);
+    conv_fwd_kernel<TS><<<grid, kThreads, 0, st>>>(s, x, wt, bias, z, tm, dkk, dk);
+  }
+  return check_launch("conv_fwd_kernel");
+}
+
+}  // namespace cbb

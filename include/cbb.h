@@ -165,6 +165,27 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
                             float* db, float* dgamma, float* dx, int dx_accumulate,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* ----------------------------------------------------------------------------
+ * Conv block forward: the tensors the backward reads, computed on the device
+ * (forward_convolutional_layer of [P1] sections 3.1-3.2 with forward_batchnorm_layer
+ * of [P1] section 4 and the *_activate functions of section 7):
+ *   z = conv(x, W)  (+ bias[o] when batch_normalize = NONE; NULL bias = 0)
+ *   BATCH: mean[o] = mean of z over (batch, space), var[o] = E[(z - mean)^2] (biased),
+ *          both written;  FIXED: mean, var read (stored statistics)
+ *   x_norm = (z - mean)/sqrt(var + eps),  u = gamma x_norm + beta  (BN),  u = z (no BN)
+ *   y = act(u)
+ * Shapes as in cbb_conv_block_backward; with BN, x_norm, mean, var, gamma, beta are
+ * required and bias must be NULL (the BN shift absorbs it); without BN they must
+ * be NULL.  y and x_norm must not overlap x or each other.  Workspace: at least
+ * cbb_conv_block_forward_workspace_size bytes, 256-byte aligned.  The rolling
+ * averages Darknet / Caffe keep for inference are not updated.
+ * ------------------------------------------------------------------------- */
+int cbb_conv_block_forward_workspace_size(const cbb_conv_desc* desc, size_t* bytes);
+int cbb_conv_block_forward(const cbb_conv_desc* desc, const float* x, const float* w,
+                           const float* bias, const float* gamma, const float* beta, float* mean,
+                           float* var, float* x_norm, float* y, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* The three stages of cbb_conv_block_backward as separate calls (Caffe splits
  * the same work into backward_cpu_bias / weight_cpu_gemm / backward_cpu_gemm,
  * [P4] BaseConvolutionLayer).  Enqueued one after another on one stream with

@@ -151,6 +151,20 @@ def test_other_entry_points_validate():
     assert L.cbb_fc_softmax_backward(4, 8, 10, BOGUS, None, 1.0, *[BOGUS] * 6, None, None) == -1
     assert L.cbb_shortcut_backward(16, 1.0, 1.0, BOGUS, BOGUS, BOGUS, None) == -1  # aliasing
     X = ctypes.c_void_p(0x3000)
+    d = _desc()                       # BN, leaky
+    F = L.cbb_conv_block_forward
+    Y, XN = ctypes.c_void_p(0x4000), ctypes.c_void_p(0x5000)
+    assert F(ctypes.byref(d), BOGUS, BOGUS, None, None, BOGUS, BOGUS, BOGUS, XN, Y, BOGUS,
+             1 << 30, None) == -1                                   # BN without gamma
+    assert F(ctypes.byref(d), BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, BOGUS, XN, Y, BOGUS,
+             1 << 30, None) == -1                                   # bias with BN
+    assert F(ctypes.byref(d), BOGUS, BOGUS, None, BOGUS, BOGUS, BOGUS, BOGUS, Y, Y, BOGUS,
+             1 << 30, None) == -1                                   # x_norm aliases y
+    assert F(ctypes.byref(d), BOGUS, BOGUS, None, BOGUS, BOGUS, BOGUS, BOGUS, XN, Y, BOGUS,
+             0, None) == -4                                         # workspace too small
+    dl = _desc(batch_normalize=0, act="linear")
+    assert F(ctypes.byref(dl), BOGUS, BOGUS, None, BOGUS, None, None, None, None, Y, BOGUS,
+             1 << 30, None) == -1                                   # gamma without BN
     assert L.cbb_softmax_backward(0, 10, 1, BOGUS, X, X, None) == -1
     assert L.cbb_softmax_backward(4, 10, 1, BOGUS, X, BOGUS, None) == -1       # dx aliases y
     assert L.cbb_softmax_backward(4, 10, 0, BOGUS, X, X, None) == -1
