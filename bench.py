@@ -238,6 +238,23 @@ def time_variants(torch, reps=10):
         out[f"conv_dW.{name}.8x{c}x52x52"] = _roof(ms, 2.0 * macs, by)
         ms = timed(lambda: cbb.conv_backward_data(dsc, w, dz, dx, False, wsc))
         out[f"conv_dX.{name}.8x{c}x52x52"] = _roof(ms, 2.0 * macs, by)
+    # the block forward (cbb_conv_block_forward: convolution, batch statistics, BN and
+    # activation in one call) at three workload layers; FLOPs of the convolution only
+    for name, (n, c, hw, oc, s) in (("yolov3_stem_conv1", (16, 3, 416, 32, 1)),
+                                    ("yolov3_stem_conv2", (16, 32, 416, 64, 2)),
+                                    ("darknet53_residual_conv2", (8, 128, 52, 256, 1))):
+        dsc = cbb.conv_desc(n, c, hw, hw, oc, 3, s, 1, 1, "leaky")
+        oh = dsc.out_h
+        x, w = rn(n, c, hw, hw), rn(oc, c, 3, 3) * 0.1
+        gam, bet = torch.ones(oc, device=dev), torch.zeros(oc, device=dev)
+        mu, va = torch.empty(oc, device=dev), torch.empty(oc, device=dev)
+        xn, yy = torch.empty(n, oc, oh, oh, device=dev), torch.empty(n, oc, oh, oh, device=dev)
+        wsf = cbb.workspace(cbb.conv_block_forward_workspace_size(dsc), dev)
+        ms = timed(lambda: cbb.conv_block_forward(dsc, x, w, None, gam, bet, mu, va, xn, yy, wsf))
+        macs = float(n) * oc * oh * oh * c * 9
+        out[f"forward.{name}"] = _roof(ms, 2.0 * macs,
+                                       4.0 * (x.numel() + w.numel() + 2 * xn.numel()))
+        del x, xn, yy
     return out
 
 

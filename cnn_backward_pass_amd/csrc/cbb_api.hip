@@ -151,7 +151,9 @@ int cbb_conv_block_forward_workspace_size(const cbb_conv_desc* desc, size_t* byt
   ConvPlan p;
   const int rc = check_desc(desc, &p);
   if (rc) return rc;
-  *bytes = p.part_bytes;
+  // enough for either route (a bias keeps the forward on the general kernel, which
+  // needs no scratch beyond the batch-norm partials)
+  *bytes = p.part_bytes + align_up(conv_forward_workspace(make_geom(*desc), false), kAlign);
   return CBB_OK;
 }
 
@@ -167,11 +169,15 @@ int cbb_conv_block_forward(const cbb_conv_desc* desc, const float* x, const floa
   if (bn && (!gamma || !beta || !mean || !var || !x_norm || bias)) return CBB_EINVAL;
   if (!bn && (gamma || beta || mean || var || x_norm)) return CBB_EINVAL;
   if (x_norm && (x_norm == y || x_norm == x)) return CBB_EINVAL;
-  if (!workspace || workspace_bytes < p.part_bytes || ((uintptr_t)workspace % kAlign))
+  const ConvGeom g = make_geom(*desc);
+  const size_t need = p.part_bytes + align_up(conv_forward_workspace(g, bias != nullptr), kAlign);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign))
     return CBB_EWORKSPACE;
   hipStream_t st = S(stream);
   // z goes where it is consumed: into x_norm (normalised in place) or, without BN, into y
-  rc = launch_conv_forward(make_geom(*desc), x, w, bn ? nullptr : bias, bn ? x_norm : y, st);
+  rc = launch_conv_forward(g, x, w, bn ? nullptr : bias, bn ? x_norm : y,
+                           reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_bytes),
+                           st);
   if (rc) return rc;
   return launch_bn_act_forward(desc->batch, desc->out_c, p.oh * p.ow, bn, desc->bn_eps, desc->act,
                                desc->slope, gamma, beta, mean, var, bn ? x_norm : y, y, workspace,

@@ -265,8 +265,10 @@ int launch_act_backward(int act, float slope, const float* y, const float* delta
 int launch_bn_act_forward(int N, int C, int64_t HW, int bn, float eps, int act, float slope,
                           const float* gamma, const float* beta, float* mean, float* var,
                           float* xn, float* y, void* ws, hipStream_t st);
+bool conv_dx_specialised(const ConvGeom& g);
+size_t conv_forward_workspace(const ConvGeom& g, bool has_bias);
 int launch_conv_forward(const ConvGeom& g, const float* x, const float* wt, const float* bias,
-                        float* z, hipStream_t st);
+                        float* z, float* ws, hipStream_t st);
 int launch_shortcut(int64_t count, float alpha, float beta, const float* delta, float* d_main,
                     float* d_from, hipStream_t st);
 int launch_shortcut_resize(int batch, int w1, int h1, int c1, int w2, int h2, int c2, float alpha,

@@ -2023,6 +2023,14 @@ static DxPlan plan_dx(const ConvGeom& g) {
   return p;
 }
 
+// 1 when launch_conv_dx runs a specialised kernel for g (tile-direct 3x3 or the 1x1
+// copy ring), not the general one.
+bool conv_dx_specialised(const ConvGeom& g) {
+  if (!dense(g)) return false;
+  const DxPlan p = plan_dx(g);
+  return p.kind == DX_D3S1 || p.kind == DX_D3S1_SMALL || p.kind == DX_D3S2 || p.kind == DX_1X1;
+}
+
 size_t conv_dx_workspace(const ConvGeom& g) {
   if (conv_depthwise(g)) return 0;
   // grouped: every group writes its channels of the same [split][n][c][hw] partials

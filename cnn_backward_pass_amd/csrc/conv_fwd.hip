@@ -130,10 +130,71 @@ __global__ __launch_bounds__(kThreads) void conv_fwd_kernel(ConvGeom g, const fl
   }
 }
 
+// ---------------------------------------------------------------------------
+// A plain stride-1 forward is the input gradient of another convolution:
+//   z[n][o][h][w] = sum_{i,kh,kw} W[o][i][kh][kw] x[n][i][h + kh - P][w + kw - P]
+//                 = sum_{i,kh,kw} W'[i][o][kh][kw] x[n][i][h + P' - kh][w + P' - kw]
+// with W'[i][o][kh][kw] = W[o][i][K-1-kh][K-1-kw] and P' = K-1-P: the dX of a
+// convolution whose input has OC channels of OH x OW and whose output has C
+// channels of H x W (stride 1, pad P'), with dz := x and weights W'.  So the
+// tiled input-gradient kernels compute the forward of the layers they cover.
+// ---------------------------------------------------------------------------
+static ConvGeom transposed_geom(const ConvGeom& g) {
+  cbb_conv_desc d{};
+  d.batch = g.N;
+  d.in_c = g.OC;
+  d.in_h = g.OH;
+  d.in_w = g.OW;
+  d.out_c = g.C;
+  d.ksize = g.K;
+  d.stride = 1;
+  d.pad = g.K - 1 - g.P;
+  return make_geom(d);
+}
+
+static bool forward_as_dx(const ConvGeom& g, bool has_bias) {
+  return !has_bias && g.G == 1 && g.D == 1 && g.S == 1 && g.P <= g.K - 1 &&
+         conv_dx_specialised(transposed_geom(g));
+}
+
+__global__ __launch_bounds__(kThreads) void flip_transpose_weights(const float* __restrict__ w,
+                                                                   float* __restrict__ wt, int oc,
+                                                                   int c, int k) {
+  const int kk = k * k;
+  const int64_t n = (int64_t)oc * c * kk;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * kThreads) {
+    const int t = (int)(e % kk);
+    const int64_t oi = e / kk;
+    const int i = (int)(oi % c), o = (int)(oi / c);
+    const int kh = t / k, kw = t - kh * k;
+    wt[((int64_t)i * oc + o) * kk + (k - 1 - kh) * k + (k - 1 - kw)] = w[e];
+  }
+}
+
+// Scratch of the forward beyond the batch-norm partials: the flipped weights and
+// the input-gradient kernel's own workspace when the forward runs as a dX.
+size_t conv_forward_workspace(const ConvGeom& g, bool has_bias) {
+  if (!forward_as_dx(g, has_bias)) return 0;
+  const size_t wbytes = align_up((size_t)g.OC * g.C * g.K * g.K * sizeof(float), 256);
+  return wbytes + conv_dx_workspace(transposed_geom(g));
+}
+
 // z = conv(x, W) (+ bias).  g is the whole layer's geometry; a grouped layer runs
 // all groups in one launch on the group geometry.
 int launch_conv_forward(const ConvGeom& g, const float* x, const float* wt, const float* bias,
-                        float* z, hipStream_t st) {
+                        float* z, float* ws, hipStream_t st) {
+  if (forward_as_dx(g, bias != nullptr)) {
+    const ConvGeom t = transposed_geom(g);
+    float* wflip = ws;
+    float* ws2 = ws + align_up((size_t)g.OC * g.C * g.K * g.K * sizeof(float), 256) / sizeof(float);
+    const int64_t n = (int64_t)g.OC * g.C * g.K * g.K;
+    flip_transpose_weights<<<(unsigned)std::min<int64_t>(ceil_div(n, kThreads), 4096), kThreads, 0,
+                             st>>>(wt, wflip, g.OC, g.C, g.K);
+    const int rc = check_launch("flip_transpose_weights");
+    if (rc) return rc;
+    return launch_conv_dx(t, wflip, x, z, 0, ws2, st);
+  }
   ConvGeom s = g;
   s.C = g.C / g.G;
   s.OC = g.OC / g.G;
