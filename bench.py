@@ -63,7 +63,7 @@ def profile_stage(spec, reps, torch):
     from cnn_backward_pass_amd.workloads import Runner
     r = Runner(name, synth.inputs(name), synth.saved_standins(name), "cuda:0")
     r.reset()
-    if stage != "act_bn":
+    if stage not in ("act_bn", "block"):
         r.run_stage(li, "act_bn")
     torch.cuda.synchronize()
     ms = []
@@ -110,6 +110,11 @@ def stage_work(runner, li, stage):
         # reads delta, y, x_hat and writes dz (BN); bias-only: reads delta (+ y)
         per = (16 if c.bn else (12 if c.act != "linear" else 4))
         return 0.0, float(per * out_elems)
+    if stage == "block":
+        # act/BN stage and the fused dW + dX kernel with dz formed in place: x, W and the
+        # saved delta, y, x_hat read once; dW, dx written
+        nread = 1 + (c.act != "linear") + bool(c.bn)
+        return 4.0 * macs, 4.0 * (2 * in_elems + nread * out_elems + 2 * w_elems)
     if stage == "dWdX":  # both gradients from one read of dz: x, dz, W read; dW, dx written
         return 4.0 * macs, 4.0 * (2 * in_elems + out_elems + 2 * w_elems)
     return 2.0 * macs, 4.0 * (in_elems + out_elems + w_elems)
@@ -415,7 +420,11 @@ def main():
             "act_bn_stages": {f"{n}.{li}": {
                 "ms": round(ms, 4),
                 "algorithmic_GBps": round(stage_work(runners[n], li, st)[1] / (ms * 1e-3) / 1e9, 1)}
-                for ms, n, li, st in stages if st == "act_bn" and ms > 0.05}}
+                for ms, n, li, st in stages if st == "act_bn" and ms > 0.05},
+            # layers whose dz is formed inside the fused dW + dX kernel: the act/BN
+            # reduction, the per-channel map and that kernel, timed together
+            "fused_dz_blocks": {f"{n}.{li}": _roof(ms, *stage_work(runners[n], li, st))
+                                for ms, n, li, st in stages if st == "block"}}
     print("[bench] variants", file=sys.stderr, flush=True)
     line["variants"] = time_variants(torch)
     if not args.no_cpu_baseline:

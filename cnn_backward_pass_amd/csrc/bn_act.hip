@@ -22,30 +22,6 @@
 
 namespace cbb {
 
-// Activation derivative read from the activation output y, as Darknet's
-// *_gradient functions compute it ("YOLOv3 backpropagation", section 7).
-__device__ __forceinline__ float act_grad(int act, float slope, float y) {
-  switch (act) {
-    case CBB_ACT_LEAKY: return y > 0.f ? 1.f : slope;
-    case CBB_ACT_LOGISTIC: return (1.f - y) * y;
-    case CBB_ACT_RELU: return y > 0.f ? 1.f : 0.f;
-    case CBB_ACT_TANH: return 1.f - y * y;
-    case CBB_ACT_ELU: return y >= 0.f ? 1.f : y + 1.f;
-    case CBB_ACT_SELU: return y >= 0.f ? 1.0507f : y + 1.0507f * 1.6732f;
-    case CBB_ACT_PLSE: return (y < 0.f || y > 1.f) ? .01f : .125f;
-    case CBB_ACT_LHTAN: return (y > 0.f && y < 1.f) ? 1.f : .001f;
-    case CBB_ACT_HARDTAN: return (y > -1.f && y < 1.f) ? 1.f : 0.f;
-    case CBB_ACT_STAIR: return floorf(y) == y ? 0.f : 1.f;
-    case CBB_ACT_RAMP: return (y > 0.f ? 1.f : 0.f) + .1f;
-    case CBB_ACT_RELIE: return y > 0.f ? 1.f : .01f;
-    case CBB_ACT_LOGGY: {
-      const float s = (y + 1.f) * .5f;
-      return 2.f * (1.f - s) * s;
-    }
-    default: return 1.f;
-  }
-}
-
 // The streaming kernels take the activation as a template argument for the four
 // the networks use (no branch in the loop); kActAny takes it from `act_rt`.
 constexpr int kActAny = -1;
@@ -132,7 +108,7 @@ template <bool VEC, int ACT, int BN>
 __global__ __launch_bounds__(kThreads) void actbn_reduce(
     SegGeom s, const float* delta, const float* __restrict__ y, const float* __restrict__ xn,
     float slope, int act_rt, const float* __restrict__ var, const float* __restrict__ gamma,
-    float eps, float* dz /* fixed statistics only; may alias delta */,
+    float eps, float* dz /* fixed statistics only, NULL: not written; may alias delta */,
     float2* __restrict__ part) {
   const int c = blockIdx.x / s.nseg, sg = blockIdx.x % s.nseg;
   float sg_ = 0.f, sgx = 0.f;
@@ -154,7 +130,7 @@ __global__ __launch_bounds__(kThreads) void actbn_reduce(
         const float4 x = ld4(xn + o);
         sgx += (d.x * x.x + d.y * x.y) + (d.z * x.z + d.w * x.w);
       }
-      if (fixed)
+      if (fixed && dz)
         *reinterpret_cast<float4*>(dz + o) = make_float4(ka * d.x, ka * d.y, ka * d.z, ka * d.w);
     });
   } else {
@@ -163,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void actbn_reduce(
       if (has_y) d *= act_grad(act, slope, y[o]);
       sg_ += d;
       if (has_x) sgx += d * xn[o];
-      if (fixed) dz[o] = ka * d;
+      if (fixed && dz) dz[o] = ka * d;
     });
   }
   __shared__ float red[4];
@@ -256,6 +232,37 @@ __global__ __launch_bounds__(kThreads) void actbn_fold(const float2* __restrict_
     dbeta[c] += sums.x;
     dgamma[c] += sums.y;
   }
+}
+
+// Pass 2 when dz is formed later by its consumer: one work-group per channel
+// folds the sums (the order actbn_apply uses), adds them into dgamma / dbeta (or
+// db) and writes the channel's map dz = a*g + b + cc*x_norm as coef[c], coef[C+c],
+// coef[2C+c] (no BN: a = 1; fixed statistics: b = cc = 0).
+__global__ __launch_bounds__(kThreads) void actbn_coef(const float2* __restrict__ part, int nseg,
+                                                       int64_t M, int C, int bn,
+                                                       const float* __restrict__ var,
+                                                       const float* __restrict__ gamma, float eps,
+                                                       float* __restrict__ dgamma,
+                                                       float* __restrict__ dbeta_or_db,
+                                                       float* __restrict__ coef) {
+  __shared__ float red[4];
+  const int c = blockIdx.x;
+  const float2 sums = fold_partials(part, c, nseg, red);
+  if (threadIdx.x != 0) return;
+  dbeta_or_db[c] += sums.x;
+  float ka = 1.f, kb = 0.f, kc = 0.f;
+  if (bn != kBnNone) {
+    dgamma[c] += sums.y;
+    ka = gamma[c] / sqrtf(var[c] + eps);
+    if (bn == kBnBatch) {
+      const float inv_m = 1.f / (float)M;
+      kb = -ka * (sums.x * inv_m);
+      kc = -ka * (sums.y * inv_m);
+    }
+  }
+  coef[c] = ka;
+  coef[C + c] = kb;
+  coef[2 * C + c] = kc;
 }
 
 __global__ __launch_bounds__(kThreads) void act_backward_kernel(int act, float slope,
@@ -452,10 +459,15 @@ template <bool VEC, int ACT, int BN>
 static void launch_actbn_t(const SegGeom& s, unsigned blocks, int act, const float* delta,
                            const float* y, const float* xn, float slope, const float* var,
                            const float* gamma, float eps, float* dz, float* dgamma,
-                           float* dbeta_or_db, float2* part, int write_dz, hipStream_t st) {
+                           float* dbeta_or_db, float2* part, int write_dz, float* coef,
+                           hipStream_t st) {
   actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(
-      s, delta, y, BN != kBnNone ? xn : nullptr, slope, act, var, gamma, eps, dz, part);
-  if constexpr (BN == kBnFixed)
+      s, delta, y, BN != kBnNone ? xn : nullptr, slope, act, var, gamma, eps,
+      coef ? nullptr : dz, part);
+  if (coef)
+    actbn_coef<<<(unsigned)s.C, kThreads, 0, st>>>(part, s.nseg, s.M, s.C, BN, var, gamma, eps,
+                                                  dgamma, dbeta_or_db, coef);
+  else if constexpr (BN == kBnFixed)
     actbn_fold<<<(unsigned)s.C, kThreads, 0, st>>>(part, s.nseg, dgamma, dbeta_or_db);
   else
     actbn_apply<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, slope, act, part, var,
@@ -467,10 +479,11 @@ template <bool VEC, int ACT>
 static void launch_actbn_a(const SegGeom& s, unsigned blocks, int act, int bn, const float* delta,
                            const float* y, const float* xn, float slope, const float* var,
                            const float* gamma, float eps, float* dz, float* dgamma,
-                           float* dbeta_or_db, float2* part, int write_dz, hipStream_t st) {
+                           float* dbeta_or_db, float2* part, int write_dz, float* coef,
+                           hipStream_t st) {
 #define CBB_ACTBN(B)                                                                        \
   launch_actbn_t<VEC, ACT, B>(s, blocks, act, delta, y, xn, slope, var, gamma, eps, dz, dgamma, \
-                              dbeta_or_db, part, write_dz, st)
+                              dbeta_or_db, part, write_dz, coef, st)
   if (bn == kBnFixed)
     CBB_ACTBN(kBnFixed);
   else if (bn == kBnBatch)
@@ -484,10 +497,11 @@ template <bool VEC>
 static void launch_actbn_v(const SegGeom& s, unsigned blocks, int act, int bn, const float* delta,
                            const float* y, const float* xn, float slope, const float* var,
                            const float* gamma, float eps, float* dz, float* dgamma,
-                           float* dbeta_or_db, float2* part, int write_dz, hipStream_t st) {
+                           float* dbeta_or_db, float2* part, int write_dz, float* coef,
+                           hipStream_t st) {
 #define CBB_ACTBN(A)                                                                          \
   launch_actbn_a<VEC, A>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma, \
-                         dbeta_or_db, part, write_dz, st)
+                         dbeta_or_db, part, write_dz, coef, st)
   switch (act) {
     case CBB_ACT_LINEAR: CBB_ACTBN(CBB_ACT_LINEAR); break;
     case CBB_ACT_LEAKY: CBB_ACTBN(CBB_ACT_LEAKY); break;
@@ -499,10 +513,12 @@ static void launch_actbn_v(const SegGeom& s, unsigned blocks, int act, int bn, c
 }
 
 // g/BN stage of a conv block, or a standalone BN backward (act = LINEAR).
-// bn: 0 none (db += sum g), 1 batch statistics, 2 fixed statistics.
+// bn: 0 none (db += sum g), 1 batch statistics, 2 fixed statistics.  coef != NULL:
+// dz is not written; the per-channel map that forms it goes to coef[3C] instead.
 int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, const float* xn,
                  int act, float slope, const float* var, const float* gamma, float eps, int bn,
-                 float* dz, float* dgamma, float* dbeta_or_db, void* ws, hipStream_t st) {
+                 float* dz, float* dgamma, float* dbeta_or_db, void* ws, hipStream_t st,
+                 float* coef) {
   const SegGeom s = plan_seg(N, C, HW);
   float2* part = reinterpret_cast<float2*>(ws);
   const bool vec = (HW % 4 == 0) && aligned16(delta) && (!y || aligned16(y)) &&
@@ -511,10 +527,10 @@ int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, c
   const int write_dz = bn || act != CBB_ACT_LINEAR;
   if (vec)
     launch_actbn_v<true>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma,
-                         dbeta_or_db, part, write_dz, st);
+                         dbeta_or_db, part, write_dz, coef, st);
   else
     launch_actbn_v<false>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma,
-                          dbeta_or_db, part, write_dz, st);
+                          dbeta_or_db, part, write_dz, coef, st);
   return check_launch("actbn_reduce/actbn_apply");
 }
 

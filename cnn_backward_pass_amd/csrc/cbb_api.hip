@@ -66,7 +66,10 @@ int check_desc(const cbb_conv_desc* d, ConvPlan* plan) {
     plan->oh = oh;
     plan->ow = ow;
     const ConvGeom g = make_geom(*d);
-    plan->part_bytes = align_up(actbn_workspace(d->batch, d->out_c, oh * ow), kAlign);
+    // act/BN partials, then the per-channel map of a block whose dz is formed by
+    // the gradient kernel (3 floats per channel)
+    plan->part_bytes = align_up(actbn_workspace(d->batch, d->out_c, oh * ow), kAlign) +
+                       align_up((size_t)3 * d->out_c * sizeof(float), kAlign);
     // dW and dX run one after the other on the stream (or as one fused kernel)
     // and share the second region
     plan->dw_bytes = align_up(
@@ -131,18 +134,36 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
   if (bn && (!x_norm || !var || !gamma || !dgamma)) return CBB_EINVAL;
   if (!bn && (x_norm || var || gamma || dgamma)) return CBB_EINVAL;
   const bool passthrough = act == CBB_ACT_LINEAR && !bn;  // dz is delta itself
-  if (!passthrough && !dz) return CBB_EINVAL;
+  const ConvGeom g = make_geom(*desc);
+  // dz = NULL: not stored; the fused dW + dX kernel forms it as it stages delta
+  const bool form_dz = !passthrough && !dz;
+  if (form_dz) {
+    auto a16 = [](const void* q) { return !q || (uintptr_t)q % 16 == 0; };
+    if (!dx || !conv_fused_dwdx_ok(g) || !a16(x) || !a16(delta) || !a16(y) || !a16(x_norm))
+      return CBB_EINVAL;
+  }
   if (dx_accumulate != 0 && dx_accumulate != 1) return CBB_EINVAL;
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return CBB_EWORKSPACE;
   if (workspace && ((uintptr_t)workspace % kAlign)) return CBB_EWORKSPACE;
 
   hipStream_t st = S(stream);
   char* ws = static_cast<char*>(workspace);
+  if (form_dz) {
+    float* coef = reinterpret_cast<float*>(
+        ws + align_up(actbn_workspace(desc->batch, desc->out_c, p.oh * p.ow), kAlign));
+    rc = launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
+                      var, gamma, desc->bn_eps, bn, nullptr, dgamma, db, ws, st, coef);
+    if (rc) return rc;
+    const DzSource src{act == CBB_ACT_LINEAR ? nullptr : y,
+                       bn == CBB_BN_BATCH ? x_norm : nullptr, coef, act, desc->slope};
+    return launch_conv_fused_dwdx(g, x, w, delta, dw, dx, dx_accumulate,
+                                  reinterpret_cast<float*>(ws + p.part_bytes), st, &src);
+  }
   const float* dz_eff = passthrough ? delta : dz;
   rc = launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
                     var, gamma, desc->bn_eps, bn, passthrough ? nullptr : dz, dgamma, db, ws, st);
   if (rc) return rc;
-  return launch_weights_data(make_geom(*desc), x, w, dz_eff, dw, dx, dx_accumulate,
+  return launch_weights_data(g, x, w, dz_eff, dw, dx, dx_accumulate,
                              reinterpret_cast<float*>(ws + p.part_bytes), st);
 }
 

@@ -250,16 +250,53 @@ size_t conv_dw_workspace(const ConvGeom& g);
 int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
                    hipStream_t st);
 size_t conv_dx_workspace(const ConvGeom& g);
+// Activation derivative read from the activation output y, as Darknet's
+// *_gradient functions compute it ("YOLOv3 backpropagation", section 7).
+__device__ __forceinline__ float act_grad(int act, float slope, float y) {
+  switch (act) {
+    case CBB_ACT_LEAKY: return y > 0.f ? 1.f : slope;
+    case CBB_ACT_LOGISTIC: return (1.f - y) * y;
+    case CBB_ACT_RELU: return y > 0.f ? 1.f : 0.f;
+    case CBB_ACT_TANH: return 1.f - y * y;
+    case CBB_ACT_ELU: return y >= 0.f ? 1.f : y + 1.f;
+    case CBB_ACT_SELU: return y >= 0.f ? 1.0507f : y + 1.0507f * 1.6732f;
+    case CBB_ACT_PLSE: return (y < 0.f || y > 1.f) ? .01f : .125f;
+    case CBB_ACT_LHTAN: return (y > 0.f && y < 1.f) ? 1.f : .001f;
+    case CBB_ACT_HARDTAN: return (y > -1.f && y < 1.f) ? 1.f : 0.f;
+    case CBB_ACT_STAIR: return floorf(y) == y ? 0.f : 1.f;
+    case CBB_ACT_RAMP: return (y > 0.f ? 1.f : 0.f) + .1f;
+    case CBB_ACT_RELIE: return y > 0.f ? 1.f : .01f;
+    case CBB_ACT_LOGGY: {
+      const float s = (y + 1.f) * .5f;
+      return 2.f * (1.f - s) * s;
+    }
+    default: return 1.f;
+  }
+}
+
 bool conv_fused_dwdx_ok(const ConvGeom& g);
 size_t conv_fused_workspace(const ConvGeom& g);
+// dz of a block formed while it is staged instead of read back: with dz = delta,
+// g = delta * act'(y) and the per-channel map of the BN backward,
+//   dz[c] = coef[c] * g + coef[C + c] + coef[2C + c] * x_norm
+// (y NULL: act linear; xn NULL: the third term is absent).
+struct DzSource {
+  const float* y;
+  const float* xn;
+  const float* coef;
+  int act;
+  float slope;
+};
 int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
-                           float* dw, float* dx, int accumulate, float* ws, hipStream_t st);
+                           float* dw, float* dx, int accumulate, float* ws, hipStream_t st,
+                           const DzSource* src = nullptr);
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
                    float* ws, hipStream_t st);
 size_t actbn_workspace(int N, int C, int64_t HW);
 int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, const float* xn,
                  int act, float slope, const float* var, const float* gamma, float eps, int bn,
-                 float* dz, float* dgamma, float* dbeta_or_db, void* ws, hipStream_t st);
+                 float* dz, float* dgamma, float* dbeta_or_db, void* ws, hipStream_t st,
+                 float* coef = nullptr);
 int launch_act_backward(int act, float slope, const float* y, const float* delta, float* g,
                         int64_t count, hipStream_t st);
 int launch_bn_act_forward(int N, int C, int64_t HW, int bn, float eps, int act, float slope,

@@ -1370,11 +1370,19 @@ __global__ __launch_bounds__(kThreads) void conv_dx_smallc_kernel(ConvGeom g,
 // odd row pitch: the dW operand reads one column across 32 channel rows
 constexpr int kFrThreads = 256, kFrPitch = 133, kFrMaxW = 120;
 
-template <int CI, bool ACC>
-__global__ __launch_bounds__(kFrThreads, 3) void conv_first_rows(
+//
+// FZ != kFzOff: dz is not read back but formed as it is staged, from delta (the
+// dz argument), y and x_norm with the per-channel map of the BN backward
+// (DzSource): the write and the re-read of dz by a separate pass disappear.  FZ
+// is the activation (kFzAny: the run-time src.act), so the per-element
+// derivative compiles to straight-line code for the common ones.
+constexpr int kFzOff = -2, kFzAny = -1;
+
+template <int CI, bool ACC, int FZ>
+__global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_rows(
     ConvGeom g, const float* __restrict__ x, const float* __restrict__ wt,
     const float* __restrict__ dz, float* __restrict__ dwpart, float* __restrict__ dx,
-    int nstrips, int sw, int nruns, int rlen) {
+    int nstrips, int sw, int nruns, int rlen, DzSource src) {
   static_assert(CI >= 1 && CI <= 3, "9*CI columns must fit one 32-wide block");
   typedef float f4 __attribute__((ext_vector_type(4)));
   constexpr int P = kFrPitch;
@@ -1402,11 +1410,27 @@ __global__ __launch_bounds__(kFrThreads, 3) void conv_first_rows(
   // (dz: channel e / 32, group e % 32; x: the same with CI channels).  Groups
   // off the image are zero, applied at the LDS store.  Two register sets: the
   // rows loaded at the end of row h are stored to LDS during row h + 2.
+  constexpr bool fz = FZ != kFzOff, fz_y = fz && FZ != CBB_ACT_LINEAR;
   struct Stage {
-    f4 pz[4], px;
+    f4 pz[4], py[fz ? 4 : 1], pn[fz ? 4 : 1], px;
     uint32_t zmask;
     bool xok;
   };
+  // FZ: the map of the four channels this thread stages, o = tid / 32 + 8k
+  const float* yb = fz_y ? src.y + (int64_t)n * g.OC * g.HW : zb;
+  // without x_norm the third coefficient is 0 and delta stands in for it
+  const float* nb = fz && src.xn ? src.xn + (int64_t)n * g.OC * g.HW : zb;
+  float ca[4], cb[4], cc[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int o = (tid >> 5) + 8 * k;
+    ca[k] = cb[k] = cc[k] = 0.f;
+    if (fz && o < g.OC) {
+      ca[k] = src.coef[o];
+      cb[k] = src.coef[g.OC + o];
+      cc[k] = src.coef[2 * g.OC + o];
+    }
+  }
   auto load_dz = [&](Stage& q, int h) {
     q.zmask = 0;
 #pragma unroll
@@ -1414,7 +1438,10 @@ __global__ __launch_bounds__(kFrThreads, 3) void conv_first_rows(
       const int e = tid + kFrThreads * k, o = e >> 5, v = e & 31;
       const int w = w0 - 4 + 4 * v;
       const bool ok = o < g.OC && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
-      q.pz[k] = *(const f4*)(zb + (ok ? (o * g.H + h) * g.W + w : 0));
+      const int off = ok ? (o * g.H + h) * g.W + w : 0;
+      q.pz[k] = *(const f4*)(zb + off);
+      if constexpr (fz_y) q.py[k] = *(const f4*)(yb + off);
+      if constexpr (fz) q.pn[k] = *(const f4*)(nb + off);
       q.zmask |= (uint32_t)ok << k;
     }
   };
@@ -1424,7 +1451,22 @@ __global__ __launch_bounds__(kFrThreads, 3) void conv_first_rows(
     for (int k = 0; k < 4; ++k) {
       const int e = tid + kFrThreads * k, o = e >> 5, v = e & 31;
       if (o < g.OC) {
-        const f4 val = ((q.zmask >> k) & 1u) ? q.pz[k] : zero;
+        f4 val = q.pz[k];
+        if constexpr (fz_y) {
+          const int act = FZ == kFzAny ? src.act : FZ;
+          val.x *= act_grad(act, src.slope, q.py[k].x);
+          val.y *= act_grad(act, src.slope, q.py[k].y);
+          val.z *= act_grad(act, src.slope, q.py[k].z);
+          val.w *= act_grad(act, src.slope, q.py[k].w);
+        }
+        if constexpr (fz) {
+          const f4 xn = q.pn[k];
+          val.x = ca[k] * val.x + cb[k] + cc[k] * xn.x;
+          val.y = ca[k] * val.y + cb[k] + cc[k] * xn.y;
+          val.z = ca[k] * val.z + cb[k] + cc[k] * xn.z;
+          val.w = ca[k] * val.w + cb[k] + cc[k] * xn.w;
+        }
+        val = ((q.zmask >> k) & 1u) ? val : zero;
         float* d = Zs + o * P + 4 * v;
         d[0] = val.x;
         d[1] = val.y;
@@ -1797,22 +1839,43 @@ size_t conv_fused_workspace(const ConvGeom& g) {
 }
 
 
-int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
-                           float* dw, float* dx, int accumulate, float* ws, hipStream_t st) {
-  const FuPlan p = plan_fused(g);
-#define CBB_FR(CI_)                                                                      \
-  if (accumulate)                                                                          \
-    conv_first_rows<CI_, true><<<p.wgs, kFrThreads, 0, st>>>(g, x, wt, dz, ws, dx, p.nstrips, \
-                                                             p.sw, p.nruns, p.rlen);       \
-  else                                                                                     \
-    conv_first_rows<CI_, false><<<p.wgs, kFrThreads, 0, st>>>(g, x, wt, dz, ws, dx,          \
-                                                              p.nstrips, p.sw, p.nruns, p.rlen)
-  switch (g.C) {
-    case 1: CBB_FR(1); break;
-    case 2: CBB_FR(2); break;
-    default: CBB_FR(3); break;
+template <int CI>
+static void launch_first_rows(const ConvGeom& g, const FuPlan& p, const float* x, const float* wt,
+                              const float* dz, float* ws, float* dx, int accumulate,
+                              const DzSource* src, hipStream_t st) {
+  const DzSource s = src ? *src : DzSource{};
+#define CBB_FR(FZ_)                                                                           \
+  if (accumulate)                                                                             \
+    conv_first_rows<CI, true, FZ_><<<p.wgs, kFrThreads, 0, st>>>(g, x, wt, dz, ws, dx,          \
+                                                                 p.nstrips, p.sw, p.nruns,    \
+                                                                 p.rlen, s);                  \
+  else                                                                                        \
+    conv_first_rows<CI, false, FZ_><<<p.wgs, kFrThreads, 0, st>>>(g, x, wt, dz, ws, dx,         \
+                                                                  p.nstrips, p.sw, p.nruns,   \
+                                                                  p.rlen, s)
+  if (!src) {
+    CBB_FR(kFzOff);
+  } else {
+    switch (src->y ? src->act : CBB_ACT_LINEAR) {
+      case CBB_ACT_LINEAR: CBB_FR(CBB_ACT_LINEAR); break;
+      case CBB_ACT_LEAKY: CBB_FR(CBB_ACT_LEAKY); break;
+      case CBB_ACT_LOGISTIC: CBB_FR(CBB_ACT_LOGISTIC); break;
+      case CBB_ACT_RELU: CBB_FR(CBB_ACT_RELU); break;
+      default: CBB_FR(kFzAny); break;
+    }
   }
 #undef CBB_FR
+}
+
+int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
+                           float* dw, float* dx, int accumulate, float* ws, hipStream_t st,
+                           const DzSource* src) {
+  const FuPlan p = plan_fused(g);
+  switch (g.C) {
+    case 1: launch_first_rows<1>(g, p, x, wt, dz, ws, dx, accumulate, src, st); break;
+    case 2: launch_first_rows<2>(g, p, x, wt, dz, ws, dx, accumulate, src, st); break;
+    default: launch_first_rows<3>(g, p, x, wt, dz, ws, dx, accumulate, src, st); break;
+  }
   const int rc = check_launch("conv_first_rows");
   if (rc) return rc;
   return launch_dw_reduce(g, dw, ws, p.wgs, p.groups, 0, st);

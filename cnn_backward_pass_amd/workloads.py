@@ -66,6 +66,10 @@ class Runner:
                 ent["dz"] = None if c.act == "linear" else torch.empty(oshape, dtype=f32,
                                                                        device=device)
             ent["fused"] = cbb.conv_fused_weights_data(desc)
+            # a fused dW + dX layer with an act/BN stage: dz is not stored, the fused
+            # kernel forms it from delta, y and x_hat (conv_block_backward with dz=None)
+            has_dx = not (name == "lenet" and li == 0)
+            ent["form_dz"] = bool(ent["fused"]) and has_dx and (c.bn or c.act != "linear")
             ent["dw"] = torch.zeros_like(ent["w"])
             ent["db"] = torch.zeros(c.out_c, dtype=f32, device=device)
             ent["ws_bytes"] = cbb.conv_block_workspace_size(desc)
@@ -129,10 +133,18 @@ class Runner:
     def _conv(self, li: int, delta, dx, dx_accumulate: bool, stream) -> None:
         e = self.convs[li]
         probe = self._probe
-        if probe is None or probe[0] != li:
+        form_dz = e["form_dz"] and dx is not None
+        if probe is None or probe[0] != li or form_dz:
+            # a fused-dz layer is one stage, "block" (its dz is never stored)
+            target = probe is not None and probe[0] == li and probe[1] == "block"
+            if target:
+                probe[2](True, True)
             cbb.conv_block_backward(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
-                                    e["gamma"], delta, e["dz"], e["dw"], e["db"], e["dgamma"], dx,
-                                    dx_accumulate, self.workspace, stream)
+                                    e["gamma"], delta, None if form_dz else e["dz"], e["dw"],
+                                    e["db"], e["dgamma"], dx, dx_accumulate, self.workspace,
+                                    stream)
+            if target:
+                probe[2](True, False)
             return
         # The same stages conv_block_backward runs, called one by one so that
         # events can bracket one of them ("act_bn", "dW", "dX", or "dWdX" where
@@ -169,6 +181,8 @@ class Runner:
     def stages(self, li: int) -> list[str]:
         """The separately timed stages of conv layer li (see step's probe)."""
         has_dx = not (self.name == "lenet" and li == 0)
+        if self.convs[li]["form_dz"]:
+            return ["block"]
         if has_dx and self.convs[li]["fused"]:
             return ["act_bn", "dWdX"]
         return ["act_bn", "dW", "dX"] if has_dx else ["act_bn", "dW"]
@@ -189,6 +203,10 @@ class Runner:
                 raise ValueError("the first LeNet conv has no input gradient")
             cbb.conv_backward_data(e["desc"], e["w"], dz, self.d_in[li], False, self.workspace,
                                    stream)
+        elif stage == "block":
+            cbb.conv_block_backward(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
+                                    e["gamma"], delta, None, e["dw"], e["db"], e["dgamma"],
+                                    self.d_in[li], False, self.workspace, stream)
         elif stage == "dWdX":
             cbb.conv_backward_weights_data(e["desc"], e["x"], e["w"], dz, e["dw"], self.d_in[li],
                                            False, self.workspace, stream)
@@ -243,7 +261,8 @@ class Runner:
         out = {"dw": [h(e["dw"]) for e in self.convs], "db": [h(e["db"]) for e in self.convs],
                "dgamma": [h(e["dgamma"]) for e in self.convs],
                "d_in": [h(t) for t in self.d_in],
-               "dz": [h(e["dz"]) for e in self.convs]}
+               # a layer whose dz the fused kernel forms in place stores none
+               "dz": [None if e["form_dz"] else h(e["dz"]) for e in self.convs]}
         if self.name == "lenet":
             out.update(dlogits=h(self.dlogits), fc_dw=[h(t) for t in self.fc_dw],
                        fc_db=[h(t) for t in self.fc_db], d_relu=h(self.d_relu),

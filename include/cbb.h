@@ -144,8 +144,14 @@ const char* cbb_last_error(void);
  *   gamma   [O]           BN scale (l.scales)                 }
  *   delta   [N,O,OH,OW]   dL/dy (l.delta on entry), read only
  *   dz      [N,O,OH,OW]   receives dL/dz (l.delta on exit); may equal delta
- *                         (in place); may be NULL iff act = LINEAR and no BN
- *                         (then dz is delta itself)
+ *                         (in place).  NULL when act = LINEAR and no BN (dz is
+ *                         delta itself), or to leave dz unstored on a layer for
+ *                         which cbb_conv_fused_weights_data returns 1, with dx
+ *                         given and x, delta, y, x_norm 16-byte aligned: the
+ *                         fused dW + dX kernel then forms dz from
+ *                         delta, y and x_norm as it stages them, and the
+ *                         separate pass that writes dz, and its re-read, go
+ *                         away.  Any other NULL dz is CBB_EINVAL.
  *   dw      [O,C/groups,k,k] += weight gradient (l.weight_updates)
  *   db      [O]           += bias gradient (l.bias_updates; with BN this is dbeta)
  *   dgamma  [O]           += scale gradient (l.scale_updates); BN only, else NULL

@@ -87,7 +87,24 @@ def _call_conv(desc, **ptrs):
 @pytest.mark.parametrize("missing", ["x", "w", "delta", "dw", "db", "y", "x_norm", "var", "gamma",
                                      "dgamma", "dz"])
 def test_conv_null_required_pointer(missing):
-    assert _call_conv(_desc(), **{missing: None}) == -1
+    # 5 input channels: not a fused first layer, where dz = NULL is a valid request
+    assert _call_conv(_desc(in_c=5), **{missing: None}) == -1
+
+
+def test_conv_formed_dz_rules():
+    """dz = NULL asks the fused first-layer kernel to form dz itself: only valid on
+    such a layer, with dx given and 16-byte aligned saved tensors."""
+    d = _desc()
+    assert cbb.lib().cbb_conv_fused_weights_data(ctypes.byref(d)) == 1
+    assert _call_conv(d, dz=None, dx=None) == -1
+    misaligned = ctypes.c_void_p(0x1004)
+    for name in ("x", "delta", "y", "x_norm"):
+        assert _call_conv(d, dz=None, **{name: misaligned}) == -1
+    for kw in (dict(in_c=4), dict(ksize=5, pad=2), dict(stride=2), dict(in_w=10),
+               dict(out_c=33)):
+        dn = _desc(**kw)
+        assert cbb.lib().cbb_conv_fused_weights_data(ctypes.byref(dn)) == 0
+        assert _call_conv(dn, dz=None) == -1
 
 
 def test_conv_pointer_rules_without_bn():

@@ -74,7 +74,7 @@ CONV_CASES = [  # n, c, h, w, oc, k, s, p, bn, act
 ]
 
 
-def run_conv(torch, case, seed, dx_accumulate=False, in_place=False, want_dx=True):
+def run_conv(torch, case, seed, dx_accumulate=False, in_place=False, want_dx=True, form_dz=False):
     from cnn_backward_pass_amd import cbb
     n, c, h, w, oc, k, s, p, bn, act = case[:10]
     groups, dil = case[10:12] if len(case) > 10 else (1, 1)
@@ -97,6 +97,8 @@ def run_conv(torch, case, seed, dx_accumulate=False, in_place=False, want_dx=Tru
     T = lambda a: None if a is None else _t(torch, a)
     d_delta = T(delta)
     d_dz = d_delta if in_place else (torch.empty_like(d_delta) if (bn or act != "linear") else None)
+    if form_dz:   # dz not stored: the fused kernel forms it from delta, y and x_hat
+        d_dz = None
     dw = T(np.ones_like(wt) * 0.5)              # accumulation target with a known start
     db = T(np.full(oc, 0.25, np.float32))
     dg = T(np.full(oc, -0.5, np.float32)) if bn else None
@@ -126,6 +128,37 @@ def test_conv_block_backward_parity(case):
     for k in ("dw", "db", "dz", "dx", "dgamma"):
         if k in got:
             assert_close(k, got[k], ref[k] if k != "dgamma" else ref["dgamma"])
+
+
+FORM_DZ_CASES = [  # first layers whose dz the fused dW + dX kernel forms as it stages delta
+    (2, 3, 32, 32, 16, 3, 1, 1, True, "leaky"),
+    (2, 3, 24, 40, 32, 3, 1, 1, True, "logistic"),
+    (1, 2, 17, 36, 12, 3, 1, 1, False, "relu"),      # bias only: dz = g
+    (2, 1, 20, 16, 5, 3, 1, 1, True, "linear"),      # BN without activation: no y
+    (1, 3, 13, 132, 30, 3, 1, 1, False, "leaky"),    # two column strips
+    (2, 3, 12, 16, 32, 3, 1, 1, 2, "tanh"),          # fixed statistics: dz = a g
+    (4, 3, 128, 128, 8, 3, 1, 1, True, "leaky"),     # many work-groups, two-level dW sum
+    (1, 3, 30, 8, 17, 3, 1, 1, True, "loggy"),       # run-time activation switch
+]
+
+
+@pytest.mark.parametrize("acc", [False, True])
+@pytest.mark.parametrize("case", FORM_DZ_CASES)
+def test_conv_block_backward_forms_dz(case, acc):
+    """dz = NULL on a fused first layer: dz is formed inside the dW + dX kernel from
+    delta, y and x_hat with the BN backward's per-channel map; dW, db, dgamma and dx
+    match the oracle as on the stored-dz route."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    n, c, h, w, oc, k, s, p, bn, act = case
+    assert cbb.conv_fused_weights_data(cbb.conv_desc(n, c, h, w, oc, k, s, p, bn, act)) == 1
+    announce(f"conv_block forming dz {case} accumulate={acc}")
+    ref, got = run_conv(torch, case, seed=500 + FORM_DZ_CASES.index(case), dx_accumulate=acc,
+                        form_dz=True)
+    assert "dz" not in got
+    for key in ("dw", "db", "dx", "dgamma"):
+        if key in got:
+            assert_close(key, got[key], ref[key])
 
 
 GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
