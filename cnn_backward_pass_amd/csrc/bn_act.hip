@@ -108,13 +108,15 @@ template <bool VEC, int ACT, int BN>
 __global__ __launch_bounds__(kThreads) void actbn_reduce(
     SegGeom s, const float* delta, const float* __restrict__ y, const float* __restrict__ xn,
     float slope, int act_rt, const float* __restrict__ var, const float* __restrict__ gamma,
-    float eps, float* dz /* fixed statistics only, NULL: not written; may alias delta */,
+    float eps, float* dz /* no batch statistics only, NULL: not written; may alias delta */,
     float2* __restrict__ part) {
   const int c = blockIdx.x / s.nseg, sg = blockIdx.x % s.nseg;
   float sg_ = 0.f, sgx = 0.f;
   const int act = ACT == kActAny ? act_rt : ACT;
   constexpr bool has_y = ACT != CBB_ACT_LINEAR, has_x = BN != kBnNone, fixed = BN == kBnFixed;
-  const float ka = fixed ? gamma[c] / sqrtf(var[c] + eps) : 0.f;
+  // dz does not depend on the sums without batch statistics: written in this pass
+  constexpr bool one_pass = BN != kBnBatch;
+  const float ka = fixed ? gamma[c] / sqrtf(var[c] + eps) : 1.f;
   if constexpr (VEC) {
     for_segment<true>(s, c, sg, [&](int64_t o) {
       float4 d = ld4(delta + o);
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void actbn_reduce(
         const float4 x = ld4(xn + o);
         sgx += (d.x * x.x + d.y * x.y) + (d.z * x.z + d.w * x.w);
       }
-      if (fixed && dz)
+      if (one_pass && dz)
         *reinterpret_cast<float4*>(dz + o) = make_float4(ka * d.x, ka * d.y, ka * d.z, ka * d.w);
     });
   } else {
@@ -139,13 +141,13 @@ __global__ __launch_bounds__(kThreads) void actbn_reduce(
       if (has_y) d *= act_grad(act, slope, y[o]);
       sg_ += d;
       if (has_x) sgx += d * xn[o];
-      if (fixed && dz) dz[o] = ka * d;
+      if (one_pass && dz) dz[o] = ka * d;
     });
   }
   __shared__ float red[4];
   sg_ = block_sum_256(sg_, red);
   sgx = block_sum_256(sgx, red);
-  if (threadIdx.x == 0) part[blockIdx.x] = make_float2(sg_, sgx);
+  if (threadIdx.x == 0) part[(int64_t)c * s.nseg + sg] = make_float2(sg_, sgx);
 }
 
 // Fold the nseg partials of channel c in a fixed order; every thread gets the sums.
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(kThreads) void actbn_fold(const float2* __restrict_
   const float2 sums = fold_partials(part, c, nseg, red);
   if (threadIdx.x == 0) {
     dbeta[c] += sums.x;
-    dgamma[c] += sums.y;
+    if (dgamma) dgamma[c] += sums.y;
   }
 }
 
@@ -461,18 +463,28 @@ static void launch_actbn_t(const SegGeom& s, unsigned blocks, int act, const flo
                            const float* gamma, float eps, float* dz, float* dgamma,
                            float* dbeta_or_db, float2* part, int write_dz, float* coef,
                            hipStream_t st) {
-  actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(
-      s, delta, y, BN != kBnNone ? xn : nullptr, slope, act, var, gamma, eps,
-      coef ? nullptr : dz, part);
-  if (coef)
-    actbn_coef<<<(unsigned)s.C, kThreads, 0, st>>>(part, s.nseg, s.M, s.C, BN, var, gamma, eps,
-                                                  dgamma, dbeta_or_db, coef);
-  else if constexpr (BN == kBnFixed)
-    actbn_fold<<<(unsigned)s.C, kThreads, 0, st>>>(part, s.nseg, dgamma, dbeta_or_db);
-  else
+  const float* xr = BN != kBnNone ? xn : nullptr;
+  if (coef || BN != kBnBatch) {
+    // one streaming pass (dz written in it, or formed later from coef)
+    actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(
+        s, delta, y, xr, slope, act, var, gamma, eps, coef || !write_dz ? nullptr : dz, part);
+    if (coef)
+      actbn_coef<<<(unsigned)s.C, kThreads, 0, st>>>(part, s.nseg, s.M, s.C, BN, var, gamma,
+                                                    eps, dgamma, dbeta_or_db, coef);
+    else
+      actbn_fold<<<(unsigned)s.C, kThreads, 0, st>>>(part, s.nseg,
+                                                    BN == kBnNone ? nullptr : dgamma,
+                                                    dbeta_or_db);
+    return;
+  }
+  // batch statistics: dz needs the channel's sums, so the data is streamed twice
+  if constexpr (BN == kBnBatch) {
+    actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xr, slope, act, var,
+                                                            gamma, eps, nullptr, part);
     actbn_apply<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, slope, act, part, var,
                                                            gamma, eps, dz, dgamma, dbeta_or_db,
                                                            write_dz);
+  }
 }
 
 template <bool VEC, int ACT>
