@@ -21,6 +21,8 @@ FWD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (2, 16, 15, 14, 16, 3, 1, 2, 2, "selu", 16, 2),      # depthwise, dilated, fixed statistics
     (1, 8, 17, 16, 12, 5, 2, 4, 1, "relu", 1, 2),        # dilated 5x5, stride 2
     (3, 32, 9, 9, 48, 3, 1, 1, 2, "leaky", 1, 1),        # fixed statistics
+    (2, 24, 14, 18, 130, 3, 2, 1, 1, "leaky", 1, 1),     # 128 x 128 tiles, ragged o and pixels
+    (1, 32, 20, 20, 80, 3, 1, 1, 0, "relu", 1, 1),       # bias: general kernel, 128 x 128 tiles
 ]
 
 
