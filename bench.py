@@ -120,6 +120,32 @@ def stage_work(runner, li, stage):
     return 2.0 * macs, 4.0 * (in_elems + out_elems + w_elems)
 
 
+def _act_bn_entry(runner, name, li, ms):
+    """An act+BN stage: algorithmic (touch-once) GB/s and, where the committed counter
+    summary matches the current sources, the HBM bytes it actually moved per second."""
+    from cnn_backward_pass_amd import profsum
+    e = {"ms": round(ms, 4),
+         "algorithmic_GBps": round(stage_work(runner, li, "act_bn")[1] / (ms * 1e-3) / 1e9, 1)}
+    rec = profsum.load_traffic(f"{name}.{li}.act_bn")
+    if rec is not None:
+        e["traffic_bytes"] = rec["traffic_bytes"]
+        e["traffic_GBps"] = round(rec["traffic_bytes"] / (ms * 1e-3) / 1e9, 1)
+        e["traffic_frac_of_hbm_peak"] = round(e["traffic_GBps"] / (PEAK_HBM / 1e9), 4)
+    return e
+
+
+def _block_entry(runner, name, li, ms):
+    """A layer whose dz the fused dW + dX kernel forms: roofline of the whole block
+    (touch-once bytes) and, where the counter summary matches, its measured HBM bytes."""
+    from cnn_backward_pass_amd import profsum
+    e = _roof(ms, *stage_work(runner, li, "block"))
+    rec = profsum.load_traffic(f"{name}.{li}.block")
+    if rec is not None:
+        e["traffic_bytes"] = rec["traffic_bytes"]
+        e["traffic_GBps"] = round(rec["traffic_bytes"] / (ms * 1e-3) / 1e9, 1)
+    return e
+
+
 def time_stages(runners, torch, reps=3):
     """Time every stage of every conv layer in place (events around it, whole steps run)."""
     res = []
@@ -417,13 +443,11 @@ def main():
                        "gflop_per_step": round(step_flops / 1e9, 3), "parallelism": "none"},
             "roofline": roof, "per_workload": per,
             "stages_ms": {f"{n}.{li}.{st}": round(ms, 4) for ms, n, li, st in stages},
-            "act_bn_stages": {f"{n}.{li}": {
-                "ms": round(ms, 4),
-                "algorithmic_GBps": round(stage_work(runners[n], li, st)[1] / (ms * 1e-3) / 1e9, 1)}
-                for ms, n, li, st in stages if st == "act_bn" and ms > 0.05},
+            "act_bn_stages": {f"{n}.{li}": _act_bn_entry(runners[n], n, li, ms)
+                              for ms, n, li, st in stages if st == "act_bn" and ms > 0.05},
             # layers whose dz is formed inside the fused dW + dX kernel: the act/BN
             # reduction, the per-channel map and that kernel, timed together
-            "fused_dz_blocks": {f"{n}.{li}": _roof(ms, *stage_work(runners[n], li, st))
+            "fused_dz_blocks": {f"{n}.{li}": _block_entry(runners[n], n, li, ms)
                                 for ms, n, li, st in stages if st == "block"}}
     print("[bench] variants", file=sys.stderr, flush=True)
     line["variants"] = time_variants(torch)

@@ -1401,6 +1401,8 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
   const int hA = max(r0 - 1, 0), hE = min(r1, g.H);
   const float* zb = dz + (int64_t)n * g.OC * g.HW;
   const float* xb = x + (int64_t)n * CI * g.HW;
+  // last 16-byte group of a row that holds a column the strip uses (LDS column sw + 4)
+  const int vlast = (sw + 4) >> 2;
 
   // channels >= OC are never staged and stay zero
   for (int e = tid; e < 32 * P; e += kFrThreads) Zs[e] = 0.f;
@@ -1437,7 +1439,9 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
     for (int k = 0; k < 4; ++k) {
       const int e = tid + kFrThreads * k, o = e >> 5, v = e & 31;
       const int w = w0 - 4 + 4 * v;
-      const bool ok = o < g.OC && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+      // only the groups under columns w0-1 .. w0+sw are fetched (the rest stay zero)
+      const bool ok = o < g.OC && v <= vlast && (unsigned)h < (unsigned)g.H &&
+                      (unsigned)w < (unsigned)g.W;
       const int off = ok ? (o * g.H + h) * g.W + w : 0;
       q.pz[k] = *(const f4*)(zb + off);
       if constexpr (fz_y) q.py[k] = *(const f4*)(yb + off);
@@ -1477,7 +1481,8 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
   };
   auto load_x = [&](Stage& q, int h) {
     const int c = tid >> 5, v = tid & 31, w = w0 - 4 + 4 * v;
-    q.xok = tid < CI * 32 && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+    q.xok = tid < CI * 32 && v <= vlast && (unsigned)h < (unsigned)g.H &&
+            (unsigned)w < (unsigned)g.W;
     q.px = *(const f4*)(xb + (q.xok ? (c * g.H + h) * g.W + w : 0));
   };
   auto store_x = [&](const Stage& q, int h) {
@@ -1814,15 +1819,16 @@ struct FuPlan {
   int nstrips, sw, nruns, rlen, wgs, groups;
 };
 
-static FuPlan plan_fused(const ConvGeom& g) {
+static FuPlan plan_fused(const ConvGeom& g, bool form_dz = false) {
   FuPlan p{};
   // strips of at most kFrMaxW columns, a multiple of 4, as even as possible
   const int ns0 = (int)ceil_div(g.W, kFrMaxW);
   p.sw = (int)(ceil_div(ceil_div(g.W, ns0), 4) * 4);
   p.nstrips = (int)ceil_div(g.W, p.sw);
-  // runs of rows: about three work-groups per CU, at least 4 rows each (each
-  // run also walks the dz rows just above and below it)
-  const int64_t target = 768;
+  // runs of rows: about three work-groups per CU (two when dz is formed in the
+  // kernel: its registers allow two per CU), at least 4 rows each (each run also
+  // walks the dz rows just above and below it, so longer runs fetch less)
+  const int64_t target = form_dz ? 512 : 768;
   const int64_t runs = std::max<int64_t>(
       1, std::min<int64_t>(ceil_div(g.H, 4), ceil_div(target, (int64_t)g.N * p.nstrips)));
   p.rlen = (int)ceil_div(g.H, runs);
@@ -1834,8 +1840,8 @@ static FuPlan plan_fused(const ConvGeom& g) {
 
 size_t conv_fused_workspace(const ConvGeom& g) {
   if (!conv_fused_dwdx_ok(g)) return 0;
-  const FuPlan p = plan_fused(g);
-  return ((size_t)p.wgs + p.groups) * g.OC * g.J * sizeof(float);
+  const FuPlan p = plan_fused(g), q = plan_fused(g, true);
+  return ((size_t)std::max(p.wgs + p.groups, q.wgs + q.groups)) * g.OC * g.J * sizeof(float);
 }
 
 
@@ -1870,7 +1876,7 @@ static void launch_first_rows(const ConvGeom& g, const FuPlan& p, const float* x
 int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
                            float* dw, float* dx, int accumulate, float* ws, hipStream_t st,
                            const DzSource* src) {
-  const FuPlan p = plan_fused(g);
+  const FuPlan p = plan_fused(g, src != nullptr);
   switch (g.C) {
     case 1: launch_first_rows<1>(g, p, x, wt, dz, ws, dx, accumulate, src, st); break;
     case 2: launch_first_rows<2>(g, p, x, wt, dz, ws, dx, accumulate, src, st); break;
