@@ -63,7 +63,7 @@ def profile_stage(spec, reps, torch):
     from cnn_backward_pass_amd.workloads import Runner
     r = Runner(name, synth.inputs(name), synth.saved_standins(name), "cuda:0")
     r.reset()
-    if stage not in ("act_bn", "block"):
+    if stage not in ("act_bn", "block", "actbn_dW"):
         r.run_stage(li, "act_bn")
     torch.cuda.synchronize()
     ms = []
@@ -110,6 +110,10 @@ def stage_work(runner, li, stage):
         # reads delta, y, x_hat and writes dz (BN); bias-only: reads delta (+ y)
         per = (16 if c.bn else (12 if c.act != "linear" else 4))
         return 0.0, float(per * out_elems)
+    if stage == "actbn_dW":
+        # act/BN sums, then dW forming dz: x, delta, y, x_hat read once; dz, dW written
+        nread = 1 + (c.act != "linear") + bool(c.bn)
+        return 2.0 * macs, 4.0 * (in_elems + (nread + 1) * out_elems + w_elems)
     if stage == "block":
         # act/BN stage and the fused dW + dX kernel with dz formed in place: x, W and the
         # saved delta, y, x_hat read once; dW, dx written
@@ -134,12 +138,13 @@ def _act_bn_entry(runner, name, li, ms):
     return e
 
 
-def _block_entry(runner, name, li, ms):
-    """A layer whose dz the fused dW + dX kernel forms: roofline of the whole block
-    (touch-once bytes) and, where the counter summary matches, its measured HBM bytes."""
+def _block_entry(runner, name, li, ms, stage):
+    """A stage in which a gradient kernel forms dz ("block": the fused dW + dX kernel;
+    "actbn_dW": the dW kernel, which also writes dz): roofline of the stage (touch-once
+    bytes) and, where the counter summary matches, its measured HBM bytes."""
     from cnn_backward_pass_amd import profsum
-    e = _roof(ms, *stage_work(runner, li, "block"))
-    rec = profsum.load_traffic(f"{name}.{li}.block")
+    e = _roof(ms, *stage_work(runner, li, stage))
+    rec = profsum.load_traffic(f"{name}.{li}.{stage}")
     if rec is not None:
         e["traffic_bytes"] = rec["traffic_bytes"]
         e["traffic_GBps"] = round(rec["traffic_bytes"] / (ms * 1e-3) / 1e9, 1)
@@ -445,10 +450,10 @@ def main():
             "stages_ms": {f"{n}.{li}.{st}": round(ms, 4) for ms, n, li, st in stages},
             "act_bn_stages": {f"{n}.{li}": _act_bn_entry(runners[n], n, li, ms)
                               for ms, n, li, st in stages if st == "act_bn" and ms > 0.05},
-            # layers whose dz is formed inside the fused dW + dX kernel: the act/BN
-            # reduction, the per-channel map and that kernel, timed together
-            "fused_dz_blocks": {f"{n}.{li}": _block_entry(runners[n], n, li, ms)
-                                for ms, n, li, st in stages if st == "block"}}
+            # stages whose dz is formed inside a gradient kernel: the act/BN reduction,
+            # the per-channel map and that kernel, timed together
+            "dz_formed_stages": {f"{n}.{li}.{st}": _block_entry(runners[n], n, li, ms, st)
+                                 for ms, n, li, st in stages if st in ("block", "actbn_dW")}}
     print("[bench] variants", file=sys.stderr, flush=True)
     line["variants"] = time_variants(torch)
     if not args.no_cpu_baseline:

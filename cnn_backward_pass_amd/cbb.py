@@ -73,6 +73,7 @@ _SIGS = {
     "cbb_conv_backward_weights_data": ([ctypes.POINTER(ConvDesc)] + [_P] * 5 + [_i32, _P, _sz, _P],
                                        _i32),
     "cbb_conv_fused_weights_data": ([ctypes.POINTER(ConvDesc)], _i32),
+    "cbb_conv_dw_forms_dz": ([ctypes.POINTER(ConvDesc)], _i32),
     "cbb_conv_block_forward_workspace_size": ([ctypes.POINTER(ConvDesc), ctypes.POINTER(_sz)],
                                               _i32),
     "cbb_conv_block_forward": ([ctypes.POINTER(ConvDesc)] + [_P] * 9 + [_P, _sz, _P], _i32),
@@ -236,6 +237,13 @@ def conv_fused_weights_data(desc: ConvDesc) -> bool:
     rc = lib().cbb_conv_fused_weights_data(ctypes.byref(desc))
     if rc < 0:
         _check("cbb_conv_fused_weights_data", rc)
+    return rc == 1
+
+
+def conv_dw_forms_dz(desc: ConvDesc) -> bool:
+    rc = lib().cbb_conv_dw_forms_dz(ctypes.byref(desc))
+    if rc < 0:
+        _check("cbb_conv_dw_forms_dz", rc)
     return rc == 1
 
 

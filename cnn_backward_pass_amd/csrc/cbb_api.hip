@@ -159,6 +159,23 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
     return launch_conv_fused_dwdx(g, x, w, delta, dw, dx, dx_accumulate,
                                   reinterpret_cast<float*>(ws + p.part_bytes), st, &src);
   }
+  // Batch statistics with dz stored: on the layers the 3x3 row-streaming dW kernel
+  // takes, that kernel forms dz from delta, y and x_norm and writes it for the
+  // input gradient, so the act/BN stage stops after the sums (no apply pass).
+  auto a16 = [](const void* q) { return !q || (uintptr_t)q % 16 == 0; };
+  if (bn == CBB_BN_BATCH && dz && dz != delta && dz != y && dz != x_norm &&
+      conv_dw_forms_dz_ok(g) && a16(x) && a16(delta) && a16(y) && a16(x_norm) && a16(dz)) {
+    float* coef = reinterpret_cast<float*>(
+        ws + align_up(actbn_workspace(desc->batch, desc->out_c, p.oh * p.ow), kAlign));
+    rc = launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
+                      var, gamma, desc->bn_eps, bn, nullptr, dgamma, db, ws, st, coef);
+    if (rc) return rc;
+    const DzSource src{act == CBB_ACT_LINEAR ? nullptr : y, x_norm, coef, act, desc->slope};
+    float* ws2 = reinterpret_cast<float*>(ws + p.part_bytes);
+    rc = launch_conv_dw_forming_dz(g, x, delta, src, dz, dw, ws2, st);
+    if (rc || !dx) return rc;
+    return launch_conv_dx(g, w, dz, dx, dx_accumulate, ws2, st);
+  }
   const float* dz_eff = passthrough ? delta : dz;
   rc = launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
                     var, gamma, desc->bn_eps, bn, passthrough ? nullptr : dz, dgamma, db, ws, st);
@@ -203,6 +220,12 @@ int cbb_conv_block_forward(const cbb_conv_desc* desc, const float* x, const floa
   return launch_bn_act_forward(desc->batch, desc->out_c, p.oh * p.ow, bn, desc->bn_eps, desc->act,
                                desc->slope, gamma, beta, mean, var, bn ? x_norm : y, y, workspace,
                                st);
+}
+
+int cbb_conv_dw_forms_dz(const cbb_conv_desc* desc) {
+  const int rc = check_desc(desc, nullptr);
+  if (rc) return rc;
+  return desc->batch_normalize == CBB_BN_BATCH && conv_dw_forms_dz_ok(make_geom(*desc)) ? 1 : 0;
 }
 
 int cbb_conv_fused_weights_data(const cbb_conv_desc* desc) {

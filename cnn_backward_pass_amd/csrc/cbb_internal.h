@@ -290,6 +290,10 @@ struct DzSource {
 int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, const float* dz,
                            float* dw, float* dx, int accumulate, float* ws, hipStream_t st,
                            const DzSource* src = nullptr);
+bool conv_dw_forms_dz_ok(const ConvGeom& g);
+int launch_conv_dw_forming_dz(const ConvGeom& g, const float* x, const float* delta,
+                              const DzSource& src, float* dzout, float* dw, float* ws,
+                              hipStream_t st);
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
                    float* ws, hipStream_t st);
 size_t actbn_workspace(int N, int C, int64_t HW);

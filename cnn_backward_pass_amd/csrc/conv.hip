@@ -10,6 +10,11 @@
 
 namespace cbb {
 
+// Kernels that form dz from delta, y and x_norm while staging it (DzSource) take
+// the activation as a template argument: kFzOff = dz is read as it is, kFzAny =
+// the activation is src.act at run time, else the activation itself.
+constexpr int kFzOff = -2, kFzAny = -1;
+
 // ---------------------------------------------------------------------------
 // Weight gradient.  dW[o][j] = sum_q A[o][q] * B[q][j] with
 //   q = (n, ho, wo),  A[o][q] = dz[n][o][ho][wo],
@@ -241,10 +246,15 @@ struct Dw3RowCfg {
 // V4: 16-byte loads (the host checks that W and OW are multiples of 4, TC too,
 // and that x and dz are 16-byte aligned); x pieces start three columns before
 // LDS column 0 and the extra columns are dropped at the LDS store.
-template <int S, int TC, bool V4>
+// FZ != kFzOff (16-byte path only): the dz argument is delta; dz is formed from
+// delta, y and x_norm with the per-channel map in src while it is staged, and the
+// work-groups of the first input-channel block also write it to dzout (each dz
+// element is staged by exactly one work-group per input-channel block), so the
+// input-gradient kernel can read it afterwards.
+template <int S, int TC, bool V4, int FZ = kFzOff>
 __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
     ConvGeom g, const float* __restrict__ x, const float* __restrict__ dz, float* __restrict__ out,
-    int strips, int rchunks, int rlen, int direct) {
+    int strips, int rchunks, int rlen, int direct, DzSource src, float* __restrict__ dzout) {
   using Cf = Dw3RowCfg<S, TC>;
   constexpr int NT = kDw3Threads;
   __shared__ float lds[Cf::LDS_FLOATS];
@@ -260,6 +270,12 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
   const int ic0 = oc0 * S - 1;      // input column held in LDS column 0
   const float* xb = x + ((int64_t)n * g.C + cb * 32) * g.HW;
   const float* zb = dz + ((int64_t)n * g.OC + ob * 64) * g.OHW;
+  constexpr bool fz = FZ != kFzOff, fz_y = fz && FZ != CBB_ACT_LINEAR;
+  static_assert(!fz || V4, "dz is formed on the 16-byte path only");
+  const int64_t zoff = ((int64_t)n * g.OC + ob * 64) * g.OHW;
+  const float* yb = fz_y ? src.y + zoff : zb;
+  const float* nb = fz && src.xn ? src.xn + zoff : zb;   // without x_norm: c = 0
+  float* dzw = fz && cb == 0 ? dzout + zoff : nullptr;
 
   // Ring rows fetched with output row q: h = S*q + 2 - S + rr, rr < S.  The
   // loads go to registers as they are (positions off the image read a clamped
@@ -274,7 +290,20 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
   constexpr int ZV = TC / 4, ZNEW4 = 64 * ZV, ZPT4 = (ZNEW4 + NT - 1) / NT;
   float px[V4 ? 1 : Cf::XPT], pz[V4 ? 1 : Cf::ZPT];
   f4 px4[V4 ? XPT4 : 1], pz4[V4 ? ZPT4 : 1];
+  f4 py4[fz ? ZPT4 : 1], pn4[fz ? ZPT4 : 1];
   uint32_t xm = 0, zm = 0;
+  // the map of the channels this thread stages (fixed over the rows)
+  float ka[fz ? ZPT4 : 1], kb[fz ? ZPT4 : 1], kc[fz ? ZPT4 : 1];
+  if constexpr (fz) {
+#pragma unroll
+    for (int i = 0; i < ZPT4; ++i) {
+      const int e = tid + i * NT;
+      const int o = ob * 64 + min(e / ZV, 63);
+      ka[i] = src.coef[o];
+      kb[i] = src.coef[g.OC + o];
+      kc[i] = src.coef[2 * g.OC + o];
+    }
+  }
   auto fetch = [&](int q) {
     const int hb = S * q + 2 - S;
     xm = 0;
@@ -295,7 +324,10 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
         const int e = tid + i * NT;
         const int o = e / ZV, v = e - o * ZV;
         const bool ok = e < ZNEW4 && oc0 + 4 * v < g.OW;
-        pz4[i] = *(const f4*)(zb + (ok ? o * g.OHW + q * g.OW + oc0 + 4 * v : 0));
+        const int zo = ok ? o * g.OHW + q * g.OW + oc0 + 4 * v : 0;
+        pz4[i] = *(const f4*)(zb + zo);
+        if constexpr (fz_y) py4[i] = *(const f4*)(yb + zo);
+        if constexpr (fz) pn4[i] = *(const f4*)(nb + zo);
         zm |= (uint32_t)ok << i;
       }
       return;
@@ -342,8 +374,18 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
         if (e < ZNEW4) {
           float* d = lds + Cf::Z0 + (q & 1) * Cf::ZB + o * Cf::OS + 4 * v;
           const bool ok = (zm >> i) & 1u;
+          f4 val = pz4[i];
+          if constexpr (fz) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) d[u] = ok ? pz4[i][u] : 0.f;
+            for (int u = 0; u < 4; ++u) {
+              float gv = val[u];
+              if constexpr (fz_y) gv *= act_grad(FZ == kFzAny ? src.act : FZ, src.slope, py4[i][u]);
+              val[u] = ka[i] * gv + kb[i] + kc[i] * pn4[i][u];
+            }
+            if (dzw && ok) *(f4*)(dzw + o * g.OHW + q * g.OW + oc0 + 4 * v) = val;
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) d[u] = ok ? val[u] : 0.f;
         }
       }
       return;
@@ -1376,8 +1418,6 @@ constexpr int kFrThreads = 256, kFrPitch = 133, kFrMaxW = 120;
 // (DzSource): the write and the re-read of dz by a separate pass disappear.  FZ
 // is the activation (kFzAny: the run-time src.act), so the per-element
 // derivative compiles to straight-line code for the common ones.
-constexpr int kFzOff = -2, kFzAny = -1;
-
 template <int CI, bool ACC, int FZ>
 __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_rows(
     ConvGeom g, const float* __restrict__ x, const float* __restrict__ wt,
@@ -1915,20 +1955,30 @@ static void launch_dw_tile(const ConvGeom& g, const DwPlan& p, const float* x, c
 
 template <int S>
 static void launch_dw3_rows(const ConvGeom& g, const DwPlan& p, const float* x, const float* dz,
-                            float* out, int direct, hipStream_t st) {
+                            float* out, int direct, hipStream_t st, const DzSource* src = nullptr,
+                            float* dzout = nullptr) {
   const unsigned blocks = (unsigned)((int64_t)p.splits * (g.OC / 64) * (g.C / 32));
   // 16-byte loads: rows and strip origins on 16-byte boundaries
   const bool v4 = aligned16(x) && aligned16(dz) && g.W % 4 == 0 && g.OW % 4 == 0 &&
                   p.rows_tc % 4 == 0;
+  const DzSource s = src ? *src : DzSource{};
+#define CBB_DW3K(TC, V4, FZ)                                                                 \
+  conv_dw3_rows<S, TC, V4, FZ><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,      \
+                                                               p.rchunks, p.rlen, direct, s, \
+                                                               dzout)
 #define CBB_DW3(TC)                                                                          \
   case TC:                                                                                   \
     if constexpr (Dw3RowCfg<S, TC>::FITS) {                                                  \
-      if (v4)                                                                                \
-        conv_dw3_rows<S, TC, true><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,  \
-                                                                   p.rchunks, p.rlen, direct); \
+      if (src && !src->y) /* no activation: y is never read */                            \
+        CBB_DW3K(TC, true, CBB_ACT_LINEAR);                                                  \
+      else if (src && src->act == CBB_ACT_LEAKY)                                             \
+        CBB_DW3K(TC, true, CBB_ACT_LEAKY);                                                   \
+      else if (src)                                                                          \
+        CBB_DW3K(TC, true, kFzAny);                                                          \
+      else if (v4)                                                                           \
+        CBB_DW3K(TC, true, kFzOff);                                                          \
       else                                                                                   \
-        conv_dw3_rows<S, TC, false><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips, \
-                                                                    p.rchunks, p.rlen, direct); \
+        CBB_DW3K(TC, false, kFzOff);                                                         \
     }                                                                                        \
     break;
   switch (p.rows_tc) {
@@ -1937,10 +1987,42 @@ static void launch_dw3_rows(const ConvGeom& g, const DwPlan& p, const float* x, 
     CBB_DW3(52)
     CBB_DW3(32)
     default:
-      conv_dw3_rows<S, 26, false><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,
-                                                                  p.rchunks, p.rlen, direct);
+      CBB_DW3K(26, false, kFzOff);
   }
 #undef CBB_DW3
+#undef CBB_DW3K
+}
+
+// Whether the weight gradient of this layer can form dz itself (conv_dw3_rows on its
+// 16-byte path) from delta, y and x_norm, writing it to dz for the input gradient.
+// Only with one block of 32 input channels: every input-channel block stages the dz
+// rows again, and with four blocks (the 128-channel residual layer) the three
+// tensors' extra loads cost more (147 against 120 + 20 µs) than the pass they save;
+// with one (the stem's second layer) the stage drops from 476 to 445 µs.
+bool conv_dw_forms_dz_ok(const ConvGeom& g) {
+  if (!dense(g) || g.C != 32) return false;
+  DwPlan p{};
+  return plan_dw3_rows(g, p) && p.rows_tc % 4 == 0 && g.W % 4 == 0 && g.OW % 4 == 0;
+}
+
+// dW with dz formed inside the kernel from delta (and src), dz written to dzout.
+// The caller has checked conv_dw_forms_dz_ok and the 16-byte alignment of every tensor.
+int launch_conv_dw_forming_dz(const ConvGeom& g, const float* x, const float* delta,
+                              const DzSource& src, float* dzout, float* dw, float* ws,
+                              hipStream_t st) {
+  DwPlan p{};
+  if (!conv_dw_forms_dz_ok(g) || !plan_dw3_rows(g, p)) return CBB_EUNSUPPORTED;
+  // the kernel reads y for every activation but LINEAR (selected when y is NULL)
+  if (!src.coef || !dzout || (src.y == nullptr && src.act != CBB_ACT_LINEAR)) return CBB_EINVAL;
+  const int direct = p.splits == 1;
+  float* out = direct ? dw : ws;
+  if (g.S == 1)
+    launch_dw3_rows<1>(g, p, x, delta, out, direct, st, &src, dzout);
+  else
+    launch_dw3_rows<2>(g, p, x, delta, out, direct, st, &src, dzout);
+  const int rc = check_launch("conv_dw3_rows (dz formed)");
+  if (rc != CBB_OK || direct) return rc;
+  return launch_dw_reduce(g, dw, ws, p.splits, p.groups, 1, st);
 }
 
 // dW of one group (or of a plain convolution).

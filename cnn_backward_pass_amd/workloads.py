@@ -70,6 +70,9 @@ class Runner:
             # kernel forms it from delta, y and x_hat (conv_block_backward with dz=None)
             has_dx = not (name == "lenet" and li == 0)
             ent["form_dz"] = bool(ent["fused"]) and has_dx and (c.bn or c.act != "linear")
+            # batch statistics on a 3x3 row-streaming layer: the dW kernel forms dz and
+            # writes it for dX (the act/BN stage stops after the channel sums)
+            ent["dw_forms_dz"] = bool(cbb.conv_dw_forms_dz(desc))
             ent["dw"] = torch.zeros_like(ent["w"])
             ent["db"] = torch.zeros(c.out_c, dtype=f32, device=device)
             ent["ws_bytes"] = cbb.conv_block_workspace_size(desc)
@@ -151,6 +154,19 @@ class Runner:
         # the library computes both gradients in one fused kernel).
         _, stage, mark = probe
         dz = delta if e["dz"] is None else e["dz"]
+        if e["dw_forms_dz"]:
+            # the block without dx (act/BN sums, then dW forming and writing dz), then dX
+            mark(stage == "actbn_dW", True)
+            cbb.conv_block_backward(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
+                                    e["gamma"], delta, e["dz"], e["dw"], e["db"], e["dgamma"],
+                                    None, False, self.workspace, stream)
+            mark(stage == "actbn_dW", False)
+            if dx is not None:
+                mark(stage == "dX", True)
+                cbb.conv_backward_data(e["desc"], e["w"], e["dz"], dx, dx_accumulate,
+                                       self.workspace, stream)
+                mark(stage == "dX", False)
+            return
         mark(stage == "act_bn", True)
         cbb.conv_act_bn_backward(e["desc"], e["y"], e["xhat"], e["var"], e["gamma"], delta,
                                  e["dz"], e["db"], e["dgamma"], self.workspace, stream)
@@ -183,6 +199,8 @@ class Runner:
         has_dx = not (self.name == "lenet" and li == 0)
         if self.convs[li]["form_dz"]:
             return ["block"]
+        if self.convs[li]["dw_forms_dz"]:
+            return ["actbn_dW", "dX"] if has_dx else ["actbn_dW"]
         if has_dx and self.convs[li]["fused"]:
             return ["act_bn", "dWdX"]
         return ["act_bn", "dW", "dX"] if has_dx else ["act_bn", "dW"]
@@ -203,6 +221,10 @@ class Runner:
                 raise ValueError("the first LeNet conv has no input gradient")
             cbb.conv_backward_data(e["desc"], e["w"], dz, self.d_in[li], False, self.workspace,
                                    stream)
+        elif stage == "actbn_dW":
+            cbb.conv_block_backward(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
+                                    e["gamma"], delta, e["dz"], e["dw"], e["db"], e["dgamma"],
+                                    None, False, self.workspace, stream)
         elif stage == "block":
             cbb.conv_block_backward(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
                                     e["gamma"], delta, None, e["dw"], e["db"], e["dgamma"],

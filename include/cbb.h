@@ -231,6 +231,16 @@ int cbb_conv_backward_weights_data(const cbb_conv_desc* desc, const float* x, co
  * aligned at the call; 0 otherwise; a negative status for an invalid
  * descriptor.  Informational: the results do not depend on it. */
 int cbb_conv_fused_weights_data(const cbb_conv_desc* desc);
+/* 1 when cbb_conv_block_backward, on this descriptor with batch statistics, forms dz
+ * inside the weight-gradient kernel: 3x3, pad 1, stride 1 or 2, 32 input channels,
+ * output channels a multiple of 64, widths multiples of 4, provided x,
+ * delta, y, x_norm and dz are 16-byte aligned and dz is none of delta, y, x_norm at the
+ * call.  That kernel then computes dz from delta, y and x_norm with the per-channel map
+ * of the BN backward while it stages them and writes dz for the input gradient, so the
+ * separate pass that writes dz goes away (dz is still written).  0 otherwise; a
+ * negative status for an invalid descriptor.  Informational: the results do not
+ * depend on it. */
+int cbb_conv_dw_forms_dz(const cbb_conv_desc* desc);
 
 /* Activation gradient alone (gradient_array, [P1] sections 3.1 and 7):
  * g[i] = delta[i] * act'(y[i]) for i < count.  g may equal delta. */

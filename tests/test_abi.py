@@ -91,6 +91,20 @@ def test_conv_null_required_pointer(missing):
     assert _call_conv(_desc(in_c=5), **{missing: None}) == -1
 
 
+def test_dw_forms_dz_query():
+    """Host-only query: which layers' weight-gradient kernel forms dz itself."""
+    q = lambda d: cbb.lib().cbb_conv_dw_forms_dz(ctypes.byref(d))
+    assert q(_desc(in_c=32, in_h=20, in_w=104, out_c=64, stride=2)) == 1
+    assert q(_desc(in_c=32, in_h=11, in_w=52, out_c=128)) == 1
+    assert q(_desc(in_c=64, in_h=11, in_w=52, out_c=128)) == 0      # more than one input block
+    assert q(_desc(in_c=32, in_h=20, in_w=104, out_c=64, stride=2, batch_normalize=2)) == 0
+    assert q(_desc(in_c=32, in_h=20, in_w=104, out_c=64, stride=2, batch_normalize=0)) == 0
+    assert q(_desc(in_c=32, in_h=26, in_w=26, out_c=64)) == 0       # width not a multiple of 4
+    assert q(_desc(in_c=48, in_h=20, in_w=104, out_c=64)) == 0      # input channels
+    assert q(_desc(in_c=32, in_h=20, in_w=104, out_c=96)) == 0      # output channels
+    assert q(_desc(ksize=3, in_c=0)) < 0
+
+
 def test_conv_formed_dz_rules():
     """dz = NULL asks the fused first-layer kernel to form dz itself: only valid on
     such a layer, with dx given and 16-byte aligned saved tensors."""

@@ -161,6 +161,34 @@ def test_conv_block_backward_forms_dz(case, acc):
             assert_close(key, got[key], ref[key])
 
 
+DW_FORMS_DZ_CASES = [  # batch statistics on the row-streaming 3x3 dW kernel's 16-byte path
+    (2, 32, 20, 104, 64, 3, 2, 1, True, "leaky"),    # stride 2, 52-wide strips
+    (2, 32, 11, 52, 128, 3, 1, 1, True, "logistic"), # run-time activation, two output blocks
+    (1, 32, 9, 64, 64, 3, 1, 1, True, "linear"),     # no activation: y not read
+    (2, 32, 12, 416, 64, 3, 2, 1, True, "relu"),     # four strips per row
+    (1, 32, 7, 32, 64, 3, 1, 1, True, "tanh"),       # 32-wide strip
+]
+
+
+@pytest.mark.parametrize("acc", [False, True])
+@pytest.mark.parametrize("case", DW_FORMS_DZ_CASES)
+def test_dw_kernel_forms_and_writes_dz(case, acc):
+    """The weight-gradient kernel forms dz from delta, y and x_hat, writes it (each element
+    once) and dX reads it: dz, dW, db, dgamma, dx match the
+    oracle.  In place (dz = delta) the stored-dz route runs instead."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    n, c, h, w, oc, k, s, p, bn, act = case
+    assert cbb.conv_dw_forms_dz(cbb.conv_desc(n, c, h, w, oc, k, s, p, bn, act))
+    announce(f"dW forming dz {case} accumulate={acc}")
+    ref, got = run_conv(torch, case, seed=700 + DW_FORMS_DZ_CASES.index(case), dx_accumulate=acc)
+    for key in ("dz", "dw", "db", "dx", "dgamma"):
+        assert_close(key, got[key], ref[key])
+    ref, got = run_conv(torch, case, seed=701, in_place=True)
+    for key in ("dz", "dw", "dx"):
+        assert_close(key + " (in place)", got[key], ref[key])
+
+
 GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (2, 8, 13, 13, 12, 3, 1, 1, True, "leaky", 2, 1),       # grouped 3x3
     (2, 16, 12, 12, 16, 3, 1, 2, True, "leaky", 16, 2),     # depthwise, dilated
