@@ -93,7 +93,7 @@ def _stage_kib(db: str, counter: str, stage: str):
     for _, name, v in counter_rows(db, counter):
         if "cbb::" not in name:
             continue
-        if not stage.endswith(("act_bn", "block")) and "actbn_" in name:
+        if not stage.endswith(("act_bn", "block", "actbn_dW")) and "actbn_" in name:
             continue   # the one act+BN pass that fills dz before the timed reps
         k = kinds[_short(name)]
         k[0] += 1
