@@ -131,6 +131,85 @@ __global__ __launch_bounds__(kThreads) void conv_fwd_kernel(ConvGeom g, const fl
 }
 
 // ---------------------------------------------------------------------------
+// Layers with a short reduction (C*K*K <= 32, at most 32 output channels: a
+// network's first layer on an image) are bound by writing z.  Each wave takes 32
+// output pixels at a time as one 32 (o) x 32 (pixels) x 32 (j) matrix-core block
+// (16 steps of v_mfma_f32_32x32x2_f32): the weights stay in registers for the
+// whole kernel (lane l: W[l % 32][2s + l / 32]), each lane gathers the 16 taps
+// 2s + l / 32 of pixel l % 32, and every accumulator row is one output channel's
+// 32 consecutive pixels (coalesced stores).  Taps j >= J and channels o >= OC are
+// zero operands.
+// ---------------------------------------------------------------------------
+constexpr int kSmallJ = 32, kSmallJOc = 32;
+
+__global__ __launch_bounds__(kThreads) void conv_fwd_smallj(ConvGeom g, const float* __restrict__ x,
+                                                           const float* __restrict__ wt,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ z, int64_t tiles) {
+  // per tap j: its input-plane offset and its row / column shift under the window
+  __shared__ int toff[kSmallJ], tdh[kSmallJ], tdw[kSmallJ];
+  if (threadIdx.x < kSmallJ) {
+    const int j = threadIdx.x, KK = g.K * g.K;
+    const int i = j / KK, t = j - i * KK, kh = t / g.K, kw = t - kh * g.K;
+    toff[j] = j < g.J ? i * g.HW : 0;
+    // taps past J get a shift that is never inside the image: their operand is 0
+    tdh[j] = j < g.J ? kh * g.D : -(1 << 28);
+    tdw[j] = j < g.J ? kw * g.D : 0;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int m = lane & 31, kq = lane >> 5;
+  float wa[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int j = 2 * s + kq;
+    wa[s] = (m < g.OC && j < g.J) ? wt[m * g.J + j] : 0.f;
+  }
+  // the output channels this lane's accumulator rows hold, and their biases
+  float bo[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int o = acc_row(r, lane);
+    bo[r] = (bias && o < g.OC) ? bias[o] : 0.f;
+  }
+  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < tiles;
+       tile += (int64_t)gridDim.x * 4) {
+    const int64_t q = tile * 32 + m;
+    const bool qv = q < g.Q;
+    int b = 0, r = 0, h0 = 0, w0 = 0;
+    if (qv) {
+      b = (int)(q / g.OHW);
+      r = (int)(q - (int64_t)b * g.OHW);
+      const int ho = r / g.OW, wo = r - ho * g.OW;
+      h0 = ho * g.S - g.P;
+      w0 = wo * g.S - g.P;
+    }
+    const float* xb = x + (int64_t)b * g.xs;
+    float bv[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int j = 2 * s + kq;
+      const int h = h0 + tdh[j], w = w0 + tdw[j];
+      const bool ok = qv && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+      bv[s] = ok ? xb[toff[j] + h * g.W + w] : 0.f;
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[s], bv[s], acc, 0, 0, 0);
+    if (qv) {
+      float* zb = z + (int64_t)b * g.zs + r;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int o = acc_row(i, lane);
+        if (o < g.OC) zb[(int64_t)o * g.OHW] = acc[i] + bo[i];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // A plain stride-1 forward is the input gradient of another convolution:
 //   z[n][o][h][w] = sum_{i,kh,kw} W[o][i][kh][kw] x[n][i][h + kh - P][w + kw - P]
 //                 = sum_{i,kh,kw} W'[i][o][kh][kw] x[n][i][h + P' - kh][w + P' - kw]
@@ -194,6 +273,12 @@ int launch_conv_forward(const ConvGeom& g, const float* x, const float* wt, cons
     const int rc = check_launch("flip_transpose_weights");
     if (rc) return rc;
     return launch_conv_dx(t, wflip, x, z, 0, ws2, st);
+  }
+  if (g.G == 1 && g.J <= kSmallJ && g.OC <= kSmallJOc) {
+    const int64_t tiles = ceil_div(g.Q, 32);
+    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(tiles, 4), 8192);
+    conv_fwd_smallj<<<blocks, kThreads, 0, st>>>(g, x, wt, bias, z, tiles);
+    return check_launch("conv_fwd_smallj");
   }
   ConvGeom s = g;
   s.C = g.C / g.G;

@@ -22,7 +22,9 @@ FWD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (1, 8, 17, 16, 12, 5, 2, 4, 1, "relu", 1, 2),        # dilated 5x5, stride 2
     (3, 32, 9, 9, 48, 3, 1, 1, 2, "leaky", 1, 1),        # fixed statistics
     (2, 24, 14, 18, 130, 3, 2, 1, 1, "leaky", 1, 1),     # 128 x 128 tiles, ragged o and pixels
-    (1, 32, 20, 20, 80, 3, 1, 1, 0, "relu", 1, 1),       # bias: general kernel, 128 x 128 tiles
+    (1, 32, 20, 20, 80, 3, 1, 1, 0, "relu", 1, 1),       # bias: general kernel, more than 64 o
+    (2, 2, 15, 17, 24, 3, 2, 1, 1, "leaky", 1, 1),       # short reduction (J = 18), stride 2
+    (1, 3, 20, 21, 32, 3, 1, 2, 0, "relu", 1, 2),        # short reduction, dilated, bias
 ]
 
 
