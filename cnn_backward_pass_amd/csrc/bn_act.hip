@@ -333,45 +333,90 @@ __device__ __forceinline__ float act_fwd(int act, float slope, float u) {
   }
 }
 
-// Per-(channel, segment) sum of z (CENTER = false) or of (z - mean)^2 (CENTER = true).
-template <bool VEC, bool CENTER>
-__global__ __launch_bounds__(kThreads) void bnf_partial(SegGeom s, const float* __restrict__ z,
-                                                        const float* __restrict__ mean,
-                                                        float* __restrict__ part) {
+// Batch statistics in one pass.  Each thread sums d = z - K and d^2 with K its own
+// first element (a shift inside the data keeps the sums small), turns them into
+// (count, mean, M2 = sum of squared deviations), and the work-group merges the 256
+// triples pairwise in a fixed tree (Chan, Golub and LeVeque's update:
+// mean = mean_a + d n_b / n, M2 = M2_a + M2_b + d^2 n_a n_b / n with d = mean_b - mean_a)
+// into its segment's (mean, M2); bnf_stats_fold merges the segments in order.
+struct Moments {
+  float n, mean, m2;
+};
+__device__ __forceinline__ Moments merge_moments(Moments a, Moments b) {
+  if (b.n == 0.f) return a;
+  if (a.n == 0.f) return b;
+  const float n = a.n + b.n, d = b.mean - a.mean, fb = b.n / n;
+  return Moments{n, a.mean + d * fb, a.m2 + b.m2 + d * d * a.n * fb};
+}
+
+// elements in segment sg of a channel (the split of for_segment)
+__device__ __forceinline__ int64_t seg_count(const SegGeom& s, int sg) {
+  if (s.parts > 1) {
+    const int part = sg % s.parts, r0 = part * s.chunk;
+    return min(s.HW, r0 + s.chunk) - r0;
+  }
+  const int n0 = sg * s.group, n1 = min(s.N, n0 + s.group);
+  return (int64_t)(n1 - n0) * s.HW;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void bnf_stats(SegGeom s, const float* __restrict__ z,
+                                                      float2* __restrict__ part) {
   const int c = blockIdx.x / s.nseg, sg = blockIdx.x % s.nseg;
-  const float mu = CENTER ? mean[c] : 0.f;
-  float acc = 0.f;
+  float k = 0.f, s1 = 0.f, s2 = 0.f;
+  int cnt = 0;
+  auto add = [&](float v) {
+    if (cnt == 0) k = v;
+    const float d = v - k;
+    s1 += d;
+    s2 += d * d;
+    ++cnt;
+  };
   if constexpr (VEC) {
     for_segment<true>(s, c, sg, [&](int64_t o) {
       const float4 v = ld4(z + o);
-      if (CENTER) {
-        const float a = v.x - mu, b = v.y - mu, cc = v.z - mu, d = v.w - mu;
-        acc += (a * a + b * b) + (cc * cc + d * d);
-      } else {
-        acc += (v.x + v.y) + (v.z + v.w);
-      }
+      add(v.x);
+      add(v.y);
+      add(v.z);
+      add(v.w);
     });
   } else {
-    for_segment<false>(s, c, sg, [&](int64_t o) {
-      const float v = z[o] - mu;
-      acc += CENTER ? v * v : v;
-    });
+    for_segment<false>(s, c, sg, [&](int64_t o) { add(z[o]); });
   }
-  __shared__ float red[4];
-  acc = block_sum_256(acc, red);
-  if (threadIdx.x == 0) part[blockIdx.x] = acc;
+  __shared__ Moments red[kThreads];
+  Moments m{0.f, 0.f, 0.f};
+  if (cnt > 0) {
+    const float n = (float)cnt, mu = s1 / n;
+    m = Moments{n, k + mu, fmaxf(s2 - s1 * mu, 0.f)};
+  }
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int stride = kThreads / 2; stride > 0; stride >>= 1) {
+    if ((int)threadIdx.x < stride) red[threadIdx.x] = merge_moments(red[threadIdx.x], red[threadIdx.x + stride]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = make_float2(red[0].mean, red[0].m2);
 }
 
-// out[c] = (the channel's segment sums, folded in a fixed order) * inv_m.
-__global__ __launch_bounds__(kThreads) void bnf_fold(const float* __restrict__ part, int nseg,
-                                                     float inv_m, float* __restrict__ out) {
-  __shared__ float red[4];
+// mean[c], var[c] (biased) from the channel's segments, merged in order in double.
+__global__ __launch_bounds__(64) void bnf_stats_fold(SegGeom s, const float2* __restrict__ part,
+                                                     float* __restrict__ mean,
+                                                     float* __restrict__ var) {
   const int c = blockIdx.x;
-  float a = 0.f;
-  for (int k = threadIdx.x; k < nseg; k += kThreads) a += part[(int64_t)c * nseg + k];
-  a = block_sum_256(a, red);
-  if (threadIdx.x == 0) out[c] = a * inv_m;
+  if (threadIdx.x != 0) return;
+  double n = 0.0, mu = 0.0, m2 = 0.0;
+  for (int sg = 0; sg < s.nseg; ++sg) {
+    const double nb = (double)seg_count(s, sg);
+    const float2 v = part[(int64_t)c * s.nseg + sg];
+    const double tot = n + nb, d = (double)v.x - mu;
+    mu += d * nb / tot;
+    m2 += (double)v.y + d * d * n * nb / tot;
+    n = tot;
+  }
+  mean[c] = (float)mu;
+  var[c] = (float)(m2 / n);
 }
+
 
 // BN: xn holds z on entry and x_norm on exit; y = act(gamma x_norm + beta).
 // No BN: y holds z (+ bias) on entry and act of it on exit (xn == y).
@@ -554,19 +599,14 @@ int launch_bn_act_forward(int N, int C, int64_t HW, int bn, float eps, int act, 
   const SegGeom s = plan_seg(N, C, HW);
   const unsigned blocks = (unsigned)((int64_t)C * s.nseg);
   const bool vec = (HW % 4 == 0) && aligned16(xn) && aligned16(y);
-  float* part = reinterpret_cast<float*>(ws);
   if (bn == 1) {
-    const float inv_m = 1.f / (float)s.M;
+    // one reading pass: per-segment (mean, M2), merged per channel
+    float2* mp = reinterpret_cast<float2*>(ws);
     if (vec)
-      bnf_partial<true, false><<<blocks, kThreads, 0, st>>>(s, xn, nullptr, part);
+      bnf_stats<true><<<blocks, kThreads, 0, st>>>(s, xn, mp);
     else
-      bnf_partial<false, false><<<blocks, kThreads, 0, st>>>(s, xn, nullptr, part);
-    bnf_fold<<<(unsigned)C, kThreads, 0, st>>>(part, s.nseg, inv_m, mean);
-    if (vec)
-      bnf_partial<true, true><<<blocks, kThreads, 0, st>>>(s, xn, mean, part);
-    else
-      bnf_partial<false, true><<<blocks, kThreads, 0, st>>>(s, xn, mean, part);
-    bnf_fold<<<(unsigned)C, kThreads, 0, st>>>(part, s.nseg, inv_m, var);
+      bnf_stats<false><<<blocks, kThreads, 0, st>>>(s, xn, mp);
+    bnf_stats_fold<<<(unsigned)C, 64, 0, st>>>(s, mp, mean, var);
   }
   if (bn) {
     if (vec)
@@ -583,7 +623,7 @@ int launch_bn_act_forward(int N, int C, int64_t HW, int bn, float eps, int act, 
       bnf_apply<false, false><<<blocks, kThreads, 0, st>>>(s, y, y, nullptr, nullptr, nullptr,
                                                             nullptr, eps, act, slope);
   }
-  return check_launch("bnf_partial/bnf_fold/bnf_apply");
+  return check_launch("bnf_stats/bnf_stats_fold/bnf_apply");
 }
 
 int launch_act_backward(int act, float slope, const float* y, const float* delta, float* g,

@@ -63,6 +63,27 @@ def gpu_forward(torch, case, x, wt, gamma, beta, bias, mean, var):
     return {"y": h_(y), "xhat": h_(xn), "mean": h_(mu), "var": h_(va)}, desc
 
 
+@pytest.mark.parametrize("case,offset", [(FWD_CASES[1], 40.0), (FWD_CASES[2], -25.0),
+                                         ((4, 3, 64, 64, 32, 3, 1, 1, 1, "leaky", 1, 1), 60.0)])
+def test_forward_statistics_with_a_large_mean(case, offset):
+    """One-pass batch statistics (shifted per-thread sums merged pairwise) when the conv
+    output's mean is large against its spread: mean, var and x_norm still match the
+    oracle's two-pass double statistics."""
+    torch = require_gpu()
+    announce(f"forward statistics, input offset {offset}: {case}")
+    n, c, h, w, oc, k, s, p, bn, act, groups, dil = case
+    x, wt, gamma, beta, bias, mean, var = _inputs(case, 950)
+    x = (x + np.float32(offset)).astype(np.float32)
+    wt = (np.abs(wt) + np.float32(0.05)).astype(np.float32)   # same-sign weights: z far from 0
+    got, _ = gpu_forward(torch, case, x, wt, gamma, beta, bias, mean, var)
+    L = _layer(c, oc, k, s, p, bn, act, h, w, groups, dil)
+    ref = M.conv_block_forward(L, x, wt, bias=bias, gamma=gamma, beta=beta, mean=mean, var=var)
+    assert_close("mean", got["mean"], ref["mean"])
+    assert_close("var", got["var"], ref["var"])
+    assert_close("x_norm", got["xhat"], ref["xhat"])
+    assert_close("y", got["y"], ref["y"])
+
+
 @pytest.mark.parametrize("case", FWD_CASES)
 def test_conv_block_forward_parity(case):
     torch = require_gpu()
