@@ -10,12 +10,17 @@
 //   dz = (g' - mean(g') - mean(g' x_norm) x_norm) / sqrt(var + eps), g' = gamma g.
 //
 // Pass 1 (actbn_reduce) : each work-group sums (g, g*x_norm) over one segment
-//                         of one channel -> workspace partials[c][seg].
+//                         of one channel -> workspace partials[c][seg].  Without
+//                         batch statistics dz does not depend on the sums and is
+//                         written here (then actbn_fold adds the sums up).
 // Pass 2 (actbn_apply)  : each work-group first folds its channel's partials in
 //                         a fixed order (deterministic), derives the per-channel
 //                         affine map dz = a*g + b + c*x_norm, writes dz for its
 //                         segment; segment 0 also adds the channel's sums into
 //                         dgamma / dbeta (or db).
+// When a gradient kernel forms dz itself, actbn_coef replaces pass 2: one
+// work-group per channel folds the sums and writes the map (a, b, c).
+// The forward's statistics, normalisation and activation (bnf_*) follow below.
 // A channel's data is N planes of HW floats, (n*C + c)*HW apart; a segment is a
 // contiguous run of the flattened (n, hw) index.
 #include "cbb_internal.h"
