@@ -113,6 +113,117 @@ __global__ __launch_bounds__(kThreads) void dwise_dx(ConvGeom g, const float* __
   }
 }
 
+// ---------------------------------------------------------------------------
+// Planes that fit in LDS (an x and a dz plane together at most kDwPlane floats,
+// 48 KB): one work-group stages whole planes once with coalesced loads and reads
+// every tap from LDS.  The LDS is sized to the planes (dynamic), so small planes
+// leave room for several work-groups per CU.
+// ---------------------------------------------------------------------------
+constexpr int kDwPlane = 12288;
+
+static bool dwise_lds_ok(const ConvGeom& g) { return g.HW + g.OHW <= kDwPlane; }
+
+// dX: work-group = one (image, channel) plane.
+template <int K>
+__global__ __launch_bounds__(kThreads) void dwise_dx_lds(ConvGeom g, const float* __restrict__ wt,
+                                                         const float* __restrict__ dz,
+                                                         float* __restrict__ dx, int accumulate) {
+  extern __shared__ float zs[];     // the dz plane, OHW floats
+  const int64_t plane = blockIdx.x;   // n * C + c
+  const int c = (int)(plane % g.C);
+  const float* dzp = dz + plane * g.OHW;
+  for (int e = threadIdx.x; e < g.OHW; e += kThreads) zs[e] = dzp[e];
+  float wk[K * K];
+#pragma unroll
+  for (int t = 0; t < K * K; ++t) wk[t] = wt[(int64_t)c * K * K + t];
+  __syncthreads();
+  float* dxp = dx + plane * g.HW;
+  if (g.S == 1) {   // every tap lands on an output position: no phase test, no division
+    for (int e = threadIdx.x; e < g.HW; e += kThreads) {
+      const int h = e / g.W, w = e - h * g.W;
+      float acc = 0.f;
+#pragma unroll
+      for (int kh = 0; kh < K; ++kh) {
+        const int ho = h + g.P - kh * g.D;
+        if ((unsigned)ho >= (unsigned)g.OH) continue;
+#pragma unroll
+        for (int kw = 0; kw < K; ++kw) {
+          const int wo = w + g.P - kw * g.D;
+          if ((unsigned)wo < (unsigned)g.OW) acc += wk[kh * K + kw] * zs[ho * g.OW + wo];
+        }
+      }
+      dxp[e] = accumulate ? dxp[e] + acc : acc;
+    }
+    return;
+  }
+  for (int e = threadIdx.x; e < g.HW; e += kThreads) {
+    const int h = e / g.W, w = e - h * g.W;
+    float acc = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < K; ++kh) {
+      const int th = h + g.P - kh * g.D;
+      if (th < 0 || th % g.S) continue;
+      const int ho = th / g.S;
+      if (ho >= g.OH) continue;
+#pragma unroll
+      for (int kw = 0; kw < K; ++kw) {
+        const int tw = w + g.P - kw * g.D;
+        if (tw < 0 || tw % g.S) continue;
+        const int wo = tw / g.S;
+        if (wo >= g.OW) continue;
+        acc += wk[kh * K + kw] * zs[ho * g.OW + wo];
+      }
+    }
+    dxp[e] = accumulate ? dxp[e] + acc : acc;
+  }
+}
+
+// dW partial sums: work-group (c, segment) walks the images n0 .. n1-1 of its
+// segment, staging each image's x and dz planes of channel c in LDS.
+template <int K>
+__global__ __launch_bounds__(kThreads) void dwise_dw_lds(ConvGeom g, const float* __restrict__ x,
+                                                         const float* __restrict__ dz,
+                                                         float* __restrict__ part, int nseg,
+                                                         int per_seg) {
+  extern __shared__ float xz[];     // the x plane (HW floats), then the dz plane
+  float* xs = xz;
+  float* zs = xz + g.HW;
+  const int c = blockIdx.x / nseg, sg = blockIdx.x % nseg;
+  const int n0 = sg * per_seg, n1 = min(g.N, n0 + per_seg);
+  float acc[K * K];
+#pragma unroll
+  for (int t = 0; t < K * K; ++t) acc[t] = 0.f;
+  for (int n = n0; n < n1; ++n) {
+    const float* xp = x + ((int64_t)n * g.C + c) * g.HW;
+    const float* dzp = dz + ((int64_t)n * g.C + c) * g.OHW;
+    __syncthreads();   // the previous image's reads are done
+    for (int e = threadIdx.x; e < g.HW; e += kThreads) xs[e] = xp[e];
+    for (int e = threadIdx.x; e < g.OHW; e += kThreads) zs[e] = dzp[e];
+    __syncthreads();
+    for (int q = threadIdx.x; q < g.OHW; q += kThreads) {
+      const int ho = q / g.OW, wo = q - ho * g.OW;
+      const float d = zs[q];
+      const int h0 = ho * g.S - g.P, w0 = wo * g.S - g.P;
+#pragma unroll
+      for (int kh = 0; kh < K; ++kh) {
+        const int h = h0 + kh * g.D;
+        const bool hv = (unsigned)h < (unsigned)g.H;
+#pragma unroll
+        for (int kw = 0; kw < K; ++kw) {
+          const int w = w0 + kw * g.D;
+          if (hv && (unsigned)w < (unsigned)g.W) acc[kh * K + kw] += d * xs[h * g.W + w];
+        }
+      }
+    }
+  }
+  __shared__ float red[4];
+#pragma unroll
+  for (int t = 0; t < K * K; ++t) {
+    const float v = block_sum_256(acc[t], red);
+    if (threadIdx.x == 0) part[((int64_t)c * nseg + sg) * (K * K) + t] = v;
+  }
+}
+
 size_t conv_depthwise_workspace(const ConvGeom& g) {
   const DwiseSeg s = dwise_plan(g);
   return (size_t)g.C * s.nseg * g.K * g.K * sizeof(float);
@@ -120,6 +231,26 @@ size_t conv_depthwise_workspace(const ConvGeom& g) {
 
 int launch_depthwise_dw(const ConvGeom& g, const float* x, const float* dz, float* dw, float* ws,
                         hipStream_t st) {
+  if (dwise_lds_ok(g)) {
+    // segments of whole images, no more than the streaming plan's (its workspace)
+    const int nseg = std::max(1, std::min(dwise_plan(g).nseg, g.N));
+    const int per_seg = (int)ceil_div(g.N, nseg);
+    const int nseg2 = (int)ceil_div(g.N, per_seg);
+    const unsigned blocks = (unsigned)((int64_t)g.C * nseg2);
+    const size_t lds = (size_t)(g.HW + g.OHW) * sizeof(float);
+#define CBB_DWL(K_)                                                                          \
+  case K_:                                                                                   \
+    dwise_dw_lds<K_><<<blocks, kThreads, lds, st>>>(g, x, dz, ws, nseg2, per_seg);           \
+    break;
+    switch (g.K) {
+      CBB_DWL(1) CBB_DWL(2) CBB_DWL(3) CBB_DWL(4) CBB_DWL(5) CBB_DWL(6) CBB_DWL(7)
+    }
+#undef CBB_DWL
+    const int rc = check_launch("dwise_dw_lds");
+    if (rc) return rc;
+    dwise_dw_fold<<<(unsigned)g.C, 64, 0, st>>>(ws, nseg2, g.K * g.K, dw);
+    return check_launch("dwise_dw_fold");
+  }
   const DwiseSeg s = dwise_plan(g);
   const unsigned blocks = (unsigned)((int64_t)g.C * s.nseg);
 #define CBB_DWW(K_)                                                                        \
@@ -138,6 +269,19 @@ int launch_depthwise_dw(const ConvGeom& g, const float* x, const float* dz, floa
 
 int launch_depthwise_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx,
                         int accumulate, hipStream_t st) {
+  if (dwise_lds_ok(g)) {
+    const unsigned blocks = (unsigned)((int64_t)g.N * g.C);
+    const size_t lds = (size_t)g.OHW * sizeof(float);
+#define CBB_DXL(K_)                                                                          \
+  case K_:                                                                                   \
+    dwise_dx_lds<K_><<<blocks, kThreads, lds, st>>>(g, wt, dz, dx, accumulate);              \
+    break;
+    switch (g.K) {
+      CBB_DXL(1) CBB_DXL(2) CBB_DXL(3) CBB_DXL(4) CBB_DXL(5) CBB_DXL(6) CBB_DXL(7)
+    }
+#undef CBB_DXL
+    return check_launch("dwise_dx_lds");
+  }
   const int64_t total = (int64_t)g.N * g.C * g.HW;
   const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(total, kThreads), 16384);
 #define CBB_DWX(K_)                                                                   \
