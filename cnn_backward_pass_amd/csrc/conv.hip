@@ -254,8 +254,14 @@ struct Dw3RowCfg {
 template <int S, int TC, bool V4, int FZ = kFzOff>
 __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
     ConvGeom g, const float* __restrict__ x, const float* __restrict__ dz, float* __restrict__ out,
-    int strips, int rchunks, int rlen, int direct, DzSource src, float* __restrict__ dzout) {
+    int strips, int rchunks, int rlen, int direct, DzSource src, float* __restrict__ dzout,
+    int64_t out_gstride) {
   using Cf = Dw3RowCfg<S, TC>;
+  // group blockIdx.y of a grouped convolution (g holds the group's channel counts and
+  // the whole tensors' image strides; dz is formed only on plain layers)
+  x += blockIdx.y * g.gx;
+  dz += blockIdx.y * g.gz;
+  out += blockIdx.y * out_gstride;
   constexpr int NT = kDw3Threads;
   __shared__ float lds[Cf::LDS_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -268,8 +274,8 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
   const int r0 = rc * rlen, r1 = min(g.OH, r0 + rlen);  // non-empty by construction
   const int oc0 = strip * TC;       // first output column of the strip
   const int ic0 = oc0 * S - 1;      // input column held in LDS column 0
-  const float* xb = x + ((int64_t)n * g.C + cb * 32) * g.HW;
-  const float* zb = dz + ((int64_t)n * g.OC + ob * 64) * g.OHW;
+  const float* xb = x + (int64_t)n * g.xs + (int64_t)cb * 32 * g.HW;
+  const float* zb = dz + (int64_t)n * g.zs + (int64_t)ob * 64 * g.OHW;
   constexpr bool fz = FZ != kFzOff, fz_y = fz && FZ != CBB_ACT_LINEAR;
   static_assert(!fz || V4, "dz is formed on the 16-byte path only");
   const int64_t zoff = ((int64_t)n * g.OC + ob * 64) * g.OHW;
@@ -1795,7 +1801,8 @@ static bool conv1x1_ok(const ConvGeom& g) {
 
 static DwPlan plan_dw(const ConvGeom& g) {
   DwPlan best{};
-  if (dense(g) && plan_dw3_rows(g, best)) return best;
+  // the row-streaming kernel also takes the groups of a grouped layer (undilated)
+  if (g.D == 1 && plan_dw3_rows(g, best)) return best;
   // 1x1: conv1x1_dw_dma when the tensors are 16-byte aligned (it has its own plan and
   // workspace, conv1x1_dw_workspace); otherwise the general kernel on these 64x64 tiles
   if (dense(g) && conv1x1_ok(g)) {
@@ -1953,19 +1960,22 @@ static void launch_dw_tile(const ConvGeom& g, const DwPlan& p, const float* x, c
                                                 direct, ostride);
 }
 
+// Grouped layers (g the group geometry): all groups in one launch on the grid's y
+// axis; group j's dW block (direct) or partial region is out_gstride floats on.
 template <int S>
 static void launch_dw3_rows(const ConvGeom& g, const DwPlan& p, const float* x, const float* dz,
                             float* out, int direct, hipStream_t st, const DzSource* src = nullptr,
                             float* dzout = nullptr) {
+  const int64_t mn = (int64_t)g.OC * g.J;
+  const int64_t out_gstride = direct ? g.gw : ((int64_t)p.splits + p.groups) * mn;
   const unsigned blocks = (unsigned)((int64_t)p.splits * (g.OC / 64) * (g.C / 32));
   // 16-byte loads: rows and strip origins on 16-byte boundaries
   const bool v4 = aligned16(x) && aligned16(dz) && g.W % 4 == 0 && g.OW % 4 == 0 &&
                   p.rows_tc % 4 == 0;
   const DzSource s = src ? *src : DzSource{};
 #define CBB_DW3K(TC, V4, FZ)                                                                 \
-  conv_dw3_rows<S, TC, V4, FZ><<<blocks, kDw3Threads, 0, st>>>(g, x, dz, out, p.strips,      \
-                                                               p.rchunks, p.rlen, direct, s, \
-                                                               dzout)
+  conv_dw3_rows<S, TC, V4, FZ><<<dim3(blocks, (unsigned)g.G), kDw3Threads, 0, st>>>(        \
+      g, x, dz, out, p.strips, p.rchunks, p.rlen, direct, s, dzout, out_gstride)
 #define CBB_DW3(TC)                                                                          \
   case TC:                                                                                   \
     if constexpr (Dw3RowCfg<S, TC>::FITS) {                                                  \

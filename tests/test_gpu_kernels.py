@@ -205,6 +205,8 @@ GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (2, 8, 9, 9, 8, 1, 1, 0, False, "leaky", 8, 1),
     (8, 64, 52, 52, 64, 3, 1, 1, True, "leaky", 64, 1),     # depthwise, many segments per channel
     (2, 16, 12, 12, 32, 3, 1, 1, True, "leaky", 16, 1),     # two filters per channel (general)
+    (2, 64, 10, 52, 128, 3, 1, 1, True, "leaky", 2, 1),     # grouped dW on the row-streaming kernel
+    (2, 64, 12, 104, 128, 3, 2, 1, False, "relu", 2, 1),    # the same at stride 2, split rows
     (1, 4, 96, 96, 4, 3, 1, 1, True, "leaky", 4, 1),        # depthwise, plane beyond LDS: streaming
     (2, 8, 90, 91, 8, 5, 2, 2, False, "relu", 8, 1),        # depthwise, 8190-pixel plane in LDS, s2
 ]
