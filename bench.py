@@ -10,16 +10,23 @@ Inputs are seeded synthetic tensors already resident in HBM when timing
 starts.  ``value`` = algorithmic conv + inner-product GFLOP (dW + dX) of one step /
 seconds per step.
 
-The JSON line also carries the roofline of the dominant kernel (the stage of
-one layer that takes the most time; it is timed in place inside the timed
-steps with HIP events on the stream it runs on) and the CPU oracle timed on a
-bounded sample of the same workloads (``cpu_baseline``).
+The JSON line also carries the roofline of the dominant kernel (the longest
+single dW / dX / fused dW+dX kernel of the step, found by timing every kernel
+in place through the library's launch hook; inside the timed steps it is
+bracketed by HIP events on the stream it runs on), every gradient kernel's
+rate (``kernels``), the peaks measured on the box (``calibration``: an fp32
+matrix-core loop and a 1 GiB device copy) next to the published ones, warm and
+cold (L2 and the 256 MB memory-side cache flushed by a 512 MB write) step-time
+medians and minima, and the CPU oracle timed on a bounded sample of the same
+workloads (``cpu_baseline``).
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -48,9 +55,8 @@ def parse():
                     help="profiling mode: run a plain device copy of this many bytes --reps times "
                          "(calibrates the HBM byte counters); no JSON line")
     ap.add_argument("--reps", type=int, default=5)
-    ap.add_argument("--graph", action="store_true",
-                    help="time replays of the step captured as HIP graphs instead of eager "
-                         "steps (measured no faster on MI355X: the step is GPU-bound)")
+    ap.add_argument("--protocol-runs", type=int, default=30,
+                    help="steps timed one by one for the warm and the cold median / min")
     return ap.parse_args()
 
 
@@ -173,31 +179,161 @@ def time_stages(runners, torch, reps=3):
     return sorted(res, reverse=True)
 
 
-def capture_step(runners, torch, dom=None):
-    """One step of every workload captured as HIP graphs (hipGraph, through
-    torch.cuda.CUDAGraph): the step is ~60 small and large kernels, and replaying a
-    graph removes the launch gaps between them.  With dom = (workload, layer, stage)
-    the step is cut into three graphs -- before that stage, the stage, after it -- so
-    that events recorded between their replays time the stage in every step."""
-    graphs = [torch.cuda.CUDAGraph() for _ in range(3 if dom else 1)]
-    cur = [0]
+# ----------------------------------------------------------------------------- peaks on the box
+class Calib:
+    """libcbb_calib.so: an fp32 matrix-core loop and a device copy (measurement only)."""
 
-    def mark(target, before):
-        if target:
-            graphs[cur[0]].capture_end()
-            cur[0] += 1
-            graphs[cur[0]].capture_begin()
+    def __init__(self, torch, dev):
+        path = os.path.join(ROOT, "cnn_backward_pass_amd", "libcbb_calib.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: run __graft_entry__.build()")
+        self.lib = ctypes.CDLL(path)
+        self.lib.calib_mfma_f32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        self.lib.calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.c_void_p]
+        self.torch = torch
+        self.blocks = 1024            # 4 work-groups of 4 waves per CU: every SIMD busy
+        self.out = torch.empty(self.blocks * 256, dtype=torch.float32, device=dev)
 
-    capture_stream = torch.cuda.Stream()
-    torch.cuda.synchronize()
-    with torch.cuda.stream(capture_stream):
-        graphs[0].capture_begin()
-        for name, r in runners.items():
-            r.step(probe=(dom[1], dom[2], mark) if dom and name == dom[0] else None)
-        graphs[-1].capture_end()
-    torch.cuda.synchronize()
-    assert cur[0] == len(graphs) - 1, "the dominant stage was not captured"
-    return graphs
+    def _stream(self):
+        return ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+
+    def mfma(self, iters):
+        rc = self.lib.calib_mfma_f32(self.blocks, iters, ctypes.c_void_p(self.out.data_ptr()),
+                                     self._stream())
+        if rc:
+            raise RuntimeError("calib_mfma_f32 failed")
+        return float(self.blocks) * 4 * iters * 4 * (32 * 32 * 2 * 2)   # FLOPs
+
+    def copy(self, src, dst):
+        rc = self.lib.calib_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                 src.numel() * src.element_size(), self._stream())
+        if rc:
+            raise RuntimeError("calib_copy failed")
+
+
+def calibrate(calib, torch, dev, reps=5):
+    """The fp32 matrix rate and the copy bandwidth this GPU sustains (best of ``reps``)."""
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return min(ms)
+    iters = 20000
+    flops = calib.mfma(iters)
+    t_mfma = best(lambda: calib.mfma(iters))
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = best(lambda: calib.copy(src, dst))
+    del src, dst
+    return {"mfma_f32_TFLOPs": round(flops / (t_mfma * 1e-3) / 1e12, 2),
+            "copy_GBps": round(2.0 * (1 << 30) / (t_copy * 1e-3) / 1e9, 1),
+            "mfma_probe": f"{calib.blocks} work-groups x 4 waves, {iters} rounds of 4 independent "
+                          "v_mfma_f32_32x32x2_f32 chains from registers",
+            "copy_probe": "1 GiB device-to-device copy, 16 B per lane (bytes read + written)",
+            "published": {"mfma_f32_TFLOPs": PEAK_MFMA_F32 / 1e12, "hbm_GBps": PEAK_HBM / 1e9}}
+
+
+# ----------------------------------------------------------------------------- kernels
+GRAD_KERNELS = ("conv_dw", "conv_dx", "conv1x1_dw", "conv1x1_dx", "conv_first_rows", "dwise_dw",
+                "dwise_dx")
+
+
+def kernel_role(kernel):
+    """'dW', 'dX' or 'dWdX' for a gradient kernel of a conv layer, else None (reductions,
+    act/BN passes, the layers' copy kernels)."""
+    if kernel == "conv_first_rows":
+        return "dWdX"
+    if kernel.startswith(("conv_dw", "conv1x1_dw", "dwise_dw")) and "reduce" not in kernel:
+        return "dW"
+    if kernel.startswith(("conv_dx", "conv1x1_dx", "dwise_dx")):
+        return "dX"
+    return None
+
+
+def kernel_work(runner, call, kernel):
+    """(flops, bytes) of one launch of a gradient kernel, algorithmic (touch-once): the
+    layer's dW and/or dX FLOPs; bytes read once and written once, including the delta, y
+    and x_hat a kernel that forms dz reads, and the dz it writes."""
+    role = kernel_role(kernel)
+    li = next(i for i, c in enumerate(runner.wl.convs) if c.name == call)
+    c, e = runner.wl.convs[li], runner.convs[li]
+    n = e["desc"].batch
+    out_e = n * c.out_c * c.out_h * c.out_w
+    in_e = n * c.in_c * c.in_h * c.in_w
+    w_e = c.out_c * c.in_c * c.k * c.k
+    macs = out_e * c.in_c * c.k * c.k
+    nread = 1 + (c.act != "linear") + bool(c.bn)   # delta, y, x_hat
+    if role == "dWdX":
+        zin = nread if e["form_dz"] else 1
+        return 4.0 * macs, 4.0 * (2 * in_e + zin * out_e + 2 * w_e)
+    if role == "dW" and e["dw_forms_dz"] and "dz formed" in kernel:
+        return 2.0 * macs, 4.0 * (in_e + (nread + 1) * out_e + w_e)
+    return 2.0 * macs, 4.0 * (in_e + out_e + w_e)
+
+
+def time_kernels(runners, torch, blocker, reps=3):
+    """Every kernel of one step of every workload, timed in place: the step is enqueued
+    behind a ~10 ms matrix-core loop (so its kernels then run back to back, as in the
+    timed steps) with an event recorded after each kernel by the launch hook.  Returns
+    [(min ms, workload, ordinal in the step, call, kernel)]."""
+    rows = {}
+    for name, r in runners.items():
+        for _ in range(reps):
+            evs = []
+
+            def hook(call, kernel, evs=evs):
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                evs.append((call, kernel, e))
+            torch.cuda.synchronize()
+            blocker()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            r.step(hook=hook)
+            torch.cuda.synchronize()
+            prev = e0
+            for i, (call, kernel, e) in enumerate(evs):
+                ent = rows.setdefault((name, i), [call, kernel, []])
+                if ent[1] != kernel:
+                    raise RuntimeError(f"{name}: kernel {i} changed between steps")
+                ent[2].append(prev.elapsed_time(e))
+                prev = e
+    return sorted(((min(ms), name, i, call, kernel) for (name, i), (call, kernel, ms)
+                   in rows.items()), reverse=True)
+
+
+def step_protocol(runners, torch, dev, runs):
+    """Steps timed one at a time: warm (back to back) and cold (a 512 MB write before
+    each step, outside its events, evicts L2 and the 256 MB memory-side cache)."""
+    flush = torch.empty(512 * (1 << 20) // 4, dtype=torch.float32, device=dev)
+    out = {}
+    for mode in ("warm", "cold"):
+        ms = []
+        for k in range(runs):
+            if mode == "cold":
+                flush.fill_(float(k))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for r in runners.values():
+                r.step()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        out[mode] = {"median_ms": round(statistics.median(ms), 4), "min_ms": round(min(ms), 4),
+                     "runs": runs}
+    del flush
+    return out
+
 
 
 def _roof(ms, flops, nbytes):
@@ -324,11 +460,45 @@ def cpu_baseline(min_seconds=10.0, max_reps=4):
             M.workload_backward(wl, inp, saved, inp.get("delta"))
         t_total += time.perf_counter() - t0
         reps += 1
+    threads = oracle.num_threads()
+    # the two small workloads on one core as well (median of three runs each)
+    single = {}
+    oracle.set_threads(1)
+    try:
+        for wl, inp, saved in cases[:2]:
+            runs_flops = 0.0
+            ts = []
+            for _ in range(3):
+                t0 = time.perf_counter()
+                M.workload_backward(wl, inp, saved, inp.get("delta"))
+                ts.append(time.perf_counter() - t0)
+            for li, c in enumerate(wl.convs):
+                macs = wl.batch * c.out_c * c.out_h * c.out_w * c.in_c * c.k * c.k
+                runs_flops += 2.0 * macs * (1 if (wl.name == "lenet" and li == 0) else 2)
+            if wl.name == "lenet":
+                runs_flops += sum(2.0 * 2 * wl.batch * i * o for i, o in synth.LENET_FC)
+            w = statistics.median(ts)
+            single[wl.name] = {"value": round(runs_flops / w / 1e9, 3), "unit": "GFLOP/s",
+                               "median_s": round(w, 4)}
+    finally:
+        oracle.set_threads(threads)
     return {"value": step_flops * reps / t_total / 1e9, "unit": "GFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": threads, "kind": "oracle",
             "sample": f"{reps} full step(s) of the five-workload suite at full batch, "
                       f"{step_flops * reps / 1e9:.1f} GFLOP in {t_total:.1f} s, double precision",
-            "seconds": t_total, "host_cpus": os.cpu_count()}
+            "seconds": t_total, "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(),
+            "single_thread": single}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -341,7 +511,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    from cnn_backward_pass_amd import cbb
+    from cnn_backward_pass_amd import cbb, profsum
     cbb.lib()
     dev = "cuda:0"
     torch.cuda.set_device(0)
@@ -351,6 +521,9 @@ def main():
     if args.copy_bytes:
         profile_copy(args.copy_bytes, args.reps, torch)
         return
+    calib = Calib(torch, dev)
+    print("[bench] calibration (fp32 matrix loop, 1 GiB copy)", file=sys.stderr, flush=True)
+    peaks = calibrate(calib, torch, dev)
     runners = build_runners(dev)
     step_flops = sum(r.flops() for r in runners.values())
     for r in runners.values():
@@ -361,87 +534,105 @@ def main():
             r.step()
     torch.cuda.synchronize()
 
-    # Find the dominant kernel before the timed region: the longest dW, dX or fused
-    # dW+dX stage (each is one kernel plus, for split reductions, a short
-    # ordered-sum kernel);
-    # act+BN stages are two streaming kernels of comparable size and are reported
-    # separately (their longest kernel is shorter than the dominant conv kernel).
+    # Every kernel of the step timed in place, before the timed region; the dominant
+    # kernel is the longest single gradient kernel (dW, dX or fused dW + dX, including
+    # a dW kernel that forms dz), without its act/BN passes and split reductions.
+    kern = time_kernels(runners, torch, lambda: calib.mfma(20000))
+    grads = [k for k in kern if kernel_role(k[4]) is not None]
+    dom_ms, dom_name, dom_i, dom_call, dom_kernel = grads[0]
+    print(f"[bench] dominant kernel {dom_name}.{dom_call}.{dom_kernel} (#{dom_i}) "
+          f"{dom_ms:.3f} ms", file=sys.stderr, flush=True)
     stages = time_stages(runners, torch)
-    conv_stages = [st for st in stages if st[3] in ("dW", "dX", "dWdX")]
-    dom_ms, dom_name, dom_li, dom_stage = conv_stages[0]
-    print(f"[bench] dominant stage {dom_name}.{dom_li}.{dom_stage} {dom_ms:.3f} ms",
-          file=sys.stderr, flush=True)
 
-    # Timed region: K steps enqueued eagerly (or, with --graph, replayed from HIP
-    # graphs with the dominant stage as its own graph); the dominant stage is bracketed
-    # by events on its stream in every step.
+    # Timed region: K steps enqueued eagerly; the dominant kernel is bracketed by events
+    # recorded (through the launch hook) after the kernel before it and after it.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
+    seen = []
 
     def eager_step(k):
-        def mark(target, before):
-            if target:
-                ev[k][0 if before else 1].record()
         for name, r in runners.items():
-            r.step(probe=(dom_li, dom_stage, mark) if name == dom_name else None)
+            if name != dom_name:
+                r.step()
+                continue
+            cnt = [0]
+            if dom_i == 0:
+                ev[k][0].record()
 
-    if args.graph:
-        g_pre, g_dom, g_post = capture_step(runners, torch, (dom_name, dom_li, dom_stage))
-        for _ in range(2):  # the first replays upload the graphs
-            g_pre.replay(); g_dom.replay(); g_post.replay()
+            def hook(call, kernel):
+                i = cnt[0]
+                cnt[0] += 1
+                if i == dom_i - 1:
+                    ev[k][0].record()
+                elif i == dom_i:
+                    ev[k][1].record()
+                    seen.append(kernel)
+            r.step(hook=hook)
+
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
     for k in range(args.steps):
-        if not args.graph:
-            eager_step(k)
-            continue
-        g_pre.replay()
-        ev[k][0].record()
-        g_dom.replay()
-        ev[k][1].record()
-        g_post.replay()
+        eager_step(k)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = start.elapsed_time(stop)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    dom_avg_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    if seen != [dom_kernel] * args.steps:
+        raise RuntimeError(f"the timed steps ran {set(seen)} where {dom_kernel} was expected")
+    dom_times = [a.elapsed_time(b) for a, b in ev]
+    dom_avg_ms = sum(dom_times) / len(dom_times)
 
-    # Per-workload breakdown (outside the timed region), also from graph replays.
+    print("[bench] per-workload and protocol timings", file=sys.stderr, flush=True)
     per = {}
     for name, r in runners.items():
-        run = r.step if not args.graph else capture_step({name: r}, torch)[0].replay
-        run()
+        r.step()
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
         for _ in range(5):
-            run()
+            r.step()
         e.record()
         torch.cuda.synchronize()
         ms = s.elapsed_time(e) / 5
         per[name] = {"ms": round(ms, 4), "gflop": round(r.flops() / 1e9, 4),
                      "gflops": round(r.flops() / ms / 1e6, 1)}
+    protocol = step_protocol(runners, torch, dev, args.protocol_runs)
 
-    flops, nbytes = stage_work(runners[dom_name], dom_li, dom_stage)
-    if dom_stage == "act_bn" or flops / nbytes < RIDGE:
-        roof = {"bound": "hbm", "achieved": nbytes / (dom_avg_ms * 1e-3) / 1e9,
-                "peak": PEAK_HBM / 1e9, "unit": "GB/s"}
-    else:
-        roof = {"bound": "mfma", "achieved": flops / (dom_avg_ms * 1e-3) / 1e12,
-                "peak": PEAK_MFMA_F32 / 1e12, "unit": "TFLOP/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    # HBM bytes per launch of this stage from the committed rocprofv3 counter summary,
+    def roof_of(ms, name, call, kernel):
+        flops, nbytes = kernel_work(runners[name], call, kernel)
+        if flops / nbytes >= RIDGE:
+            ach = flops / (ms * 1e-3) / 1e12
+            e = {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_F32 / 1e12,
+                 "unit": "TFLOP/s", "peak_measured": peaks["mfma_f32_TFLOPs"]}
+        else:
+            ach = nbytes / (ms * 1e-3) / 1e9
+            e = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                 "peak_measured": peaks["copy_GBps"]}
+        e["frac"] = ach / e["peak"]
+        e["frac_of_measured"] = ach / e["peak_measured"]
+        e["algorithmic_flops"], e["algorithmic_bytes"] = flops, nbytes
+        return e
+
+    roof = roof_of(dom_avg_ms, dom_name, dom_call, dom_kernel)
+    # HBM bytes of one launch of this kernel from the committed rocprofv3 counter summary,
     # reported only while the kernel sources are the ones that were profiled.
-    from cnn_backward_pass_amd import profsum
-    rec = profsum.load_traffic(f"{dom_name}.{dom_li}.{dom_stage}")
-    roof["traffic"] = None if rec is None else rec["traffic_bytes"]
-    roof["kernel"] = f"{dom_name}.{runners[dom_name].wl.convs[dom_li].name}.{dom_stage}"
+    dom_li = next(i for i, c in enumerate(runners[dom_name].wl.convs) if c.name == dom_call)
+    rec = profsum.load_kernel_traffic(dom_name, dom_li, dom_kernel)
+    roof["traffic"] = None if rec is None else rec
+    roof["kernel"] = f"{dom_name}.{dom_call}.{dom_kernel}"
     roof["avg_ms"] = dom_avg_ms
-    roof["algorithmic_flops"] = flops
-    roof["algorithmic_bytes"] = nbytes
+    roof["median_ms"] = statistics.median(dom_times)
+
+    kernels = {}
+    for ms, name, i, call, kernel in grads:
+        e = roof_of(ms, name, call, kernel)
+        kernels[f"{name}.{call}.{kernel}"] = {
+            "ms": round(ms, 4), "bound": e["bound"], "achieved": round(e["achieved"], 2),
+            "unit": e["unit"], "frac": round(e["frac"], 4),
+            "frac_of_measured": round(e["frac_of_measured"], 4)}
 
     line = {"metric": METRIC, "value": round(step_flops / (ms_per_step * 1e-3) / 1e9, 1),
             "unit": "GFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -451,7 +642,10 @@ def main():
                                    "batch: single_block b2@32x32, lenet b64, darknet53_residual "
                                    "b8@52x52, yolov3_stem b16@416x416, yolov3_head b8@26x26",
                        "gflop_per_step": round(step_flops / 1e9, 3), "parallelism": "none"},
-            "roofline": roof, "per_workload": per,
+            "roofline": roof, "calibration": peaks, "protocol": protocol,
+            "per_workload": per, "kernels": kernels,
+            "kernel_ms": {f"{n}#{i}.{call}.{k}": round(ms, 4)
+                          for ms, n, i, call, k in sorted(kern, key=lambda t: (t[1], t[2]))},
             "stages_ms": {f"{n}.{li}.{st}": round(ms, 4) for ms, n, li, st in stages},
             "act_bn_stages": {f"{n}.{li}": _act_bn_entry(runners[n], n, li, ms)
                               for ms, n, li, st in stages if st == "act_bn" and ms > 0.015},

@@ -90,7 +90,12 @@ _SIGS = {
     "cbb_route_backward": ([_i32, _i32, ctypes.POINTER(_i64), _P, ctypes.POINTER(_P), _P], _i32),
     "cbb_upsample_backward": ([_i32] * 5 + [_P, _P, _P], _i32),
     "cbb_maxpool_backward": ([_i32] * 6 + [_P, _P, _P, _P], _i32),
+    "cbb_get_device_error": ([_P, ctypes.POINTER(_i32)], _i32),
+    "cbb_set_launch_hook": ([_P, _P], _i32),
 }
+DEVERR_LABEL = 1
+# void (*)(void* user, const char* kernel, void* stream)
+LAUNCH_HOOK = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_void_p)
 EXPORTS = tuple(_SIGS)
 
 _lib = None
@@ -130,6 +135,41 @@ def _ptr(t: torch.Tensor | None, dtype=torch.float32, name: str = "tensor"):
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _sized(fn: str, **spec) -> None:
+    """Check each named tensor against the element count (or shape) its call implies:
+    a tensor too small for what the kernels read or write would be accessed out of
+    bounds on the device.  spec maps name -> (tensor or None, expected numel or shape)."""
+    for name, (t, want) in spec.items():
+        if t is None:
+            continue
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{fn}: {name}: expected a torch.Tensor")
+        if isinstance(want, tuple):
+            if tuple(t.shape) != want:
+                raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {want}")
+        elif t.numel() != int(want):
+            raise ValueError(f"{fn}: {name} has {t.numel()} elements, expected {int(want)}")
+
+
+def _conv_sizes(fn: str, desc: "ConvDesc", **tensors) -> None:
+    """Sizes of a conv block's tensors from its descriptor: x, dx [N,C,H,W]; y, x_norm,
+    delta, dz [N,O,OH,OW]; w, dw [O,C/groups,k,k]; per-channel vectors [O]."""
+    g = max(1, desc.groups)
+    if desc.in_c % g or desc.out_c % g or desc.out_h < 1 or desc.out_w < 1:
+        return  # the library rejects the descriptor itself with a status code
+    xs = (desc.batch, desc.in_c, desc.in_h, desc.in_w)
+    ys = (desc.batch, desc.out_c, desc.out_h, desc.out_w)
+    ws = (desc.out_c, desc.in_c // g, desc.ksize, desc.ksize)
+    kind = {"x": xs, "dx": xs, "y": ys, "x_norm": ys, "delta": ys, "dz": ys, "w": ws, "dw": ws}
+    spec = {}
+    for name, t in tensors.items():
+        want = kind.get(name, desc.out_c)
+        if isinstance(want, tuple) and t is not None and t.dim() != 4:
+            want = int(torch.Size(want).numel())
+        spec[name] = (t, want)
+    _sized(fn, **spec)
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -175,6 +215,8 @@ def conv_block_workspace_size(desc: ConvDesc) -> int:
 
 def conv_block_backward(desc: ConvDesc, x, w, y, x_norm, var, gamma, delta, dz, dw, db, dgamma,
                         dx, dx_accumulate: bool = False, workspace=None, stream=None) -> None:
+    _conv_sizes("conv_block_backward", desc, x=x, w=w, y=y, x_norm=x_norm, var=var, gamma=gamma,
+                delta=delta, dz=dz, dw=dw, db=db, dgamma=dgamma, dx=dx)
     wsp, wsb = _ws(workspace)
     _check("cbb_conv_block_backward", lib().cbb_conv_block_backward(
         ctypes.byref(desc), _ptr(x, name="x"), _ptr(w, name="w"), _ptr(y, name="y"),
@@ -193,6 +235,8 @@ def conv_block_forward_workspace_size(desc: ConvDesc) -> int:
 
 def conv_block_forward(desc: ConvDesc, x, w, bias, gamma, beta, mean, var, x_norm, y,
                        workspace=None, stream=None) -> None:
+    _conv_sizes("conv_block_forward", desc, x=x, w=w, bias=bias, gamma=gamma, beta=beta,
+                mean=mean, var=var, x_norm=x_norm, y=y)
     wsp, wsb = _ws(workspace)
     _check("cbb_conv_block_forward", lib().cbb_conv_block_forward(
         ctypes.byref(desc), _ptr(x, name="x"), _ptr(w, name="w"), _ptr(bias, name="bias"),
@@ -203,6 +247,8 @@ def conv_block_forward(desc: ConvDesc, x, w, bias, gamma, beta, mean, var, x_nor
 
 def conv_act_bn_backward(desc: ConvDesc, y, x_norm, var, gamma, delta, dz, db, dgamma,
                          workspace=None, stream=None) -> None:
+    _conv_sizes("conv_act_bn_backward", desc, y=y, x_norm=x_norm, var=var, gamma=gamma,
+                delta=delta, dz=dz, db=db, dgamma=dgamma)
     wsp, wsb = _ws(workspace)
     _check("cbb_conv_act_bn_backward", lib().cbb_conv_act_bn_backward(
         ctypes.byref(desc), _ptr(y, name="y"), _ptr(x_norm, name="x_norm"), _ptr(var, name="var"),
@@ -211,6 +257,7 @@ def conv_act_bn_backward(desc: ConvDesc, y, x_norm, var, gamma, delta, dz, db, d
 
 
 def conv_backward_weights(desc: ConvDesc, x, dz, dw, workspace=None, stream=None) -> None:
+    _conv_sizes("conv_backward_weights", desc, x=x, dz=dz, dw=dw)
     wsp, wsb = _ws(workspace)
     _check("cbb_conv_backward_weights", lib().cbb_conv_backward_weights(
         ctypes.byref(desc), _ptr(x, name="x"), _ptr(dz, name="dz"), _ptr(dw, name="dw"), wsp, wsb,
@@ -219,6 +266,7 @@ def conv_backward_weights(desc: ConvDesc, x, dz, dw, workspace=None, stream=None
 
 def conv_backward_data(desc: ConvDesc, w, dz, dx, dx_accumulate: bool = False, workspace=None,
                        stream=None) -> None:
+    _conv_sizes("conv_backward_data", desc, w=w, dz=dz, dx=dx)
     wsp, wsb = _ws(workspace)
     _check("cbb_conv_backward_data", lib().cbb_conv_backward_data(
         ctypes.byref(desc), _ptr(w, name="w"), _ptr(dz, name="dz"), _ptr(dx, name="dx"),
@@ -227,6 +275,7 @@ def conv_backward_data(desc: ConvDesc, w, dz, dx, dx_accumulate: bool = False, w
 
 def conv_backward_weights_data(desc: ConvDesc, x, w, dz, dw, dx=None, dx_accumulate: bool = False,
                                workspace=None, stream=None) -> None:
+    _conv_sizes("conv_backward_weights_data", desc, x=x, w=w, dz=dz, dw=dw, dx=dx)
     wsp, wsb = _ws(workspace)
     _check("cbb_conv_backward_weights_data", lib().cbb_conv_backward_weights_data(
         ctypes.byref(desc), _ptr(x, name="x"), _ptr(w, name="w"), _ptr(dz, name="dz"),
@@ -267,6 +316,8 @@ def bn_backward(g, x_norm, var, gamma, dz, dgamma, dbeta, eps: float = 1e-5, wor
                 stream=None) -> None:
     n, c = g.shape[0], g.shape[1]
     hw = g.numel() // (n * c)
+    _sized("bn_backward", x_norm=(x_norm, g.numel()), dz=(dz, g.numel()), var=(var, c),
+           gamma=(gamma, c), dgamma=(dgamma, c), dbeta=(dbeta, c))
     wsp, wsb = _ws(workspace)
     _check("cbb_bn_backward", lib().cbb_bn_backward(
         n, c, hw, eps, _ptr(g, name="g"), _ptr(x_norm, name="x_norm"), _ptr(var, name="var"),
@@ -278,6 +329,8 @@ def bn_backward_fixed(g, x_norm, var, gamma, dz, dgamma, dbeta, eps: float = 1e-
                 stream=None) -> None:
     n, c = g.shape[0], g.shape[1]
     hw = g.numel() // (n * c)
+    _sized("bn_backward_fixed", x_norm=(x_norm, g.numel()), dz=(dz, g.numel()), var=(var, c),
+           gamma=(gamma, c), dgamma=(dgamma, c), dbeta=(dbeta, c))
     wsp, wsb = _ws(workspace)
     _check("cbb_bn_backward_fixed", lib().cbb_bn_backward_fixed(
         n, c, hw, eps, _ptr(g, name="g"), _ptr(x_norm, name="x_norm"), _ptr(var, name="var"),
@@ -288,6 +341,8 @@ def bn_backward_fixed(g, x_norm, var, gamma, dz, dgamma, dbeta, eps: float = 1e-
 def fc_backward(x, w, delta, dw, db, dx, dx_accumulate: bool = False, stream=None) -> None:
     batch, in_dim = x.shape
     out_dim = w.shape[0]
+    _sized("fc_backward", w=(w, (out_dim, in_dim)), delta=(delta, batch * out_dim),
+           dw=(dw, out_dim * in_dim), db=(db, out_dim), dx=(dx, batch * in_dim))
     _check("cbb_fc_backward", lib().cbb_fc_backward(
         batch, in_dim, out_dim, _ptr(x, name="x"), _ptr(w, name="w"), _ptr(delta, name="delta"),
         _ptr(dw, name="dw"), _ptr(db, name="db"), _ptr(dx, name="dx"), int(dx_accumulate),
@@ -297,6 +352,8 @@ def fc_backward(x, w, delta, dw, db, dx, dx_accumulate: bool = False, stream=Non
 def softmax_loss_backward(prob, labels, dlogits, loss_weight: float = 1.0, bad_labels=None,
                           stream=None) -> None:
     batch, classes = prob.shape
+    _sized("softmax_loss_backward", labels=(labels, batch), dlogits=(dlogits, batch * classes),
+           bad_labels=(bad_labels, 1))
     _check("cbb_softmax_loss_backward", lib().cbb_softmax_loss_backward(
         batch, classes, _ptr(prob, name="prob"), _ptr(labels, torch.int32, "labels"), loss_weight,
         _ptr(dlogits, name="dlogits"), _ptr(bad_labels, torch.int32, "bad_labels"),
@@ -307,6 +364,10 @@ def fc_softmax_backward(prob, labels, x, w, dlogits, dw, db, dx, loss_weight: fl
                         bad_labels=None, stream=None) -> None:
     batch, classes = prob.shape
     in_dim = x.shape[1]
+    _sized("fc_softmax_backward", labels=(labels, batch), x=(x, batch * in_dim),
+           w=(w, classes * in_dim), dlogits=(dlogits, batch * classes),
+           dw=(dw, classes * in_dim), db=(db, classes), dx=(dx, batch * in_dim),
+           bad_labels=(bad_labels, 1))
     _check("cbb_fc_softmax_backward", lib().cbb_fc_softmax_backward(
         batch, in_dim, classes, _ptr(prob, name="prob"), _ptr(labels, torch.int32, "labels"),
         loss_weight, _ptr(x, name="x"), _ptr(w, name="w"), _ptr(dlogits, name="dlogits"),
@@ -351,6 +412,9 @@ def shortcut_backward_resize(delta, d_main, d_from, alpha: float = 1.0, beta: fl
 
 def route_backward(delta, d_ins: Sequence[torch.Tensor], stream=None) -> None:
     batch = delta.shape[0]
+    if any(t.numel() % batch for t in d_ins):
+        raise ValueError("route_backward: every input must hold `batch` images")
+    _sized("route_backward", delta=(delta, sum(t.numel() for t in d_ins)))
     sizes = (ctypes.c_int64 * len(d_ins))(*[t.numel() // batch for t in d_ins])
     ptrs = (ctypes.c_void_p * len(d_ins))(*[_ptr(t, name="d_in").value for t in d_ins])
     _check("cbb_route_backward", lib().cbb_route_backward(
@@ -373,3 +437,27 @@ def maxpool_backward(idx, delta, dx, ksize: int = 2, stride: int = 2, stream=Non
     _check("cbb_maxpool_backward", lib().cbb_maxpool_backward(
         n, c, ih, iw, ksize, stride, _ptr(idx, torch.int32, "idx"), _ptr(delta, name="delta"),
         _ptr(dx, name="dx"), _stream(stream)))
+
+
+def get_device_error(stream=None) -> int:
+    """Wait for the stream, then read and clear the GPU's error word (CBB_DEVERR_* bits
+    raised by kernels since the previous read; 0 when none)."""
+    code = ctypes.c_int(0)
+    _check("cbb_get_device_error", lib().cbb_get_device_error(_stream(stream), ctypes.byref(code)))
+    return code.value
+
+
+_hook_ref = None  # keeps the ctypes callback alive while the library holds it
+
+
+def set_launch_hook(fn) -> None:
+    """fn(kernel_name: str, stream_handle: int) after each kernel the library enqueues;
+    None removes the hook.  Process-wide (tracing and per-kernel event timing)."""
+    global _hook_ref
+    if fn is None:
+        _check("cbb_set_launch_hook", lib().cbb_set_launch_hook(None, None))
+        _hook_ref = None
+        return
+    cb = LAUNCH_HOOK(lambda user, name, st: fn(name.decode(), st or 0))
+    _check("cbb_set_launch_hook", lib().cbb_set_launch_hook(ctypes.cast(cb, ctypes.c_void_p), None))
+    _hook_ref = cb

@@ -518,22 +518,28 @@ static void launch_actbn_t(const SegGeom& s, unsigned blocks, int act, const flo
     // one streaming pass (dz written in it, or formed later from coef)
     actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(
         s, delta, y, xr, slope, act, var, gamma, eps, coef || !write_dz ? nullptr : dz, part);
-    if (coef)
+    note_launch("actbn_reduce", st);
+    if (coef) {
       actbn_coef<<<(unsigned)s.C, kThreads, 0, st>>>(part, s.nseg, s.M, s.C, BN, var, gamma,
                                                     eps, dgamma, dbeta_or_db, coef);
-    else
+      note_launch("actbn_coef", st);
+    } else {
       actbn_fold<<<(unsigned)s.C, kThreads, 0, st>>>(part, s.nseg,
                                                     BN == kBnNone ? nullptr : dgamma,
                                                     dbeta_or_db);
+      note_launch("actbn_fold", st);
+    }
     return;
   }
   // batch statistics: dz needs the channel's sums, so the data is streamed twice
   if constexpr (BN == kBnBatch) {
     actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xr, slope, act, var,
                                                             gamma, eps, nullptr, part);
+    note_launch("actbn_reduce", st);
     actbn_apply<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, slope, act, part, var,
                                                            gamma, eps, dz, dgamma, dbeta_or_db,
                                                            write_dz);
+    note_launch("actbn_apply", st);
   }
 }
 
@@ -593,7 +599,7 @@ int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, c
   else
     launch_actbn_v<false>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma,
                           dbeta_or_db, part, write_dz, coef, st);
-  return check_launch("actbn_reduce/actbn_apply");
+  return check_error("actbn_reduce/actbn_apply");
 }
 
 // Forward after the convolution (see bnf_apply).  bn: 0 none (z + bias already in y),
@@ -611,7 +617,9 @@ int launch_bn_act_forward(int N, int C, int64_t HW, int bn, float eps, int act, 
       bnf_stats<true><<<blocks, kThreads, 0, st>>>(s, xn, mp);
     else
       bnf_stats<false><<<blocks, kThreads, 0, st>>>(s, xn, mp);
+    note_launch("bnf_stats", st);
     bnf_stats_fold<<<(unsigned)C, 64, 0, st>>>(s, mp, mean, var);
+    note_launch("bnf_stats_fold", st);
   }
   if (bn) {
     if (vec)
@@ -628,7 +636,8 @@ int launch_bn_act_forward(int N, int C, int64_t HW, int bn, float eps, int act, 
       bnf_apply<false, false><<<blocks, kThreads, 0, st>>>(s, y, y, nullptr, nullptr, nullptr,
                                                             nullptr, eps, act, slope);
   }
-  return check_launch("bnf_stats/bnf_stats_fold/bnf_apply");
+  if (bn || act != CBB_ACT_LINEAR) note_launch("bnf_apply", st);
+  return check_error("bnf_stats/bnf_stats_fold/bnf_apply");
 }
 
 int launch_act_backward(int act, float slope, const float* y, const float* delta, float* g,
@@ -640,7 +649,7 @@ int launch_act_backward(int act, float slope, const float* y, const float* delta
     const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(count, kThreads), 8192));
     act_backward_scalar<<<(unsigned)blocks, kThreads, 0, st>>>(act, slope, y, delta, g, count);
   }
-  return check_launch("act_backward_kernel");
+  return check_launch("act_backward_kernel", st);
 }
 
 }  // namespace cbb

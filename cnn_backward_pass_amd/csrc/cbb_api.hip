@@ -6,25 +6,6 @@
 
 #include "cbb_internal.h"
 
-namespace cbb {
-
-static thread_local char g_err[512] = "";
-
-void set_hip_error(hipError_t e, const char* where) {
-  snprintf(g_err, sizeof g_err, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
-}
-
-int check_launch(const char* where) {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    set_hip_error(e, where);
-    return CBB_EHIP;
-  }
-  return CBB_OK;
-}
-
-}  // namespace cbb
-
 using namespace cbb;
 
 namespace {
@@ -97,7 +78,7 @@ extern "C" {
 
 int cbb_abi_version(void) { return CBB_ABI_VERSION; }
 
-const char* cbb_last_error(void) { return g_err; }
+const char* cbb_last_error(void) { return last_error_text(); }
 
 const char* cbb_status_string(int status) {
   switch (status) {
@@ -106,7 +87,7 @@ const char* cbb_status_string(int status) {
     case CBB_ESHAPE: return "inconsistent or empty shape";
     case CBB_EUNSUPPORTED: return "unsupported configuration";
     case CBB_EWORKSPACE: return "workspace missing or too small";
-    case CBB_EHIP: return g_err[0] ? g_err : "HIP error";
+    case CBB_EHIP: return last_error_text()[0] ? last_error_text() : "HIP error";
   }
   return "unknown status";
 }
@@ -120,13 +101,17 @@ int cbb_conv_block_workspace_size(const cbb_conv_desc* desc, size_t* bytes) {
   return CBB_OK;
 }
 
-int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const float* w,
-                            const float* y, const float* x_norm, const float* var,
-                            const float* gamma, const float* delta, float* dz, float* dw,
-                            float* db, float* dgamma, float* dx, int dx_accumulate,
-                            void* workspace, size_t workspace_bytes, void* stream) {
-  ConvPlan p;
-  int rc = check_desc(desc, &p);
+}  // extern "C"
+
+namespace cbb {
+
+// The argument rules of cbb_conv_block_backward other than the workspace's.
+int check_block_backward(const cbb_conv_desc* desc, const float* x, const float* w,
+                         const float* y, const float* x_norm, const float* var,
+                         const float* gamma, const float* delta, const float* dz,
+                         const float* dw, const float* db, const float* dgamma, const float* dx,
+                         int dx_accumulate) {
+  const int rc = check_desc(desc, nullptr);
   if (rc) return rc;
   const int bn = desc->batch_normalize, act = desc->act;
   if (!x || !w || !delta || !dw || !db) return CBB_EINVAL;
@@ -134,15 +119,35 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
   if (bn && (!x_norm || !var || !gamma || !dgamma)) return CBB_EINVAL;
   if (!bn && (x_norm || var || gamma || dgamma)) return CBB_EINVAL;
   const bool passthrough = act == CBB_ACT_LINEAR && !bn;  // dz is delta itself
-  const ConvGeom g = make_geom(*desc);
   // dz = NULL: not stored; the fused dW + dX kernel forms it as it stages delta
-  const bool form_dz = !passthrough && !dz;
-  if (form_dz) {
+  if (!passthrough && !dz) {
     auto a16 = [](const void* q) { return !q || (uintptr_t)q % 16 == 0; };
-    if (!dx || !conv_fused_dwdx_ok(g) || !a16(x) || !a16(delta) || !a16(y) || !a16(x_norm))
+    if (!dx || !conv_fused_dwdx_ok(make_geom(*desc)) || !a16(x) || !a16(delta) || !a16(y) ||
+        !a16(x_norm))
       return CBB_EINVAL;
   }
   if (dx_accumulate != 0 && dx_accumulate != 1) return CBB_EINVAL;
+  return CBB_OK;
+}
+
+}  // namespace cbb
+
+extern "C" {
+
+int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const float* w,
+                            const float* y, const float* x_norm, const float* var,
+                            const float* gamma, const float* delta, float* dz, float* dw,
+                            float* db, float* dgamma, float* dx, int dx_accumulate,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  ConvPlan p;
+  int rc = check_block_backward(desc, x, w, y, x_norm, var, gamma, delta, dz, dw, db, dgamma, dx,
+                                dx_accumulate);
+  if (rc) return rc;
+  check_desc(desc, &p);
+  const int bn = desc->batch_normalize, act = desc->act;
+  const bool passthrough = act == CBB_ACT_LINEAR && !bn;  // dz is delta itself
+  const ConvGeom g = make_geom(*desc);
+  const bool form_dz = !passthrough && !dz;
   if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return CBB_EWORKSPACE;
   if (workspace && ((uintptr_t)workspace % kAlign)) return CBB_EWORKSPACE;
 

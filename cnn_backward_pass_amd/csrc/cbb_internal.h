@@ -37,7 +37,23 @@ struct ConvGeom {
 
 // Host-side launch bookkeeping -------------------------------------------------
 void set_hip_error(hipError_t e, const char* where);
-int check_launch(const char* where);  // CBB_OK or CBB_EHIP after a launch
+const char* last_error_text();
+// After a kernel is enqueued: note_launch calls the launch hook (cbb_set_launch_hook)
+// with the kernel's name; check_error records a pending HIP error; check_launch does
+// both (CBB_OK or CBB_EHIP).
+void note_launch(const char* kernel, hipStream_t st);
+int check_error(const char* where);
+int check_launch(const char* where, hipStream_t st);
+// The argument rules of cbb_conv_block_backward other than the workspace's
+// (CBB_OK or the status the call returns), checked before any HIP call.
+int check_block_backward(const cbb_conv_desc* desc, const float* x, const float* w,
+                         const float* y, const float* x_norm, const float* var,
+                         const float* gamma, const float* delta, const float* dz,
+                         const float* dw, const float* db, const float* dgamma, const float* dx,
+                         int dx_accumulate);
+// This device's error word (CBB_DEVERR_* bits, read by cbb_get_device_error), or
+// nullptr with the HIP error recorded.
+int32_t* device_error_word();
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -1929,7 +1929,7 @@ int launch_conv_fused_dwdx(const ConvGeom& g, const float* x, const float* wt, c
     case 2: launch_first_rows<2>(g, p, x, wt, dz, ws, dx, accumulate, src, st); break;
     default: launch_first_rows<3>(g, p, x, wt, dz, ws, dx, accumulate, src, st); break;
   }
-  const int rc = check_launch("conv_first_rows");
+  const int rc = check_launch("conv_first_rows", st);
   if (rc) return rc;
   return launch_dw_reduce(g, dw, ws, p.wgs, p.groups, 0, st);
 }
@@ -2030,7 +2030,7 @@ int launch_conv_dw_forming_dz(const ConvGeom& g, const float* x, const float* de
     launch_dw3_rows<1>(g, p, x, delta, out, direct, st, &src, dzout);
   else
     launch_dw3_rows<2>(g, p, x, delta, out, direct, st, &src, dzout);
-  const int rc = check_launch("conv_dw3_rows (dz formed)");
+  const int rc = check_launch("conv_dw3_rows (dz formed)", st);
   if (rc != CBB_OK || direct) return rc;
   return launch_dw_reduce(g, dw, ws, p.splits, p.groups, 1, st);
 }
@@ -2061,7 +2061,7 @@ static int launch_conv_dw_plain(const ConvGeom& g, const float* x, const float* 
     case DW_64x128: launch_dw_tile<TileShape<2, 2, 1, 1, 1, 2>>(g, p, x, dz, out, direct, st); break;
     default: launch_dw_tile<TileShape<2, 2, 1, 1, 2, 2>>(g, p, x, dz, out, direct, st); break;
   }
-  int rc = check_launch(p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel");
+  int rc = check_launch(p.rows_tc > 0 ? "conv_dw3_rows" : "conv_dw_kernel", st);
   if (rc != CBB_OK || direct) return rc;
   return launch_dw_reduce(g, dw, ws, p.splits, p.groups, p.rows_tc > 0, st);
 }
@@ -2085,15 +2085,15 @@ int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int gr
   if (groups == 0) {
     dw_reduce_l2<<<dim3(eblocks, 1, g.G), kThreads, 0, st>>>(dw, ws, splits, mn, kk, g.OC, g.C,
                                                                region);
-    return check_launch("dw_reduce_l2");
+    return check_launch("dw_reduce_l2", st);
   }
   float* part2 = ws + (int64_t)splits * mn;
   dw_reduce_l1<<<dim3(eblocks, groups, g.G), kThreads, 0, st>>>(ws, part2, splits, mn, region);
-  const int rc = check_launch("dw_reduce_l1");
+  const int rc = check_launch("dw_reduce_l1", st);
   if (rc) return rc;
   dw_reduce_l2<<<dim3(eblocks, 1, g.G), kThreads, 0, st>>>(dw, part2, groups, mn, kk, g.OC, g.C,
                                                              region);
-  return check_launch("dw_reduce_l2");
+  return check_launch("dw_reduce_l2", st);
 }
 
 // ----------------------------------------------------------------------------- dX planning
@@ -2237,12 +2237,12 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
     else
       launch_dx_mfma<TileShape<2, 2, 1>>(s, p, wt, dz, dx, p.ksplits > 1 ? ws : nullptr,
                                          accumulate, st);
-    const int rc = check_launch("conv_dx_kernel");
+    const int rc = check_launch("conv_dx_kernel", st);
     if (rc || p.ksplits == 1) return rc;
     const int64_t n = (int64_t)g.N * g.C * g.HW;
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
     dx_splitk_reduce<<<blocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
-    return check_launch("dx_splitk_reduce");
+    return check_launch("dx_splitk_reduce", st);
   }
   const DxPlan p = plan_dx(g);
   if (p.kind == DX_D3S1 || p.kind == DX_D3S1_SMALL || p.kind == DX_D3S2) {
@@ -2270,7 +2270,7 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
       else
         conv_dx3_s2p<8><<<grid, kThreads, 0, st>>>(g, wt, dz, dx, accumulate, ntiles, p.pixtiles,
                                                    tiles_w);
-      return check_launch("conv_dx3_s2p");
+      return check_launch("conv_dx3_s2p", st);
     }
     if (p.kind == DX_D3S1) {
       if (z4) {
@@ -2292,18 +2292,18 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
       }
     }
 #undef CBB_DX3
-    int rc = check_launch("conv_dx3_direct");
+    int rc = check_launch("conv_dx3_direct", st);
     if (rc || p.ksplits == 1) return rc;
     const int64_t n = (int64_t)g.N * g.C * g.HW;
     const unsigned rblocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
     dx_splitk_reduce<<<rblocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
-    return check_launch("dx_splitk_reduce");
+    return check_launch("dx_splitk_reduce", st);
   }
   if (p.kind == DX_1X1) {
     if (conv1x1_dma_ok(g, wt, dz)) return launch_conv1x1_dx(g, wt, dz, dx, accumulate, st);
     // misaligned tensors: the general kernel on 64 x 64 tiles, no split
     launch_dx_mfma<TileShape<2, 2, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
-    return check_launch("conv_dx_kernel");
+    return check_launch("conv_dx_kernel", st);
   }
   if (p.kind == DX_SMALLC) {
     switch (g.C) {
@@ -2312,18 +2312,18 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
       case 3: launch_smallc<3>(g, wt, dz, dx, accumulate, st); break;
       default: launch_smallc<4>(g, wt, dz, dx, accumulate, st); break;
     }
-    return check_launch("conv_dx_smallc_kernel");
+    return check_launch("conv_dx_smallc_kernel", st);
   }
   if (p.kind == DX_32x128)
     launch_dx_mfma<TileShape<1, 4, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
   else
     launch_dx_mfma<TileShape<2, 2, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
-  int rc = check_launch("conv_dx_kernel");
+  int rc = check_launch("conv_dx_kernel", st);
   if (rc || p.ksplits == 1) return rc;
   const int64_t n = (int64_t)g.N * g.C * g.HW;
   const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
   dx_splitk_reduce<<<blocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
-  return check_launch("dx_splitk_reduce");
+  return check_launch("dx_splitk_reduce", st);
 }
 
 }  // namespace cbb

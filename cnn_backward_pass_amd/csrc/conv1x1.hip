@@ -401,7 +401,7 @@ int launch_conv1x1_dw(const ConvGeom& g, const float* x, const float* dz, float*
   const unsigned blocks = (unsigned)((int64_t)p.mtiles * p.ntiles * p.splits);
   conv1x1_dw_dma<kC1DwStages><<<blocks, kC1DwThreads, 0, st>>>(g, x, dz, out, p.k_chunk,
                                                                p.mtiles, p.ntiles, direct);
-  const int rc = check_launch("conv1x1_dw_dma");
+  const int rc = check_launch("conv1x1_dw_dma", st);
   if (rc != CBB_OK || direct) return rc;
   return launch_dw_reduce(g, dw, ws, p.splits, p.groups, 0, st);
 }
@@ -412,7 +412,7 @@ int launch_conv1x1_dx(const ConvGeom& g, const float* wt, const float* dz, float
   const unsigned blocks = (unsigned)(mtiles * ceil_div(g.Q, kC1T));
   conv1x1_dx_dma<kC1T, kC1T, kC1DxStages><<<blocks, kThreads, 0, st>>>(g, wt, dz, dx, mtiles,
                                                                       accumulate);
-  return check_launch("conv1x1_dx_dma");
+  return check_launch("conv1x1_dx_dma", st);
 }
 
 }  // namespace cbb

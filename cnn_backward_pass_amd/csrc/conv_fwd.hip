@@ -270,7 +270,7 @@ int launch_conv_forward(const ConvGeom& g, const float* x, const float* wt, cons
     const int64_t n = (int64_t)g.OC * g.C * g.K * g.K;
     flip_transpose_weights<<<(unsigned)std::min<int64_t>(ceil_div(n, kThreads), 4096), kThreads, 0,
                              st>>>(wt, wflip, g.OC, g.C, g.K);
-    const int rc = check_launch("flip_transpose_weights");
+    const int rc = check_launch("flip_transpose_weights", st);
     if (rc) return rc;
     return launch_conv_dx(t, wflip, x, z, 0, ws2, st);
   }
@@ -278,7 +278,7 @@ int launch_conv_forward(const ConvGeom& g, const float* x, const float* wt, cons
     const int64_t tiles = ceil_div(g.Q, 32);
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(tiles, 4), 8192);
     conv_fwd_smallj<<<blocks, kThreads, 0, st>>>(g, x, wt, bias, z, tiles);
-    return check_launch("conv_fwd_smallj");
+    return check_launch("conv_fwd_smallj", st);
   }
   ConvGeom s = g;
   s.C = g.C / g.G;
@@ -297,7 +297,7 @@ int launch_conv_forward(const ConvGeom& g, const float* x, const float* wt, cons
     const dim3 grid((unsigned)(tm * ceil_div(g.Q, TS::BN)), (unsigned)g.G);
     conv_fwd_kernel<TS><<<grid, kThreads, 0, st>>>(s, x, wt, bias, z, tm, dkk, dk);
   }
-  return check_launch("conv_fwd_kernel");
+  return check_launch("conv_fwd_kernel", st);
 }
 
 }  // namespace cbb

@@ -246,10 +246,10 @@ int launch_depthwise_dw(const ConvGeom& g, const float* x, const float* dz, floa
       CBB_DWL(1) CBB_DWL(2) CBB_DWL(3) CBB_DWL(4) CBB_DWL(5) CBB_DWL(6) CBB_DWL(7)
     }
 #undef CBB_DWL
-    const int rc = check_launch("dwise_dw_lds");
+    const int rc = check_launch("dwise_dw_lds", st);
     if (rc) return rc;
     dwise_dw_fold<<<(unsigned)g.C, 64, 0, st>>>(ws, nseg2, g.K * g.K, dw);
-    return check_launch("dwise_dw_fold");
+    return check_launch("dwise_dw_fold", st);
   }
   const DwiseSeg s = dwise_plan(g);
   const unsigned blocks = (unsigned)((int64_t)g.C * s.nseg);
@@ -261,10 +261,10 @@ int launch_depthwise_dw(const ConvGeom& g, const float* x, const float* dz, floa
     CBB_DWW(1) CBB_DWW(2) CBB_DWW(3) CBB_DWW(4) CBB_DWW(5) CBB_DWW(6) CBB_DWW(7)
   }
 #undef CBB_DWW
-  const int rc = check_launch("dwise_dw_partial");
+  const int rc = check_launch("dwise_dw_partial", st);
   if (rc) return rc;
   dwise_dw_fold<<<(unsigned)g.C, 64, 0, st>>>(ws, s.nseg, g.K * g.K, dw);
-  return check_launch("dwise_dw_fold");
+  return check_launch("dwise_dw_fold", st);
 }
 
 int launch_depthwise_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx,
@@ -280,7 +280,7 @@ int launch_depthwise_dx(const ConvGeom& g, const float* wt, const float* dz, flo
       CBB_DXL(1) CBB_DXL(2) CBB_DXL(3) CBB_DXL(4) CBB_DXL(5) CBB_DXL(6) CBB_DXL(7)
     }
 #undef CBB_DXL
-    return check_launch("dwise_dx_lds");
+    return check_launch("dwise_dx_lds", st);
   }
   const int64_t total = (int64_t)g.N * g.C * g.HW;
   const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(total, kThreads), 16384);
@@ -292,7 +292,7 @@ int launch_depthwise_dx(const ConvGeom& g, const float* wt, const float* dz, flo
     CBB_DWX(1) CBB_DWX(2) CBB_DWX(3) CBB_DWX(4) CBB_DWX(5) CBB_DWX(6) CBB_DWX(7)
   }
 #undef CBB_DWX
-  return check_launch("dwise_dx");
+  return check_launch("dwise_dx", st);
 }
 
 }  // namespace cbb

@@ -81,12 +81,12 @@ int launch_shortcut_resize(int batch, int w1, int h1, int c1, int w2, int h2, in
   if (d_main) {
     const int64_t n1 = (int64_t)batch * c1 * h1 * w1;
     axpy_kernel<<<grid_for(n1), kThreads, 0, st>>>(n1, alpha, delta, d_main);
-    const int rc = check_launch("axpy_kernel");
+    const int rc = check_launch("axpy_kernel", st);
     if (rc) return rc;
   }
   shortcut_resize_kernel<<<grid_for((int64_t)batch * minc * minh * minw), kThreads, 0, st>>>(
       batch, w1, h1, c1, w2, h2, c2, stride, sample, minw, minh, minc, beta, delta, d_from);
-  return check_launch("shortcut_resize_kernel");
+  return check_launch("shortcut_resize_kernel", st);
 }
 
 // ------------------------------------------------------------- softmax
@@ -144,12 +144,12 @@ int launch_softmax_backward(int outer, int channels, int64_t inner, const float*
   if (inner == 1) {
     softmax_bwd_rows<<<(unsigned)ceil_div(outer, kThreads / 64), kThreads, 0, st>>>(outer, channels,
                                                                                  y, dy, dx);
-    return check_launch("softmax_bwd_rows");
+    return check_launch("softmax_bwd_rows", st);
   }
   const int64_t ktiles = ceil_div(inner, kSmK);
   softmax_bwd_strided<<<(unsigned)(outer * ktiles), kThreads, 0, st>>>(outer, channels, inner,
                                                                        ktiles, y, dy, dx);
-  return check_launch("softmax_bwd_strided");
+  return check_launch("softmax_bwd_strided", st);
 }
 
 int launch_shortcut(int64_t count, float alpha, float beta, const float* delta, float* d_main,
@@ -157,7 +157,7 @@ int launch_shortcut(int64_t count, float alpha, float beta, const float* delta, 
   const int vec = aligned16(delta) && aligned16(d_main) && aligned16(d_from);
   shortcut_kernel<<<grid_for(vec ? ceil_div(count, 4) : count), kThreads, 0, st>>>(
       count, alpha, beta, delta, d_main, d_from, vec);
-  return check_launch("shortcut_kernel");
+  return check_launch("shortcut_kernel", st);
 }
 
 // --------------------------------------------------------------- route
@@ -199,7 +199,7 @@ int launch_route(int batch, int n_in, const int64_t* sizes, const float* delta,
     const int64_t work = (int64_t)batch * (vec ? sizes[t] / 4 : sizes[t]);
     route_kernel<<<grid_for(work), kThreads, 0, st>>>(batch, sizes[t], outputs, offset, delta,
                                                       d_in[t], vec);
-    const int rc = check_launch("route_kernel");
+    const int rc = check_launch("route_kernel", st);
     if (rc) return rc;
     offset += sizes[t];
   }
@@ -232,7 +232,7 @@ int launch_upsample(int n, int c, int h, int w, int scale, const float* delta, f
   const int64_t planes = (int64_t)n * c;
   upsample_bwd_kernel<<<grid_for(planes * h * w), kThreads, 0, st>>>(planes, h, w, scale, delta,
                                                                      dx);
-  return check_launch("upsample_bwd_kernel");
+  return check_launch("upsample_bwd_kernel", st);
 }
 
 // --------------------------------------------------------------- max pool
@@ -270,13 +270,14 @@ int launch_maxpool(int n, int c, int ih, int iw, int k, int s, const int32_t* id
   const int64_t planes = (int64_t)n * c;
   maxpool_bwd_kernel<<<grid_for(planes * ih * iw), kThreads, 0, st>>>(planes, ih, iw, oh, ow, k,
                                                                       s, idx, delta, dx);
-  return check_launch("maxpool_bwd_kernel");
+  return check_launch("maxpool_bwd_kernel", st);
 }
 
 // --------------------------------------------------------------- softmax loss
 __global__ __launch_bounds__(kThreads) void softmax_loss_bwd_kernel(
     int batch, int classes, const float* __restrict__ prob, const int32_t* __restrict__ labels,
-    float scale, float* __restrict__ dlogits, int32_t* __restrict__ bad) {
+    float scale, float* __restrict__ dlogits, int32_t* __restrict__ bad,
+    int32_t* __restrict__ dev_err) {
   const int64_t total = (int64_t)batch * classes;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += stride) {
@@ -286,15 +287,20 @@ __global__ __launch_bounds__(kThreads) void softmax_loss_bwd_kernel(
     float p = prob[i];
     if (valid && j == lab) p -= 1.f;
     dlogits[i] = p * scale;
-    if (!valid && j == 0 && bad) atomicAdd(bad, 1);
+    if (!valid && j == 0) {
+      if (bad) atomicAdd(bad, 1);
+      atomicOr(dev_err, CBB_DEVERR_LABEL);
+    }
   }
 }
 
 int launch_softmax_loss(int batch, int classes, const float* prob, const int32_t* labels,
                         float loss_weight, float* dlogits, int32_t* bad, hipStream_t st) {
+  int32_t* dev_err = device_error_word();
+  if (!dev_err) return CBB_EHIP;
   softmax_loss_bwd_kernel<<<grid_for((int64_t)batch * classes), kThreads, 0, st>>>(
-      batch, classes, prob, labels, loss_weight / (float)batch, dlogits, bad);
-  return check_launch("softmax_loss_bwd_kernel");
+      batch, classes, prob, labels, loss_weight / (float)batch, dlogits, bad, dev_err);
+  return check_launch("softmax_loss_bwd_kernel", st);
 }
 
 // --------------------------------------------------------------- inner product
@@ -396,7 +402,7 @@ static int launch_gemm(const GemmArgs& a, hipStream_t st) {
     const int tiles = (int)ceil_div(a.M, 64) * tiles_n;
     strided_gemm_kernel<TS><<<tiles, kThreads, 0, st>>>(a, tiles_n);
   }
-  return check_launch("strided_gemm_kernel");
+  return check_launch("strided_gemm_kernel", st);
 }
 
 // db[o] += sum over the batch of delta[b][o], batch rows in order.
@@ -428,7 +434,7 @@ int launch_fc(int batch, int in_dim, int out_dim, const float* x, const float* w
   if (db) {
     fc_bias_kernel<<<(unsigned)ceil_div(out_dim, kThreads), kThreads, 0, st>>>(batch, out_dim,
                                                                                delta, db);
-    rc = check_launch("fc_bias_kernel");
+    rc = check_launch("fc_bias_kernel", st);
     if (rc) return rc;
   }
   if (dx) {

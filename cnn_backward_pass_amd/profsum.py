@@ -117,9 +117,11 @@ def write_traffic(a) -> None:
     write = _stage_kib(a.write, "WRITE_SIZE", a.stage)
     f_bytes = sum(v for _, v in fetch.values()) * 1024.0 * f_scale / a.reps
     w_bytes = sum(v for _, v in write.values()) * 1024.0 * w_scale / a.reps
+    per_kernel = {k: (fetch.get(k, (0, 0.0))[1] * f_scale + write.get(k, (0, 0.0))[1] * w_scale)
+                  * 1024.0 / a.reps for k in sorted(set(fetch) | set(write))}
     rec = {"stage": a.stage, "reps": a.reps, "fetch_bytes": f_bytes, "write_bytes": w_bytes,
            "traffic_bytes": f_bytes + w_bytes, "fetch_scale": f_scale, "write_scale": w_scale,
-           "sources": sources_digest()}
+           "kernels": per_kernel, "sources": sources_digest()}
     lines = [f"# HBM traffic of {a.stage} (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
              "Commands (from the repository root, one MI355X), one counter per run:", "", "```"]
     lines += a.cmd
@@ -152,6 +154,28 @@ def load_traffic(stage: str, profiles_dir: str | None = None):
                     rec = json.loads(line[len(TRAFFIC_TAG):])
                     if rec.get("stage") == stage and rec.get("sources") == cur:
                         return rec
+    return None
+
+
+def load_kernel_traffic(workload: str, layer: int, kernel: str, profiles_dir: str | None = None):
+    """HBM bytes of one launch of ``kernel`` (a launch-hook name such as "conv_dx3_s2p" or
+    "conv_dw3_rows (dz formed)") in a stage of conv layer ``layer`` of ``workload``, from a
+    traffic record whose source digest matches the current sources; else None."""
+    d = profiles_dir or os.path.join(ROOT, "profiles")
+    cur = sources_digest()
+    base = kernel.split(" ")[0]
+    for p in sorted(glob.glob(os.path.join(d, "*.md"))):
+        with open(p) as f:
+            for line in f:
+                if not line.startswith(TRAFFIC_TAG):
+                    continue
+                rec = json.loads(line[len(TRAFFIC_TAG):])
+                if rec.get("sources") != cur or not str(rec.get("stage", "")).startswith(
+                        f"{workload}.{layer}."):
+                    continue
+                hits = [v for k, v in rec.get("kernels", {}).items() if k.split("<")[0] == base]
+                if len(hits) == 1:
+                    return hits[0]
     return None
 
 

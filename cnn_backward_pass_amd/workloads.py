@@ -40,6 +40,7 @@ class Runner:
     def __init__(self, name: str, inputs: dict, saved: dict, device: str = "cuda"):
         self.name = name
         self._probe = None
+        self._ctx = None
         self.wl = synth.WORKLOADS[name]
         self.device = device
         self.inp = inputs
@@ -135,6 +136,7 @@ class Runner:
 
     def _conv(self, li: int, delta, dx, dx_accumulate: bool, stream) -> None:
         e = self.convs[li]
+        self._ctx = self.wl.convs[li].name
         probe = self._probe
         form_dz = e["form_dz"] and dx is not None
         if probe is None or probe[0] != li or form_dz:
@@ -239,31 +241,46 @@ class Runner:
         e = self.convs[li]
         return delta if e["dz"] is None else e["dz"]
 
-    def step(self, stream=None, probe=None) -> None:
+    def step(self, stream=None, probe=None, hook=None) -> None:
         """Enqueue one backward pass.  ``probe = (layer, stage, mark)`` runs that conv layer
-        stage by stage and calls ``mark(is_target_stage, before)`` around each stage."""
+        stage by stage and calls ``mark(is_target_stage, before)`` around each stage.
+        ``hook(call, kernel)`` is called right after each kernel the library enqueues
+        (cbb_set_launch_hook), with ``call`` the step's current call: a conv layer's name
+        or the other layer's ("ip2+loss", "relu", "ip1", "pool2", "pool1", "shortcut",
+        "route", "upsample")."""
         self._probe = probe
+        self._ctx = None
+        if hook is not None:
+            cbb.set_launch_hook(lambda kernel, st: hook(self._ctx, kernel))
         try:
             self._step(stream)
         finally:
             self._probe = None
+            if hook is not None:
+                cbb.set_launch_hook(None)
 
     def _step(self, stream) -> None:
         name = self.name
         if name == "lenet":
+            self._ctx = "ip2+loss"
             cbb.fc_softmax_backward(self.prob, self.labels, self.relu_y, self.fc_w[1],
                                     self.dlogits, self.fc_dw[1], self.fc_db[1], self.d_relu,
                                     1.0, self.bad_labels, stream)
+            self._ctx = "relu"
             cbb.act_backward("relu", 0.0, self.relu_y, self.d_relu, self.g_relu, stream)
+            self._ctx = "ip1"
             cbb.fc_backward(self.pool2_out, self.fc_w[0], self.g_relu, self.fc_dw[0],
                             self.fc_db[0], self.d_pool2.view(self.batch, -1), False, stream)
+            self._ctx = "pool2"
             cbb.maxpool_backward(self.idx[1], self.d_pool2, self.d_c2, 2, 2, stream)
             self._conv(1, self.d_c2, self.d_in[1], False, stream)
+            self._ctx = "pool1"
             cbb.maxpool_backward(self.idx[0], self.d_in[1], self.d_c1, 2, 2, stream)
             self._conv(0, self.d_c1, None, False, stream)
             return
         if name == "darknet53_residual":
             # shortcut: delta to the last conv's output (alpha) and to the block input (beta)
+            self._ctx = "shortcut"
             cbb.shortcut_backward(self.delta, self.d_main, self.d_in[0], 1.0, 1.0, stream)
             self._conv(1, self.d_main, self.d_in[1], False, stream)
             self._conv(0, self.d_in[1], self.d_in[0], True, stream)
@@ -273,7 +290,9 @@ class Runner:
             self._conv(li, d, self.d_in[li], False, stream)
             d = self.d_in[li]
         if name == "yolov3_head":
+            self._ctx = "route"
             cbb.route_backward(self.d_in[0], [self.d_route_a, self.d_up], stream)
+            self._ctx = "upsample"
             cbb.upsample_backward(self.d_up, self.d_up_src, 2, stream)
 
     # ------------------------------------------------------------------ results

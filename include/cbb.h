@@ -119,6 +119,25 @@ int cbb_abi_version(void);
 const char* cbb_status_string(int status);
 const char* cbb_last_error(void);
 
+/* Device-side failure detection.  Host checks cover every argument error (the
+ * asserts / CHECKs of the pages become status codes); a condition only the data
+ * reveals is raised by the kernel that meets it as a bit in a per-GPU error word:
+ *   CBB_DEVERR_LABEL  a softmax-loss label outside [0, classes) ([P2] layer 9).
+ * cbb_get_device_error waits for `stream` (a host synchronisation, unlike every
+ * other call), stores in *code the OR of the bits raised on the current GPU since
+ * the previous query (0: none), and clears the word.  Kernels of other streams
+ * still running on that GPU may raise bits after the read.  CBB_EINVAL when code
+ * is NULL; CBB_EHIP when the wait or the read fails. */
+#define CBB_DEVERR_LABEL 1
+int cbb_get_device_error(void* stream, int* code);
+
+/* Tracing: fn(user, kernel, stream) is called on the calling thread right after
+ * each kernel the library enqueues (kernel = its name, stream = the hipStream_t
+ * it went to), e.g. to record a HIP event after it.  Process-wide; NULL removes
+ * the hook.  A hook must not call back into the library.  Always CBB_OK. */
+typedef void (*cbb_launch_hook)(void* user, const char* kernel, void* stream);
+int cbb_set_launch_hook(cbb_launch_hook fn, void* user);
+
 /* ----------------------------------------------------------------------------
  * Conv block backward: backward_convolutional_layer of [P1] section 3.1 with
  * backward_batchnorm_layer of [P1] section 4:
@@ -161,8 +180,11 @@ const char* cbb_last_error(void);
  *                         bytes, 256-byte aligned; contents on entry ignored.
  * Supported: 1 <= ksize <= 7, 1 <= stride <= 4, 0 <= pad <= dilation (ksize - 1),
  * all sizes whose element counts fit in int32 per tensor index and int64 overall.
- * Grouped or dilated layers run the general implicit-GEMM kernels, one launch
- * per group; the specialised kernels cover groups = dilation = 1.
+ * Grouped or dilated layers run all groups in one launch (the group index on
+ * the grid's y axis): the general implicit-GEMM kernels, except that grouped
+ * undilated 3x3 pad-1 layers with in_c/groups a multiple of 32 and
+ * out_c/groups a multiple of 64 take the row-streaming 3x3 weight-gradient
+ * kernel, and depthwise layers (groups = in_c = out_c) take streaming kernels.
  * ------------------------------------------------------------------------- */
 int cbb_conv_block_workspace_size(const cbb_conv_desc* desc, size_t* bytes);
 int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const float* w,
@@ -278,8 +300,11 @@ int cbb_fc_backward(int batch, int in_dim, int out_dim, const float* x, const fl
  * sample's label, times loss_weight / batch (one label per sample, so the
  * normalised count and the outer count are both `batch`).  prob, dlogits
  * [batch, classes]; labels int32 [batch].  A label outside [0, classes)
- * leaves its row without the -1 and adds 1 to *bad_labels (device int32,
- * may be NULL); the caller reads it when it wants to know. */
+ * leaves its row without the -1, adds 1 to *bad_labels (device int32, may be
+ * NULL; a count the caller reads when it wants to) and raises
+ * CBB_DEVERR_LABEL in the GPU's error word (cbb_get_device_error).  The
+ * pages store labels as floats and cast them to int ([P2] layer 9), so a bad
+ * value is a property of the data that only the kernel sees. */
 int cbb_softmax_loss_backward(int batch, int classes, const float* prob, const int32_t* labels,
                               float loss_weight, float* dlogits, int32_t* bad_labels,
                               void* stream);

@@ -57,6 +57,7 @@ _i, _l, _d = ctypes.c_int, ctypes.c_long, ctypes.c_double
 _SIGS = {
     "orc_version": ([], _i),
     "orc_num_threads": ([], _i),
+    "orc_set_threads": ([_i], None),
     "orc_act_forward": ([_i, _d, _D, _D, _l], None),
     "orc_act_backward": ([_i, _d, _D, _D, _D, _l], None),
     "orc_bn_forward": ([_i, _i, _l, _d, _D, _D, _D, _D, _D, _D, _D], None),
@@ -122,6 +123,11 @@ def _pi(a: np.ndarray):
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use (omp_get_max_threads)."""
     return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> None:
+    """Threads of the oracle's following OpenMP loops (1: single core)."""
+    lib().orc_set_threads(int(n))
 
 
 def conv_out_dim(size: int, k: int, s: int, p: int) -> int:

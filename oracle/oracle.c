@@ -53,8 +53,11 @@ int orc_version(void) { return 1; }
 #ifdef _OPENMP
 #include <omp.h>
 int orc_num_threads(void) { return omp_get_max_threads(); }
+/* threads of the following parallel loops (timing the oracle on one core) */
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
 #else
 int orc_num_threads(void) { return 1; }
+void orc_set_threads(int n) { (void)n; }
 #endif
 
 /* ------------------------------------------------------------------ */

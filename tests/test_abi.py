@@ -224,3 +224,55 @@ def test_binding_refuses_host_tensors():
     t = torch.zeros(4)
     with pytest.raises(ValueError):
         cbb.act_backward("leaky", 0.1, t, t, t)
+
+
+def test_device_error_and_hook_validate():
+    """cbb_get_device_error rejects a NULL result pointer before touching the GPU; the
+    launch hook is set and removed on the host."""
+    L = cbb.lib()
+    assert L.cbb_get_device_error(None, None) == -1
+    calls = []
+    cbb.set_launch_hook(lambda name, st: calls.append(name))
+    cbb.set_launch_hook(None)
+    assert calls == []          # nothing was launched
+    assert cbb.DEVERR_LABEL == 1
+
+
+def test_binding_checks_sizes_against_the_descriptor():
+    """The binding compares every tensor with the sizes its call implies before any
+    pointer reaches the library: an undersized tensor would be read or written out of
+    bounds by the kernels."""
+    torch = pytest.importorskip("torch")
+    d = cbb.conv_desc(2, 3, 8, 8, 4, 3, 1, 1, 1, "leaky")
+    z = lambda *s: torch.zeros(*s)
+    ok = dict(x=z(2, 3, 8, 8), w=z(4, 3, 3, 3), y=z(2, 4, 8, 8), x_norm=z(2, 4, 8, 8),
+              var=z(4), gamma=z(4), delta=z(2, 4, 8, 8), dz=z(2, 4, 8, 8), dw=z(4, 3, 3, 3),
+              db=z(4), dgamma=z(4), dx=z(2, 3, 8, 8))
+    for name, bad in (("dx", z(2, 3, 8, 7)), ("dx", z(2 * 3 * 8 * 8 - 1)), ("delta", z(1, 4, 8, 8)),
+                      ("w", z(4, 3, 3, 2)), ("var", z(3)), ("dgamma", z(5)), ("x", z(2, 3, 8))):
+        kw = dict(ok, **{name: bad})
+        with pytest.raises(ValueError, match=name):
+            cbb.conv_block_backward(d, **kw)
+    with pytest.raises(ValueError, match="dw"):
+        cbb.conv_backward_weights(d, ok["x"], ok["dz"], z(4, 3, 3, 3 - 1))
+    with pytest.raises(ValueError, match="dx"):
+        cbb.conv_backward_data(d, ok["w"], ok["dz"], z(2, 3, 4, 8))
+    with pytest.raises(ValueError, match="y"):
+        cbb.conv_block_forward(d, ok["x"], ok["w"], None, z(4), z(4), z(4), z(4), z(2, 4, 8, 8),
+                               z(2, 4, 8, 9))
+    # inner product, batch norm, softmax loss, route
+    with pytest.raises(ValueError, match="dw"):
+        cbb.fc_backward(z(4, 8), z(5, 8), z(4, 5), z(5, 7), z(5), z(4, 8))
+    with pytest.raises(ValueError, match="dx"):
+        cbb.fc_backward(z(4, 8), z(5, 8), z(4, 5), z(5, 8), z(5), z(4, 7))
+    with pytest.raises(ValueError, match="dz"):
+        cbb.bn_backward(z(2, 4, 16), z(2, 4, 16), z(4), z(4), z(2, 4, 15), z(4), z(4))
+    with pytest.raises(ValueError, match="gamma"):
+        cbb.bn_backward_fixed(z(2, 4, 16), z(2, 4, 16), z(4), z(3), z(2, 4, 16), z(4), z(4))
+    with pytest.raises(ValueError, match="labels"):
+        cbb.softmax_loss_backward(z(4, 10), torch.zeros(3, dtype=torch.int32), z(4, 10))
+    with pytest.raises(ValueError, match="dlogits"):
+        cbb.fc_softmax_backward(z(4, 10), torch.zeros(4, dtype=torch.int32), z(4, 8), z(10, 8),
+                                z(4, 9), z(10, 8), z(10), None)
+    with pytest.raises(ValueError, match="delta"):
+        cbb.route_backward(z(2, 7, 4, 4), [z(2, 4, 4, 4), z(2, 2, 4, 4)])

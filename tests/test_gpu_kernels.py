@@ -206,7 +206,11 @@ GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (8, 64, 52, 52, 64, 3, 1, 1, True, "leaky", 64, 1),     # depthwise, many segments per channel
     (2, 16, 12, 12, 32, 3, 1, 1, True, "leaky", 16, 1),     # two filters per channel (general)
     (2, 64, 10, 52, 128, 3, 1, 1, True, "leaky", 2, 1),     # grouped dW on the row-streaming kernel
-    (2, 64, 12, 104, 128, 3, 2, 1, False, "relu", 2, 1),    # the same at stride 2, split rows
+    (2, 64, 40, 104, 128, 3, 2, 1, False, "relu", 2, 1),    # the same at stride 2, 5 row runs
+    # grouped row-streaming dW with more than 32 splits per group: the two-level
+    # ordered reduction (dw_reduce_l1 / l2) on tap-major partials, stride 1 and 2
+    (4, 64, 64, 104, 128, 3, 1, 1, True, "leaky", 2, 1),
+    (4, 64, 64, 208, 128, 3, 2, 1, False, "relu", 2, 1),
     (1, 4, 96, 96, 4, 3, 1, 1, True, "leaky", 4, 1),        # depthwise, plane beyond LDS: streaming
     (2, 8, 90, 91, 8, 5, 2, 2, False, "relu", 8, 1),        # depthwise, 8190-pixel plane in LDS, s2
 ]
@@ -214,8 +218,10 @@ GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
 
 @pytest.mark.parametrize("case", GD_CASES)
 def test_grouped_dilated_conv_block(case):
-    """Grouped and dilated layers (general kernels, one launch per group) against the
-    oracle's grouped / dilated loops; overwrite, then accumulate in place."""
+    """Grouped and dilated layers (all groups in one launch: the general kernels, the
+    row-streaming 3x3 dW kernel for grouped 3x3 layers with 32k input and 64k output
+    channels per group, streaming kernels for depthwise layers) against the oracle's
+    grouped / dilated loops; overwrite, then accumulate in place."""
     torch = require_gpu()
     announce(f"grouped/dilated conv_block {case}")
     ref, got = run_conv(torch, case, seed=300 + GD_CASES.index(case))
@@ -650,15 +656,19 @@ def test_fc_and_softmax_loss():
     labels = r.integers(0, 10, size=64).astype(np.int32)
     dl = torch.empty(64, 10, device="cuda")
     bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cbb.get_device_error()   # start from a clear error word
     cbb.softmax_loss_backward(_t(torch, prob), _t(torch, labels, torch.int32), dl, 1.0, bad)
     torch.cuda.synchronize()
     assert_close("dlogits", dl.cpu().double().numpy(), O.softmax_loss_backward(prob, labels), tol=1e-6)
     assert int(bad.item()) == 0
-    # out-of-range labels: row keeps prob * scale, counted once per bad sample
+    assert cbb.get_device_error() == 0
+    # out-of-range labels: row keeps prob * scale, counted once per bad sample, and the
+    # GPU's error word carries the label bit until it is read
     lab2 = labels.copy()
     lab2[[3, 9]] = [10, -1]
     cbb.softmax_loss_backward(_t(torch, prob), _t(torch, lab2, torch.int32), dl, 1.0, bad)
-    torch.cuda.synchronize()
+    assert cbb.get_device_error() == cbb.DEVERR_LABEL
+    assert cbb.get_device_error() == 0
     got = dl.cpu().double().numpy()
     assert int(bad.item()) == 2
     np.testing.assert_allclose(got[3], prob[3].astype(np.float64) / 64, rtol=1e-6)
@@ -666,3 +676,33 @@ def test_fc_and_softmax_loss():
     ok[[3, 9]] = False
     assert_close("dlogits valid rows", got[ok], O.softmax_loss_backward(prob[ok], labels[ok]) * ok.sum() / 64,
                  tol=1e-6)
+
+
+def test_launch_hook_names_each_kernel():
+    """The tracing hook sees every kernel of a call, in launch order, on the call's stream
+    (act/BN reduction and the per-channel map, then the gradient kernels)."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    announce("launch hook")
+    d = cbb.conv_desc(2, 8, 12, 12, 16, 3, 1, 1, 1, "leaky")
+    g = torch.Generator(device="cuda").manual_seed(5)
+    rn = lambda *s: torch.randn(*s, device="cuda", generator=g)
+    x, w, y, xn, dl = rn(2, 8, 12, 12), rn(16, 8, 3, 3), rn(2, 16, 12, 12), rn(2, 16, 12, 12), rn(2, 16, 12, 12)
+    var, gam = torch.rand(16, device="cuda") + 0.5, torch.ones(16, device="cuda")
+    dz, dw, db, dg, dx = (torch.empty_like(dl), torch.zeros_like(w), torch.zeros(16, device="cuda"),
+                          torch.zeros(16, device="cuda"), torch.empty_like(x))
+    ws = cbb.workspace(cbb.conv_block_workspace_size(d))
+    seen = []
+    stream = torch.cuda.current_stream()
+    cbb.set_launch_hook(lambda name, st: seen.append((name, st)))
+    try:
+        cbb.conv_block_backward(d, x, w, y, xn, var, gam, dl, dz, dw, db, dg, dx, False, ws)
+    finally:
+        cbb.set_launch_hook(None)
+    torch.cuda.synchronize()
+    names = [n for n, _ in seen]
+    assert names[:2] == ["actbn_reduce", "actbn_apply"], names
+    assert len(names) >= 4 and all(st == stream.cuda_stream for _, st in seen)
+    cbb.conv_block_backward(d, x, w, y, xn, var, gam, dl, dz, dw, db, dg, dx, False, ws)
+    torch.cuda.synchronize()
+    assert len(seen) == len(names)   # removed: no more calls
