@@ -21,7 +21,8 @@ ACT = {"linear": 0, "leaky": 1, "logistic": 2, "relu": 3, "tanh": 4, "elu": 5, "
        "lhtan": 8, "hardtan": 9, "stair": 10, "ramp": 11, "relie": 12, "loggy": 13}
 BN_NONE, BN_BATCH, BN_FIXED = 0, 1, 2
 STATUS = {0: "CBB_OK", -1: "CBB_EINVAL", -2: "CBB_ESHAPE", -3: "CBB_EUNSUPPORTED",
-          -4: "CBB_EWORKSPACE", -5: "CBB_EHIP"}
+          -4: "CBB_EWORKSPACE", -5: "CBB_EHIP", -6: "CBB_ESCRATCH"}
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 WORKSPACE_ALIGN = 256
 
 
@@ -67,6 +68,7 @@ _SIGS = {
     "cbb_last_error": ([], ctypes.c_char_p),
     "cbb_conv_block_workspace_size": ([ctypes.POINTER(ConvDesc), ctypes.POINTER(_sz)], _i32),
     "cbb_conv_block_backward": ([ctypes.POINTER(ConvDesc)] + [_P] * 12 + [_i32, _P, _sz, _P], _i32),
+    "cbb_conv_block_backward_noalloc": ([ctypes.POINTER(ConvDesc)] + [_P] * 12 + [_i32, _P], _i32),
     "cbb_conv_act_bn_backward": ([ctypes.POINTER(ConvDesc)] + [_P] * 8 + [_P, _sz, _P], _i32),
     "cbb_conv_backward_weights": ([ctypes.POINTER(ConvDesc), _P, _P, _P, _P, _sz, _P], _i32),
     "cbb_conv_backward_data": ([ctypes.POINTER(ConvDesc), _P, _P, _P, _i32, _P, _sz, _P], _i32),
@@ -224,6 +226,19 @@ def conv_block_backward(desc: ConvDesc, x, w, y, x_norm, var, gamma, delta, dz, 
         _ptr(delta, name="delta"), _ptr(dz, name="dz"), _ptr(dw, name="dw"),
         _ptr(db, name="db"), _ptr(dgamma, name="dgamma"), _ptr(dx, name="dx"),
         int(dx_accumulate), wsp, wsb, _stream(stream)))
+
+
+def conv_block_backward_noalloc(desc: ConvDesc, x, w, y, x_norm, var, gamma, delta, dz, dw, db,
+                                dgamma, dx, dx_accumulate: bool = False, stream=None) -> None:
+    """conv_block_backward with the library's static scratch buffer (no workspace)."""
+    _conv_sizes("conv_block_backward_noalloc", desc, x=x, w=w, y=y, x_norm=x_norm, var=var,
+                gamma=gamma, delta=delta, dz=dz, dw=dw, db=db, dgamma=dgamma, dx=dx)
+    _check("cbb_conv_block_backward_noalloc", lib().cbb_conv_block_backward_noalloc(
+        ctypes.byref(desc), _ptr(x, name="x"), _ptr(w, name="w"), _ptr(y, name="y"),
+        _ptr(x_norm, name="x_norm"), _ptr(var, name="var"), _ptr(gamma, name="gamma"),
+        _ptr(delta, name="delta"), _ptr(dz, name="dz"), _ptr(dw, name="dw"),
+        _ptr(db, name="db"), _ptr(dgamma, name="dgamma"), _ptr(dx, name="dx"),
+        int(dx_accumulate), _stream(stream)))
 
 
 def conv_block_forward_workspace_size(desc: ConvDesc) -> int:

@@ -88,6 +88,9 @@ const char* cbb_status_string(int status) {
     case CBB_EUNSUPPORTED: return "unsupported configuration";
     case CBB_EWORKSPACE: return "workspace missing or too small";
     case CBB_EHIP: return last_error_text()[0] ? last_error_text() : "HIP error";
+    case CBB_ESCRATCH:
+      return "the call needs more scratch than the static buffer of "
+             "cbb_conv_block_backward_noalloc holds (CBB_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -54,7 +54,8 @@ typedef enum cbb_status {
   CBB_ESHAPE = -2,        /* geometry yields an empty or inconsistent output          */
   CBB_EUNSUPPORTED = -3,  /* valid but not implemented (e.g. ksize > 7, scale > 8)     */
   CBB_EWORKSPACE = -4,    /* workspace NULL or smaller than the reported size         */
-  CBB_EHIP = -5           /* a HIP launch failed; cbb_last_error() has its text       */
+  CBB_EHIP = -5,          /* a HIP launch failed; cbb_last_error() has its text       */
+  CBB_ESCRATCH = -6       /* needs more scratch than CBB_NOALLOC_SCRATCH_BYTES        */
 } cbb_status;
 
 /* Activation whose gradient is taken, read from the activation OUTPUT y as
@@ -192,6 +193,27 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
                             const float* gamma, const float* delta, float* dz, float* dw,
                             float* db, float* dgamma, float* dx, int dx_accumulate,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------------------------------------
+ * The conv block backward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * cbb_conv_block_backward with the same arguments, results and errors, except that
+ * its scratch memory is a static device buffer of CBB_NOALLOC_SCRATCH_BYTES that
+ * the library owns (one per GPU, held from the library's load until the process
+ * ends) instead of a workspace argument.  It allocates nothing and calls no
+ * allocating routine.  The first call on a GPU looks up that GPU's buffer.
+ * CBB_ESCRATCH, before any HIP call, when cbb_conv_block_workspace_size exceeds
+ * the buffer (64 MiB holds every layer of the five workloads the library is
+ * measured on).  Every call on a GPU shares that GPU's buffer, so calls that
+ * overlap on one GPU (several streams or host threads) race: serialise them.
+ * The buffer keeps whatever the last call left; no call relies on its contents.
+ * ------------------------------------------------------------------------- */
+#define CBB_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+int cbb_conv_block_backward_noalloc(const cbb_conv_desc* desc, const float* x, const float* w,
+                                    const float* y, const float* x_norm, const float* var,
+                                    const float* gamma, const float* delta, float* dz, float* dw,
+                                    float* db, float* dgamma, float* dx, int dx_accumulate,
+                                    void* stream);
 
 /* ----------------------------------------------------------------------------
  * Conv block forward: the tensors the backward reads, computed on the device

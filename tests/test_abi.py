@@ -276,3 +276,23 @@ def test_binding_checks_sizes_against_the_descriptor():
                                 z(4, 9), z(10, 8), z(10), None)
     with pytest.raises(ValueError, match="delta"):
         cbb.route_backward(z(2, 7, 4, 4), [z(2, 4, 4, 4), z(2, 2, 4, 4)])
+
+
+def test_noalloc_entry_point_validates_on_the_host():
+    """The no-allocation variant rejects, before any HIP call, a layer whose scratch
+    would not fit its static buffer (CBB_ESCRATCH) and every argument error of the
+    workspace entry point."""
+    L = cbb.lib()
+    big = _desc(batch=16, in_c=256, in_h=26, in_w=26, out_c=512)
+    _, need = ws_size(big)
+    assert need > cbb.NOALLOC_SCRATCH_BYTES
+    names = ["x", "w", "y", "x_norm", "var", "gamma", "delta", "dz", "dw", "db", "dgamma", "dx"]
+    call = lambda d, **kw: L.cbb_conv_block_backward_noalloc(
+        ctypes.byref(d), *[kw.get(k, BOGUS) for k in names], kw.get("acc", 0), None)
+    assert call(big) == -6
+    assert "static buffer" in cbb.status_string(-6)
+    d = _desc(in_c=5)
+    for missing in ("x", "w", "delta", "dw", "db", "x_norm", "gamma"):
+        assert call(d, **{missing: None}) == -1
+    assert call(d, acc=2) == -1
+    assert call(_desc(batch=0)) == -1
