@@ -191,7 +191,7 @@ class Calib:
         self.lib.calib_mfma_f32.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
                                             ctypes.c_void_p]
         self.lib.calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
-                                        ctypes.c_void_p]
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         self.torch = torch
         self.blocks = 1024            # 4 work-groups of 4 waves per CU: every SIMD busy
         self.out = torch.empty(self.blocks * 256, dtype=torch.float32, device=dev)
@@ -206,9 +206,9 @@ class Calib:
             raise RuntimeError("calib_mfma_f32 failed")
         return float(self.blocks) * 4 * iters * 4 * (32 * 32 * 2 * 2)   # FLOPs
 
-    def copy(self, src, dst):
+    def copy(self, src, dst, blocks=0, unroll=1):
         rc = self.lib.calib_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
-                                 src.numel() * src.element_size(), self._stream())
+                                 src.numel() * src.element_size(), blocks, unroll, self._stream())
         if rc:
             raise RuntimeError("calib_copy failed")
 
@@ -227,19 +227,27 @@ def calibrate(calib, torch, dev, reps=5):
             torch.cuda.synchronize()
             ms.append(a.elapsed_time(b))
         return min(ms)
-    iters = 20000
-    flops = calib.mfma(iters)
-    t_mfma = best(lambda: calib.mfma(iters))
+    # short (~1 ms) and long (~10 ms) loops: the clock a sustained matrix load holds
+    mfma = {}
+    for iters in (2000, 20000):
+        flops = calib.mfma(iters)
+        mfma[iters] = flops / (best(lambda: calib.mfma(iters)) * 1e-3) / 1e12
     n = (1 << 30) // 4
     src = torch.ones(n, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
-    t_copy = best(lambda: calib.copy(src, dst))
+    copy = {}
+    for blocks, unroll in ((0, 1), (8192, 1), (8192, 2), (4096, 4), (16384, 2)):
+        t = best(lambda: calib.copy(src, dst, blocks, unroll))
+        copy[f"{blocks or 'one-pass'}x{unroll}"] = 2.0 * (1 << 30) / (t * 1e-3) / 1e9
     del src, dst
-    return {"mfma_f32_TFLOPs": round(flops / (t_mfma * 1e-3) / 1e12, 2),
-            "copy_GBps": round(2.0 * (1 << 30) / (t_copy * 1e-3) / 1e9, 1),
-            "mfma_probe": f"{calib.blocks} work-groups x 4 waves, {iters} rounds of 4 independent "
-                          "v_mfma_f32_32x32x2_f32 chains from registers",
-            "copy_probe": "1 GiB device-to-device copy, 16 B per lane (bytes read + written)",
+    return {"mfma_f32_TFLOPs": round(max(mfma.values()), 2),
+            "copy_GBps": round(max(copy.values()), 1),
+            "mfma_by_iters": {str(k): round(v, 2) for k, v in mfma.items()},
+            "copy_by_variant": {k: round(v, 1) for k, v in copy.items()},
+            "mfma_probe": f"{calib.blocks} work-groups x 4 waves, rounds of 4 independent "
+                          "v_mfma_f32_32x32x2_f32 chains from registers (best variant)",
+            "copy_probe": "1 GiB device-to-device copy, non-temporal 16 B pieces (bytes read + "
+                          "written; best of grid x pieces-in-flight variants)",
             "published": {"mfma_f32_TFLOPs": PEAK_MFMA_F32 / 1e12, "hbm_GBps": PEAK_HBM / 1e9}}
 
 
@@ -537,7 +545,7 @@ def main():
     # Every kernel of the step timed in place, before the timed region; the dominant
     # kernel is the longest single gradient kernel (dW, dX or fused dW + dX, including
     # a dW kernel that forms dz), without its act/BN passes and split reductions.
-    kern = time_kernels(runners, torch, lambda: calib.mfma(20000))
+    kern = time_kernels(runners, torch, lambda: calib.mfma(20000))   # ~10 ms blocker
     grads = [k for k in kern if kernel_role(k[4]) is not None]
     dom_ms, dom_name, dom_i, dom_call, dom_kernel = grads[0]
     print(f"[bench] dominant kernel {dom_name}.{dom_call}.{dom_kernel} (#{dom_i}) "

@@ -5,8 +5,11 @@
     python -m cnn_backward_pass_amd.profsum traffic --stage yolov3_stem.1.dW --reps 3 \\
         --fetch F.db --write W.db --copy-fetch CF.db --copy-write CW.db --copy-bytes N \\
         --out profiles/Y.md --cmd "..." [--cmd "..."]
+    python -m cnn_backward_pass_amd.profsum mfma --stage yolov3_stem.1.dX --db M.db \\
+        --out profiles/Z.md --cmd "..."
 
-``trace`` tabulates per-kernel durations of a ``--kernel-trace`` run.  ``traffic``
+``trace`` tabulates per-kernel durations of a ``--kernel-trace`` run.  ``mfma``
+tabulates one ``--pmc`` run of the matrix-core counters per kernel.  ``traffic``
 turns two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of ``bench.py --stage``
 into HBM bytes per launch of that stage, each counter scaled by what it reads for
 a plain device copy of known size (``bench.py --copy-bytes``).  The traffic file
@@ -143,6 +146,60 @@ def write_traffic(a) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
+                 "SQ_BUSY_CU_CYCLES")
+
+
+def dispatch_counters(db: str):
+    """{dispatch_id: (kernel name, {counter: [values of its rows]})} of a --pmc run."""
+    con = sqlite3.connect(db)
+    cols = [d[1] for d in con.execute("pragma table_info(counters_collection)")]
+    idx = {c: i for i, c in enumerate(cols)}
+    out = {}
+    for r in con.execute("select * from counters_collection"):
+        d = out.setdefault(r[idx["dispatch_id"]], (r[idx["kernel_name"]], {}))
+        d[1].setdefault(r[idx["counter_name"]], []).append(r[idx["value"]])
+    return out
+
+
+def mfma_rows(db: str, simds: int):
+    """Per kernel of the profiled stage: dispatches, fp32 matrix FLOPs per launch
+    (SQ_INSTS_VALU_MFMA_MOPS_F32 x 512, summed over the rows of a dispatch) and the
+    matrix-core busy share SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), the
+    MfmaUtil formula of rocprofv3's derived counters."""
+    kinds = collections.defaultdict(lambda: [0, 0.0, 0.0, 0.0])
+    for name, vals in dispatch_counters(db).values():
+        if "cbb::" not in name or not all(c in vals for c in MFMA_COUNTERS[:3]):
+            continue
+        k = kinds[_short(name)]
+        gui = max(vals["GRBM_GUI_ACTIVE"])
+        k[0] += 1
+        k[1] += sum(vals["SQ_INSTS_VALU_MFMA_MOPS_F32"]) * 512.0
+        k[2] += sum(vals["SQ_VALU_MFMA_BUSY_CYCLES"]) / max(gui * simds, 1.0)
+        k[3] += gui
+    return {k: {"dispatches": v[0], "mfma_flops": v[1] / v[0], "mfma_busy": v[2] / v[0],
+                "gui_active_cycles": v[3] / v[0]} for k, v in kinds.items()}
+
+
+def write_mfma(a) -> None:
+    rows = mfma_rows(a.db, a.simds)
+    rec = {"stage": a.stage, "simds": a.simds, "kernels": rows, "sources": sources_digest()}
+    lines = [f"# Matrix-core counters of {a.stage} (rocprofv3 --pmc)", "",
+             "Command (from the repository root, one MI355X):", "", "```", a.cmd, "```", "",
+             f"Per kernel: fp32 matrix FLOPs per launch counted by the hardware "
+             f"(SQ_INSTS_VALU_MFMA_MOPS_F32 x 512) and the matrix-core busy share "
+             f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {a.simds} SIMDs).", "",
+             "| kernel | dispatches | MFMA GFLOP / launch | matrix cores busy | GUI active cycles |",
+             "|---|---|---|---|---|"]
+    for k in sorted(rows, key=lambda k: -rows[k]["mfma_flops"]):
+        r = rows[k]
+        lines.append(f"| `{k}` | {r['dispatches']} | {r['mfma_flops'] / 1e9:.3f} | "
+                     f"{r['mfma_busy'] * 100:.1f}% | {r['gui_active_cycles']:.0f} |")
+    lines += ["", "mfma-json: " + json.dumps(rec)]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def load_traffic(stage: str, profiles_dir: str | None = None):
     """Traffic record for ``stage`` whose source digest matches the current sources, else None."""
     d = profiles_dir or os.path.join(ROOT, "profiles")
@@ -194,9 +251,17 @@ def main(argv=None) -> None:
         r.add_argument(f"--{k}", required=True)
     r.add_argument("--copy-bytes", type=int, required=True)
     r.add_argument("--cmd", action="append", required=True)
+    m = sub.add_parser("mfma")
+    m.add_argument("--stage", required=True)
+    m.add_argument("--db", required=True)
+    m.add_argument("--out", required=True)
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--simds", type=int, default=1024, help="SIMDs on the GPU (256 CUs x 4)")
     a = ap.parse_args(argv)
     if a.cmd_name == "trace":
         write_trace(a.db, a.out, a.title, a.cmd)
+    elif a.cmd_name == "mfma":
+        write_mfma(a)
     else:
         write_traffic(a)
 

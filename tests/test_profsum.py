@@ -44,3 +44,22 @@ def test_traffic_scaling_and_gate(tmp_path):
     assert profsum.load_traffic("wl.1.dW", str(tmp_path)) is None
     line = [l for l in text.splitlines() if l.startswith(profsum.TRAFFIC_TAG)][0]
     assert json.loads(line[len(profsum.TRAFFIC_TAG):])["stage"] == "wl.1.dW"
+
+
+def test_mfma_rows_per_kernel(tmp_path):
+    """Matrix FLOPs sum over a dispatch's rows (x 512); the busy share divides the summed
+    busy cycles by the largest GRBM_GUI_ACTIVE row times the SIMD count."""
+    k = "void cbb::conv_dx3_s2p<4>(int)"
+    db = tmp_path / "m.db"
+    _db(db, [(1, k, "SQ_INSTS_VALU_MFMA_MOPS_F32", 1000.0), (1, k, "SQ_INSTS_VALU_MFMA_MOPS_F32", 1000.0),
+             (1, k, "SQ_VALU_MFMA_BUSY_CYCLES", 4000.0), (1, k, "GRBM_GUI_ACTIVE", 10.0),
+             (1, k, "GRBM_GUI_ACTIVE", 8.0),
+             (2, k, "SQ_INSTS_VALU_MFMA_MOPS_F32", 3000.0), (2, k, "SQ_VALU_MFMA_BUSY_CYCLES", 2000.0),
+             (2, k, "GRBM_GUI_ACTIVE", 10.0),
+             (3, "at::native::fill", "SQ_INSTS_VALU_MFMA_MOPS_F32", 7.0)])
+    rows = profsum.mfma_rows(str(db), simds=1000)
+    assert list(rows) == ["conv_dx3_s2p<4>"]
+    r = rows["conv_dx3_s2p<4>"]
+    assert r["dispatches"] == 2
+    assert r["mfma_flops"] == (2000.0 + 3000.0) * 512 / 2
+    assert abs(r["mfma_busy"] - (0.4 + 0.2) / 2) < 1e-12
