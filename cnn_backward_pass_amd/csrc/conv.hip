@@ -267,10 +267,15 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int oh = wave & 1, kh = (wave >> 1) % 3, kq = wave / 6;
   const int cblocks = g.C >> 5, nblk = (g.OC >> 6) * cblocks;
-  const int split = blockIdx.x / nblk, blk = blockIdx.x - split * nblk;
+  // XCD-aware order: consecutive logical indices run on one XCD (one L2), and they
+  // go (o, i) block first, then strip: the blocks that stage the same input and dz
+  // rows, and the strips whose row pieces share cache lines, hit one L2.
+  const int bid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int blk = bid % nblk, t0 = bid / nblk;
+  const int strip = t0 % strips, t1 = t0 / strips;
+  const int rc = t1 % rchunks, n = t1 / rchunks;
+  const int split = (n * rchunks + rc) * strips + strip;
   const int ob = blk / cblocks, cb = blk - ob * cblocks;
-  const int rc = split % rchunks, ns = split / rchunks;
-  const int strip = ns % strips, n = ns / strips;
   const int r0 = rc * rlen, r1 = min(g.OH, r0 + rlen);  // non-empty by construction
   const int oc0 = strip * TC;       // first output column of the strip
   const int ic0 = oc0 * S - 1;      // input column held in LDS column 0
@@ -740,9 +745,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, khalf = lane >> 5;
   const int ctiles = (g.C + C::BMC - 1) / C::BMC;
-  const int ctile = blockIdx.x % ctiles;
-  const int split = (blockIdx.x / ctiles) % ksplits;
-  const int t = blockIdx.x / (ctiles * ksplits);
+  // XCD-aware order: the channel tiles and K splits of one pixel tile, which copy
+  // the same dz tile, and then the neighbouring pixel tiles run on one XCD (one L2)
+  const int bid = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int ctile = bid % ctiles;
+  const int split = (bid / ctiles) % ksplits;
+  const int t = bid / (ctiles * ksplits);
   const int b = t / tiles_per_img, tt = t - b * tiles_per_img;
   const int i0 = ctile * C::BMC;
 
@@ -1438,8 +1446,9 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
   __shared__ float Z0[64];   // zeros: masked operands read here (no branches around reads)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int run = blockIdx.x % nruns, strip = (blockIdx.x / nruns) % nstrips;
-  const int n = blockIdx.x / (nruns * nstrips);
+  const int bid = blockIdx.x;
+  const int run = bid % nruns, strip = (bid / nruns) % nstrips;
+  const int n = bid / (nruns * nstrips);
   const int w0 = strip * sw, r0 = run * rlen, r1 = min(g.H, r0 + rlen);
   // dz rows hA .. hE are walked (row H, past the image, reads as zeros and
   // completes dx row H-1); the count is rounded up to even, and the extra row
@@ -1680,7 +1689,7 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
   for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = adw[r];
   __syncthreads();
   if (wave == 0) {
-    float* dst = dwpart + (int64_t)blockIdx.x * g.OC * g.J;
+    float* dst = dwpart + (int64_t)bid * g.OC * g.J;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float v = (red[r * 64 + lane] + red[(16 + r) * 64 + lane]) +

@@ -395,7 +395,13 @@ def test_conv_one_hot_probes_bit_exact():
         assert_exact("probe dw", dw.cpu().double().numpy(), O.conv_backward_weights(x, d, k, s, p))
 
 
-@pytest.mark.parametrize("shape", [(2, 16, 32, 32), (8, 256, 26, 26), (3, 5, 7, 9), (2, 3, 1, 1)])
+@pytest.mark.parametrize("shape", [
+    (2, 16, 32, 32), (8, 256, 26, 26),          # one pass, 256-thread work-groups
+    (1, 8, 96, 64),                             # one pass at its 256 x 6 float4 limit
+    (1, 8, 96, 68), (8, 32, 52, 52),            # one pass, 1024-thread work-groups
+    (6, 4, 64, 64),                             # one pass at its 1024 x 6 float4 limit
+    (6, 4, 64, 68), (2, 4, 128, 128),           # two streaming passes (16-byte loads)
+    (3, 5, 7, 9), (2, 3, 1, 1)])                # two passes, element loads
 def test_bn_backward_entry_point(shape):
     torch = require_gpu()
     from cnn_backward_pass_amd import cbb
@@ -680,7 +686,7 @@ def test_fc_and_softmax_loss():
 
 def test_launch_hook_names_each_kernel():
     """The tracing hook sees every kernel of a call, in launch order, on the call's stream
-    (act/BN reduction and the per-channel map, then the gradient kernels)."""
+    (the one-pass act/BN kernel, then the gradient kernels)."""
     torch = require_gpu()
     from cnn_backward_pass_amd import cbb
     announce("launch hook")
@@ -701,8 +707,9 @@ def test_launch_hook_names_each_kernel():
         cbb.set_launch_hook(None)
     torch.cuda.synchronize()
     names = [n for n, _ in seen]
-    assert names[:2] == ["actbn_reduce", "actbn_apply"], names
-    assert len(names) >= 4 and all(st == stream.cuda_stream for _, st in seen)
+    assert names[0] == "actbn_channel", names     # a channel fits one work-group
+    assert len(names) >= 3 and all(st == stream.cuda_stream for _, st in seen)
+    assert any(n.startswith("conv_dw") for n in names) and any(n.startswith("conv_dx") for n in names)
     cbb.conv_block_backward(d, x, w, y, xn, var, gam, dl, dz, dw, db, dg, dx, False, ws)
     torch.cuda.synchronize()
     assert len(seen) == len(names)   # removed: no more calls
