@@ -88,6 +88,7 @@ _SIGS = {
     "orc_route_backward": ([_i, _i, _L, _D, ctypes.POINTER(_D)], None),
     "orc_upsample_forward": ([_i] * 5 + [_D, _D], None),
     "orc_upsample_backward": ([_i] * 5 + [_D, _D], None),
+    "orc_sgd_update": ([_l, _i, _d, _d, _d, _D, _D], None),
 }
 
 
@@ -443,3 +444,11 @@ def upsample_backward(delta, scale: int = 2, dx=None) -> np.ndarray:
     dx = np.zeros((n, c, h, w)) if dx is None else _f64(dx).copy()
     lib().orc_upsample_backward(n, c, h, w, scale, _p(delta), _p(dx))
     return dx
+
+
+def sgd_update(w, dw, batch: int, lr: float, momentum: float, decay: float):
+    """One parameter update (orc_sgd_update): returns the new (w, dw)."""
+    w = _f64(w).copy()
+    dw = _f64(dw).copy()
+    lib().orc_sgd_update(w.size, batch, lr, momentum, decay, _p(w), _p(dw))
+    return w, dw

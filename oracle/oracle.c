@@ -725,3 +725,24 @@ void orc_upsample_backward(int n, int c, int h, int w, int scale, const double* 
         dx[(pl * h + r) * w + q] += acc;
       }
 }
+
+/* ------------------------------------------------------------------ */
+/* Parameter update after a full batch ([P1] section 1: update_network ->
+ * l.update once (seen / batch) % subdivisions == 0; [P3] layer struct: update
+ * takes (layer, batch, learning_rate, momentum, decay), and weight_updates is
+ * "the term that gradient descent multiplies by the step size").  The pages give
+ * no formula; the reading used here is gradient descent with momentum and L2
+ * weight decay in which the accumulated-gradient buffer doubles as the momentum
+ * buffer (the next backward adds onto it):
+ *   u = dw + decay * batch * w      (dw holds the gradient summed over the batch)
+ *   w = w - (learning_rate / batch) * u
+ *   dw = momentum * u
+ * Biases and BN scales take decay = 0. */
+void orc_sgd_update(long n, int batch, double lr, double momentum, double decay, double* w,
+                    double* dw) {
+  for (long i = 0; i < n; ++i) {
+    const double u = dw[i] + decay * batch * w[i];
+    w[i] -= lr / batch * u;
+    dw[i] = momentum * u;
+  }
+}

@@ -139,6 +139,10 @@ FORM_DZ_CASES = [  # first layers whose dz the fused dW + dX kernel forms as it 
     (2, 3, 12, 16, 32, 3, 1, 1, 2, "tanh"),          # fixed statistics: dz = a g
     (4, 3, 128, 128, 8, 3, 1, 1, True, "leaky"),     # many work-groups, two-level dW sum
     (1, 3, 30, 8, 17, 3, 1, 1, True, "loggy"),       # run-time activation switch
+    (1, 3, 1, 60, 32, 3, 1, 1, True, "leaky"),       # a single row
+    (3, 2, 2, 28, 9, 3, 1, 1, True, "relu"),         # two rows
+    (2, 3, 33, 56, 32, 3, 1, 1, True, "leaky"),      # an odd row count
+    (2, 3, 40, 416, 32, 3, 1, 1, True, "leaky"),     # the stem's width: four strips
 ]
 
 
