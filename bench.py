@@ -423,6 +423,18 @@ def time_variants(torch, reps=10):
         out[f"conv_dW.{name}.8x{c}x52x52"] = _roof(ms, 2.0 * macs, by)
         ms = timed(lambda: cbb.conv_backward_data(dsc, w, dz, dx, False, wsc))
         out[f"conv_dX.{name}.8x{c}x52x52"] = _roof(ms, 2.0 * macs, by)
+    # the parameter update after a full batch (cbb_sgd_update), over one flat buffer the
+    # size of every weight, bias and BN scale of the five workloads (16 B per element)
+    from cnn_backward_pass_amd import synth
+    nparam = 0
+    for wl in synth.WORKLOADS.values():
+        for c in wl.convs:
+            nparam += c.out_c * c.in_c * c.k * c.k + c.out_c * (2 if c.bn else 1)
+    nparam += sum(i * o + o for i, o in synth.LENET_FC)
+    pw, pg = rn(nparam), rn(nparam)
+    ms = timed(lambda: cbb.sgd_update(pw, pg, 8, 1e-3, 0.9, 5e-4))
+    out["sgd_update.all_parameters_of_the_five_workloads"] = _roof(ms, 0.0, 16.0 * nparam)
+    del pw, pg
     # the block forward (cbb_conv_block_forward: convolution, batch statistics, BN and
     # activation in one call) at three workload layers; FLOPs of the convolution only
     for name, (n, c, hw, oc, s) in (("yolov3_stem_conv1", (16, 3, 416, 32, 1)),

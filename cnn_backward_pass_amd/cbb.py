@@ -93,6 +93,7 @@ _SIGS = {
     "cbb_upsample_backward": ([_i32] * 5 + [_P, _P, _P], _i32),
     "cbb_maxpool_backward": ([_i32] * 6 + [_P, _P, _P, _P], _i32),
     "cbb_get_device_error": ([_P, ctypes.POINTER(_i32)], _i32),
+    "cbb_sgd_update": ([_i64, _i32, _f, _f, _f, _P, _P, _P], _i32),
     "cbb_set_launch_hook": ([_P, _P], _i32),
 }
 DEVERR_LABEL = 1
@@ -476,3 +477,12 @@ def set_launch_hook(fn) -> None:
     cb = LAUNCH_HOOK(lambda user, name, st: fn(name.decode(), st or 0))
     _check("cbb_set_launch_hook", lib().cbb_set_launch_hook(ctypes.cast(cb, ctypes.c_void_p), None))
     _hook_ref = cb
+
+
+def sgd_update(w, dw, batch: int, learning_rate: float, momentum: float = 0.0,
+               decay: float = 0.0, stream=None) -> None:
+    """Parameter update in place: u = dw + decay*batch*w; w -= lr/batch*u; dw = momentum*u."""
+    _sized("sgd_update", dw=(dw, w.numel()))
+    _check("cbb_sgd_update", lib().cbb_sgd_update(
+        w.numel(), batch, learning_rate, momentum, decay, _ptr(w, name="w"), _ptr(dw, name="dw"),
+        _stream(stream)))

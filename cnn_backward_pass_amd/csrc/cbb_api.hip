@@ -437,6 +437,14 @@ int cbb_upsample_backward(int n, int c, int h, int w, int scale, const float* de
   return launch_upsample(n, c, h, w, scale, delta, dx, S(stream));
 }
 
+int cbb_sgd_update(int64_t n, int batch, float learning_rate, float momentum, float decay,
+                   float* w, float* dw, void* stream) {
+  if (n < 0 || batch < 1 || !w || !dw || w == dw) return CBB_EINVAL;
+  if (!(learning_rate >= 0.f) || !(momentum >= 0.f) || !(decay >= 0.f)) return CBB_EINVAL;
+  if (n == 0) return CBB_OK;
+  return launch_sgd_update(n, batch, learning_rate, momentum, decay, w, dw, S(stream));
+}
+
 int cbb_maxpool_backward(int n, int c, int ih, int iw, int ksize, int stride,
                          const int32_t* idx, const float* delta, float* dx, void* stream) {
   if (n < 1 || c < 1 || ih < 1 || iw < 1 || ksize < 1 || stride < 1 || !idx || !delta || !dx)

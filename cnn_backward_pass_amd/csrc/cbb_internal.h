@@ -341,6 +341,8 @@ int launch_maxpool(int n, int c, int ih, int iw, int k, int s, const int32_t* id
                    const float* delta, float* dx, hipStream_t st);
 int launch_softmax_loss(int batch, int classes, const float* prob, const int32_t* labels,
                         float loss_weight, float* dlogits, int32_t* bad, hipStream_t st);
+int launch_sgd_update(int64_t n, int batch, float lr, float momentum, float decay, float* w,
+                      float* dw, hipStream_t st);
 int launch_fc(int batch, int in_dim, int out_dim, const float* x, const float* w,
               const float* delta, float* dw, float* db, float* dx, int dx_accumulate,
               hipStream_t st);

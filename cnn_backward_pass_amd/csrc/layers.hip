@@ -447,3 +447,50 @@ int launch_fc(int batch, int in_dim, int out_dim, const float* x, const float* w
 }
 
 }  // namespace cbb
+
+namespace cbb {
+
+// --------------------------------------------------------------- parameter update
+// Gradient descent after the backward pass, once per full batch (the pages' update
+// step; see cbb_sgd_update): u = dw + decay*batch*w; w -= lr/batch * u;
+// dw = momentum * u.  One read and one write of w and dw per element, 16-byte
+// accesses, the ragged tail element by element.
+__global__ __launch_bounds__(kThreads) void sgd_update_kernel(int64_t n, int vec, float kdecay,
+                                                              float step, float momentum,
+                                                              float* __restrict__ w,
+                                                              float* __restrict__ dw) {
+  const int64_t n4 = vec ? n >> 2 : 0;   // 16-byte accesses need 16-byte aligned w and dw
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += stride) {
+    float4 a = reinterpret_cast<float4*>(w)[i];
+    float4 g = reinterpret_cast<float4*>(dw)[i];
+    g.x += kdecay * a.x;
+    g.y += kdecay * a.y;
+    g.z += kdecay * a.z;
+    g.w += kdecay * a.w;
+    a.x -= step * g.x;
+    a.y -= step * g.y;
+    a.z -= step * g.z;
+    a.w -= step * g.w;
+    reinterpret_cast<float4*>(w)[i] = a;
+    reinterpret_cast<float4*>(dw)[i] = make_float4(momentum * g.x, momentum * g.y,
+                                                   momentum * g.z, momentum * g.w);
+  }
+  for (int64_t i = 4 * n4 + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) {
+    const float u = dw[i] + kdecay * w[i];
+    w[i] -= step * u;
+    dw[i] = momentum * u;
+  }
+}
+
+int launch_sgd_update(int64_t n, int batch, float lr, float momentum, float decay, float* w,
+                      float* dw, hipStream_t st) {
+  const int vec = ((uintptr_t)w % 16 == 0) && ((uintptr_t)dw % 16 == 0);
+  const int64_t items = vec ? std::max<int64_t>(n >> 2, 1) : n;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(ceil_div(items, kThreads), 8192));
+  sgd_update_kernel<<<(unsigned)blocks, kThreads, 0, st>>>(n, vec, decay * (float)batch,
+                                                            lr / (float)batch, momentum, w, dw);
+  return check_launch("sgd_update_kernel", st);
+}
+
+}  // namespace cbb

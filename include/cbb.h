@@ -392,6 +392,21 @@ int cbb_upsample_backward(int n, int c, int h, int w, int scale, const float* de
 int cbb_maxpool_backward(int n, int c, int ih, int iw, int ksize, int stride,
                          const int32_t* idx, const float* delta, float* dx, void* stream);
 
+/* Parameter update after a full batch (update_network -> l.update(layer, batch,
+ * learning_rate, momentum, decay), called once (seen / batch) % subdivisions == 0,
+ * [P1] section 1; the update hook and weight_updates, "the term gradient descent
+ * multiplies by the step size", [P3] layer struct).  The pages print no formula;
+ * this is gradient descent with momentum and L2 weight decay in which the
+ * accumulated-gradient buffer doubles as the momentum buffer (the next backward
+ * adds onto it, as every parameter gradient here accumulates):
+ *   u = dw + decay * batch * w;   w -= (learning_rate / batch) * u;   dw = momentum * u
+ * for i < n.  dw holds the gradient summed over the batch (dw, db, dgamma of the
+ * calls above); pass decay = 0 for biases and BN scales.  w and dw device arrays
+ * of n floats that do not overlap.  CBB_EINVAL for a negative size or rate,
+ * batch < 1 or NULL pointers. */
+int cbb_sgd_update(int64_t n, int batch, float learning_rate, float momentum, float decay,
+                   float* w, float* dw, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -296,3 +296,19 @@ def test_noalloc_entry_point_validates_on_the_host():
         assert call(d, **{missing: None}) == -1
     assert call(d, acc=2) == -1
     assert call(_desc(batch=0)) == -1
+
+
+def test_sgd_update_validates():
+    L = cbb.lib()
+    X, Y = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)
+    assert L.cbb_sgd_update(-1, 1, 0.1, 0.9, 0.0, X, Y, None) == -1
+    assert L.cbb_sgd_update(10, 0, 0.1, 0.9, 0.0, X, Y, None) == -1
+    assert L.cbb_sgd_update(10, 1, -0.1, 0.9, 0.0, X, Y, None) == -1
+    assert L.cbb_sgd_update(10, 1, 0.1, float("nan"), 0.0, X, Y, None) == -1
+    assert L.cbb_sgd_update(10, 1, 0.1, 0.9, -1.0, X, Y, None) == -1
+    assert L.cbb_sgd_update(10, 1, 0.1, 0.9, 0.0, X, X, None) == -1
+    assert L.cbb_sgd_update(10, 1, 0.1, 0.9, 0.0, None, Y, None) == -1
+    assert L.cbb_sgd_update(0, 1, 0.1, 0.9, 0.0, X, Y, None) == 0     # empty: no launch
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match="dw"):
+        cbb.sgd_update(torch.zeros(10), torch.zeros(9), 1, 0.1)

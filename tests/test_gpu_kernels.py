@@ -717,3 +717,33 @@ def test_launch_hook_names_each_kernel():
     cbb.conv_block_backward(d, x, w, y, xn, var, gam, dl, dz, dw, db, dg, dx, False, ws)
     torch.cuda.synchronize()
     assert len(seen) == len(names)   # removed: no more calls
+
+
+@pytest.mark.parametrize("n,batch,lr,mom,decay,off", [
+    (294912, 8, 0.1, 0.9, 5e-4, 0),      # the residual 3x3 layer's weights, 16-byte path
+    (1001, 64, 0.01, 0.0, 0.0, 0),       # ragged tail
+    (777, 3, 0.5, 0.5, 1e-2, 1),         # misaligned: element path only
+    (1, 1, 1.0, 0.9, 0.0, 0)])
+def test_sgd_update(n, batch, lr, mom, decay, off):
+    """The parameter update against the oracle's, over three steps with new gradients
+    added onto the buffer in between (as a backward pass accumulates)."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    announce(f"sgd_update n={n} batch={batch} off={off}")
+    r = np.random.default_rng(n)
+    w0 = r.normal(size=n).astype(np.float32)
+    wb = torch.zeros(n + off, device="cuda")
+    db = torch.zeros(n + off, device="cuda")
+    w, d = wb[off:], db[off:]
+    w.copy_(torch.from_numpy(w0))
+    rw, rd = w0.astype(np.float64), np.zeros(n)
+    for step in range(3):
+        g = (r.normal(size=n) * batch).astype(np.float32)
+        d.add_(torch.from_numpy(g).cuda())
+        rd = rd + g
+        cbb.sgd_update(w, d, batch, lr, mom, decay)
+        rw, rd = O.sgd_update(rw, rd.astype(np.float32), batch, lr, mom, decay)
+        torch.cuda.synchronize()
+        assert_close(f"w step {step}", w.cpu().double().numpy(), rw, tol=1e-6)
+        assert_close(f"dw step {step}", d.cpu().double().numpy(), rd, tol=1e-6)
+        rw, rd = w.cpu().double().numpy(), d.cpu().double().numpy()
