@@ -9,8 +9,9 @@
 // "Understanding BatchNorm" (javaforall.cn): Caffe's closed form
 //   dz = (g' - mean(g') - mean(g' x_norm) x_norm) / sqrt(var + eps), g' = gamma g.
 //
-// A channel small enough for one work-group (batch statistics, N*HW <= 24576)
-// takes one pass instead (actbn_channel): loads, sums, dz, all in registers.
+// A channel small enough for one work-group (N*HW <= 24576 with BN, 40960
+// without) takes one pass instead (actbn_channel): loads, sums, dz (or the map),
+// all in registers.
 // Pass 1 (actbn_reduce) : each work-group sums (g, g*x_norm) over one segment
 //                         of one channel -> workspace partials[c][seg].  Without
 //                         batch statistics dz does not depend on the sums and is
@@ -157,43 +158,46 @@ __global__ __launch_bounds__(kThreads) void actbn_reduce(
   if (threadIdx.x == 0) part[(int64_t)c * s.nseg + sg] = make_float2(sg_, sgx);
 }
 
-// One pass for a channel that one work-group can hold (batch statistics): the
-// work-group loads the whole channel -- TPB threads x NV float4 of g = delta *
-// act'(y) and of x_norm, in registers -- sums g and g*x_norm (fixed tree order),
-// adds the sums into dbeta[c] / dgamma[c] (one work-group per channel: no other
-// writer), forms the map dz = a*g + b + cc*x_norm and writes dz.  delta, y and
-// x_norm are read once, dz written once: the 16 bytes per element of the
-// touch-once bound, where the two-pass form reads the three tensors twice.
+// One pass for a channel that one work-group can hold: the work-group loads the
+// whole channel -- TPB threads x NV float4 of g = delta * act'(y) and (BN) of
+// x_norm, in registers -- sums g and g*x_norm (fixed tree order), adds the sums
+// into dbeta[c] (db without BN) and dgamma[c] (one work-group per channel: no
+// other writer), forms the map dz = a*g + b + cc*x_norm (batch statistics; a =
+// gamma/sqrt(var+eps), b = cc = 0 with fixed statistics; a = 1 without BN) and
+// writes dz -- or, when a gradient kernel forms dz itself, writes the map to
+// coef[c], coef[C+c], coef[2C+c] instead.  delta, y and x_norm are read once and
+// dz written once: the 16 bytes per element of the touch-once bound, where the
+// two-pass form reads the three tensors twice; a bias-only stage is one launch.
 // Needs HW % 4 == 0, 16-byte aligned tensors and N*HW/4 <= TPB*NV.
-template <int ACT, int TPB, int NV>
+template <int ACT, int BN, int TPB, int NV>
 __global__ __launch_bounds__(TPB) void actbn_channel(
     int N, int C, int HW, const float* delta, const float* __restrict__ y,
     const float* __restrict__ xn, float slope, int act_rt, const float* __restrict__ var,
-    const float* __restrict__ gamma, float eps, float* dz /* may alias delta */,
-    float* __restrict__ dgamma, float* __restrict__ dbeta) {
+    const float* __restrict__ gamma, float eps, float* dz /* NULL: not written; may alias delta */,
+    float* __restrict__ dgamma, float* __restrict__ dbeta_or_db, float* __restrict__ coef) {
   constexpr int NW = TPB / 64;
   const int act = ACT == kActAny ? act_rt : ACT;
-  constexpr bool has_y = ACT != CBB_ACT_LINEAR;
+  constexpr bool has_y = ACT != CBB_ACT_LINEAR, has_x = BN != kBnNone;
   const int c = blockIdx.x, per = HW >> 2, total = N * per;
-  float4 g[NV], x[NV];
-  int64_t off[NV];
+  float4 g[NV], x[has_x ? NV : 1];
+  int off[NV];   // element offsets (tensors index in int32)
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int e = threadIdx.x + k * TPB;
     const int n = e / per, r = e - n * per;
-    off[k] = e < total ? ((int64_t)n * C + c) * HW + 4 * r : -1;
+    off[k] = e < total ? (n * C + c) * HW + 4 * r : -1;
   }
+  const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
   // every load of the channel is issued before the first use
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
     g[k] = off[k] >= 0 ? ld4(delta + off[k]) : zero;
-    x[k] = off[k] >= 0 ? ld4(xn + off[k]) : zero;
+    if constexpr (has_x) x[k] = off[k] >= 0 ? ld4(xn + off[k]) : zero;
   }
   if constexpr (has_y) {
     float4 yy[NV];
 #pragma unroll
-    for (int k = 0; k < NV; ++k) yy[k] = off[k] >= 0 ? ld4(y + off[k]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < NV; ++k) yy[k] = off[k] >= 0 ? ld4(y + off[k]) : zero;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       g[k].x *= act_grad(act, slope, yy[k].x);
@@ -206,11 +210,12 @@ __global__ __launch_bounds__(TPB) void actbn_channel(
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     sg += (g[k].x + g[k].y) + (g[k].z + g[k].w);
-    sgx += (g[k].x * x[k].x + g[k].y * x[k].y) + (g[k].z * x[k].z + g[k].w * x[k].w);
+    if constexpr (has_x)
+      sgx += (g[k].x * x[k].x + g[k].y * x[k].y) + (g[k].z * x[k].z + g[k].w * x[k].w);
   }
   __shared__ float red[2][NW];
   sg = wave_sum(sg);
-  sgx = wave_sum(sgx);
+  if constexpr (has_x) sgx = wave_sum(sgx);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     red[0][wave] = sg;
@@ -224,19 +229,34 @@ __global__ __launch_bounds__(TPB) void actbn_channel(
     sg += red[0][w];
     sgx += red[1][w];
   }
-  if (threadIdx.x == 0) {
-    dbeta[c] += sg;
-    dgamma[c] += sgx;
+  float ka = 1.f, kb = 0.f, kc = 0.f;
+  if constexpr (has_x) ka = gamma[c] / sqrtf(var[c] + eps);
+  if constexpr (BN == kBnBatch) {
+    const float inv_m = 1.f / (float)((int64_t)N * HW);
+    kb = -ka * (sg * inv_m);
+    kc = -ka * (sgx * inv_m);
   }
-  const float inv_m = 1.f / (float)((int64_t)N * HW);
-  const float ka = gamma[c] / sqrtf(var[c] + eps);
-  const float kb = -ka * (sg * inv_m), kc = -ka * (sgx * inv_m);
+  if (threadIdx.x == 0) {
+    dbeta_or_db[c] += sg;
+    if constexpr (has_x) dgamma[c] += sgx;
+    if (coef) {
+      coef[c] = ka;
+      coef[C + c] = kb;
+      coef[2 * C + c] = kc;
+    }
+  }
+  if (coef || !dz) return;
 #pragma unroll
   for (int k = 0; k < NV; ++k)
-    if (off[k] >= 0)
-      *reinterpret_cast<float4*>(dz + off[k]) =
-          make_float4(ka * g[k].x + kb + kc * x[k].x, ka * g[k].y + kb + kc * x[k].y,
-                      ka * g[k].z + kb + kc * x[k].z, ka * g[k].w + kb + kc * x[k].w);
+    if (off[k] >= 0) {
+      float4 v;
+      if constexpr (has_x)
+        v = make_float4(ka * g[k].x + kb + kc * x[k].x, ka * g[k].y + kb + kc * x[k].y,
+                        ka * g[k].z + kb + kc * x[k].z, ka * g[k].w + kb + kc * x[k].w);
+      else
+        v = g[k];
+      *reinterpret_cast<float4*>(dz + off[k]) = v;
+    }
 }
 
 // Fold the nseg partials of channel c in a fixed order; every thread gets the sums.
@@ -590,8 +610,9 @@ size_t actbn_workspace(int N, int C, int64_t HW) {
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 // float4 per thread of the one-pass form: channels of up to 256 x 6 x 4 = 6144
-// elements take 256-thread work-groups, up to 1024 x 6 x 4 = 24576 elements 1024.
-constexpr int kChanNV = 6;
+// elements take 256-thread work-groups, up to 1024 x 6 x 4 = 24576 elements (BN) or
+// 1024 x 10 x 4 = 40960 (no BN: no x_norm held) 1024.
+constexpr int kChanNV = 6, kChanNV1024 = 10;
 
 // g/BN stage of a conv block, or a standalone BN backward (act = LINEAR).
 // Writes dz (when needed), adds to dgamma/dbeta (BN) or db (no BN).
@@ -602,6 +623,24 @@ static void launch_actbn_t(const SegGeom& s, unsigned blocks, int act, const flo
                            float* dbeta_or_db, float2* part, int write_dz, float* coef,
                            hipStream_t st) {
   const float* xr = BN != kBnNone ? xn : nullptr;
+  // A channel that one work-group holds in registers takes one pass for any mode:
+  // sums, then dz (or the map for a kernel that forms dz itself).
+  const int64_t q = (int64_t)s.N * s.HW / 4;
+  if (VEC && q <= 256 * kChanNV) {
+    actbn_channel<ACT, BN, 256, kChanNV><<<(unsigned)s.C, 256, 0, st>>>(
+        s.N, s.C, s.HW, delta, y, xr, slope, act, var, gamma, eps, write_dz ? dz : nullptr,
+        dgamma, dbeta_or_db, coef);
+    note_launch("actbn_channel", st);
+    return;
+  }
+  constexpr int NV1024 = BN != kBnNone ? kChanNV : kChanNV1024;   // g and x_norm: 128 VGPRs
+  if (VEC && q <= 1024 * NV1024) {
+    actbn_channel<ACT, BN, 1024, NV1024><<<(unsigned)s.C, 1024, 0, st>>>(
+        s.N, s.C, s.HW, delta, y, xr, slope, act, var, gamma, eps, write_dz ? dz : nullptr,
+        dgamma, dbeta_or_db, coef);
+    note_launch("actbn_channel", st);
+    return;
+  }
   if (coef || BN != kBnBatch) {
     // one streaming pass (dz written in it, or formed later from coef)
     actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(
@@ -619,22 +658,9 @@ static void launch_actbn_t(const SegGeom& s, unsigned blocks, int act, const flo
     }
     return;
   }
-  // batch statistics: dz needs the channel's sums.  A channel that one work-group
-  // holds in registers is read once (actbn_channel); otherwise it is streamed twice.
+  // batch statistics on a channel too large for one work-group: dz needs the
+  // channel's sums, so the data is streamed twice
   if constexpr (BN == kBnBatch) {
-    const int64_t q = (int64_t)s.N * s.HW / 4;
-    if (VEC && q <= 256 * kChanNV) {
-      actbn_channel<ACT, 256, kChanNV><<<(unsigned)s.C, 256, 0, st>>>(
-          s.N, s.C, s.HW, delta, y, xn, slope, act, var, gamma, eps, dz, dgamma, dbeta_or_db);
-      note_launch("actbn_channel", st);
-      return;
-    }
-    if (VEC && q <= 1024 * kChanNV) {
-      actbn_channel<ACT, 1024, kChanNV><<<(unsigned)s.C, 1024, 0, st>>>(
-          s.N, s.C, s.HW, delta, y, xn, slope, act, var, gamma, eps, dz, dgamma, dbeta_or_db);
-      note_launch("actbn_channel", st);
-      return;
-    }
     actbn_reduce<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xr, slope, act, var,
                                                             gamma, eps, nullptr, part);
     note_launch("actbn_reduce", st);

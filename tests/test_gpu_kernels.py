@@ -446,7 +446,9 @@ def test_bn_backward_entry_point(shape):
         assert np.all(np.abs(s) <= 1e-5 * terms)
 
 
-@pytest.mark.parametrize("shape", [(2, 16, 32, 32), (4, 64, 13, 13), (3, 5, 7, 9), (1, 3, 1, 1)])
+@pytest.mark.parametrize("shape", [(2, 16, 32, 32), (4, 64, 13, 13), (3, 5, 7, 9), (1, 3, 1, 1),
+                                   (6, 4, 64, 64),      # one pass at its 1024 x 6 float4 limit
+                                   (2, 4, 128, 128)])   # the streaming pass
 def test_bn_backward_fixed_entry_point(shape):
     """Fixed statistics: dz = gamma g / sqrt(var + eps) in the streaming pass, dgamma /
     dbeta from the per-segment sums, added onto non-zero values."""
@@ -747,3 +749,30 @@ def test_sgd_update(n, batch, lr, mom, decay, off):
         assert_close(f"w step {step}", w.cpu().double().numpy(), rw, tol=1e-6)
         assert_close(f"dw step {step}", d.cpu().double().numpy(), rd, tol=1e-6)
         rw, rd = w.cpu().double().numpy(), d.cpu().double().numpy()
+
+
+@pytest.mark.parametrize("act", ["leaky", "linear"])
+@pytest.mark.parametrize("n,oc,h,w", [(4, 3, 96, 104),     # one pass, 1024 threads x 10 float4
+                                      (4, 3, 104, 104),    # beyond it: the streaming pass
+                                      (3, 7, 9, 12)])      # one pass, 256 threads
+def test_bias_only_act_stage(n, oc, h, w, act):
+    """The act stage of a conv without BN: db += sum g and, with an activation, dz = g,
+    on both sides of the one-pass size limit."""
+    torch = require_gpu()
+    from cnn_backward_pass_amd import cbb
+    announce(f"bias-only act stage {(n, oc, h, w)} {act}")
+    r = np.random.default_rng(oc * h + w)
+    y = r.normal(size=(n, oc, h, w)).astype(np.float32)
+    d = r.normal(size=(n, oc, h, w)).astype(np.float32)
+    desc = cbb.conv_desc(n, 3, h, w, oc, 1, 1, 0, 0, act)
+    ws = cbb.workspace(cbb.conv_block_workspace_size(desc))
+    db0 = r.normal(size=oc).astype(np.float32)
+    db = _t(torch, db0)
+    dz = torch.empty(n, oc, h, w, device="cuda") if act != "linear" else None
+    cbb.conv_act_bn_backward(desc, _t(torch, y) if act != "linear" else None, None, None, None,
+                             _t(torch, d), dz, db, None, ws)
+    torch.cuda.synchronize()
+    g = O.act_backward(cbb.ACT[act], 0.1, y, d)
+    assert_close("db", db.cpu().double().numpy(), db0 + g.sum(axis=(0, 2, 3)), tol=1e-5)
+    if dz is not None:
+        assert_close("dz", dz.cpu().double().numpy(), g, tol=1e-6)
