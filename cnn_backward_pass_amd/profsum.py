@@ -162,17 +162,22 @@ def dispatch_counters(db: str):
     return out
 
 
-def mfma_rows(db: str, simds: int):
+def mfma_rows(db: str, simds: int, xcds: int = 8):
     """Per kernel of the profiled stage: dispatches, fp32 matrix FLOPs per launch
     (SQ_INSTS_VALU_MFMA_MOPS_F32 x 512, summed over the rows of a dispatch) and the
-    matrix-core busy share SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), the
-    MfmaUtil formula of rocprofv3's derived counters."""
+    matrix-core busy share SQ_VALU_MFMA_BUSY_CYCLES / (GUI cycles x SIMDs).
+
+    GRBM_GUI_ACTIVE comes back as one value per dispatch summed over the chip's
+    ``xcds`` dies (8 on MI355X: a 360 us launch reads ~6.3 M cycles, eight times its
+    ~786 k cycles at 2.2 GHz), so the GPU's active cycles are that value / xcds.  The
+    busy counter adds 64 cycles per 32x32x2 step and SIMD, so a share of 1.0 is every
+    SIMD issuing matrix work on every active cycle."""
     kinds = collections.defaultdict(lambda: [0, 0.0, 0.0, 0.0])
     for name, vals in dispatch_counters(db).values():
         if "cbb::" not in name or not all(c in vals for c in MFMA_COUNTERS[:3]):
             continue
         k = kinds[_short(name)]
-        gui = max(vals["GRBM_GUI_ACTIVE"])
+        gui = sum(vals["GRBM_GUI_ACTIVE"]) / max(xcds, 1)
         k[0] += 1
         k[1] += sum(vals["SQ_INSTS_VALU_MFMA_MOPS_F32"]) * 512.0
         k[2] += sum(vals["SQ_VALU_MFMA_BUSY_CYCLES"]) / max(gui * simds, 1.0)
@@ -182,14 +187,16 @@ def mfma_rows(db: str, simds: int):
 
 
 def write_mfma(a) -> None:
-    rows = mfma_rows(a.db, a.simds)
-    rec = {"stage": a.stage, "simds": a.simds, "kernels": rows, "sources": sources_digest()}
+    rows = mfma_rows(a.db, a.simds, a.xcds)
+    rec = {"stage": a.stage, "simds": a.simds, "xcds": a.xcds, "kernels": rows,
+           "sources": sources_digest()}
     lines = [f"# Matrix-core counters of {a.stage} (rocprofv3 --pmc)", "",
              "Command (from the repository root, one MI355X):", "", "```", a.cmd, "```", "",
              f"Per kernel: fp32 matrix FLOPs per launch counted by the hardware "
              f"(SQ_INSTS_VALU_MFMA_MOPS_F32 x 512) and the matrix-core busy share "
-             f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x {a.simds} SIMDs).", "",
-             "| kernel | dispatches | MFMA GFLOP / launch | matrix cores busy | GUI active cycles |",
+             f"SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {a.xcds} dies x {a.simds} SIMDs); "
+             f"GRBM_GUI_ACTIVE is read summed over the {a.xcds} dies.", "",
+             "| kernel | dispatches | MFMA GFLOP / launch | matrix cores busy | GPU active cycles |",
              "|---|---|---|---|---|"]
     for k in sorted(rows, key=lambda k: -rows[k]["mfma_flops"]):
         r = rows[k]
@@ -257,6 +264,7 @@ def main(argv=None) -> None:
     m.add_argument("--out", required=True)
     m.add_argument("--cmd", required=True)
     m.add_argument("--simds", type=int, default=1024, help="SIMDs on the GPU (256 CUs x 4)")
+    m.add_argument("--xcds", type=int, default=8, help="dies GRBM_GUI_ACTIVE is summed over")
     a = ap.parse_args(argv)
     if a.cmd_name == "trace":
         write_trace(a.db, a.out, a.title, a.cmd)

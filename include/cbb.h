@@ -394,8 +394,8 @@ int cbb_maxpool_backward(int n, int c, int ih, int iw, int ksize, int stride,
 
 /* Parameter update after a full batch (update_network -> l.update(layer, batch,
  * learning_rate, momentum, decay), called once (seen / batch) % subdivisions == 0,
- * [P1] section 1; the update hook and weight_updates, "the term gradient descent
- * multiplies by the step size", [P3] layer struct).  The pages print no formula;
+ * [P1] section 1; [P3] layer struct: the update hook and the weight_updates buffer
+ * it consumes).  The pages print no formula;
  * this is gradient descent with momentum and L2 weight decay in which the
  * accumulated-gradient buffer doubles as the momentum buffer (the next backward
  * adds onto it, as every parameter gradient here accumulates):

@@ -729,8 +729,8 @@ void orc_upsample_backward(int n, int c, int h, int w, int scale, const double* 
 /* ------------------------------------------------------------------ */
 /* Parameter update after a full batch ([P1] section 1: update_network ->
  * l.update once (seen / batch) % subdivisions == 0; [P3] layer struct: update
- * takes (layer, batch, learning_rate, momentum, decay), and weight_updates is
- * "the term that gradient descent multiplies by the step size").  The pages give
+ * takes (layer, batch, learning_rate, momentum, decay), and weight_updates holds
+ * the gradient term that the step size scales).  The pages give
  * no formula; the reading used here is gradient descent with momentum and L2
  * weight decay in which the accumulated-gradient buffer doubles as the momentum
  * buffer (the next backward adds onto it):

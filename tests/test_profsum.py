@@ -48,18 +48,20 @@ def test_traffic_scaling_and_gate(tmp_path):
 
 def test_mfma_rows_per_kernel(tmp_path):
     """Matrix FLOPs sum over a dispatch's rows (x 512); the busy share divides the summed
-    busy cycles by the largest GRBM_GUI_ACTIVE row times the SIMD count."""
+    busy cycles by the GPU's active cycles (GRBM_GUI_ACTIVE, read summed over the dies,
+    divided by their count) times the SIMD count."""
     k = "void cbb::conv_dx3_s2p<4>(int)"
     db = tmp_path / "m.db"
     _db(db, [(1, k, "SQ_INSTS_VALU_MFMA_MOPS_F32", 1000.0), (1, k, "SQ_INSTS_VALU_MFMA_MOPS_F32", 1000.0),
-             (1, k, "SQ_VALU_MFMA_BUSY_CYCLES", 4000.0), (1, k, "GRBM_GUI_ACTIVE", 10.0),
-             (1, k, "GRBM_GUI_ACTIVE", 8.0),
+             (1, k, "SQ_VALU_MFMA_BUSY_CYCLES", 4000.0), (1, k, "GRBM_GUI_ACTIVE", 50.0),
+             (1, k, "GRBM_GUI_ACTIVE", 30.0),
              (2, k, "SQ_INSTS_VALU_MFMA_MOPS_F32", 3000.0), (2, k, "SQ_VALU_MFMA_BUSY_CYCLES", 2000.0),
-             (2, k, "GRBM_GUI_ACTIVE", 10.0),
+             (2, k, "GRBM_GUI_ACTIVE", 80.0),
              (3, "at::native::fill", "SQ_INSTS_VALU_MFMA_MOPS_F32", 7.0)])
-    rows = profsum.mfma_rows(str(db), simds=1000)
+    rows = profsum.mfma_rows(str(db), simds=1000, xcds=8)
     assert list(rows) == ["conv_dx3_s2p<4>"]
     r = rows["conv_dx3_s2p<4>"]
     assert r["dispatches"] == 2
     assert r["mfma_flops"] == (2000.0 + 3000.0) * 512 / 2
     assert abs(r["mfma_busy"] - (0.4 + 0.2) / 2) < 1e-12
+    assert r["gui_active_cycles"] == 10.0
