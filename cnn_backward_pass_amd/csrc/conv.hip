@@ -315,10 +315,11 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
       kc[i] = src.coef[2 * g.OC + o];
     }
   }
-  auto fetch = [&](int q) {
+  // Input rows (x) and the dz row are fetched and committed separately, so each
+  // part can go between matrix-core steps of the previous row.
+  auto fetch_x = [&](int q) {
     const int hb = S * q + 2 - S;
     xm = 0;
-    zm = 0;
     if constexpr (V4) {
 #pragma unroll
       for (int i = 0; i < XPT4; ++i) {
@@ -330,6 +331,23 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
         px4[i] = *(const f4*)(xb + (ok ? c * g.HW + h * g.W + w : 0));
         xm |= (uint32_t)ok << i;
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < Cf::XPT; ++i) {
+        const int e = tid + i * NT;
+        const int rr = e / (32 * Cf::XC), rem = e - rr * (32 * Cf::XC);
+        const int c = rem / Cf::XC, j = rem - c * Cf::XC;
+        const int h = hb + rr, w = ic0 + j;
+        const bool ok =
+            e < Cf::XNEW && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+        px[i] = xb[ok ? c * g.HW + h * g.W + w : 0];
+        xm |= (uint32_t)ok << i;
+      }
+    }
+  };
+  auto fetch_z = [&](int q) {
+    zm = 0;
+    if constexpr (V4) {
 #pragma unroll
       for (int i = 0; i < ZPT4; ++i) {
         const int e = tid + i * NT;
@@ -341,28 +359,18 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
         if constexpr (fz) pn4[i] = *(const f4*)(nb + zo);
         zm |= (uint32_t)ok << i;
       }
-      return;
-    }
+    } else {
 #pragma unroll
-    for (int i = 0; i < Cf::XPT; ++i) {
-      const int e = tid + i * NT;
-      const int rr = e / (32 * Cf::XC), rem = e - rr * (32 * Cf::XC);
-      const int c = rem / Cf::XC, j = rem - c * Cf::XC;
-      const int h = hb + rr, w = ic0 + j;
-      const bool ok = e < Cf::XNEW && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
-      px[i] = xb[ok ? c * g.HW + h * g.W + w : 0];
-      xm |= (uint32_t)ok << i;
-    }
-#pragma unroll
-    for (int i = 0; i < Cf::ZPT; ++i) {
-      const int e = tid + i * NT;
-      const int o = e / TC, j = e - o * TC;
-      const bool ok = e < Cf::ZNEW && oc0 + j < g.OW;
-      pz[i] = zb[ok ? o * g.OHW + q * g.OW + oc0 + j : 0];
-      zm |= (uint32_t)ok << i;
+      for (int i = 0; i < Cf::ZPT; ++i) {
+        const int e = tid + i * NT;
+        const int o = e / TC, j = e - o * TC;
+        const bool ok = e < Cf::ZNEW && oc0 + j < g.OW;
+        pz[i] = zb[ok ? o * g.OHW + q * g.OW + oc0 + j : 0];
+        zm |= (uint32_t)ok << i;
+      }
     }
   };
-  auto commit = [&](int q) {
+  auto commit_x = [&](int q) {
     const int hb = S * q + 2 - S;
     if constexpr (V4) {
 #pragma unroll
@@ -378,6 +386,20 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
             if ((unsigned)(4 * v - 3 + u) < (unsigned)Cf::XC) d[u] = ok ? px4[i][u] : 0.f;
         }
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < Cf::XPT; ++i) {
+        const int e = tid + i * NT;
+        const int rr = e / (32 * Cf::XC), rem = e - rr * (32 * Cf::XC);
+        const int c = rem / Cf::XC, j = rem - c * Cf::XC;
+        if (e < Cf::XNEW)
+          lds[((hb + rr + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + j] =
+              ((xm >> i) & 1u) ? px[i] : 0.f;
+      }
+    }
+  };
+  auto commit_z = [&](int q) {
+    if constexpr (V4) {
 #pragma unroll
       for (int i = 0; i < ZPT4; ++i) {
         const int e = tid + i * NT;
@@ -399,23 +421,14 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
           for (int u = 0; u < 4; ++u) d[u] = ok ? val[u] : 0.f;
         }
       }
-      return;
-    }
+    } else {
 #pragma unroll
-    for (int i = 0; i < Cf::XPT; ++i) {
-      const int e = tid + i * NT;
-      const int rr = e / (32 * Cf::XC), rem = e - rr * (32 * Cf::XC);
-      const int c = rem / Cf::XC, j = rem - c * Cf::XC;
-      if (e < Cf::XNEW)
-        lds[((hb + rr + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + j] =
-            ((xm >> i) & 1u) ? px[i] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < Cf::ZPT; ++i) {
-      const int e = tid + i * NT;
-      const int o = e / TC, j = e - o * TC;
-      if (e < Cf::ZNEW)
-        lds[Cf::Z0 + (q & 1) * Cf::ZB + o * Cf::OS + j] = ((zm >> i) & 1u) ? pz[i] : 0.f;
+      for (int i = 0; i < Cf::ZPT; ++i) {
+        const int e = tid + i * NT;
+        const int o = e / TC, j = e - o * TC;
+        if (e < Cf::ZNEW)
+          lds[Cf::Z0 + (q & 1) * Cf::ZB + o * Cf::OS + j] = ((zm >> i) & 1u) ? pz[i] : 0.f;
+      }
     }
   };
 
@@ -428,10 +441,15 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
     const float v = xb[ok ? c * g.HW + h * g.W + w : 0];
     lds[((h + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + j] = ok ? v : 0.f;
   }
-  fetch(r0);
-  commit(r0);
+  fetch_x(r0);
+  fetch_z(r0);
+  commit_x(r0);
+  commit_z(r0);
   __syncthreads();
-  if (r0 + 1 < r1) fetch(r0 + 1);
+  if (r0 + 1 < r1) {
+    fetch_x(r0 + 1);
+    fetch_z(r0 + 1);
+  }
 
   f32x16 acc[3];
 #pragma unroll
@@ -443,12 +461,22 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
   const int abase0 = Cf::Z0 + (32 * oh + (lane & 31)) * Cf::OS + (lane >> 5) + 2 * Cf::KH * kq;
   const int bbase = (lane & 31) * Cf::CS + S * (lane >> 5) + 2 * S * Cf::KH * kq;
   // One barrier per row: the rows and the dz buffer that arrive for row r+1 go
-  // to slots (buffer) that row r does not read, so the staging of r+1 overlaps
-  // other waves' matrix work on r.
+  // to slots (buffer) that row r does not read.  When dz is formed here (three
+  // tensors' rows to stage and transform per row), each wave stages its part of
+  // row r+1 between its own matrix-core steps on row r (input rows after the
+  // second step, the dz row half way) and sends the loads for row r+2 as soon as
+  // the registers they land in are free: stem conv2 (16x32x416x416 -> 64, s2)
+  // 321 -> 284 us.  With a stored dz the staging is light and it goes after the
+  // row's matrix work (interleaved it measured 4-6% slower on the 52x52 and
+  // 26x26 layers).  (The run-time activation switch on 104-column strips would
+  // not fit the registers interleaved.)
+  constexpr bool kInter = fz && (FZ != kFzAny || TC <= 64);
+  constexpr int kStepX = Cf::KH > 2 ? 1 : 0, kStepZ = Cf::KH > 4 ? Cf::KH / 2 : Cf::KH - 1;
   for (int r = r0; r < r1; ++r) {
     // input row S*r - 1 + kh sits in slot (S*r - 1 + kh) mod NSLOT
     const int bs = ((S * r + kh - 1 + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + bbase;
     const int abase = abase0 + (r & 1) * Cf::ZB;
+    const bool next = r + 1 < r1, next2 = r + 2 < r1;
 #pragma unroll
     for (int sp = 0; sp < Cf::KH; ++sp) {
       if (Cf::KS % 2 == 0 || kq == 0 || sp < Cf::KS / 2) {
@@ -460,10 +488,22 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
         for (int kw = 0; kw < 3; ++kw)
           acc[kw] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[kw], acc[kw], 0, 0, 0);
       }
+      if (kInter && sp == kStepX && next) {
+        commit_x(r + 1);
+        if (next2) fetch_x(r + 2);
+      }
+      if (kInter && sp == kStepZ && next) {
+        commit_z(r + 1);
+        if (next2) fetch_z(r + 2);
+      }
     }
-    if (r + 1 < r1) {
-      commit(r + 1);
-      if (r + 2 < r1) fetch(r + 2);
+    if (!kInter && next) {
+      commit_x(r + 1);
+      commit_z(r + 1);
+      if (next2) {
+        fetch_x(r + 2);
+        fetch_z(r + 2);
+      }
     }
     __syncthreads();
   }
