@@ -1460,8 +1460,13 @@ __global__ __launch_bounds__(kThreads) void conv_dx_smallc_kernel(ConvGeom g,
 //       goes through LDS, strip column c takes, in a fixed order,
 //       P[(i,kh,0)][c+1] + P[(i,kh,1)][c] + P[(i,kh,2)][c-1] into dx row
 //       h + kh - 1; each dx row stays in registers until its third dz row.
-// dz row h+1 and x row h+2 are loaded into registers during row h and stored
-// to LDS after its matrix work; x rows live in a ring of four (slot = row & 3).
+// dz rows and the P block live in two LDS buffers each (row h uses buffer h & 1)
+// and x rows in a ring of four (slot = row & 3), so a row needs one barrier: at
+// its start each thread stores dz row h+1 and x row h+2 (loaded two rows earlier
+// into one of two register sets) into the buffers row h does not read, while the
+// other work-group's waves on the CU keep the matrix cores busy, and after its
+// matrix work sends the loads for rows h+3 / h+4; the combine of row h reads its
+// own P buffer after the barrier.
 // ---------------------------------------------------------------------------
 // odd row pitch: the dW operand reads one column across 32 channel rows
 constexpr int kFrThreads = 256, kFrPitch = 133, kFrMaxW = 120;
@@ -1480,9 +1485,9 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
   static_assert(CI >= 1 && CI <= 3, "9*CI columns must fit one 32-wide block");
   typedef float f4 __attribute__((ext_vector_type(4)));
   constexpr int P = kFrPitch;
-  __shared__ float Zs[32 * P];
+  __shared__ float Zs[2][32 * P];
   __shared__ float Xs[4 * CI * P];
-  __shared__ float Ps[32 * P];
+  __shared__ float Ps[2][32 * P];
   __shared__ float Z0[64];   // zeros: masked operands read here (no branches around reads)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1500,13 +1505,13 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
   const int vlast = (sw + 4) >> 2;
 
   // channels >= OC are never staged and stay zero
-  for (int e = tid; e < 32 * P; e += kFrThreads) Zs[e] = 0.f;
+  for (int e = tid; e < 2 * 32 * P; e += kFrThreads) (&Zs[0][0])[e] = 0.f;
   if (tid < 64) Z0[tid] = 0.f;
 
   // ---- staging: thread slot k takes 16-byte group e = tid + 256k of a row
   // (dz: channel e / 32, group e % 32; x: the same with CI channels).  Groups
   // off the image are zero, applied at the LDS store.  Two register sets: the
-  // rows loaded at the end of row h are stored to LDS during row h + 2.
+  // rows loaded during row h are stored to LDS at the start of row h + 2.
   constexpr bool fz = FZ != kFzOff, fz_y = fz && FZ != CBB_ACT_LINEAR;
   struct Stage {
     f4 pz[4], py[fz ? 4 : 1], pn[fz ? 4 : 1], px;
@@ -1544,7 +1549,7 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
       q.zmask |= (uint32_t)ok << k;
     }
   };
-  auto store_dz = [&](const Stage& q) {
+  auto store_dz = [&](const Stage& q, int buf) {
     const f4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -1566,7 +1571,7 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
           val.w = ca[k] * val.w + cb[k] + cc[k] * xn.w;
         }
         val = ((q.zmask >> k) & 1u) ? val : zero;
-        float* d = Zs + o * P + 4 * v;
+        float* d = Zs[buf] + o * P + 4 * v;
         d[0] = val.x;
         d[1] = val.y;
         d[2] = val.z;
@@ -1623,15 +1628,20 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
   const int pb = 3 + 32 * wave;   // LDS column of this wave's first pixel w0 - 1 + 32 * wave
 
   // One dz row.  `q` holds dz row h+1 and x row h+2 on entry; refilled with
-  // dz row h+3 and x row h+4 on exit.
+  // dz row h+3 and x row h+4.
   auto row = [&](int h, Stage& q) {
+    const int zb_ = h & 1;
+    // staging is unconditional (rows past the image are zeros): straight-line
+    // code keeps the compiler's waits on these loads precise
+    store_dz(q, zb_ ^ 1);
+    store_x(q, h + 2);
     // dW over this wave's 32 pixels of row h (rows of the run only)
     if (h >= r0 && h < r1) {
       // masked operands (pixels outside the strip, columns j >= 9*CI) read zeros:
       // the address is selected, so every read is unconditional
       const float* xr =
           jv ? Xs + (((h + xkh - 1) & 3) * CI + xi) * P + pb + xkw - 1 + kq : Z0;
-      const float* zr = Zs + j * P + pb + kq;
+      const float* zr = Zs[zb_] + j * P + pb + kq;
       float av[16], bv[16];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1653,7 +1663,7 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
       f32x16 ap;
 #pragma unroll
       for (int r = 0; r < 16; ++r) ap[r] = 0.f;
-      const float* zc = Zs + kq * P + pb + j;
+      const float* zc = Zs[zb_] + kq * P + pb + j;
       float zv[16];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1665,14 +1675,14 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Ps[acc_row(r, lane) * P + pb + j] = ap[r];
+      for (int r = 0; r < 16; ++r) Ps[zb_][acc_row(r, lane) * P + pb + j] = ap[r];
     }
-    __syncthreads();   // P complete; row h's reads of Zs and Xs are done
-
-    // staging is unconditional (rows past the image are zeros): straight-line
-    // code keeps the compiler's waits on these loads precise
-    store_dz(q);
-    store_x(q, h + 2);
+    // the registers of q are free again (not live across the matrix work)
+    load_dz(q, h + 3);
+    load_x(q, h + 4);
+    // P and the staged rows h+1 / h+2 complete; row h's reads of Zs and Xs are
+    // done, so row h+1 may overwrite them (the other buffer, the ring's free slot)
+    __syncthreads();
     if (cown) {
       // dx row h-1 is complete after this row; rows h and h+1 take their share
       float qv[CI][3];
@@ -1681,7 +1691,7 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
       for (int i = 0; i < CI; ++i)
 #pragma unroll
         for (int kh = 0; kh < 3; ++kh) {
-          const float* pr = Ps + (i * 9 + kh * 3) * P + k0;
+          const float* pr = Ps[zb_] + (i * 9 + kh * 3) * P + k0;
           qv[i][kh] = (pr[1] + pr[P]) + pr[2 * P - 1];
         }
       const int hp = h - 1;
@@ -1696,9 +1706,6 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
         dcur[i] = qv[i][2];
       }
     }
-    load_dz(q, h + 3);
-    load_x(q, h + 4);
-    __syncthreads();   // row h+1 staged; P reads done
   };
 
   // ---- prologue: x rows hA-1 .. hA+1 and dz row hA staged; rows hA+1 and hA+2
@@ -1710,7 +1717,7 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
   }
   load_dz(s0, hA);
   __syncthreads();   // the zero fill is done before the staged rows land
-  store_dz(s0);
+  store_dz(s0, hA & 1);
   load_dz(s0, hA + 1);
   load_x(s0, hA + 2);
   load_dz(s1, hA + 2);
@@ -1724,7 +1731,7 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
 
   // Sum the four waves' dW blocks (fixed order) and write this work-group's partial.
   __syncthreads();
-  float* red = Zs;  // 4 x 16 x 64 floats
+  float* red = Zs[0];  // 4 x 16 x 64 floats
 #pragma unroll
   for (int r = 0; r < 16; ++r) red[(wave * 16 + r) * 64 + lane] = adw[r];
   __syncthreads();
