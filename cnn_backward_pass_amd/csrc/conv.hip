@@ -227,7 +227,12 @@ struct Dw3RowCfg {
   static constexpr int KS = TC / 2;            // 32x32x2 steps per output row
   static constexpr int KH = (KS + 1) / 2;      // steps per half
   static constexpr int XC = S * (TC - 1) + 3;  // input columns under TC output columns
-  static constexpr int CS = XC | 1;            // channel pitch inside a ring slot (odd)
+  // input column j of a channel sits at LDS column X0 + j: the three columns before
+  // it take the head of the first 16-byte piece, so whole pieces are stored (the
+  // XP pieces of a row cover LDS columns 0 .. 4 XP - 1, all inside the pitch)
+  static constexpr int X0 = 3;
+  static constexpr int XP = (XC + 6) / 4;
+  static constexpr int CS = ((XC + X0) > 4 * XP ? XC + X0 : 4 * XP) | 1;   // channel pitch (odd)
   static constexpr int SLOT = 32 * CS;
   static constexpr int NSLOT = 3 + S;          // ring: the three rows in use + the S arriving
   static constexpr int OS = TC + 1;            // dz row pitch per output channel (odd)
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
   static_assert(Cf::XPT <= 32 && Cf::ZPT <= 32, "one mask bit per fetched element");
   static_assert(!V4 || TC % 4 == 0, "16-byte loads need a strip width multiple of 4");
   typedef float f4 __attribute__((ext_vector_type(4)));
-  constexpr int XV = (Cf::XC + 6) / 4;   // 16-byte pieces per input row (columns -3 ..)
+  constexpr int XV = Cf::XP;   // 16-byte pieces per input row (columns -3 ..)
   constexpr int XNEW4 = S * 32 * XV, XPT4 = (XNEW4 + NT - 1) / NT;
   constexpr int ZV = TC / 4, ZNEW4 = 64 * ZV, ZPT4 = (ZNEW4 + NT - 1) / NT;
   float px[V4 ? 1 : Cf::XPT], pz[V4 ? 1 : Cf::ZPT];
@@ -379,11 +384,12 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
         const int rr = e / (32 * XV), rem = e - rr * (32 * XV);
         const int c = rem / XV, v = rem - c * XV;
         if (e < XNEW4) {
-          float* d = lds + ((hb + rr + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + 4 * v - 3;
+          // piece v holds input columns 4v - 3 .. 4v (LDS columns 4v .. 4v + 3, all
+          // inside the channel's pitch; the ones outside 0 .. XC-1 are never read)
+          float* d = lds + ((hb + rr + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + 4 * v;
           const bool ok = (xm >> i) & 1u;
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if ((unsigned)(4 * v - 3 + u) < (unsigned)Cf::XC) d[u] = ok ? px4[i][u] : 0.f;
+          for (int u = 0; u < 4; ++u) d[u] = ok ? px4[i][u] : 0.f;
         }
       }
     } else {
@@ -393,7 +399,7 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
         const int rr = e / (32 * Cf::XC), rem = e - rr * (32 * Cf::XC);
         const int c = rem / Cf::XC, j = rem - c * Cf::XC;
         if (e < Cf::XNEW)
-          lds[((hb + rr + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + j] =
+          lds[((hb + rr + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + Cf::X0 + j] =
               ((xm >> i) & 1u) ? px[i] : 0.f;
       }
     }
@@ -439,7 +445,7 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
     const int h = S * r0 - 1 + rr, w = ic0 + j;
     const bool ok = (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
     const float v = xb[ok ? c * g.HW + h * g.W + w : 0];
-    lds[((h + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + j] = ok ? v : 0.f;
+    lds[((h + Cf::NSLOT) % Cf::NSLOT) * Cf::SLOT + c * Cf::CS + Cf::X0 + j] = ok ? v : 0.f;
   }
   fetch_x(r0);
   fetch_z(r0);
@@ -459,7 +465,7 @@ __global__ __launch_bounds__(kDw3Threads, 1) void conv_dw3_rows(
 
   // this wave's half of the row: steps [kq*KH, min(KS, kq*KH + KH))
   const int abase0 = Cf::Z0 + (32 * oh + (lane & 31)) * Cf::OS + (lane >> 5) + 2 * Cf::KH * kq;
-  const int bbase = (lane & 31) * Cf::CS + S * (lane >> 5) + 2 * S * Cf::KH * kq;
+  const int bbase = (lane & 31) * Cf::CS + Cf::X0 + S * (lane >> 5) + 2 * S * Cf::KH * kq;
   // One barrier per row: the rows and the dz buffer that arrive for row r+1 go
   // to slots (buffer) that row r does not read.  When dz is formed here (three
   // tensors' rows to stage and transform per row), each wave stages its part of
@@ -1478,7 +1484,7 @@ constexpr int kFrThreads = 256, kFrPitch = 133, kFrMaxW = 120;
 // is the activation (kFzAny: the run-time src.act), so the per-element
 // derivative compiles to straight-line code for the common ones.
 template <int CI, bool ACC, int FZ>
-__global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_rows(
+__global__ __launch_bounds__(kFrThreads, 2) void conv_first_rows(
     ConvGeom g, const float* __restrict__ x, const float* __restrict__ wt,
     const float* __restrict__ dz, float* __restrict__ dwpart, float* __restrict__ dx,
     int nstrips, int sw, int nruns, int rlen, DzSource src) {
@@ -1507,6 +1513,11 @@ __global__ __launch_bounds__(kFrThreads, FZ != kFzOff ? 2 : 3) void conv_first_r
   // channels >= OC are never staged and stay zero
   for (int e = tid; e < 2 * 32 * P; e += kFrThreads) (&Zs[0][0])[e] = 0.f;
   if (tid < 64) Z0[tid] = 0.f;
+  // x columns 128 .. P-1 are never staged but are read as the dW operand of the
+  // masked pixels past the strip (times a zero dz): they must hold zeros, not
+  // whatever the LDS held before (0 x NaN is NaN)
+  for (int e = tid; e < 4 * CI * (P - 128); e += kFrThreads)
+    Xs[(e / (P - 128)) * P + 128 + e % (P - 128)] = 0.f;
 
   // ---- staging: thread slot k takes 16-byte group e = tid + 256k of a row
   // (dz: channel e / 32, group e % 32; x: the same with CI channels).  Groups
