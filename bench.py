@@ -286,6 +286,9 @@ def kernel_work(runner, call, kernel):
         return 4.0 * macs, 4.0 * (2 * in_e + zin * out_e + 2 * w_e)
     if role == "dW" and e["dw_forms_dz"] and "dz formed" in kernel:
         return 2.0 * macs, 4.0 * (in_e + (nread + 1) * out_e + w_e)
+    if role == "dX" and "sums below" in kernel:
+        # also reads the block below's y and x_hat (dx's shape) for its act/BN sums
+        return 2.0 * macs, 4.0 * (3 * in_e + out_e + w_e)
     return 2.0 * macs, 4.0 * (in_e + out_e + w_e)
 
 

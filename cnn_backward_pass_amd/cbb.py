@@ -53,6 +53,13 @@ class ConvDesc(ctypes.Structure):
         return (self.in_w + 2 * self.pad - self._span()) // self.stride + 1
 
 
+class BlockOpts(ctypes.Structure):
+    """cbb_block_opts."""
+    _fields_ = [("sums", ctypes.c_void_p), ("below_sums", ctypes.c_void_p),
+                ("below_y", ctypes.c_void_p), ("below_x_norm", ctypes.c_void_p),
+                ("below_act", ctypes.c_int32), ("below_slope", ctypes.c_float)]
+
+
 def conv_desc(batch, in_c, in_h, in_w, out_c, ksize, stride, pad, batch_normalize, act,
               slope=0.1, bn_eps=1e-5, groups=1, dilation=1) -> ConvDesc:
     a = ACT[act] if isinstance(act, str) else int(act)
@@ -69,6 +76,11 @@ _SIGS = {
     "cbb_conv_block_workspace_size": ([ctypes.POINTER(ConvDesc), ctypes.POINTER(_sz)], _i32),
     "cbb_conv_block_backward": ([ctypes.POINTER(ConvDesc)] + [_P] * 12 + [_i32, _P, _sz, _P], _i32),
     "cbb_conv_block_backward_noalloc": ([ctypes.POINTER(ConvDesc)] + [_P] * 12 + [_i32, _P], _i32),
+    "cbb_conv_block_backward_ex": ([ctypes.POINTER(ConvDesc)] + [_P] * 12 +
+                                   [_i32, ctypes.POINTER(BlockOpts), _P, _sz, _P], _i32),
+    "cbb_conv_backward_data_ex": ([ctypes.POINTER(ConvDesc), _P, _P, _P, _i32,
+                                   ctypes.POINTER(BlockOpts), _P, _sz, _P], _i32),
+    "cbb_conv_fuses_below_sums": ([ctypes.POINTER(ConvDesc)], _i32),
     "cbb_conv_act_bn_backward": ([ctypes.POINTER(ConvDesc)] + [_P] * 8 + [_P, _sz, _P], _i32),
     "cbb_conv_backward_weights": ([ctypes.POINTER(ConvDesc), _P, _P, _P, _P, _sz, _P], _i32),
     "cbb_conv_backward_data": ([ctypes.POINTER(ConvDesc), _P, _P, _P, _i32, _P, _sz, _P], _i32),
@@ -227,6 +239,64 @@ def conv_block_backward(desc: ConvDesc, x, w, y, x_norm, var, gamma, delta, dz, 
         _ptr(delta, name="delta"), _ptr(dz, name="dz"), _ptr(dw, name="dw"),
         _ptr(db, name="db"), _ptr(dgamma, name="dgamma"), _ptr(dx, name="dx"),
         int(dx_accumulate), wsp, wsb, _stream(stream)))
+
+
+def _block_opts(fn: str, desc: ConvDesc, sums, below) -> BlockOpts:
+    """cbb_block_opts from `sums` (float32 [2*O]) and `below` (dict: "sums" [2*C] out,
+    "y" (None under linear) and "x_norm" [N,C,H,W] of the block below, "act", "slope")."""
+    xs = (desc.batch, desc.in_c, desc.in_h, desc.in_w)
+    opts = BlockOpts()
+    if sums is not None:
+        _sized(fn, sums=(sums, 2 * desc.out_c))
+        opts.sums = _ptr(sums, name="sums").value
+    if below is not None:
+        by, bxn = below.get("y"), below.get("x_norm")
+        shape = lambda t: xs if t is None or t.dim() == 4 else int(torch.Size(xs).numel())
+        _sized(fn, below_sums=(below["sums"], 2 * desc.in_c), below_y=(by, shape(by)),
+               below_x_norm=(bxn, shape(bxn)))
+        opts.below_sums = _ptr(below["sums"], name="below.sums").value
+        opts.below_y = None if by is None else _ptr(by, name="below.y").value
+        opts.below_x_norm = None if bxn is None else _ptr(bxn, name="below.x_norm").value
+        act = below["act"]
+        opts.below_act = ACT[act] if isinstance(act, str) else int(act)
+        opts.below_slope = float(below.get("slope", 0.1))
+    return opts
+
+
+def conv_block_backward_ex(desc: ConvDesc, x, w, y, x_norm, var, gamma, delta, dz, dw, db, dgamma,
+                           dx, dx_accumulate: bool = False, sums=None, below=None, workspace=None,
+                           stream=None) -> None:
+    """conv_block_backward with this block's act/BN sums given (`sums`: (sum g,
+    sum g*x_norm) per channel from the call of the block above) and/or the act/BN sums of
+    the block below produced on the way (`below`, see _block_opts)."""
+    _conv_sizes("conv_block_backward_ex", desc, x=x, w=w, y=y, x_norm=x_norm, var=var,
+                gamma=gamma, delta=delta, dz=dz, dw=dw, db=db, dgamma=dgamma, dx=dx)
+    opts = _block_opts("conv_block_backward_ex", desc, sums, below)
+    wsp, wsb = _ws(workspace)
+    _check("cbb_conv_block_backward_ex", lib().cbb_conv_block_backward_ex(
+        ctypes.byref(desc), _ptr(x, name="x"), _ptr(w, name="w"), _ptr(y, name="y"),
+        _ptr(x_norm, name="x_norm"), _ptr(var, name="var"), _ptr(gamma, name="gamma"),
+        _ptr(delta, name="delta"), _ptr(dz, name="dz"), _ptr(dw, name="dw"),
+        _ptr(db, name="db"), _ptr(dgamma, name="dgamma"), _ptr(dx, name="dx"),
+        int(dx_accumulate), ctypes.byref(opts), wsp, wsb, _stream(stream)))
+
+
+def conv_backward_data_ex(desc: ConvDesc, w, dz, dx, dx_accumulate: bool = False, below=None,
+                          workspace=None, stream=None) -> None:
+    """conv_backward_data producing the act/BN sums of the block below on the way."""
+    _conv_sizes("conv_backward_data_ex", desc, w=w, dz=dz, dx=dx)
+    opts = _block_opts("conv_backward_data_ex", desc, None, below)
+    wsp, wsb = _ws(workspace)
+    _check("cbb_conv_backward_data_ex", lib().cbb_conv_backward_data_ex(
+        ctypes.byref(desc), _ptr(w, name="w"), _ptr(dz, name="dz"), _ptr(dx, name="dx"),
+        int(dx_accumulate), ctypes.byref(opts), wsp, wsb, _stream(stream)))
+
+
+def conv_fuses_below_sums(desc: ConvDesc) -> bool:
+    rc = lib().cbb_conv_fuses_below_sums(ctypes.byref(desc))
+    if rc < 0:
+        _check("cbb_conv_fuses_below_sums", rc)
+    return rc == 1
 
 
 def conv_block_backward_noalloc(desc: ConvDesc, x, w, y, x_norm, var, gamma, delta, dz, dw, db,

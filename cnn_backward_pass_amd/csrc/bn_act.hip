@@ -345,6 +345,23 @@ __global__ __launch_bounds__(kThreads) void actbn_fold(const float2* __restrict_
   }
 }
 
+// sums[c] = the channel's partials folded in the fixed order of actbn_apply.
+__global__ __launch_bounds__(kThreads) void bn_sums_fold(const float2* __restrict__ part, int nseg,
+                                                         float2* __restrict__ sums) {
+  __shared__ float red[4];
+  const int c = blockIdx.x;
+  const float2 v = fold_partials(part, c, nseg, red);
+  if (threadIdx.x == 0) sums[c] = v;
+}
+
+// Given sums as partials of nseg segments: segment 0 holds the sum, the rest zero.
+__global__ __launch_bounds__(kThreads) void bn_sums_expand(const float2* __restrict__ sums,
+                                                           float2* __restrict__ part, int nseg) {
+  const int c = blockIdx.x;
+  for (int j = threadIdx.x; j < nseg; j += kThreads)
+    part[(int64_t)c * nseg + j] = j == 0 ? sums[c] : make_float2(0.f, 0.f);
+}
+
 // Pass 2 when dz is formed later by its consumer: one work-group per channel
 // folds the sums (the order actbn_apply uses), adds them into dgamma / dbeta (or
 // db) and writes the channel's map dz = a*g + b + cc*x_norm as coef[c], coef[C+c],
@@ -621,8 +638,26 @@ static void launch_actbn_t(const SegGeom& s, unsigned blocks, int act, const flo
                            const float* y, const float* xn, float slope, const float* var,
                            const float* gamma, float eps, float* dz, float* dgamma,
                            float* dbeta_or_db, float2* part, int write_dz, float* coef,
-                           hipStream_t st) {
+                           const float2* sums, hipStream_t st) {
   const float* xr = BN != kBnNone ? xn : nullptr;
+  if (sums) {
+    // batch statistics whose sums another call produced: no reduction pass
+    if constexpr (BN == kBnBatch) {
+      if (coef) {
+        actbn_coef<<<(unsigned)s.C, kThreads, 0, st>>>(sums, 1, s.M, s.C, BN, var, gamma, eps,
+                                                      dgamma, dbeta_or_db, coef);
+        note_launch("actbn_coef", st);
+        return;
+      }
+      bn_sums_expand<<<(unsigned)s.C, kThreads, 0, st>>>(sums, part, s.nseg);
+      note_launch("bn_sums_expand", st);
+      actbn_apply<VEC, ACT, BN><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, slope, act, part,
+                                                             var, gamma, eps, dz, dgamma,
+                                                             dbeta_or_db, write_dz);
+      note_launch("actbn_apply", st);
+    }
+    return;
+  }
   // A channel that one work-group holds in registers takes one pass for any mode:
   // sums, then dz (or the map for a kernel that forms dz itself).
   const int64_t q = (int64_t)s.N * s.HW / 4;
@@ -676,10 +711,10 @@ static void launch_actbn_a(const SegGeom& s, unsigned blocks, int act, int bn, c
                            const float* y, const float* xn, float slope, const float* var,
                            const float* gamma, float eps, float* dz, float* dgamma,
                            float* dbeta_or_db, float2* part, int write_dz, float* coef,
-                           hipStream_t st) {
+                           const float2* sums, hipStream_t st) {
 #define CBB_ACTBN(B)                                                                        \
   launch_actbn_t<VEC, ACT, B>(s, blocks, act, delta, y, xn, slope, var, gamma, eps, dz, dgamma, \
-                              dbeta_or_db, part, write_dz, coef, st)
+                              dbeta_or_db, part, write_dz, coef, sums, st)
   if (bn == kBnFixed)
     CBB_ACTBN(kBnFixed);
   else if (bn == kBnBatch)
@@ -694,10 +729,10 @@ static void launch_actbn_v(const SegGeom& s, unsigned blocks, int act, int bn, c
                            const float* y, const float* xn, float slope, const float* var,
                            const float* gamma, float eps, float* dz, float* dgamma,
                            float* dbeta_or_db, float2* part, int write_dz, float* coef,
-                           hipStream_t st) {
+                           const float2* sums, hipStream_t st) {
 #define CBB_ACTBN(A)                                                                          \
   launch_actbn_a<VEC, A>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma, \
-                         dbeta_or_db, part, write_dz, coef, st)
+                         dbeta_or_db, part, write_dz, coef, sums, st)
   switch (act) {
     case CBB_ACT_LINEAR: CBB_ACTBN(CBB_ACT_LINEAR); break;
     case CBB_ACT_LEAKY: CBB_ACTBN(CBB_ACT_LEAKY); break;
@@ -714,20 +749,59 @@ static void launch_actbn_v(const SegGeom& s, unsigned blocks, int act, int bn, c
 int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, const float* xn,
                  int act, float slope, const float* var, const float* gamma, float eps, int bn,
                  float* dz, float* dgamma, float* dbeta_or_db, void* ws, hipStream_t st,
-                 float* coef) {
+                 float* coef, const float2* sums) {
   const SegGeom s = plan_seg(N, C, HW);
   float2* part = reinterpret_cast<float2*>(ws);
   const bool vec = (HW % 4 == 0) && aligned16(delta) && (!y || aligned16(y)) &&
                    (!xn || aligned16(xn)) && (!dz || aligned16(dz));
   const unsigned blocks = (unsigned)((int64_t)C * s.nseg);
   const int write_dz = bn || act != CBB_ACT_LINEAR;
+  if (sums && bn != kBnBatch) return CBB_EINVAL;
   if (vec)
     launch_actbn_v<true>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma,
-                         dbeta_or_db, part, write_dz, coef, st);
+                         dbeta_or_db, part, write_dz, coef, sums, st);
   else
     launch_actbn_v<false>(s, blocks, act, bn, delta, y, xn, slope, var, gamma, eps, dz, dgamma,
-                          dbeta_or_db, part, write_dz, coef, st);
+                          dbeta_or_db, part, write_dz, coef, sums, st);
   return check_error("actbn_reduce/actbn_apply");
+}
+
+size_t bn_sums_workspace(int N, int C, int64_t HW) { return actbn_workspace(N, C, HW); }
+
+template <bool VEC, int ACT>
+static void launch_bn_sums_t(const SegGeom& s, unsigned blocks, int act, const float* delta,
+                             const float* y, const float* xn, float slope, float2* part,
+                             hipStream_t st) {
+  actbn_reduce<VEC, ACT, kBnBatch><<<blocks, kThreads, 0, st>>>(s, delta, y, xn, slope, act,
+                                                                nullptr, nullptr, 0.f, nullptr,
+                                                                part);
+  note_launch("actbn_reduce", st);
+}
+
+int launch_bn_sums(int N, int C, int64_t HW, const float* delta, const float* y, const float* xn,
+                   int act, float slope, void* ws, float2* sums, hipStream_t st) {
+  const SegGeom s = plan_seg(N, C, HW);
+  float2* part = reinterpret_cast<float2*>(ws);
+  const bool vec = (HW % 4 == 0) && aligned16(delta) && (!y || aligned16(y)) && aligned16(xn);
+  const unsigned blocks = (unsigned)((int64_t)C * s.nseg);
+#define CBB_SUMS(V, A) launch_bn_sums_t<V, A>(s, blocks, act, delta, y, xn, slope, part, st)
+  if (vec) {
+    if (act == CBB_ACT_LEAKY) CBB_SUMS(true, CBB_ACT_LEAKY);
+    else if (act == CBB_ACT_LINEAR) CBB_SUMS(true, CBB_ACT_LINEAR);
+    else CBB_SUMS(true, kActAny);
+  } else {
+    if (act == CBB_ACT_LEAKY) CBB_SUMS(false, CBB_ACT_LEAKY);
+    else if (act == CBB_ACT_LINEAR) CBB_SUMS(false, CBB_ACT_LINEAR);
+    else CBB_SUMS(false, kActAny);
+  }
+#undef CBB_SUMS
+  return launch_bn_sums_fold(part, C, s.nseg, sums, st);
+}
+
+int launch_bn_sums_fold(const float2* part, int C, int nseg, float2* sums, hipStream_t st) {
+  bn_sums_fold<<<(unsigned)C, kThreads, 0, st>>>(part, nseg, sums);
+  note_launch("bn_sums_fold", st);
+  return check_error("bn_sums_fold");
 }
 
 // Forward after the convolution (see bnf_apply).  bn: 0 none (z + bias already in y),

@@ -17,7 +17,7 @@ inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 struct ConvPlan {
   int64_t oh, ow;
-  size_t part_bytes, dw_bytes, total;
+  size_t part_bytes, dw_bytes, below_bytes, total;
 };
 
 int check_desc(const cbb_conv_desc* d, ConvPlan* plan) {
@@ -55,9 +55,41 @@ int check_desc(const cbb_conv_desc* d, ConvPlan* plan) {
     // and share the second region
     plan->dw_bytes = align_up(
         std::max({conv_dw_workspace(g), conv_dx_workspace(g), conv_fused_workspace(g)}), kAlign);
-    plan->total = plan->part_bytes + plan->dw_bytes;
+    // partials of the act/BN sums of the block below (cbb_conv_block_backward_ex):
+    // those of the stride-2 input-gradient kernel, or of a reduction pass over dx
+    plan->below_bytes = align_up(
+        std::max(bn_sums_workspace(d->batch, d->in_c, (int64_t)d->in_h * d->in_w),
+                 (size_t)kDxS2pGroups * d->in_c * sizeof(float2)),
+        kAlign);
+    plan->total = plan->part_bytes + plan->dw_bytes + plan->below_bytes;
   }
   return CBB_OK;
+}
+
+// The rules of cbb_block_opts (see include/cbb.h).
+int check_block_opts(const cbb_conv_desc* d, const float* dx, const cbb_block_opts* o) {
+  if (!o) return CBB_OK;
+  if (o->sums && d->batch_normalize != CBB_BN_BATCH) return CBB_EINVAL;
+  if (o->below_sums) {
+    if (!dx || !o->below_x_norm) return CBB_EINVAL;
+    if (o->below_act < CBB_ACT_LINEAR || o->below_act > CBB_ACT_LOGGY) return CBB_EINVAL;
+    if (o->below_act != CBB_ACT_LINEAR && !o->below_y) return CBB_EINVAL;
+    if (o->below_sums == o->sums) return CBB_EINVAL;
+  } else if (o->below_y || o->below_x_norm) {
+    return CBB_EINVAL;   // the block below's tensors without a place for its sums
+  }
+  return CBB_OK;
+}
+
+// The block below's act/BN sums into opts->below_sums: folded from the partials
+// the input-gradient kernel wrote (bb->nseg > 0), else a reduction pass over dx.
+int below_sums(const cbb_conv_desc* d, const float* dx, const cbb_block_opts* o,
+               const BnBelow* bb, char* ws, hipStream_t st) {
+  float2* out = reinterpret_cast<float2*>(o->below_sums);
+  if (bb && bb->nseg > 0) return launch_bn_sums_fold(bb->part, d->in_c, bb->nseg, out, st);
+  return launch_bn_sums(d->batch, d->in_c, (int64_t)d->in_h * d->in_w, dx,
+                        o->below_act == CBB_ACT_LINEAR ? nullptr : o->below_y, o->below_x_norm,
+                        o->below_act, o->below_slope, ws, out, st);
 }
 
 // dW and (when dx is given) dX from dz: one fused kernel for the layers it
@@ -142,11 +174,26 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
                             const float* gamma, const float* delta, float* dz, float* dw,
                             float* db, float* dgamma, float* dx, int dx_accumulate,
                             void* workspace, size_t workspace_bytes, void* stream) {
+  return cbb_conv_block_backward_ex(desc, x, w, y, x_norm, var, gamma, delta, dz, dw, db, dgamma,
+                                    dx, dx_accumulate, nullptr, workspace, workspace_bytes,
+                                    stream);
+}
+
+int cbb_conv_block_backward_ex(const cbb_conv_desc* desc, const float* x, const float* w,
+                               const float* y, const float* x_norm, const float* var,
+                               const float* gamma, const float* delta, float* dz, float* dw,
+                               float* db, float* dgamma, float* dx, int dx_accumulate,
+                               const cbb_block_opts* opts, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   ConvPlan p;
   int rc = check_block_backward(desc, x, w, y, x_norm, var, gamma, delta, dz, dw, db, dgamma, dx,
                                 dx_accumulate);
   if (rc) return rc;
+  rc = check_block_opts(desc, dx, opts);
+  if (rc) return rc;
   check_desc(desc, &p);
+  const float2* sums_in = opts ? reinterpret_cast<const float2*>(opts->sums) : nullptr;
+  const bool below = opts && opts->below_sums;
   const int bn = desc->batch_normalize, act = desc->act;
   const bool passthrough = act == CBB_ACT_LINEAR && !bn;  // dz is delta itself
   const ConvGeom g = make_geom(*desc);
@@ -160,12 +207,14 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
     float* coef = reinterpret_cast<float*>(
         ws + align_up(actbn_workspace(desc->batch, desc->out_c, p.oh * p.ow), kAlign));
     rc = launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
-                      var, gamma, desc->bn_eps, bn, nullptr, dgamma, db, ws, st, coef);
+                      var, gamma, desc->bn_eps, bn, nullptr, dgamma, db, ws, st, coef, sums_in);
     if (rc) return rc;
     const DzSource src{act == CBB_ACT_LINEAR ? nullptr : y,
                        bn == CBB_BN_BATCH ? x_norm : nullptr, coef, act, desc->slope};
-    return launch_conv_fused_dwdx(g, x, w, delta, dw, dx, dx_accumulate,
-                                  reinterpret_cast<float*>(ws + p.part_bytes), st, &src);
+    rc = launch_conv_fused_dwdx(g, x, w, delta, dw, dx, dx_accumulate,
+                                reinterpret_cast<float*>(ws + p.part_bytes), st, &src);
+    if (rc || !below) return rc;
+    return below_sums(desc, dx, opts, nullptr, ws + p.part_bytes + p.dw_bytes, st);
   }
   // Batch statistics with dz stored: on the layers the 3x3 row-streaming dW kernel
   // takes, that kernel forms dz from delta, y and x_norm and writes it for the
@@ -176,20 +225,36 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
     float* coef = reinterpret_cast<float*>(
         ws + align_up(actbn_workspace(desc->batch, desc->out_c, p.oh * p.ow), kAlign));
     rc = launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
-                      var, gamma, desc->bn_eps, bn, nullptr, dgamma, db, ws, st, coef);
+                      var, gamma, desc->bn_eps, bn, nullptr, dgamma, db, ws, st, coef, sums_in);
     if (rc) return rc;
     const DzSource src{act == CBB_ACT_LINEAR ? nullptr : y, x_norm, coef, act, desc->slope};
     float* ws2 = reinterpret_cast<float*>(ws + p.part_bytes);
     rc = launch_conv_dw_forming_dz(g, x, delta, src, dz, dw, ws2, st);
     if (rc || !dx) return rc;
-    return launch_conv_dx(g, w, dz, dx, dx_accumulate, ws2, st);
+    char* wsb = ws + p.part_bytes + p.dw_bytes;
+    BnBelow bb{opts && below ? opts->below_y : nullptr, below ? opts->below_x_norm : nullptr,
+               below ? opts->below_act : 0, below ? opts->below_slope : 0.f,
+               reinterpret_cast<float2*>(wsb), 0};
+    rc = launch_conv_dx(g, w, dz, dx, dx_accumulate, ws2, st, below ? &bb : nullptr);
+    if (rc || !below) return rc;
+    return below_sums(desc, dx, opts, &bb, wsb, st);
   }
   const float* dz_eff = passthrough ? delta : dz;
   rc = launch_actbn(desc->batch, desc->out_c, p.oh * p.ow, delta, y, x_norm, act, desc->slope,
-                    var, gamma, desc->bn_eps, bn, passthrough ? nullptr : dz, dgamma, db, ws, st);
+                    var, gamma, desc->bn_eps, bn, passthrough ? nullptr : dz, dgamma, db, ws, st,
+                    nullptr, sums_in);
   if (rc) return rc;
-  return launch_weights_data(g, x, w, dz_eff, dw, dx, dx_accumulate,
-                             reinterpret_cast<float*>(ws + p.part_bytes), st);
+  float* ws2 = reinterpret_cast<float*>(ws + p.part_bytes);
+  if (!below) return launch_weights_data(g, x, w, dz_eff, dw, dx, dx_accumulate, ws2, st);
+  // the sums below go with the input gradient: the two gradient kernels in turn
+  rc = launch_conv_dw(g, x, dz_eff, dw, ws2, st);
+  if (rc) return rc;
+  char* wsb = ws + p.part_bytes + p.dw_bytes;
+  BnBelow bb{opts->below_y, opts->below_x_norm, opts->below_act, opts->below_slope,
+             reinterpret_cast<float2*>(wsb), 0};
+  rc = launch_conv_dx(g, w, dz_eff, dx, dx_accumulate, ws2, st, &bb);
+  if (rc) return rc;
+  return below_sums(desc, dx, opts, &bb, wsb, st);
 }
 
 int cbb_conv_block_forward_workspace_size(const cbb_conv_desc* desc, size_t* bytes) {
@@ -305,6 +370,38 @@ int cbb_conv_backward_data(const cbb_conv_desc* desc, const float* w, const floa
   char* ws = static_cast<char*>(workspace);
   return launch_conv_dx(make_geom(*desc), w, dz, dx, dx_accumulate,
                         reinterpret_cast<float*>(ws ? ws + p.part_bytes : nullptr), S(stream));
+}
+
+int cbb_conv_backward_data_ex(const cbb_conv_desc* desc, const float* w, const float* dz,
+                              float* dx, int dx_accumulate, const cbb_block_opts* opts,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  ConvPlan p;
+  int rc = check_desc(desc, &p);
+  if (rc) return rc;
+  if (!w || !dz || !dx) return CBB_EINVAL;
+  if (dx_accumulate != 0 && dx_accumulate != 1) return CBB_EINVAL;
+  if (opts && opts->sums) return CBB_EINVAL;   // no act/BN stage in this call
+  rc = check_block_opts(desc, dx, opts);
+  if (rc) return rc;
+  if (p.total > 0 && (!workspace || workspace_bytes < p.total)) return CBB_EWORKSPACE;
+  if (workspace && ((uintptr_t)workspace % kAlign)) return CBB_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const bool below = opts && opts->below_sums;
+  char* wsb = ws + p.part_bytes + p.dw_bytes;
+  BnBelow bb{below ? opts->below_y : nullptr, below ? opts->below_x_norm : nullptr,
+             below ? opts->below_act : 0, below ? opts->below_slope : 0.f,
+             reinterpret_cast<float2*>(wsb), 0};
+  rc = launch_conv_dx(make_geom(*desc), w, dz, dx, dx_accumulate,
+                      reinterpret_cast<float*>(ws + p.part_bytes), S(stream),
+                      below ? &bb : nullptr);
+  if (rc || !below) return rc;
+  return below_sums(desc, dx, opts, &bb, wsb, S(stream));
+}
+
+int cbb_conv_fuses_below_sums(const cbb_conv_desc* desc) {
+  const int rc = check_desc(desc, nullptr);
+  if (rc) return rc;
+  return conv_dx_sums_below_ok(make_geom(*desc)) ? 1 : 0;
 }
 
 int cbb_act_backward(int act, float slope, const float* y, const float* delta, float* g,

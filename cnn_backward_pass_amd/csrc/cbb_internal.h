@@ -296,6 +296,22 @@ size_t conv_fused_workspace(const ConvGeom& g);
 // g = delta * act'(y) and the per-channel map of the BN backward,
 //   dz[c] = coef[c] * g + coef[C + c] + coef[2C + c] * x_norm
 // (y NULL: act linear; xn NULL: the third term is absent).
+// The act/BN sums of the block below a convolution, added up by the kernel that
+// writes this convolution's input gradient (the delta of that block): that
+// block's y and x_norm (dx's shape; y may stand in for nothing under LINEAR) and
+// activation.  The kernel writes partials part[c][nseg]; the launcher sets nseg
+// (0: the route taken could not add them up, the caller reduces dx instead).
+// Work-groups of the persistent stride-2 input-gradient kernel (two per CU), which
+// also bounds the partials it writes for the block below.
+constexpr int kDxS2pGroups = 2 * 256;
+struct BnBelow {
+  const float* y;
+  const float* xn;
+  int act;
+  float slope;
+  float2* part;
+  int nseg;
+};
 struct DzSource {
   const float* y;
   const float* xn;
@@ -311,12 +327,22 @@ int launch_conv_dw_forming_dz(const ConvGeom& g, const float* x, const float* de
                               const DzSource& src, float* dzout, float* dw, float* ws,
                               hipStream_t st);
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
-                   float* ws, hipStream_t st);
+                   float* ws, hipStream_t st, BnBelow* below = nullptr);
+// Whether launch_conv_dx adds up the block below's act/BN sums in its kernel (given
+// 16-byte aligned tensors at run time).
+bool conv_dx_sums_below_ok(const ConvGeom& g);
 size_t actbn_workspace(int N, int C, int64_t HW);
 int launch_actbn(int N, int C, int64_t HW, const float* delta, const float* y, const float* xn,
                  int act, float slope, const float* var, const float* gamma, float eps, int bn,
                  float* dz, float* dgamma, float* dbeta_or_db, void* ws, hipStream_t st,
-                 float* coef = nullptr);
+                 float* coef = nullptr, const float2* sums = nullptr);
+// sums[c] = (sum g, sum g*x_norm) of a batch-statistics act/BN stage over its channel
+// c (g = delta * act'(y)): a reduction pass into the partials in ws, then a fixed-
+// order fold; launch_bn_sums_fold folds partials part[c][nseg] another kernel wrote.
+size_t bn_sums_workspace(int N, int C, int64_t HW);
+int launch_bn_sums(int N, int C, int64_t HW, const float* delta, const float* y, const float* xn,
+                   int act, float slope, void* ws, float2* sums, hipStream_t st);
+int launch_bn_sums_fold(const float2* part, int C, int nseg, float2* sums, hipStream_t st);
 int launch_act_backward(int act, float slope, const float* y, const float* delta, float* g,
                         int64_t count, hipStream_t st);
 int launch_bn_act_forward(int N, int C, int64_t HW, int bn, float eps, int act, float slope,

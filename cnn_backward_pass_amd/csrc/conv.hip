@@ -1111,14 +1111,27 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
 // chunk's copies can count past them (memory operations complete in order).
 __device__ float g_dx3_sink[4 * kThreads];
 
-template <int NCH>
+//
+// BA != kFzOff (the activation of the block below, kFzAny: ba.act at run time;
+// one 32-channel tile column, 16-byte rows): dx is the delta of a block below
+// with batch statistics, and the epilogue also adds up that block's act/BN sums
+// sum g and sum g*x_norm, g = dx * act'(y), over the elements it stores: the y
+// and x_norm pieces at a pass's store positions are loaded before the pass's
+// regroup, each thread keeps the sums of its 16 (pass, piece) channel slots over
+// all its tiles, and at the end the work-group adds them up (a fixed shuffle tree
+// per wave, then the two waves of a channel in order) into ba.part[c][blockIdx.x].
+template <int NCH, int BA = kFzOff>
 __global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
                                                            const float* __restrict__ wt,
                                                            const float* __restrict__ dz,
                                                            float* __restrict__ dx, int accumulate,
                                                            int ntiles, int tiles_per_img,
-                                                           int tiles_w) {
+                                                           int tiles_w, BnBelow ba) {
   using C = Dx3Cfg<2, 1, 1>;
+  constexpr bool sums = BA != kFzOff;
+  float ss[sums ? 16 : 1][2];
+#pragma unroll
+  for (int j = 0; j < (sums ? 16 : 1); ++j) ss[j][0] = ss[j][1] = 0.f;
   static_assert(NCH % 2 == 0, "chunks alternate between the two buffers within a tile");
   constexpr int OCB = C::OCB, BMC = C::BMC, NFRAG = C::NFRAG;   // 16, 32, 4
   constexpr int ZC2 = 36, ZR2 = C::ZR2, ZP = ZR2 * ZC2, ZFL = OCB * ZP;
@@ -1246,6 +1259,23 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
   auto epilogue = [&](const Tile& ct, float* buf) {
 #pragma unroll
     for (int pass = 0; pass < 4; ++pass) {
+      // the block below's y and x_norm at this pass's store positions, in flight
+      // during the regroup
+      float4 yv[sums ? NV : 1], xv[sums ? NV : 1];
+      if constexpr (sums) {
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+          const int u = tid + kThreads * k;
+          const int il = u / (RR * TP / 4), rem = u - il * (RR * TP / 4);
+          const int rr = rem / (TP / 4), c4 = rem - rr * (TP / 4);
+          const int h = ct.h0 + rr, w = ct.w0 + 4 * c4;
+          const int64_t o = h < g.H && w + 3 < g.W
+                                ? (((int64_t)ct.b * g.C + ct.i0 + 8 * pass + il) * g.H + h) * g.W + w
+                                : 0;
+          yv[k] = *reinterpret_cast<const float4*>(ba.y + o);
+          xv[k] = *reinterpret_cast<const float4*>(ba.xn + o);
+        }
+      }
       __syncthreads();   // the buffer is free (matrix work or previous pass done)
 #pragma unroll
       for (int f = 0; f < NFRAG; ++f) {
@@ -1277,6 +1307,17 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
           v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
         }
         *d = v;
+        if constexpr (sums) {
+          if (whole) {
+            const int act = BA == kFzAny ? ba.act : BA;
+            const float g0 = v.x * act_grad(act, ba.slope, yv[k].x);
+            const float g1 = v.y * act_grad(act, ba.slope, yv[k].y);
+            const float g2 = v.z * act_grad(act, ba.slope, yv[k].z);
+            const float g3 = v.w * act_grad(act, ba.slope, yv[k].w);
+            ss[4 * pass + k][0] += (g0 + g1) + (g2 + g3);
+            ss[4 * pass + k][1] += (g0 * xv[k].x + g1 * xv[k].y) + (g2 * xv[k].z + g3 * xv[k].w);
+          }
+        }
       }
     }
   };
@@ -1324,6 +1365,35 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
     cur = nxt;
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // nothing in flight at exit
+  if constexpr (sums) {
+    // thread tid holds channel 8 pass + 2 k + (tid >> 7) in slot 4 pass + k: waves 0-1
+    // the even channels, waves 2-3 the odd ones
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float v = ss[j][e];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+        ss[j][e] = v;
+      }
+    __syncthreads();   // every wave is past its last use of the LDS buffers
+    float* red = Z;    // [wave][slot][2]
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        red[(wave * 16 + j) * 2] = ss[j][0];
+        red[(wave * 16 + j) * 2 + 1] = ss[j][1];
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int c = tid >> 1, e = tid & 1, par = c & 1;
+      const int j = 4 * (c >> 3) + ((c & 7) >> 1);
+      const float v = red[((2 * par) * 16 + j) * 2 + e] + red[((2 * par + 1) * 16 + j) * 2 + e];
+      reinterpret_cast<float*>(ba.part + (int64_t)c * gridDim.x + blockIdx.x)[e] = v;
+    }
+  }
 }
 
 // dx[e] (+)= sum over splits s (in order) of ws[s][e].
@@ -2251,6 +2321,13 @@ static DxPlan plan_dx(const ConvGeom& g) {
   return p;
 }
 
+bool conv_dx_sums_below_ok(const ConvGeom& g) {
+  if (!dense(g)) return false;
+  const DxPlan p = plan_dx(g);
+  return p.kind == DX_D3S2 && p.ksplits == 1 && (g.OC == 64 || g.OC == 128) && p.ctiles == 1 &&
+         g.OW % 4 == 0 && g.W % 4 == 0;
+}
+
 // 1 when launch_conv_dx runs a specialised kernel for g (tile-direct 3x3 or the 1x1
 // copy ring), not the general one.
 bool conv_dx_specialised(const ConvGeom& g) {
@@ -2290,7 +2367,8 @@ static void launch_dx_mfma(const ConvGeom& g, const DxPlan& p, const float* wt, 
 }
 
 int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* dx, int accumulate,
-                   float* ws, hipStream_t st) {
+                   float* ws, hipStream_t st, BnBelow* below) {
+  if (below) below->nseg = 0;
   if (conv_depthwise(g)) return launch_depthwise_dx(g, wt, dz, dx, accumulate, st);
   if (!dense(g)) {
     // grouped or dilated: the general kernel on the group geometry, all groups in
@@ -2330,14 +2408,30 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
         g, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);
     if (p.kind == DX_D3S2 && z4 && p.ksplits == 1 && (g.OC == 64 || g.OC == 128)) {
       const int ntiles = (int)((int64_t)g.N * p.pixtiles * p.ctiles);
-      const unsigned grid = (unsigned)std::min(ntiles, 2 * 256);
-      if (g.OC == 64)
-        conv_dx3_s2p<4><<<grid, kThreads, 0, st>>>(g, wt, dz, dx, accumulate, ntiles, p.pixtiles,
-                                                   tiles_w);
-      else
-        conv_dx3_s2p<8><<<grid, kThreads, 0, st>>>(g, wt, dz, dx, accumulate, ntiles, p.pixtiles,
-                                                   tiles_w);
-      return check_launch("conv_dx3_s2p", st);
+      const unsigned grid = (unsigned)std::min(ntiles, kDxS2pGroups);
+      // the block below's act/BN sums in the epilogue: one 32-channel tile column
+      // (a work-group's tiles then all hold the same channels) and whole 16-byte rows
+      const bool sums = below && below->part && below->xn && p.ctiles == 1 &&
+                        g.W % 4 == 0 && aligned16(dx) && aligned16(below->xn) &&
+                        (!below->y || aligned16(below->y));
+      BnBelow ba{};
+      if (sums) {
+        ba = *below;
+        if (!ba.y) ba.y = ba.xn;   // LINEAR: y is not read, any valid address will do
+        below->nseg = (int)grid;
+      }
+#define CBB_S2P(NCH_, BA_)                                                                 \
+  conv_dx3_s2p<NCH_, BA_><<<grid, kThreads, 0, st>>>(g, wt, dz, dx, accumulate, ntiles,  \
+                                                     p.pixtiles, tiles_w, ba)
+      if (!sums) {
+        if (g.OC == 64) CBB_S2P(4, kFzOff); else CBB_S2P(8, kFzOff);
+      } else if (ba.act == CBB_ACT_LEAKY) {
+        if (g.OC == 64) CBB_S2P(4, CBB_ACT_LEAKY); else CBB_S2P(8, CBB_ACT_LEAKY);
+      } else {
+        if (g.OC == 64) CBB_S2P(4, kFzAny); else CBB_S2P(8, kFzAny);
+      }
+#undef CBB_S2P
+      return check_launch(sums ? "conv_dx3_s2p (act/BN sums below)" : "conv_dx3_s2p", st);
     }
     if (p.kind == DX_D3S1) {
       if (z4) {

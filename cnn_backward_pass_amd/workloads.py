@@ -78,6 +78,21 @@ class Runner:
             ent["db"] = torch.zeros(c.out_c, dtype=f32, device=device)
             ent["ws_bytes"] = cbb.conv_block_workspace_size(desc)
             self.convs.append(ent)
+        # Consecutive blocks whose upper input-gradient kernel adds up the lower block's
+        # act/BN sums (batch statistics) as it writes that block's delta: the lower
+        # call takes the sums instead of reducing its delta again (cbb_block_opts).
+        for e in self.convs:
+            e["below"] = None
+            e["sums_in"] = None
+        if name not in ("lenet", "darknet53_residual"):   # layer li-1's delta is li's dx
+            for li in range(1, len(self.convs)):
+                lo, c_lo = self.convs[li - 1], wl.convs[li - 1]
+                if c_lo.bn and cbb.conv_fuses_below_sums(
+                        self.convs[li]["desc"]):
+                    lo["sums_in"] = torch.empty(2 * c_lo.out_c, dtype=f32, device=device)
+                    self.convs[li]["below"] = {"sums": lo["sums_in"], "y": lo["y"],
+                                               "x_norm": lo["xhat"], "act": c_lo.act,
+                                               "slope": synth.LEAKY_SLOPE}
         self.workspace = cbb.workspace(max(e["ws_bytes"] for e in self.convs), device)
         self.batch = self.convs[0]["desc"].batch
         n = self.batch
@@ -144,10 +159,11 @@ class Runner:
             target = probe is not None and probe[0] == li and probe[1] == "block"
             if target:
                 probe[2](True, True)
-            cbb.conv_block_backward(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
-                                    e["gamma"], delta, None if form_dz else e["dz"], e["dw"],
-                                    e["db"], e["dgamma"], dx, dx_accumulate, self.workspace,
-                                    stream)
+            cbb.conv_block_backward_ex(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
+                                       e["gamma"], delta, None if form_dz else e["dz"], e["dw"],
+                                       e["db"], e["dgamma"], dx, dx_accumulate,
+                                       sums=e["sums_in"], below=e["below"] if dx is not None
+                                       else None, workspace=self.workspace, stream=stream)
             if target:
                 probe[2](True, False)
             return
@@ -159,16 +175,21 @@ class Runner:
         if e["dw_forms_dz"]:
             # the block without dx (act/BN sums, then dW forming and writing dz), then dX
             mark(stage == "actbn_dW", True)
-            cbb.conv_block_backward(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
-                                    e["gamma"], delta, e["dz"], e["dw"], e["db"], e["dgamma"],
-                                    None, False, self.workspace, stream)
+            cbb.conv_block_backward_ex(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
+                                       e["gamma"], delta, e["dz"], e["dw"], e["db"], e["dgamma"],
+                                       None, False, sums=e["sums_in"], workspace=self.workspace,
+                                       stream=stream)
             mark(stage == "actbn_dW", False)
             if dx is not None:
                 mark(stage == "dX", True)
-                cbb.conv_backward_data(e["desc"], e["w"], e["dz"], dx, dx_accumulate,
-                                       self.workspace, stream)
+                cbb.conv_backward_data_ex(e["desc"], e["w"], e["dz"], dx, dx_accumulate,
+                                          below=e["below"], workspace=self.workspace,
+                                          stream=stream)
                 mark(stage == "dX", False)
             return
+        if e["sums_in"] is not None or e["below"] is not None:
+            raise RuntimeError("a chained layer is timed stage by stage only on the routes "
+                               "above")
         mark(stage == "act_bn", True)
         cbb.conv_act_bn_backward(e["desc"], e["y"], e["xhat"], e["var"], e["gamma"], delta,
                                  e["dz"], e["db"], e["dgamma"], self.workspace, stream)
@@ -221,16 +242,19 @@ class Runner:
         elif stage == "dX":
             if self.name == "lenet" and li == 0:
                 raise ValueError("the first LeNet conv has no input gradient")
-            cbb.conv_backward_data(e["desc"], e["w"], dz, self.d_in[li], False, self.workspace,
-                                   stream)
+            cbb.conv_backward_data_ex(e["desc"], e["w"], dz, self.d_in[li], False,
+                                      below=e["below"], workspace=self.workspace, stream=stream)
         elif stage == "actbn_dW":
-            cbb.conv_block_backward(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
-                                    e["gamma"], delta, e["dz"], e["dw"], e["db"], e["dgamma"],
-                                    None, False, self.workspace, stream)
+            cbb.conv_block_backward_ex(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
+                                       e["gamma"], delta, e["dz"], e["dw"], e["db"], e["dgamma"],
+                                       None, False, sums=e["sums_in"], workspace=self.workspace,
+                                       stream=stream)
         elif stage == "block":
-            cbb.conv_block_backward(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
-                                    e["gamma"], delta, None, e["dw"], e["db"], e["dgamma"],
-                                    self.d_in[li], False, self.workspace, stream)
+            cbb.conv_block_backward_ex(e["desc"], e["x"], e["w"], e["y"], e["xhat"], e["var"],
+                                       e["gamma"], delta, None, e["dw"], e["db"], e["dgamma"],
+                                       self.d_in[li], False, sums=e["sums_in"],
+                                       below=e["below"], workspace=self.workspace,
+                                       stream=stream)
         elif stage == "dWdX":
             cbb.conv_backward_weights_data(e["desc"], e["x"], e["w"], dz, e["dw"], self.d_in[li],
                                            False, self.workspace, stream)

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CBB_ABI_VERSION 1
+#define CBB_ABI_VERSION 2
 
 typedef enum cbb_status {
   CBB_OK = 0,
@@ -194,6 +194,44 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
                             float* db, float* dgamma, float* dx, int dx_accumulate,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/* Two consecutive blocks of a network ([P3] backward_network: layer i's input
+ * gradient is layer i-1's delta; [P1] section 4: a block's act/BN backward first
+ * sums g = delta * act'(y) and g * x_norm over its batch) can share a pass: the
+ * kernel that writes the upper block's dx can add up the lower block's two sums
+ * as it stores each element, so the lower block's call needs no reduction pass
+ * over its delta.  Zero-initialise, then set:
+ *   sums          this block's act/BN sums, produced by the call of the block above
+ *                 it (its below_sums): float2 per output channel, (sum g,
+ *                 sum g * x_norm) over the batch.  Batch-statistics BN only
+ *                 (else CBB_EINVAL).  NULL: computed here.
+ *   below_sums    receives the act/BN sums of the block below this one (whose delta
+ *                 is this call's dx): float2 per input channel, as above.  Needs dx.
+ *   below_y       that block's activation output [N,C,H,W] (NULL iff below_act is
+ *                 LINEAR) and normalised conv output below_x_norm [N,C,H,W];
+ *   below_act     its activation and leaky slope below_slope.
+ * The sums are over dx as the call leaves it (after dx_accumulate).  Where dx is
+ * written by the stride-2 3x3 kernel over one 32-channel block (16-byte aligned,
+ * width a multiple of 4) the sums are added up in its epilogue; otherwise a
+ * reduction pass over dx follows.  Results equal those of separate calls up to
+ * the order of the summation. */
+typedef struct cbb_block_opts {
+  const float* sums;
+  float* below_sums;
+  const float* below_y;
+  const float* below_x_norm;
+  int32_t below_act;
+  float below_slope;
+} cbb_block_opts;
+
+/* cbb_conv_block_backward with options (opts NULL: the same call); the same
+ * workspace size.  CBB_EINVAL for options that break the rules above. */
+int cbb_conv_block_backward_ex(const cbb_conv_desc* desc, const float* x, const float* w,
+                               const float* y, const float* x_norm, const float* var,
+                               const float* gamma, const float* delta, float* dz, float* dw,
+                               float* db, float* dgamma, float* dx, int dx_accumulate,
+                               const cbb_block_opts* opts, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 /* ----------------------------------------------------------------------------
  * The conv block backward for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
@@ -259,6 +297,17 @@ int cbb_conv_backward_weights(const cbb_conv_desc* desc, const float* x, const f
 int cbb_conv_backward_data(const cbb_conv_desc* desc, const float* w, const float* dz, float* dx,
                            int dx_accumulate, void* workspace, size_t workspace_bytes,
                            void* stream);
+/* Stage 3 with the act/BN sums of the block below (cbb_block_opts: below_sums,
+ * below_y, below_x_norm, below_act, below_slope; sums must be NULL), the same
+ * workspace size. */
+int cbb_conv_backward_data_ex(const cbb_conv_desc* desc, const float* w, const float* dz,
+                              float* dx, int dx_accumulate, const cbb_block_opts* opts,
+                              void* workspace, size_t workspace_bytes, void* stream);
+/* 1 when the input-gradient kernel of this layer adds up the act/BN sums of the
+ * block below in its epilogue (cbb_block_opts, given 16-byte aligned tensors and
+ * a width that is a multiple of 4); 0 when a reduction pass over dx follows
+ * instead; a negative status for a bad descriptor. */
+int cbb_conv_fuses_below_sums(const cbb_conv_desc* desc);
 /* Stages 2 and 3 together (the two GEMMs of [P1] section 3.1 that read the
  * same delta): dw += weight gradient and, when dx is not NULL, dx (+)= input
  * gradient, with the meanings and buffers of the two calls above.  For the

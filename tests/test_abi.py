@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported_and_bound():
 
 
 def test_version_and_status_strings():
-    assert cbb.abi_version() == 1
+    assert cbb.abi_version() == 2
     for code in (0, -1, -2, -3, -4):
         assert cbb.status_string(code)
     assert cbb.status_string(123) == "unknown status"
@@ -312,3 +312,43 @@ def test_sgd_update_validates():
     torch = pytest.importorskip("torch")
     with pytest.raises(ValueError, match="dw"):
         cbb.sgd_update(torch.zeros(10), torch.zeros(9), 1, 0.1)
+
+
+def test_block_options_validate_on_the_host():
+    """cbb_block_opts: sums only with batch statistics, below sums need dx, the block
+    below's x_norm (and y unless it is linear) and a valid activation; tensors of the
+    block below without a place for its sums are refused; the data-only call takes no
+    sums of its own.  All refused before any HIP call."""
+    L = cbb.lib()
+    names = ["x", "w", "y", "x_norm", "var", "gamma", "delta", "dz", "dw", "db", "dgamma", "dx"]
+
+    def call(d, opts, **kw):
+        return L.cbb_conv_block_backward_ex(ctypes.byref(d), *[kw.get(k, BOGUS) for k in names],
+                                            kw.get("acc", 0), ctypes.byref(opts), BOGUS, 1 << 30,
+                                            None)
+
+    nobn = _desc(in_c=5, batch_normalize=0)
+    o = cbb.BlockOpts(sums=0x2000)
+    assert call(nobn, o, x_norm=None, var=None, gamma=None, dgamma=None) == -1
+    fixed = _desc(in_c=5, batch_normalize=2)
+    assert call(fixed, o) == -1
+    d = _desc(in_c=5)
+    o = cbb.BlockOpts(below_sums=0x2000, below_x_norm=0x3000, below_act=1)
+    assert call(d, o) == -1                       # leaky below without its y
+    o.below_y = 0x4000
+    assert call(d, o, dx=None) == -1              # the sums below need dx
+    assert call(d, cbb.BlockOpts(below_sums=0x2000, below_y=0x4000, below_act=1)) == -1
+    assert call(d, cbb.BlockOpts(below_sums=0x2000, below_x_norm=0x3000, below_act=14)) == -1
+    assert call(d, cbb.BlockOpts(below_y=0x4000, below_x_norm=0x3000)) == -1
+    assert call(d, cbb.BlockOpts(sums=0x2000, below_sums=0x2000, below_x_norm=0x3000)) == -1
+    o4 = cbb.BlockOpts(sums=0x2000)
+    assert L.cbb_conv_backward_data_ex(ctypes.byref(d), BOGUS, BOGUS, BOGUS, 0, ctypes.byref(o4),
+                                       BOGUS, 1 << 30, None) == -1
+    # which layers add the sums up in their input-gradient kernel
+    assert cbb.conv_fuses_below_sums(cbb.conv_desc(16, 32, 416, 416, 64, 3, 2, 1, 1, "leaky"))
+    assert cbb.conv_fuses_below_sums(cbb.conv_desc(2, 32, 40, 72, 64, 3, 2, 1, 1, "leaky"))
+    # 128 output channels on a small image: the input gradient is split over them
+    assert not cbb.conv_fuses_below_sums(cbb.conv_desc(2, 32, 40, 72, 128, 3, 2, 1, 1, "leaky"))
+    assert not cbb.conv_fuses_below_sums(cbb.conv_desc(8, 128, 52, 52, 256, 3, 1, 1, 1, "leaky"))
+    assert not cbb.conv_fuses_below_sums(cbb.conv_desc(2, 64, 40, 72, 64, 3, 2, 1, 1, "leaky"))
+    assert L.cbb_conv_fuses_below_sums(ctypes.byref(_desc(batch=0))) == -1
