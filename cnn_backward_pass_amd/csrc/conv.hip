@@ -6,6 +6,8 @@
 // section 3.1 (backward_convolutional_layer: dW = delta x im2col(x)^T with
 // beta = 1, dX = col2im(W^T x delta)) and section 3.2 (im2col_cpu/col2im_cpu
 // index map, output size (size + 2 pad - k)/stride + 1).
+#include <type_traits>
+
 #include "cbb_internal.h"
 
 namespace cbb {
@@ -151,52 +153,77 @@ __global__ __launch_bounds__(kThreads) void conv_dw_kernel(ConvGeom g, const flo
 // the splits directly) in index order.  Every output element is summed by one
 // thread in a fixed order, so the result does not depend on scheduling.
 
-// part[s0*mn + e] + ... + part[(s1-1)*mn + e] (s1 - s0 <= kReduceGroup), added in
-// index order; all the loads are issued before the first add.
-__device__ __forceinline__ float sum_in_order(const float* __restrict__ part, int s0, int s1,
-                                              int64_t mn, int64_t e) {
-  float v[kReduceGroup];
+// part[s0*mn + e] + ... + part[(s1-1)*mn + e] for W = 1 or 4 consecutive elements
+// (one float or one 16-byte piece per split), added in index order; the loads go
+// out eight at a time (clamped to the last split, so every address is valid; the
+// extra values are not added).
+typedef float rf4 __attribute__((ext_vector_type(4)));
+constexpr int64_t kRedVecMin = int64_t(1) << 20;   // elements: 16-byte form from here on
+template <int W>
+using RedVec = typename std::conditional<W == 4, rf4, float>::type;
+
+template <int W>
+__device__ __forceinline__ RedVec<W> vsum_in_order(const float* __restrict__ part, int s0, int s1,
+                                                   int64_t mn, int64_t e) {
+  using V = RedVec<W>;
+  auto ld = [&](int k) { return *reinterpret_cast<const V*>(part + (int64_t)k * mn + e); };
+  V acc = ld(s0);
+  for (int k = s0 + 1; k < s1; k += 8) {
+    V v[8];
 #pragma unroll
-  for (int k = 0; k < kReduceGroup; ++k) v[k] = part[(int64_t)min(s0 + k, s1 - 1) * mn + e];
-  float acc = v[0];
+    for (int u = 0; u < 8; ++u) v[u] = ld(min(k + u, s1 - 1));
 #pragma unroll
-  for (int k = 1; k < kReduceGroup; ++k)
-    if (s0 + k < s1) acc += v[k];
+    for (int u = 0; u < 8; ++u)
+      if (k + u < s1) acc += v[u];
+  }
   return acc;
 }
 
+template <int W>
 __global__ __launch_bounds__(kThreads) void dw_reduce_l1(const float* __restrict__ part,
                                                          float* __restrict__ part2, int splits,
                                                          int64_t mn, int64_t region) {
   part += blockIdx.z * region;    // grouped convolution: one partial region per group
   part2 += blockIdx.z * region;
-  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * W;
   if (e >= mn) return;
   const int s0 = blockIdx.y * kReduceGroup, s1 = min(splits, s0 + kReduceGroup);
-  part2[(int64_t)blockIdx.y * mn + e] = sum_in_order(part, s0, s1, mn, e);
+  *reinterpret_cast<RedVec<W>*>(part2 + (int64_t)blockIdx.y * mn + e) =
+      vsum_in_order<W>(part, s0, s1, mn, e);
 }
 
-// Partials are either in dW's own [o][i][tap] order or, with kk > 0, tap-major
-// [tap][o][i] (kk taps, oc x c per tap), which the row-streaming kernel writes
-// so that its stores are contiguous; the sum is mapped back to dW's order here.
+// Partials in dW's own [o][i][tap] order: dw[e] += their ordered sum.
+template <int W>
 __global__ __launch_bounds__(kThreads) void dw_reduce_l2(float* __restrict__ dw,
                                                          const float* __restrict__ part, int n,
-                                                         int64_t mn, int kk, int oc, int c,
-                                                         int64_t region) {
+                                                         int64_t mn, int64_t region) {
   part += blockIdx.z * region;    // grouped convolution: group blockIdx.z's partials
   dw += blockIdx.z * mn;          // and its dW block
-  const int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * W;
   if (e >= mn) return;
-  float s = 0.f;
-  for (int k0 = 0; k0 < n; k0 += kReduceGroup)
-    s += sum_in_order(part, k0, min(n, k0 + kReduceGroup), mn, e);
-  int64_t d = e;
-  if (kk > 0) {
-    const int t = (int)(e / ((int64_t)oc * c)), r = (int)(e - (int64_t)t * oc * c);
-    const int o = r / c, i = r - o * c;
-    d = ((int64_t)o * c + i) * kk + t;
-  }
-  dw[d] += s;
+  RedVec<W>* d = reinterpret_cast<RedVec<W>*>(dw + e);
+  *d += vsum_in_order<W>(part, 0, n, mn, e);
+}
+
+// Tap-major partials [tap][o][i] (9 taps, oc x c per tap), which the row-streaming
+// kernel writes so that its stores are contiguous: work-group (i block, o) sums
+// taps x 64 input channels with coalesced reads (thread = (tap, i)), regroups them
+// in LDS and adds them into dW's [o][i][tap] order as one contiguous run.
+constexpr int kTapRedThreads = 9 * 64;
+__global__ __launch_bounds__(kTapRedThreads) void dw_reduce_tap(float* __restrict__ dw,
+                                                               const float* __restrict__ part,
+                                                               int n, int64_t mn, int oc, int c,
+                                                               int64_t region) {
+  part += blockIdx.z * region;
+  dw += blockIdx.z * mn;
+  __shared__ float tile[kTapRedThreads];
+  const int tid = threadIdx.x, tap = tid >> 6, il = tid & 63;
+  const int o = blockIdx.y, i0 = blockIdx.x * 64, ni = min(64, c - i0);
+  if (il < ni)
+    tile[il * 9 + tap] =
+        vsum_in_order<1>(part, 0, n, mn, ((int64_t)tap * oc + o) * c + i0 + il);
+  __syncthreads();
+  if (tid < 9 * ni) dw[((int64_t)o * c + i0) * 9 + tid] += tile[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -1397,17 +1424,31 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
 }
 
 // dx[e] (+)= sum over splits s (in order) of ws[s][e].
+template <int W>
 __global__ __launch_bounds__(kThreads) void dx_splitk_reduce(float* __restrict__ dx,
                                                              const float* __restrict__ ws,
                                                              int splits, int64_t n,
                                                              int accumulate) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += stride) {
-    float s = 0.f;
-    for (int k0 = 0; k0 < splits; k0 += kReduceGroup)
-      s += sum_in_order(ws, k0, min(splits, k0 + kReduceGroup), n, e);
-    dx[e] = accumulate ? dx[e] + s : s;
+  using V = RedVec<W>;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * W;
+  for (int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * W; e < n; e += stride) {
+    const V s = vsum_in_order<W>(ws, 0, splits, n, e);
+    V* d = reinterpret_cast<V*>(dx + e);
+    *d = accumulate ? *d + s : s;
   }
+}
+
+// dx (+)= the ordered sum of the `splits` input-gradient partials in ws.
+static int launch_dx_reduce(float* dx, const float* ws, int splits, int64_t n, int accumulate,
+                            hipStream_t st) {
+  const bool v4 = n % 4 == 0 && (((uintptr_t)dx | (uintptr_t)ws) & 15) == 0 && n >= kRedVecMin;
+  const unsigned blocks =
+      (unsigned)std::min<int64_t>(ceil_div(v4 ? n / 4 : n, kThreads), 8192);
+  if (v4)
+    dx_splitk_reduce<4><<<blocks, kThreads, 0, st>>>(dx, ws, splits, n, accumulate);
+  else
+    dx_splitk_reduce<1><<<blocks, kThreads, 0, st>>>(dx, ws, splits, n, accumulate);
+  return check_launch("dx_splitk_reduce", st);
 }
 
 // ---------------------------------------------------------------------------
@@ -2215,22 +2256,41 @@ int launch_conv_dw(const ConvGeom& g, const float* x, const float* dz, float* dw
 int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int groups,
                      int tapmajor, hipStream_t st) {
   const int64_t mn = (int64_t)g.OC * g.J;
-  const unsigned eblocks = (unsigned)ceil_div(mn, kThreads);
+  // 16-byte pieces of the partials when each region stays 16-byte aligned (ws is) and
+  // there are enough of them (on small layers the scalar form, with 4x the threads,
+  // measured faster)
+  const bool v4 = mn % 4 == 0 && aligned16(ws) && mn >= kRedVecMin;
+  const unsigned eblocks = (unsigned)ceil_div(v4 ? mn / 4 : mn, kThreads);
   const int kk = tapmajor ? g.K * g.K : 0;
   // grouped convolution: grid z = group, each with its own partial region
   const int64_t region = ((int64_t)splits + groups) * mn;
-  if (groups == 0) {
-    dw_reduce_l2<<<dim3(eblocks, 1, g.G), kThreads, 0, st>>>(dw, ws, splits, mn, kk, g.OC, g.C,
-                                                               region);
+  // the last level: dW order, or the tap-major partials regrouped (9 taps)
+  auto last = [&](const float* part, int n) -> int {
+    if (kk == 9) {
+      dw_reduce_tap<<<dim3((unsigned)ceil_div(g.C, 64), (unsigned)g.OC, g.G), kTapRedThreads, 0,
+                      st>>>(dw, part, n, mn, g.OC, g.C, region);
+      return check_launch("dw_reduce_l2", st);
+    }
+    if (kk != 0) return CBB_EUNSUPPORTED;
+    const bool w4 = v4 && aligned16(dw);   // 16-byte adds into dW too
+    const unsigned b2 = (unsigned)ceil_div(w4 ? mn / 4 : mn, kThreads);
+    if (w4)
+      dw_reduce_l2<4><<<dim3(b2, 1, g.G), kThreads, 0, st>>>(dw, part, n, mn, region);
+    else
+      dw_reduce_l2<1><<<dim3(b2, 1, g.G), kThreads, 0, st>>>(dw, part, n, mn, region);
     return check_launch("dw_reduce_l2", st);
-  }
+  };
+  if (groups == 0) return last(ws, splits);
   float* part2 = ws + (int64_t)splits * mn;
-  dw_reduce_l1<<<dim3(eblocks, groups, g.G), kThreads, 0, st>>>(ws, part2, splits, mn, region);
+  if (v4)
+    dw_reduce_l1<4><<<dim3(eblocks, groups, g.G), kThreads, 0, st>>>(ws, part2, splits, mn,
+                                                                     region);
+  else
+    dw_reduce_l1<1><<<dim3(eblocks, groups, g.G), kThreads, 0, st>>>(ws, part2, splits, mn,
+                                                                     region);
   const int rc = check_launch("dw_reduce_l1", st);
   if (rc) return rc;
-  dw_reduce_l2<<<dim3(eblocks, 1, g.G), kThreads, 0, st>>>(dw, part2, groups, mn, kk, g.OC, g.C,
-                                                             region);
-  return check_launch("dw_reduce_l2", st);
+  return last(part2, groups);
 }
 
 // ----------------------------------------------------------------------------- dX planning
@@ -2384,10 +2444,7 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
                                          accumulate, st);
     const int rc = check_launch("conv_dx_kernel", st);
     if (rc || p.ksplits == 1) return rc;
-    const int64_t n = (int64_t)g.N * g.C * g.HW;
-    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
-    dx_splitk_reduce<<<blocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
-    return check_launch("dx_splitk_reduce", st);
+    return launch_dx_reduce(dx, ws, p.ksplits, (int64_t)g.N * g.C * g.HW, accumulate, st);
   }
   const DxPlan p = plan_dx(g);
   if (p.kind == DX_D3S1 || p.kind == DX_D3S1_SMALL || p.kind == DX_D3S2) {
@@ -2455,10 +2512,7 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
 #undef CBB_DX3
     int rc = check_launch("conv_dx3_direct", st);
     if (rc || p.ksplits == 1) return rc;
-    const int64_t n = (int64_t)g.N * g.C * g.HW;
-    const unsigned rblocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
-    dx_splitk_reduce<<<rblocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
-    return check_launch("dx_splitk_reduce", st);
+    return launch_dx_reduce(dx, ws, p.ksplits, (int64_t)g.N * g.C * g.HW, accumulate, st);
   }
   if (p.kind == DX_1X1) {
     if (conv1x1_dma_ok(g, wt, dz)) return launch_conv1x1_dx(g, wt, dz, dx, accumulate, st);
@@ -2481,10 +2535,7 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
     launch_dx_mfma<TileShape<2, 2, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
   int rc = check_launch("conv_dx_kernel", st);
   if (rc || p.ksplits == 1) return rc;
-  const int64_t n = (int64_t)g.N * g.C * g.HW;
-  const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 8192);
-  dx_splitk_reduce<<<blocks, kThreads, 0, st>>>(dx, ws, p.ksplits, n, accumulate);
-  return check_launch("dx_splitk_reduce", st);
+  return launch_dx_reduce(dx, ws, p.ksplits, (int64_t)g.N * g.C * g.HW, accumulate, st);
 }
 
 }  // namespace cbb
