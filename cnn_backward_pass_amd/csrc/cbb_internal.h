@@ -369,6 +369,20 @@ int launch_softmax_loss(int batch, int classes, const float* prob, const int32_t
                         float loss_weight, float* dlogits, int32_t* bad, hipStream_t st);
 int launch_sgd_update(int64_t n, int batch, float lr, float momentum, float decay, float* w,
                       float* dw, hipStream_t st);
+// C[m][n] (+)= sum_k A(m,k) B(k,n) on the fp32 matrix cores (layers.hip), `batch`
+// problems with B and C offset by sbb / scb elements each.
+struct GemmArgs {
+  int M, N, K;
+  const float* A;
+  int64_t sam, sak;
+  const float* B;
+  int64_t sbk, sbn;
+  float* C;
+  int64_t ldc;
+  int accumulate;
+  int64_t sbb, scb;
+};
+int launch_gemm(const GemmArgs& a, hipStream_t st, int batch = 1);
 int launch_fc(int batch, int in_dim, int out_dim, const float* x, const float* w,
               const float* delta, float* dw, float* db, float* dx, int dx_accumulate,
               hipStream_t st);

@@ -1423,6 +1423,50 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
   }
 }
 
+// Input gradient from the column buffer (the pages' route: P1 section 3.1's
+// gemm(1,0,...) of W^T and delta, then section 3.2's col2im):
+// dx[n][i][h][w] (+)= sum over (kh, kw), in that order, of col[n][(i,kh,kw)][ho][wo]
+// with ho*S = h + P - kh, wo*S = w + P - kw on the map (dense layers).
+// S1: stride 1, where the taps that reach an element form one rectangle
+// kh in [h + P - OH + 1, h + P], kw likewise, visited without tests.
+template <bool S1>
+__global__ __launch_bounds__(kThreads) void col2im_kernel(ConvGeom g, const float* __restrict__ col,
+                                                          float* __restrict__ dx, int accumulate) {
+  const int64_t total = (int64_t)g.N * g.C * g.HW;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < total; e += stride) {
+    const int n = (int)(e / ((int64_t)g.C * g.HW));
+    const int rem = (int)(e - (int64_t)n * g.C * g.HW);
+    const int i = rem / g.HW, pix = rem - i * g.HW;
+    const int h = pix / g.W, w = pix - h * g.W;
+    const float* cb = col + ((int64_t)n * g.J + (int64_t)i * g.K * g.K) * g.OHW;
+    float s = 0.f;
+    if constexpr (S1) {
+      const int kh0 = max(0, h + g.P - g.OH + 1), kh1 = min(g.K - 1, h + g.P);
+      const int kw0 = max(0, w + g.P - g.OW + 1), kw1 = min(g.K - 1, w + g.P);
+      for (int kh = kh0; kh <= kh1; ++kh) {
+        const float* r = cb + (int64_t)kh * g.K * g.OHW + (h + g.P - kh) * g.OW + w + g.P;
+        for (int kw = kw0; kw <= kw1; ++kw) s += r[kw * (g.OHW - 1)];
+      }
+    } else {
+      for (int kh = 0; kh < g.K; ++kh) {
+        const int hn = h + g.P - kh;
+        if (hn < 0 || hn % g.S) continue;
+        const int ho = hn / g.S;
+        if (ho >= g.OH) continue;
+        for (int kw = 0; kw < g.K; ++kw) {
+          const int wn = w + g.P - kw;
+          if (wn < 0 || wn % g.S) continue;
+          const int wo = wn / g.S;
+          if (wo >= g.OW) continue;
+          s += cb[(int64_t)(kh * g.K + kw) * g.OHW + ho * g.OW + wo];
+        }
+      }
+    }
+    dx[e] = accumulate ? dx[e] + s : s;
+  }
+}
+
 // dx[e] (+)= sum over splits s (in order) of ws[s][e].
 template <int W>
 __global__ __launch_bounds__(kThreads) void dx_splitk_reduce(float* __restrict__ dx,
@@ -2294,7 +2338,11 @@ int launch_dw_reduce(const ConvGeom& g, float* dw, float* ws, int splits, int gr
 }
 
 // ----------------------------------------------------------------------------- dX planning
-enum DxKind { DX_SMALLC = 0, DX_32x128, DX_64x64, DX_D3S1, DX_D3S2, DX_1X1, DX_D3S1_SMALL };
+enum DxKind { DX_SMALLC = 0, DX_32x128, DX_64x64, DX_D3S1, DX_D3S2, DX_1X1, DX_D3S1_SMALL, DX_COL };
+
+// The column-buffer route (below) for small layers: its buffer, N x C k^2 x OH OW floats.
+constexpr int64_t kColMaxBytes = int64_t(32) << 20;
+static int64_t col_bytes(const ConvGeom& g) { return (int64_t)g.N * g.J * g.OHW * 4; }
 
 struct DxPlan {
   int kind, bm, bn, bk, ctiles, pixtiles, ksplits;
@@ -2358,6 +2406,14 @@ static DxPlan plan_dx(const ConvGeom& g) {
     p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB);
     return p;
   }
+  // small layers with a 4x4 or larger window: the column buffer (a batched matrix-core
+  // GEMM, then a gather of k^2 entries per element) beats the implicit GEMM, whose
+  // index work per gathered element dominates at these sizes
+  if (special && g.K >= 4 && g.OHW <= 1024 && col_bytes(g) <= kColMaxBytes) {
+    p.kind = DX_COL;
+    p.ksplits = 1;
+    return p;
+  }
   const int S = g.S;
   const int64_t maxpix = (int64_t)g.N * ((g.H + S - 1) / S) * ((g.W + S - 1) / S);
   p.bk = 32;
@@ -2400,6 +2456,7 @@ size_t conv_dx_workspace(const ConvGeom& g) {
   if (conv_depthwise(g)) return 0;
   // grouped: every group writes its channels of the same [split][n][c][hw] partials
   const DxPlan p = plan_dx(dense(g) ? g : group_geom(g));
+  if (p.kind == DX_COL) return (size_t)col_bytes(g);
   if (p.ksplits <= 1) return 0;
   return (size_t)p.ksplits * g.N * g.C * g.HW * sizeof(float);
 }
@@ -2519,6 +2576,20 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
     // misaligned tensors: the general kernel on 64 x 64 tiles, no split
     launch_dx_mfma<TileShape<2, 2, 1>>(g, p, wt, dz, dx, ws, accumulate, st);
     return check_launch("conv_dx_kernel", st);
+  }
+  if (p.kind == DX_COL) {
+    // col[n][(i,kh,kw)][p] = sum_o W[o][i][kh][kw] dz[n][o][p], one GEMM per image
+    GemmArgs ga{g.J, g.OHW, g.OC, wt, 1, g.J, dz, g.OHW, 1, ws, g.OHW, 0, g.zs,
+                (int64_t)g.J * g.OHW};
+    int rc = launch_gemm(ga, st, g.N);
+    if (rc) return rc;
+    const int64_t n = (int64_t)g.N * g.C * g.HW;
+    const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(n, kThreads), 16384);
+    if (g.S == 1)
+      col2im_kernel<true><<<blocks, kThreads, 0, st>>>(g, ws, dx, accumulate);
+    else
+      col2im_kernel<false><<<blocks, kThreads, 0, st>>>(g, ws, dx, accumulate);
+    return check_launch("conv_dx_col2im", st);
   }
   if (p.kind == DX_SMALLC) {
     switch (g.C) {

@@ -306,16 +306,8 @@ int launch_softmax_loss(int batch, int classes, const float* prob, const int32_t
 // --------------------------------------------------------------- inner product
 // C[m][n] (+)= sum_k A(m,k) B(k,n), A(m,k) = A[m*sam + k*sak], B(k,n) = B[k*sbk + n*sbn],
 // C[m*ldc + n].  64x64 tiles on the 32x32x2 fp32 matrix cores, K in steps of 32.
-struct GemmArgs {
-  int M, N, K;
-  const float* A;
-  int64_t sam, sak;
-  const float* B;
-  int64_t sbk, sbn;
-  float* C;
-  int64_t ldc;
-  int accumulate;
-};
+// Batched over grid y: problem b reads B + b*sbb and writes C + b*scb (A shared);
+// GemmArgs is declared in cbb_internal.h.
 
 // TS = TileShape<2, 2, 1> (64x64 tiles), or TileShape<1, 1, 4> (32x32 tiles,
 // the four waves splitting each K tile) for small outputs with a long K.
@@ -325,6 +317,8 @@ __global__ __launch_bounds__(kThreads) void strided_gemm_kernel(GemmArgs a, int 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % TS::WM, wn = (wave / TS::WM) % TS::WN, wk = wave / (TS::WM * TS::WN);
   const int m0 = (blockIdx.x / tiles_n) * TS::BM, n0 = (blockIdx.x % tiles_n) * TS::BN;
+  a.B += blockIdx.y * a.sbb;
+  a.C += blockIdx.y * a.scb;
   // Register-prefetched K tiles (two ahead, see gemm_mainloop); out-of-range
   // elements read a clamped address and are zeroed at the LDS store, so the
   // loads stay in flight during the matrix-core work.
@@ -388,19 +382,19 @@ __global__ __launch_bounds__(kThreads) void strided_gemm_kernel(GemmArgs a, int 
     }
 }
 
-static int launch_gemm(const GemmArgs& a, hipStream_t st) {
-  const int64_t tiles64 = ceil_div(a.M, 64) * ceil_div(a.N, 64);
+int launch_gemm(const GemmArgs& a, hipStream_t st, int batch) {
+  const int64_t tiles64 = ceil_div(a.M, 64) * ceil_div(a.N, 64) * batch;
   if (tiles64 < 64 && a.K >= 256) {
     // few 64x64 tiles over a long K: 32x32 tiles, K split over the four waves
     using TS = TileShape<1, 1, 4>;
     const int tiles_n = (int)ceil_div(a.N, 32);
     const int tiles = (int)ceil_div(a.M, 32) * tiles_n;
-    strided_gemm_kernel<TS><<<tiles, kThreads, 0, st>>>(a, tiles_n);
+    strided_gemm_kernel<TS><<<dim3(tiles, batch), kThreads, 0, st>>>(a, tiles_n);
   } else {
     using TS = TileShape<2, 2, 1>;
     const int tiles_n = (int)ceil_div(a.N, 64);
     const int tiles = (int)ceil_div(a.M, 64) * tiles_n;
-    strided_gemm_kernel<TS><<<tiles, kThreads, 0, st>>>(a, tiles_n);
+    strided_gemm_kernel<TS><<<dim3(tiles, batch), kThreads, 0, st>>>(a, tiles_n);
   }
   return check_launch("strided_gemm_kernel", st);
 }
