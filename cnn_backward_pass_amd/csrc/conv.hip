@@ -2098,8 +2098,14 @@ static FuPlan plan_fused(const ConvGeom& g, bool form_dz = false) {
   // kernel: its registers allow two per CU), at least 4 rows each (each run also
   // walks the dz rows just above and below it, so longer runs fetch less)
   const int64_t target = form_dz ? 512 : 768;
-  const int64_t runs = std::max<int64_t>(
+  int64_t runs = std::max<int64_t>(
       1, std::min<int64_t>(ceil_div(g.H, 4), ceil_div(target, (int64_t)g.N * p.nstrips)));
+  // small layers (fewer than 64 work-groups that way): shorter runs, as many as keep
+  // one level of the ordered dW sum (32 work-groups); the single 3x3 block (2 x 32 x
+  // 32) measured 19 us on 16 four-row runs
+  const int64_t cols = (int64_t)g.N * p.nstrips;
+  if (cols * runs < 64 && cols < kReduceGroup)
+    runs = std::max<int64_t>(runs, std::min<int64_t>(g.H, kReduceGroup / cols));
   p.rlen = (int)ceil_div(g.H, runs);
   p.nruns = (int)ceil_div(g.H, p.rlen);
   p.wgs = g.N * p.nstrips * p.nruns;
