@@ -1132,10 +1132,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
 // over output channels, NCH chunks of 16 output channels per tile).  Each
 // work-group walks the tiles blockIdx.x, blockIdx.x + gridDim.x, ... as one
 // sequence of chunk steps: the first chunk of the next tile is copied while the
-// last chunk of this one is computed, and a tile's output stores overlap the
-// next tile's work.  Output positions off the image store to a sink, so every
-// thread issues the same number of stores per tile and the waits for the next
-// chunk's copies can count past them (memory operations complete in order).
+// last chunk of this one is computed.  Output positions off the image store to
+// a sink, so every thread issues the same number of stores per tile.  The wait
+// for the next tile's first chunk counts past those stores, but the barrier after
+// it (its memory fence) waits for every store in flight anyway, and that full
+// wait is what makes the copies safe to read: a count that stops short of
+// younger stores does not prove older copies into LDS landed.
 __device__ float g_dx3_sink[4 * kThreads];
 
 //
@@ -1371,8 +1373,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
       float* wr = (c & 1) ? Wl1 : Wl;
       float* zn = (c & 1) ? Z : Z1;
       float* wn = (c & 1) ? Wl : Wl1;
-      // this wave's copies of chunk c have landed (only the previous tile's stores
-      // can be younger); after the barrier everyone's have, and the other buffer is free
+      // this wave's copies of chunk c have landed (at c == 0 once the barrier's fence
+      // has waited for the stores too); after the barrier everyone's have, and the
+      // other buffer is free
       static_assert(NST == 16, "the wait below counts 16 stores");
       if (c == 0)
         asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -1559,13 +1562,16 @@ __global__ __launch_bounds__(kThreads) void conv_dx_smallc_kernel(ConvGeom g,
       }
     }
     // the K-1 halo columns beyond the first 64
-    for (int e = tid; e < ROWS * (LW - 64); e += kThreads) {
-      const int row = e / (LW - 64), cc = 64 + e % (LW - 64);
-      const int o = row / LH, rr = row - o * LH;
-      const int ho = ho0 + rr, wo = wo0 + cc;
-      const bool ok = ob + o < g.OC && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
-      const float t = dzb[ok ? (int64_t)(ob + o) * g.OHW + ho * g.OW + wo : 0];
-      tile[o][rr][cc] = ok ? t : 0.f;
+    if constexpr (LW > 64) {
+      for (int e = tid; e < ROWS * (LW - 64); e += kThreads) {
+        const int row = e / (LW - 64), cc = 64 + e % (LW - 64);
+        const int o = row / LH, rr = row - o * LH;
+        const int ho = ho0 + rr, wo = wo0 + cc;
+        const bool ok =
+            ob + o < g.OC && (unsigned)ho < (unsigned)g.OH && (unsigned)wo < (unsigned)g.OW;
+        const float t = dzb[ok ? (int64_t)(ob + o) * g.OHW + ho * g.OW + wo : 0];
+        tile[o][rr][cc] = ok ? t : 0.f;
+      }
     }
     __syncthreads();
     const int onum = min(kScOCB, g.OC - ob);
