@@ -2,10 +2,13 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
-One step = the full backward pass of all five workloads back to back (single
-3x3 block, LeNet, Darknet-53 residual unit, YOLOv3 stem, YOLOv3 head), each at
-its full batch: that covers every step of the path (activation, BN, conv
-dW/dX/db, shortcut, route, upsample, max-pool, inner product, softmax loss).
+One step = the full backward pass of all five workloads (single 3x3 block,
+LeNet, Darknet-53 residual unit, YOLOv3 stem, YOLOv3 head), each at its full
+batch: that covers every step of the path (activation, BN, conv dW/dX/db,
+shortcut, route, upsample, max-pool, inner product, softmax loss).  The five
+are independent, so a step enqueues the three smaller ones on a second stream
+(default priority) beside the stem and the head and joins it with an event;
+``schedule`` gives the split and the same step on one stream.
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts.  ``value`` = algorithmic conv + inner-product GFLOP (dW + dX) of one step /
 seconds per step.
@@ -35,6 +38,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "conv-block backward GFLOP/s (dW+dX+BN) and % of fp32-MFMA / HBM roofline"
 ORDER = ["single_block", "lenet", "darknet53_residual", "yolov3_stem", "yolov3_head"]
+# workloads of a step enqueued on the second stream (they share no buffer with the others)
+SIDE = ("single_block", "lenet", "darknet53_residual")
 PEAK_MFMA_F32 = 157.3e12   # MI355X dense fp32 matrix, FLOP/s
 PEAK_HBM = 8.0e12          # MI355X HBM3E, B/s
 RIDGE = PEAK_MFMA_F32 / PEAK_HBM
@@ -323,7 +328,32 @@ def time_kernels(runners, torch, blocker, reps=3):
                    in rows.items()), reverse=True)
 
 
-def step_protocol(runners, torch, dev, runs):
+def enqueue_step(runners, torch, side, run=None):
+    """One step of all workloads: SIDE on stream `side`, forked from and joined back into
+    the current stream by events; run(name, runner) enqueues one workload (default:
+    runner.step()) and is called with the stream it runs on current.  side=None: every
+    workload on the current stream, in ORDER."""
+    run = run or (lambda name, r: r.step())
+    if side is None:
+        for name, r in runners.items():
+            run(name, r)
+        return
+    main = torch.cuda.current_stream()
+    fork = torch.cuda.Event()
+    fork.record(main)
+    side.wait_event(fork)
+    with torch.cuda.stream(side):
+        for name in SIDE:
+            run(name, runners[name])
+    for name, r in runners.items():
+        if name not in SIDE:
+            run(name, r)
+    join = torch.cuda.Event()
+    join.record(side)
+    main.wait_event(join)
+
+
+def step_protocol(runners, torch, dev, runs, side):
     """Steps timed one at a time: warm (back to back) and cold (a 512 MB write before
     each step, outside its events, evicts L2 and the 256 MB memory-side cache)."""
     flush = torch.empty(512 * (1 << 20) // 4, dtype=torch.float32, device=dev)
@@ -335,8 +365,7 @@ def step_protocol(runners, torch, dev, runs):
                 flush.fill_(float(k))
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            for r in runners.values():
-                r.step()
+            enqueue_step(runners, torch, side)
             b.record()
             torch.cuda.synchronize()
             ms.append(a.elapsed_time(b))
@@ -549,12 +578,12 @@ def main():
     peaks = calibrate(calib, torch, dev)
     runners = build_runners(dev)
     step_flops = sum(r.flops() for r in runners.values())
+    side = torch.cuda.Stream()   # default priority, like the current stream
     for r in runners.values():
         r.reset()
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        for r in runners.values():
-            r.step()
+        enqueue_step(runners, torch, side)
     torch.cuda.synchronize()
 
     # Every kernel of the step timed in place, before the timed region; the dominant
@@ -574,13 +603,13 @@ def main():
     seen = []
 
     def eager_step(k):
-        for name, r in runners.items():
+        def run(name, r):
             if name != dom_name:
                 r.step()
-                continue
+                return
             cnt = [0]
             if dom_i == 0:
-                ev[k][0].record()
+                ev[k][0].record()   # on the stream the workload runs on (current here)
 
             def hook(call, kernel):
                 i = cnt[0]
@@ -591,6 +620,7 @@ def main():
                     ev[k][1].record()
                     seen.append(kernel)
             r.step(hook=hook)
+        enqueue_step(runners, torch, side, run)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -622,7 +652,18 @@ def main():
         ms = s.elapsed_time(e) / 5
         per[name] = {"ms": round(ms, 4), "gflop": round(r.flops() / 1e9, 4),
                      "gflops": round(r.flops() / ms / 1e6, 1)}
-    protocol = step_protocol(runners, torch, dev, args.protocol_runs)
+    protocol = step_protocol(runners, torch, dev, args.protocol_runs, side)
+    # the same steps on one stream, for comparison
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        enqueue_step(runners, torch, None)
+    b.record()
+    torch.cuda.synchronize()
+    schedule = {"side_stream": list(SIDE),
+                "main_stream": [n for n in runners if n not in SIDE],
+                "one_stream_ms_per_step": round(a.elapsed_time(b) / args.steps, 4)}
 
     def roof_of(ms, name, call, kernel):
         flops, nbytes = kernel_work(runners[name], call, kernel)
@@ -665,7 +706,7 @@ def main():
                                    "batch: single_block b2@32x32, lenet b64, darknet53_residual "
                                    "b8@52x52, yolov3_stem b16@416x416, yolov3_head b8@26x26",
                        "gflop_per_step": round(step_flops / 1e9, 3), "parallelism": "none"},
-            "roofline": roof, "calibration": peaks, "protocol": protocol,
+            "roofline": roof, "calibration": peaks, "protocol": protocol, "schedule": schedule,
             "per_workload": per, "kernels": kernels,
             "kernel_ms": {f"{n}#{i}.{call}.{k}": round(ms, 4)
                           for ms, n, i, call, k in sorted(kern, key=lambda t: (t[1], t[2]))},
