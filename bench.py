@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "conv-block backward GFLOP/s (dW+dX+BN) and % of fp32-MFMA / HBM roofline"
 ORDER = ["single_block", "lenet", "darknet53_residual", "yolov3_stem", "yolov3_head"]
 # workloads of a step enqueued on the second stream (they share no buffer with the others)
-SIDE = ("single_block", "lenet", "darknet53_residual")
+SIDE = ("darknet53_residual", "lenet", "single_block")
 PEAK_MFMA_F32 = 157.3e12   # MI355X dense fp32 matrix, FLOP/s
 PEAK_HBM = 8.0e12          # MI355X HBM3E, B/s
 RIDGE = PEAK_MFMA_F32 / PEAK_HBM
