@@ -2379,14 +2379,16 @@ static DxPlan plan_dx(const ConvGeom& g) {
     p.pixtiles = (int)ceil_div(g.Q, 64);
     return p;
   }
-  // tile-direct 3x3: split the output channels when the grid cannot fill the GPU,
-  // keeping >= 4 chunks per split.  Measured on MI355X: a small grid (the 26x26
-  // head, 96 blocks) is best at ~1000 work-groups, a mid-size one (the 52x52
-  // residual unit, 176 blocks) at ~350, where more splits cost more partial traffic
-  auto direct_splits = [&](int64_t blocks, int nchunks) {
-    int64_t ks = ceil_div(blocks < 128 ? 1024 : 256, blocks);
+  // tile-direct 3x3: split the output channels when the grid cannot fill the GPU, as
+  // many splits as fit one round of resident work-groups (`per_cu` of them on each of
+  // the 256 CUs: a partial second round leaves most CUs idle while it runs), keeping
+  // >= 4 chunks per split.  Measured on MI355X on the 26x26 head (96 blocks, two per
+  // CU): 5 splits (480 work-groups) 139 + 9 us for the split sum, 11 splits (1056)
+  // 150 + 14 us, 16 splits 147 + 18 us
+  auto direct_splits = [&](int64_t blocks, int nchunks, int per_cu) {
+    int64_t ks = std::max<int64_t>(1, 256 * per_cu / blocks);
     ks = std::min<int64_t>(ks, std::max<int64_t>(1, nchunks / 4));
-    return (int)std::max<int64_t>(1, std::min<int64_t>(ks, 16));
+    return (int)std::min<int64_t>(ks, 16);
   };
   // stride 1: larger images (>= 1024 pixels per plane) measured faster with the
   // small (128-pixel, 32-channel) tile, smaller ones with the 256-pixel, 64-channel tile
@@ -2397,7 +2399,7 @@ static DxPlan plan_dx(const ConvGeom& g) {
     p.kind = DX_D3S1_SMALL;
     p.pixtiles = (int)ceil_div((int64_t)g.H * g.W, 128);
     p.ctiles = g.C / Cf::BMC;
-    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB);
+    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB, 3);
     return p;
   }
   if (special && g.K == 3 && g.P == 1 && g.S == 1 && dx3_s1_fits(g.W, 2, Dx3Cfg<1, 2, 2>::ZPLANE) &&
@@ -2406,7 +2408,7 @@ static DxPlan plan_dx(const ConvGeom& g) {
     p.kind = DX_D3S1;
     p.pixtiles = (int)ceil_div((int64_t)g.H * g.W, 128 * 2);
     p.ctiles = g.C / Cf::BMC;
-    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB);
+    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB, 2);
     return p;
   }
   if (special && g.K == 3 && g.P == 1 && g.S == 2 && g.C % Dx3Cfg<2, 1, 1>::BMC == 0 &&
@@ -2415,7 +2417,7 @@ static DxPlan plan_dx(const ConvGeom& g) {
     p.kind = DX_D3S2;
     p.pixtiles = (int)(ceil_div(g.H, 8) * ceil_div(g.W, 64));
     p.ctiles = g.C / Cf::BMC;
-    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB);
+    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB, 2);
     return p;
   }
   // small layers with a 4x4 or larger window: the column buffer (a batched matrix-core
