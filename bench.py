@@ -7,8 +7,10 @@ LeNet, Darknet-53 residual unit, YOLOv3 stem, YOLOv3 head), each at its full
 batch: that covers every step of the path (activation, BN, conv dW/dX/db,
 shortcut, route, upsample, max-pool, inner product, softmax loss).  The five
 are independent, so a step enqueues the three smaller ones on a second stream
-(default priority) beside the stem and the head and joins it with an event;
-``schedule`` gives the split and the same step on one stream.
+(default priority) that forks from the current stream once the stem's stride-2
+input-gradient kernel is queued, runs beside the rest of the stem and the head,
+and is joined back by an event; ``schedule`` gives the split and the same step
+on one stream.
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts.  ``value`` = algorithmic conv + inner-product GFLOP (dW + dX) of one step /
 seconds per step.
@@ -40,6 +42,11 @@ METRIC = "conv-block backward GFLOP/s (dW+dX+BN) and % of fp32-MFMA / HBM roofli
 ORDER = ["single_block", "lenet", "darknet53_residual", "yolov3_stem", "yolov3_head"]
 # workloads of a step enqueued on the second stream (they share no buffer with the others)
 SIDE = ("darknet53_residual", "lenet", "single_block")
+# The second stream forks right after this kernel of this workload is queued: the stem's
+# persistent stride-2 input-gradient kernel holds every CU's work-group slots, so work
+# beside it only stretches it, while the first-layer kernel and the head after it leave
+# room (forking at the step's start measured within noise of this, 1.72-1.79 ms)
+FORK = ("yolov3_stem", "conv_dx3_s2p (act/BN sums below)")
 PEAK_MFMA_F32 = 157.3e12   # MI355X dense fp32 matrix, FLOP/s
 PEAK_HBM = 8.0e12          # MI355X HBM3E, B/s
 RIDGE = PEAK_MFMA_F32 / PEAK_HBM
@@ -328,26 +335,40 @@ def time_kernels(runners, torch, blocker, reps=3):
                    in rows.items()), reverse=True)
 
 
-def enqueue_step(runners, torch, side, run=None):
-    """One step of all workloads: SIDE on stream `side`, forked from and joined back into
-    the current stream by events; run(name, runner) enqueues one workload (default:
-    runner.step()) and is called with the stream it runs on current.  side=None: every
-    workload on the current stream, in ORDER."""
-    run = run or (lambda name, r: r.step())
+def enqueue_step(runners, torch, side, hook_for=None):
+    """One step of all workloads.  The FORK workload goes first on the current stream; an
+    event recorded right after its FORK kernel is queued (or after the workload, should
+    that kernel not run) forks stream `side`, which runs SIDE; the other workloads follow
+    on the current stream, and an event joins `side` back.  hook_for(name) gives the launch
+    hook for that workload's step or None; a hook runs with the workload's stream current.
+    side=None: every workload on the current stream, in ORDER."""
+    hook_for = hook_for or (lambda name: None)
     if side is None:
         for name, r in runners.items():
-            run(name, r)
+            r.step(hook=hook_for(name))
         return
     main = torch.cuda.current_stream()
     fork = torch.cuda.Event()
-    fork.record(main)
+    forked = [False]
+    fork_name, fork_kernel = FORK
+    inner = hook_for(fork_name)
+
+    def fork_hook(call, kernel):
+        if inner is not None:
+            inner(call, kernel)
+        if kernel == fork_kernel and not forked[0]:
+            fork.record(main)
+            forked[0] = True
+    runners[fork_name].step(hook=fork_hook)
+    if not forked[0]:
+        fork.record(main)
     side.wait_event(fork)
     with torch.cuda.stream(side):
         for name in SIDE:
-            run(name, runners[name])
+            runners[name].step(hook=hook_for(name))
     for name, r in runners.items():
-        if name not in SIDE:
-            run(name, r)
+        if name not in SIDE and name != fork_name:
+            r.step(hook=hook_for(name))
     join = torch.cuda.Event()
     join.record(side)
     main.wait_event(join)
@@ -603,10 +624,9 @@ def main():
     seen = []
 
     def eager_step(k):
-        def run(name, r):
+        def hook_for(name):
             if name != dom_name:
-                r.step()
-                return
+                return None
             cnt = [0]
             if dom_i == 0:
                 ev[k][0].record()   # on the stream the workload runs on (current here)
@@ -619,8 +639,8 @@ def main():
                 elif i == dom_i:
                     ev[k][1].record()
                     seen.append(kernel)
-            r.step(hook=hook)
-        enqueue_step(runners, torch, side, run)
+            return hook
+        enqueue_step(runners, torch, side, hook_for)
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -661,7 +681,7 @@ def main():
         enqueue_step(runners, torch, None)
     b.record()
     torch.cuda.synchronize()
-    schedule = {"side_stream": list(SIDE),
+    schedule = {"side_stream": list(SIDE), "side_forks_after": ".".join(FORK),
                 "main_stream": [n for n in runners if n not in SIDE],
                 "one_stream_ms_per_step": round(a.elapsed_time(b) / args.steps, 4)}
 
