@@ -7,10 +7,10 @@ LeNet, Darknet-53 residual unit, YOLOv3 stem, YOLOv3 head), each at its full
 batch: that covers every step of the path (activation, BN, conv dW/dX/db,
 shortcut, route, upsample, max-pool, inner product, softmax loss).  The five
 are independent, so a step enqueues the three smaller ones on a second stream
-(default priority) that forks from the current stream once the stem's stride-2
-input-gradient kernel is queued, runs beside the rest of the stem and the head,
-and is joined back by an event; ``schedule`` gives the split and the same step
-on one stream.
+(default priority): LeNet and the single block from the start, the residual unit
+once the stem's stride-2 input-gradient kernel is queued, beside the rest of the
+stem and the head; an event joins it back.  ``schedule`` gives the split and the
+same step on one stream.
 Inputs are seeded synthetic tensors already resident in HBM when timing
 starts.  ``value`` = algorithmic conv + inner-product GFLOP (dW + dX) of one step /
 seconds per step.
@@ -40,12 +40,14 @@ sys.path.insert(0, ROOT)
 
 METRIC = "conv-block backward GFLOP/s (dW+dX+BN) and % of fp32-MFMA / HBM roofline"
 ORDER = ["single_block", "lenet", "darknet53_residual", "yolov3_stem", "yolov3_head"]
-# workloads of a step enqueued on the second stream (they share no buffer with the others)
-SIDE = ("darknet53_residual", "lenet", "single_block")
-# The second stream forks right after this kernel of this workload is queued: the stem's
-# persistent stride-2 input-gradient kernel holds every CU's work-group slots, so work
-# beside it only stretches it, while the first-layer kernel and the head after it leave
-# room (forking at the step's start measured within noise of this, 1.72-1.79 ms)
+# Workloads of a step enqueued on a second stream (they share no buffer with the others).
+# SIDE_EARLY start with the step and end well before the stem reaches FORK, a kernel that
+# holds every CU's work-group slots (the stem's persistent stride-2 input gradient): work
+# beside it only stretches it.  SIDE_LATE wait until FORK is queued, then run beside the
+# first-layer kernel and the head, which leave room.
+SIDE_EARLY = ("lenet", "single_block")
+SIDE_LATE = ("darknet53_residual",)
+SIDE = SIDE_EARLY + SIDE_LATE
 FORK = ("yolov3_stem", "conv_dx3_s2p (act/BN sums below)")
 PEAK_MFMA_F32 = 157.3e12   # MI355X dense fp32 matrix, FLOP/s
 PEAK_HBM = 8.0e12          # MI355X HBM3E, B/s
@@ -336,18 +338,25 @@ def time_kernels(runners, torch, blocker, reps=3):
 
 
 def enqueue_step(runners, torch, side, hook_for=None):
-    """One step of all workloads.  The FORK workload goes first on the current stream; an
-    event recorded right after its FORK kernel is queued (or after the workload, should
-    that kernel not run) forks stream `side`, which runs SIDE; the other workloads follow
-    on the current stream, and an event joins `side` back.  hook_for(name) gives the launch
-    hook for that workload's step or None; a hook runs with the workload's stream current.
-    side=None: every workload on the current stream, in ORDER."""
+    """One step of all workloads.  Stream `side` forks from the current stream at the start
+    and runs SIDE_EARLY; the FORK workload goes first on the current stream, and an event
+    recorded right after its FORK kernel is queued (or after the workload, should that
+    kernel not run) releases SIDE_LATE on `side`; the other workloads follow on the current
+    stream, and an event joins `side` back.  hook_for(name) gives the launch hook for that
+    workload's step or None; a hook runs with the workload's stream current.  side=None:
+    every workload on the current stream, in ORDER."""
     hook_for = hook_for or (lambda name: None)
     if side is None:
         for name, r in runners.items():
             r.step(hook=hook_for(name))
         return
     main = torch.cuda.current_stream()
+    start = torch.cuda.Event()
+    start.record(main)
+    side.wait_event(start)
+    with torch.cuda.stream(side):
+        for name in SIDE_EARLY:
+            runners[name].step(hook=hook_for(name))
     fork = torch.cuda.Event()
     forked = [False]
     fork_name, fork_kernel = FORK
@@ -364,7 +373,7 @@ def enqueue_step(runners, torch, side, hook_for=None):
         fork.record(main)
     side.wait_event(fork)
     with torch.cuda.stream(side):
-        for name in SIDE:
+        for name in SIDE_LATE:
             runners[name].step(hook=hook_for(name))
     for name, r in runners.items():
         if name not in SIDE and name != fork_name:
@@ -681,7 +690,8 @@ def main():
         enqueue_step(runners, torch, None)
     b.record()
     torch.cuda.synchronize()
-    schedule = {"side_stream": list(SIDE), "side_forks_after": ".".join(FORK),
+    schedule = {"side_stream_from_start": list(SIDE_EARLY),
+                "side_stream_after": {".".join(FORK): list(SIDE_LATE)},
                 "main_stream": [n for n in runners if n not in SIDE],
                 "one_stream_ms_per_step": round(a.elapsed_time(b) / args.steps, 4)}
 
