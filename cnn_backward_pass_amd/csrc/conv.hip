@@ -805,6 +805,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
                                                             int tiles_w, int ksplits) {
   using C = Dx3Cfg<S, F, RM>;
   static_assert(!Z4 || DMA, "16-byte tile copies are direct copies");
+  // group blockIdx.y of a grouped convolution (g holds the group's channel counts and
+  // the whole tensors' image strides; 0 on a plain one)
+  wt += blockIdx.y * g.gw;
+  dz += blockIdx.y * g.gz;
+  dx += blockIdx.y * g.gx;
+  if (ws) ws += blockIdx.y * g.gx;
   // stride 2 with 16-byte copies: tile columns zc0 .. zc0+35 (nine pieces)
   constexpr int ZC2 = (S == 2 && Z4) ? 36 : C::ZC2;
   constexpr int ZFL = S == 2 ? C::OCB * C::ZR2 * ZC2 : C::ZFLOATS;   // tile floats, at most
@@ -881,7 +887,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   // (one float, or a 16-byte piece with Z4) is staged by thread e % 256
   // (wave-contiguous blocks of 64 units).  Planes are ZR*ZC floats apart (dense).
   const int ZP = ZR * ZC;
-  const float* dzb = dz + (int64_t)b * g.OC * g.OHW;
+  const float* dzb = dz + (int64_t)b * g.zs;
   const int zcount = C::OCB * ZP;
   constexpr int ZU = Z4 ? 4 : 1;   // floats per staged unit
   constexpr int ZQ = Z4 ? (ZFL / 4 + kThreads - 1) / kThreads : C::ZPT;
@@ -1059,7 +1065,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
 
   // ---- epilogue: lane holds pixel `col` of each fragment, channels acc_row(r)
   // with several splits each writes its partial at the pixel's dx position in ws[split]
-  float* out = ksplits == 1 ? dx : ws + (int64_t)split * g.N * g.C * g.HW;
+  float* out = ksplits == 1 ? dx : ws + (int64_t)split * g.N * g.xs;
   const bool add = ksplits == 1 && accumulate;
   if constexpr (S == 2 && DMA) {
     // Stride 2: a fragment's pixels are two columns apart, so the region is first
@@ -1093,7 +1099,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
           const int h = h0 + rr, w = w0 + 4 * c4;
           if (h >= g.H || w >= g.W) continue;
           const float4 v = *reinterpret_cast<const float4*>(&Wl[(il * RR + rr) * TP + 4 * c4]);
-          float* q = out + (((int64_t)b * g.C + ib + il) * g.H + h) * g.W + w;
+          float* q = out + (int64_t)b * g.xs + ((int64_t)(ib + il) * g.H + h) * g.W + w;
           if (vec && w + 3 < g.W) {
             float4 o = v;
             if (add) {
@@ -1114,7 +1120,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
 #pragma unroll
   for (int f = 0; f < C::NFRAG; ++f) {
     if (!pval[f]) continue;
-    float* d = out + ((int64_t)b * g.C) * g.HW + prow[f] * g.W + pcol[f];
+    float* d = out + (int64_t)b * g.xs + prow[f] * g.W + pcol[f];
 #pragma unroll
     for (int m = 0; m < RM; ++m)
 #pragma unroll
@@ -2367,6 +2373,9 @@ static bool smallc_ok(const ConvGeom& g) {
 static DxPlan plan_dx(const ConvGeom& g) {
   DxPlan p{};
   const bool special = dense(g);   // the specialised kernels assume a plain convolution
+  // the tile-direct 3x3 kernels also take the groups of a grouped convolution (g is
+  // then the group geometry; one grid row per group)
+  const bool tile3 = special || (g.G > 1 && g.D == 1);
   if (special && smallc_ok(g)) {
     p.kind = DX_SMALLC;
     p.ksplits = 1;
@@ -2392,32 +2401,32 @@ static DxPlan plan_dx(const ConvGeom& g) {
   };
   // stride 1: larger images (>= 1024 pixels per plane) measured faster with the
   // small (128-pixel, 32-channel) tile, smaller ones with the 256-pixel, 64-channel tile
-  if (special && g.K == 3 && g.P == 1 && g.S == 1 && (int64_t)g.H * g.W >= 1024 &&
+  if (tile3 && g.K == 3 && g.P == 1 && g.S == 1 && (int64_t)g.H * g.W >= 1024 &&
       dx3_s1_fits(g.W, 1, Dx3Cfg<1, 1, 1>::ZPLANE) && g.C % Dx3Cfg<1, 1, 1>::BMC == 0 &&
       g.OC % Dx3Cfg<1, 1, 1>::OCB == 0) {
     using Cf = Dx3Cfg<1, 1, 1>;
     p.kind = DX_D3S1_SMALL;
     p.pixtiles = (int)ceil_div((int64_t)g.H * g.W, 128);
     p.ctiles = g.C / Cf::BMC;
-    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB, 3);
+    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles * g.G, g.OC / Cf::OCB, 3);
     return p;
   }
-  if (special && g.K == 3 && g.P == 1 && g.S == 1 && dx3_s1_fits(g.W, 2, Dx3Cfg<1, 2, 2>::ZPLANE) &&
+  if (tile3 && g.K == 3 && g.P == 1 && g.S == 1 && dx3_s1_fits(g.W, 2, Dx3Cfg<1, 2, 2>::ZPLANE) &&
       g.C % Dx3Cfg<1, 2, 2>::BMC == 0 && g.OC % Dx3Cfg<1, 2, 2>::OCB == 0) {
     using Cf = Dx3Cfg<1, 2, 2>;
     p.kind = DX_D3S1;
     p.pixtiles = (int)ceil_div((int64_t)g.H * g.W, 128 * 2);
     p.ctiles = g.C / Cf::BMC;
-    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB, 2);
+    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles * g.G, g.OC / Cf::OCB, 2);
     return p;
   }
-  if (special && g.K == 3 && g.P == 1 && g.S == 2 && g.C % Dx3Cfg<2, 1, 1>::BMC == 0 &&
+  if (tile3 && g.K == 3 && g.P == 1 && g.S == 2 && g.C % Dx3Cfg<2, 1, 1>::BMC == 0 &&
       g.OC % Dx3Cfg<2, 1, 1>::OCB == 0) {
     using Cf = Dx3Cfg<2, 1, 1>;
     p.kind = DX_D3S2;
     p.pixtiles = (int)(ceil_div(g.H, 8) * ceil_div(g.W, 64));
     p.ctiles = g.C / Cf::BMC;
-    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles, g.OC / Cf::OCB, 2);
+    p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles * g.G, g.OC / Cf::OCB, 2);
     return p;
   }
   // small layers with a 4x4 or larger window: the column buffer (a batched matrix-core
@@ -2501,12 +2510,63 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
                    float* ws, hipStream_t st, BnBelow* below) {
   if (below) below->nseg = 0;
   if (conv_depthwise(g)) return launch_depthwise_dx(g, wt, dz, dx, accumulate, st);
+  // the tile-direct 3x3 kernel over g (a plain layer, or the group geometry of a
+  // grouped one: one grid row per group), then the ordered sum of the split partials
+  auto tile_direct = [&](const ConvGeom& t, const DxPlan& p) {
+    const unsigned blocks = (unsigned)((int64_t)t.N * p.pixtiles * p.ctiles * p.ksplits);
+    const dim3 grid(blocks, (unsigned)t.G);
+    const int tiles_w = p.kind == DX_D3S2 ? (int)ceil_div(t.W, 64) : 0;
+    // 16-byte copies need every group's weights and dz 16-byte aligned too
+    const bool wal = aligned16(wt) && (t.G == 1 || t.gw % 4 == 0);
+    // 16-byte tile copies: the tile rows (W + 8 floats) must still fit the plane
+    const int f1 = p.kind == DX_D3S1 ? 2 : 1;
+    const bool z4 = wal && aligned16(dz) && (t.G == 1 || t.gz % 4 == 0) &&
+                    (t.S == 1 ? t.W % 4 == 0 &&
+                                    ((128 * f1 - 1) / t.W + 4) * (t.W + 8) <= Dx3Cfg<1, 1, 1>::ZPLANE
+                              : t.OW % 4 == 0);
+#define CBB_DX3(S_, F_, RM_, Z4_)                                                         \
+  if (wal)                                                                                \
+    conv_dx3_direct<S_, F_, RM_, true, Z4_><<<grid, kThreads, 0, st>>>(                   \
+        t, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);                   \
+  else                                                                                    \
+    conv_dx3_direct<S_, F_, RM_, false, false><<<grid, kThreads, 0, st>>>(                \
+        t, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);
+    if (p.kind == DX_D3S1) {
+      if (z4) {
+        CBB_DX3(1, 2, 2, true)
+      } else {
+        CBB_DX3(1, 2, 2, false)
+      }
+    } else if (p.kind == DX_D3S1_SMALL) {
+      if (z4) {
+        CBB_DX3(1, 1, 1, true)
+      } else {
+        CBB_DX3(1, 1, 1, false)
+      }
+    } else {
+      if (z4) {
+        CBB_DX3(2, 1, 1, true)
+      } else {
+        CBB_DX3(2, 1, 1, false)
+      }
+    }
+#undef CBB_DX3
+    int rc = check_launch("conv_dx3_direct", st);
+    if (rc || p.ksplits == 1) return rc;
+    return launch_dx_reduce(dx, ws, p.ksplits, (int64_t)g.N * g.C * g.HW, accumulate, st);
+  };
+  auto is_tile3 = [](const DxPlan& p) {
+    return p.kind == DX_D3S1 || p.kind == DX_D3S1_SMALL || p.kind == DX_D3S2;
+  };
   if (!dense(g)) {
-    // grouped or dilated: the general kernel on the group geometry, all groups in
-    // one launch (group j: input channels j*C/G.., output channels j*OC/G.., weight
-    // block j), then one ordered sum of the split partials over all channels
     const ConvGeom s = group_geom(g);
     const DxPlan p = plan_dx(s);
+    // grouped, undilated 3x3 pad 1: the tile-direct kernel, all groups in one launch
+    if (is_tile3(p)) return tile_direct(s, p);
+    // grouped or dilated otherwise: the general kernel on the group geometry, all
+    // groups in one launch (group j: input channels j*C/G.., output channels
+    // j*OC/G.., weight block j), then one ordered sum of the split partials over all
+    // channels
     if (p.kind == DX_32x128)
       launch_dx_mfma<TileShape<1, 4, 1>>(s, p, wt, dz, dx, p.ksplits > 1 ? ws : nullptr,
                                          accumulate, st);
@@ -2518,23 +2578,10 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
     return launch_dx_reduce(dx, ws, p.ksplits, (int64_t)g.N * g.C * g.HW, accumulate, st);
   }
   const DxPlan p = plan_dx(g);
-  if (p.kind == DX_D3S1 || p.kind == DX_D3S1_SMALL || p.kind == DX_D3S2) {
-    const unsigned blocks = (unsigned)((int64_t)g.N * p.pixtiles * p.ctiles * p.ksplits);
+  if (is_tile3(p)) {
     const int tiles_w = p.kind == DX_D3S2 ? (int)ceil_div(g.W, 64) : 0;
-    // 16-byte tile copies: the tile rows (W + 8 floats) must still fit the plane
-    const int f1 = p.kind == DX_D3S1 ? 2 : 1;
-    const bool z4 = aligned16(wt) && aligned16(dz) &&
-                    (g.S == 1 ? g.W % 4 == 0 &&
-                                    ((128 * f1 - 1) / g.W + 4) * (g.W + 8) <= Dx3Cfg<1, 1, 1>::ZPLANE
-                              : g.OW % 4 == 0);
-#define CBB_DX3(S_, F_, RM_, Z4_)                                                         \
-  if (aligned16(wt))                                                                      \
-    conv_dx3_direct<S_, F_, RM_, true, Z4_><<<blocks, kThreads, 0, st>>>(                 \
-        g, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);                   \
-  else                                                                                    \
-    conv_dx3_direct<S_, F_, RM_, false, false><<<blocks, kThreads, 0, st>>>(              \
-        g, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);
-    if (p.kind == DX_D3S2 && z4 && p.ksplits == 1 && (g.OC == 64 || g.OC == 128)) {
+    if (p.kind == DX_D3S2 && aligned16(wt) && aligned16(dz) && g.OW % 4 == 0 &&
+        p.ksplits == 1 && (g.OC == 64 || g.OC == 128)) {
       const int ntiles = (int)((int64_t)g.N * p.pixtiles * p.ctiles);
       const unsigned grid = (unsigned)std::min(ntiles, kDxS2pGroups);
       // the block below's act/BN sums in the epilogue: one 32-channel tile column
@@ -2561,29 +2608,7 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
 #undef CBB_S2P
       return check_launch(sums ? "conv_dx3_s2p (act/BN sums below)" : "conv_dx3_s2p", st);
     }
-    if (p.kind == DX_D3S1) {
-      if (z4) {
-        CBB_DX3(1, 2, 2, true)
-      } else {
-        CBB_DX3(1, 2, 2, false)
-      }
-    } else if (p.kind == DX_D3S1_SMALL) {
-      if (z4) {
-        CBB_DX3(1, 1, 1, true)
-      } else {
-        CBB_DX3(1, 1, 1, false)
-      }
-    } else {
-      if (z4) {
-        CBB_DX3(2, 1, 1, true)
-      } else {
-        CBB_DX3(2, 1, 1, false)
-      }
-    }
-#undef CBB_DX3
-    int rc = check_launch("conv_dx3_direct", st);
-    if (rc || p.ksplits == 1) return rc;
-    return launch_dx_reduce(dx, ws, p.ksplits, (int64_t)g.N * g.C * g.HW, accumulate, st);
+    return tile_direct(g, p);
   }
   if (p.kind == DX_1X1) {
     if (conv1x1_dma_ok(g, wt, dz)) return launch_conv1x1_dx(g, wt, dz, dx, accumulate, st);

@@ -216,6 +216,11 @@ GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (4, 64, 64, 104, 128, 3, 1, 1, True, "leaky", 2, 1),
     (4, 64, 64, 208, 128, 3, 2, 1, False, "relu", 2, 1),
     (1, 4, 96, 96, 4, 3, 1, 1, True, "leaky", 4, 1),        # depthwise, plane beyond LDS: streaming
+    # grouped 3x3 dX on the tile-direct kernel (one grid row per group): 32-channel tiles
+    # split over K, the same at stride 2, and 64-channel tiles split four ways
+    (2, 64, 32, 32, 128, 3, 1, 1, True, "leaky", 2, 1),
+    (2, 64, 16, 64, 256, 3, 2, 1, True, "leaky", 2, 1),
+    (2, 128, 16, 16, 256, 3, 1, 1, False, "linear", 2, 1),
     (2, 8, 90, 91, 8, 5, 2, 2, False, "relu", 8, 1),        # depthwise, 8190-pixel plane in LDS, s2
 ]
 
@@ -224,8 +229,9 @@ GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
 def test_grouped_dilated_conv_block(case):
     """Grouped and dilated layers (all groups in one launch: the general kernels, the
     row-streaming 3x3 dW kernel for grouped 3x3 layers with 32k input and 64k output
-    channels per group, streaming kernels for depthwise layers) against the oracle's
-    grouped / dilated loops; overwrite, then accumulate in place."""
+    channels per group, the tile-direct 3x3 dX kernel for grouped 3x3 pad-1 layers,
+    streaming kernels for depthwise layers) against the oracle's grouped / dilated
+    loops; overwrite, then accumulate in place."""
     torch = require_gpu()
     announce(f"grouped/dilated conv_block {case}")
     ref, got = run_conv(torch, case, seed=300 + GD_CASES.index(case))
