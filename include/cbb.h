@@ -185,7 +185,10 @@ int cbb_set_launch_hook(cbb_launch_hook fn, void* user);
  * the grid's y axis): the general implicit-GEMM kernels, except that grouped
  * undilated 3x3 pad-1 layers with in_c/groups a multiple of 32 and
  * out_c/groups a multiple of 64 take the row-streaming 3x3 weight-gradient
- * kernel, and depthwise layers (groups = in_c = out_c) take streaming kernels.
+ * kernel, grouped undilated 3x3 pad-1 layers with in_c/groups a multiple of 32
+ * and out_c/groups a multiple of 8 (16 at stride 2) take the tile-direct 3x3
+ * input-gradient kernel, and depthwise layers (groups = in_c = out_c) take
+ * streaming kernels.
  * ------------------------------------------------------------------------- */
 int cbb_conv_block_workspace_size(const cbb_conv_desc* desc, size_t* bytes);
 int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const float* w,
