@@ -130,14 +130,14 @@ def stage_work(runner, li, stage):
         # reads delta, y, x_hat and writes dz (BN); bias-only: reads delta (+ y)
         per = (16 if c.bn else (12 if c.act != "linear" else 4))
         return 0.0, float(per * out_elems)
+    # delta, y (unless linear, or the delta already holds g), x_hat
+    nread = 1 + (runner.convs[li]["y"] is not None) + bool(c.bn)
     if stage == "actbn_dW":
         # act/BN sums, then dW forming dz: x, delta, y, x_hat read once; dz, dW written
-        nread = 1 + (c.act != "linear") + bool(c.bn)
         return 2.0 * macs, 4.0 * (in_elems + (nread + 1) * out_elems + w_elems)
     if stage == "block":
         # act/BN stage and the fused dW + dX kernel with dz formed in place: x, W and the
         # saved delta, y, x_hat read once; dW, dx written
-        nread = 1 + (c.act != "linear") + bool(c.bn)
         return 4.0 * macs, 4.0 * (2 * in_elems + nread * out_elems + 2 * w_elems)
     if stage == "dWdX":  # both gradients from one read of dz: x, dz, W read; dW, dx written
         return 4.0 * macs, 4.0 * (2 * in_elems + out_elems + 2 * w_elems)
@@ -298,7 +298,7 @@ def kernel_work(runner, call, kernel):
     in_e = n * c.in_c * c.in_h * c.in_w
     w_e = c.out_c * c.in_c * c.k * c.k
     macs = out_e * c.in_c * c.k * c.k
-    nread = 1 + (c.act != "linear") + bool(c.bn)   # delta, y, x_hat
+    nread = 1 + (e["y"] is not None) + bool(c.bn)   # delta, y (unless not read), x_hat
     if role == "dWdX":
         zin = nread if e["form_dz"] else 1
         return 4.0 * macs, 4.0 * (2 * in_e + zin * out_e + 2 * w_e)

@@ -57,7 +57,8 @@ class BlockOpts(ctypes.Structure):
     """cbb_block_opts."""
     _fields_ = [("sums", ctypes.c_void_p), ("below_sums", ctypes.c_void_p),
                 ("below_y", ctypes.c_void_p), ("below_x_norm", ctypes.c_void_p),
-                ("below_act", ctypes.c_int32), ("below_slope", ctypes.c_float)]
+                ("below_act", ctypes.c_int32), ("below_slope", ctypes.c_float),
+                ("below_apply_act", ctypes.c_int32)]
 
 
 def conv_desc(batch, in_c, in_h, in_w, out_c, ksize, stride, pad, batch_normalize, act,
@@ -243,7 +244,8 @@ def conv_block_backward(desc: ConvDesc, x, w, y, x_norm, var, gamma, delta, dz, 
 
 def _block_opts(fn: str, desc: ConvDesc, sums, below) -> BlockOpts:
     """cbb_block_opts from `sums` (float32 [2*O]) and `below` (dict: "sums" [2*C] out,
-    "y" (None under linear) and "x_norm" [N,C,H,W] of the block below, "act", "slope")."""
+    "y" (None under linear) and "x_norm" [N,C,H,W] of the block below, "act", "slope",
+    and "apply_act": True to leave g = dx * act'(y) in dx)."""
     xs = (desc.batch, desc.in_c, desc.in_h, desc.in_w)
     opts = BlockOpts()
     if sums is not None:
@@ -260,6 +262,7 @@ def _block_opts(fn: str, desc: ConvDesc, sums, below) -> BlockOpts:
         act = below["act"]
         opts.below_act = ACT[act] if isinstance(act, str) else int(act)
         opts.below_slope = float(below.get("slope", 0.1))
+        opts.below_apply_act = int(bool(below.get("apply_act", False)))
     return opts
 
 

@@ -70,6 +70,8 @@ int check_desc(const cbb_conv_desc* d, ConvPlan* plan) {
 int check_block_opts(const cbb_conv_desc* d, const float* dx, const cbb_block_opts* o) {
   if (!o) return CBB_OK;
   if (o->sums && d->batch_normalize != CBB_BN_BATCH) return CBB_EINVAL;
+  if (o->below_apply_act != 0 && o->below_apply_act != 1) return CBB_EINVAL;
+  if (o->below_apply_act && !o->below_sums) return CBB_EINVAL;
   if (o->below_sums) {
     if (!dx || !o->below_x_norm) return CBB_EINVAL;
     if (o->below_act < CBB_ACT_LINEAR || o->below_act > CBB_ACT_LOGGY) return CBB_EINVAL;
@@ -82,14 +84,19 @@ int check_block_opts(const cbb_conv_desc* d, const float* dx, const cbb_block_op
 }
 
 // The block below's act/BN sums into opts->below_sums: folded from the partials
-// the input-gradient kernel wrote (bb->nseg > 0), else a reduction pass over dx.
-int below_sums(const cbb_conv_desc* d, const float* dx, const cbb_block_opts* o,
-               const BnBelow* bb, char* ws, hipStream_t st) {
+// the input-gradient kernel wrote (bb->nseg > 0; that kernel also stored g when
+// asked), else a reduction pass over dx, then (below_apply_act) dx *= act'(y).
+int below_sums(const cbb_conv_desc* d, float* dx, const cbb_block_opts* o, const BnBelow* bb,
+               char* ws, hipStream_t st) {
   float2* out = reinterpret_cast<float2*>(o->below_sums);
   if (bb && bb->nseg > 0) return launch_bn_sums_fold(bb->part, d->in_c, bb->nseg, out, st);
-  return launch_bn_sums(d->batch, d->in_c, (int64_t)d->in_h * d->in_w, dx,
-                        o->below_act == CBB_ACT_LINEAR ? nullptr : o->below_y, o->below_x_norm,
-                        o->below_act, o->below_slope, ws, out, st);
+  const bool lin = o->below_act == CBB_ACT_LINEAR;
+  const int64_t hw = (int64_t)d->in_h * d->in_w;
+  int rc = launch_bn_sums(d->batch, d->in_c, hw, dx, lin ? nullptr : o->below_y, o->below_x_norm,
+                          o->below_act, o->below_slope, ws, out, st);
+  if (rc || !o->below_apply_act || lin) return rc;
+  return launch_act_backward(o->below_act, o->below_slope, o->below_y, dx, dx,
+                             (int64_t)d->batch * d->in_c * hw, st);
 }
 
 // dW and (when dx is given) dX from dz: one fused kernel for the layers it
@@ -234,7 +241,7 @@ int cbb_conv_block_backward_ex(const cbb_conv_desc* desc, const float* x, const 
     char* wsb = ws + p.part_bytes + p.dw_bytes;
     BnBelow bb{opts && below ? opts->below_y : nullptr, below ? opts->below_x_norm : nullptr,
                below ? opts->below_act : 0, below ? opts->below_slope : 0.f,
-               reinterpret_cast<float2*>(wsb), 0};
+               reinterpret_cast<float2*>(wsb), 0, below ? opts->below_apply_act : 0};
     rc = launch_conv_dx(g, w, dz, dx, dx_accumulate, ws2, st, below ? &bb : nullptr);
     if (rc || !below) return rc;
     return below_sums(desc, dx, opts, &bb, wsb, st);
@@ -251,7 +258,7 @@ int cbb_conv_block_backward_ex(const cbb_conv_desc* desc, const float* x, const 
   if (rc) return rc;
   char* wsb = ws + p.part_bytes + p.dw_bytes;
   BnBelow bb{opts->below_y, opts->below_x_norm, opts->below_act, opts->below_slope,
-             reinterpret_cast<float2*>(wsb), 0};
+             reinterpret_cast<float2*>(wsb), 0, opts->below_apply_act};
   rc = launch_conv_dx(g, w, dz_eff, dx, dx_accumulate, ws2, st, &bb);
   if (rc) return rc;
   return below_sums(desc, dx, opts, &bb, wsb, st);
@@ -390,7 +397,7 @@ int cbb_conv_backward_data_ex(const cbb_conv_desc* desc, const float* w, const f
   char* wsb = ws + p.part_bytes + p.dw_bytes;
   BnBelow bb{below ? opts->below_y : nullptr, below ? opts->below_x_norm : nullptr,
              below ? opts->below_act : 0, below ? opts->below_slope : 0.f,
-             reinterpret_cast<float2*>(wsb), 0};
+             reinterpret_cast<float2*>(wsb), 0, below ? opts->below_apply_act : 0};
   rc = launch_conv_dx(make_geom(*desc), w, dz, dx, dx_accumulate,
                       reinterpret_cast<float*>(ws + p.part_bytes), S(stream),
                       below ? &bb : nullptr);

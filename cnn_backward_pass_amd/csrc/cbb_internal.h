@@ -310,7 +310,8 @@ struct BnBelow {
   int act;
   float slope;
   float2* part;
-  int nseg;
+  int nseg;    // > 0: the input-gradient kernel wrote nseg partials per channel
+  int apply;   // store g = dx * act'(y) in place of dx (the kernel does it when nseg > 0)
 };
 struct DzSource {
   const float* y;

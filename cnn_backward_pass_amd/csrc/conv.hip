@@ -1155,6 +1155,7 @@ __device__ float g_dx3_sink[4 * kThreads];
 // regroup, each thread keeps the sums of its 16 (pass, piece) channel slots over
 // all its tiles, and at the end the work-group adds them up (a fixed shuffle tree
 // per wave, then the two waves of a channel in order) into ba.part[c][blockIdx.x].
+// ba.apply: the stores hold g itself (the block below's activation step done).
 template <int NCH, int BA = kFzOff>
 __global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
                                                            const float* __restrict__ wt,
@@ -1341,18 +1342,19 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_s2p(ConvGeom g,
           const float4 a = *d;
           v.x += a.x; v.y += a.y; v.z += a.z; v.w += a.w;
         }
-        *d = v;
         if constexpr (sums) {
+          const int act = BA == kFzAny ? ba.act : BA;
+          const float g0 = v.x * act_grad(act, ba.slope, yv[k].x);
+          const float g1 = v.y * act_grad(act, ba.slope, yv[k].y);
+          const float g2 = v.z * act_grad(act, ba.slope, yv[k].z);
+          const float g3 = v.w * act_grad(act, ba.slope, yv[k].w);
           if (whole) {
-            const int act = BA == kFzAny ? ba.act : BA;
-            const float g0 = v.x * act_grad(act, ba.slope, yv[k].x);
-            const float g1 = v.y * act_grad(act, ba.slope, yv[k].y);
-            const float g2 = v.z * act_grad(act, ba.slope, yv[k].z);
-            const float g3 = v.w * act_grad(act, ba.slope, yv[k].w);
             ss[4 * pass + k][0] += (g0 + g1) + (g2 + g3);
             ss[4 * pass + k][1] += (g0 * xv[k].x + g1 * xv[k].y) + (g2 * xv[k].z + g3 * xv[k].w);
           }
+          if (ba.apply) v = make_float4(g0, g1, g2, g3);   // the delta below, act step done
         }
+        *d = v;
       }
     }
   };

@@ -81,18 +81,31 @@ class Runner:
         # Consecutive blocks whose upper input-gradient kernel adds up the lower block's
         # act/BN sums (batch statistics) as it writes that block's delta: the lower
         # call takes the sums instead of reducing its delta again (cbb_block_opts).
+        # The same epilogue reads the lower block's y, so it also leaves that block's
+        # g = delta * act'(y) in the delta (the in-place activation step done), and
+        # the lower call runs with a linear activation and reads no y.
         for e in self.convs:
             e["below"] = None
             e["sums_in"] = None
+        self.d_in_act = [None] * len(self.convs)   # d_in[li] holds g of this activation
         if name not in ("lenet", "darknet53_residual"):   # layer li-1's delta is li's dx
             for li in range(1, len(self.convs)):
                 lo, c_lo = self.convs[li - 1], wl.convs[li - 1]
                 if c_lo.bn and cbb.conv_fuses_below_sums(
                         self.convs[li]["desc"]):
                     lo["sums_in"] = torch.empty(2 * c_lo.out_c, dtype=f32, device=device)
+                    apply = c_lo.act != "linear"
                     self.convs[li]["below"] = {"sums": lo["sums_in"], "y": lo["y"],
                                                "x_norm": lo["xhat"], "act": c_lo.act,
-                                               "slope": synth.LEAKY_SLOPE}
+                                               "slope": synth.LEAKY_SLOPE, "apply_act": apply}
+                    if apply:
+                        self.d_in_act[li] = c_lo.act
+                        dl = lo["desc"]
+                        lo["desc"] = cbb.conv_desc(dl.batch, c_lo.in_c, c_lo.in_h, c_lo.in_w,
+                                                   c_lo.out_c, c_lo.k, c_lo.stride, c_lo.pad,
+                                                   c_lo.bn, "linear", synth.LEAKY_SLOPE,
+                                                   synth.BN_EPS)
+                        lo["y"] = None
         self.workspace = cbb.workspace(max(e["ws_bytes"] for e in self.convs), device)
         self.batch = self.convs[0]["desc"].batch
         n = self.batch
@@ -326,6 +339,8 @@ class Runner:
         out = {"dw": [h(e["dw"]) for e in self.convs], "db": [h(e["db"]) for e in self.convs],
                "dgamma": [h(e["dgamma"]) for e in self.convs],
                "d_in": [h(t) for t in self.d_in],
+               # None, or the activation whose g = delta * act'(y of conv li-1) d_in[li] holds
+               "d_in_act": list(self.d_in_act),
                # a layer whose dz the fused kernel forms in place stores none
                "dz": [None if e["form_dz"] else h(e["dz"]) for e in self.convs]}
         if self.name == "lenet":

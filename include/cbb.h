@@ -211,12 +211,19 @@ int cbb_conv_block_backward(const cbb_conv_desc* desc, const float* x, const flo
  *                 is this call's dx): float2 per input channel, as above.  Needs dx.
  *   below_y       that block's activation output [N,C,H,W] (NULL iff below_act is
  *                 LINEAR) and normalised conv output below_x_norm [N,C,H,W];
- *   below_act     its activation and leaky slope below_slope.
+ *   below_act     its activation and leaky slope below_slope;
+ *   below_apply_act  1: dx is left holding g = dx * act'(below_y) itself, the value
+ *                 the block below's activation step turns its delta into ([P1]
+ *                 sections 3.1 and 7: gradient_array scales the delta in place), so
+ *                 that block's call can run with a LINEAR activation and read no y;
+ *                 0: dx as without options.  Only 0 or 1, and 1 only with
+ *                 below_sums.
  * The sums are over dx as the call leaves it (after dx_accumulate).  Where dx is
  * written by the stride-2 3x3 kernel over one 32-channel block (16-byte aligned,
  * width a multiple of 4) the sums are added up in its epilogue; otherwise a
- * reduction pass over dx follows.  Results equal those of separate calls up to
- * the order of the summation. */
+ * reduction pass over dx follows (and, with below_apply_act, a pass that scales dx
+ * in place).  Results equal those of separate calls up to the order of the
+ * summation. */
 typedef struct cbb_block_opts {
   const float* sums;
   float* below_sums;
@@ -224,6 +231,7 @@ typedef struct cbb_block_opts {
   const float* below_x_norm;
   int32_t below_act;
   float below_slope;
+  int32_t below_apply_act;
 } cbb_block_opts;
 
 /* cbb_conv_block_backward with options (opts NULL: the same call); the same
@@ -301,7 +309,7 @@ int cbb_conv_backward_data(const cbb_conv_desc* desc, const float* w, const floa
                            int dx_accumulate, void* workspace, size_t workspace_bytes,
                            void* stream);
 /* Stage 3 with the act/BN sums of the block below (cbb_block_opts: below_sums,
- * below_y, below_x_norm, below_act, below_slope; sums must be NULL), the same
+ * below_y, below_x_norm, below_act, below_slope, below_apply_act; sums must be NULL), the same
  * workspace size. */
 int cbb_conv_backward_data_ex(const cbb_conv_desc* desc, const float* w, const float* dz,
                               float* dx, int dx_accumulate, const cbb_block_opts* opts,

@@ -52,3 +52,16 @@ def assert_exact(name, got, ref):
 
 def with_batch(wl, batch):
     return dataclasses.replace(wl, batch=batch)
+
+
+def expected_d_in(got, ref, saved, li):
+    """The oracle's value for a workload's d_in[li]: its delta of conv li-1's output, or,
+    where the runner left that block's g in it (results' "d_in_act"), that delta times
+    act'(y) of conv li-1 by the oracle's own activation gradient."""
+    act = got.get("d_in_act", [None] * (li + 1))[li]
+    if act is None:
+        return ref["d_in"][li]
+    import oracle
+    from cnn_backward_pass_amd import synth
+    y = saved["layers"][li - 1]["y"]
+    return oracle.act_backward(oracle.ACT_NAMES[act], synth.LEAKY_SLOPE, y, ref["d_in"][li])

@@ -317,8 +317,8 @@ def test_sgd_update_validates():
 def test_block_options_validate_on_the_host():
     """cbb_block_opts: sums only with batch statistics, below sums need dx, the block
     below's x_norm (and y unless it is linear) and a valid activation; tensors of the
-    block below without a place for its sums are refused; the data-only call takes no
-    sums of its own.  All refused before any HIP call."""
+    block below without a place for its sums are refused, and so is the apply flag
+    (0 or 1) without them; the data-only call takes no sums of its own.  All refused before any HIP call."""
     L = cbb.lib()
     names = ["x", "w", "y", "x_norm", "var", "gamma", "delta", "dz", "dw", "db", "dgamma", "dx"]
 
@@ -341,6 +341,10 @@ def test_block_options_validate_on_the_host():
     assert call(d, cbb.BlockOpts(below_sums=0x2000, below_x_norm=0x3000, below_act=14)) == -1
     assert call(d, cbb.BlockOpts(below_y=0x4000, below_x_norm=0x3000)) == -1
     assert call(d, cbb.BlockOpts(sums=0x2000, below_sums=0x2000, below_x_norm=0x3000)) == -1
+    # dx left holding g only where the sums below are made, and the flag is 0 or 1
+    assert call(d, cbb.BlockOpts(below_apply_act=1)) == -1
+    assert call(d, cbb.BlockOpts(below_sums=0x2000, below_y=0x4000, below_x_norm=0x3000,
+                                 below_act=1, below_apply_act=2)) == -1
     o4 = cbb.BlockOpts(sums=0x2000)
     assert L.cbb_conv_backward_data_ex(ctypes.byref(d), BOGUS, BOGUS, BOGUS, 0, ctypes.byref(o4),
                                        BOGUS, 1 << 30, None) == -1

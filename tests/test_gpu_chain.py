@@ -1,8 +1,10 @@
 """Two consecutive conv blocks in one chain of calls (cbb_block_opts): the upper call
 also produces the lower block's act/BN sums (in the stride-2 input-gradient kernel's
 epilogue where it can, else by a reduction pass over dx) and the lower call takes them
-instead of reducing its delta.  Both blocks are compared with the oracle's blocks
-run one after the other (the lower block's delta is the upper block's dx)."""
+instead of reducing its delta.  With below_apply_act the upper call leaves
+g = dx * act'(y) of the block below in dx, and the lower call runs with a linear
+activation on it.  Both blocks are compared with the oracle's blocks run one after the
+other (the lower block's delta is the upper block's dx)."""
 import types
 
 import numpy as np
@@ -45,12 +47,13 @@ CHAIN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("apply_act", [False, True])
 @pytest.mark.parametrize("case", CHAIN_CASES)
-def test_chained_blocks_match_oracle(case):
+def test_chained_blocks_match_oracle(case, apply_act):
     torch = require_gpu()
     from cnn_backward_pass_amd import cbb
     n, c0, c1, act0, c2, s1, h, w, acc, fused = case
-    announce(f"chained blocks {case}")
+    announce(f"chained blocks {case} apply_act {apply_act}")
     r = np.random.default_rng(4000 + CHAIN_CASES.index(case))
     L0 = _layer(c0, c1, 3, 1, 1, act0, h, w)
     L1 = _layer(c1, c2, 3, s1, 1, "leaky", h, w)
@@ -68,7 +71,8 @@ def test_chained_blocks_match_oracle(case):
                                  dx_init=prior if acc else None)
     ref0 = M.conv_block_backward(L0, s0, ref1["dx"], want_dx=True)
 
-    d0 = cbb.conv_desc(n, c0, h, w, c1, 3, 1, 1, 1, act0)
+    # the lower call: its own activation, or linear when dx already holds its g
+    d0 = cbb.conv_desc(n, c0, h, w, c1, 3, 1, 1, 1, "linear" if apply_act else act0)
     d1 = cbb.conv_desc(n, c1, h, w, c2, 3, s1, 1, 1, "leaky")
     assert cbb.conv_fuses_below_sums(d1) == fused
     T = lambda a: _t(torch, a)
@@ -86,7 +90,8 @@ def test_chained_blocks_match_oracle(case):
         cbb.conv_block_backward_ex(d1, T(s1_["x_in"]), T(w1), T(s1_["y"]), T(s1_["xhat"]),
                                    T(s1_["var"]), T(s1_["gamma"]), T(delta1), dz1, dw1, db1, dg1,
                                    dx1, acc, below={"sums": sums, "y": y0, "x_norm": xn0,
-                                                    "act": act0, "slope": 0.1},
+                                                    "act": act0, "slope": 0.1,
+                                                    "apply_act": apply_act},
                                    workspace=ws)
         upper = list(seen)
         form_dz = cbb.conv_fused_weights_data(d0)
@@ -94,8 +99,9 @@ def test_chained_blocks_match_oracle(case):
             torch.zeros(c1, device="cuda")
         dz0 = None if form_dz else torch.empty(s0["y"].shape, device="cuda")
         dx0 = torch.empty(x0.shape, device="cuda")
-        cbb.conv_block_backward_ex(d0, T(x0), T(w0), y0, xn0, T(s0["var"]), T(s0["gamma"]), dx1,
-                                   dz0, dw0, db0, dg0, dx0, False, sums=sums, workspace=ws)
+        cbb.conv_block_backward_ex(d0, T(x0), T(w0), None if apply_act else y0, xn0,
+                                   T(s0["var"]), T(s0["gamma"]), dx1, dz0, dw0, db0, dg0, dx0,
+                                   False, sums=sums, workspace=ws)
         lower = seen[len(upper):]
     finally:
         cbb.set_launch_hook(None)
@@ -107,9 +113,9 @@ def test_chained_blocks_match_oracle(case):
     assert_close("upper db", h_(db1), ref1["db"])
     assert_close("upper dgamma", h_(dg1), ref1["dgamma"])
     assert_close("upper dz", h_(dz1), ref1["dz"])
-    assert_close("upper dx", h_(dx1), ref1["dx"])
     # the sums the upper call left for the lower block: sum g, sum g * x_hat per channel
     g = ref1["dx"] * _act_grad(act0, s0["y"])
+    assert_close("upper dx", h_(dx1), g if apply_act else ref1["dx"])
     want = np.stack([g.sum(axis=(0, 2, 3)), (g * s0["xhat"]).sum(axis=(0, 2, 3))], axis=1)
     assert_close("below sums", h_(sums).reshape(-1, 2), want)
     assert_close("lower dw", h_(dw0), ref0["dw"])
@@ -139,6 +145,16 @@ def test_backward_data_with_sums_below():
     cbb.conv_backward_data(d, w, dz, ref, False, ws)
     torch.cuda.synchronize()
     assert torch.equal(dx, ref)    # the epilogue's sums change nothing it stores
-    gg = (ref * torch.where(y > 0, 1.0, 0.1)).double()
+    gf = ref * torch.where(y > 0, 1.0, 0.1)
+    gg = gf.double()
     want = torch.stack([gg.sum(dim=(0, 2, 3)), (gg * xn.double()).sum(dim=(0, 2, 3))], dim=1)
     assert_close("sums", sums.view(-1, 2).double().cpu().numpy(), want.cpu().numpy())
+    # dx left holding g: one fp32 product per element, as the activation step makes it
+    dx2, sums2 = torch.empty_like(dx), torch.empty_like(sums)
+    cbb.conv_backward_data_ex(d, w, dz, dx2, False,
+                              below={"sums": sums2, "y": y, "x_norm": xn, "act": "leaky",
+                                     "apply_act": True},
+                              workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dx2, gf)
+    assert torch.equal(sums2, sums)
