@@ -210,6 +210,169 @@ __global__ __launch_bounds__(kThreads) void conv_fwd_smallj(ConvGeom g, const fl
 }
 
 // ---------------------------------------------------------------------------
+// 3x3, pad-1, stride-2 forward (a downsampling layer: z of OH x OW from x of H x W)
+// as a tile-direct implicit GEMM on the matrix cores.  A work-group owns 64 output
+// channels (blockIdx.y) of one 16 x 16 output tile of one image and walks the input
+// channels 4 at a time.  Per chunk the input patch under the tile (rows 2*h0-1 ..
+// 2*h0+31, columns 2*w0-4 .. 2*w0+35 in 16-byte pieces; 0 off the image) is copied
+// into LDS once by the LDS-DMA loads (padding pieces read a zero page), and the chunk's
+// 64 x 36 weights go beside it as [channel, tap][o], copied in 16-byte pieces from the
+// weights transposed to that order once per call (wtr[(i*9 + tap)*OCP + o], OCP = OC
+// rounded up to 64, zero past OC: 64 consecutive o, where W's own order puts them C*9
+// floats apart, a cache line per lane).  One 32x32x2 step takes two input channels at
+// one tap (lanes 0-31 the first, 32-63 the second); each wave accumulates 2 (o) x 2
+// (32 pixels = two tile rows) blocks over the 18 steps of a chunk.  A tap reads every
+// other patch column (some bank conflicts: four LDS reads per 256 cycles of matrix
+// work leave the LDS far from its limit).  Two LDS buffers, declared apart so that the
+// compiler sees the copies into one never alias the matrix work's reads of the other:
+// the next chunk's copies are in flight during this chunk's matrix work, one wait and
+// one barrier per chunk.  A weight row (one (channel, tap) over 64 o) is 96 floats.
+// Needs a width that is a multiple of 4 and 16-byte aligned x (checked at launch).
+// ---------------------------------------------------------------------------
+constexpr int kF2Tile = 16, kF2CC = 4, kF2PR = 33, kF2XP = 40, kF2CP = kF2PR * kF2XP, kF2WP = 96;
+// 256-float copies (64 lanes x 16 bytes) per chunk: 21 of the patch, 14 of the weights
+constexpr int kF2XN = (kF2CC * kF2CP + 255) / 256, kF2WN = (kF2CC * 9 * kF2WP + 255) / 256;
+constexpr int kF2XFl = 256 * kF2XN, kF2WFl = 256 * kF2WN;   // floats per buffer
+
+// Source of the zero padding of the copies (never written).
+__device__ __align__(16) float g_fwd_zero[4];
+
+template <bool BIAS>
+__global__ __launch_bounds__(kThreads, 2) void conv_fwd3_s2(ConvGeom g, const float* __restrict__ x,
+                                                           const float* __restrict__ wtr,
+                                                           const float* __restrict__ bias,
+                                                           float* __restrict__ z, int tiles_h,
+                                                           int tiles_w) {
+  __shared__ float X0[kF2XFl], W0[kF2WFl], X1[kF2XFl], W1[kF2WFl];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int tpi = tiles_h * tiles_w;
+  const int b = blockIdx.x / tpi, tr = blockIdx.x - b * tpi;
+  const int h0 = (tr / tiles_w) * kF2Tile, w0 = (tr % tiles_w) * kF2Tile;
+  const int o0 = blockIdx.y * 64;
+  const float* xb = x + (int64_t)b * g.xs;
+  const int nch = (g.C + kF2CC - 1) / kF2CC;
+  const int ocp = (g.OC + 63) / 64 * 64;   // row pitch of the transposed weights
+
+  // offset inside a chunk of the 16-byte piece each of this lane's patch copies fetches
+  // (-1: padding), the same for every chunk.  Piece u: channel u / 330, patch row
+  // (u % 330) / 10, image columns 2*w0 - 4 + 4*(u % 10) .. + 3 (whole pieces: the width
+  // is a multiple of 4).
+  constexpr int XR = (kF2XN + 3) / 4;
+  int xofs[XR];
+#pragma unroll
+  for (int r = 0; r < XR; ++r) {
+    const int u = 64 * (wave + 4 * r) + lane;
+    const int ch = u / (kF2CP / 4), rem = u - ch * (kF2CP / 4);
+    const int row = rem / (kF2XP / 4), pc = rem - row * (kF2XP / 4);
+    const int h = 2 * h0 - 1 + row, w = 2 * w0 - 4 + 4 * pc;
+    const bool ok = ch < kF2CC && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+    xofs[r] = ok ? (ch * g.H + h) * g.W + w : -1;
+  }
+  auto issue = [&](int c, float* Xl, float* Wl) {
+    const int i0 = c * kF2CC;
+    const float* xc = xb + (int64_t)i0 * g.HW;
+#pragma unroll
+    for (int r = 0; r < XR; ++r) {
+      const int q = wave + 4 * r;
+      int xo = xofs[r];
+      asm volatile("" : "+v"(xo));   // keeps the 64-bit addresses from being hoisted
+      const int ch = (64 * q + lane) / (kF2CP / 4);
+      const float* src = xo >= 0 && i0 + ch < g.C ? xc + xo : g_fwd_zero;
+      if (q < kF2XN) __builtin_amdgcn_global_load_lds(src, lds_ptr(Xl + 256 * q), 16, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < (kF2WN + 3) / 4; ++r) {
+      const int q = wave + 4 * r;
+      const int u = 4 * (64 * q + lane), kk = u / kF2WP, o = u - kk * kF2WP;
+      const bool ok = kk < kF2CC * 9 && o < 64 && i0 + kk / 9 < g.C;
+      const float* src = ok ? wtr + (int64_t)(i0 * 9 + kk) * ocp + o0 + o : g_fwd_zero;
+      if (q < kF2WN) __builtin_amdgcn_global_load_lds(src, lds_ptr(Wl + 256 * q), 16, 0, 0);
+    }
+  };
+
+  // this lane's operand offsets: A = W[o0 + 32 m + l32][(2 pc + hi, tap)], B = patch of
+  // channel 2 pc + hi at pixel p = 32 nf + l32 (tile row p / 16, column p % 16) for the
+  // wave's two pixel blocks nf = 2 wave, 2 wave + 1
+  const int abase = hi * 9 * kF2WP + l32;
+  int bbase[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int p = 32 * (2 * wave + f) + l32;
+    bbase[f] = hi * kF2CP + 2 * (p >> 4) * kF2XP + 2 * (p & 15) + 3;
+  }
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][f][r] = 0.f;
+
+  auto compute = [&](const float* Xs, const float* Ws) {
+#pragma unroll
+    for (int pc = 0; pc < kF2CC / 2; ++pc)
+#pragma unroll
+      for (int t = 0; t < 9; ++t) {
+        const int kh = t / 3, kw = t % 3;
+        const int ao = (2 * pc * 9 + t) * kF2WP;
+        const int bo = 2 * pc * kF2CP + kh * kF2XP + kw;
+        const float a0 = Ws[abase + ao], a1 = Ws[abase + ao + 32];
+        const float b0 = Xs[bbase[0] + bo], b1 = Xs[bbase[1] + bo];
+        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+      }
+  };
+
+  // chunk c in buffer c & 1: wait for this wave's copies of it (nothing younger is in
+  // flight), barrier (everyone's have landed and the other buffer's readers are done),
+  // send the next chunk's copies into the other buffer, then the matrix work
+  issue(0, X0, W0);
+  for (int c = 0; c < nch; c += 2) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (c + 1 < nch) issue(c + 1, X1, W1);
+    compute(X0, W0);
+    if (c + 1 >= nch) break;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (c + 2 < nch) issue(c + 2, X0, W0);
+    compute(X1, W1);
+  }
+
+  // the biases added before the first store: no load is in flight among the stores
+  // (a wait for a load there would also wait for every store before it)
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float bv = bias[min(o0 + 32 * m + acc_row(r, lane), g.OC - 1)];
+        acc[m][0][r] += bv;
+        acc[m][1][r] += bv;
+        // the sums made here, not sunk into the conditional stores
+        asm volatile("" : "+v"(acc[m][0][r]), "+v"(acc[m][1][r]));
+      }
+  }
+  float* zb = z + (int64_t)b * g.zs;
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int p = 32 * (2 * wave + f) + l32;
+    const int ho = h0 + (p >> 4), wo = w0 + (p & 15);
+    if (ho >= g.OH || wo >= g.OW) continue;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = o0 + 32 * m + acc_row(r, lane);
+        if (o < g.OC) zb[(int64_t)o * g.OHW + ho * g.OW + wo] = acc[m][f][r];
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // A plain stride-1 forward is the input gradient of another convolution:
 //   z[n][o][h][w] = sum_{i,kh,kw} W[o][i][kh][kw] x[n][i][h + kh - P][w + kw - P]
 //                 = sum_{i,kh,kw} W'[i][o][kh][kw] x[n][i][h + P' - kh][w + P' - kw]
@@ -251,9 +414,33 @@ __global__ __launch_bounds__(kThreads) void flip_transpose_weights(const float* 
   }
 }
 
+// wtr[(i*9 + tap)*ocp + o] = W[o][i][tap] (0 for o >= oc): the stride-2 kernel's
+// weight order, ocp = oc rounded up to 64.
+__global__ __launch_bounds__(kThreads) void transpose_weights3(const float* __restrict__ w,
+                                                              float* __restrict__ wtr, int oc,
+                                                              int ocp, int c) {
+  const int64_t n = (int64_t)ocp * c * 9;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n;
+       e += (int64_t)gridDim.x * kThreads) {
+    const int64_t rem = e / ocp, o = e - rem * ocp;
+    wtr[e] = o < oc ? w[o * c * 9 + rem] : 0.f;
+  }
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+static bool forward_smallj(const ConvGeom& g) {
+  return g.G == 1 && g.J <= kSmallJ && g.OC <= kSmallJOc;
+}
+static bool forward_s2(const ConvGeom& g) {
+  return g.G == 1 && g.K == 3 && g.S == 2 && g.P == 1 && g.D == 1 && !forward_smallj(g);
+}
+
 // Scratch of the forward beyond the batch-norm partials: the flipped weights and
-// the input-gradient kernel's own workspace when the forward runs as a dX.
+// the input-gradient kernel's own workspace when the forward runs as a dX; the
+// transposed weights of the stride-2 kernel.
 size_t conv_forward_workspace(const ConvGeom& g, bool has_bias) {
+  if (forward_s2(g)) return align_up((size_t)ceil_div(g.OC, 64) * 64 * g.C * 9 * sizeof(float), 256);
   if (!forward_as_dx(g, has_bias)) return 0;
   const size_t wbytes = align_up((size_t)g.OC * g.C * g.K * g.K * sizeof(float), 256);
   return wbytes + conv_dx_workspace(transposed_geom(g));
@@ -274,11 +461,27 @@ int launch_conv_forward(const ConvGeom& g, const float* x, const float* wt, cons
     if (rc) return rc;
     return launch_conv_dx(t, wflip, x, z, 0, ws2, st);
   }
-  if (g.G == 1 && g.J <= kSmallJ && g.OC <= kSmallJOc) {
+  if (forward_smallj(g)) {
     const int64_t tiles = ceil_div(g.Q, 32);
     const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(tiles, 4), 8192);
     conv_fwd_smallj<<<blocks, kThreads, 0, st>>>(g, x, wt, bias, z, tiles);
     return check_launch("conv_fwd_smallj", st);
+  }
+  if (forward_s2(g) && g.W % 4 == 0 && aligned16(x)) {
+    float* wtr = ws;
+    const int ocp = (int)ceil_div(g.OC, 64) * 64;
+    const int64_t n = (int64_t)ocp * g.C * 9;
+    transpose_weights3<<<(unsigned)std::min<int64_t>(ceil_div(n, kThreads), 4096), kThreads, 0,
+                         st>>>(wt, wtr, g.OC, ocp, g.C);
+    const int rc = check_launch("transpose_weights3", st);
+    if (rc) return rc;
+    const int th = (int)ceil_div(g.OH, kF2Tile), tw = (int)ceil_div(g.OW, kF2Tile);
+    const dim3 grid((unsigned)((int64_t)g.N * th * tw), (unsigned)ceil_div(g.OC, 64));
+    if (bias)
+      conv_fwd3_s2<true><<<grid, kThreads, 0, st>>>(g, x, wtr, bias, z, th, tw);
+    else
+      conv_fwd3_s2<false><<<grid, kThreads, 0, st>>>(g, x, wtr, bias, z, th, tw);
+    return check_launch("conv_fwd3_s2", st);
   }
   ConvGeom s = g;
   s.C = g.C / g.G;

@@ -25,6 +25,10 @@ FWD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (1, 32, 20, 20, 80, 3, 1, 1, 0, "relu", 1, 1),       # bias: general kernel, more than 64 o
     (2, 2, 15, 17, 24, 3, 2, 1, 1, "leaky", 1, 1),       # short reduction (J = 18), stride 2
     (1, 3, 20, 21, 32, 3, 1, 2, 0, "relu", 1, 2),        # short reduction, dilated, bias
+    (2, 32, 40, 72, 64, 3, 2, 1, 1, "leaky", 1, 1),      # stride-2 tiles: 2 x 3, both ragged
+    (1, 6, 34, 36, 100, 3, 2, 1, 0, "relu", 1, 1),       # stride 2: 2 chunks, 2 o blocks, bias
+    (1, 6, 33, 35, 100, 3, 2, 1, 0, "relu", 1, 1),       # stride 2, width not a multiple of 4
+    (3, 5, 16, 16, 20, 3, 2, 1, 1, "leaky", 1, 1),       # stride 2: odd channel count
 ]
 
 
@@ -98,6 +102,26 @@ def test_conv_block_forward_parity(case):
         assert_close("x_norm", got["xhat"], ref["xhat"])
         assert_close("mean", got["mean"], ref["mean"])
         assert_close("var", got["var"], ref["var"])
+
+
+def test_stride2_forward_full_size_stem_conv2_sampled():
+    """The stem's stride-2 layer at its full batch and size (z + bias, so y is the
+    convolution itself), in the launch the benchmark times: 16 x 16 output windows at the
+    corners, the ragged edges and inside, against the oracle's convolution of the input
+    patch under each window (pad applied to the patch, the same definition)."""
+    import oracle
+    torch = require_gpu()
+    case = (16, 32, 416, 416, 64, 3, 2, 1, 0, "linear", 1, 1)
+    announce(f"stride-2 forward full size {case}")
+    x, wt, gamma, beta, bias, mean, var = _inputs(case, 78)
+    got, desc = gpu_forward(torch, case, x, wt, gamma, beta, bias, mean, var)
+    oh, ow = desc.out_h, desc.out_w
+    for b, h0, w0 in [(0, 0, 0), (15, oh - 16, ow - 16), (7, 100, 37), (3, 0, ow - 16),
+                      (11, oh - 16, 5), (5, 61, 144)]:
+        xp = np.pad(x[b], ((0, 0), (1, 1), (1, 1)))
+        patch = xp[:, 2 * h0:2 * h0 + 33, 2 * w0:2 * w0 + 33][None]
+        ref = oracle.conv_forward(patch, wt, 2, 0, bias=bias)[0]
+        assert_close(f"y window {(b, h0, w0)}", got["y"][b, :, h0:h0 + 16, w0:w0 + 16], ref)
 
 
 def test_conv_block_forward_full_size_residual_conv2():
