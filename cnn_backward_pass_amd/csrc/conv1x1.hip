@@ -205,6 +205,30 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_dx_dma(ConvGeom g, const 
   dma_ring<NS, AI + BI>((g.OC + BK - 1) / BK, issue, fetch, mma);
 
   // ---- epilogue: lane holds pixel q of column `col` of each block, channels acc_row(r)
+  if (accumulate) {
+    // every earlier value read (clamped addresses, so each load is issued) and added
+    // before the first store: a wait for a load among the stores would also wait for
+    // every store before it
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      const int64_t q = min(q0 + wn * (TN / 2) + j * 32 + col, g.Q - 1);
+      const int n = (int)q / g.HW, p = (int)q - n * g.HW;
+      const float* base = dx + (int64_t)n * g.C * g.HW + p;
+#pragma unroll
+      for (int i = 0; i < RM; ++i) {
+        const int cb = i0 + wm * (TM / 2) + i * 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[i][j][r] += base[(int64_t)min(cb + acc_row(r, lane), g.C - 1) * g.HW];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RN; ++j)
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) asm volatile("" : "+v"(acc[i][j][r]));
+  }
 #pragma unroll
   for (int j = 0; j < RN; ++j) {
     const int64_t q = q0 + wn * (TN / 2) + j * 32 + col;
@@ -214,24 +238,10 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_dx_dma(ConvGeom g, const 
 #pragma unroll
     for (int i = 0; i < RM; ++i) {
       const int cb = i0 + wm * (TM / 2) + i * 32;
-      if (accumulate) {   // all reads of the block first, then the stores
-        float old[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = cb + acc_row(r, lane);
-          old[r] = c < g.C ? base[(int64_t)c * g.HW] : 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = cb + acc_row(r, lane);
-          if (c < g.C) base[(int64_t)c * g.HW] = old[r] + acc[i][j][r];
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = cb + acc_row(r, lane);
-          if (c < g.C) base[(int64_t)c * g.HW] = acc[i][j][r];
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int c = cb + acc_row(r, lane);
+        if (c < g.C) base[(int64_t)c * g.HW] = acc[i][j][r];
       }
     }
   }
