@@ -431,49 +431,12 @@ __global__ __launch_bounds__(kThreads) void act_backward_scalar(int act, float s
 // u = gamma x_norm + beta (scale_bias, add_bias), y = act(u) (section 7's
 // *_activate functions).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float act_fwd(int act, float slope, float u) {
-  switch (act) {
-    case CBB_ACT_LEAKY: return u > 0.f ? u : slope * u;
-    case CBB_ACT_LOGISTIC: return 1.f / (1.f + expf(-u));
-    case CBB_ACT_RELU: return u > 0.f ? u : 0.f;
-    case CBB_ACT_TANH: return tanhf(u);
-    case CBB_ACT_ELU: return u >= 0.f ? u : expm1f(u);
-    case CBB_ACT_SELU: return u >= 0.f ? 1.0507f * u : 1.0507f * 1.6732f * expm1f(u);
-    case CBB_ACT_PLSE:
-      if (u < -4.f) return .01f * (u + 4.f);
-      if (u > 4.f) return .01f * (u - 4.f) + 1.f;
-      return .125f * u + .5f;
-    case CBB_ACT_LHTAN:
-      if (u < 0.f) return .001f * u;
-      if (u > 1.f) return .001f * (u - 1.f) + 1.f;
-      return u;
-    case CBB_ACT_HARDTAN: return u < -1.f ? -1.f : (u > 1.f ? 1.f : u);
-    case CBB_ACT_STAIR: {
-      const float n = floorf(u);
-      return fmodf(n, 2.f) == 0.f ? floorf(u * .5f) : (u - n) + floorf(u * .5f);
-    }
-    case CBB_ACT_RAMP: return (u > 0.f ? u : 0.f) + .1f * u;
-    case CBB_ACT_RELIE: return u > 0.f ? u : .01f * u;
-    case CBB_ACT_LOGGY: return 2.f / (1.f + expf(-u)) - 1.f;
-    default: return u;
-  }
-}
 
 // Batch statistics in one pass.  Each thread sums d = z - K and d^2 with K its own
 // first element (a shift inside the data keeps the sums small), turns them into
 // (count, mean, M2 = sum of squared deviations), and the work-group merges the 256
-// triples pairwise in a fixed tree (Chan, Golub and LeVeque's update:
-// mean = mean_a + d n_b / n, M2 = M2_a + M2_b + d^2 n_a n_b / n with d = mean_b - mean_a)
-// into its segment's (mean, M2); bnf_stats_fold merges the segments in order.
-struct Moments {
-  float n, mean, m2;
-};
-__device__ __forceinline__ Moments merge_moments(Moments a, Moments b) {
-  if (b.n == 0.f) return a;
-  if (a.n == 0.f) return b;
-  const float n = a.n + b.n, d = b.mean - a.mean, fb = b.n / n;
-  return Moments{n, a.mean + d * fb, a.m2 + b.m2 + d * d * a.n * fb};
-}
+// triples pairwise in a fixed tree (merge_moments) into its segment's (mean, M2);
+// bnf_stats_fold merges the segments in order.
 
 // elements in segment sg of a channel (the split of for_segment)
 __device__ __forceinline__ int64_t seg_count(const SegGeom& s, int sg) {

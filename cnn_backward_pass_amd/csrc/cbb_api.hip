@@ -292,6 +292,10 @@ int cbb_conv_block_forward(const cbb_conv_desc* desc, const float* x, const floa
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign))
     return CBB_EWORKSPACE;
   hipStream_t st = S(stream);
+  float* wsf = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_bytes);
+  if (conv_forward_first_fused(g, bn))
+    return launch_conv_block_forward_first(g, x, w, bn, desc->bn_eps, desc->act, desc->slope,
+                                           gamma, beta, mean, var, x_norm, y, wsf, st);
   // z goes where it is consumed: into x_norm (normalised in place) or, without BN, into y
   rc = launch_conv_forward(g, x, w, bn ? nullptr : bias, bn ? x_norm : y,
                            reinterpret_cast<float*>(static_cast<char*>(workspace) + p.part_bytes),

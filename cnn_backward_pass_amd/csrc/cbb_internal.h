@@ -290,6 +290,48 @@ __device__ __forceinline__ float act_grad(int act, float slope, float y) {
   }
 }
 
+// Activation of u (the forward's *_activate functions, "YOLOv3 backpropagation",
+// section 7).
+__device__ __forceinline__ float act_fwd(int act, float slope, float u) {
+  switch (act) {
+    case CBB_ACT_LEAKY: return u > 0.f ? u : slope * u;
+    case CBB_ACT_LOGISTIC: return 1.f / (1.f + expf(-u));
+    case CBB_ACT_RELU: return u > 0.f ? u : 0.f;
+    case CBB_ACT_TANH: return tanhf(u);
+    case CBB_ACT_ELU: return u >= 0.f ? u : expm1f(u);
+    case CBB_ACT_SELU: return u >= 0.f ? 1.0507f * u : 1.0507f * 1.6732f * expm1f(u);
+    case CBB_ACT_PLSE:
+      if (u < -4.f) return .01f * (u + 4.f);
+      if (u > 4.f) return .01f * (u - 4.f) + 1.f;
+      return .125f * u + .5f;
+    case CBB_ACT_LHTAN:
+      if (u < 0.f) return .001f * u;
+      if (u > 1.f) return .001f * (u - 1.f) + 1.f;
+      return u;
+    case CBB_ACT_HARDTAN: return u < -1.f ? -1.f : (u > 1.f ? 1.f : u);
+    case CBB_ACT_STAIR: {
+      const float n = floorf(u);
+      return fmodf(n, 2.f) == 0.f ? floorf(u * .5f) : (u - n) + floorf(u * .5f);
+    }
+    case CBB_ACT_RAMP: return (u > 0.f ? u : 0.f) + .1f * u;
+    case CBB_ACT_RELIE: return u > 0.f ? u : .01f * u;
+    case CBB_ACT_LOGGY: return 2.f / (1.f + expf(-u)) - 1.f;
+    default: return u;
+  }
+}
+// (count, mean, M2 = sum of squared deviations) of a run of values, and the merge of
+// two runs (Chan, Golub and LeVeque's update: mean = mean_a + d n_b / n,
+// M2 = M2_a + M2_b + d^2 n_a n_b / n with d = mean_b - mean_a).
+struct Moments {
+  float n, mean, m2;
+};
+__device__ __forceinline__ Moments merge_moments(Moments a, Moments b) {
+  if (b.n == 0.f) return a;
+  if (a.n == 0.f) return b;
+  const float n = a.n + b.n, d = b.mean - a.mean, fb = b.n / n;
+  return Moments{n, a.mean + d * fb, a.m2 + b.m2 + d * d * a.n * fb};
+}
+
 bool conv_fused_dwdx_ok(const ConvGeom& g);
 size_t conv_fused_workspace(const ConvGeom& g);
 // dz of a block formed while it is staged instead of read back: with dz = delta,
@@ -351,6 +393,13 @@ int launch_bn_act_forward(int N, int C, int64_t HW, int bn, float eps, int act, 
                           float* xn, float* y, void* ws, hipStream_t st);
 bool conv_dx_specialised(const ConvGeom& g);
 size_t conv_forward_workspace(const ConvGeom& g, bool has_bias);
+// The block forward of a short-reduction layer (C*K*K <= 32, at most 32 output channels)
+// with BN in kernels that compute z again instead of storing it.
+bool conv_forward_first_fused(const ConvGeom& g, int bn);
+int launch_conv_block_forward_first(const ConvGeom& g, const float* x, const float* wt, int bn,
+                                    float eps, int act, float slope, const float* gamma,
+                                    const float* beta, float* mean, float* var, float* xn,
+                                    float* y, float* ws, hipStream_t st);
 int launch_conv_forward(const ConvGeom& g, const float* x, const float* wt, const float* bias,
                         float* z, float* ws, hipStream_t st);
 int launch_shortcut(int64_t count, float alpha, float beta, const float* delta, float* d_main,

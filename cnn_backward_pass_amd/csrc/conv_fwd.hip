@@ -210,6 +210,215 @@ __global__ __launch_bounds__(kThreads) void conv_fwd_smallj(ConvGeom g, const fl
 }
 
 // ---------------------------------------------------------------------------
+// The whole block forward of a layer with a short reduction (C*K*K <= 32, at most 32
+// output channels) and batch normalisation, without ever storing z: its convolution
+// costs 16 matrix-core steps per 32 pixels, far less than writing z and reading it
+// back twice (statistics, then normalisation), so each of the two passes below
+// computes z again from x, the way conv_fwd_smallj does.
+//   fwd_first_stats: work-group blk takes pixels [blk*L, min(Q, (blk+1)*L)) of the
+//     flattened (image, pixel) index for every output channel; each lane keeps, per
+//     accumulator row (channel), the sums of d = z - K and d^2 with K the first z it
+//     saw (as bnf_stats does), turns them into (count, mean, M2), and the 32 lanes of a
+//     channel merge in a fixed butterfly, then the four waves in order, into
+//     part[c][blk] = (mean, M2).
+//   fwd_first_fold: per channel, one wave merges the work-groups' moments in double
+//     (each lane a contiguous run in order, then a fixed butterfly): mean, biased var.
+//   fwd_first_apply: z again, x_norm = (z - mean)/sqrt(var + eps), y = act(gamma x_norm
+//     + beta) (bnf_apply's arithmetic), both stored; with fixed statistics only this.
+// ---------------------------------------------------------------------------
+struct FirstTaps {
+  int off[kSmallJ], dh[kSmallJ], dw[kSmallJ];
+};
+// fwd_first_apply's activation as a template argument (the common ones compile to
+// straight-line code); kActAnyFwd takes it from the run-time argument
+constexpr int kActAnyFwd = -1;
+// per tap j: its input-plane offset and its row / column shift under the window (taps
+// past J get a shift that is never inside the image: their operand is 0)
+__device__ __forceinline__ void first_taps(const ConvGeom& g, FirstTaps& t) {
+  if (threadIdx.x < kSmallJ) {
+    const int j = threadIdx.x, KK = g.K * g.K;
+    const int i = j / KK, r = j - i * KK, kh = r / g.K, kw = r - kh * g.K;
+    t.off[j] = j < g.J ? i * g.HW : 0;
+    t.dh[j] = j < g.J ? kh * g.D : -(1 << 28);
+    t.dw[j] = j < g.J ? kw * g.D : 0;
+  }
+}
+// z of output pixel q (lane's column) for the 16 channels of this lane's accumulator
+// rows: 16 steps of 32x32x2 over the taps 2s + lane / 32
+__device__ __forceinline__ f32x16 first_z(const ConvGeom& g, const float* __restrict__ x,
+                                          const FirstTaps& t, const float (&wa)[16], int64_t q,
+                                          bool qv, int kq) {
+  int b = 0, h0 = 0, w0 = 0;
+  if (qv) {
+    const uint32_t qq = (uint32_t)q;   // Q < 2^31 (checked on the host)
+    b = (int)(qq / (uint32_t)g.OHW);
+    const int r = (int)(qq - (uint32_t)b * (uint32_t)g.OHW);
+    const int ho = r / g.OW, wo = r - ho * g.OW;
+    h0 = ho * g.S - g.P;
+    w0 = wo * g.S - g.P;
+  }
+  const float* xb = x + (int64_t)b * g.xs;
+  float bv[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int j = 2 * s + kq;
+    const int h = h0 + t.dh[j], w = w0 + t.dw[j];
+    const bool ok = qv && (unsigned)h < (unsigned)g.H && (unsigned)w < (unsigned)g.W;
+    bv[s] = ok ? xb[t.off[j] + h * g.W + w] : 0.f;
+  }
+  f32x16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(wa[s], bv[s], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ void first_weights(const ConvGeom& g, const float* __restrict__ wt,
+                                              float (&wa)[16], int lane) {
+  const int m = lane & 31, kq = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 16; ++s) {
+    const int j = 2 * s + kq;
+    wa[s] = (m < g.OC && j < g.J) ? wt[m * g.J + j] : 0.f;
+  }
+}
+__device__ __forceinline__ Moments shfl_moments(Moments m, int lane_mask) {
+  return Moments{__shfl_xor(m.n, lane_mask), __shfl_xor(m.mean, lane_mask),
+                 __shfl_xor(m.m2, lane_mask)};
+}
+
+__global__ __launch_bounds__(kThreads) void fwd_first_stats(ConvGeom g, const float* __restrict__ x,
+                                                           const float* __restrict__ wt,
+                                                           int64_t L, float2* __restrict__ part) {
+  __shared__ FirstTaps taps;
+  __shared__ Moments red[4][32];
+  first_taps(g, taps);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, kq = lane >> 5;
+  float wa[16];
+  first_weights(g, wt, wa, lane);
+  const int64_t q0 = (int64_t)blockIdx.x * L, q1 = min(g.Q, q0 + L);
+  float K[16], s1[16], s2[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) K[r] = s1[r] = s2[r] = 0.f;
+  int cnt = 0;
+  for (int64_t t0 = q0 + 32 * wave; t0 < q1; t0 += 128) {
+    const int64_t q = t0 + (lane & 31);
+    const bool qv = q < q1;
+    const f32x16 z = first_z(g, x, taps, wa, q, qv, kq);
+    if (qv) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (cnt == 0) K[r] = z[r];
+        const float d = z[r] - K[r];
+        s1[r] += d;
+        s2[r] += d * d;
+      }
+      ++cnt;
+    }
+  }
+  // per channel row r: this lane's moments, then the 32 lanes holding the channel
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    Moments m{0.f, 0.f, 0.f};
+    if (cnt > 0) {
+      const float n = (float)cnt, mu = s1[r] / n;
+      m = Moments{n, K[r] + mu, fmaxf(s2[r] - s1[r] * mu, 0.f)};
+    }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) {
+      const Moments o = shfl_moments(m, off);
+      // the lower lane of each pair keeps (lower, upper); both end with the same value
+      m = (lane & off) ? merge_moments(o, m) : merge_moments(m, o);
+    }
+    if ((lane & 31) == 0) red[wave][acc_row(r, lane)] = m;
+  }
+  __syncthreads();
+  const int c = threadIdx.x;
+  if (c < g.OC) {
+    Moments m = red[0][c];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) m = merge_moments(m, red[w][c]);
+    part[(int64_t)c * gridDim.x + blockIdx.x] = make_float2(m.mean, m.m2);
+  }
+}
+
+__global__ __launch_bounds__(64) void fwd_first_fold(const float2* __restrict__ part, int nblk,
+                                                     int64_t L, int64_t Q, float* __restrict__ mean,
+                                                     float* __restrict__ var) {
+  const int c = blockIdx.x, lane = threadIdx.x;
+  const int per = (nblk + 63) / 64, b0 = lane * per, b1 = min(nblk, b0 + per);
+  double n = 0.0, mu = 0.0, m2 = 0.0;
+  for (int b = b0; b < b1; ++b) {
+    const double nb = (double)(min(Q, (int64_t)(b + 1) * L) - (int64_t)b * L);
+    const float2 v = part[(int64_t)c * nblk + b];
+    const double tot = n + nb, d = (double)v.x - mu;
+    mu += d * nb / tot;
+    m2 += (double)v.y + d * d * n * nb / tot;
+    n = tot;
+  }
+  // lanes hold consecutive runs: merge (lower, upper) pairs in a fixed butterfly
+  for (int off = 1; off < 64; off <<= 1) {
+    const double on = __shfl_xor(n, off), omu = __shfl_xor(mu, off), om2 = __shfl_xor(m2, off);
+    double an = n, amu = mu, am2 = m2, bn = on, bmu = omu, bm2 = om2;
+    if (lane & off) { an = on; amu = omu; am2 = om2; bn = n; bmu = mu; bm2 = m2; }
+    const double tot = an + bn;
+    if (bn == 0.0) { n = an; mu = amu; m2 = am2; }
+    else if (an == 0.0) { n = bn; mu = bmu; m2 = bm2; }
+    else {
+      const double d = bmu - amu;
+      mu = amu + d * bn / tot;
+      m2 = am2 + bm2 + d * d * an * bn / tot;
+      n = tot;
+    }
+  }
+  if (lane == 0) {
+    mean[c] = (float)mu;
+    var[c] = (float)(m2 / n);
+  }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(kThreads, 4) void fwd_first_apply(
+    ConvGeom g, const float* __restrict__ x, const float* __restrict__ wt,
+    const float* __restrict__ mean, const float* __restrict__ var,
+    const float* __restrict__ gamma, const float* __restrict__ beta, float eps, int act,
+    float slope, float* __restrict__ xn, float* __restrict__ y, int64_t tiles) {
+  __shared__ FirstTaps taps;
+  __shared__ float prm[4][32];   // per channel: mean, 1/sqrt(var + eps), gamma, beta
+  first_taps(g, taps);
+  if (threadIdx.x < 32) {
+    const int o = min((int)threadIdx.x, g.OC - 1);
+    prm[0][threadIdx.x] = mean[o];
+    prm[1][threadIdx.x] = 1.f / sqrtf(var[o] + eps);
+    prm[2][threadIdx.x] = gamma[o];
+    prm[3][threadIdx.x] = beta[o];
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, kq = lane >> 5;
+  float wa[16];
+  first_weights(g, wt, wa, lane);
+  const int a = ACT == kActAnyFwd ? act : ACT;
+  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < tiles;
+       tile += (int64_t)gridDim.x * 4) {
+    const int64_t q = tile * 32 + (lane & 31);
+    const bool qv = q < g.Q;
+    const f32x16 z = first_z(g, x, taps, wa, q, qv, kq);
+    if (!qv) continue;
+    const uint32_t b = (uint32_t)q / (uint32_t)g.OHW;
+    const int64_t p = (int64_t)b * g.zs + ((uint32_t)q - b * (uint32_t)g.OHW);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int o = acc_row(r, lane);
+      if (o >= g.OC) continue;
+      const float xh = (z[r] - prm[0][o]) * prm[1][o];
+      xn[p + (int64_t)o * g.OHW] = xh;
+      y[p + (int64_t)o * g.OHW] = act_fwd(a, slope, prm[2][o] * xh + prm[3][o]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 3x3, pad-1, stride-2 forward (a downsampling layer: z of OH x OW from x of H x W)
 // as a tile-direct implicit GEMM on the matrix cores.  A work-group owns 64 output
 // channels (blockIdx.y) of one 16 x 16 output tile of one image and walks the input
@@ -436,14 +645,63 @@ static bool forward_s2(const ConvGeom& g) {
   return g.G == 1 && g.K == 3 && g.S == 2 && g.P == 1 && g.D == 1 && !forward_smallj(g);
 }
 
+// Pixels per work-group of fwd_first_stats: at most 768 work-groups (one round at three
+// per CU), at least 512 pixels each, a multiple of 128 (one 32-pixel tile per wave per
+// step).
+static int64_t first_stats_len(const ConvGeom& g) {
+  return std::max<int64_t>(512, ceil_div(ceil_div(g.Q, 768), 128) * 128);
+}
+
+bool conv_forward_first_fused(const ConvGeom& g, int bn) {
+  return bn && forward_smallj(g) && g.Q < ((int64_t)1 << 31);   // 32-bit pixel division
+}
+
+// The fused block forward of a short-reduction layer with batch normalisation (bn 1:
+// batch statistics, written to mean / var; 2: fixed, read).  ws: the moments,
+// OC x ceil(Q / L) float2.
+int launch_conv_block_forward_first(const ConvGeom& g, const float* x, const float* wt, int bn,
+                                    float eps, int act, float slope, const float* gamma,
+                                    const float* beta, float* mean, float* var, float* xn,
+                                    float* y, float* ws, hipStream_t st) {
+  if (bn == 1) {
+    const int64_t L = first_stats_len(g);
+    const int nblk = (int)ceil_div(g.Q, L);
+    float2* part = reinterpret_cast<float2*>(ws);
+    fwd_first_stats<<<(unsigned)nblk, kThreads, 0, st>>>(g, x, wt, L, part);
+    int rc = check_launch("fwd_first_stats", st);
+    if (rc) return rc;
+    fwd_first_fold<<<(unsigned)g.OC, 64, 0, st>>>(part, nblk, L, g.Q, mean, var);
+    rc = check_launch("fwd_first_fold", st);
+    if (rc) return rc;
+  }
+  const int64_t tiles = ceil_div(g.Q, 32);
+  const unsigned blocks = (unsigned)std::min<int64_t>(ceil_div(tiles, 4), 8192);
+#define CBB_FIRST(A)                                                                        \
+  fwd_first_apply<A><<<blocks, kThreads, 0, st>>>(g, x, wt, mean, var, gamma, beta, eps, act, \
+                                                  slope, xn, y, tiles)
+  if (act == CBB_ACT_LEAKY) CBB_FIRST(CBB_ACT_LEAKY);
+  else if (act == CBB_ACT_LINEAR) CBB_FIRST(CBB_ACT_LINEAR);
+  else if (act == CBB_ACT_RELU) CBB_FIRST(CBB_ACT_RELU);
+  else CBB_FIRST(kActAnyFwd);
+#undef CBB_FIRST
+  return check_launch("fwd_first_apply", st);
+}
+
 // Scratch of the forward beyond the batch-norm partials: the flipped weights and
 // the input-gradient kernel's own workspace when the forward runs as a dX; the
-// transposed weights of the stride-2 kernel.
+// transposed weights of the stride-2 kernel; the moments of the fused first-layer
+// forward.
 size_t conv_forward_workspace(const ConvGeom& g, bool has_bias) {
-  if (forward_s2(g)) return align_up((size_t)ceil_div(g.OC, 64) * 64 * g.C * 9 * sizeof(float), 256);
-  if (!forward_as_dx(g, has_bias)) return 0;
-  const size_t wbytes = align_up((size_t)g.OC * g.C * g.K * g.K * sizeof(float), 256);
-  return wbytes + conv_dx_workspace(transposed_geom(g));
+  size_t bytes = 0;
+  if (forward_smallj(g))
+    bytes = align_up((size_t)g.OC * ceil_div(g.Q, first_stats_len(g)) * sizeof(float2), 256);
+  if (forward_s2(g))
+    bytes = std::max(bytes, align_up((size_t)ceil_div(g.OC, 64) * 64 * g.C * 9 * sizeof(float), 256));
+  if (forward_as_dx(g, has_bias)) {
+    const size_t wbytes = align_up((size_t)g.OC * g.C * g.K * g.K * sizeof(float), 256);
+    bytes = std::max(bytes, wbytes + conv_dx_workspace(transposed_geom(g)));
+  }
+  return bytes;
 }
 
 // z = conv(x, W) (+ bias).  g is the whole layer's geometry; a grouped layer runs

@@ -29,6 +29,8 @@ FWD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (1, 6, 34, 36, 100, 3, 2, 1, 0, "relu", 1, 1),       # stride 2: 2 chunks, 2 o blocks, bias
     (1, 6, 33, 35, 100, 3, 2, 1, 0, "relu", 1, 1),       # stride 2, width not a multiple of 4
     (3, 5, 16, 16, 20, 3, 2, 1, 1, "leaky", 1, 1),       # stride 2: odd channel count
+    (2, 3, 20, 24, 32, 3, 1, 1, 2, "relu", 1, 1),        # first layer, fixed statistics
+    (1, 3, 18, 19, 8, 3, 1, 1, 1, "tanh", 1, 1),         # first layer, run-time activation
 ]
 
 
@@ -122,6 +124,21 @@ def test_stride2_forward_full_size_stem_conv2_sampled():
         patch = xp[:, 2 * h0:2 * h0 + 33, 2 * w0:2 * w0 + 33][None]
         ref = oracle.conv_forward(patch, wt, 2, 0, bias=bias)[0]
         assert_close(f"y window {(b, h0, w0)}", got["y"][b, :, h0:h0 + 16, w0:w0 + 16], ref)
+
+
+def test_first_layer_forward_full_size_stem_conv1():
+    """The stem's first layer at its full batch and size, in the launch the benchmark
+    times (z computed twice, never stored: statistics, then x_norm and y), every element
+    and the statistics against the oracle in double."""
+    torch = require_gpu()
+    case = (16, 3, 416, 416, 32, 3, 1, 1, 1, "leaky", 1, 1)
+    announce(f"first-layer forward full size {case}")
+    x, wt, gamma, beta, bias, mean, var = _inputs(case, 79)
+    got, _ = gpu_forward(torch, case, x, wt, gamma, beta, bias, mean, var)
+    L = _layer(3, 32, 3, 1, 1, 1, "leaky", 416, 416, 1, 1)
+    ref = M.conv_block_forward(L, x, wt, gamma=gamma, beta=beta)
+    for key in ("y", "xhat", "mean", "var"):
+        assert_close(key, got[key], ref[key])
 
 
 def test_conv_block_forward_full_size_residual_conv2():
