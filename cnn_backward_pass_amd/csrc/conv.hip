@@ -745,7 +745,9 @@ __global__ __launch_bounds__(kThreads) void conv_dx_kernel(ConvGeom g, const flo
 }
 
 // ---------------------------------------------------------------------------
-// Input gradient of a 3x3, pad-1 convolution at stride 1 or 2 ("tile-direct").
+// Input gradient of a 3x3, pad-1 convolution at stride 1 or 2 ("tile-direct"); at
+// stride 1 also dilation DIL = 2 with pad 2 (the halo and the tap offsets scale by DIL,
+// a compile-time constant so that the offsets stay immediates).
 // The GEMM above fetches dz once per tap; here a work-group stages one dz tile
 // (with its halo) and the matching weights in LDS per chunk of 16 output
 // channels and runs all nine taps from LDS, so every dz element crosses the
@@ -779,11 +781,11 @@ struct Dx3Cfg {
 };
 
 // Stride-1 tile of 128*F pixels of a W-wide image spans at most floor((128F-1)/W) + 2
-// rows; with the 3x3 halo the dz tile is (that + 2) x (W + 2).
-static bool dx3_s1_fits(int W, int F, int zplane) {
-  if (W < 8 || W > 62) return false;
+// rows; with the halo of a 3x3 window at dilation D the dz tile is (that + 2D) x (W + 2D).
+static bool dx3_s1_fits(int W, int F, int zplane, int D = 1) {
+  if (W < 8 || W + 2 * D > 64) return false;
   const int rows = (128 * F - 1) / W + 2;
-  return (rows + 2) * (W + 2) <= zplane;
+  return (rows + 2 * D) * (W + 2 * D) <= zplane;
 }
 
 // Source of the zero padding staged by the LDS-DMA loads (never written).
@@ -796,7 +798,7 @@ __device__ float g_dx3_zero[4];
 // Z4 (DMA, dz width a multiple of 4, 16-byte aligned dz): the dz tile is copied
 // in 16-byte pieces (a quarter of the copy instructions); its rows span columns
 // -4 .. W+3 at stride 1 and 36 columns at stride 2.
-template <int S, int F, int RM, bool DMA, bool Z4>
+template <int S, int F, int RM, bool DMA, bool Z4, int DIL = 1>
 __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const float* __restrict__ wt,
                                                             const float* __restrict__ dz,
                                                             float* __restrict__ dx,
@@ -839,13 +841,15 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
   int ph_[C::NFRAG], pw_[C::NFRAG], prow[C::NFRAG], pcol[C::NFRAG];
   bool pval[C::NFRAG];
   if constexpr (S == 1) {
+    // dilation D (pad D): tap (kh, kw) reads dz[h + D(1-kh)][w + D(1-kw)]
+    constexpr int D = DIL;
     const int p0 = tt * 128 * F;                       // first pixel of the tile
     const int hmin = p0 / g.W;
-    zr0 = hmin - 1;
-    zc0 = Z4 ? -4 : -1;
-    ZC = Z4 ? g.W + 8 : g.W + 2;
+    zr0 = hmin - D;
+    zc0 = Z4 ? -4 : -D;
+    ZC = Z4 ? g.W + 8 : g.W + 2 * D;
     const int plast = min(p0 + 128 * F, g.H * g.W) - 1;
-    ZR = plast / g.W - hmin + 3;
+    ZR = plast / g.W - hmin + 1 + 2 * D;
 #pragma unroll
     for (int f = 0; f < C::NFRAG; ++f) {
       const int p = p0 + (wave * F + f) * 32 + col;
@@ -853,8 +857,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
       pval[f] = p < g.H * g.W;
       prow[f] = h;
       pcol[f] = w;
-      // dz[h+1-kh][w+1-kw] sits at Z row (h-hmin)+2-kh, col w+2-kw (+3 with Z4)
-      pbase[f] = pval[f] ? (h - hmin) * ZC + w + (Z4 ? 3 : 0) : 0;
+      // dz[h+D-D kh][w+D-D kw] sits at Z row (h-hmin) + D(2-kh), col w + D(2-kw)
+      // (+ 4-D with Z4, whose rows start at column -4)
+      pbase[f] = pval[f] ? (h - hmin) * ZC + w + (Z4 ? 4 - D : 0) : 0;
       ph_[f] = pw_[f] = 0;
     }
   } else {
@@ -991,7 +996,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv_dx3_direct(ConvGeom g, const
           if (!tap_hits(f, kh, kw)) continue;
           int off;
           if constexpr (S == 1)
-            off = (2 - kh) * ZC + (2 - kw);
+            off = DIL * ((2 - kh) * ZC + (2 - kw));
           else
             off = ((ph_[f] + 1 - kh) >> 1) * ZC2 + ((pw_[f] + 1 - kw) >> 1);
           bv[sl][kk][f] = zl[o * ZP + pbase[f] + off];
@@ -2378,6 +2383,13 @@ static DxPlan plan_dx(const ConvGeom& g) {
   // the tile-direct 3x3 kernels also take the groups of a grouped convolution (g is
   // then the group geometry; one grid row per group)
   const bool tile3 = special || (g.G > 1 && g.D == 1);
+  // stride-1 tile-direct: the plain or grouped 3x3 pad-1 layers, and ungrouped 3x3
+  // layers at dilation 2 with pad 2 (the same output size)
+  const bool s1_direct =
+      g.K == 3 && g.S == 1 &&
+      ((tile3 && g.P == 1 && g.D == 1) ||
+       (g.G == 1 && g.D == 2 && g.P == 2 && g.xs == (int64_t)g.C * g.HW &&
+        g.zs == (int64_t)g.OC * g.OHW));
   if (special && smallc_ok(g)) {
     p.kind = DX_SMALLC;
     p.ksplits = 1;
@@ -2403,8 +2415,8 @@ static DxPlan plan_dx(const ConvGeom& g) {
   };
   // stride 1: larger images (>= 1024 pixels per plane) measured faster with the
   // small (128-pixel, 32-channel) tile, smaller ones with the 256-pixel, 64-channel tile
-  if (tile3 && g.K == 3 && g.P == 1 && g.S == 1 && (int64_t)g.H * g.W >= 1024 &&
-      dx3_s1_fits(g.W, 1, Dx3Cfg<1, 1, 1>::ZPLANE) && g.C % Dx3Cfg<1, 1, 1>::BMC == 0 &&
+  if (s1_direct && (int64_t)g.H * g.W >= 1024 &&
+      dx3_s1_fits(g.W, 1, Dx3Cfg<1, 1, 1>::ZPLANE, g.D) && g.C % Dx3Cfg<1, 1, 1>::BMC == 0 &&
       g.OC % Dx3Cfg<1, 1, 1>::OCB == 0) {
     using Cf = Dx3Cfg<1, 1, 1>;
     p.kind = DX_D3S1_SMALL;
@@ -2413,7 +2425,7 @@ static DxPlan plan_dx(const ConvGeom& g) {
     p.ksplits = direct_splits((int64_t)g.N * p.pixtiles * p.ctiles * g.G, g.OC / Cf::OCB, 3);
     return p;
   }
-  if (tile3 && g.K == 3 && g.P == 1 && g.S == 1 && dx3_s1_fits(g.W, 2, Dx3Cfg<1, 2, 2>::ZPLANE) &&
+  if (s1_direct && dx3_s1_fits(g.W, 2, Dx3Cfg<1, 2, 2>::ZPLANE, g.D) &&
       g.C % Dx3Cfg<1, 2, 2>::BMC == 0 && g.OC % Dx3Cfg<1, 2, 2>::OCB == 0) {
     using Cf = Dx3Cfg<1, 2, 2>;
     p.kind = DX_D3S1;
@@ -2523,24 +2535,38 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
     // 16-byte tile copies: the tile rows (W + 8 floats) must still fit the plane
     const int f1 = p.kind == DX_D3S1 ? 2 : 1;
     const bool z4 = wal && aligned16(dz) && (t.G == 1 || t.gz % 4 == 0) &&
-                    (t.S == 1 ? t.W % 4 == 0 &&
-                                    ((128 * f1 - 1) / t.W + 4) * (t.W + 8) <= Dx3Cfg<1, 1, 1>::ZPLANE
+                    (t.S == 1 ? t.W % 4 == 0 && t.D <= 4 &&
+                                    ((128 * f1 - 1) / t.W + 2 + 2 * t.D) * (t.W + 8) <=
+                                        Dx3Cfg<1, 1, 1>::ZPLANE
                               : t.OW % 4 == 0);
-#define CBB_DX3(S_, F_, RM_, Z4_)                                                         \
+#define CBB_DX3D(S_, F_, RM_, Z4_, DIL_)                                                  \
   if (wal)                                                                                \
-    conv_dx3_direct<S_, F_, RM_, true, Z4_><<<grid, kThreads, 0, st>>>(                   \
+    conv_dx3_direct<S_, F_, RM_, true, Z4_, DIL_><<<grid, kThreads, 0, st>>>(             \
         t, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);                   \
   else                                                                                    \
-    conv_dx3_direct<S_, F_, RM_, false, false><<<grid, kThreads, 0, st>>>(                \
+    conv_dx3_direct<S_, F_, RM_, false, false, DIL_><<<grid, kThreads, 0, st>>>(          \
         t, wt, dz, dx, ws, accumulate, p.pixtiles, tiles_w, p.ksplits);
+#define CBB_DX3(S_, F_, RM_, Z4_) CBB_DX3D(S_, F_, RM_, Z4_, 1)
     if (p.kind == DX_D3S1) {
-      if (z4) {
+      if (t.D == 2) {
+        if (z4) {
+          CBB_DX3D(1, 2, 2, true, 2)
+        } else {
+          CBB_DX3D(1, 2, 2, false, 2)
+        }
+      } else if (z4) {
         CBB_DX3(1, 2, 2, true)
       } else {
         CBB_DX3(1, 2, 2, false)
       }
     } else if (p.kind == DX_D3S1_SMALL) {
-      if (z4) {
+      if (t.D == 2) {
+        if (z4) {
+          CBB_DX3D(1, 1, 1, true, 2)
+        } else {
+          CBB_DX3D(1, 1, 1, false, 2)
+        }
+      } else if (z4) {
         CBB_DX3(1, 1, 1, true)
       } else {
         CBB_DX3(1, 1, 1, false)
@@ -2553,6 +2579,7 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
       }
     }
 #undef CBB_DX3
+#undef CBB_DX3D
     int rc = check_launch("conv_dx3_direct", st);
     if (rc || p.ksplits == 1) return rc;
     return launch_dx_reduce(dx, ws, p.ksplits, (int64_t)g.N * g.C * g.HW, accumulate, st);
@@ -2563,7 +2590,8 @@ int launch_conv_dx(const ConvGeom& g, const float* wt, const float* dz, float* d
   if (!dense(g)) {
     const ConvGeom s = group_geom(g);
     const DxPlan p = plan_dx(s);
-    // grouped, undilated 3x3 pad 1: the tile-direct kernel, all groups in one launch
+    // grouped, undilated 3x3 pad 1 (all groups in one launch), or dilated 3x3 with pad
+    // equal to the dilation: the tile-direct kernel
     if (is_tile3(p)) return tile_direct(s, p);
     // grouped or dilated otherwise: the general kernel on the group geometry, all
     // groups in one launch (group j: input channels j*C/G.., output channels

@@ -222,6 +222,13 @@ GD_CASES = [  # n, c, h, w, oc, k, s, p, bn, act, groups, dilation
     (2, 64, 16, 64, 256, 3, 2, 1, True, "leaky", 2, 1),
     (2, 128, 16, 16, 256, 3, 1, 1, False, "linear", 2, 1),
     (2, 8, 90, 91, 8, 5, 2, 2, False, "relu", 8, 1),        # depthwise, 8190-pixel plane in LDS, s2
+    # dilation-2 3x3 (pad 2) dX on the stride-1 tile-direct kernel: 256-pixel tiles with
+    # 16-byte tile copies, 128-pixel tiles, and 4-byte copies (width not a multiple of 4);
+    # dilation 3 stays on the general kernel
+    (2, 64, 12, 20, 16, 3, 1, 2, True, "leaky", 1, 2),
+    (1, 32, 40, 36, 24, 3, 1, 2, False, "relu", 1, 2),
+    (2, 64, 9, 18, 8, 3, 1, 2, True, "linear", 1, 2),
+    (1, 32, 40, 36, 24, 3, 1, 3, False, "relu", 1, 3),
 ]
 
 
