@@ -518,21 +518,34 @@ __global__ __launch_bounds__(kThreads, 2) void conv_fwd3_s2(ConvGeom g, const fl
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][f][r] = 0.f;
 
+  // the operands of step k+1 are read from LDS while the matrix instructions of step k
+  // issue (two register sets), so each step waits only for reads issued a step earlier
   auto compute = [&](const float* Xs, const float* Ws) {
+    constexpr int NST = kF2CC / 2 * 9;
+    float op[2][4];
+    auto fetch = [&](int st, int sl) {
+      const int pc = st / 9, t = st % 9, kh = t / 3, kw = t % 3;
+      const int ao = (2 * pc * 9 + t) * kF2WP;
+      const int bo = 2 * pc * kF2CP + kh * kF2XP + kw;
+      op[sl][0] = Ws[abase + ao];
+      op[sl][1] = Ws[abase + ao + 32];
+      op[sl][2] = Xs[bbase[0] + bo];
+      op[sl][3] = Xs[bbase[1] + bo];
+    };
+    fetch(0, 0);
 #pragma unroll
-    for (int pc = 0; pc < kF2CC / 2; ++pc)
-#pragma unroll
-      for (int t = 0; t < 9; ++t) {
-        const int kh = t / 3, kw = t % 3;
-        const int ao = (2 * pc * 9 + t) * kF2WP;
-        const int bo = 2 * pc * kF2CP + kh * kF2XP + kw;
-        const float a0 = Ws[abase + ao], a1 = Ws[abase + ao + 32];
-        const float b0 = Xs[bbase[0] + bo], b1 = Xs[bbase[1] + bo];
-        acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-        acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-        acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-        acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
-      }
+    for (int st = 0; st < NST; ++st) {
+      const int sl = st & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 1 < NST) fetch(st + 1, sl ^ 1);
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[sl][0], op[sl][2], acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[sl][0], op[sl][3], acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[sl][1], op[sl][2], acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(op[sl][1], op[sl][3], acc[1][1], 0, 0, 0);
+      if (st + 1 < NST) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // 4 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                     // 4 MFMA
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // chunk c in buffer c & 1: wait for this wave's copies of it (nothing younger is in
