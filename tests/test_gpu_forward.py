@@ -70,11 +70,13 @@ def gpu_forward(torch, case, x, wt, gamma, beta, bias, mean, var):
 
 
 @pytest.mark.parametrize("case,offset", [(FWD_CASES[1], 40.0), (FWD_CASES[2], -25.0),
-                                         ((4, 3, 64, 64, 32, 3, 1, 1, 1, "leaky", 1, 1), 60.0)])
+                                         ((4, 3, 64, 64, 32, 3, 1, 1, 1, "leaky", 1, 1), 60.0),
+                                         ((2, 16, 40, 72, 64, 3, 2, 1, 1, "leaky", 1, 1), 40.0)])
 def test_forward_statistics_with_a_large_mean(case, offset):
-    """One-pass batch statistics (shifted per-thread sums merged pairwise) when the conv
-    output's mean is large against its spread: mean, var and x_norm still match the
-    oracle's two-pass double statistics."""
+    """Batch statistics when the conv output's mean is large against its spread (the
+    one-pass shifted sums of the statistics pass and of the first-layer kernels; the
+    last case's z comes from the stride-2 tile kernel): mean, var and x_norm still match
+    the oracle's two-pass double statistics."""
     torch = require_gpu()
     announce(f"forward statistics, input offset {offset}: {case}")
     n, c, h, w, oc, k, s, p, bn, act, groups, dil = case
