@@ -161,49 +161,61 @@ int launch_shortcut(int64_t count, float alpha, float beta, const float* delta, 
 }
 
 // --------------------------------------------------------------- route
-// d_in[j*size + e] += delta[offset + j*outputs + e], for all images j, e < size.
-__global__ __launch_bounds__(kThreads) void route_kernel(int batch, int64_t size, int64_t outputs,
-                                                         int64_t offset,
+// d_in[t][j*size_t + e] += delta[j*outputs + off_t + e] for every image j and e < size_t:
+// one pass over the columns of delta that up to kRouteMax inputs cover (column e of that
+// span belongs to the last input whose offset in it is <= e).  vec: every size a multiple
+// of 4 (so are the offsets and `outputs`) and the tensors 16-byte aligned; then indices
+// count 16-byte units.
+constexpr int kRouteMax = 8;
+struct RouteArgs {
+  int n;
+  int64_t size[kRouteMax], off[kRouteMax];
+  float* d[kRouteMax];
+};
+__global__ __launch_bounds__(kThreads) void route_kernel(int batch, int64_t outputs, int64_t span,
                                                          const float* __restrict__ delta,
-                                                         float* __restrict__ d_in, int vec) {
+                                                         RouteArgs a, int vec) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   const int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (vec) {
-    const int64_t s4 = size >> 2, total = (int64_t)batch * s4;
-    for (int64_t i = i0; i < total; i += stride) {
-      const int64_t j = i / s4, e4 = i - j * s4;
-      const float4 d =
-          *reinterpret_cast<const float4*>(delta + offset + j * outputs + 4 * e4);
-      float4* p = reinterpret_cast<float4*>(d_in + j * size) + e4;
+  const int u = vec ? 4 : 1;
+  const int64_t spu = span / u, outu = outputs / u, total = (int64_t)batch * spu;
+  for (int64_t i = i0; i < total; i += stride) {
+    const int64_t j = i / spu, e = i - j * spu;
+    int t = 0;
+#pragma unroll
+    for (int k = 1; k < kRouteMax; ++k)
+      if (k < a.n && a.off[k] / u <= e) t = k;
+    const int64_t dst = j * (a.size[t] / u) + e - a.off[t] / u, src = j * outu + e;
+    if (vec) {
+      const float4 d = reinterpret_cast<const float4*>(delta)[src];
+      float4* p = reinterpret_cast<float4*>(a.d[t]) + dst;
       float4 v = *p;
       v.x += d.x; v.y += d.y; v.z += d.z; v.w += d.w;
       *p = v;
-    }
-  } else {
-    const int64_t total = (int64_t)batch * size;
-    for (int64_t i = i0; i < total; i += stride) {
-      const int64_t j = i / size, e = i - j * size;
-      d_in[j * size + e] += delta[offset + j * outputs + e];
+    } else {
+      a.d[t][dst] += delta[src];
     }
   }
 }
 
 int launch_route(int batch, int n_in, const int64_t* sizes, const float* delta,
                  float* const* d_in, hipStream_t st) {
+  // n_in <= kRouteMax (checked by the API): one launch over the whole route delta
+  RouteArgs a{};
+  a.n = n_in;
   int64_t outputs = 0;
-  for (int t = 0; t < n_in; ++t) outputs += sizes[t];
-  int64_t offset = 0;
-  for (int t = 0; t < n_in; ++t) {
-    const int vec = sizes[t] % 4 == 0 && outputs % 4 == 0 && offset % 4 == 0 &&
-                    aligned16(delta) && aligned16(d_in[t]);
-    const int64_t work = (int64_t)batch * (vec ? sizes[t] / 4 : sizes[t]);
-    route_kernel<<<grid_for(work), kThreads, 0, st>>>(batch, sizes[t], outputs, offset, delta,
-                                                      d_in[t], vec);
-    const int rc = check_launch("route_kernel", st);
-    if (rc) return rc;
-    offset += sizes[t];
+  bool vec = aligned16(delta);
+  for (int k = 0; k < n_in; ++k) {
+    a.size[k] = sizes[k];
+    a.off[k] = outputs;
+    a.d[k] = d_in[k];
+    vec = vec && sizes[k] % 4 == 0 && aligned16(d_in[k]);
+    outputs += sizes[k];
   }
-  return CBB_OK;
+  const int64_t work = (int64_t)batch * (vec ? outputs / 4 : outputs);
+  route_kernel<<<grid_for(work), kThreads, 0, st>>>(batch, outputs, outputs, delta, a,
+                                                    vec ? 1 : 0);
+  return check_launch("route_kernel", st);
 }
 
 // --------------------------------------------------------------- upsample

@@ -629,6 +629,17 @@ def test_shortcut_route_upsample_maxpool_exact():
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(zip(ins, refs)):
         assert_exact(f"route{i}", a.cpu().numpy(), b.astype(np.float32))
+    # route: the most inputs a call takes (8, one launch), 16-byte pieces (sizes multiples
+    # of 4) and ragged sizes, each added onto nonzero deltas
+    for chans, hw in (((4, 8, 4, 12, 4, 4, 8, 4), 2), ((1, 3, 2, 5, 1, 1, 2, 3), 3)):
+        dr = r.normal(size=(2, sum(chans), hw, hw)).astype(np.float32)
+        ins0 = [r.normal(size=(2, cc, hw, hw)).astype(np.float32) for cc in chans]
+        ins = [_t(torch, a) for a in ins0]
+        cbb.route_backward(_t(torch, dr), ins)
+        refs = O.route_backward(dr, [a.copy() for a in ins0])
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(ins, refs)):
+            assert_exact(f"route{len(chans)}.{hw}.{i}", a.cpu().numpy(), b.astype(np.float32))
     # upsample with integer deltas: exact; random deltas: tolerance
     du = r.integers(-20, 20, size=(2, 3, 8, 6)).astype(np.float32)
     dsrc = torch.zeros(2, 3, 4, 3, device="cuda")
