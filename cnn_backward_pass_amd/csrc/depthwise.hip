@@ -138,6 +138,28 @@ __global__ __launch_bounds__(kThreads) void dwise_dx_lds(ConvGeom g, const float
   for (int t = 0; t < K * K; ++t) wk[t] = wt[(int64_t)c * K * K + t];
   __syncthreads();
   float* dxp = dx + plane * g.HW;
+  if (g.S == 1 && g.W <= kThreads) {
+    // every tap lands on an output position: no phase test; each thread keeps one column
+    // and walks every R-th row (R = rows per pass), so no index division per element
+    const int R = kThreads / g.W, r0 = threadIdx.x / g.W, w = threadIdx.x - r0 * g.W;
+    if (r0 >= R) return;
+    for (int h = r0; h < g.H; h += R) {
+      float acc = 0.f;
+#pragma unroll
+      for (int kh = 0; kh < K; ++kh) {
+        const int ho = h + g.P - kh * g.D;
+        if ((unsigned)ho >= (unsigned)g.OH) continue;
+#pragma unroll
+        for (int kw = 0; kw < K; ++kw) {
+          const int wo = w + g.P - kw * g.D;
+          if ((unsigned)wo < (unsigned)g.OW) acc += wk[kh * K + kw] * zs[ho * g.OW + wo];
+        }
+      }
+      const int e = h * g.W + w;
+      dxp[e] = accumulate ? dxp[e] + acc : acc;
+    }
+    return;
+  }
   if (g.S == 1) {   // every tap lands on an output position: no phase test, no division
     for (int e = threadIdx.x; e < g.HW; e += kThreads) {
       const int h = e / g.W, w = e - h * g.W;
@@ -200,9 +222,10 @@ __global__ __launch_bounds__(kThreads) void dwise_dw_lds(ConvGeom g, const float
     for (int e = threadIdx.x; e < g.HW; e += kThreads) xs[e] = xp[e];
     for (int e = threadIdx.x; e < g.OHW; e += kThreads) zs[e] = dzp[e];
     __syncthreads();
-    for (int q = threadIdx.x; q < g.OHW; q += kThreads) {
-      const int ho = q / g.OW, wo = q - ho * g.OW;
-      const float d = zs[q];
+    // each thread keeps one output column and walks every R-th output row (R = rows per
+    // pass; OW <= 256), else the flat walk with a division per position
+    auto one = [&](int ho, int wo) {
+      const float d = zs[ho * g.OW + wo];
       const int h0 = ho * g.S - g.P, w0 = wo * g.S - g.P;
 #pragma unroll
       for (int kh = 0; kh < K; ++kh) {
@@ -213,6 +236,16 @@ __global__ __launch_bounds__(kThreads) void dwise_dw_lds(ConvGeom g, const float
           const int w = w0 + kw * g.D;
           if (hv && (unsigned)w < (unsigned)g.W) acc[kh * K + kw] += d * xs[h * g.W + w];
         }
+      }
+    };
+    if (g.OW <= kThreads) {
+      const int R = kThreads / g.OW, r0 = threadIdx.x / g.OW, wo = threadIdx.x - r0 * g.OW;
+      if (r0 < R)
+        for (int ho = r0; ho < g.OH; ho += R) one(ho, wo);
+    } else {
+      for (int q = threadIdx.x; q < g.OHW; q += kThreads) {
+        const int ho = q / g.OW;
+        one(ho, q - ho * g.OW);
       }
     }
   }
