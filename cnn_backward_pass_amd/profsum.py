@@ -207,6 +207,48 @@ def write_mfma(a) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+LDS_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS")
+
+
+def lds_rows(db: str):
+    """Per kernel of the profiled stage: dispatches, LDS instructions per launch and the
+    bank-conflict share SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles the LDS stalled
+    on bank conflicts over cycles it was busy with indexed accesses), each counter summed
+    over the rows of a dispatch."""
+    kinds = collections.defaultdict(lambda: [0, 0.0, 0.0, 0.0])
+    for name, vals in dispatch_counters(db).values():
+        if "cbb::" not in name or not all(c in vals for c in LDS_COUNTERS):
+            continue
+        k = kinds[_short(name)]
+        k[0] += 1
+        k[1] += sum(vals["SQ_INSTS_LDS"])
+        k[2] += sum(vals["SQ_LDS_BANK_CONFLICT"])
+        k[3] += sum(vals["SQ_LDS_IDX_ACTIVE"])
+    return {k: {"dispatches": v[0], "lds_insts": v[1] / v[0],
+                "conflict_share": v[2] / v[3] if v[3] > 0 else 0.0}
+            for k, v in kinds.items() if v[1] > 0}
+
+
+def write_lds(a) -> None:
+    lines = ["# LDS bank conflicts (rocprofv3 --pmc)", "",
+             "Per kernel of each stage: LDS instructions per launch (SQ_INSTS_LDS) and the share "
+             "of the LDS-busy cycles (SQ_LDS_IDX_ACTIVE) stalled on bank conflicts "
+             "(SQ_LDS_BANK_CONFLICT).", ""]
+    for stage, db, cmd in zip(a.stage, a.db, a.cmd):
+        rows = lds_rows(db)
+        lines += [f"## {stage}", "", "```", cmd, "```", "",
+                  "| kernel | dispatches | LDS instructions / launch | bank-conflict share |",
+                  "|---|---|---|---|"]
+        for k in sorted(rows, key=lambda k: -rows[k]["lds_insts"]):
+            r = rows[k]
+            lines.append(f"| `{k}` | {r['dispatches']} | {r['lds_insts']:.3g} | "
+                         f"{r['conflict_share'] * 100:.1f}% |")
+        lines += ["", "lds-json: " + json.dumps({"stage": stage, "kernels": rows,
+                                                   "sources": sources_digest()}), ""]
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines))
+
+
 def load_traffic(stage: str, profiles_dir: str | None = None):
     """Traffic record for ``stage`` whose source digest matches the current sources, else None."""
     d = profiles_dir or os.path.join(ROOT, "profiles")
@@ -265,8 +307,15 @@ def main(argv=None) -> None:
     m.add_argument("--cmd", required=True)
     m.add_argument("--simds", type=int, default=1024, help="SIMDs on the GPU (256 CUs x 4)")
     m.add_argument("--xcds", type=int, default=8, help="dies GRBM_GUI_ACTIVE is summed over")
+    ld = sub.add_parser("lds")
+    ld.add_argument("--stage", action="append", required=True)
+    ld.add_argument("--db", action="append", required=True)
+    ld.add_argument("--cmd", action="append", required=True)
+    ld.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    if a.cmd_name == "trace":
+    if a.cmd_name == "lds":
+        write_lds(a)
+    elif a.cmd_name == "trace":
         write_trace(a.db, a.out, a.title, a.cmd)
     elif a.cmd_name == "mfma":
         write_mfma(a)

@@ -65,3 +65,27 @@ def test_mfma_rows_per_kernel(tmp_path):
     assert r["mfma_flops"] == (2000.0 + 3000.0) * 512 / 2
     assert abs(r["mfma_busy"] - (0.4 + 0.2) / 2) < 1e-12
     assert r["gui_active_cycles"] == 10.0
+
+
+def test_lds_rows_per_kernel(tmp_path):
+    """LDS instructions average over dispatches; the conflict share divides the summed
+    conflict cycles by the summed LDS-busy cycles; kernels without LDS work are left out."""
+    k = "void cbb::conv_first_rows<3, false, 0>(int)"
+    db = tmp_path / "l.db"
+    _db(db, [(1, k, "SQ_INSTS_LDS", 100.0), (1, k, "SQ_INSTS_LDS", 100.0),
+             (1, k, "SQ_LDS_BANK_CONFLICT", 30.0), (1, k, "SQ_LDS_IDX_ACTIVE", 100.0),
+             (2, k, "SQ_INSTS_LDS", 200.0), (2, k, "SQ_LDS_BANK_CONFLICT", 10.0),
+             (2, k, "SQ_LDS_IDX_ACTIVE", 100.0),
+             (3, "void cbb::actbn_coef(int)", "SQ_INSTS_LDS", 0.0),
+             (3, "void cbb::actbn_coef(int)", "SQ_LDS_BANK_CONFLICT", 0.0),
+             (3, "void cbb::actbn_coef(int)", "SQ_LDS_IDX_ACTIVE", 0.0)])
+    rows = profsum.lds_rows(str(db))
+    assert list(rows) == ["conv_first_rows<3, false, 0>"]
+    r = rows["conv_first_rows<3, false, 0>"]
+    assert r["dispatches"] == 2 and r["lds_insts"] == 200.0
+    assert abs(r["conflict_share"] - 0.2) < 1e-12
+    out = tmp_path / "lds.md"
+    profsum.main(["lds", "--stage", "wl.0.block", "--db", str(db), "--cmd", "c", "--out",
+                  str(out)])
+    assert "20.0%" in out.read_text()
+
